@@ -1,0 +1,584 @@
+"""Pins of the CPU oracle against things other than itself: values the pages
+print for their worked examples, closed forms, exact integer arithmetic,
+library routines in fp64 within a rounding-error bound, and spec tables.
+
+All tests here run on the CPU (no GPU marker)."""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import golden
+from invariant_reductions_amd import inputs
+
+U32 = 2.0 ** -24          # unit roundoff of fp32
+
+
+def gamma(n: int) -> float:
+    return n * U32 / (1 - n * U32)
+
+
+# ---------------------------------------------------------------------------
+# Case 1 / Case 2: fold primitives (printed worked examples)
+# ---------------------------------------------------------------------------
+
+def test_case1_three_terms():
+    g = golden("case1_nonassociativity.json")["three_terms"]
+    assert oracle.fold_seq_f64([0.1, 1e20, -1e20]) == g["(0.1+1e20)-1e20"]
+    assert oracle.fold_seq_f64([1e20, -1e20, 0.1]) == g["0.1+(1e20-1e20)"]
+
+
+def test_case1_shuffled_left_folds():
+    g = golden("case1_nonassociativity.json")["shuffle"]
+    random.seed(g["seed"])
+    seen = set()
+    for _ in range(g["draws"]):
+        vals = list(g["values"])
+        random.shuffle(vals)
+        seen.add(oracle.fold_seq_f64(vals))
+    assert len(seen) == g["left_fold_unique"]
+    assert min(seen) == g["left_fold_min"] and max(seen) == g["left_fold_max"]
+
+
+def _case2_vector():
+    rng = np.random.default_rng(0)
+    return (rng.standard_normal(4096) * 1e3).astype(np.float32)
+
+
+def test_case2_sequential_pairwise_split():
+    g = golden("case2_reduction_orders.json")
+    a = _case2_vector()
+    seq = oracle.fold_seq_f32(a)
+    assert f"{seq:.8e}" == g["sequential"]
+    assert f"{oracle.fold_pairwise_f32(a):.8e}" == g["pairwise"]
+    for s, (val, diff) in g["split"].items():
+        v = oracle.fold_split_f32(a, int(s))
+        assert f"{v:.8e}" == val, s
+        assert f"{abs(v - seq):.8e}" == diff, s
+
+
+def test_case2_matmul_accumulates_in_the_sequential_order():
+    """y = a . ones with f32 inputs is the sequential fold of a (x*1 is exact),
+    so the matmul oracle must print the page's sequential value."""
+    g = golden("case2_reduction_orders.json")
+    a = _case2_vector()
+    y = oracle.matmul(a[None, :], np.ones((1, 4096), np.float32), "f32", True)
+    assert f"{y[0, 0]:.8e}" == g["sequential"]
+    y2 = oracle.matmul(a[None, :], np.ones((4096, 1), np.float32), "f32", False)
+    assert y2[0, 0] == y[0, 0]
+
+
+# ---------------------------------------------------------------------------
+# Case 4: RMSNorm sum of squares and output (printed worked example)
+# ---------------------------------------------------------------------------
+
+def test_case4_rmsnorm_printed_values():
+    g = golden("case4_rmsnorm.json")
+    H = 4096
+    row = np.array([2.0 ** -(i // 64) for i in range(H)], np.float32)
+    w = np.ones(H, np.float32)
+    y_f, ss_f = oracle.rmsnorm(row[None], w, "f32", 1e-6, return_ss=True)
+    y_r, ss_r = oracle.rmsnorm(np.ascontiguousarray(row[::-1])[None], w, "f32", 1e-6, return_ss=True)
+    assert f"{ss_f[0]:.8e}" == g["sum_sq_forward"]
+    assert f"{ss_r[0]:.8e}" == g["sum_sq_reverse"]
+    assert f"{abs(ss_f[0] - ss_r[0]):.8e}" == g["sum_sq_absdiff"]
+    # the reversed tree's output, put back in the original order: x * inv_rev * w
+    y_rev = y_r[0][::-1]
+    d = np.abs(y_f[0] - y_rev)
+    assert f"{d.max():.6e}" == g["output_max_absdiff"]
+    assert int(np.sum(y_f[0] != y_rev)) == g["output_differing"]
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def test_bf16_decode_all_patterns_vs_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.widen(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_decode_all_patterns_vs_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.widen(bits, "f16")
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _encode_probe_values():
+    rng = np.random.default_rng(5)
+    vals = [rng.standard_normal(20000).astype(np.float32) * s for s in (1e-8, 1e-5, 1e-3, 1, 300, 7e4)]
+    # exact halfway points of both formats and the overflow edges
+    mids_bf = (np.arange(1, 65535, 97, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    h = np.arange(0, 0x7bff, 13, dtype=np.uint16).view(np.float16).astype(np.float64)
+    h2 = np.arange(1, 0x7c00, 13, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids_h = ((h + h2) / 2).astype(np.float32)
+    special = np.array([0.0, -0.0, 65504, 65519.99, 65520, 65536, 3.4e38, np.inf, -np.inf,
+                        2 ** -24, 2 ** -25, 3 * 2 ** -26, 2 ** -14 * (1 - 2 ** -11), 1e-45], np.float32)
+    return np.concatenate(vals + [mids_bf, -mids_bf, mids_h, -mids_h, special, -special]).astype(np.float32)
+
+
+def test_bf16_encode_vs_torch():
+    v = _encode_probe_values()
+    ours = oracle.round_to(v, "bf16")
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    isnan = np.isnan(v)
+    assert np.array_equal(ours[~isnan], ref[~isnan])
+    assert np.all(np.isnan(oracle.widen(ours[isnan], "bf16")))
+    nanin = np.array([np.nan, -np.nan], np.float32)
+    assert np.all(np.isnan(oracle.widen(oracle.round_to(nanin, "bf16"), "bf16")))
+
+
+def test_f16_encode_vs_numpy():
+    v = _encode_probe_values()
+    ours = oracle.round_to(v, "f16")
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    isnan = np.isnan(v)
+    assert np.array_equal(ours[~isnan], ref[~isnan])
+    assert np.all(np.isnan(oracle.widen(ours[isnan], "f16")))
+
+
+def test_e2m1_table_matches_spec():
+    g = golden("ocp_fp4_fp8_values.json")
+    pos = g["e2m1_positive_codes_0_to_7"]
+    for c in range(8):
+        assert oracle.e2m1_value(c) == pos[c]
+        assert oracle.e2m1_value(c | g["e2m1_sign_bit"]) == -pos[c]
+
+
+def test_e4m3_all_codes_vs_torch_and_spec():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    ours = np.array([oracle.e4m3_value(int(c)) for c in codes], np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    g = golden("ocp_fp4_fp8_values.json")["e4m3"]
+    for k, val in g.items():
+        if k == "nan_codes":
+            for c in val:
+                assert np.isnan(oracle.e4m3_value(int(c, 16)))
+        else:
+            assert oracle.e4m3_value(int(k, 16)) == val
+
+
+# ---------------------------------------------------------------------------
+# dense matmul
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", inputs.DTYPES)
+@pytest.mark.parametrize("transposed", [True, False])
+def test_matmul_integer_inputs_are_exact(dtype, transposed):
+    """Integer-valued inputs in [-4, 4] with K = 4096: every partial sum is an
+    integer below 2^24, so any order gives the exact integer result."""
+    rng = np.random.default_rng(11)
+    M, N, K = 5, 67, 4096
+    x = inputs.integer_values(rng, (M, K), -4, 4, dtype)
+    w = inputs.integer_values(rng, (N, K), -4, 4, dtype)
+    exact = inputs.from_storage(x, dtype).astype(np.int64) @ inputs.from_storage(w, dtype).astype(np.int64).T
+    wl = w if transposed else np.ascontiguousarray(w.T)
+    y = oracle.matmul(x, wl, dtype, transposed)
+    assert np.array_equal(y.astype(np.int64), exact)
+
+
+def test_matmul_one_hot_rows_select_weight_columns():
+    rng = np.random.default_rng(3)
+    N, K = 40, 300
+    w = inputs.normal(rng, (N, K), 0.02, dtype="bf16")
+    x = np.zeros((4, K), np.float32)
+    picks = [0, 17, 150, 299]
+    for i, k in enumerate(picks):
+        x[i, k] = 1.0
+    y = oracle.matmul(inputs.to_storage(x, "bf16"), w, "bf16", True)
+    wf = inputs.from_storage(w, "bf16")
+    for i, k in enumerate(picks):
+        assert np.array_equal(y[i], wf[:, k])
+
+
+@pytest.mark.parametrize("dtype", inputs.DTYPES)
+def test_matmul_within_rounding_bound_of_fp64(dtype):
+    x, w, wn = inputs.dense_case(3, 96, 4096, dtype, seed=0)
+    xf = inputs.from_storage(x, dtype).astype(np.float64)
+    wf = inputs.from_storage(w, dtype).astype(np.float64)
+    exact = xf @ wf.T
+    absum = np.abs(xf) @ np.abs(wf).T
+    y = oracle.matmul(x, w, dtype, True)
+    assert np.all(np.abs(y - exact) <= gamma(4096 + 1) * absum)
+    # same order in both layouts -> identical bits
+    assert np.array_equal(oracle.matmul(x, wn, dtype, False), y)
+
+
+# ---------------------------------------------------------------------------
+# quantized matmul
+# ---------------------------------------------------------------------------
+
+def _affine_unit(rng, rows, cols, gs):
+    """scale 1, bias -8: dequantized value = q - 8 exactly."""
+    codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint32)
+    wq = inputs.pack_nibbles(codes)
+    s = np.full((rows, cols // gs), 0x3C00, np.uint16)       # binary16 1.0
+    b = np.full((rows, cols // gs), 0xC800, np.uint16)       # binary16 -8.0
+    return codes, wq, s, b
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("transposed", [True, False])
+def test_affine_unit_scale_is_exact(gs, transposed):
+    rng = np.random.default_rng(gs)
+    M, N, K = 7, 256, 1024
+    rows, cols = (N, K) if transposed else (K, N)
+    codes, wq, s, b = _affine_unit(rng, rows, cols, gs)
+    deq = oracle.dequantize(wq, s, b, rows, cols, oracle.AFFINE, gs)
+    assert np.array_equal(inputs.from_storage(deq, "f16"), codes.astype(np.float32) - 8)
+    x = inputs.integer_values(rng, (M, K), -4, 4, "f16")
+    wmat = codes.astype(np.int64) - 8
+    wmat = wmat if transposed else wmat.T
+    exact = inputs.from_storage(x, "f16").astype(np.int64) @ wmat.T
+    y = oracle.qmatmul(x, wq, s, b, M, N, K, oracle.AFFINE, gs, transposed)
+    assert np.array_equal(y.astype(np.int64), exact)
+
+
+@pytest.mark.parametrize("shape", [(3, 1040, 128), (2, 512, 1040), (4, 64, 48)])
+@pytest.mark.parametrize("transposed", [True, False])
+def test_nvfp4_unit_scale_matches_spec_values(shape, transposed):
+    """Scale byte 0x38 (= 1.0): the dequantized weights are the spec's e2m1
+    values; with integer x every partial sum is a multiple of 1/2 below 2^22,
+    so the result is exact."""
+    g = golden("ocp_fp4_fp8_values.json")
+    spec = np.array(g["e2m1_positive_codes_0_to_7"] + [-v for v in g["e2m1_positive_codes_0_to_7"]])
+    M, K, N = shape
+    rows, cols = (N, K) if transposed else (K, N)
+    rng = np.random.default_rng(K + N)
+    codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint32)
+    wq = inputs.pack_nibbles(codes)
+    s = np.full((rows, cols // 16), 0x38, np.uint8)
+    deq = inputs.from_storage(oracle.dequantize(wq, s, None, rows, cols, oracle.NVFP4, 16), "f16")
+    assert np.array_equal(deq, spec[codes].astype(np.float32))
+    x = inputs.integer_values(rng, (M, K), -8, 8, "f16")
+    wmat = spec[codes] if transposed else spec[codes].T
+    exact = inputs.from_storage(x, "f16").astype(np.float64) @ wmat.T
+    y = oracle.qmatmul(x, wq, s, None, M, N, K, oracle.NVFP4, 16, transposed)
+    assert np.array_equal(y.astype(np.float64), exact)
+
+
+def test_nvfp4_scales_multiply_exactly():
+    """Every (code, scale) pair: the dequantized value equals the product of the
+    spec value and torch's e4m3 decode, exactly."""
+    g = golden("ocp_fp4_fp8_values.json")
+    spec = np.array(g["e2m1_positive_codes_0_to_7"] + [-v for v in g["e2m1_positive_codes_0_to_7"]])
+    scales = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    rows = scales.size
+    codes = np.tile(np.arange(16, dtype=np.uint32), (rows, 1))           # 16 codes per row = 1 group
+    wq = inputs.pack_nibbles(codes)
+    deq = inputs.from_storage(oracle.dequantize(wq, scales[:, None].copy(), None, rows, 16,
+                                                oracle.NVFP4, 16), "f16")
+    sval = torch.from_numpy(scales).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(deq.astype(np.float64), spec[None, :] * sval[:, None])
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128])
+def test_affine_quantize_dequantize_error_bound(gs):
+    rng = np.random.default_rng(9)
+    w = rng.standard_normal((64, 512)).astype(np.float32)
+    wq, s, b = inputs.quantize_affine(w, gs)
+    deq = inputs.from_storage(oracle.dequantize(wq, s, b, 64, 512, oracle.AFFINE, gs), "f16")
+    sv = np.repeat(inputs.from_storage(s, "f16"), gs, axis=1)
+    # half a step, plus binary16 rounding of s, b and of the result
+    bound = 0.5 * sv + 2.0 ** -10 * (np.abs(w) + 16 * sv) + 2.0 ** -11 * np.abs(deq)
+    assert np.all(np.abs(deq - w) <= bound)
+
+
+def test_nvfp4_grid_values_round_trip():
+    """Weights already on the e2m1 grid times a power-of-two scale, with the
+    group maximum 6 * scale, come back exactly."""
+    g = golden("ocp_fp4_fp8_values.json")
+    spec = np.array(g["e2m1_positive_codes_0_to_7"] + [-v for v in g["e2m1_positive_codes_0_to_7"]])
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 16, size=(32, 256))
+    codes[:, ::16] = 7                                                     # group max = 6
+    sc = 2.0 ** rng.integers(-6, 6, size=(32, 16))
+    w = (spec[codes] * np.repeat(sc, 16, axis=1)).astype(np.float32)
+    wq, s = inputs.quantize_nvfp4(w)
+    deq = inputs.from_storage(oracle.dequantize(wq, s, None, 32, 256, oracle.NVFP4, 16), "f16")
+    assert np.array_equal(deq, w)
+
+
+@pytest.mark.parametrize("qmode,gs", [("affine", 32), ("affine", 128), ("nvfp4", 16)])
+@pytest.mark.parametrize("transposed", [True, False])
+def test_qmatmul_tiny_brute_force(qmode, gs, transposed):
+    """Tiny shapes, every output summed in fp64 from the dequantized weights:
+    the oracle lies within the fp32 rounding bound."""
+    M, K, N = 3, 256, 128
+    x, wq, s, b = inputs.qmatmul_case(M, K, N, qmode, gs, transposed, seed=2)
+    qm = oracle.AFFINE if qmode == "affine" else oracle.NVFP4
+    rows, cols = (N, K) if transposed else (K, N)
+    deq = inputs.from_storage(oracle.dequantize(wq, s, b, rows, cols, qm, gs), "f16").astype(np.float64)
+    wmat = deq if transposed else deq.T                                   # [N, K]
+    xf = inputs.from_storage(x, "f16").astype(np.float64)
+    exact = np.zeros((M, N))
+    absum = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            exact[m, n] = sum(xf[m, k] * wmat[n, k] for k in range(K))
+            absum[m, n] = sum(abs(xf[m, k] * wmat[n, k]) for k in range(K))
+    y = oracle.qmatmul(x, wq, s, b, M, N, K, qm, gs, transposed)
+    assert np.all(np.abs(y - exact) <= gamma(K) * absum)
+
+
+def test_quantized_k_tail_defect_signature_is_detectable():
+    """The defect the quantized-matmul page describes (the last 16 K elements of
+    some columns dropped) moves those outputs by exactly x[:, K-16:] @ W[:, K-16:]^T;
+    on the config's tail shape that is far outside the 2e-2 gate, so a GPU
+    kernel with that bug cannot pass the parity test."""
+    M, K, N = 50, 1040, 128
+    x, wq, s, _ = inputs.qmatmul_case(M, K, N, "nvfp4", 16, True, seed=0)
+    good = oracle.qmatmul(x, wq, s, None, M, N, K, oracle.NVFP4, 16, True)
+    deq = inputs.from_storage(oracle.dequantize(wq, s, None, N, K, oracle.NVFP4, 16), "f16")
+    xf = inputs.from_storage(x, "f16")
+    broken = good.copy()
+    cols = (np.arange(N) % 32) >= 16
+    broken[:, cols] -= (xf[:, K - 16:] @ deq[cols, K - 16:].T)
+    rel = np.abs(broken - good).max() / np.abs(good).max()
+    assert rel > 2e-2 * 2
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_constant_rows_closed_form():
+    H = 4096
+    for c in (0.25, -2.0, 8.0):
+        x = inputs.to_storage(np.full((1, H), c, np.float32), "bf16")
+        w = inputs.to_storage(np.linspace(0.5, 1.5, H), "bf16")
+        y = oracle.rmsnorm(x, w, "bf16", 1e-6)
+        wf = inputs.from_storage(w, "bf16").astype(np.float64)
+        expect = np.sign(c) * wf * abs(c) / np.sqrt(c * c + 1e-6)
+        assert np.allclose(y[0], expect, rtol=4 * U32 * 8, atol=0)
+
+
+@pytest.mark.parametrize("dtype", inputs.DTYPES)
+def test_rmsnorm_within_bound_of_torch_fp64(dtype):
+    x, w = inputs.rmsnorm_case(64, 4096, seed=0, dtype=dtype)
+    y = oracle.rmsnorm(x, w, dtype, 1e-6)
+    xt = torch.from_numpy(inputs.from_storage(x, dtype).astype(np.float64))
+    wt = torch.from_numpy(inputs.from_storage(w, dtype).astype(np.float64))
+    ref = torch.nn.functional.rms_norm(xt, (4096,), wt, eps=1e-6).numpy()
+    assert np.all(np.abs(y - ref) <= (gamma(4096) + 10 * U32) * np.abs(ref) + 1e-30)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _torch_sdpa_fp64(q, k, v, kv_len, causal, dtype):
+    qf = torch.from_numpy(inputs.from_storage(q, dtype).astype(np.float64))
+    kf = torch.from_numpy(inputs.from_storage(k, dtype).astype(np.float64))
+    vf = torch.from_numpy(inputs.from_storage(v, dtype).astype(np.float64))
+    B, Q, Hq, D = qf.shape
+    Hkv = kf.shape[2]
+    out = torch.empty(B, Q, Hq, D, dtype=torch.float64)
+    for b in range(B):
+        L = int(kv_len[b])
+        kk = kf[b, :L].permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)      # [Hq, L, D]
+        vv = vf[b, :L].permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+        qq = qf[b].permute(1, 0, 2)                                                # [Hq, Q, D]
+        pos = torch.arange(Q) + (L - Q)
+        mask = (torch.arange(L)[None, :] <= pos[:, None]) if causal else torch.ones(Q, L, dtype=torch.bool)
+        o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=1 / np.sqrt(D))
+        out[b] = o.permute(1, 0, 2)
+    return out.numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sdpa_within_bound_of_torch_fp64(causal):
+    B, Q, Lcap = 2, 8, 300
+    q, k, v = inputs.sdpa_case(B, Q, Lcap, 8, 2, 64, seed=1)
+    kv_len = np.array([300, 131], np.int32)
+    o = oracle.sdpa(q, k, v, kv_len, 1 / np.sqrt(64), causal, "bf16")
+    ref = _torch_sdpa_fp64(q, k, v, kv_len, causal, "bf16")
+    # scores carry ~gamma(D) * |q||k| * scale of error, doubled through exp and
+    # the normalisation; the value sums add gamma(L)
+    err = np.abs(o - ref)
+    tol = (2 * gamma(64) * 64 * 16 / 8 + 2 * gamma(300) + 8 * U32) * np.abs(inputs.from_storage(v, "bf16")).max()
+    assert err.max() <= tol * 4, (err.max(), tol)
+    assert np.abs(o - ref).max() < 1e-4
+
+
+def test_sdpa_single_key_returns_value_row():
+    q, k, v = inputs.sdpa_case(1, 1, 16, 4, 1, 128, seed=3)
+    o = oracle.sdpa(q, k, v, np.array([1], np.int32), 1 / np.sqrt(128), True, "bf16")
+    vf = inputs.from_storage(v, "bf16")
+    for h in range(4):
+        assert np.array_equal(o[0, 0, h], vf[0, 0, 0])
+
+
+def test_sdpa_constant_values_closed_form():
+    q, k, v = inputs.sdpa_case(1, 4, 500, 8, 2, 128, seed=4)
+    v = inputs.to_storage(np.full(v.shape, -0.5, np.float32), "bf16")
+    o = oracle.sdpa(q, k, v, np.array([437], np.int32), 1 / np.sqrt(128), True, "bf16")
+    assert np.all(o == np.float32(-0.5))
+
+
+def test_sdpa_zero_query_is_mean_of_values():
+    rng = np.random.default_rng(6)
+    q = inputs.to_storage(np.zeros((1, 1, 4, 128), np.float32), "bf16")
+    k = inputs.normal(rng, (1, 64, 1, 128))
+    v = inputs.integer_values(rng, (1, 64, 1, 128), -8, 8, "bf16")
+    o = oracle.sdpa(q, k, v, np.array([50], np.int32), 0.1, True, "bf16")
+    mean = inputs.from_storage(v, "bf16")[0, :50, 0].astype(np.float64).mean(axis=0)
+    assert np.all(np.abs(o[0, 0] - mean[None]) <= 2 * U32 * np.abs(mean[None]))
+
+
+def test_sdpa_causal_block_row_equals_lone_query():
+    """Query j of a causal block at length L reduces over keys 0..L-Q+j, the
+    same keys as a lone query at length L-Q+j+1."""
+    L, Q = 1028, 8
+    q, k, v = inputs.sdpa_case(1, Q, L, 8, 2, 128, seed=0)
+    blk = oracle.sdpa(q, k, v, np.array([L], np.int32), 1 / np.sqrt(128), True, "bf16")
+    for j in range(Q):
+        one = oracle.sdpa(np.ascontiguousarray(q[:, j:j + 1]), k, v, np.array([L - Q + j + 1], np.int32),
+                          1 / np.sqrt(128), True, "bf16")
+        assert np.array_equal(one[0, 0], blk[0, j])
+
+
+# ---------------------------------------------------------------------------
+# pointwise ops and the decoder composition
+# ---------------------------------------------------------------------------
+
+def test_rope_rotates_the_right_pairs():
+    D = 16
+    cos_t, sin_t = inputs.rope_tables(8, D)
+    x = np.zeros((D // 2, 1, D), np.float32)
+    for i in range(D // 2):
+        x[i, 0, i] = 1.0
+    pos = np.full(D // 2, 5, np.int32)
+    out = oracle.rope(x, pos, cos_t, sin_t, "f32")
+    for i in range(D // 2):
+        expect = np.zeros(D, np.float32)
+        expect[i] = cos_t[5, i]
+        expect[i + D // 2] = sin_t[5, i]
+        assert np.array_equal(out[i, 0], expect)
+    out0 = oracle.rope(np.ones((1, 2, D), np.float32), np.zeros(1, np.int32), cos_t, sin_t, "f32")
+    assert np.array_equal(out0, np.ones((1, 2, D), np.float32))
+
+
+def test_silu_mul_vs_torch_fp64():
+    rng = np.random.default_rng(8)
+    g = inputs.normal(rng, (4096,), 4.0)
+    u = inputs.normal(rng, (4096,), 1.0)
+    out = oracle.silu_mul(g, u, "bf16")
+    gf = torch.from_numpy(inputs.from_storage(g, "bf16").astype(np.float64))
+    ref = (torch.nn.functional.silu(gf) * torch.from_numpy(inputs.from_storage(u, "bf16").astype(np.float64))).numpy()
+    assert np.all(np.abs(out - ref) <= 8 * U32 * np.abs(ref) + 1e-30)
+
+
+def test_argmax_lowest_index_wins_ties():
+    x = inputs.to_storage(np.array([[1, 3, 3, 2], [5, 5, 5, 5], [-1, -2, -1, -3]], np.float32), "bf16")
+    assert oracle.argmax(x, "bf16").tolist() == [1, 0, 0]
+
+
+def test_pointwise_ops_are_batch_invariant():
+    """Each row of a pointwise op on a batch equals the op on that row alone."""
+    rng = np.random.default_rng(10)
+    g = inputs.normal(rng, (16, 512), 3.0)
+    u = inputs.normal(rng, (16, 512))
+    full = oracle.silu_mul(g, u, "bf16")
+    cos_t, sin_t = inputs.rope_tables(64, 128)
+    x = inputs.normal(rng, (16, 4, 128))
+    pos = rng.integers(0, 64, size=16).astype(np.int32)
+    rfull = oracle.rope(x, pos, cos_t, sin_t, "bf16")
+    for i in (0, 7, 15):
+        assert np.array_equal(oracle.silu_mul(g[i:i + 1].copy(), u[i:i + 1].copy(), "bf16"), full[i:i + 1])
+        assert np.array_equal(oracle.rope(x[i:i + 1].copy(), pos[i:i + 1].copy(), cos_t, sin_t, "bf16"),
+                              rfull[i:i + 1])
+
+
+TINY = dict(hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, ffn=96, vocab=50, n_layers=2, eps=1e-6)
+
+
+def _tiny_weights(seed=0, scale=0.2):
+    rng = np.random.default_rng(seed)
+    c = TINY
+    H, F, V = c["hidden"], c["ffn"], c["vocab"]
+    qkv = (c["n_heads"] + 2 * c["n_kv_heads"]) * c["head_dim"]
+    layers = []
+    for _ in range(c["n_layers"]):
+        layers.append(dict(
+            attn_norm=inputs.normal(rng, (H,), 0.1, loc=1.0),
+            wqkv=inputs.normal(rng, (qkv, H), scale),
+            wo=inputs.normal(rng, (H, c["n_heads"] * c["head_dim"]), scale),
+            mlp_norm=inputs.normal(rng, (H,), 0.1, loc=1.0),
+            wgu=inputs.normal(rng, (2 * F, H), scale),
+            wdown=inputs.normal(rng, (H, F), scale)))
+    return dict(embed=inputs.normal(rng, (V, H), 1.0), layers=layers,
+                final_norm=inputs.normal(rng, (H,), 0.1, loc=1.0),
+                lm_head=inputs.normal(rng, (V, H), scale))
+
+
+def _torch_tiny_forward(W, tokens, cos_t, sin_t):
+    """fp64 reference of the same model built from torch library ops, rounding
+    each op's output to bf16 as the model stores it."""
+    c = TINY
+    f = lambda a: torch.from_numpy(inputs.from_storage(a, "bf16").astype(np.float64))
+    bf = lambda t: t.to(torch.bfloat16).to(torch.float64)
+    H, Hq, Hkv, D, F = c["hidden"], c["n_heads"], c["n_kv_heads"], c["head_dim"], c["ffn"]
+    T = len(tokens)
+    x = f(W["embed"])[torch.from_numpy(np.asarray(tokens, np.int64))]
+    ct = torch.from_numpy(cos_t[:T].astype(np.float64))
+    st = torch.from_numpy(sin_t[:T].astype(np.float64))
+
+    def rot(t):                                                  # t [T, h, D]
+        a, b = t[..., :D // 2], t[..., D // 2:]
+        return torch.cat([a * ct[:, None] - b * st[:, None], b * ct[:, None] + a * st[:, None]], dim=-1)
+
+    for L in W["layers"]:
+        h = bf(torch.nn.functional.rms_norm(x, (H,), f(L["attn_norm"]), eps=c["eps"]))
+        qkv = bf(h @ f(L["wqkv"]).T)
+        q = bf(rot(qkv[:, :Hq * D].reshape(T, Hq, D)))
+        k = bf(rot(qkv[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)))
+        v = qkv[:, (Hq + Hkv) * D:].reshape(T, Hkv, D)
+        kk = k.permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+        vv = v.permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+        o = torch.nn.functional.scaled_dot_product_attention(q.permute(1, 0, 2), kk, vv, is_causal=True)
+        o = bf(o.permute(1, 0, 2).reshape(T, Hq * D))
+        x = bf(x + bf(o @ f(L["wo"]).T))
+        h = bf(torch.nn.functional.rms_norm(x, (H,), f(L["mlp_norm"]), eps=c["eps"]))
+        gu = bf(h @ f(L["wgu"]).T)
+        a = bf(torch.nn.functional.silu(gu[:, :F]) * gu[:, F:])
+        x = bf(x + bf(a @ f(L["wdown"]).T))
+    h = bf(torch.nn.functional.rms_norm(x, (H,), f(W["final_norm"]), eps=c["eps"]))
+    return (h @ f(W["lm_head"]).T).numpy()
+
+
+def test_decoder_matches_torch_fp64_reference():
+    from oracle import decoder
+    W = _tiny_weights()
+    cos_t, sin_t = inputs.rope_tables(64, TINY["head_dim"])
+    tokens = np.random.default_rng(1).integers(0, TINY["vocab"], size=24)
+    logits, _, _ = decoder.forward(W, TINY, tokens, cos_t, sin_t)
+    ref = _torch_tiny_forward(W, tokens, cos_t, sin_t)
+    rel = np.abs(logits - ref).max() / np.abs(ref).max()
+    assert rel < 2e-2, rel
+
+
+def test_decoder_is_causal():
+    from oracle import decoder
+    W = _tiny_weights(1)
+    cos_t, sin_t = inputs.rope_tables(64, TINY["head_dim"])
+    t1 = np.random.default_rng(2).integers(0, TINY["vocab"], size=20)
+    t2 = t1.copy()
+    t2[12:] = (t2[12:] + 7) % TINY["vocab"]
+    a, _, _ = decoder.forward(W, TINY, t1, cos_t, sin_t)
+    b, _, _ = decoder.forward(W, TINY, t2, cos_t, sin_t)
+    assert np.array_equal(a[:12], b[:12])
+    assert not np.array_equal(a[12:], b[12:])
