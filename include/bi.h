@@ -1,0 +1,225 @@
+/*
+ * bi.h -- C ABI of the batch-invariant reduction library for AMD MI355X (gfx950).
+ *
+ * Every product entry point computes each output row with a reduction tree
+ * fixed by the reduction dimension alone (K for the matmuls, H for RMSNorm,
+ * the key position for attention).  Row i therefore returns the same bits
+ * whether it is evaluated alone, inside a larger batch, at any position of the
+ * batch, or inside a speculative-verification block.  There is no runtime
+ * switch for this: invariance is unconditional.
+ *
+ * Sources (page title, section):
+ *   - "Fix/speculative shape invariance" -- Problem: a single row and a short
+ *     matrix must not select different matmul paths, and two-pass SDPA must
+ *     not derive its split count from the query length; Changes: the canonical
+ *     per-row reduction and the single-query split configuration.
+ *   - "Batch-invariant kernels: why temperature-0 decoding is still
+ *     nondeterministic" -- Mental model (batch invariance; data-parallel vs
+ *     split reductions), Case 6 (RMSNorm data-parallel always; matmul one
+ *     configuration with no split-K; attention with a fixed split size and
+ *     the KV cache updated before the kernel), The boring rule.
+ *   - "Fix fp quantized matmul corruption when the quantized dim is not a
+ *     multiple of 32" -- Problem and Fix (nvfp4 group size 16 makes
+ *     K % 32 == 16 legal; tails must be bounded on loads and stores), Why fix
+ *     the kernel rather than reject the dimension.
+ *
+ * Conventions shared by every call
+ *   - Pointers are device pointers unless stated; every base pointer must be
+ *     16-byte aligned (BI_ERR_ALIGN otherwise).  Tensors are dense row-major.
+ *   - bf16 / f16 data are 16-bit IEEE-style patterns (bfloat16, binary16);
+ *     f32 is binary32.  Accumulation is fp32; outputs are rounded to the
+ *     output type with round-to-nearest-even.
+ *   - The caller owns and allocates every buffer (outputs and workspaces).
+ *     The library never allocates, frees or synchronizes; it keeps no mutable
+ *     global state.  Calls are asynchronous and ordered on `stream`.
+ *   - Inputs are never written.  Outputs are fully overwritten for every
+ *     in-range element; no byte outside an output's extent is written.
+ *   - Errors: arguments are validated on the host before anything is
+ *     launched; on any error nothing is launched and nothing is written.  A
+ *     launch failure reported by the runtime returns BI_ERR_LAUNCH.  Every
+ *     shape that passes validation is computed correctly -- tails are bounded
+ *     on loads and stores, never silently truncated.
+ *   - No exception crosses this interface.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BI_OK = 0,
+    BI_ERR_NULL = 1,        /* a required pointer is NULL */
+    BI_ERR_SHAPE = 2,       /* a dimension is out of range or inconsistent */
+    BI_ERR_DTYPE = 3,       /* unsupported data type code */
+    BI_ERR_GROUP = 4,       /* illegal quantization mode / group size / bits for the shape */
+    BI_ERR_ALIGN = 5,       /* a base pointer is not 16-byte aligned */
+    BI_ERR_WORKSPACE = 6,   /* workspace missing or smaller than the *_workspace_bytes figure */
+    BI_ERR_LAUNCH = 7,      /* the HIP runtime rejected a launch */
+    BI_ERR_UNSUPPORTED = 8  /* legal request this build does not implement */
+} bi_status;
+
+typedef enum { BI_BF16 = 0, BI_F16 = 1, BI_F32 = 2 } bi_dtype;
+typedef enum { BI_AFFINE = 0, BI_NVFP4 = 1 } bi_qmode;
+
+/* ------------------------------------------------------------------------
+ * Dense matmul   y[m,n] = sum_k x[m,k] * W[n,k]
+ * Source: "Fix/speculative shape invariance", Problem and Changes (dense
+ * matmul reduced the same way for one row or a short block, for both
+ * orientations of the weight); "Batch-invariant kernels ...", Case 3 and
+ * Case 6 (one tile configuration for every batch size, no split-K).
+ *   x : [M,K] of `dtype`.
+ *   w : [N,K] of `dtype` when w_transposed != 0, else [K,N].
+ *   y : [M,N] of `dtype` (fp32 accumulation, RNE to `dtype`).
+ *   dtype: BI_BF16, BI_F16 or BI_F32.
+ *   M >= 1, N >= 1, K >= 1.
+ * Row m of y depends only on row m of x, on W and on K -- not on M, N, or
+ * where row m sits in x.
+ * ------------------------------------------------------------------------ */
+bi_status bi_matmul(const void *x, const void *w, void *y,
+                    int64_t M, int64_t N, int64_t K,
+                    int32_t dtype, int32_t w_transposed, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Group-quantized 4-bit matmul   y = x @ dequantize(W)^T
+ * Source: "Fix fp quantized matmul corruption when the quantized dim is not a
+ * multiple of 32", Problem (reference x @ dequantize(w).T; nvfp4 group size
+ * 16), Fix (bounded K remainder and N tail; loader masks); "Fix/speculative
+ * shape invariance", Problem (quantized matmul selected different paths by M).
+ *   x      : [M,K] binary16.
+ *   y      : [M,N] binary16.
+ *   Transposed weights (w_transposed != 0), quantized along K:
+ *     wq [N, K/8] uint32, scales [N, K/gs], biases [N, K/gs].
+ *   Natural weights (w_transposed == 0), quantized along N:
+ *     wq [K, N/8] uint32, scales [K, N/gs], biases [K, N/gs].
+ *   Packing: eight 4-bit codes per little-endian uint32; the element with the
+ *   lowest index along the quantized axis is in bits 0..3.
+ *   qmode BI_AFFINE: gs in {32, 64, 128}; binary16 scales s and biases b;
+ *     w = s*q + b (q in 0..15), evaluated in fp32 and rounded to binary16.
+ *   qmode BI_NVFP4: gs == 16; codes are e2m1 (sign in bit 3), scales are one
+ *     OCP e4m3fn byte per group; w = e2m1(q) * e4m3(s) (exact in binary16);
+ *     biases must be NULL.
+ *   bits must be 4.  The quantized dimension must be a multiple of gs
+ *   (BI_ERR_GROUP otherwise).  Any M >= 1 is legal, as is K % 32 == 16 at
+ *   gs 16 and N % 32 != 0 -- tails are bounded on loads and stores.
+ * ------------------------------------------------------------------------ */
+bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, const void *biases,
+                     void *y, int64_t M, int64_t N, int64_t K,
+                     int32_t qmode, int32_t bits, int32_t group_size, int32_t w_transposed,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * RMSNorm   y = (x * inv) * w,   inv = 1 / sqrt(sum_i x_i^2 / H + eps)
+ * Source: "Batch-invariant kernels ...", Case 4 (the sum-of-squares tree must
+ * not depend on the batch) and Case 6 (data-parallel, one row never split).
+ *   x, y : [rows, H] of `dtype`;  w : [H] of `dtype`.
+ *   rows >= 1, H >= 1, eps >= 0.
+ * ------------------------------------------------------------------------ */
+bi_status bi_rmsnorm(const void *x, const void *w, void *y, int64_t rows, int64_t H,
+                     float eps, int32_t dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode / verify scaled-dot-product attention (GQA), two passes.
+ * Source: "Fix/speculative shape invariance", Problem and Changes (the
+ * softmax reduction layout of a query must be the same alone or inside a
+ * short causal block); "Batch-invariant kernels ...", Case 6 (fixed split
+ * size with a varying number of splits; cache updated before the kernel).
+ *   q, o   : [B, Q, Hq, D] of `dtype` (BI_BF16 or BI_F16).
+ *   k, v   : [B, Lcap, Hkv, D] of `dtype` (the KV cache, already holding the
+ *            keys/values of the Q new tokens).
+ *   kv_len : device int32 [B]; sequence b holds kv_len[b] valid positions.
+ *            Query j of sequence b sits at position p = kv_len[b] - Q + j.
+ *            With causal != 0 it attends to keys 0..p, else to 0..kv_len[b]-1.
+ *            Requires Q <= kv_len[b] <= max_kv_len <= Lcap (not checked on the
+ *            host because kv_len lives on the device; positions beyond a
+ *            row's limit are never read).
+ *   Query head h reads key/value head h / (Hq / Hkv); Hq % Hkv == 0.
+ *   D must be 128 in this build.  scale is applied to q.k in fp32.
+ *   ws     : device workspace of at least bi_sdpa_workspace_bytes(...) bytes,
+ *            16-byte aligned; its contents on entry are ignored.
+ * Keys are processed in chunks of a constant size (bi_build_info reports it);
+ * the chunk a key falls in depends only on its position.  Each chunk's
+ * partial (max, sum, weighted values) is merged in ascending chunk order, and
+ * chunks past a query's last key are never merged.
+ * ------------------------------------------------------------------------ */
+size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int32_t Hq, int32_t D);
+
+bi_status bi_sdpa(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len,
+                  int64_t max_kv_len, int64_t B, int64_t Q, int64_t Lcap,
+                  int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t causal,
+                  int32_t dtype, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Pointwise glue of a Llama-style decoder.  Pointwise ops are batch-invariant
+ * by construction ("Batch-invariant kernels ...", Mental model).  All tensors
+ * are bf16 unless stated.
+ * ------------------------------------------------------------------------ */
+
+/* out[t, :] = table[ids[t], :];  ids: device int32 [T] (each in [0, V)),
+ * table [V, H], out [T, H].  Ids outside [0, V) produce a zero row. */
+bi_status bi_embed(const int32_t *ids, const void *table, void *out, int64_t T, int64_t V,
+                   int64_t H, hipStream_t stream);
+
+/* Rotary embedding (rotate-half pairs i, i + D/2) of the q and k parts of a
+ * fused projection, then the KV-cache write, in one launch.
+ *   qkv   : [B*Q, (Hq + 2*Hkv) * D]; row (b, j) holds q | k | v of token j of
+ *           sequence b.
+ *   q_out : [B*Q, Hq*D]   rotated q.
+ *   kc, vc: [B, Lcap, Hkv, D] caches; token j of sequence b is written at
+ *           position kv_len[b] - Q + j (rotated k, and v unchanged).
+ *   cos_t, sin_t: fp32 [max_pos, D/2] tables; positions must be < max_pos.
+ *   out_i = x_i * c_i - x_{i+D/2} * s_i;  out_{i+D/2} = x_{i+D/2} * c_i + x_i * s_i
+ *   (each product and the difference/sum rounded separately in fp32). */
+bi_status bi_rope_kv_write(const void *qkv, void *q_out, void *kc, void *vc,
+                           const int32_t *kv_len, const float *cos_t, const float *sin_t,
+                           int64_t B, int64_t Q, int64_t Lcap, int32_t Hq, int32_t Hkv,
+                           int32_t D, int64_t max_pos, hipStream_t stream);
+
+/* out[r, i] = silu(gu[r, i]) * gu[r, F + i],  silu(g) = g / (1 + exp(-g));
+ * gu [rows, 2F], out [rows, F]. */
+bi_status bi_silu_mul(const void *gu, void *out, int64_t rows, int64_t F, hipStream_t stream);
+
+/* out = a + b (fp32 add, RNE to bf16); n elements; out may alias a or b. */
+bi_status bi_add(const void *a, const void *b, void *out, int64_t n, hipStream_t stream);
+
+/* idx[r] = argmax_c x[r, c] over a bf16 [rows, cols] matrix; the lowest
+ * index wins ties; idx device int32 [rows]. */
+bi_status bi_argmax(const void *x, int32_t *idx, int64_t rows, int64_t cols, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Non-invariant comparison variants.  These reproduce the strategies the
+ * pages identify as the source of batch dependence -- split-K matmul with a
+ * cleanup reduction and an RMSNorm row split across workgroups -- so that
+ * the cost of invariance can be measured against the best of them.
+ * They are deterministic run to run for fixed arguments, but a caller that
+ * picks `splits` from the batch size gets batch-dependent bits.
+ * Source: "Batch-invariant kernels ...", Case 2 (split-k), Case 3, Case 4,
+ * Case 6 (Split-K / Split-KV); "Fix/speculative shape invariance", Problem.
+ * ------------------------------------------------------------------------ */
+size_t bi_matmul_split_workspace_bytes(int64_t M, int64_t N, int32_t splits);
+bi_status bi_matmul_split(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
+                          int32_t dtype, int32_t w_transposed, int32_t splits,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+size_t bi_rmsnorm_split_workspace_bytes(int64_t rows, int32_t splits);
+bi_status bi_rmsnorm_split(const void *x, const void *w, void *y, int64_t rows, int64_t H,
+                           float eps, int32_t dtype, int32_t splits,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Human-readable status name (static string, never NULL). */
+const char *bi_status_str(int32_t status);
+/* Static string naming the frozen reduction constants of this build (MFMA
+ * instructions, K slicing, attention chunk size, lane mappings). */
+const char *bi_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H */

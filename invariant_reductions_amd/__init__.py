@@ -1,0 +1,263 @@
+"""invariant_reductions_amd -- batch-invariant reductions for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/bi.h`` (``libbi.so``, built
+in-tree by ``invariant_reductions_amd.build``).  The binding only marshals
+arguments: it checks devices, dtypes and contiguity, passes raw device
+pointers and torch's current HIP stream, and raises :class:`BIError` on a
+non-OK status.  Every step of the computation runs in the HIP kernels; there
+is no CPU path.  If the library has not been built, every op raises.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BIError", "library_path", "lib", "build_info",
+    "matmul", "qmatmul", "rmsnorm", "sdpa", "sdpa_workspace_bytes",
+    "matmul_split", "rmsnorm_split",
+    "embed", "rope_kv_write", "silu_mul", "add", "argmax",
+    "BF16", "F16", "F32", "AFFINE", "NVFP4",
+]
+
+BF16, F16, F32 = 0, 1, 2
+AFFINE, NVFP4 = 0, 1
+_TORCH_DT = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libbi.so")
+
+
+class BIError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib_handle.bi_status_str(status).decode() if _lib_handle is not None else str(status)
+        super().__init__(f"{where}: {msg}")
+
+
+_lib_handle = None
+
+
+def lib():
+    """The loaded libbi.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"libbi.so not found at {path}; build it with "
+                               "`python -m invariant_reductions_amd.build`")
+        L = ctypes.CDLL(path)
+        P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        SZ = ctypes.c_size_t
+        sig = {
+            "bi_matmul": [P, P, P, I64, I64, I64, I32, I32, P],
+            "bi_qmatmul": [P, P, P, P, P, I64, I64, I64, I32, I32, I32, I32, P],
+            "bi_rmsnorm": [P, P, P, I64, I64, F, I32, P],
+            "bi_sdpa": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, P, SZ, P],
+            "bi_embed": [P, P, P, I64, I64, I64, P],
+            "bi_rope_kv_write": [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, I64, P],
+            "bi_silu_mul": [P, P, I64, I64, P],
+            "bi_add": [P, P, P, I64, P],
+            "bi_argmax": [P, P, I64, I64, P],
+            "bi_matmul_split": [P, P, P, I64, I64, I64, I32, I32, I32, P, SZ, P],
+            "bi_rmsnorm_split": [P, P, P, I64, I64, F, I32, I32, P, SZ, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int32
+        L.bi_sdpa_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
+        L.bi_sdpa_workspace_bytes.restype = SZ
+        L.bi_matmul_split_workspace_bytes.argtypes = [I64, I64, I32]
+        L.bi_matmul_split_workspace_bytes.restype = SZ
+        L.bi_rmsnorm_split_workspace_bytes.argtypes = [I64, I32]
+        L.bi_rmsnorm_split_workspace_bytes.restype = SZ
+        L.bi_status_str.argtypes = [I32]
+        L.bi_status_str.restype = ctypes.c_char_p
+        L.bi_build_info.argtypes = []
+        L.bi_build_info.restype = ctypes.c_char_p
+        _lib_handle = L
+    return _lib_handle
+
+
+def build_info() -> str:
+    return lib().bi_build_info().decode()
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("invariant_reductions_amd ops take GPU tensors only")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _dt(t) -> int:
+    if t.dtype not in _TORCH_DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _TORCH_DT[t.dtype]
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise BIError(rc, where)
+
+
+# ---------------------------------------------------------------------------
+# the four reductions
+# ---------------------------------------------------------------------------
+
+def matmul(x: torch.Tensor, w: torch.Tensor, transposed: bool = True, out=None, stream=None):
+    """y = x @ w.T (w [N,K], transposed=True) or x @ w (w [K,N])."""
+    _dev(x, w, out)
+    M, K = x.shape
+    N = w.shape[0] if transposed else w.shape[1]
+    if (w.shape[1] if transposed else w.shape[0]) != K or w.dtype != x.dtype:
+        raise ValueError("matmul: shape/dtype mismatch")
+    y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(lib().bi_matmul(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dt(x), int(transposed), _stream(stream)),
+           "bi_matmul")
+    return y
+
+
+def matmul_split(x, w, splits: int, transposed: bool = True, out=None, ws=None, stream=None):
+    """Non-invariant split-K comparison variant (see include/bi.h)."""
+    _dev(x, w, out, ws)
+    M, K = x.shape
+    N = w.shape[0] if transposed else w.shape[1]
+    y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+    need = lib().bi_matmul_split_workspace_bytes(M, N, splits)
+    if ws is None and splits > 1:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().bi_matmul_split(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dt(x), int(transposed), splits,
+                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "bi_matmul_split")
+    return y
+
+
+def qmatmul(x, wq, scales, biases, N: int, K: int, qmode: int, group_size: int, transposed: bool = True,
+            out=None, stream=None):
+    """y = x @ dequantize(W)^T; x float16 [M,K]; wq int32 (uint32 bit patterns)."""
+    _dev(x, wq, scales, biases, out)
+    if x.dtype != torch.float16:
+        raise ValueError("qmatmul: x must be float16")
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("qmatmul: x shape")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _check(lib().bi_qmatmul(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, qmode, 4,
+                            group_size, int(transposed), _stream(stream)), "bi_qmatmul")
+    return y
+
+
+def rmsnorm(x, w, eps: float = 1e-6, out=None, stream=None):
+    _dev(x, w, out)
+    rows, H = x.shape
+    y = out if out is not None else torch.empty_like(x)
+    _check(lib().bi_rmsnorm(_ptr(x), _ptr(w), _ptr(y), rows, H, eps, _dt(x), _stream(stream)), "bi_rmsnorm")
+    return y
+
+
+def rmsnorm_split(x, w, splits: int, eps: float = 1e-6, out=None, ws=None, stream=None):
+    _dev(x, w, out, ws)
+    rows, H = x.shape
+    y = out if out is not None else torch.empty_like(x)
+    need = lib().bi_rmsnorm_split_workspace_bytes(rows, splits)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().bi_rmsnorm_split(_ptr(x), _ptr(w), _ptr(y), rows, H, eps, _dt(x), splits, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)), "bi_rmsnorm_split")
+    return y
+
+
+def sdpa_workspace_bytes(B: int, Q: int, max_kv_len: int, Hq: int, D: int) -> int:
+    return lib().bi_sdpa_workspace_bytes(B, Q, max_kv_len, Hq, D)
+
+
+def sdpa(q, k, v, kv_len, max_kv_len: int, scale: float, causal: bool = True, out=None, ws=None, stream=None):
+    """q [B,Q,Hq,D]; k, v [B,Lcap,Hkv,D]; kv_len int32 [B] on the device."""
+    _dev(q, k, v, kv_len, out, ws)
+    B, Q, Hq, D = q.shape
+    _, Lcap, Hkv, _ = k.shape
+    if kv_len.dtype != torch.int32:
+        raise ValueError("kv_len must be int32")
+    o = out if out is not None else torch.empty_like(q)
+    need = sdpa_workspace_bytes(B, Q, max_kv_len, Hq, D)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().bi_sdpa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_len), max_kv_len, B, Q, Lcap, Hq, Hkv, D,
+                         scale, int(causal), _dt(q), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "bi_sdpa")
+    return o
+
+
+# ---------------------------------------------------------------------------
+# decoder glue
+# ---------------------------------------------------------------------------
+
+def embed(ids, table, out=None, stream=None):
+    _dev(ids, table, out)
+    T = ids.numel()
+    V, H = table.shape
+    y = out if out is not None else torch.empty((T, H), dtype=table.dtype, device=table.device)
+    _check(lib().bi_embed(_ptr(ids), _ptr(table), _ptr(y), T, V, H, _stream(stream)), "bi_embed")
+    return y
+
+
+def rope_kv_write(qkv, q_out, kc, vc, kv_len, cos_t, sin_t, B: int, Q: int, Hq: int, Hkv: int, D: int, stream=None):
+    _dev(qkv, q_out, kc, vc, kv_len, cos_t, sin_t)
+    Lcap = kc.shape[1]
+    _check(lib().bi_rope_kv_write(_ptr(qkv), _ptr(q_out), _ptr(kc), _ptr(vc), _ptr(kv_len), _ptr(cos_t),
+                                  _ptr(sin_t), B, Q, Lcap, Hq, Hkv, D, cos_t.shape[0], _stream(stream)),
+           "bi_rope_kv_write")
+
+
+def silu_mul(gu, out=None, stream=None):
+    _dev(gu, out)
+    rows, F2 = gu.shape
+    y = out if out is not None else torch.empty((rows, F2 // 2), dtype=gu.dtype, device=gu.device)
+    _check(lib().bi_silu_mul(_ptr(gu), _ptr(y), rows, F2 // 2, _stream(stream)), "bi_silu_mul")
+    return y
+
+
+def add(a, b, out=None, stream=None):
+    _dev(a, b, out)
+    y = out if out is not None else torch.empty_like(a)
+    _check(lib().bi_add(_ptr(a), _ptr(b), _ptr(y), a.numel(), _stream(stream)), "bi_add")
+    return y
+
+
+def argmax(x, out=None, stream=None):
+    _dev(x, out)
+    rows, cols = x.shape
+    y = out if out is not None else torch.empty(rows, dtype=torch.int32, device=x.device)
+    _check(lib().bi_argmax(_ptr(x), _ptr(y), rows, cols, _stream(stream)), "bi_argmax")
+    return y

@@ -1,0 +1,83 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libbi.
+//
+// Everything here is HIP for CDNA4 (wave64, MFMA).  No host fallback exists:
+// the library is built for gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bi.h"
+
+namespace bi {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------
+struct BF16 {
+    using store_t = uint16_t;
+    static constexpr int kElemsPer16B = 8;
+    __device__ static inline float widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+    __device__ static inline uint16_t narrow(float f) {
+        __bf16 h = (__bf16)f;                       // v_cvt_pk_bf16_f32: round to nearest even
+        return __builtin_bit_cast(uint16_t, h);
+    }
+};
+struct F16 {
+    using store_t = uint16_t;
+    static constexpr int kElemsPer16B = 8;
+    __device__ static inline float widen(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+    __device__ static inline uint16_t narrow(float f) {
+        _Float16 h = (_Float16)f;                   // v_cvt_f16_f32: round to nearest even
+        return __builtin_bit_cast(uint16_t, h);
+    }
+};
+struct F32 {
+    using store_t = float;
+    static constexpr int kElemsPer16B = 4;
+    __device__ static inline float widen(float b) { return b; }
+    __device__ static inline float narrow(float f) { return f; }
+};
+
+// ---------------------------------------------------------------------------
+// bounded 16-byte chunk loads
+// ---------------------------------------------------------------------------
+// Loads elements [k, k + E) of a row (E = 16 bytes worth of elements), with
+// every element at index >= limit, or the whole chunk when !ok, read as zero.
+// VEC: the caller guarantees that a chunk is either entirely below `limit` or
+// entirely at/above it and that the address is 16-byte aligned.
+template <typename S, bool VEC>
+__device__ inline uint4 load_chunk(const typename S::store_t *row, int64_t k, int64_t limit, bool ok)
+{
+    constexpr int E = S::kElemsPer16B;
+    uint4 r = make_uint4(0, 0, 0, 0);
+    if (VEC) {
+        if (ok && k < limit) r = *reinterpret_cast<const uint4 *>(row + k);
+    } else {
+        typename S::store_t tmp[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) tmp[e] = (ok && k + e < limit) ? row[k + e] : (typename S::store_t)0;
+        r = __builtin_bit_cast(uint4, tmp);
+    }
+    return r;
+}
+
+__device__ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline bool host_aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline bi_status launch_status()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? BI_OK : BI_ERR_LAUNCH;
+}
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace bi

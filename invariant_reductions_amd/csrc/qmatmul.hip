@@ -1,0 +1,282 @@
+// qmatmul.hip -- batch-invariant 4-bit group-quantized matmul on gfx950.
+//
+// Sources: "Fix fp quantized matmul corruption when the quantized dim is not a
+// multiple of 32" (Problem: the reference is x @ dequantize(w).T and nvfp4's
+// group size 16 makes K % 32 == 16 legal; The three defects and Fix: the K loop
+// must stop at K, the N tail must be bounded on loads and stores, and masks
+// must test rows against rows and columns against columns); "Fix/speculative
+// shape invariance" (Problem: quantized matmul picked its path from M).
+//
+// What is computed: W is dequantized in registers to binary16 --
+//   affine: w = RNE16(fma(s, q, b)) with binary16 s, b (the product s*q is
+//           exact in fp32, so the fma rounds once, exactly like mul-then-add);
+//   nvfp4 : w = e2m1(q) * e4m3(s), exact in fp32 and in binary16 --
+// and multiplied against binary16 x by the same MFMA tree as the dense
+// kernel: K blocks of 128, block b owned by wave b mod 8, lane group g
+// supplying elements [32g, 32g + 32) of a block as four v_mfma_f32_16x16x32_f16
+// steps, wave partials added in order 0..7, RNE to binary16.  The tree depends
+// on K only; M, the M-tile a row falls in and the N-tile width are free.
+//
+// Bounds: a block that runs past K reads no packed word, scale or bias at or
+// beyond K and feeds exact zeros to the MFMA; a column n >= N reads nothing and
+// stores nothing.  The K % 32 == 16 shape (nvfp4) takes the word-granular path.
+#include "common.hpp"
+
+namespace bi {
+
+constexpr int kQWaves = 8;          // frozen: same K slicing as the dense kernel
+constexpr int kQBlock = 128;
+
+__device__ inline f32x4 qmfma(uint4 a, uint4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// e4m3fn byte -> fp32 (exact); S.1111.111 -> NaN.
+__device__ inline float e4m3_to_f32(uint32_t s)
+{
+    const uint32_t sign = (s & 0x80u) << 24, e = (s >> 3) & 0xfu, m = s & 7u;
+    if (e == 0xfu && m == 7u) return __uint_as_float(0x7fc00000u);
+    if (e == 0) return __uint_as_float(sign) + (float)m * 0x1p-9f;   // subnormal m/8 * 2^-6 (exact)
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// e2m1 nibble -> fp32 (exact): magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6, sign in bit 3.
+__device__ inline float e2m1_to_f32(uint32_t c)
+{
+    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    const uint32_t mag = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3f000000u : 0u);
+    return __uint_as_float(((c & 8u) << 28) | mag);
+}
+
+template <int QM>
+struct QGroup {                      // per-group dequantization constants
+    float s, b;
+};
+
+template <int QM>
+__device__ inline QGroup<QM> load_group(const void *scales, const uint16_t *biases, int64_t gi)
+{
+    QGroup<QM> g;
+    if (QM == BI_AFFINE) {
+        g.s = F16::widen(((const uint16_t *)scales)[gi]);
+        g.b = F16::widen(biases[gi]);
+    } else {
+        g.s = e4m3_to_f32(((const uint8_t *)scales)[gi]);
+        g.b = 0.0f;
+    }
+    return g;
+}
+
+template <int QM>
+__device__ inline uint16_t deq1(uint32_t q, const QGroup<QM> &g)
+{
+    float v;
+    if (QM == BI_AFFINE) v = __builtin_fmaf(g.s, (float)q, g.b);
+    else v = e2m1_to_f32(q) * g.s;
+    return F16::narrow(v);
+}
+
+// Eight codes of one word -> one 16-byte MFMA operand chunk (element e = nibble e).
+template <int QM>
+__device__ inline uint4 deq_word(uint32_t w, const QGroup<QM> &g)
+{
+    uint16_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = deq1<QM>((w >> (4 * e)) & 15u, g);
+    return __builtin_bit_cast(uint4, h);
+}
+
+// Transposed weights [N, K/8]: lane (g, c) of block b supplies the 32 codes of
+// row n at k in [b*128 + 32g, +32) -- four consecutive words.
+template <int QM, int GS, bool WVEC>
+__device__ inline void qload_trans(uint4 *dst, const uint32_t *wq, const void *scales, const uint16_t *biases,
+                                   int64_t n, bool nok, int64_t K, int64_t kbase)
+{
+    const int64_t words = K / 8, groups = K / GS;
+    uint32_t w[4];
+    if (WVEC) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (nok && kbase < K) v = *reinterpret_cast<const uint4 *>(wq + n * words + kbase / 8);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int64_t k = kbase + s * 8;
+            w[s] = (nok && k < K) ? wq[n * words + k / 8] : 0u;
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int64_t k = kbase + s * 8;
+        if (nok && k < K) {
+            const QGroup<QM> gr = load_group<QM>(scales, biases, n * groups + k / GS);
+            dst[s] = deq_word<QM>(w[s], gr);
+        } else {
+            dst[s] = make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+// Natural weights [K, N/8] quantized along N: column n's code at row k sits in
+// word (k, n/8), nibble n % 8.
+template <int QM, int GS>
+__device__ inline void qload_nat(uint4 *dst, const uint32_t *wq, const void *scales, const uint16_t *biases,
+                                 int64_t n, bool nok, int64_t N, int64_t K, int64_t kbase)
+{
+    const int64_t words = N / 8, groups = N / GS;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        uint16_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = kbase + s * 8 + e;
+            if (nok && k < K) {
+                const uint32_t q = (wq[k * words + n / 8] >> (4 * (n % 8))) & 15u;
+                const QGroup<QM> gr = load_group<QM>(scales, biases, k * groups + n / GS);
+                h[e] = deq1<QM>(q, gr);
+            } else {
+                h[e] = 0;
+            }
+        }
+        dst[s] = __builtin_bit_cast(uint4, h);
+    }
+}
+
+template <int QM, int GS, bool TRANS, bool WVEC, int MT, int NS>
+__global__ __launch_bounds__(kQWaves * kWave)
+void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wq, const void *__restrict__ scales,
+                    const uint16_t *__restrict__ biases, uint16_t *__restrict__ y, int64_t M, int64_t N, int64_t K)
+{
+    constexpr int P = kQWaves;
+    constexpr int TR = MT * 16, TC = NS * 16;
+    __shared__ float red[P][TR][TC + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * TC;
+    const int64_t m0 = (int64_t)blockIdx.y * TR;
+    const int64_t nblocks = cdiv(K, kQBlock);
+    const bool xvec = (K % 8) == 0;                 // x rows 16-byte aligned: chunks never straddle K
+
+    f32x4 acc[MT][NS];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const uint16_t *xrow[MT];
+    bool xok[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int64_t r = m0 + i * 16 + c;
+        xok[i] = r < M;
+        xrow[i] = x + (xok[i] ? r : 0) * K;
+    }
+    int64_t wn[NS];
+    bool wok[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int64_t n = n0 + j * 16 + c;
+        wok[j] = n < N;
+        wn[j] = wok[j] ? n : 0;
+    }
+
+    for (int64_t b = wave; b < nblocks; b += P) {
+        const int64_t kbase = b * kQBlock + (int64_t)g * 32;
+        uint4 A[MT][4], Bf[NS][4];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            if (TRANS) qload_trans<QM, GS, WVEC>(Bf[j], wq, scales, biases, wn[j], wok[j], K, kbase);
+            else qload_nat<QM, GS>(Bf[j], wq, scales, biases, wn[j], wok[j], N, K, kbase);
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                A[i][s] = xvec ? load_chunk<F16, true>(xrow[i], kbase + s * 8, K, xok[i])
+                               : load_chunk<F16, false>(xrow[i], kbase + s * 8, K, xok[i]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NS; ++j) acc[i][j] = qmfma(A[i][s], Bf[j][s], acc[i][j]);
+    }
+
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][i * 16 + g * 4 + r][j * 16 + c] = acc[i][j][r];
+    __syncthreads();
+    for (int o = threadIdx.x; o < TR * TC; o += P * kWave) {
+        const int r = o / TC, cc = o % TC;
+        const int64_t row = m0 + r, col = n0 + cc;
+        if (row >= M || col >= N) continue;
+        float v = red[0][r][cc];
+#pragma unroll
+        for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+        y[row * N + col] = F16::narrow(v);
+    }
+}
+
+template <int QM, int GS, bool TRANS, bool WVEC, int MT>
+static void launch_q_t(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
+                       int64_t N, int64_t K, hipStream_t st)
+{
+    dim3 grid((unsigned)cdiv(N, 16), (unsigned)cdiv(M, MT * 16));
+    hipLaunchKernelGGL((qmatmul_kernel<QM, GS, TRANS, WVEC, MT, 1>), grid, dim3(kQWaves * kWave), 0, st,
+                       (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, M, N, K);
+}
+
+template <int QM, int GS, bool TRANS, bool WVEC>
+static void launch_q_mt(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
+                        int64_t N, int64_t K, hipStream_t st)
+{
+    const int64_t mt = cdiv(M, 16);
+    if (mt <= 1) launch_q_t<QM, GS, TRANS, WVEC, 1>(x, wq, s, b, y, M, N, K, st);
+    else if (mt <= 2) launch_q_t<QM, GS, TRANS, WVEC, 2>(x, wq, s, b, y, M, N, K, st);
+    else launch_q_t<QM, GS, TRANS, WVEC, 4>(x, wq, s, b, y, M, N, K, st);
+}
+
+template <int QM, int GS>
+static void launch_q(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M, int64_t N,
+                     int64_t K, bool trans, hipStream_t st)
+{
+    if (!trans) launch_q_mt<QM, GS, false, false>(x, wq, s, b, y, M, N, K, st);
+    else if (K % 32 == 0) launch_q_mt<QM, GS, true, true>(x, wq, s, b, y, M, N, K, st);
+    else launch_q_mt<QM, GS, true, false>(x, wq, s, b, y, M, N, K, st);
+}
+
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, const void *biases, void *y,
+                                int64_t M, int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size,
+                                int32_t w_transposed, hipStream_t stream)
+{
+    if (!x || !wq || !scales || !y) return BI_ERR_NULL;
+    if (M < 1 || N < 1 || K < 1 || M > (1ll << 31) || N > (1ll << 31) || K > (1ll << 31)) return BI_ERR_SHAPE;
+    if (bits != 4) return BI_ERR_GROUP;
+    if (qmode == BI_AFFINE) {
+        if (group_size != 32 && group_size != 64 && group_size != 128) return BI_ERR_GROUP;
+        if (!biases) return BI_ERR_NULL;
+    } else if (qmode == BI_NVFP4) {
+        if (group_size != 16) return BI_ERR_GROUP;
+        if (biases) return BI_ERR_GROUP;
+    } else {
+        return BI_ERR_GROUP;
+    }
+    const int64_t qdim = w_transposed ? K : N;
+    if (qdim % group_size) return BI_ERR_GROUP;
+    if (!host_aligned16(x) || !host_aligned16(wq) || !host_aligned16(y)) return BI_ERR_ALIGN;
+    (void)hipGetLastError();
+    const bool t = w_transposed != 0;
+    if (qmode == BI_NVFP4) launch_q<BI_NVFP4, 16>(x, wq, scales, biases, y, M, N, K, t, stream);
+    else if (group_size == 32) launch_q<BI_AFFINE, 32>(x, wq, scales, biases, y, M, N, K, t, stream);
+    else if (group_size == 64) launch_q<BI_AFFINE, 64>(x, wq, scales, biases, y, M, N, K, t, stream);
+    else launch_q<BI_AFFINE, 128>(x, wq, scales, biases, y, M, N, K, t, stream);
+    return launch_status();
+}

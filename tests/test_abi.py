@@ -1,0 +1,128 @@
+"""The C-ABI library loads on the host, exports every entry point its header
+declares, and rejects bad arguments with the documented status codes before
+touching the GPU (no test here launches anything)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_reductions_amd as bi
+from conftest import ROOT
+
+HDR = os.path.join(ROOT, "include", "bi.h")
+
+P = ctypes.c_void_p
+A = P(0x10000)          # 16-byte aligned, never dereferenced: every call below fails validation first
+ODD = P(0x10008)        # 8-byte aligned only
+
+OK, NULL, SHAPE, DTYPE, GROUP, ALIGN, WORKSPACE, LAUNCH, UNSUP = range(9)
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_builds_into_the_package():
+    assert os.path.exists(bi.library_path()), "run `python -m invariant_reductions_amd.build` first"
+
+
+def test_every_declared_symbol_is_exported():
+    L = bi.lib()
+    names = declared_functions()
+    assert "bi_matmul" in names and "bi_qmatmul" in names and "bi_rmsnorm" in names and "bi_sdpa" in names
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_build_info():
+    L = bi.lib()
+    for s in range(9):
+        assert L.bi_status_str(s)
+    assert b"unknown" in L.bi_status_str(99)
+    info = bi.build_info()
+    assert "gfx950" in info and "256 keys" in info
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, A, A, 4, 512, 4096, 0, 1), NULL),
+    ((A, None, A, 4, 512, 4096, 0, 1), NULL),
+    ((A, A, A, 0, 512, 4096, 0, 1), SHAPE),
+    ((A, A, A, 4, -1, 4096, 0, 1), SHAPE),
+    ((A, A, A, 4, 512, 0, 0, 1), SHAPE),
+    ((A, A, A, 4, 512, 4096, 7, 1), DTYPE),
+    ((ODD, A, A, 4, 512, 4096, 0, 1), ALIGN),
+    ((A, A, ODD, 4, 512, 4096, 0, 1), ALIGN),
+])
+def test_matmul_validation(args, code):
+    assert bi.lib().bi_matmul(*args, None) == code
+
+
+@pytest.mark.parametrize("M,N,K,qmode,bits,gs,trans,biases,code", [
+    (1, 512, 4096, 0, 3, 32, 1, A, GROUP),          # bits must be 4
+    (1, 512, 4096, 0, 4, 48, 1, A, GROUP),          # illegal affine group size
+    (1, 512, 4096, 0, 4, 16, 1, A, GROUP),          # 16 is nvfp4 only
+    (1, 512, 4096, 1, 4, 32, 1, None, GROUP),       # nvfp4 needs gs 16
+    (1, 512, 4096, 1, 4, 16, 1, A, GROUP),          # nvfp4 takes no biases
+    (1, 512, 4096, 0, 4, 32, 1, None, NULL),        # affine needs biases
+    (50, 128, 1040, 0, 4, 32, 1, A, GROUP),         # affine K % gs != 0 (transposed)
+    (64, 100, 32768, 0, 4, 32, 0, A, GROUP),        # natural layout quantizes N: 100 % 32 != 0
+    (1, 512, 4096, 2, 4, 32, 1, A, GROUP),          # unknown mode
+    (0, 512, 4096, 0, 4, 32, 1, A, SHAPE),
+])
+def test_qmatmul_validation(M, N, K, qmode, bits, gs, trans, biases, code):
+    assert bi.lib().bi_qmatmul(A, A, A, biases, A, M, N, K, qmode, bits, gs, trans, None) == code
+
+
+def test_rmsnorm_validation():
+    L = bi.lib()
+    assert L.bi_rmsnorm(None, A, A, 4, 4096, 1e-6, 0, None) == NULL
+    assert L.bi_rmsnorm(A, A, A, 0, 4096, 1e-6, 0, None) == SHAPE
+    assert L.bi_rmsnorm(A, A, A, 4, 0, 1e-6, 0, None) == SHAPE
+    assert L.bi_rmsnorm(A, A, A, 4, 4096, -1.0, 0, None) == SHAPE
+    assert L.bi_rmsnorm(A, A, A, 4, 4096, float("nan"), 0, None) == SHAPE
+    assert L.bi_rmsnorm(A, A, A, 4, 4096, 1e-6, 5, None) == DTYPE
+    assert L.bi_rmsnorm(A, ODD, A, 4, 4096, 1e-6, 0, None) == ALIGN
+
+
+def test_sdpa_validation_and_workspace_size():
+    L = bi.lib()
+    ws_need = L.bi_sdpa_workspace_bytes(1, 8, 65540, 32, 128)
+    assert ws_need == 1 * 8 * 32 * 257 * 132 * 4
+    assert L.bi_sdpa_workspace_bytes(1, 8, 65540, 32, 64) == 0
+    def call(**kw):
+        a = dict(q=A, k=A, v=A, o=A, kv=A, maxkv=1028, B=1, Q=8, Lcap=2048, Hq=32, Hkv=8, D=128,
+                 scale=0.088, causal=1, dt=0, ws=A, wsb=10 ** 9)
+        a.update(kw)
+        return L.bi_sdpa(a["q"], a["k"], a["v"], a["o"], a["kv"], a["maxkv"], a["B"], a["Q"], a["Lcap"],
+                         a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["dt"], a["ws"], a["wsb"], None)
+    assert call(kv=None) == NULL
+    assert call(Hkv=5) == SHAPE
+    assert call(maxkv=4) == SHAPE                   # max_kv_len < Q
+    assert call(maxkv=4096) == SHAPE                # max_kv_len > Lcap
+    assert call(D=64) == UNSUP
+    assert call(dt=2) == DTYPE
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=100) == WORKSPACE
+    assert call(q=ODD) == ALIGN
+
+
+def test_split_variant_validation():
+    L = bi.lib()
+    assert L.bi_matmul_split(A, A, A, 4, 512, 4096, 0, 1, 0, A, 10 ** 9, None) == SHAPE
+    assert L.bi_matmul_split(A, A, A, 4, 512, 4096, 0, 1, 4, None, 0, None) == WORKSPACE
+    assert L.bi_matmul_split(A, A, A, 4, 512, 4096, 0, 1, 4, A, 16, None) == WORKSPACE
+    assert L.bi_rmsnorm_split(A, A, A, 4, 4096, 1e-6, 0, 4, None, 0, None) == WORKSPACE
+    assert L.bi_matmul_split_workspace_bytes(4, 512, 8) == 4 * 512 * 8 * 4
+
+
+def test_glue_validation():
+    L = bi.lib()
+    assert L.bi_embed(None, A, A, 1, 10, 64, None) == NULL
+    assert L.bi_embed(A, A, A, 1, 10, 12, None) == SHAPE
+    assert L.bi_rope_kv_write(A, A, A, A, A, A, A, 1, 1, 16, 4, 2, 7, 16, None) == SHAPE
+    assert L.bi_silu_mul(A, None, 4, 8, None) == NULL
+    assert L.bi_add(A, A, ODD, 8, None) == ALIGN
+    assert L.bi_argmax(A, A, 0, 8, None) == SHAPE

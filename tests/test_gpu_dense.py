@@ -1,0 +1,150 @@
+"""Dense matmul on the GPU: parity with the oracle and bitwise batch invariance.
+
+Workload: W [N=512, K=4096] ~ N(0,1)*0.02, x [M,4096] ~ N(0,1), seed 0, both
+weight layouts, bf16 / f16 / f32 -- the dense-matmul case of
+"Fix/speculative shape invariance" (Problem; Changes; the reviewer's dense
+M=4 check in f16 and f32)."""
+import numpy as np
+import pytest
+import torch
+
+import invariant_reductions_amd as bi
+import oracle
+from gpu_util import Guarded, TOL, assert_parity, bits_equal, dev, to_dev, to_np
+from invariant_reductions_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def run(x, w, dtype, transposed):
+    return to_np(bi.matmul(to_dev(x, dtype), to_dev(w, dtype), transposed))
+
+
+@pytest.mark.parametrize("dtype", inputs.DTYPES)
+@pytest.mark.parametrize("transposed", [True, False])
+def test_config_rows_match_m1_and_oracle(dtype, transposed):
+    x, wt, wn = inputs.dense_case(4, 512, 4096, dtype, seed=0)
+    w = wt if transposed else wn
+    ref = oracle.matmul(x, w, dtype, transposed)
+    alone = [run(x[i:i + 1], w, dtype, transposed) for i in range(4)]
+    for M in (1, 2, 3, 4):
+        y = run(x[:M], w, dtype, transposed)
+        assert_parity(y, ref[:M], dtype, f"M={M}")
+        for i in range(M):
+            assert bits_equal(y[i:i + 1], alone[i]), f"row {i} of M={M} differs from its M=1 result"
+
+
+@pytest.mark.parametrize("dtype", inputs.DTYPES)
+def test_layouts_share_one_tree(dtype):
+    x, wt, wn = inputs.dense_case(8, 512, 4096, dtype, seed=1)
+    assert bits_equal(run(x, wt, dtype, True), run(x, wn, dtype, False))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_every_m_from_1_to_64_and_beyond(dtype):
+    """Rows are bit-identical for every M in 1..64 (the metric's range) and at
+    prefill-sized M, at every position of the batch."""
+    Mmax = 300
+    x, wt, _ = inputs.dense_case(Mmax, 512, 4096, dtype, seed=2)
+    xd, wd = to_dev(x, dtype), to_dev(wt, dtype)
+    full = to_np(bi.matmul(xd, wd))
+    ref = oracle.matmul(x[:64], wt, dtype, True)
+    assert_parity(full[:64], ref, dtype)
+    for M in list(range(1, 65)) + [65, 100, 257, 300]:
+        y = to_np(bi.matmul(xd[:M].contiguous(), wd))
+        assert bits_equal(y, full[:M]), f"M={M}"
+    # the same rows at other offsets of the batch
+    for off in (1, 5, 17, 63):
+        y = to_np(bi.matmul(xd[off:off + 40].contiguous(), wd))
+        assert bits_equal(y, full[off:off + 40]), f"offset {off}"
+
+
+def test_batch_position_permutation():
+    x, wt, _ = inputs.dense_case(48, 512, 4096, "bf16", seed=3)
+    xd, wd = to_dev(x, "bf16"), to_dev(wt, "bf16")
+    base = to_np(bi.matmul(xd, wd))
+    perm = torch.randperm(48, generator=torch.Generator().manual_seed(0)).to(xd.device)
+    y = to_np(bi.matmul(xd[perm].contiguous(), wd))
+    assert bits_equal(y, base[perm.cpu().numpy()])
+
+
+def test_mfma_row_independence():
+    """Row 0 fixed, the other 15 rows of its MFMA tile redrawn: row 0 keeps its bits."""
+    rng = np.random.default_rng(4)
+    x, wt, _ = inputs.dense_case(16, 1024, 4096, "bf16", seed=4)
+    wd = to_dev(wt, "bf16")
+    first = to_np(bi.matmul(to_dev(x, "bf16"), wd))[0]
+    for _ in range(5):
+        x2 = x.copy()
+        x2[1:] = inputs.normal(rng, (15, 4096), float(rng.uniform(0.1, 100)))
+        assert bits_equal(to_np(bi.matmul(to_dev(x2, "bf16"), wd))[0], first)
+
+
+@pytest.mark.parametrize("dtype", inputs.DTYPES)
+@pytest.mark.parametrize("transposed", [True, False])
+def test_integer_inputs_bit_exact_vs_oracle(dtype, transposed):
+    """Integer-valued inputs: every partial sum is exact, so the GPU's tree and
+    the oracle's sequential fold give the same fp32 value and the same RNE bits."""
+    rng = np.random.default_rng(5)
+    M, N, K = 37, 200, 4096
+    x = inputs.integer_values(rng, (M, K), -4, 4, dtype)
+    w = inputs.integer_values(rng, (N, K), -4, 4, dtype)
+    wl = w if transposed else np.ascontiguousarray(w.T)
+    ref = oracle.round_to(oracle.matmul(x, wl, dtype, transposed), dtype)
+    assert bits_equal(run(x, wl, dtype, transposed), ref)
+
+
+@pytest.mark.parametrize("dtype", inputs.DTYPES)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 17, 7), (5, 100, 100), (33, 45, 1040), (2, 64, 4100),
+                                   (17, 3, 129), (65, 130, 250), (80, 4096, 256), (1, 6144, 4096)])
+@pytest.mark.parametrize("transposed", [True, False])
+def test_ragged_shapes(dtype, M, N, K, transposed):
+    x, wt, wn = inputs.dense_case(M, N, K, dtype, seed=M + N + K)
+    w = wt if transposed else wn
+    ref = oracle.matmul(x, w, dtype, transposed)
+    y = run(x, w, dtype, transposed)
+    assert_parity(y, ref, dtype, f"{M}x{N}x{K}")
+    if M > 1:
+        assert bits_equal(run(x[-1:], w, dtype, transposed), y[-1:])
+
+
+@pytest.mark.parametrize("K", [4096, 1040, 999])
+def test_bounded_loads_and_stores(K):
+    """Inputs followed by NaN poison, output surrounded by canaries: an
+    over-read turns results into NaN, an over-write breaks a canary."""
+    M, N = 19, 100
+    x, wt, _ = inputs.dense_case(M, N, K, "bf16", seed=7)
+    xg = Guarded((M, K), torch.bfloat16, poison=0xFF, init=to_dev(x, "bf16"))
+    wg = Guarded((N, K), torch.bfloat16, poison=0xFF, init=to_dev(wt, "bf16"))
+    yg = Guarded((M, N), torch.bfloat16, poison=0xA5)
+    bi.matmul(xg.view, wg.view, True, out=yg.view)
+    torch.cuda.synchronize()
+    assert yg.canaries_intact()
+    assert_parity(to_np(yg.view), oracle.matmul(x, wt, "bf16", True), "bf16")
+
+
+def test_run_to_run_determinism():
+    x, wt, _ = inputs.dense_case(50, 512, 4096, "bf16", seed=8)
+    xd, wd = to_dev(x, "bf16"), to_dev(wt, "bf16")
+    first = bi.matmul(xd, wd)
+    for _ in range(50):
+        assert torch.equal(bi.matmul(xd, wd).view(torch.int16), first.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_variant_is_correct_but_not_invariant(dtype):
+    """Negative control: split-K with a cleanup reduction computes the same
+    product within tolerance but changes bits -- so the invariance tests above
+    can tell a split tree from the invariant one."""
+    x, wt, _ = inputs.dense_case(4, 512, 4096, dtype, seed=0)
+    xd, wd = to_dev(x, dtype), to_dev(wt, dtype)
+    inv = to_np(bi.matmul(xd, wd))
+    ref = oracle.matmul(x, wt, dtype, True)
+    differs = 0
+    for s in (2, 3, 4, 8, 16):
+        y = to_np(bi.matmul_split(xd, wd, s))
+        assert_parity(y, ref, dtype, f"splits={s}")
+        differs += int(not bits_equal(y, inv))
+    assert differs > 0
+    # split 1 is the invariant kernel itself
+    assert bits_equal(to_np(bi.matmul_split(xd, wd, 1)), inv)

@@ -1,0 +1,145 @@
+"""Decode / verify attention on the GPU: parity with the oracle and bitwise
+identity between a lone query and the same query inside a causal verify block.
+
+Workload: GQA with 32 query heads, 8 KV heads, head_dim 128; K, V, q ~ N(0,1)
+bf16; key lengths Lk in {1028, 8196, 16388, 65540}; scale 1/sqrt(128); a query
+block of 1 token or a causal block of 8 tokens at the end of the context --
+the SDPA check of "Fix/speculative shape invariance" (Changes; the reviewer's
+SDPA scenario)."""
+import numpy as np
+import pytest
+import torch
+
+import invariant_reductions_amd as bi
+import oracle
+from gpu_util import Guarded, assert_parity, bits_equal, dev, to_dev, to_np
+from invariant_reductions_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+HQ, HKV, D = 32, 8, 128
+SCALE = 1.0 / np.sqrt(128.0)
+
+
+def run(q, k, v, kv_len, causal=True, dtype="bf16", max_kv=None):
+    kvd = torch.tensor(np.asarray(kv_len, np.int32), device=dev())
+    mk = int(max(kv_len)) if max_kv is None else max_kv
+    return to_np(bi.sdpa(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), kvd, mk, SCALE, causal))
+
+
+@pytest.mark.parametrize("Lk", [1028, 8196, 16388, 65540])
+def test_config_lone_query_equals_verify_block(Lk):
+    q8, k, v = inputs.sdpa_case(1, 8, Lk, HQ, HKV, D, seed=0)
+    kd, vd = to_dev(k, "bf16"), to_dev(v, "bf16")
+    blk = to_np(bi.sdpa(to_dev(q8, "bf16"), kd, vd, torch.tensor([Lk], dtype=torch.int32, device=dev()),
+                        Lk, SCALE, True))
+    ref = oracle.sdpa(q8, k, v, np.array([Lk], np.int32), SCALE, True, "bf16")
+    assert_parity(blk, ref, "bf16", f"Lk={Lk} Q=8")
+    for j in range(8):
+        L = Lk - 8 + j + 1
+        one = to_np(bi.sdpa(to_dev(np.ascontiguousarray(q8[:, j:j + 1]), "bf16"), kd, vd,
+                            torch.tensor([L], dtype=torch.int32, device=dev()), L, SCALE, True))
+        assert bits_equal(one[0, 0], blk[0, j]), f"Lk={Lk} query {j}"
+
+
+def test_q1_at_full_length_equals_last_block_row():
+    Lk = 8196
+    q8, k, v = inputs.sdpa_case(1, 8, Lk, HQ, HKV, D, seed=1)
+    blk = run(q8, k, v, [Lk])
+    one = run(np.ascontiguousarray(q8[:, 7:8]), k, v, [Lk])
+    assert bits_equal(one[0, 0], blk[0, 7])
+
+
+@pytest.mark.parametrize("Q", [1, 2, 5, 8, 13])
+def test_every_block_width(Q):
+    """Any verify width: query j of a causal block of Q equals the lone query."""
+    Lk = 700
+    qq, k, v = inputs.sdpa_case(1, Q, Lk, HQ, HKV, D, seed=Q)
+    blk = run(qq, k, v, [Lk])
+    assert_parity(blk, oracle.sdpa(qq, k, v, np.array([Lk], np.int32), SCALE, True, "bf16"), "bf16")
+    for j in range(Q):
+        one = run(np.ascontiguousarray(qq[:, j:j + 1]), k, v, [Lk - Q + j + 1])
+        assert bits_equal(one[0, 0], blk[0, j]), f"Q={Q} j={j}"
+
+
+def test_ragged_batch_and_batch_invariance():
+    """Sequences of different lengths in one call; each sequence's output equals
+    the output of the same sequence run alone, and matches the oracle."""
+    B, Q, Lcap = 4, 5, 1300
+    qq, k, v = inputs.sdpa_case(B, Q, Lcap, HQ, HKV, D, seed=2)
+    kv_len = [1300, 5, 257, 1024]
+    full = run(qq, k, v, kv_len, max_kv=1300)
+    assert_parity(full, oracle.sdpa(qq, k, v, np.array(kv_len, np.int32), SCALE, True, "bf16"), "bf16")
+    for b in range(B):
+        one = run(np.ascontiguousarray(qq[b:b + 1]), np.ascontiguousarray(k[b:b + 1]),
+                  np.ascontiguousarray(v[b:b + 1]), [kv_len[b]])
+        assert bits_equal(one, full[b:b + 1]), f"sequence {b}"
+
+
+@pytest.mark.parametrize("Lk", [1, 8, 255, 256, 257, 511, 512, 513])
+def test_chunk_edges(Lk):
+    Q = min(8, Lk)
+    qq, k, v = inputs.sdpa_case(1, Q, Lk, HQ, HKV, D, seed=Lk)
+    out = run(qq, k, v, [Lk])
+    assert_parity(out, oracle.sdpa(qq, k, v, np.array([Lk], np.int32), SCALE, True, "bf16"), "bf16", f"Lk={Lk}")
+
+
+def test_non_causal_and_f16():
+    qq, k, v = inputs.sdpa_case(2, 3, 900, HQ, HKV, D, seed=5, dtype="f16")
+    kv = [900, 600]
+    for causal in (False, True):
+        out = run(qq, k, v, kv, causal=causal, dtype="f16")
+        ref = oracle.sdpa(qq, k, v, np.array(kv, np.int32), SCALE, causal, "f16")
+        assert_parity(out, ref, "f16", f"causal={causal}")
+
+
+def test_other_gqa_groupings():
+    for hq, hkv in ((8, 8), (16, 2), (4, 1)):
+        qq, k, v = inputs.sdpa_case(1, 4, 600, hq, hkv, D, seed=hq + hkv)
+        kvd = torch.tensor([600], dtype=torch.int32, device=dev())
+        out = to_np(bi.sdpa(to_dev(qq, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), kvd, 600, SCALE, True))
+        assert_parity(out, oracle.sdpa(qq, k, v, np.array([600], np.int32), SCALE, True, "bf16"), "bf16")
+
+
+def test_single_key_and_constant_values():
+    qq, k, v = inputs.sdpa_case(1, 1, 64, HQ, HKV, D, seed=9)
+    out = run(qq, k, v, [1])
+    vf = v[0, 0]                                           # [Hkv, D]
+    for h in range(HQ):
+        assert bits_equal(out[0, 0, h], vf[h // 4])
+    vc = inputs.to_storage(np.full(v.shape, -0.5, np.float32), "bf16")
+    out = run(qq, k, vc, [37])
+    assert np.all(out == vc.flat[0])
+
+
+def test_cache_beyond_kv_len_is_never_read():
+    """Positions at and past kv_len hold NaN: the output must not change."""
+    Lcap, L = 1024, 700
+    qq, k, v = inputs.sdpa_case(1, 8, Lcap, HQ, HKV, D, seed=11)
+    base = run(qq, k, v, [L], max_kv=L)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, L:] = 0x7FC1
+    v2[:, L:] = 0xFFC1
+    assert bits_equal(run(qq, k2, v2, [L], max_kv=L), base)
+
+
+def test_bounded_stores():
+    B, Q, L = 2, 8, 300
+    qq, k, v = inputs.sdpa_case(B, Q, L, HQ, HKV, D, seed=12)
+    og = Guarded((B, Q, HQ, D), torch.bfloat16, poison=0x3C)
+    kvd = torch.tensor([L, 100], dtype=torch.int32, device=dev())
+    need = bi.sdpa_workspace_bytes(B, Q, L, HQ, D)
+    wsg = Guarded((need,), torch.uint8, poison=0x77)
+    bi.sdpa(to_dev(qq, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), kvd, L, SCALE, True, out=og.view, ws=wsg.view)
+    torch.cuda.synchronize()
+    assert og.canaries_intact() and wsg.canaries_intact()
+    assert_parity(to_np(og.view), oracle.sdpa(qq, k, v, np.array([L, 100], np.int32), SCALE, True, "bf16"), "bf16")
+
+
+def test_run_to_run_determinism():
+    qq, k, v = inputs.sdpa_case(1, 8, 4100, HQ, HKV, D, seed=13)
+    qd, kd, vd = to_dev(qq, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    kvd = torch.tensor([4100], dtype=torch.int32, device=dev())
+    first = bi.sdpa(qd, kd, vd, kvd, 4100, SCALE, True)
+    for _ in range(30):
+        assert torch.equal(bi.sdpa(qd, kd, vd, kvd, 4100, SCALE, True).view(torch.int16), first.view(torch.int16))
