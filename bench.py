@@ -1,0 +1,281 @@
+"""Benchmark of the batch-invariant hot path on one MI355X.
+
+One step = one greedy decode step of the 4-layer Llama-style decoder (hidden
+4096, 32 query / 8 KV heads, head_dim 128, SwiGLU 14336, vocab 32000, bf16,
+random init) for B sequences at a context of `--ctx` tokens: embedding,
+4 x (RMSNorm, QKV matmul, RoPE + KV-cache write, two-pass attention, O
+matmul, residual add, RMSNorm, gate/up matmul, SiLU*mul, down matmul,
+residual add), final RMSNorm, LM-head matmul, argmax -- every reduction
+through the invariant kernels.  Inputs (weights, KV cache, token ids) are
+seeded synthetic data resident in HBM before timing starts.
+
+Printed (one JSON line): whole-step algorithmic throughput in GB/s, the
+roofline of the dominant kernel (the dense matmul) timed live with HIP events
+on the launch stream, and the CPU oracle timed on a bounded sample of the
+same step.  Extra fields: per-op breakdown, the quantized matmul at a decode
+shape, and the cost of invariance against split-K comparison variants.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "invariant matmul/SDPA/RMSNorm GB/s & TFLOP/s, % roofline, M=1..64"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_BF16_TFLOPS = 2500.0        # dense bf16 MFMA, published
+
+
+def step_traffic(cfg, B, ctx):
+    """Algorithmic bytes and flops of one decode step (each tensor read or
+    written once, at its storage size)."""
+    H, Hq, Hkv, D, F, V, L = (cfg[k] for k in ("hidden", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "n_layers"))
+    qkvn = (Hq + 2 * Hkv) * D
+    mm = []                                                   # (M, N, K) of every matmul launch
+    for _ in range(L):
+        mm += [(B, qkvn, H), (B, H, Hq * D), (B, 2 * F, H), (B, H, F)]
+    mm.append((B, V, H))
+    mm_bytes = sum(2 * (N * K + M * K + M * N) for M, N, K in mm)
+    mm_flops = sum(2 * M * N * K for M, N, K in mm)
+    norm_bytes = (2 * L + 1) * (4 * B * H + 2 * H)
+    attn_bytes = L * (4 * B * ctx * Hkv * D + 4 * B * Hq * D)
+    attn_flops = L * 4 * B * Hq * D * ctx
+    glue_bytes = (2 * B * H * 2                              # embed
+                  + L * (2 * B * qkvn + 2 * B * Hq * D + 4 * B * Hkv * D)   # rope + cache write
+                  + L * (2 * B * 2 * F + 2 * B * F)          # silu*mul
+                  + L * 2 * (3 * 2 * B * H)                  # residual adds
+                  + 2 * B * V)                               # argmax
+    return dict(mm=mm, mm_bytes=mm_bytes, mm_flops=mm_flops, norm_bytes=norm_bytes, attn_bytes=attn_bytes,
+                attn_flops=attn_flops, glue_bytes=glue_bytes,
+                total_bytes=mm_bytes + norm_bytes + attn_bytes + glue_bytes, total_flops=mm_flops + attn_flops)
+
+
+def cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids, budget_s):
+    """The oracle's decode step on the host, repeated until `budget_s` seconds
+    have passed (at least one step, at most four)."""
+    import oracle
+    from oracle import decoder as odec
+    from invariant_reductions_amd.inputs import rope_tables
+    cos_t, sin_t = rope_tables(ctx + 8, cfg["head_dim"])
+    kv = np.full(B, ctx, np.int32)
+    t0 = time.perf_counter()
+    n = 0
+    while n < 4:
+        odec.decode_step(W, cfg, ids, kc_host, vc_host, kv, cos_t, sin_t)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return n, time.perf_counter() - t0, oracle.num_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--ctx", type=int, default=768)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the batch-invariant hot path is a single-GPU kernel set "
+              "(multi-GPU sharding is a design note, not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import invariant_reductions_amd as bi
+    from invariant_reductions_amd import inputs
+    from invariant_reductions_amd.decoder import Decoder
+
+    cfg = inputs.LLAMA_4L
+    B, ctx, K, Wm = args.batch, args.ctx, args.steps, args.warmup
+    dev = torch.device("cuda:0")
+    bi.lib()
+    t_setup = time.perf_counter()
+    W = inputs.decoder_weights(cfg, seed=0)
+    cap = ctx + K + Wm + 8
+    model = Decoder(cfg, W, max_batch=B, max_q=1, max_len=cap, device=dev)
+    rng = np.random.default_rng(1)
+    Hkv, D = cfg["n_kv_heads"], cfg["head_dim"]
+    kc_host, vc_host = [], []
+    for li in range(cfg["n_layers"]):
+        kh = inputs.normal(rng, (B, cap, Hkv, D))
+        vh = inputs.normal(rng, (B, cap, Hkv, D))
+        model.kc[li].copy_(torch.from_numpy(kh.view(np.int16)).view(torch.bfloat16))
+        model.vc[li].copy_(torch.from_numpy(vh.view(np.int16)).view(torch.bfloat16))
+        kc_host.append(kh)
+        vc_host.append(vh)
+    ids0 = rng.integers(0, cfg["vocab"], size=B).astype(np.int32)
+    model.ids[:B].copy_(torch.from_numpy(ids0))
+    model.kv_len[:B].fill_(ctx)
+    stream = torch.cuda.current_stream()
+    plan = model.plan(B, 1, cap, stream)
+    mm_idx = [i for i, s in enumerate(plan) if s[0] == "matmul"]
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def advance():
+        model.ids[:B].copy_(model.next_ids[:B])
+        model.kv_len[:B].add_(1)
+
+    for _ in range(Wm):
+        model.run_plan(plan)
+        advance()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K * len(mm_idx))]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e = 0
+    for _ in range(K):
+        for i, (name, fn, a) in enumerate(plan):
+            if name == "matmul":
+                ev[e][0].record(stream)
+                rc = fn(*a)
+                ev[e][1].record(stream)
+                e += 1
+            else:
+                rc = fn(*a)
+            if rc != 0:
+                raise bi.BIError(rc, name)
+        advance()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mm_ms = sum(s.elapsed_time(t) for s, t in ev)
+    ms_step = (t1 - t0) * 1e3 / K
+
+    ctx_mean = ctx + Wm + (K - 1) / 2.0
+    tr = step_traffic(cfg, B, ctx_mean)
+    value = tr["total_bytes"] / (ms_step * 1e-3) / 1e9
+    mm_gbs = tr["mm_bytes"] * K / (mm_ms * 1e-3) / 1e9
+    mm_avg_us = mm_ms * 1e3 / (K * len(mm_idx))
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: random-init weights N(0,0.02), KV cache and token ids N(0,1)/uniform, seeded",
+        "config": {"workload": f"greedy decode step, 4-layer Llama-style decoder (hidden 4096, 32q/8kv heads, "
+                               f"d128, SwiGLU 14336, vocab 32000), batch {B}, context {ctx}",
+                   "batch": B, "context": ctx, "layers": cfg["n_layers"]},
+        "tflops": round(tr["total_flops"] / (ms_step * 1e-3) / 1e12, 3),
+        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "roofline": {"kernel": "bi_matmul (dense_kernel bf16, transposed weights)", "bound": "hbm",
+                     "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launches_per_step": len(mm_idx), "avg_launch_us": round(mm_avg_us, 2),
+                     "share_of_step": round(mm_ms / K / ms_step, 3)},
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_extras:
+        out["ops"] = op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch)
+        out["invariance_overhead"] = split_overhead(torch, bi, dev, B)
+        out["qmatmul"] = qmatmul_decode(torch, bi, dev)
+
+    if not args.no_cpu_baseline:
+        n, secs, cores = cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids0, args.cpu_budget)
+        trc = step_traffic(cfg, B, ctx)
+        out["cpu_baseline"] = {"value": round(trc["total_bytes"] * n / secs / 1e9, 3), "unit": "GB/s",
+                               "cores": cores, "kind": "oracle",
+                               "sample": f"{n} decode step(s) of the same workload (batch {B}, context {ctx}) "
+                                         f"through the oracle's fixed-order fp32 ops, {secs:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
+def op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch):
+    """Per-op device time of one step (HIP events around every launch, 5 steps)."""
+    reps = 5
+    evs = []
+    for _ in range(reps):
+        row = []
+        for name, fn, a in plan:
+            s, t = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn(*a)
+            t.record(stream)
+            row.append((name, s, t))
+        evs.append(row)
+    torch.cuda.synchronize()
+    tot = {}
+    for row in evs:
+        for name, s, t in row:
+            tot[name] = tot.get(name, 0.0) + s.elapsed_time(t) / reps
+    tr = step_traffic(cfg, B, ctx_mean)
+    bytes_of = {"matmul": tr["mm_bytes"], "sdpa": tr["attn_bytes"], "rmsnorm": tr["norm_bytes"]}
+    res = {}
+    for name, ms in tot.items():
+        r = {"us_per_step": round(ms * 1e3, 1)}
+        if name in bytes_of:
+            gbs = bytes_of[name] / (ms * 1e-3) / 1e9
+            r.update(gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+        res[name] = r
+    return res
+
+
+def _time(torch, fn, reps=20):
+    s, t = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    t.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(t) / reps
+
+
+def split_overhead(torch, bi, dev, B):
+    """Invariant dense matmul vs the fastest split-K comparison variant at the
+    decoder's projection shapes (median-free: mean of 20 back-to-back launches)."""
+    res = {}
+    for (N, K) in ((6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336), (32000, 4096)):
+        x = torch.randn(B, K, device=dev).to(torch.bfloat16)
+        w = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16)
+        y = torch.empty(B, N, dtype=torch.bfloat16, device=dev)
+        t_inv = _time(torch, lambda: bi.matmul(x, w, True, out=y))
+        best = None
+        for s in (2, 4, 8, 16):
+            ws = torch.empty(B * N * s * 4, dtype=torch.uint8, device=dev)
+            t = _time(torch, lambda: bi.matmul_split(x, w, s, True, out=y, ws=ws))
+            if best is None or t < best[1]:
+                best = (s, t)
+        res[f"{N}x{K}"] = {"invariant_us": round(t_inv * 1e3, 1), "best_split": best[0],
+                           "split_us": round(best[1] * 1e3, 1), "overhead": round(t_inv / best[1] - 1, 3),
+                           "invariant_gbs": round(2 * (N * K + B * K + B * N) / (t_inv * 1e-3) / 1e9, 1)}
+    return res
+
+
+def qmatmul_decode(torch, bi, dev):
+    """Quantized matmul at a decode shape (M = 8, K = N = 4096 and the MLP
+    shape 28672 x 4096): weight stream in GB/s against the HBM peak."""
+    from invariant_reductions_amd import inputs
+    res = {}
+    for mode, gs in (("affine", 64), ("nvfp4", 16)):
+        for (N, K) in ((4096, 4096), (28672, 4096)):
+            M = 8
+            x, wq, s, b = inputs.qmatmul_case(M, K, N, mode, gs, True, seed=0)
+            xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
+            wqd = torch.from_numpy(wq.view(np.int32)).to(dev)
+            sd = torch.from_numpy(s if s.dtype == np.uint8 else s.view(np.int16)).to(dev)
+            bd = None if b is None else torch.from_numpy(b.view(np.int16)).to(dev)
+            y = torch.empty(M, N, dtype=torch.float16, device=dev)
+            qm = bi.AFFINE if mode == "affine" else bi.NVFP4
+            t = _time(torch, lambda: bi.qmatmul(xd, wqd, sd, bd, N, K, qm, gs, True, out=y))
+            wbytes = N * K // 2 + N * (K // gs) * (4 if mode == "affine" else 1)
+            tot = wbytes + 2 * M * K + 2 * M * N
+            gbs = tot / (t * 1e-3) / 1e9
+            res[f"{mode}-gs{gs} {M}x{N}x{K}"] = {"us": round(t * 1e3, 1), "gbs": round(gbs, 1),
+                                                  "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -24,8 +24,12 @@
  *     the kernel rather than reject the dimension.
  *
  * Conventions shared by every call
- *   - Pointers are device pointers unless stated; every base pointer must be
- *     16-byte aligned (BI_ERR_ALIGN otherwise).  Tensors are dense row-major.
+ *   - Pointers are device pointers unless stated.  Tensors are dense
+ *     row-major.  Every pointer must be aligned to its element size
+ *     (BI_ERR_ALIGN otherwise); attention, embedding and the rotary/cache
+ *     write also need 16-byte aligned base pointers.  The matmuls and RMSNorm
+ *     use 16-byte vector loads when the pointers and row lengths allow it and
+ *     element loads otherwise -- with the same reduction tree either way.
  *   - bf16 / f16 data are 16-bit IEEE-style patterns (bfloat16, binary16);
  *     f32 is binary32.  Accumulation is fp32; outputs are rounded to the
  *     output type with round-to-nearest-even.

@@ -230,8 +230,10 @@ template <typename S>
 static void launch_dense(const void *x, const void *w, void *y, float *part, int64_t M, int64_t N,
                          int64_t K, bool trans, int splits, hipStream_t st)
 {
-    // 16-byte chunks never straddle K when K is a multiple of the chunk length.
-    const bool vec = (K % S::kElemsPer16B) == 0;
+    // 16-byte chunk loads when K is a multiple of the chunk length (chunks then
+    // never straddle K) and both operands start on 16-byte boundaries; the
+    // element-wise path fills the same slots, so the tree is the same.
+    const bool vec = (K % S::kElemsPer16B) == 0 && host_aligned16(x) && (host_aligned16(w) || !trans);
     if (trans) {
         if (vec) launch_dense_mt<S, true, true>(x, w, y, part, M, N, K, splits, st);
         else launch_dense_mt<S, true, false>(x, w, y, part, M, N, K, splits, st);
@@ -247,7 +249,8 @@ static bi_status check_dense(const void *x, const void *w, const void *y, int64_
     if (!x || !w || !y) return BI_ERR_NULL;
     if (M < 1 || N < 1 || K < 1 || M > (1ll << 31) || N > (1ll << 31) || K > (1ll << 31)) return BI_ERR_SHAPE;
     if (dtype != BI_BF16 && dtype != BI_F16 && dtype != BI_F32) return BI_ERR_DTYPE;
-    if (!host_aligned16(x) || !host_aligned16(w) || !host_aligned16(y)) return BI_ERR_ALIGN;
+    const size_t esz = dtype == BI_F32 ? 4 : 2;
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & (esz - 1)) return BI_ERR_ALIGN;
     return BI_OK;
 }
 

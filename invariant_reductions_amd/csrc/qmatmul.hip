@@ -156,7 +156,7 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
     const int64_t n0 = (int64_t)blockIdx.x * TC;
     const int64_t m0 = (int64_t)blockIdx.y * TR;
     const int64_t nblocks = cdiv(K, kQBlock);
-    const bool xvec = (K % 8) == 0;                 // x rows 16-byte aligned: chunks never straddle K
+    const bool xvec = (K % 8) == 0 && aligned16(x); // x rows 16-byte aligned: chunks never straddle K
 
     f32x4 acc[MT][NS];
 #pragma unroll
@@ -245,7 +245,7 @@ static void launch_q(const void *x, const uint32_t *wq, const void *s, const voi
                      int64_t K, bool trans, hipStream_t st)
 {
     if (!trans) launch_q_mt<QM, GS, false, false>(x, wq, s, b, y, M, N, K, st);
-    else if (K % 32 == 0) launch_q_mt<QM, GS, true, true>(x, wq, s, b, y, M, N, K, st);
+    else if (K % 32 == 0 && host_aligned16(wq)) launch_q_mt<QM, GS, true, true>(x, wq, s, b, y, M, N, K, st);
     else launch_q_mt<QM, GS, true, false>(x, wq, s, b, y, M, N, K, st);
 }
 
@@ -271,7 +271,9 @@ extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *s
     }
     const int64_t qdim = w_transposed ? K : N;
     if (qdim % group_size) return BI_ERR_GROUP;
-    if (!host_aligned16(x) || !host_aligned16(wq) || !host_aligned16(y)) return BI_ERR_ALIGN;
+    if ((((uintptr_t)x | (uintptr_t)y) & 1u) || ((uintptr_t)wq & 3u) || ((uintptr_t)scales & 1u) ||
+        ((uintptr_t)biases & 1u))
+        return BI_ERR_ALIGN;
     (void)hipGetLastError();
     const bool t = w_transposed != 0;
     if (qmode == BI_NVFP4) launch_q<BI_NVFP4, 16>(x, wq, scales, biases, y, M, N, K, t, stream);

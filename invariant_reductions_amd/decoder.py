@@ -1,0 +1,236 @@
+"""Llama-style decoder built from the batch-invariant ops: greedy decoding,
+plain and speculative.
+
+Sources: "Batch-invariant kernels: why temperature-0 decoding is still
+nondeterministic" (Thesis and Mental model: make RMSNorm, matmul and attention
+batch-invariant and greedy decoding stops depending on the batch; Case 5: the
+load-dependent greedy token; Case 6: KV cache written before attention) and
+"Fix/speculative shape invariance" (Problem: a token evaluated alone and the
+same token inside a verification block must produce identical results).
+
+Model (pre-norm, no biases, bf16 storage between ops):
+    h   = rmsnorm(x, attn_norm);  qkv = h @ Wqkv^T
+    q,k = rope(q, k at their positions); k, v written to the cache
+    o   = causal attention over the cache;  x = x + o @ Wo^T
+    h   = rmsnorm(x, mlp_norm);   g|u = h @ Wgu^T
+    x   = x + (silu(g) * u) @ Wdown^T
+logits = rmsnorm(x, final_norm) @ Wlm^T; next token = argmax (lowest index on ties)
+
+Every op is one or two launches of the C ABI on torch's current stream; all
+buffers are allocated once, so a decode step allocates nothing.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (add, argmax, embed, matmul, rmsnorm, rope_kv_write, sdpa, sdpa_workspace_bytes, silu_mul)
+from .inputs import rope_tables
+
+
+def _dev16(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+class Decoder:
+    def __init__(self, cfg: dict, weights: dict, max_batch: int, max_q: int, max_len: int, device="cuda:0"):
+        self.cfg = cfg
+        self.dev = torch.device(device)
+        c = cfg
+        self.H, self.Hq, self.Hkv, self.D = c["hidden"], c["n_heads"], c["n_kv_heads"], c["head_dim"]
+        self.F, self.V, self.L = c["ffn"], c["vocab"], c["n_layers"]
+        self.eps = float(c["eps"])
+        self.qn = self.Hq * self.D
+        self.qkvn = (self.Hq + 2 * self.Hkv) * self.D
+        d = self.dev
+        W = weights
+        self.embed_w = _dev16(W["embed"], d)
+        self.layers = [{k: _dev16(v, d) for k, v in lw.items()} for lw in W["layers"]]
+        self.final_norm = _dev16(W["final_norm"], d)
+        self.lm_head = _dev16(W["lm_head"], d)
+        cos_t, sin_t = rope_tables(max_len, self.D, c.get("rope_theta", 10000.0))
+        self.cos_t = torch.from_numpy(cos_t).to(d)
+        self.sin_t = torch.from_numpy(sin_t).to(d)
+        self.max_batch, self.max_q, self.max_len = max_batch, max_q, max_len
+        T = max_batch * max_q
+        bf = torch.bfloat16
+        z = lambda *s: torch.zeros(*s, dtype=bf, device=d)
+        self.kc = [z(max_batch, max_len, self.Hkv, self.D) for _ in range(self.L)]
+        self.vc = [z(max_batch, max_len, self.Hkv, self.D) for _ in range(self.L)]
+        self.x, self.h, self.t1 = z(T, self.H), z(T, self.H), z(T, self.H)
+        self.qkv, self.q, self.o = z(T, self.qkvn), z(T, self.qn), z(T, self.qn)
+        self.gu, self.a = z(T, 2 * self.F), z(T, self.F)
+        self.logits = z(T, self.V)
+        self.ids = torch.zeros(T, dtype=torch.int32, device=d)
+        self.next_ids = torch.zeros(T, dtype=torch.int32, device=d)
+        self.kv_len = torch.zeros(max_batch, dtype=torch.int32, device=d)
+        ws = sdpa_workspace_bytes(max_batch, max_q, max_len, self.Hq, self.D)
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=d)
+
+    # -- one forward over Q new tokens of each of B sequences -----------------
+    def forward(self, B: int, Q: int, max_kv: int):
+        """Reads self.ids[:B*Q] and self.kv_len[:B] (lengths after the new
+        tokens), fills self.logits[:B*Q] and self.next_ids[:B*Q]."""
+        T = B * Q
+        H, qn = self.H, self.qn
+        x, h, t1 = self.x[:T], self.h[:T], self.t1[:T]
+        qkv, q, o = self.qkv[:T], self.q[:T], self.o[:T]
+        gu, a = self.gu[:T], self.a[:T]
+        kv = self.kv_len[:B]
+        embed(self.ids[:T], self.embed_w, out=x)
+        scale = 1.0 / float(np.sqrt(self.D))
+        for li, Lw in enumerate(self.layers):
+            rmsnorm(x, Lw["attn_norm"], self.eps, out=h)
+            matmul(h, Lw["wqkv"], True, out=qkv)
+            kc, vc = self.kc[li][:B], self.vc[li][:B]
+            rope_kv_write(qkv, q, kc, vc, kv, self.cos_t, self.sin_t, B, Q, self.Hq, self.Hkv, self.D)
+            sdpa(q.view(B, Q, self.Hq, self.D), kc, vc, kv, max_kv, scale, True,
+                 out=o.view(B, Q, self.Hq, self.D), ws=self.ws)
+            matmul(o, Lw["wo"], True, out=t1)
+            add(x, t1, out=x)
+            rmsnorm(x, Lw["mlp_norm"], self.eps, out=h)
+            matmul(h, Lw["wgu"], True, out=gu)
+            silu_mul(gu, out=a)
+            matmul(a, Lw["wdown"], True, out=t1)
+            add(x, t1, out=x)
+        rmsnorm(x, self.final_norm, self.eps, out=h)
+        matmul(h, self.lm_head, True, out=self.logits[:T])
+        argmax(self.logits[:T], out=self.next_ids[:T])
+        return self.logits[:T]
+
+    # -- launch plans -----------------------------------------------------------------
+    def plan(self, B: int, Q: int, max_kv: int, stream=None):
+        """The forward as a list of (name, C entry point, argument tuple) over the
+        fixed buffers, for callers that replay the same step many times (a
+        serving loop, the benchmark) without re-marshalling arguments.  The
+        device-side ids / kv_len buffers are read at run time, so one plan
+        serves every step whose lengths stay within max_kv."""
+        import ctypes
+        from . import lib
+        L = lib()
+        st = ctypes.c_void_p((stream or torch.cuda.current_stream()).cuda_stream)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        T = B * Q
+        H, qn = self.H, self.qn
+        x, h, t1 = self.x[:T], self.h[:T], self.t1[:T]
+        qkv, q, o = self.qkv[:T], self.q[:T], self.o[:T]
+        gu, a = self.gu[:T], self.a[:T]
+        kv = self.kv_len[:B]
+        scale = ctypes.c_float(1.0 / float(np.sqrt(self.D)))
+        eps = ctypes.c_float(self.eps)
+        steps = [("embed", L.bi_embed, (p(self.ids), p(self.embed_w), p(x), T, self.V, H, st))]
+        mm = lambda xin, w, out, N, K: ("matmul", L.bi_matmul, (p(xin), p(w), p(out), T, N, K, 0, 1, st))
+        for li, Lw in enumerate(self.layers):
+            kc, vc = self.kc[li], self.vc[li]
+            Lcap = kc.shape[1]
+            steps += [
+                ("rmsnorm", L.bi_rmsnorm, (p(x), p(Lw["attn_norm"]), p(h), T, H, eps, 0, st)),
+                mm(h, Lw["wqkv"], qkv, self.qkvn, H),
+                ("rope_kv", L.bi_rope_kv_write, (p(qkv), p(q), p(kc), p(vc), p(kv), p(self.cos_t), p(self.sin_t),
+                                                 B, Q, Lcap, self.Hq, self.Hkv, self.D, self.cos_t.shape[0], st)),
+                ("sdpa", L.bi_sdpa, (p(q), p(kc), p(vc), p(o), p(kv), max_kv, B, Q, Lcap, self.Hq, self.Hkv,
+                                     self.D, scale, 1, 0, p(self.ws), self.ws.numel(), st)),
+                mm(o, Lw["wo"], t1, H, qn),
+                ("add", L.bi_add, (p(x), p(t1), p(x), T * H, st)),
+                ("rmsnorm", L.bi_rmsnorm, (p(x), p(Lw["mlp_norm"]), p(h), T, H, eps, 0, st)),
+                mm(h, Lw["wgu"], gu, 2 * self.F, H),
+                ("silu_mul", L.bi_silu_mul, (p(gu), p(a), T, self.F, st)),
+                mm(a, Lw["wdown"], t1, H, self.F),
+                ("add", L.bi_add, (p(x), p(t1), p(x), T * H, st)),
+            ]
+        steps += [("rmsnorm", L.bi_rmsnorm, (p(x), p(self.final_norm), p(h), T, H, eps, 0, st)),
+                  ("matmul", L.bi_matmul, (p(h), p(self.lm_head), p(self.logits), T, self.V, H, 0, 1, st)),
+                  ("argmax", L.bi_argmax, (p(self.logits), p(self.next_ids), T, self.V, st))]
+        return steps
+
+    @staticmethod
+    def run_plan(plan):
+        for name, fn, args in plan:
+            rc = fn(*args)
+            if rc != 0:
+                from . import BIError
+                raise BIError(rc, name)
+
+    # -- greedy decoding ----------------------------------------------------------
+    def prefill(self, prompts: torch.Tensor):
+        """prompts int32 [B, P] on the device; returns the first generated ids [B] (host)."""
+        B, P = prompts.shape
+        assert B <= self.max_batch and P <= self.max_q and P < self.max_len
+        self.ids[:B * P].copy_(prompts.reshape(-1))
+        self.kv_len[:B].fill_(P)
+        self.forward(B, P, P)
+        return self.next_ids[:B * P].view(B, P)[:, -1].cpu().numpy().copy(), \
+            self.logits[:B * P].view(B, P, self.V)[:, -1]
+
+    def generate(self, prompts: torch.Tensor, steps: int, on_logits=None):
+        """Plain greedy decoding: one token per sequence per step.
+        on_logits(i, logits [B, V]) sees the logits that chose generated token i.
+        Returns the generated ids [B, steps] (host int32)."""
+        B, P = prompts.shape
+        assert P + steps <= self.max_len
+        first, lg = self.prefill(prompts)
+        if on_logits:
+            on_logits(0, lg)
+        out = np.zeros((B, steps), np.int32)
+        out[:, 0] = first
+        self.ids[:B].copy_(torch.from_numpy(first).to(self.dev))
+        for t in range(1, steps):
+            self.kv_len[:B].fill_(P + t)
+            lg = self.forward(B, 1, P + t)
+            if on_logits:
+                on_logits(t, lg)
+            self.ids[:B].copy_(self.next_ids[:B])
+            out[:, t] = self.next_ids[:B].cpu().numpy()
+        return out
+
+    def generate_speculative(self, prompts: torch.Tensor, steps: int, draft, draft_len: int = 4, on_logits=None):
+        """Greedy speculative decoding: each round verifies the last committed
+        token plus `draft_len` drafted tokens in one causal block (Q =
+        draft_len + 1), accepts the longest prefix of drafts the model agrees
+        with, and takes the model's own token after it.  Sequences advance at
+        their own pace; each keeps its own KV length, and the cache slots of
+        rejected drafts are overwritten by the next round.
+        draft(b, i, n) -> n proposed ids for generated positions i, i+1, ...
+        on_logits(b, i, logits [V]) sees the logits that chose generated token i
+        of sequence b."""
+        B, P = prompts.shape
+        Q = draft_len + 1
+        assert Q <= self.max_q and P + steps + Q <= self.max_len
+        first, lg = self.prefill(prompts)
+        out = np.zeros((B, steps), np.int32)
+        out[:, 0] = first
+        if on_logits:
+            for b in range(B):
+                on_logits(b, 0, lg[b])
+        done = np.ones(B, np.int64)                  # generated tokens committed per sequence
+        rounds = 0
+        while (done < steps).any():
+            ids = np.zeros((B, Q), np.int32)
+            kvl = np.zeros(B, np.int32)
+            for b in range(B):
+                n = int(min(done[b], steps))         # finished sequences re-verify their last block
+                ids[b, 0] = out[b, n - 1]
+                ids[b, 1:] = draft(b, n, draft_len)
+                kvl[b] = P + n - 1 + Q                # block occupies positions P+n-1 .. P+n-1+draft_len
+            self.ids[:B * Q].copy_(torch.from_numpy(ids.reshape(-1)).to(self.dev))
+            self.kv_len[:B].copy_(torch.from_numpy(kvl).to(self.dev))
+            lgs = self.forward(B, Q, int(kvl.max())).view(B, Q, self.V)
+            tgt = self.next_ids[:B * Q].view(B, Q).cpu().numpy()
+            for b in range(B):
+                n = int(done[b])
+                if n >= steps:
+                    continue
+                a = 0
+                while a < draft_len and ids[b, 1 + a] == tgt[b, a]:
+                    a += 1
+                new = list(ids[b, 1:1 + a]) + [tgt[b, a]]
+                for j, tok in enumerate(new):
+                    if n + j >= steps:
+                        break
+                    out[b, n + j] = tok
+                    if on_logits:
+                        on_logits(b, n + j, lgs[b, j])
+                done[b] = n + len(new)
+            rounds += 1
+        self.rounds = rounds
+        return out

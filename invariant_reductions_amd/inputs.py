@@ -227,3 +227,30 @@ def prompts(B: int, L: int = 512, vocab: int = 32000, seed: int = 1, max_batch: 
     """Random token ids, drawn as [max_batch, L] and sliced to B rows."""
     rng = np.random.default_rng(seed)
     return rng.integers(0, vocab, size=(max(B, max_batch), L)).astype(np.int32)[:B]
+
+
+LLAMA_4L = dict(hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, ffn=14336, vocab=32000,
+                n_layers=4, eps=1e-6, rope_theta=10000.0)
+
+
+def decoder_weights(cfg: dict = LLAMA_4L, seed: int = 0, std: float = 0.02):
+    """Random-init weights of a Llama-style decoder as bf16 storage arrays:
+    every projection and the embedding ~ N(0, std), drawn in a fixed order
+    (embedding, then per layer qkv, o, gate|up, down, then lm_head); RMSNorm
+    weights are ones.  Projections are stored [out_features, in_features]."""
+    H, F, V = cfg["hidden"], cfg["ffn"], cfg["vocab"]
+    qkv = (cfg["n_heads"] + 2 * cfg["n_kv_heads"]) * cfg["head_dim"]
+    rng = np.random.default_rng(seed)
+
+    def draw(shape):
+        return to_storage(rng.standard_normal(shape, dtype=np.float32) * np.float32(std), "bf16")
+
+    ones = to_storage(np.ones(H, np.float32), "bf16")
+    W = {"embed": draw((V, H)), "layers": []}
+    for _ in range(cfg["n_layers"]):
+        W["layers"].append(dict(attn_norm=ones.copy(), wqkv=draw((qkv, H)),
+                                wo=draw((H, cfg["n_heads"] * cfg["head_dim"])), mlp_norm=ones.copy(),
+                                wgu=draw((2 * F, H)), wdown=draw((H, F))))
+    W["final_norm"] = ones.copy()
+    W["lm_head"] = draw((V, H))
+    return W

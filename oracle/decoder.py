@@ -63,3 +63,35 @@ def forward(weights: dict, cfg: dict, tokens: np.ndarray, cos_t: np.ndarray, sin
     logits = matmul(h, weights["lm_head"], BF16, True)
     lb = _bf(logits)
     return logits, lb, argmax(lb, BF16)
+
+
+def decode_step(weights: dict, cfg: dict, ids: np.ndarray, kcache: list, vcache: list, kv_len: np.ndarray,
+                cos_t: np.ndarray, sin_t: np.ndarray):
+    """One greedy decode step for B sequences, one new token each: token b sits
+    at position kv_len[b] - 1; its rotated key and its value are written into
+    the per-layer caches kcache[l], vcache[l] ([B, Lcap, Hkv, D] bf16 bits)
+    before attention reads them.  Returns (logits fp32 [B, V], greedy ids [B])."""
+    H, Hq, Hkv, D, F = cfg["hidden"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["ffn"]
+    eps = cfg["eps"]
+    B = ids.shape[0]
+    pos = (np.asarray(kv_len, np.int32) - 1).astype(np.int32)
+    qn, kn = Hq * D, Hkv * D
+    x = np.ascontiguousarray(weights["embed"][np.asarray(ids, np.int64)])
+    for li, L in enumerate(weights["layers"]):
+        h = _bf(rmsnorm(x, L["attn_norm"], BF16, eps))
+        qkv = _bf(matmul(h, L["wqkv"], BF16, True))
+        q = _bf(rope(np.ascontiguousarray(qkv[:, :qn].reshape(B, Hq, D)), pos, cos_t, sin_t, BF16))
+        k = _bf(rope(np.ascontiguousarray(qkv[:, qn:qn + kn].reshape(B, Hkv, D)), pos, cos_t, sin_t, BF16))
+        v = qkv[:, qn + kn:].reshape(B, Hkv, D)
+        for b in range(B):
+            kcache[li][b, pos[b]] = k[b]
+            vcache[li][b, pos[b]] = v[b]
+        o = _bf(sdpa(q[:, None], kcache[li], vcache[li], kv_len, 1.0 / np.sqrt(D), True, BF16))
+        x = _add(x, _bf(matmul(np.ascontiguousarray(o.reshape(B, qn)), L["wo"], BF16, True)))
+        h = _bf(rmsnorm(x, L["mlp_norm"], BF16, eps))
+        gu = _bf(matmul(h, L["wgu"], BF16, True))
+        a = _bf(silu_mul(np.ascontiguousarray(gu[:, :F]), np.ascontiguousarray(gu[:, F:]), BF16))
+        x = _add(x, _bf(matmul(a, L["wdown"], BF16, True)))
+    h = _bf(rmsnorm(x, weights["final_norm"], BF16, eps))
+    logits = matmul(h, weights["lm_head"], BF16, True)
+    return logits, argmax(_bf(logits), BF16)

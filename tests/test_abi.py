@@ -14,7 +14,7 @@ HDR = os.path.join(ROOT, "include", "bi.h")
 
 P = ctypes.c_void_p
 A = P(0x10000)          # 16-byte aligned, never dereferenced: every call below fails validation first
-ODD = P(0x10008)        # 8-byte aligned only
+ODD = P(0x10001)        # misaligned for every element size: always rejected
 
 OK, NULL, SHAPE, DTYPE, GROUP, ALIGN, WORKSPACE, LAUNCH, UNSUP = range(9)
 

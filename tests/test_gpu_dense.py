@@ -131,11 +131,14 @@ def test_run_to_run_determinism():
         assert torch.equal(bi.matmul(xd, wd).view(torch.int16), first.view(torch.int16))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_split_variant_is_correct_but_not_invariant(dtype):
     """Negative control: split-K with a cleanup reduction computes the same
     product within tolerance but changes bits -- so the invariance tests above
-    can tell a split tree from the invariant one."""
+    can tell a split tree from the invariant one.  In bf16 the 8-bit mantissa
+    usually rounds the fp32 difference away at this shape (the reviewer on
+    "Fix/speculative shape invariance" saw bf16 pass with the feature off for
+    the same reason), so the bit check is made in f16 and f32."""
     x, wt, _ = inputs.dense_case(4, 512, 4096, dtype, seed=0)
     xd, wd = to_dev(x, dtype), to_dev(wt, dtype)
     inv = to_np(bi.matmul(xd, wd))
@@ -145,6 +148,7 @@ def test_split_variant_is_correct_but_not_invariant(dtype):
         y = to_np(bi.matmul_split(xd, wd, s))
         assert_parity(y, ref, dtype, f"splits={s}")
         differs += int(not bits_equal(y, inv))
-    assert differs > 0
+    if dtype != "bf16":
+        assert differs > 0
     # split 1 is the invariant kernel itself
     assert bits_equal(to_np(bi.matmul_split(xd, wd, 1)), inv)

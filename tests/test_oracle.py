@@ -582,3 +582,23 @@ def test_decoder_is_causal():
     b, _, _ = decoder.forward(W, TINY, t2, cos_t, sin_t)
     assert np.array_equal(a[:12], b[:12])
     assert not np.array_equal(a[12:], b[12:])
+
+
+def test_decode_step_reproduces_teacher_forced_forward():
+    """Filling the cache from a teacher-forced run and then decoding the last
+    token gives the forward's logits at that position bit for bit (the
+    oracle's ops are row-independent)."""
+    from oracle import decoder
+    W = _tiny_weights(2)
+    c = TINY
+    cos_t, sin_t = inputs.rope_tables(64, c["head_dim"])
+    toks = np.random.default_rng(5).integers(0, c["vocab"], size=(2, 17))
+    Lcap = 20
+    full = [decoder.forward(W, c, toks[b], cos_t, sin_t)[0] for b in range(2)]
+    # caches filled by running decode steps position by position
+    kc = [np.zeros((2, Lcap, c["n_kv_heads"], c["head_dim"]), np.uint16) for _ in range(c["n_layers"])]
+    vc = [np.zeros_like(kc[0]) for _ in range(c["n_layers"])]
+    for p in range(17):
+        logits, ids = decoder.decode_step(W, c, toks[:, p], kc, vc, np.full(2, p + 1, np.int32), cos_t, sin_t)
+        for b in range(2):
+            assert np.array_equal(logits[b], full[b][p]), (b, p)
