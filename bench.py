@@ -118,8 +118,16 @@ def main():
     model.ids[:B].copy_(torch.from_numpy(ids0))
     model.kv_len[:B].fill_(ctx)
     stream = torch.cuda.current_stream()
+    # A plain 256 MiB device-to-device copy: counter runs of this command
+    # (FETCH_SIZE, WRITE_SIZE) read it to scale the counters to bytes.
+    calib = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+    calib.fill_(1.0)
+    calib2 = torch.empty_like(calib)
+    calib2.copy_(calib)
+    del calib, calib2
     plan = model.plan(B, 1, cap, stream)
     mm_idx = [i for i, s in enumerate(plan) if s[0] == "matmul"]
+    mm_shape = [(plan[i][2][4], plan[i][2][5]) for i in mm_idx]          # (N, K) of each matmul launch
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -148,8 +156,12 @@ def main():
         advance()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    mm_ms = sum(s.elapsed_time(t) for s, t in ev)
+    durs = [s.elapsed_time(t) for s, t in ev]
+    mm_ms = sum(durs)
     ms_step = (t1 - t0) * 1e3 / K
+    per_shape = {}
+    for j, d in enumerate(durs):
+        per_shape.setdefault(mm_shape[j % len(mm_idx)], []).append(d)
 
     ctx_mean = ctx + Wm + (K - 1) / 2.0
     tr = step_traffic(cfg, B, ctx_mean)
@@ -167,17 +179,22 @@ def main():
                    "batch": B, "context": ctx, "layers": cfg["n_layers"]},
         "tflops": round(tr["total_flops"] / (ms_step * 1e-3) / 1e12, 3),
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
-        "roofline": {"kernel": "bi_matmul (dense_kernel bf16, transposed weights)", "bound": "hbm",
+        "roofline": {"kernel": "bi_matmul -> dense_stream_kernel<bf16, MT, NS> (every instantiation the step "
+                               "launches; achieved = all matmul algorithmic bytes / all matmul launch time)",
+                     "bound": "hbm",
                      "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "launches_per_step": len(mm_idx), "avg_launch_us": round(mm_avg_us, 2),
-                     "share_of_step": round(mm_ms / K / ms_step, 3)},
+                     "share_of_step": round(mm_ms / K / ms_step, 3),
+                     "per_shape": {f"{B}x{N}x{Kk}": {"us": round(1e3 * np.mean(v), 1),
+                                                     "gbs": round(2 * (N * Kk + B * Kk + B * N) / (np.mean(v) * 1e-3) / 1e9, 1)}
+                                   for (N, Kk), v in per_shape.items()}},
         "setup_s": round(setup_s, 1),
     }
 
     if not args.no_extras:
         out["ops"] = op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch)
-        out["invariance_overhead"] = split_overhead(torch, bi, dev, B)
+        out["invariance_overhead"] = split_overhead(torch, bi, model, B, per_shape)
         out["qmatmul"] = qmatmul_decode(torch, bi, dev)
 
     if not args.no_cpu_baseline:
@@ -232,24 +249,28 @@ def _time(torch, fn, reps=20):
     return s.elapsed_time(t) / reps
 
 
-def split_overhead(torch, bi, dev, B):
-    """Invariant dense matmul vs the fastest split-K comparison variant at the
-    decoder's projection shapes (median-free: mean of 20 back-to-back launches)."""
+def split_overhead(torch, bi, model, B, per_shape):
+    """Invariant dense matmul (its launches inside the timed decode steps) vs the
+    fastest split-K comparison variant at the same shapes, on the decoder's own
+    weights, rotating over the layers so the weights are as cold as in a step."""
+    dev = model.dev
     res = {}
-    for (N, K) in ((6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336), (32000, 4096)):
+    mats = {(model.qkvn, model.H): [L["wqkv"] for L in model.layers], (model.H, model.qn): [L["wo"] for L in model.layers],
+            (2 * model.F, model.H): [L["wgu"] for L in model.layers], (model.H, model.F): [L["wdown"] for L in model.layers],
+            (model.V, model.H): [model.lm_head]}
+    for (N, K), ws_list in mats.items():
         x = torch.randn(B, K, device=dev).to(torch.bfloat16)
-        w = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16)
         y = torch.empty(B, N, dtype=torch.bfloat16, device=dev)
-        t_inv = _time(torch, lambda: bi.matmul(x, w, True, out=y))
+        t_inv = float(np.mean(per_shape[(N, K)]))
         best = None
         for s in (2, 4, 8, 16):
             ws = torch.empty(B * N * s * 4, dtype=torch.uint8, device=dev)
-            t = _time(torch, lambda: bi.matmul_split(x, w, s, True, out=y, ws=ws))
+            it = iter(range(1 << 30))
+            t = _time(torch, lambda: bi.matmul_split(x, ws_list[next(it) % len(ws_list)], s, True, out=y, ws=ws))
             if best is None or t < best[1]:
                 best = (s, t)
-        res[f"{N}x{K}"] = {"invariant_us": round(t_inv * 1e3, 1), "best_split": best[0],
-                           "split_us": round(best[1] * 1e3, 1), "overhead": round(t_inv / best[1] - 1, 3),
-                           "invariant_gbs": round(2 * (N * K + B * K + B * N) / (t_inv * 1e-3) / 1e9, 1)}
+        res[f"{B}x{N}x{K}"] = {"invariant_us": round(t_inv * 1e3, 1), "best_split": best[0],
+                               "split_us": round(best[1] * 1e3, 1), "overhead": round(t_inv / best[1] - 1, 3)}
     return res
 
 

@@ -68,6 +68,10 @@ __device__ inline uint4 load_chunk(const typename S::store_t *row, int64_t k, in
     return r;
 }
 
+// Index of the calling wavefront within its workgroup, as a scalar (the
+// compiler then treats loops and branches that depend on it as uniform).
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline bool host_aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }

@@ -151,7 +151,7 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
     constexpr int P = kQWaves;
     constexpr int TR = MT * 16, TC = NS * 16;
     __shared__ float red[P][TR][TC + 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int64_t n0 = (int64_t)blockIdx.x * TC;
     const int64_t m0 = (int64_t)blockIdx.y * TR;

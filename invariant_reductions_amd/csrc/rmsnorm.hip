@@ -98,7 +98,7 @@ void rmsnorm_kernel(const typename S::store_t *__restrict__ x, const typename S:
 {
     constexpr int E = S::kElemsPer16B;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kNormRowsPerBlock + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * kNormRowsPerBlock + wave_id();
     if (row >= rows) return;
     const typename S::store_t *xr = x + row * H;
     typename S::store_t *yr = y + row * H;
@@ -159,7 +159,7 @@ void rmsnorm_split_finish(const typename S::store_t *__restrict__ x, const typen
 {
     constexpr int E = S::kElemsPer16B;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kNormRowsPerBlock + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * kNormRowsPerBlock + wave_id();
     if (row >= rows) return;
     float ss = part[row * splits];
     for (int s = 1; s < splits; ++s) ss = ss + part[row * splits + s];

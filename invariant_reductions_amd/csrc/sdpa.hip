@@ -89,7 +89,7 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
     PTile *pl = reinterpret_cast<PTile *>(lds);
     OTile *ol = reinterpret_cast<OTile *>(lds + sizeof(PTile) * kAttnWaves);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int g4 = lane >> 4, c16 = lane & 15;
     const int64_t c = blockIdx.x;
     const int hk = blockIdx.y;
