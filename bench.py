@@ -179,7 +179,7 @@ def main():
                    "batch": B, "context": ctx, "layers": cfg["n_layers"]},
         "tflops": round(tr["total_flops"] / (ms_step * 1e-3) / 1e12, 3),
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
-        "roofline": {"kernel": "bi_matmul -> dense_stream_kernel<bf16, MT, NS> (every instantiation the step "
+        "roofline": {"kernel": "bi_matmul_ws -> dense_slots_kernel<bf16, MT, Q> (every instantiation the step "
                                "launches; achieved = all matmul algorithmic bytes / all matmul launch time)",
                      "bound": "hbm",
                      "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -90,6 +90,31 @@ bi_status bi_matmul(const void *x, const void *w, void *y,
                     int32_t dtype, int32_t w_transposed, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Dense matmul with a caller workspace: bitwise the same y as bi_matmul.
+ * Same source as bi_matmul.  The reduction tree of every output is bi_matmul's
+ * (K blocks of 128 in eight slots, block b in slot b mod 8, each slot summed
+ * in ascending block order, the slots added pairwise).  For M <= 64 with
+ * transposed 16-bit weights, K a multiple of 128 and 16-byte aligned x, w and
+ * workspace, the slots of one output may be computed by different workgroups;
+ * the partial sums of aligned slot groups meet in the workspace and are added
+ * in the fixed tree order by whichever workgroup finishes last.  Every other
+ * call runs bi_matmul's kernels.
+ *   ws, ws_bytes: device memory of at least
+ *     bi_matmul_ws_workspace_bytes(M, N, K, dtype, w_transposed) bytes
+ *     (0 means no workspace is needed and ws may be NULL), 16-byte aligned,
+ *     filled with zero bytes before its first use.  Its first 64 KiB hold
+ *     per-column-tile counters that every call leaves at zero again, so one
+ *     workspace sized for the largest shape serves calls of any shape.
+ *     Calls that share a workspace must be ordered (same stream or
+ *     synchronised); concurrent ones race.
+ *   Errors: as bi_matmul, plus BI_ERR_WORKSPACE when ws is NULL or too small
+ *   and BI_ERR_ALIGN when ws is misaligned.
+ * ------------------------------------------------------------------------ */
+size_t bi_matmul_ws_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t w_transposed);
+bi_status bi_matmul_ws(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
+                       int32_t dtype, int32_t w_transposed, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Group-quantized 4-bit matmul   y = x @ dequantize(W)^T
  * Source: "Fix fp quantized matmul corruption when the quantized dim is not a
  * multiple of 32", Problem (reference x @ dequantize(w).T; nvfp4 group size

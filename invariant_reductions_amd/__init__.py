@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "BIError", "library_path", "lib", "build_info",
-    "matmul", "qmatmul", "rmsnorm", "sdpa", "sdpa_workspace_bytes",
+    "matmul", "matmul_ws", "matmul_workspace", "qmatmul", "rmsnorm", "sdpa", "sdpa_workspace_bytes",
     "matmul_split", "rmsnorm_split",
     "embed", "rope_kv_write", "silu_mul", "add", "argmax",
     "BF16", "F16", "F32", "AFFINE", "NVFP4",
@@ -67,6 +67,7 @@ def lib():
             "bi_add": [P, P, P, I64, P],
             "bi_argmax": [P, P, I64, I64, P],
             "bi_matmul_split": [P, P, P, I64, I64, I64, I32, I32, I32, P, SZ, P],
+            "bi_matmul_ws": [P, P, P, I64, I64, I64, I32, I32, P, SZ, P],
             "bi_rmsnorm_split": [P, P, P, I64, I64, F, I32, I32, P, SZ, P],
         }
         for name, args in sig.items():
@@ -75,6 +76,8 @@ def lib():
             fn.restype = ctypes.c_int32
         L.bi_sdpa_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
         L.bi_sdpa_workspace_bytes.restype = SZ
+        L.bi_matmul_ws_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
+        L.bi_matmul_ws_workspace_bytes.restype = SZ
         L.bi_matmul_split_workspace_bytes.argtypes = [I64, I64, I32]
         L.bi_matmul_split_workspace_bytes.restype = SZ
         L.bi_rmsnorm_split_workspace_bytes.argtypes = [I64, I32]
@@ -145,6 +148,28 @@ def matmul(x: torch.Tensor, w: torch.Tensor, transposed: bool = True, out=None, 
     y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
     _check(lib().bi_matmul(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dt(x), int(transposed), _stream(stream)),
            "bi_matmul")
+    return y
+
+
+def matmul_workspace(M: int, N: int, K: int, dtype=torch.bfloat16, transposed: bool = True, device=None):
+    """A zero-filled workspace for `matmul_ws` at this shape (a 16-byte
+    placeholder when the shape needs none)."""
+    need = lib().bi_matmul_ws_workspace_bytes(M, N, K, _TORCH_DT[dtype], int(transposed))
+    return torch.zeros(max(int(need), 16), dtype=torch.uint8, device=device)
+
+
+def matmul_ws(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, transposed: bool = True, out=None, stream=None):
+    """Same bits as `matmul`; `ws` from `matmul_workspace` (or any zero-filled
+    buffer of at least the workspace size), reused across calls in stream
+    order."""
+    _dev(x, w, out, ws)
+    M, K = x.shape
+    N = w.shape[0] if transposed else w.shape[1]
+    if (w.shape[1] if transposed else w.shape[0]) != K or w.dtype != x.dtype:
+        raise ValueError("matmul_ws: shape/dtype mismatch")
+    y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(lib().bi_matmul_ws(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dt(x), int(transposed), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "bi_matmul_ws")
     return y
 
 

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "bi.h"
 
 namespace bi {
@@ -66,6 +68,18 @@ __device__ inline uint4 load_chunk(const typename S::store_t *row, int64_t k, in
         r = __builtin_bit_cast(uint4, tmp);
     }
     return r;
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = B .. E-1: the index is a
+// compile-time constant inside f, so register arrays indexed by it stay in
+// registers.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // Index of the calling wavefront within its workgroup, as a scalar (the

@@ -10,30 +10,47 @@
 //
 // Reduction tree of one output y[m,n] (frozen; depends on K only):
 //   * K is cut into blocks of KB elements (128 for bf16/f16, 16 for f32);
-//     block b is reduced by wave (b mod P) of the workgroup, P = kDenseWaves.
+//     block b belongs to slot (b mod P), P = kDenseWaves = 8.
 //   * Inside a block, four MFMA steps (v_mfma_f32_16x16x32_{bf16,f16} or
 //     v_mfma_f32_16x16x4_f32) consume the block.  16-bit types: step s takes
 //     elements [32s, 32s + 32) of the block, lane group g (lanes 16g..16g+15)
 //     the 8 at 32s + 8g, so every load instruction reads 64 contiguous bytes
 //     of each row.  f32: lane group g holds the 4 elements at 4g and step s
-//     takes the s-th of them.  A wave accumulates its blocks in ascending order
-//     in the MFMA accumulator.
-//   * The P wave partials are added in wave order 0..P-1 in fp32, then rounded
-//     to the output type (RNE).
+//     takes the s-th of them.  A slot's blocks are accumulated in ascending
+//     order in one MFMA accumulator (one wave owns the slot).
+//   * The P slot partials are added pairwise in fp32,
+//     ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)), then rounded to the
+//     output type (RNE).
 // Row m of the output only ever meets row m of x inside an MFMA, so the M-tile
 // it falls in, the other rows of that tile, the number of M-tiles and the
 // N-tile width (all chosen from the shape) leave its bits unchanged.  M = 1 is
-// the same MFMA with fifteen zero rows.
+// the same MFMA with fifteen padding rows.  Which workgroup owns a slot (all
+// eight in one workgroup, or spread over several with the partials of each
+// aligned slot group combined through a workspace) is a launch choice that
+// the tree does not see.
 #include "common.hpp"
 
 namespace bi {
 
-constexpr int kDenseWaves = 8;   // P: K-block owners per output tile (frozen)
+constexpr int kDenseWaves = 8;   // P: K-block slots per output (frozen)
+
+// The frozen combine of the P = 8 slot partials, pairwise:
+//   ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)).
+// Every aligned group of 1, 2, 4 or 8 consecutive slots is a subtree of it, so
+// a workgroup that owns such a group may add its own slots first.
+template <typename F>
+__device__ inline float slot_tree(F p)
+{
+    return ((p(0) + p(1)) + (p(2) + p(3))) + ((p(4) + p(5)) + (p(6) + p(7)));
+}
 
 template <typename S> struct DenseMfma;
 
 template <> struct DenseMfma<BF16> {
     static constexpr int CPB = 4;                 // 16-byte chunks per lane per block
+    __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
     __device__ static f32x4 step(const uint4 *a, const uint4 *b, int s, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s]),
                                                        __builtin_bit_cast(bf16x8, b[s]), c, 0, 0, 0);
@@ -41,6 +58,9 @@ template <> struct DenseMfma<BF16> {
 };
 template <> struct DenseMfma<F16> {
     static constexpr int CPB = 4;
+    __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
     __device__ static f32x4 step(const uint4 *a, const uint4 *b, int s, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[s]),
                                                       __builtin_bit_cast(f16x8, b[s]), c, 0, 0, 0);
@@ -232,9 +252,7 @@ void dense_kernel(const typename S::store_t *__restrict__ x, const typename S::s
         const int r = o / TC, cc = o % TC;
         const int64_t row = m0 + r, col = n0 + cc;
         if (row >= M || col >= N) continue;
-        float v = red[0][r][cc];
-#pragma unroll
-        for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+        const float v = slot_tree([&](int p) { return red[p][r][cc]; });
         if (PART) part[((int64_t)blockIdx.z * M + row) * N + col] = v;
         else y[row * N + col] = S::narrow(v);
     }
@@ -247,7 +265,7 @@ void dense_kernel(const typename S::store_t *__restrict__ x, const typename S::s
 // that runs across tile boundaries, so the loads of the next tile are in
 // flight while the current tile's eight partials are combined.  Per output
 // the tree is exactly that of dense_kernel: block b of K belongs to wave
-// b mod P, accumulated in ascending order, partials added in wave order.
+// b mod P, accumulated in ascending order, partials added by slot_tree.
 template <typename S, int MT, int NS>
 __global__ __launch_bounds__(kDenseWaves * kWave, (MT >= 4 && NS >= 2) ? 2 : 4)
 void dense_stream_kernel(const typename S::store_t *__restrict__ x, const typename S::store_t *__restrict__ w,
@@ -263,33 +281,37 @@ void dense_stream_kernel(const typename S::store_t *__restrict__ x, const typena
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
-    const int64_t nb = K / G::KB;                                  // every block is full here
-    const int64_t nmine = wave < nb ? (nb - wave + P - 1) / P : 0; // blocks of this wave per tile
-    const int64_t ntiles = ntm * ntn;
-    const int64_t mytiles = blockIdx.x < ntiles ? (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
-    const int64_t items = mytiles * nmine;
+    const int nb = (int)(K / G::KB);                               // every block is full here
+    const int nmine = wave < nb ? (nb - wave + P - 1) / P : 0;     // blocks of this wave per tile
+    const int ntiles = (int)(ntm * ntn);
+    const int mytiles = (int)blockIdx.x < ntiles ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    const int items = mytiles * nmine;
 
     // tile u of this workgroup -> (row tile, column tile).  Tiles are walked in
     // groups of up to 64 row tiles, row tile fastest, so the workgroups in
     // flight at any time share a few column tiles of W and a group's rows of x
     // stay cache-resident while W streams past (only matters for large M).
-    auto tile_of = [&](int64_t u, int64_t &tm, int64_t &tn) {
-        constexpr int64_t GM = 64;
-        const int64_t t = blockIdx.x + u * gridDim.x;
-        const int64_t grp = t / (GM * ntn), r = t % (GM * ntn);
-        const int64_t gm = ntm - grp * GM < GM ? ntm - grp * GM : GM;
-        tm = grp * GM + r % gm;
+    // 32-bit arithmetic, evaluated once per tile.
+    auto tile_of = [&](int u, int &tm, int &tn) {
+        constexpr int GM = 64;
+        const int t = (int)blockIdx.x + u * (int)gridDim.x;
+        const int gsz = GM * (int)ntn;
+        const int grp = t / gsz, r = t - grp * gsz;
+        const int gm = (int)ntm - grp * GM < GM ? (int)ntm - grp * GM : GM;
         tn = r / gm;
+        tm = grp * GM + (r - tn * gm);
     };
 
     uint4 Ab[DEPTH][MT][G::CPB], Bb[DEPTH][NS][G::CPB];
-    auto load_item = [&](uint4 (&A)[MT][G::CPB], uint4 (&B)[NS][G::CPB], int64_t it) {
-        int64_t tm, tn;
-        tile_of(it / nmine, tm, tn);
-        const int64_t kblk = (wave + (it % nmine) * P) * G::KB;
+    // Prefetch cursor: item (pu, pj) = block wave + pj*P of tile pu; it walks the
+    // items in order and holds at the last one (the ring's final re-reads).
+    int pu = 0, pj = 0, ptm = 0, ptn = 0;
+    if (items > 0) tile_of(0, ptm, ptn);
+    auto load_next = [&](uint4 (&A)[MT][G::CPB], uint4 (&B)[NS][G::CPB]) {
+        const int64_t kblk = (int64_t)(wave + pj * P) * G::KB;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            int64_t n = tn * TC + j * 16 + c;
+            int64_t n = (int64_t)ptn * TC + j * 16 + c;
             n = n < N ? n : N - 1;                                // padding columns read a real row
             const T *wr = w + n * K + kblk;
 #pragma unroll
@@ -297,11 +319,19 @@ void dense_stream_kernel(const typename S::store_t *__restrict__ x, const typena
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-            int64_t r = tm * TR + i * 16 + c;
+            int64_t r = (int64_t)ptm * TR + i * 16 + c;
             r = r < M ? r : M - 1;
             const T *xr = x + r * K + kblk;
 #pragma unroll
             for (int ci = 0; ci < G::CPB; ++ci) A[i][ci] = *reinterpret_cast<const uint4 *>(xr + G::chunk_off(g, ci));
+        }
+        // advance (wave-uniform scalars)
+        if (pj + 1 < nmine) {
+            ++pj;
+        } else if (pu + 1 < mytiles) {
+            pj = 0;
+            ++pu;
+            tile_of(pu, ptm, ptn);
         }
     };
 
@@ -311,7 +341,7 @@ void dense_stream_kernel(const typename S::store_t *__restrict__ x, const typena
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto finish_tile = [&](int64_t u) {
+    auto finish_tile = [&](int u) {
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -321,29 +351,27 @@ void dense_stream_kernel(const typename S::store_t *__restrict__ x, const typena
                 acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         __syncthreads();
-        int64_t tm, tn;
+        int tm, tn;
         tile_of(u, tm, tn);
         for (int o = threadIdx.x; o < TR * TC; o += P * kWave) {
             const int r = o / TC, cc = o % TC;
-            const int64_t row = tm * TR + r, col = tn * TC + cc;
+            const int64_t row = (int64_t)tm * TR + r, col = (int64_t)tn * TC + cc;
             if (row >= M || col >= N) continue;
-            float v = red[0][r][cc];
-#pragma unroll
-            for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+            const float v = slot_tree([&](int p) { return red[p][r][cc]; });
             y[row * N + col] = S::narrow(v);
         }
         __syncthreads();
     };
 
     if (items > 0) {
-        const int64_t last = items - 1;
+        // compute cursor: tile cu, block cj within it
+        int cu = 0, cj = 0;
 #pragma unroll
-        for (int d = 0; d < DEPTH - 1; ++d) load_item(Ab[d], Bb[d], d < last ? d : last);
-        for (int64_t i = 0; i < items; i += DEPTH) {
+        for (int d = 0; d < DEPTH - 1; ++d) load_next(Ab[d], Bb[d]);
+        for (int i = 0; i < items; i += DEPTH) {
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d) {
-                const int64_t li = i + d + DEPTH - 1;
-                load_item(Ab[(d + DEPTH - 1) % DEPTH], Bb[(d + DEPTH - 1) % DEPTH], li < last ? li : last);
+                load_next(Ab[(d + DEPTH - 1) % DEPTH], Bb[(d + DEPTH - 1) % DEPTH]);
                 __builtin_amdgcn_sched_barrier(0);
                 if (i + d < items) {
 #pragma unroll
@@ -353,14 +381,18 @@ void dense_stream_kernel(const typename S::store_t *__restrict__ x, const typena
 #pragma unroll
                             for (int b2 = 0; b2 < NS; ++b2)
                                 acc[a][b2] = DenseMfma<S>::step(Ab[d][a], Bb[d][b2], s, acc[a][b2]);
-                    if ((i + d) % nmine == nmine - 1) finish_tile((i + d) / nmine);
+                    if (++cj == nmine) {
+                        finish_tile(cu);
+                        cj = 0;
+                        ++cu;
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     } else {
         // a wave that owns no block of K still takes part in every combine
-        for (int64_t u = 0; u < mytiles; ++u) finish_tile(u);
+        for (int u = 0; u < mytiles; ++u) finish_tile(u);
     }
 }
 
@@ -447,6 +479,268 @@ static bool try_launch_stream(const void *x, const void *w, void *y, int64_t M, 
     return true;
 }
 
+// ---------------------------------------------------------------------------
+// Slot-group form for short M (at most 64 rows): transposed W, 16-bit types,
+// K a multiple of the block, x and W 16-byte aligned.
+//
+// Workgroup (ct, grp) owns the 128 output columns of tile ct (wave v: columns
+// 16v .. 16v + 15) and the Q consecutive slots grp*Q .. grp*Q + Q - 1.  It
+// walks its blocks as items u -> (step j = u / Q, slot grp*Q + u % Q), i.e.
+// block 8j + grp*Q + u % Q.  Each block of x (all rows of the M tile) is
+// staged once in LDS and read by all eight waves; each wave streams its 16
+// rows of W through a register ring.  Slot i of the group accumulates in its
+// own MFMA accumulator, block by block in ascending order, exactly as a wave
+// of the kernels above does, and the Q slot partials are added by their
+// subtree of slot_tree.  With 8/Q > 1 groups per tile, each group writes that
+// sum to the workspace; the last workgroup of the tile to arrive (counted with
+// a device-scope atomic) reads all group sums, adds them by the rest of
+// slot_tree and stores y.  Arrival order decides only who adds, never how.
+template <typename S, int MT, int Q>
+__global__ __launch_bounds__(kDenseWaves * kWave, 2)
+void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typename S::store_t *__restrict__ w,
+                        typename S::store_t *__restrict__ y, float *__restrict__ part,
+                        unsigned *__restrict__ counters, int64_t M, int64_t N, int64_t K)
+{
+    using G = DenseGeom<S>;
+    using T = typename S::store_t;
+    constexpr int P = kDenseWaves, NT = P * kWave;
+    constexpr int GRP = P / Q;                     // slot groups per column tile
+    constexpr int TR = MT * 16, KB = G::KB;
+    constexpr int XS = KB + 8;                     // LDS row stride: 272 bytes, 16-byte aligned, 4-bank shift per row
+    constexpr int XCH = TR * (KB / 8);             // 16-byte chunks in one block of x
+    constexpr int XPT = XCH > NT ? XCH / NT : 1;   // chunks staged per thread
+    constexpr int DX = 3, DW = 4;                  // x and W register ring depths
+    constexpr int U = Q <= 4 ? 12 : 24;            // unroll: a multiple of 3 (LDS ring), DX, DW and Q
+    static_assert(G::CPB == 4 && XPT <= 2 && (XCH % NT == 0 || XPT == 1), "slot kernel geometry");
+    __shared__ __attribute__((aligned(16))) T xs[3][TR][XS];
+    __shared__ int s_last;
+
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    const int ct = blockIdx.x, grp = blockIdx.y;
+    const int nb = (int)(K / KB);
+    const int slot0 = grp * Q;
+    const int nsteps = slot0 < nb ? (nb - slot0 + P - 1) / P : 0;
+    const int nitems = nsteps * Q;
+    // Block of item u.  Items past the last block re-read block slot0 (valid
+    // whenever nitems > 0) and are never multiplied.
+    auto block_of = [&](int u) {
+        const int b = (u / Q) * P + slot0 + (u % Q);
+        return b < nb ? b : slot0;
+    };
+
+    const int64_t n = (int64_t)ct * (P * 16) + wave * 16 + c;
+    const bool nok = n < N;
+    const T *wr = w + (nok ? n : N - 1) * K;     // padding columns read a real row, never stored
+    const int t = threadIdx.x, xc = t & 15;
+
+    struct XChunks { uint4 v0, v1; };
+    XChunks xr0, xr1, xr2;
+    auto xreg = [&](auto sc) -> XChunks & {
+        constexpr int sl = decltype(sc)::value % DX;
+        if constexpr (sl == 0) return xr0;
+        else if constexpr (sl == 1) return xr1;
+        else return xr2;
+    };
+    // thread t stages chunk (t + h*NT) mod XCH of the block: row / 16, 16 bytes at (chunk % 16) * 16
+    auto load_x = [&](XChunks &r, int u) {
+        const int64_t kb = (int64_t)block_of(u) * KB + xc * 8;
+        static_for<0, XPT>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const int row = ((t + h * NT) % XCH) >> 4;
+            const uint4 v = *reinterpret_cast<const uint4 *>(x + (int64_t)(row < M ? row : M - 1) * K + kb);
+            if constexpr (h == 0) r.v0 = v;
+            else r.v1 = v;
+        });
+    };
+    auto store_x = [&](const XChunks &r, int buf) {
+        static_for<0, XPT>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const int row = ((t + h * NT) % XCH) >> 4;
+            *reinterpret_cast<uint4 *>(&xs[buf][row][xc * 8]) = h == 0 ? r.v0 : r.v1;
+        });
+    };
+    uint4 wb[DW][G::CPB];
+    auto load_w = [&](uint4 (&B)[G::CPB], int u) {
+        const T *p = wr + (int64_t)block_of(u) * KB;
+#pragma unroll
+        for (int ci = 0; ci < G::CPB; ++ci) B[ci] = *reinterpret_cast<const uint4 *>(p + G::chunk_off(g, ci));
+    };
+
+    f32x4 acc[Q][MT];
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (nitems > 0) {
+        // Pipeline: x of item u + 1 goes to LDS slot (u + 1) % 3 at item u (its
+        // register slot is refilled with item u + 1 + DX); W runs DW - 1 items
+        // ahead.  Three LDS slots let one barrier per item separate the writers
+        // of slot (u + 1) % 3 from the last readers of that slot (item u - 2).
+        static_for<0, DX>([&](auto dc) { load_x(xreg(dc), decltype(dc)::value); });
+        store_x(xr0, 0);
+        load_x(xr0, DX);
+        static_for<0, DW - 1>([&](auto dc) { load_w(wb[decltype(dc)::value], decltype(dc)::value); });
+        // One item: stage x of item u + 1, refill the rings, wait for the
+        // workgroup, multiply item u (unless it lies past the last block).
+        auto item = [&](auto dc, int u) {
+            constexpr int d = decltype(dc)::value;
+            XChunks &nx = xreg(std::integral_constant<int, d + 1>{});
+            store_x(nx, (d + 1) % 3);
+            load_x(nx, u + 1 + DX);
+            load_w(wb[(d + DW - 1) % DW], u + DW - 1);
+            __syncthreads();
+            if ((u / Q) * P + slot0 + (d % Q) < nb) {
+                uint4 a[4][MT];
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        a[st][m] = *reinterpret_cast<const uint4 *>(&xs[d % 3][m * 16 + c][G::chunk_off(g, st)]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) acc[d % Q][m] = DenseMfma<S>::mma(a[st][m], wb[d % DW][st], acc[d % Q][m]);
+            }
+        };
+        // Whole unrolled rounds run without item guards (exact load waits);
+        // the last partial round is guarded.
+        int u0 = 0;
+        for (; u0 + U <= nitems; u0 += U) static_for<0, U>([&](auto dc) { item(dc, u0 + decltype(dc)::value); });
+        if (u0 < nitems)
+            static_for<0, U>([&](auto dc) {
+                if (u0 + decltype(dc)::value < nitems) item(dc, u0 + decltype(dc)::value);
+            });
+    }
+
+    // the group's subtree of slot_tree
+    f32x4 h[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        if constexpr (Q == 1) h[m] = acc[0][m];
+        else if constexpr (Q == 2) h[m] = acc[0][m] + acc[1][m];
+        else if constexpr (Q == 4) h[m] = (acc[0][m] + acc[1][m]) + (acc[2][m] + acc[3][m]);
+        else h[m] = ((acc[0][m] + acc[1][m]) + (acc[2][m] + acc[3][m])) + ((acc[4][m] + acc[5][m]) + (acc[6][m] + acc[7][m]));
+    }
+    // MFMA accumulator layout: lane (g, c), register r holds row 4g + r, column c.
+    auto store_y = [&](const f32x4 (&v)[MT]) {
+        if (!nok) return;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m * 16 + g * 4 + r;
+                if (row < M) y[row * N + n] = S::narrow(v[m][r]);
+            }
+    };
+    if constexpr (GRP == 1) {
+        store_y(h);
+    } else {
+        // group sum -> workspace, one contiguous 64-lane record per (register, wave)
+        constexpr int REC = MT * 4 * kWave;
+        float *base = part + (int64_t)ct * GRP * P * REC;
+        float *mine = base + ((int64_t)grp * P + wave) * REC;
+        // The group sums are written and read with device-scope accesses (they
+        // go through to the level all CUs share), so no cache-wide write-back
+        // or invalidate is needed: the barrier waits for this workgroup's
+        // stores to complete before thread 0 bumps the tile's counter, and the
+        // last workgroup reads the sums only after it has seen the count.
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __hip_atomic_store(&mine[(m * 4 + r) * kWave + lane], h[m][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);             // every store of this wave acknowledged
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(&counters[ct], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = prev == (unsigned)(GRP - 1);
+        }
+        __syncthreads();
+        if (!s_last) return;
+        if (threadIdx.x == 0) __hip_atomic_store(&counters[ct], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        f32x4 out[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            f32x4 v[GRP];
+#pragma unroll
+            for (int q = 0; q < GRP; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[q][r] = __hip_atomic_load(base + ((int64_t)q * P + wave) * REC + (m * 4 + r) * kWave + lane,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if constexpr (GRP == 2) out[m] = v[0] + v[1];
+            else if constexpr (GRP == 4) out[m] = (v[0] + v[1]) + (v[2] + v[3]);
+            else out[m] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+        }
+        store_y(out);
+    }
+}
+
+// Workspace of the slot-group form: a fixed counter area (one counter per
+// column tile, room for kSlotMaxTiles tiles, left zero by every call) followed
+// by the group sums.  The counter area has the same place and size for every
+// shape, so the group sums of one call never land on the counters of another
+// call that shares the workspace.
+constexpr int64_t kSlotTileCols = kDenseWaves * 16;
+constexpr int64_t kSlotMaxTiles = 16384;                    // N up to 2^21 columns
+constexpr size_t kSlotCounterBytes = kSlotMaxTiles * sizeof(unsigned);
+
+static int slot_mt(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
+static size_t slot_ws_bytes(int64_t M, int64_t N, int groups)
+{
+    const int64_t rec = (int64_t)slot_mt(M) * 4 * kWave * (int64_t)sizeof(float);
+    return kSlotCounterBytes + (size_t)(cdiv(N, kSlotTileCols) * groups * kDenseWaves * rec);
+}
+
+template <typename S, int MT, int Q>
+static void launch_slots_t(const void *x, const void *w, void *y, void *ws, int64_t M, int64_t N, int64_t K,
+                           hipStream_t st)
+{
+    using T = typename S::store_t;
+    const int64_t ntc = cdiv(N, kSlotTileCols);
+    unsigned *counters = (unsigned *)ws;
+    float *part = (float *)((char *)ws + kSlotCounterBytes);
+    hipLaunchKernelGGL((dense_slots_kernel<S, MT, Q>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
+                       dim3(kDenseWaves * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, counters, M, N, K);
+}
+
+// Slots per workgroup: the largest group that still gives at least one
+// workgroup per CU (MT = 4 keeps at most four slots in registers).
+template <typename S, int MT>
+static void launch_slots_mt(const void *x, const void *w, void *y, void *ws, int64_t M, int64_t N, int64_t K,
+                            hipStream_t st)
+{
+    const int64_t ntc = cdiv(N, kSlotTileCols), cu = device_cu_count();
+    if constexpr (MT < 4) {
+        if (ntc >= cu) {
+            launch_slots_t<S, MT, 8>(x, w, y, ws, M, N, K, st);
+            return;
+        }
+    }
+    if (ntc * 2 >= cu) launch_slots_t<S, MT, 4>(x, w, y, ws, M, N, K, st);
+    else if (ntc * 4 >= cu) launch_slots_t<S, MT, 2>(x, w, y, ws, M, N, K, st);
+    else launch_slots_t<S, MT, 1>(x, w, y, ws, M, N, K, st);
+}
+
+template <typename S>
+static bool try_launch_slots(const void *x, const void *w, void *y, void *ws, size_t ws_bytes, int64_t M,
+                             int64_t N, int64_t K, hipStream_t st)
+{
+    using G = DenseGeom<S>;
+    if (!ws || M > 64 || K % G::KB != 0 || !host_aligned16(x) || !host_aligned16(w) || !host_aligned16(ws))
+        return false;
+    if (ws_bytes < slot_ws_bytes(M, N, kDenseWaves)) return false;
+    const int mt = slot_mt(M);
+    if (mt == 1) launch_slots_mt<S, 1>(x, w, y, ws, M, N, K, st);
+    else if (mt == 2) launch_slots_mt<S, 2>(x, w, y, ws, M, N, K, st);
+    else launch_slots_mt<S, 4>(x, w, y, ws, M, N, K, st);
+    return true;
+}
+
 template <typename S>
 static void launch_dense(const void *x, const void *w, void *y, float *part, int64_t M, int64_t N,
                          int64_t K, bool trans, int splits, hipStream_t st)
@@ -495,6 +789,32 @@ extern "C" bi_status bi_matmul(const void *x, const void *w, void *y, int64_t M,
     if (s != BI_OK) return s;
     (void)hipGetLastError();
     dispatch_dense(x, w, y, nullptr, M, N, K, dtype, w_transposed != 0, 1, stream);
+    return launch_status();
+}
+
+extern "C" size_t bi_matmul_ws_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t w_transposed)
+{
+    if (M < 1 || N < 1 || K < 1 || M > 64 || !w_transposed || (dtype != BI_BF16 && dtype != BI_F16) ||
+        cdiv(N, kSlotTileCols) > kSlotMaxTiles)
+        return 0;
+    return slot_ws_bytes(M, N, kDenseWaves);
+}
+
+extern "C" bi_status bi_matmul_ws(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
+                                  int32_t dtype, int32_t w_transposed, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    bi_status s = check_dense(x, w, y, M, N, K, dtype);
+    if (s != BI_OK) return s;
+    const size_t need = bi_matmul_ws_workspace_bytes(M, N, K, dtype, w_transposed);
+    if (need > 0 && (!ws || ws_bytes < need)) return BI_ERR_WORKSPACE;
+    if (need > 0 && !host_aligned16(ws)) return BI_ERR_ALIGN;
+    (void)hipGetLastError();
+    bool done = false;
+    if (need > 0) {
+        if (dtype == BI_BF16) done = try_launch_slots<BF16>(x, w, y, ws, ws_bytes, M, N, K, stream);
+        else done = try_launch_slots<F16>(x, w, y, ws, ws_bytes, M, N, K, stream);
+    }
+    if (!done) dispatch_dense(x, w, y, nullptr, M, N, K, dtype, w_transposed != 0, 1, stream);
     return launch_status();
 }
 

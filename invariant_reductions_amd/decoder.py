@@ -24,7 +24,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (add, argmax, embed, matmul, rmsnorm, rope_kv_write, sdpa, sdpa_workspace_bytes, silu_mul)
+from . import (add, argmax, embed, lib, matmul_ws, rmsnorm, rope_kv_write, sdpa, sdpa_workspace_bytes, silu_mul)
 from .inputs import rope_tables
 
 
@@ -66,6 +66,10 @@ class Decoder:
         self.kv_len = torch.zeros(max_batch, dtype=torch.int32, device=d)
         ws = sdpa_workspace_bytes(max_batch, max_q, max_len, self.Hq, self.D)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=d)
+        # one zero-filled matmul workspace for every projection (calls are stream-ordered)
+        mshapes = [(self.qkvn, self.H), (self.H, self.qn), (2 * self.F, self.H), (self.H, self.F), (self.V, self.H)]
+        need = max(lib().bi_matmul_ws_workspace_bytes(min(T, 64), n, k, 0, 1) for n, k in mshapes)
+        self.mws = torch.zeros(max(int(need), 16), dtype=torch.uint8, device=d)
 
     # -- one forward over Q new tokens of each of B sequences -----------------
     def forward(self, B: int, Q: int, max_kv: int):
@@ -81,20 +85,20 @@ class Decoder:
         scale = 1.0 / float(np.sqrt(self.D))
         for li, Lw in enumerate(self.layers):
             rmsnorm(x, Lw["attn_norm"], self.eps, out=h)
-            matmul(h, Lw["wqkv"], True, out=qkv)
+            matmul_ws(h, Lw["wqkv"], self.mws, True, out=qkv)
             kc, vc = self.kc[li][:B], self.vc[li][:B]
             rope_kv_write(qkv, q, kc, vc, kv, self.cos_t, self.sin_t, B, Q, self.Hq, self.Hkv, self.D)
             sdpa(q.view(B, Q, self.Hq, self.D), kc, vc, kv, max_kv, scale, True,
                  out=o.view(B, Q, self.Hq, self.D), ws=self.ws)
-            matmul(o, Lw["wo"], True, out=t1)
+            matmul_ws(o, Lw["wo"], self.mws, True, out=t1)
             add(x, t1, out=x)
             rmsnorm(x, Lw["mlp_norm"], self.eps, out=h)
-            matmul(h, Lw["wgu"], True, out=gu)
+            matmul_ws(h, Lw["wgu"], self.mws, True, out=gu)
             silu_mul(gu, out=a)
-            matmul(a, Lw["wdown"], True, out=t1)
+            matmul_ws(a, Lw["wdown"], self.mws, True, out=t1)
             add(x, t1, out=x)
         rmsnorm(x, self.final_norm, self.eps, out=h)
-        matmul(h, self.lm_head, True, out=self.logits[:T])
+        matmul_ws(h, self.lm_head, self.mws, True, out=self.logits[:T])
         argmax(self.logits[:T], out=self.next_ids[:T])
         return self.logits[:T]
 
@@ -119,7 +123,8 @@ class Decoder:
         scale = ctypes.c_float(1.0 / float(np.sqrt(self.D)))
         eps = ctypes.c_float(self.eps)
         steps = [("embed", L.bi_embed, (p(self.ids), p(self.embed_w), p(x), T, self.V, H, st))]
-        mm = lambda xin, w, out, N, K: ("matmul", L.bi_matmul, (p(xin), p(w), p(out), T, N, K, 0, 1, st))
+        mws, mwsb = p(self.mws), self.mws.numel()
+        mm = lambda xin, w, out, N, K: ("matmul", L.bi_matmul_ws, (p(xin), p(w), p(out), T, N, K, 0, 1, mws, mwsb, st))
         for li, Lw in enumerate(self.layers):
             kc, vc = self.kc[li], self.vc[li]
             Lcap = kc.shape[1]
@@ -139,7 +144,7 @@ class Decoder:
                 ("add", L.bi_add, (p(x), p(t1), p(x), T * H, st)),
             ]
         steps += [("rmsnorm", L.bi_rmsnorm, (p(x), p(self.final_norm), p(h), T, H, eps, 0, st)),
-                  ("matmul", L.bi_matmul, (p(h), p(self.lm_head), p(self.logits), T, self.V, H, 0, 1, st)),
+                  mm(h, self.lm_head, self.logits, self.V, H),
                   ("argmax", L.bi_argmax, (p(self.logits), p(self.next_ids), T, self.V, st))]
         return steps
 

@@ -118,6 +118,26 @@ def test_split_variant_validation():
     assert L.bi_matmul_split_workspace_bytes(4, 512, 8) == 4 * 512 * 8 * 4
 
 
+def test_matmul_ws_validation_and_workspace_size():
+    """Workspace errors are reported before any launch; shapes that need no
+    workspace report 0 bytes."""
+    L = bi.lib()
+    need = L.bi_matmul_ws_workspace_bytes(64, 4096, 4096, 0, 1)
+    # fixed 64 KiB counter area + 32 column tiles x 8 groups x 8 waves x 4 KiB records
+    assert need == 65536 + 32 * 8 * 8 * 4 * 4 * 64 * 4
+    assert L.bi_matmul_ws_workspace_bytes(1, 4096, 4096, 0, 1) == 65536 + 32 * 8 * 8 * 1 * 4 * 64 * 4
+    assert L.bi_matmul_ws_workspace_bytes(64, 128 * 16385, 128, 0, 1) == 0   # beyond the counter area
+    assert L.bi_matmul_ws_workspace_bytes(65, 4096, 4096, 0, 1) == 0      # long M: bi_matmul's kernels
+    assert L.bi_matmul_ws_workspace_bytes(64, 4096, 4096, 2, 1) == 0      # f32
+    assert L.bi_matmul_ws_workspace_bytes(64, 4096, 4096, 0, 0) == 0      # natural layout
+    assert L.bi_matmul_ws(A, A, A, 64, 4096, 4096, 0, 1, None, 0, None) == WORKSPACE
+    assert L.bi_matmul_ws(A, A, A, 64, 4096, 4096, 0, 1, A, need - 1, None) == WORKSPACE
+    assert L.bi_matmul_ws(A, A, A, 64, 4096, 4096, 0, 1, P(0x10010 + 2), need, None) == ALIGN
+    assert L.bi_matmul_ws(ODD, A, A, 64, 4096, 4096, 0, 1, A, need, None) == ALIGN
+    assert L.bi_matmul_ws(A, A, A, 0, 4096, 4096, 0, 1, A, need, None) == SHAPE
+    assert L.bi_matmul_ws(A, A, A, 64, 4096, 4096, 7, 1, A, need, None) == DTYPE
+
+
 def test_glue_validation():
     L = bi.lib()
     assert L.bi_embed(None, A, A, 1, 10, 64, None) == NULL
