@@ -44,13 +44,14 @@ def step_traffic(cfg, B, ctx):
     mm.append((B, V, H))
     mm_bytes = sum(2 * (N * K + M * K + M * N) for M, N, K in mm)
     mm_flops = sum(2 * M * N * K for M, N, K in mm)
-    norm_bytes = (2 * L + 1) * (4 * B * H + 2 * H)
+    # one plain RMSNorm (x -> h), then 2L residual adds fused with the norm that
+    # follows them (x, r -> x, h)
+    norm_bytes = (4 * B * H + 2 * H) + 2 * L * (8 * B * H + 2 * H)
     attn_bytes = L * (4 * B * ctx * Hkv * D + 4 * B * Hq * D)
     attn_flops = L * 4 * B * Hq * D * ctx
     glue_bytes = (2 * B * H * 2                              # embed
                   + L * (2 * B * qkvn + 2 * B * Hq * D + 4 * B * Hkv * D)   # rope + cache write
                   + L * (2 * B * 2 * F + 2 * B * F)          # silu*mul
-                  + L * 2 * (3 * 2 * B * H)                  # residual adds
                   + 2 * B * V)                               # argmax
     return dict(mm=mm, mm_bytes=mm_bytes, mm_flops=mm_flops, norm_bytes=norm_bytes, attn_bytes=attn_bytes,
                 attn_flops=attn_flops, glue_bytes=glue_bytes,
@@ -226,7 +227,9 @@ def op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch):
         for name, s, t in row:
             tot[name] = tot.get(name, 0.0) + s.elapsed_time(t) / reps
     tr = step_traffic(cfg, B, ctx_mean)
-    bytes_of = {"matmul": tr["mm_bytes"], "sdpa": tr["attn_bytes"], "rmsnorm": tr["norm_bytes"]}
+    H, L = cfg["hidden"], cfg["n_layers"]
+    bytes_of = {"matmul": tr["mm_bytes"], "sdpa": tr["attn_bytes"], "rmsnorm": 4 * B * H + 2 * H,
+                "add_rmsnorm": 2 * L * (8 * B * H + 2 * H)}
     res = {}
     for name, ms in tot.items():
         r = {"us_per_step": round(ms * 1e3, 1)}

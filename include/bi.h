@@ -153,6 +153,20 @@ bi_status bi_rmsnorm(const void *x, const void *w, void *y, int64_t rows, int64_
                      float eps, int32_t dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Residual add fused with the RMSNorm that follows it in a pre-norm block:
+ *   x_out = RNE(x + r)          (the bits bi_add gives)
+ *   y     = bi_rmsnorm(x_out)   (the same tree, the same bits)
+ * Source: as bi_rmsnorm; "Batch-invariant kernels ...", Mental model
+ * (pointwise ops are invariant by construction, so fusing the add changes no
+ * reduction).
+ *   x, r, x_out, y : [rows, H] of `dtype`;  w : [H].  x_out may alias x
+ *   (in-place residual); y must not alias x, r or x_out.
+ *   Errors: as bi_rmsnorm (BI_ERR_NULL also for r or x_out).
+ * ------------------------------------------------------------------------ */
+bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *w, void *y,
+                         int64_t rows, int64_t H, float eps, int32_t dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Decode / verify scaled-dot-product attention (GQA), two passes.
  * Source: "Fix/speculative shape invariance", Problem and Changes (the
  * softmax reduction layout of a query must be the same alone or inside a

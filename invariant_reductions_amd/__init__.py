@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "BIError", "library_path", "lib", "build_info",
-    "matmul", "matmul_ws", "matmul_workspace", "qmatmul", "rmsnorm", "sdpa", "sdpa_workspace_bytes",
+    "matmul", "matmul_ws", "matmul_workspace", "qmatmul", "rmsnorm", "add_rmsnorm", "sdpa", "sdpa_workspace_bytes",
     "matmul_split", "rmsnorm_split",
     "embed", "rope_kv_write", "silu_mul", "add", "argmax",
     "BF16", "F16", "F32", "AFFINE", "NVFP4",
@@ -60,6 +60,7 @@ def lib():
             "bi_matmul": [P, P, P, I64, I64, I64, I32, I32, P],
             "bi_qmatmul": [P, P, P, P, P, I64, I64, I64, I32, I32, I32, I32, P],
             "bi_rmsnorm": [P, P, P, I64, I64, F, I32, P],
+            "bi_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I32, P],
             "bi_sdpa": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, P, SZ, P],
             "bi_embed": [P, P, P, I64, I64, I64, P],
             "bi_rope_kv_write": [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, I64, P],
@@ -209,6 +210,17 @@ def rmsnorm(x, w, eps: float = 1e-6, out=None, stream=None):
     y = out if out is not None else torch.empty_like(x)
     _check(lib().bi_rmsnorm(_ptr(x), _ptr(w), _ptr(y), rows, H, eps, _dt(x), _stream(stream)), "bi_rmsnorm")
     return y
+
+
+def add_rmsnorm(x, r, w, eps: float = 1e-6, x_out=None, out=None, stream=None):
+    """x_out = x + r (rounded as `add`), out = rmsnorm(x_out); x_out may be x."""
+    _dev(x, r, w, x_out, out)
+    rows, H = x.shape
+    xo = x_out if x_out is not None else torch.empty_like(x)
+    y = out if out is not None else torch.empty_like(x)
+    _check(lib().bi_add_rmsnorm(_ptr(x), _ptr(r), _ptr(xo), _ptr(w), _ptr(y), rows, H, eps, _dt(x), _stream(stream)),
+           "bi_add_rmsnorm")
+    return xo, y
 
 
 def rmsnorm_split(x, w, splits: int, eps: float = 1e-6, out=None, ws=None, stream=None):

@@ -22,57 +22,101 @@ __global__ void embed_kernel(const int32_t *__restrict__ ids, const uint4 *__res
         out[t * H16 + i] = ok ? table[(int64_t)id * H16 + i] : make_uint4(0, 0, 0, 0);
 }
 
-// One thread per (token, head, pair i < D/2).
+// One thread per (token, head, group of G pairs): G = 8 with 16-byte accesses
+// when D / 2 is a multiple of 8, else G = 1.  Pair i of a head rotates
+// elements i and i + D/2.
+template <int G>
 __global__ void rope_kv_kernel(const uint16_t *__restrict__ qkv, uint16_t *__restrict__ q_out,
                                uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
                                const int32_t *__restrict__ kv_len, const float *__restrict__ cos_t,
                                const float *__restrict__ sin_t, int64_t B, int64_t Q, int64_t Lcap,
                                int Hq, int Hkv, int D, int64_t max_pos)
 {
-    const int half = D / 2;
+    typedef uint16_t vec_t __attribute__((ext_vector_type(G)));
+    const int half = D / 2, ng = half / G;
     const int heads = Hq + 2 * Hkv;
-    const int64_t n = B * Q * heads * half;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
-        const int i = (int)(idx % half);
-        const int hh = (int)((idx / half) % heads);
-        const int64_t tok = idx / ((int64_t)half * heads);       // b * Q + j
-        const int64_t b = tok / Q, j = tok % Q;
+    const int64_t per_tok = (int64_t)heads * ng;
+    const int64_t n = B * Q * per_tok;
+    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < n; it += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t tok = it / per_tok;                          // b * Q + j
+        const int rem = (int)(it - tok * per_tok);
+        const int hh = rem / ng, i = (rem - hh * ng) * G;
+        const int64_t b = tok / Q, j = tok - b * Q;
         const int64_t pos = (int64_t)kv_len[b] - Q + j;
         if (pos < 0 || pos >= Lcap || pos >= max_pos) continue;   // out-of-range positions write nothing
         const uint16_t *src = qkv + tok * (int64_t)heads * D + (int64_t)hh * D;
-        const float a = BF16::widen(src[i]), bb = BF16::widen(src[i + half]);
+        const vec_t lo_in = *reinterpret_cast<const vec_t *>(src + i);
+        const vec_t hi_in = *reinterpret_cast<const vec_t *>(src + i + half);
         if (hh >= Hq + Hkv) {                                      // v: copied to the cache unchanged
             uint16_t *dst = vc + ((b * Lcap + pos) * Hkv + (hh - Hq - Hkv)) * (int64_t)D;
-            dst[i] = src[i];
-            dst[i + half] = src[i + half];
+            *reinterpret_cast<vec_t *>(dst + i) = lo_in;
+            *reinterpret_cast<vec_t *>(dst + i + half) = hi_in;
             continue;
         }
-        const float c = cos_t[pos * half + i], s = sin_t[pos * half + i];
-        const float lo = a * c - bb * s;
-        const float hi = bb * c + a * s;
+        vec_t lo_out, hi_out;
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            const float a = BF16::widen(lo_in[e]), bb = BF16::widen(hi_in[e]);
+            const float c = cos_t[pos * half + i + e], sn = sin_t[pos * half + i + e];
+            lo_out[e] = BF16::narrow(a * c - bb * sn);
+            hi_out[e] = BF16::narrow(bb * c + a * sn);
+        }
         uint16_t *dst = hh < Hq ? q_out + tok * (int64_t)Hq * D + (int64_t)hh * D
                                 : kc + ((b * Lcap + pos) * Hkv + (hh - Hq)) * (int64_t)D;
-        dst[i] = BF16::narrow(lo);
-        dst[i + half] = BF16::narrow(hi);
+        *reinterpret_cast<vec_t *>(dst + i) = lo_out;
+        *reinterpret_cast<vec_t *>(dst + i + half) = hi_out;
     }
 }
 
+__device__ inline uint16_t silu_mul1(uint16_t gb, uint16_t ub)
+{
+    const float g = BF16::widen(gb), u = BF16::widen(ub);
+    const float sg = g / (1.0f + expf(-g));
+    return BF16::narrow(sg * u);
+}
+
+// VEC: F % 8 == 0 and 16-byte aligned rows; thread = 8 consecutive outputs.
+template <bool VEC>
 __global__ void silu_mul_kernel(const uint16_t *__restrict__ gu, uint16_t *__restrict__ out, int64_t rows, int64_t F)
 {
-    const int64_t n = rows * F;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = idx / F, i = idx % F;
-        const float g = BF16::widen(gu[r * 2 * F + i]);
-        const float u = BF16::widen(gu[r * 2 * F + F + i]);
-        const float sg = g / (1.0f + expf(-g));
-        out[idx] = BF16::narrow(sg * u);
+    if (VEC) {
+        const int64_t fc = F / 8, n = rows * fc;
+        for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n; c += (int64_t)gridDim.x * blockDim.x) {
+            const int64_t r = c / fc, i = (c - r * fc) * 8;
+            const uint4 gv = *reinterpret_cast<const uint4 *>(gu + r * 2 * F + i);
+            const uint4 uv = *reinterpret_cast<const uint4 *>(gu + r * 2 * F + F + i);
+            const uint16_t *g8 = reinterpret_cast<const uint16_t *>(&gv), *u8 = reinterpret_cast<const uint16_t *>(&uv);
+            uint16_t o8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = silu_mul1(g8[e], u8[e]);
+            *reinterpret_cast<uint4 *>(out + r * F + i) = __builtin_bit_cast(uint4, o8);
+        }
+    } else {
+        const int64_t n = rows * F;
+        for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+            const int64_t r = idx / F, i = idx % F;
+            out[idx] = silu_mul1(gu[r * 2 * F + i], gu[r * 2 * F + F + i]);
+        }
     }
 }
 
+// VEC: n % 8 == 0 (pointers are 16-byte aligned by contract); out may alias a or b.
+template <bool VEC>
 __global__ void add_kernel(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t n)
 {
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x)
-        out[idx] = BF16::narrow(BF16::widen(a[idx]) + BF16::widen(b[idx]));
+    if (VEC) {
+        for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n / 8; c += (int64_t)gridDim.x * blockDim.x) {
+            const uint4 av = reinterpret_cast<const uint4 *>(a)[c], bv = reinterpret_cast<const uint4 *>(b)[c];
+            const uint16_t *a8 = reinterpret_cast<const uint16_t *>(&av), *b8 = reinterpret_cast<const uint16_t *>(&bv);
+            uint16_t o8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = BF16::narrow(BF16::widen(a8[e]) + BF16::widen(b8[e]));
+            reinterpret_cast<uint4 *>(out)[c] = __builtin_bit_cast(uint4, o8);
+        }
+    } else {
+        for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x)
+            out[idx] = BF16::narrow(BF16::widen(a[idx]) + BF16::widen(b[idx]));
+    }
 }
 
 __device__ inline bool better(float v, int64_t i, float bv, int64_t bi)
@@ -80,35 +124,76 @@ __device__ inline bool better(float v, int64_t i, float bv, int64_t bi)
     return v > bv || (v == bv && i < bi);
 }
 
-constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxThreads = 1024;
+constexpr int kArgmaxUnroll = 4;           // independent 16-byte loads in flight per thread
 
+__device__ inline void argmax_take(float v, int i, float &bv, int &bi, int none)
+{
+    if (i != none && (bi == none || better(v, i, bv, bi))) {
+        bv = v;
+        bi = i;
+    }
+}
+
+// One workgroup per row.  VEC (cols % 8 == 0): thread t reads the 16-byte
+// chunks t, t + 1024, ... of the row, kArgmaxUnroll loads at a time.  The
+// winner -- the largest value, lowest index among equals -- is the same for
+// any order of comparison, so the wave butterfly and the cross-wave step may
+// meet candidates in any order.
+template <bool VEC>
 __global__ __launch_bounds__(kArgmaxThreads)
 void argmax_kernel(const uint16_t *__restrict__ x, int32_t *__restrict__ idx, int64_t rows, int64_t cols)
 {
-    __shared__ float sv[kArgmaxThreads];
-    __shared__ int64_t si[kArgmaxThreads];
-    const int64_t r = blockIdx.x;
+    __shared__ float sv[kArgmaxThreads / kWave];
+    __shared__ int si[kArgmaxThreads / kWave];
+    const int none = (int)cols;                 // sentinel: loses every comparison with a real index
+    const uint16_t *xr = x + (int64_t)blockIdx.x * cols;
     float bv = -INFINITY;
-    int64_t bi = cols;                          // sentinel: loses every comparison with a real index
-    for (int64_t cc = threadIdx.x; cc < cols; cc += kArgmaxThreads) {
-        const float v = BF16::widen(x[r * cols + cc]);
-        if (bi == cols || better(v, cc, bv, bi)) { bv = v; bi = cc; }
-    }
-    sv[threadIdx.x] = bv;
-    si[threadIdx.x] = bi;
-    __syncthreads();
-    for (int off = kArgmaxThreads / 2; off > 0; off >>= 1) {
-        if (threadIdx.x < off) {
-            const float v = sv[threadIdx.x + off];
-            const int64_t i = si[threadIdx.x + off];
-            if (i < cols && (si[threadIdx.x] == cols || better(v, i, sv[threadIdx.x], si[threadIdx.x]))) {
-                sv[threadIdx.x] = v;
-                si[threadIdx.x] = i;
+    int bi = none;
+    if (VEC) {
+        const int nch = (int)(cols / 8);
+        for (int c0 = threadIdx.x; c0 < nch; c0 += kArgmaxThreads * kArgmaxUnroll) {
+            uint4 v[kArgmaxUnroll];
+#pragma unroll
+            for (int u = 0; u < kArgmaxUnroll; ++u) {
+                const int ch = c0 + u * kArgmaxThreads;
+                v[u] = ch < nch ? reinterpret_cast<const uint4 *>(xr)[ch] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kArgmaxUnroll; ++u) {
+                const int ch = c0 + u * kArgmaxThreads;
+                if (ch >= nch) break;
+                const uint16_t *e8 = reinterpret_cast<const uint16_t *>(&v[u]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) argmax_take(BF16::widen(e8[e]), ch * 8 + e, bv, bi, none);
             }
         }
-        __syncthreads();
+    } else {
+        for (int c = threadIdx.x; c < (int)cols; c += kArgmaxThreads) argmax_take(BF16::widen(xr[c]), c, bv, bi, none);
     }
-    if (threadIdx.x == 0) idx[r] = (int32_t)si[0];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, kWave);
+        const int oi = __shfl_xor(bi, off, kWave);
+        argmax_take(ov, oi, bv, bi, none);
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        sv[wave] = bv;
+        si[wave] = bi;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        bv = lane < kArgmaxThreads / kWave ? sv[lane] : -INFINITY;
+        bi = lane < kArgmaxThreads / kWave ? si[lane] : none;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, kWave);
+            const int oi = __shfl_xor(bi, off, kWave);
+            argmax_take(ov, oi, bv, bi, none);
+        }
+        if (lane == 0) idx[blockIdx.x] = bi;
+    }
 }
 
 inline unsigned grid_for(int64_t n, int threads)
@@ -143,10 +228,17 @@ extern "C" bi_status bi_rope_kv_write(const void *qkv, void *q_out, void *kc, vo
         !host_aligned16(cos_t) || !host_aligned16(sin_t) || ((uintptr_t)kv_len & 3u))
         return BI_ERR_ALIGN;
     (void)hipGetLastError();
-    const int64_t n = B * Q * (Hq + 2 * Hkv) * (D / 2);
-    hipLaunchKernelGGL(rope_kv_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)qkv,
-                       (uint16_t *)q_out, (uint16_t *)kc, (uint16_t *)vc, kv_len, cos_t, sin_t, B, Q, Lcap,
-                       Hq, Hkv, D, max_pos);
+    if ((int64_t)(Hq + 2 * Hkv) * D > (1ll << 31) - 1) return BI_ERR_SHAPE;
+    const bool vec = (D / 2) % 8 == 0;
+    const int64_t n = B * Q * (Hq + 2 * Hkv) * (vec ? D / 16 : D / 2);
+    if (vec)
+        hipLaunchKernelGGL(rope_kv_kernel<8>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)qkv,
+                           (uint16_t *)q_out, (uint16_t *)kc, (uint16_t *)vc, kv_len, cos_t, sin_t, B, Q, Lcap,
+                           Hq, Hkv, D, max_pos);
+    else
+        hipLaunchKernelGGL(rope_kv_kernel<1>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)qkv,
+                           (uint16_t *)q_out, (uint16_t *)kc, (uint16_t *)vc, kv_len, cos_t, sin_t, B, Q, Lcap,
+                           Hq, Hkv, D, max_pos);
     return launch_status();
 }
 
@@ -156,8 +248,12 @@ extern "C" bi_status bi_silu_mul(const void *gu, void *out, int64_t rows, int64_
     if (rows < 1 || F < 1) return BI_ERR_SHAPE;
     if (!host_aligned16(gu) || !host_aligned16(out)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(silu_mul_kernel, dim3(grid_for(rows * F, 256)), dim3(256), 0, stream,
-                       (const uint16_t *)gu, (uint16_t *)out, rows, F);
+    if (F % 8 == 0)
+        hipLaunchKernelGGL(silu_mul_kernel<true>, dim3(grid_for(rows * F / 8, 256)), dim3(256), 0, stream,
+                           (const uint16_t *)gu, (uint16_t *)out, rows, F);
+    else
+        hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(grid_for(rows * F, 256)), dim3(256), 0, stream,
+                           (const uint16_t *)gu, (uint16_t *)out, rows, F);
     return launch_status();
 }
 
@@ -167,8 +263,12 @@ extern "C" bi_status bi_add(const void *a, const void *b, void *out, int64_t n, 
     if (n < 1) return BI_ERR_SHAPE;
     if (!host_aligned16(a) || !host_aligned16(b) || !host_aligned16(out)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(add_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)a,
-                       (const uint16_t *)b, (uint16_t *)out, n);
+    if (n % 8 == 0)
+        hipLaunchKernelGGL(add_kernel<true>, dim3(grid_for(n / 8, 256)), dim3(256), 0, stream, (const uint16_t *)a,
+                           (const uint16_t *)b, (uint16_t *)out, n);
+    else
+        hipLaunchKernelGGL(add_kernel<false>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)a,
+                           (const uint16_t *)b, (uint16_t *)out, n);
     return launch_status();
 }
 
@@ -178,8 +278,12 @@ extern "C" bi_status bi_argmax(const void *x, int32_t *idx, int64_t rows, int64_
     if (rows < 1 || cols < 1 || rows > (1ll << 31) - 1 || cols > (1ll << 31) - 1) return BI_ERR_SHAPE;
     if (!host_aligned16(x) || ((uintptr_t)idx & 3u)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)rows), dim3(kArgmaxThreads), 0, stream,
-                       (const uint16_t *)x, idx, rows, cols);
+    if (cols % 8 == 0)
+        hipLaunchKernelGGL(argmax_kernel<true>, dim3((unsigned)rows), dim3(kArgmaxThreads), 0, stream,
+                           (const uint16_t *)x, idx, rows, cols);
+    else
+        hipLaunchKernelGGL(argmax_kernel<false>, dim3((unsigned)rows), dim3(kArgmaxThreads), 0, stream,
+                           (const uint16_t *)x, idx, rows, cols);
     return launch_status();
 }
 
@@ -203,7 +307,8 @@ extern "C" const char *bi_build_info(void)
 {
     return "libbi gfx950;"
            " matmul: v_mfma_f32_16x16x32_bf16/f16 and v_mfma_f32_16x16x4_f32 for every M,"
-           " K blocks of 128 (16-bit) / 16 (f32), block b owned by wave b%8 of 8, wave partials added in order;"
+           " K blocks of 128 (16-bit) / 16 (f32), block b in slot b%8 of 8, each slot summed in block order,"
+           " slots added pairwise ((0+1)+(2+3))+((4+5)+(6+7));"
            " qmatmul: dequantize to binary16 in registers, v_mfma_f32_16x16x32_f16, same K slicing;"
            " rmsnorm: one wave per row, 16-byte chunk v to lane v%64, per-lane fma fold, xor butterfly 32..1;"
            " sdpa: chunks of 256 keys, 4 waves x 64 keys, bf16 P in MFMA, pass-2 weights exp(m_c-M) summed in chunk order";

@@ -89,11 +89,40 @@ __device__ inline void normalize_chunks(const typename S::store_t *xr, const typ
     }
 }
 
+// Chunk v of the row as the norm sees it: x itself, or with ADD the residual
+// sum RNE(x + r) (the bits bi_add produces), which is also stored to xo.
+template <typename S, bool VEC, bool ADD>
+__device__ inline uint4 row_chunk(const typename S::store_t *xr, const typename S::store_t *rr,
+                                  typename S::store_t *xor_, int64_t v, int64_t H, bool ok)
+{
+    constexpr int E = S::kElemsPer16B;
+    const uint4 a = load_chunk<S, VEC>(xr, v * E, H, ok);
+    if constexpr (!ADD) {
+        return a;
+    } else {
+        float av[E], bv[E], sv[E];
+        chunk_vals<S>(a, av);
+        chunk_vals<S>(load_chunk<S, VEC>(rr, v * E, H, ok), bv);
+        typename S::store_t tmp[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            tmp[e] = S::narrow(av[e] + bv[e]);
+            sv[e] = S::widen(tmp[e]);
+        }
+        if (ok) store_chunk<S, VEC>(xor_, v * E, H, sv);
+        return __builtin_bit_cast(uint4, tmp);
+    }
+}
+
 // CACHED: the row's chunks stay in registers between the two phases
-// (H <= 64 * kNormCached * E); otherwise the second phase re-reads the row.
-template <typename S, bool VEC, bool CACHED>
+// (H <= 64 * kNormCached * E); otherwise the second phase re-reads the row
+// (with ADD, the sums this lane stored in the first phase).
+// ADD: the row is RNE(x + r), written to xo (which may alias x), and then
+// normalized -- the residual add of a pre-norm block fused with its norm.
+template <typename S, bool VEC, bool CACHED, bool ADD>
 __global__ __launch_bounds__(kNormRowsPerBlock * kWave)
-void rmsnorm_kernel(const typename S::store_t *__restrict__ x, const typename S::store_t *__restrict__ w,
+void rmsnorm_kernel(const typename S::store_t *x, const typename S::store_t *__restrict__ r,
+                    typename S::store_t *xo, const typename S::store_t *__restrict__ w,
                     typename S::store_t *__restrict__ y, int64_t rows, int64_t H, float eps)
 {
     constexpr int E = S::kElemsPer16B;
@@ -101,6 +130,8 @@ void rmsnorm_kernel(const typename S::store_t *__restrict__ x, const typename S:
     const int64_t row = (int64_t)blockIdx.x * kNormRowsPerBlock + wave_id();
     if (row >= rows) return;
     const typename S::store_t *xr = x + row * H;
+    const typename S::store_t *rr = ADD ? r + row * H : nullptr;
+    typename S::store_t *xor_ = ADD ? xo + row * H : nullptr;
     typename S::store_t *yr = y + row * H;
     const int64_t nch = cdiv(H, E);
 
@@ -110,7 +141,7 @@ void rmsnorm_kernel(const typename S::store_t *__restrict__ x, const typename S:
 #pragma unroll
         for (int i = 0; i < kNormCached; ++i) {
             const int64_t v = lane + (int64_t)i * kWave;
-            cache[i] = load_chunk<S, VEC>(xr, v * E, H, v < nch);
+            cache[i] = row_chunk<S, VEC, ADD>(xr, rr, xor_, v, H, v < nch);
             float xv[E];
             chunk_vals<S>(cache[i], xv);
 #pragma unroll
@@ -130,9 +161,16 @@ void rmsnorm_kernel(const typename S::store_t *__restrict__ x, const typename S:
             store_chunk<S, VEC>(yr, v * E, H, yv);
         }
     } else {
-        float ss = wave_sum_butterfly(lane_sumsq<S, VEC>(xr, H, 0, nch, lane));
+        float ss = 0.0f;
+        for (int64_t v = lane; v < nch; v += kWave) {
+            float xv[E];
+            chunk_vals<S>(row_chunk<S, VEC, ADD>(xr, rr, xor_, v, H, true), xv);
+#pragma unroll
+            for (int e = 0; e < E; ++e) ss = __builtin_fmaf(xv[e], xv[e], ss);
+        }
+        ss = wave_sum_butterfly(ss);
         const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-        normalize_chunks<S, VEC>(xr, w, yr, H, 0, nch, lane, inv);
+        normalize_chunks<S, VEC>(ADD ? xor_ : xr, w, yr, H, 0, nch, lane, inv);
     }
 }
 
@@ -167,19 +205,22 @@ void rmsnorm_split_finish(const typename S::store_t *__restrict__ x, const typen
     normalize_chunks<S, VEC>(x + row * H, w, y + row * H, H, 0, cdiv(H, E), lane, inv);
 }
 
-template <typename S>
-static void launch_rmsnorm(const void *x, const void *w, void *y, int64_t rows, int64_t H, float eps,
-                           hipStream_t st)
+template <typename S, bool ADD>
+static void launch_rmsnorm(const void *x, const void *r, void *xo, const void *w, void *y, int64_t rows, int64_t H,
+                           float eps, hipStream_t st)
 {
     using T = typename S::store_t;
     constexpr int E = S::kElemsPer16B;
-    const bool vec = (H % E) == 0 && host_aligned16(x) && host_aligned16(w) && host_aligned16(y);
+    const bool vec = (H % E) == 0 && host_aligned16(x) && host_aligned16(w) && host_aligned16(y) &&
+                     (!ADD || (host_aligned16(r) && host_aligned16(xo)));
     const bool cached = cdiv(cdiv(H, E), kWave) <= kNormCached;
     dim3 grid((unsigned)cdiv(rows, kNormRowsPerBlock)), block(kNormRowsPerBlock * kWave);
-    if (vec && cached) hipLaunchKernelGGL((rmsnorm_kernel<S, true, true>), grid, block, 0, st, (const T *)x, (const T *)w, (T *)y, rows, H, eps);
-    else if (vec) hipLaunchKernelGGL((rmsnorm_kernel<S, true, false>), grid, block, 0, st, (const T *)x, (const T *)w, (T *)y, rows, H, eps);
-    else if (cached) hipLaunchKernelGGL((rmsnorm_kernel<S, false, true>), grid, block, 0, st, (const T *)x, (const T *)w, (T *)y, rows, H, eps);
-    else hipLaunchKernelGGL((rmsnorm_kernel<S, false, false>), grid, block, 0, st, (const T *)x, (const T *)w, (T *)y, rows, H, eps);
+    const T *xt = (const T *)x, *rt = (const T *)r, *wt = (const T *)w;
+    T *xot = (T *)xo, *yt = (T *)y;
+    if (vec && cached) hipLaunchKernelGGL((rmsnorm_kernel<S, true, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
+    else if (vec) hipLaunchKernelGGL((rmsnorm_kernel<S, true, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
+    else if (cached) hipLaunchKernelGGL((rmsnorm_kernel<S, false, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
+    else hipLaunchKernelGGL((rmsnorm_kernel<S, false, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
 }
 
 template <typename S>
@@ -218,9 +259,24 @@ extern "C" bi_status bi_rmsnorm(const void *x, const void *w, void *y, int64_t r
     bi_status s = check_norm(x, w, y, rows, H, eps, dtype);
     if (s != BI_OK) return s;
     (void)hipGetLastError();
-    if (dtype == BI_BF16) launch_rmsnorm<BF16>(x, w, y, rows, H, eps, stream);
-    else if (dtype == BI_F16) launch_rmsnorm<F16>(x, w, y, rows, H, eps, stream);
-    else launch_rmsnorm<F32>(x, w, y, rows, H, eps, stream);
+    if (dtype == BI_BF16) launch_rmsnorm<BF16, false>(x, nullptr, nullptr, w, y, rows, H, eps, stream);
+    else if (dtype == BI_F16) launch_rmsnorm<F16, false>(x, nullptr, nullptr, w, y, rows, H, eps, stream);
+    else launch_rmsnorm<F32, false>(x, nullptr, nullptr, w, y, rows, H, eps, stream);
+    return launch_status();
+}
+
+extern "C" bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *w, void *y,
+                                    int64_t rows, int64_t H, float eps, int32_t dtype, hipStream_t stream)
+{
+    bi_status s = check_norm(x, w, y, rows, H, eps, dtype);
+    if (s != BI_OK) return s;
+    if (!r || !x_out) return BI_ERR_NULL;
+    const size_t esz = dtype == BI_F32 ? 4 : 2;
+    if (((uintptr_t)r | (uintptr_t)x_out) & (esz - 1)) return BI_ERR_ALIGN;
+    (void)hipGetLastError();
+    if (dtype == BI_BF16) launch_rmsnorm<BF16, true>(x, r, x_out, w, y, rows, H, eps, stream);
+    else if (dtype == BI_F16) launch_rmsnorm<F16, true>(x, r, x_out, w, y, rows, H, eps, stream);
+    else launch_rmsnorm<F32, true>(x, r, x_out, w, y, rows, H, eps, stream);
     return launch_status();
 }
 

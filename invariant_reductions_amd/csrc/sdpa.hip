@@ -68,7 +68,12 @@ __device__ inline int64_t row_last_key(int64_t kvlen, int64_t Q, int64_t j, int 
     return causal ? kvlen - Q + j : kvlen - 1;
 }
 
-// Pass 1: grid (nchunks, Hkv, B), kAttnWaves waves.
+// Pass 1: one workgroup of kAttnWaves waves per (sequence b, chunk c, KV head
+// hk), on a 1-D grid ordered so that the workgroups of all KV heads of one
+// (b, c) are dispatched together onto one XCD: id L -> XCD L % 8 (the
+// hardware's round-robin), heads hk = (L / 8) % Hkv, item (b, c) =
+// (L / (8 Hkv)) * 8 + L % 8.  Their key rows [b][pos][0..Hkv)[0..D) are
+// contiguous, so each cache line of K and V is wanted by one XCD at one time.
 template <typename S>
 __global__ __launch_bounds__(kAttnWaves * kWave)
 void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -91,14 +96,16 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g4 = lane >> 4, c16 = lane & 15;
-    const int64_t c = blockIdx.x;
-    const int hk = blockIdx.y;
-    const int64_t b = blockIdx.z;
+    const int64_t L = blockIdx.x;
+    const int hk = (int)((L >> 3) % sh.Hkv);
+    const int64_t item = (L >> 3) / sh.Hkv * 8 + (L & 7);
+    if (item >= sh.B * sh.nchunks) return;
+    const int64_t b = item / sh.nchunks, c = item - b * sh.nchunks;
     // kv_len is device data the host cannot validate; clamping it keeps every
     // access inside the cache and the workspace even for a bad value.
     const int64_t kvlen = min((int64_t)kv_len[b], sh.max_kv);
     const int64_t key0 = c * kChunk;
-    const int64_t R = sh.Q * sh.G;                                       // query rows of this KV head
+    const int R = (int)sh.Q * sh.G;                                      // query rows of this KV head
 
     // Largest position any row of this (b, hk) attends to; chunks past it have no work.
     const int64_t pmax = row_last_key(kvlen, sh.Q, sh.Q - 1, sh.causal);
@@ -141,26 +148,26 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
         }
     __syncthreads();                                                   // V staging bytes are reused below
 
-    const int64_t ntiles = cdiv(R, 16);
-    for (int64_t mt = 0; mt < ntiles; ++mt) {
+    const int ntiles = (R + 15) / 16;
+    for (int mt = 0; mt < ntiles; ++mt) {
         // Query row handled as A-operand row c16 of this tile.
-        const int64_t ra = mt * 16 + c16;
+        const int ra = mt * 16 + c16;
         const bool ra_ok = ra < R;
-        const int64_t ja = ra_ok ? ra / sh.G : 0, ia = ra_ok ? ra % sh.G : 0;
+        const int ja = ra_ok ? ra / sh.G : 0, ia = ra_ok ? ra - ja * sh.G : 0;
         // Rows of the accumulator layout held by this lane: 4*g4 + i.
         int64_t lastk[4];
         bool rowok[4];
         bool any = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t r = mt * 16 + g4 * 4 + i;
+            const int r = mt * 16 + g4 * 4 + i;
             rowok[i] = r < R;
             lastk[i] = rowok[i] ? row_last_key(kvlen, sh.Q, r / sh.G, sh.causal) : -1;
             rowok[i] = rowok[i] && lastk[i] >= key0;
         }
         // Tile-uniform skip: no row of this tile reaches this chunk.
         {
-            const int64_t rlast = mt * 16 + 15 < R ? mt * 16 + 15 : R - 1;
+            const int rlast = mt * 16 + 15 < R ? mt * 16 + 15 : R - 1;
             any = row_last_key(kvlen, sh.Q, rlast / sh.G, sh.causal) >= key0;
         }
         if (!any) continue;
@@ -246,11 +253,11 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
         // combine the four wave partials in order and write this chunk's partial
         for (int e = threadIdx.x; e < 16 * kHeadDim; e += kAttnWaves * kWave) {
             const int rr = e / kHeadDim, d = e % kHeadDim;
-            const int64_t r = mt * 16 + rr;
+            const int r = mt * 16 + rr;
             if (r >= R) continue;
-            const int64_t j = r / sh.G;
+            const int j = r / sh.G;
             if (row_last_key(kvlen, sh.Q, j, sh.causal) < key0) continue;
-            const int64_t h = (int64_t)hk * sh.G + r % sh.G;
+            const int64_t h = (int64_t)hk * sh.G + (r - j * sh.G);
             float* dst = part + (((b * sh.Q + j) * sh.Hq + h) * sh.nchunks + c) * kPartStride;
             const float o = ((ol[0][rr][d] + ol[1][rr][d]) + ol[2][rr][d]) + ol[3][rr][d];
             dst[d] = o;
@@ -312,7 +319,9 @@ static bi_status check_attn(const void *q, const void *k, const void *v, const v
     if (!q || !k || !v || !o || !kv_len) return BI_ERR_NULL;
     if (B < 1 || Q < 1 || Lcap < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
     if (max_kv_len < Q || max_kv_len > Lcap || max_kv_len > kMaxKv) return BI_ERR_SHAPE;
-    if (B > 65535 || Hkv > 65535 || B * Q * Hq > (1ll << 31) - 1) return BI_ERR_SHAPE;
+    if (Hkv > 65535 || B * Q * Hq > (1ll << 31) - 1 || Q * (Hq / Hkv) > (1ll << 30) ||
+        cdiv(B * cdiv(max_kv_len, kChunk), 8) * 8 * Hkv > (1ll << 31) - 1)
+        return BI_ERR_SHAPE;
     if (D != kHeadDim) return BI_ERR_UNSUPPORTED;
     if (dtype != BI_BF16 && dtype != BI_F16) return BI_ERR_DTYPE;
     if (!host_aligned16(q) || !host_aligned16(k) || !host_aligned16(v) || !host_aligned16(o) ||
@@ -325,7 +334,8 @@ template <typename S>
 static void launch_attn(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len, float *part,
                         const AttnShape &sh, int64_t chunk, hipStream_t st)
 {
-    hipLaunchKernelGGL((attn_chunk_kernel<S>), dim3((unsigned)sh.nchunks, (unsigned)sh.Hkv, (unsigned)sh.B),
+    const int64_t groups = cdiv(sh.B * sh.nchunks, 8);
+    hipLaunchKernelGGL((attn_chunk_kernel<S>), dim3((unsigned)(groups * 8 * sh.Hkv)),
                        dim3(kAttnWaves * kWave), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                        (const uint16_t *)v, kv_len, part, sh);
     const size_t smem = (size_t)sh.nchunks * 2 * sizeof(float);

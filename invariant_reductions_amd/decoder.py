@@ -24,7 +24,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (add, argmax, embed, lib, matmul_ws, rmsnorm, rope_kv_write, sdpa, sdpa_workspace_bytes, silu_mul)
+from . import (add_rmsnorm, argmax, embed, lib, matmul_ws, rmsnorm, rope_kv_write, sdpa, sdpa_workspace_bytes,
+               silu_mul)
 from .inputs import rope_tables
 
 
@@ -83,21 +84,22 @@ class Decoder:
         kv = self.kv_len[:B]
         embed(self.ids[:T], self.embed_w, out=x)
         scale = 1.0 / float(np.sqrt(self.D))
+        # Every residual add is fused with the RMSNorm that reads its result
+        # (the next block's norm, or the final norm after the last layer).
+        rmsnorm(x, self.layers[0]["attn_norm"], self.eps, out=h)
         for li, Lw in enumerate(self.layers):
-            rmsnorm(x, Lw["attn_norm"], self.eps, out=h)
             matmul_ws(h, Lw["wqkv"], self.mws, True, out=qkv)
             kc, vc = self.kc[li][:B], self.vc[li][:B]
             rope_kv_write(qkv, q, kc, vc, kv, self.cos_t, self.sin_t, B, Q, self.Hq, self.Hkv, self.D)
             sdpa(q.view(B, Q, self.Hq, self.D), kc, vc, kv, max_kv, scale, True,
                  out=o.view(B, Q, self.Hq, self.D), ws=self.ws)
             matmul_ws(o, Lw["wo"], self.mws, True, out=t1)
-            add(x, t1, out=x)
-            rmsnorm(x, Lw["mlp_norm"], self.eps, out=h)
+            add_rmsnorm(x, t1, Lw["mlp_norm"], self.eps, x_out=x, out=h)
             matmul_ws(h, Lw["wgu"], self.mws, True, out=gu)
             silu_mul(gu, out=a)
             matmul_ws(a, Lw["wdown"], self.mws, True, out=t1)
-            add(x, t1, out=x)
-        rmsnorm(x, self.final_norm, self.eps, out=h)
+            nxt = self.layers[li + 1]["attn_norm"] if li + 1 < self.L else self.final_norm
+            add_rmsnorm(x, t1, nxt, self.eps, x_out=x, out=h)
         matmul_ws(h, self.lm_head, self.mws, True, out=self.logits[:T])
         argmax(self.logits[:T], out=self.next_ids[:T])
         return self.logits[:T]
@@ -125,26 +127,25 @@ class Decoder:
         steps = [("embed", L.bi_embed, (p(self.ids), p(self.embed_w), p(x), T, self.V, H, st))]
         mws, mwsb = p(self.mws), self.mws.numel()
         mm = lambda xin, w, out, N, K: ("matmul", L.bi_matmul_ws, (p(xin), p(w), p(out), T, N, K, 0, 1, mws, mwsb, st))
+        steps.append(("rmsnorm", L.bi_rmsnorm, (p(x), p(self.layers[0]["attn_norm"]), p(h), T, H, eps, 0, st)))
         for li, Lw in enumerate(self.layers):
             kc, vc = self.kc[li], self.vc[li]
             Lcap = kc.shape[1]
+            nxt = self.layers[li + 1]["attn_norm"] if li + 1 < self.L else self.final_norm
             steps += [
-                ("rmsnorm", L.bi_rmsnorm, (p(x), p(Lw["attn_norm"]), p(h), T, H, eps, 0, st)),
                 mm(h, Lw["wqkv"], qkv, self.qkvn, H),
                 ("rope_kv", L.bi_rope_kv_write, (p(qkv), p(q), p(kc), p(vc), p(kv), p(self.cos_t), p(self.sin_t),
                                                  B, Q, Lcap, self.Hq, self.Hkv, self.D, self.cos_t.shape[0], st)),
                 ("sdpa", L.bi_sdpa, (p(q), p(kc), p(vc), p(o), p(kv), max_kv, B, Q, Lcap, self.Hq, self.Hkv,
                                      self.D, scale, 1, 0, p(self.ws), self.ws.numel(), st)),
                 mm(o, Lw["wo"], t1, H, qn),
-                ("add", L.bi_add, (p(x), p(t1), p(x), T * H, st)),
-                ("rmsnorm", L.bi_rmsnorm, (p(x), p(Lw["mlp_norm"]), p(h), T, H, eps, 0, st)),
+                ("add_rmsnorm", L.bi_add_rmsnorm, (p(x), p(t1), p(x), p(Lw["mlp_norm"]), p(h), T, H, eps, 0, st)),
                 mm(h, Lw["wgu"], gu, 2 * self.F, H),
                 ("silu_mul", L.bi_silu_mul, (p(gu), p(a), T, self.F, st)),
                 mm(a, Lw["wdown"], t1, H, self.F),
-                ("add", L.bi_add, (p(x), p(t1), p(x), T * H, st)),
+                ("add_rmsnorm", L.bi_add_rmsnorm, (p(x), p(t1), p(x), p(nxt), p(h), T, H, eps, 0, st)),
             ]
-        steps += [("rmsnorm", L.bi_rmsnorm, (p(x), p(self.final_norm), p(h), T, H, eps, 0, st)),
-                  mm(h, self.lm_head, self.logits, self.V, H),
+        steps += [mm(h, self.lm_head, self.logits, self.V, H),
                   ("argmax", L.bi_argmax, (p(self.logits), p(self.next_ids), T, self.V, st))]
         return steps
 

@@ -138,6 +138,17 @@ def test_matmul_ws_validation_and_workspace_size():
     assert L.bi_matmul_ws(A, A, A, 64, 4096, 4096, 7, 1, A, need, None) == DTYPE
 
 
+def test_add_rmsnorm_validation():
+    L = bi.lib()
+    assert L.bi_add_rmsnorm(A, None, A, A, A, 4, 4096, 1e-6, 0, None) == NULL
+    assert L.bi_add_rmsnorm(A, A, None, A, A, 4, 4096, 1e-6, 0, None) == NULL
+    assert L.bi_add_rmsnorm(A, ODD, A, A, A, 4, 4096, 1e-6, 0, None) == ALIGN
+    assert L.bi_add_rmsnorm(A, A, ODD, A, A, 4, 4096, 1e-6, 0, None) == ALIGN
+    assert L.bi_add_rmsnorm(A, A, A, A, A, 0, 4096, 1e-6, 0, None) == SHAPE
+    assert L.bi_add_rmsnorm(A, A, A, A, A, 4, 4096, -1.0, 0, None) == SHAPE
+    assert L.bi_add_rmsnorm(A, A, A, A, A, 4, 4096, 1e-6, 9, None) == DTYPE
+
+
 def test_glue_validation():
     L = bi.lib()
     assert L.bi_embed(None, A, A, 1, 10, 64, None) == NULL

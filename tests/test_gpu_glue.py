@@ -19,11 +19,13 @@ def test_embed_gathers_rows():
     assert bits_equal(out, table[ids])
 
 
-def test_rope_and_kv_write_bit_exact():
+@pytest.mark.parametrize("D", [128, 24])
+def test_rope_and_kv_write_bit_exact(D):
     """Rotation uses separately rounded products and sums on both sides, so the
-    GPU equals the oracle bit for bit; k and v land at positions kv_len-Q+j."""
+    GPU equals the oracle bit for bit; k and v land at positions kv_len-Q+j.
+    D = 128 takes the 8-pair vector path, D = 24 the pair-at-a-time one."""
     rng = np.random.default_rng(1)
-    B, Q, Hq, Hkv, D, Lcap = 3, 5, 8, 2, 128, 64
+    B, Q, Hq, Hkv, Lcap = 3, 5, 8, 2, 64
     qkv = inputs.normal(rng, (B * Q, (Hq + 2 * Hkv) * D), 2.0)
     kv_len = np.array([5, 17, 64], np.int32)
     cos_t, sin_t = inputs.rope_tables(128, D)
@@ -51,10 +53,12 @@ def test_rope_and_kv_write_bit_exact():
     assert np.all(kcn[untouched] == 0) and np.all(vcn[untouched] == 0)
 
 
-def test_silu_mul_within_one_ulp():
+@pytest.mark.parametrize("F", [1000, 1001, 14336])
+def test_silu_mul_within_one_ulp(F):
+    """F % 8 == 0 takes the 16-byte path, F = 1001 the element-wise one."""
     rng = np.random.default_rng(2)
-    g = inputs.normal(rng, (64, 1000), 4.0)
-    u = inputs.normal(rng, (64, 1000), 1.0)
+    g = inputs.normal(rng, (64 if F < 14336 else 8, F), 4.0)
+    u = inputs.normal(rng, g.shape, 1.0)
     gu = np.concatenate([g, u], axis=1)
     out = to_np(bi.silu_mul(to_dev(gu, "bf16")))
     r = oracle.round_to(oracle.silu_mul(g, u, "bf16"), "bf16")
@@ -63,10 +67,11 @@ def test_silu_mul_within_one_ulp():
     assert d.max() <= 1 and np.mean(d == 0) > 0.99
 
 
-def test_add_bit_exact():
+@pytest.mark.parametrize("n", [4097, 4096 * 64])
+def test_add_bit_exact(n):
     rng = np.random.default_rng(3)
-    a = inputs.normal(rng, (4097,), 3.0)
-    b = inputs.normal(rng, (4097,), 0.01)
+    a = inputs.normal(rng, (n,), 3.0)
+    b = inputs.normal(rng, (n,), 0.01)
     out = to_np(bi.add(to_dev(a, "bf16"), to_dev(b, "bf16")))
     r = oracle.round_to(inputs.from_storage(a, "bf16") + inputs.from_storage(b, "bf16"), "bf16")
     assert bits_equal(out, r)
@@ -80,3 +85,22 @@ def test_argmax_matches_oracle_and_breaks_ties_low():
     got = to_np(bi.argmax(to_dev(x, "bf16")))
     assert np.array_equal(got, oracle.argmax(x, "bf16"))
     assert got[5] == 100 and got[6] == 0
+
+
+@pytest.mark.parametrize("rows,cols", [(64, 32000), (5, 32001), (3, 8), (2, 1), (4, 65536 + 24)])
+def test_argmax_ties_across_threads_and_ragged_rows(rows, cols):
+    """Equal maxima placed in different threads' chunks and in the last
+    chunk: the lowest index wins on the 16-byte path (cols % 8 == 0) and the
+    element-wise path alike."""
+    rng = np.random.default_rng(rows + cols)
+    x = inputs.normal(rng, (rows, cols), 1.0)
+    big = inputs.to_storage(np.array([60.0], np.float32), "bf16")[0]
+    if cols > 9000:
+        x[0, [8 * 1024 + 7, 7, cols - 1]] = big          # three threads hold the maximum
+        x[1, [cols - 1, cols - 2]] = big                 # ties in the final chunk
+    x[-1, :] = x[-1, 0]                                  # every element equal: index 0
+    got = to_np(bi.argmax(to_dev(x, "bf16")))
+    assert np.array_equal(got, oracle.argmax(x, "bf16"))
+    assert got[-1] == 0
+    if cols > 9000:
+        assert got[0] == 7 and got[1] == cols - 2

@@ -85,3 +85,48 @@ def test_split_variant_is_correct_but_not_invariant():
         assert_parity(y, ref, "f32", f"splits={s}")
         differs += int(not bits_equal(y, inv))
     assert differs > 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("rows,H", [(64, 4096), (3, 4100), (5, 8192), (7, 5000), (1, 1)])
+def test_add_rmsnorm_equals_add_then_norm(dtype, rows, H):
+    """The fused residual add + RMSNorm gives the bits of bi_add (for bf16)
+    followed by bi_rmsnorm, in place (x_out = x) and out of place, on the
+    cached / streamed and vector / element-wise paths; the norm is within
+    the tolerance of the oracle's norm of the rounded sum."""
+    rng = np.random.default_rng(rows * 7 + H)
+    x = inputs.normal(rng, (rows, H), 3.0, dtype=dtype)
+    r = inputs.normal(rng, (rows, H), 0.5, dtype=dtype)
+    w = inputs.normal(rng, (H,), 0.1, loc=1.0, dtype=dtype)
+    xd, rd, wd = to_dev(x, dtype), to_dev(r, dtype), to_dev(w, dtype)
+    s_ref = oracle.round_to(inputs.from_storage(x, dtype) + inputs.from_storage(r, dtype), dtype)
+    xo, y = bi.add_rmsnorm(xd, rd, wd, 1e-6)
+    assert bits_equal(to_np(xo), s_ref)
+    assert bits_equal(to_np(y), to_np(bi.rmsnorm(xo, wd, 1e-6)))
+    assert_parity(to_np(y), oracle.rmsnorm(s_ref, w, dtype, 1e-6), dtype)
+    xi = xd.clone()
+    yi = torch.empty_like(xi)
+    bi.add_rmsnorm(xi, rd, wd, 1e-6, x_out=xi, out=yi)
+    assert bits_equal(to_np(xi), s_ref) and bits_equal(to_np(yi), to_np(y))
+    if dtype == "bf16":
+        assert bits_equal(to_np(bi.add(xd, rd)), s_ref)
+
+
+def test_add_rmsnorm_rows_invariant_and_bounded():
+    """Rows of the fused op at B = 64 equal those at B = 1, 7; the outputs are
+    fenced by canaries."""
+    rng = np.random.default_rng(9)
+    x = inputs.normal(rng, (64, 4096), 3.0)
+    r = inputs.normal(rng, (64, 4096), 0.5)
+    w = inputs.normal(rng, (4096,), 0.1, loc=1.0)
+    xd, rd, wd = to_dev(x, "bf16"), to_dev(r, "bf16"), to_dev(w, "bf16")
+    _, full = bi.add_rmsnorm(xd, rd, wd, 1e-6)
+    for B in (1, 7):
+        _, y = bi.add_rmsnorm(xd[:B].contiguous(), rd[:B].contiguous(), wd, 1e-6)
+        assert bits_equal(to_np(y), to_np(full[:B]))
+    xg = Guarded((64, 4096), torch.bfloat16, poison=0xA5)
+    yg = Guarded((64, 4096), torch.bfloat16, poison=0x5A)
+    bi.add_rmsnorm(xd, rd, wd, 1e-6, x_out=xg.view, out=yg.view)
+    torch.cuda.synchronize()
+    assert xg.canaries_intact() and yg.canaries_intact()
+    assert bits_equal(to_np(yg.view), to_np(full))
