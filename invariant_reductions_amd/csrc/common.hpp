@@ -90,6 +90,20 @@ __device__ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) ==
 
 inline bool host_aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+inline int device_cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+        cached[dev] = cu;                       // benign race: every writer stores the same value
+    }
+    return cached[dev];
+}
+
 inline bi_status launch_status()
 {
     hipError_t e = hipGetLastError();

@@ -440,19 +440,6 @@ static void launch_dense_mt(const void *x, const void *w, void *y, float *part, 
     else launch_dense_t<S, TRANS, VEC, 4, 1>(x, w, y, part, M, N, K, splits, st);
 }
 
-static int device_cu_count()
-{
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int cu = 0;
-        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
-        cached[dev] = cu;                       // benign race: every writer stores the same value
-    }
-    return cached[dev];
-}
-
 template <typename S, int MT, int NS>
 static void launch_stream_t(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K, hipStream_t st)
 {

@@ -68,205 +68,279 @@ __device__ inline int64_t row_last_key(int64_t kvlen, int64_t Q, int64_t j, int 
     return causal ? kvlen - Q + j : kvlen - 1;
 }
 
-// Pass 1: one workgroup of kAttnWaves waves per (sequence b, chunk c, KV head
-// hk), on a 1-D grid ordered so that the workgroups of all KV heads of one
-// (b, c) are dispatched together onto one XCD: id L -> XCD L % 8 (the
-// hardware's round-robin), heads hk = (L / 8) % Hkv, item (b, c) =
-// (L / (8 Hkv)) * 8 + L % 8.  Their key rows [b][pos][0..Hkv)[0..D) are
-// contiguous, so each cache line of K and V is wanted by one XCD at one time.
+// In-place 8 x 8 transpose of 16-bit elements held by one lane: row e is
+// m[e] (elements j = 0..7); afterwards m[j] holds column j.  Pairs of rows
+// are interleaved at 16-bit granularity with v_perm_b32; the rest is
+// register selection.  Every input is read before any output is written.
+__device__ inline void transpose8x8_b16(uint4 (&m)[8])
+{
+    const uint4 (&in)[8] = m;
+    uint32_t t0[4][4], t1[4][4];        // t0[p][w]: (row 2p, row 2p+1) of column 2w; t1: column 2w+1
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t a[4] = {in[2 * p].x, in[2 * p].y, in[2 * p].z, in[2 * p].w};
+        const uint32_t b[4] = {in[2 * p + 1].x, in[2 * p + 1].y, in[2 * p + 1].z, in[2 * p + 1].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            t0[p][w] = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);   // lo16(a), lo16(b)
+            t1[p][w] = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);   // hi16(a), hi16(b)
+        }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        m[2 * w] = make_uint4(t0[0][w], t0[1][w], t0[2][w], t0[3][w]);
+        m[2 * w + 1] = make_uint4(t1[0][w], t1[1][w], t1[2][w], t1[3][w]);
+    }
+}
+
+// Pass 1 as a persistent, software-pipelined kernel.  Work item = (sequence
+// b, chunk c, KV head hk); a fixed grid of workgroups walks the item ids
+// t = blockIdx.x, blockIdx.x + gridDim.x, ...  The ids are ordered so that
+// the items of all KV heads of one (b, c) are processed together on one XCD:
+// id t -> XCD t % 8 (the hardware's round-robin when gridDim.x % 8 == 0),
+// hk = (t / 8) % Hkv, (b, c) = (t / (8 Hkv)) * 8 + t % 8; their key rows
+// [b][pos][0..Hkv)[0..D) are contiguous in the cache.  Inside an item, wave w
+// owns keys [64w, 64w + 64) of the chunk (the frozen tree above).  The
+// resident workgroups drift out of step, so the cache streams without the
+// idle gaps of a grid that starts and finishes its workgroups in rounds.
+//
+// Register layouts (lane = 16 g4 + c16):
+//   K  : kf[kt][s] = key 16kt + c16, d in [32 g4 + 8 s, +8)   (MFMA B of q . k)
+//   V  : rows loaded as vr[s2][e] = key 32 s2 + 8 g4 + e, d in [8 c16, +8),
+//        transposed in place to vr[s2][j] = those 8 keys at d = 8 c16 + j,
+//        the MFMA B operand of P . V (k slot 8 g4 + e of step s2 = key
+//        32 s2 + 8 g4 + e, column c16 = d 8 c16 + j of output tile j).
 template <typename S>
-__global__ __launch_bounds__(kAttnWaves * kWave)
+__global__ __launch_bounds__(kAttnWaves * kWave, 2)
 void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                        const uint16_t *__restrict__ v, const int32_t *__restrict__ kv_len,
-                       float *__restrict__ part, AttnShape sh)
+                       float *__restrict__ part, AttnShape sh, int64_t nid)
 {
-    // The staged V tiles are dead once each wave holds its V fragments; the P
-    // tiles and the wave partials of o then reuse the same bytes.
-    typedef uint16_t VTile[kKeysPerWave][kVStride];
     typedef uint16_t PTile[16][kKeysPerWave + 8];
-    typedef float OTile[16][kHeadDim + 1];
-    constexpr size_t kVBytes = sizeof(VTile) * kAttnWaves;
-    constexpr size_t kPOBytes = (sizeof(PTile) + sizeof(OTile)) * kAttnWaves;
-    static_assert(kPOBytes <= kVBytes, "P/O tiles must fit in the V staging buffer");
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kVBytes];
-    __shared__ float xm[kAttnWaves][16], xl[kAttnWaves][16];           // wave partials of max / sum
-    VTile *vl = reinterpret_cast<VTile *>(lds);
-    PTile *pl = reinterpret_cast<PTile *>(lds);
-    OTile *ol = reinterpret_cast<OTile *>(lds + sizeof(PTile) * kAttnWaves);
+    typedef float OTile[16][kHeadDim + 4];
+    __shared__ __attribute__((aligned(16))) PTile pl[kAttnWaves];
+    __shared__ __attribute__((aligned(16))) OTile ol[kAttnWaves];
+    __shared__ float xm[kAttnWaves][16], xl[kAttnWaves][16];
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g4 = lane >> 4, c16 = lane & 15;
-    const int64_t L = blockIdx.x;
-    const int hk = (int)((L >> 3) % sh.Hkv);
-    const int64_t item = (L >> 3) / sh.Hkv * 8 + (L & 7);
-    if (item >= sh.B * sh.nchunks) return;
-    const int64_t b = item / sh.nchunks, c = item - b * sh.nchunks;
-    // kv_len is device data the host cannot validate; clamping it keeps every
+    const int R = (int)sh.Q * sh.G;                                      // query rows per KV head
+    const int ntm = (R + 15) / 16;
+    const int64_t nitems = sh.B * sh.nchunks;
+
+    // b, c, hk and the clamped length of one item; kv_len is device data the
+    // host cannot validate, so it is clamped to max_kv, which keeps every
     // access inside the cache and the workspace even for a bad value.
-    const int64_t kvlen = min((int64_t)kv_len[b], sh.max_kv);
-    const int64_t key0 = c * kChunk;
-    const int R = (int)sh.Q * sh.G;                                      // query rows of this KV head
-
-    // Largest position any row of this (b, hk) attends to; chunks past it have no work.
-    const int64_t pmax = row_last_key(kvlen, sh.Q, sh.Q - 1, sh.causal);
-    if (key0 > pmax) return;
-
-    // --- K fragments for this wave's 64 keys: 4 key tiles x 4 d-chunks -------
-    const int64_t wkey0 = key0 + wave * kKeysPerWave;
-    uint4 kf[4][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        const int64_t key = wkey0 + kt * 16 + c16;
-        const bool ok = key < kvlen;
-        const uint16_t *kr = k + (((b * sh.Lcap + (ok ? key : 0)) * sh.Hkv + hk) * kHeadDim) + g4 * 32;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kf[kt][s] = ok ? *reinterpret_cast<const uint4 *>(kr + s * 8) : make_uint4(0, 0, 0, 0);
-    }
-    // --- stage this wave's V tile [64 keys][128 d] in LDS ------------------------
-    // lane covers 16 bytes of a key row per step: 16 chunks per row, 4 rows per step.
-#pragma unroll
-    for (int it = 0; it < kKeysPerWave * (kHeadDim / 8) / kWave; ++it) {
-        const int flat = it * kWave + lane;
-        const int kr = flat >> 4, dc = (flat & 15) * 8;
-        const int64_t key = wkey0 + kr;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (key < kvlen) val = *reinterpret_cast<const uint4 *>(v + ((b * sh.Lcap + key) * sh.Hkv + hk) * kHeadDim + dc);
-        uint32_t *dst = reinterpret_cast<uint32_t *>(&vl[wave][kr][dc]);
-        dst[0] = val.x; dst[1] = val.y; dst[2] = val.z; dst[3] = val.w;
-    }
-    __syncthreads();
-    // V as the B operand: lane (g4, c16), d tile dt, step s2 holds keys s2*32 + 8*g4 + e (e < 8), column dt*16 + c16.
-    uint4 vf[8][2];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            uint16_t tmp[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = vl[wave][s2 * 32 + g4 * 8 + e][dt * 16 + c16];
-            vf[dt][s2] = __builtin_bit_cast(uint4, tmp);
-        }
-    __syncthreads();                                                   // V staging bytes are reused below
-
-    const int ntiles = (R + 15) / 16;
-    for (int mt = 0; mt < ntiles; ++mt) {
-        // Query row handled as A-operand row c16 of this tile.
-        const int ra = mt * 16 + c16;
-        const bool ra_ok = ra < R;
-        const int ja = ra_ok ? ra / sh.G : 0, ia = ra_ok ? ra - ja * sh.G : 0;
-        // Rows of the accumulator layout held by this lane: 4*g4 + i.
-        int64_t lastk[4];
-        bool rowok[4];
-        bool any = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = mt * 16 + g4 * 4 + i;
-            rowok[i] = r < R;
-            lastk[i] = rowok[i] ? row_last_key(kvlen, sh.Q, r / sh.G, sh.causal) : -1;
-            rowok[i] = rowok[i] && lastk[i] >= key0;
-        }
-        // Tile-uniform skip: no row of this tile reaches this chunk.
-        {
-            const int rlast = mt * 16 + 15 < R ? mt * 16 + 15 : R - 1;
-            any = row_last_key(kvlen, sh.Q, rlast / sh.G, sh.causal) >= key0;
-        }
-        if (!any) continue;
-
-        uint4 qf[4];
-        {
-            const int64_t h = (int64_t)hk * sh.G + ia;
-            const uint16_t *qr = q + ((b * sh.Q + ja) * sh.Hq + h) * kHeadDim + g4 * 32;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) qf[s] = ra_ok ? *reinterpret_cast<const uint4 *>(qr + s * 8) : make_uint4(0, 0, 0, 0);
-        }
-        // scores: tile kt -> lane (g4, c16) reg i = row 4*g4 + i, key wkey0 + kt*16 + c16
-        float sc[4][4];
+    struct Item {
+        int b, c, hk, kvlen;
+    };
+    auto decode = [&](int64_t t) {
+        Item it;
+        it.hk = (int)((t >> 3) % sh.Hkv);
+        const int64_t bc = (t >> 3) / sh.Hkv * 8 + (t & 7);
+        const bool exists = bc < nitems;
+        it.b = exists ? (int)(bc / sh.nchunks) : 0;
+        it.c = exists ? (int)(bc - (int64_t)it.b * sh.nchunks) : -1;
+        it.kvlen = (int)min((int64_t)kv_len[it.b], sh.max_kv);
+        return it;
+    };
+    const int Qi = (int)sh.Q;
+    auto last_key = [&](int kvlen, int j) { return sh.causal ? kvlen - Qi + j : kvlen - 1; };
+    // an item has work when it exists and its first key is visible to the last row
+    auto has_work = [&](const Item &it) { return it.c >= 0 && it.c * kChunk <= last_key(it.kvlen, Qi - 1); };
+    auto next_id = [&](int64_t t) {
+        for (; t < nid; t += gridDim.x)
+            if (has_work(decode(t))) break;
+        return t;
+    };
+    // Loads are unconditional: a missing key (position >= kv_len) reads the
+    // item's first key, which always exists (the item has work), and the
+    // value is then replaced by zero.  Bases are wave-uniform; per-lane
+    // offsets are 32-bit.
+    const int rs = sh.Hkv * kHeadDim;                                    // elements between keys
+    auto item_base = [&](const uint16_t *p, const Item &it) {
+        return p + ((int64_t)it.b * sh.Lcap + (int64_t)it.c * kChunk) * rs + (int64_t)it.hk * kHeadDim;
+    };
+    // keys of this wave that exist
+    auto wave_valid = [&](const Item &it) { return min(max(it.kvlen - (it.c * kChunk + wave * kKeysPerWave), 0), kKeysPerWave); };
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    auto load_k = [&](const Item &it, uint4 (&kf)[4][4]) {
+        const uint16_t *kb = item_base(k, it);
+        const int nv = wave_valid(it);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int kk = kt * 16 + c16;
+            const bool ok = kk < nv;
+            const uint16_t *kr = kb + (ok ? wave * kKeysPerWave + kk : 0) * rs + g4 * 32;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma16<S>(qf[s], kf[kt][s], acc);
-            const int64_t key = wkey0 + kt * 16 + c16;
+            for (int s = 0; s < 4; ++s) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(kr + s * 8);
+                kf[kt][s] = ok ? x : zero4;
+            }
+        }
+    };
+    auto load_v = [&](const Item &it, uint4 (&vr)[2][8]) {
+        const uint16_t *vb = item_base(v, it);
+        const int nv = wave_valid(it);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = s2 * 32 + g4 * 8 + e;
+                const bool ok = kk < nv;
+                const uint4 x = *reinterpret_cast<const uint4 *>(vb + (ok ? wave * kKeysPerWave + kk : 0) * rs + c16 * 8);
+                vr[s2][e] = ok ? x : zero4;
+            }
+    };
+    // q rows of M tile mt as the MFMA A operand: row c16 of the tile, d in [32 g4 + 8 s, +8)
+    auto load_q = [&](const Item &it, int mt, uint4 (&qf)[4]) {
+        const int ra = mt * 16 + c16;
+        const bool ok = ra < R;
+        const int ja = ok ? ra / sh.G : 0, ia = ok ? ra - ja * sh.G : 0;
+        const uint16_t *qb = q + ((int64_t)it.b * sh.Q * sh.Hq + (int64_t)it.hk * sh.G) * kHeadDim;
+        const uint16_t *qr = qb + (ja * sh.Hq + ia) * kHeadDim + g4 * 32;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(qr + s * 8);
+            qf[s] = ok ? x : zero4;
+        }
+    };
+
+    uint4 kf[4][4], vr[2][8], qf[4];
+    for (int64_t t = next_id(blockIdx.x); t < nid; t = next_id(t + gridDim.x)) {
+        const Item it = decode(t);
+        const int key0 = it.c * kChunk;
+        const int wkey0 = key0 + wave * kKeysPerWave;
+        load_q(it, 0, qf);
+        load_k(it, kf);
+        load_v(it, vr);
+        transpose8x8_b16(vr[0]);                       // this item's V as the P . V B operand
+        transpose8x8_b16(vr[1]);
+
+        for (int mt = 0; mt < ntm; ++mt) {
+            // Rows of the accumulator layout held by this lane: 4 g4 + i.
+            int lastk[4];
+            bool rowok[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool vis = rowok[i] && key <= lastk[i];
-                sc[kt][i] = vis ? acc[i] * sh.scale : -INFINITY;
+                const int r = mt * 16 + g4 * 4 + i;
+                rowok[i] = r < R;
+                lastk[i] = rowok[i] ? last_key(it.kvlen, r / sh.G) : -1;
+                rowok[i] = rowok[i] && lastk[i] >= key0;
             }
-        }
-        // chunk max per row
-        float mx[4];
+            // Tile-uniform skip: no row of this tile reaches this chunk.
+            const int rlast = mt * 16 + 15 < R ? mt * 16 + 15 : R - 1;
+            const bool any = last_key(it.kvlen, rlast / sh.G) >= key0;
+            if (mt > 0) load_q(it, mt, qf);
+
+            // scores: tile kt -> lane (g4, c16) reg i = row 4 g4 + i, key wkey0 + 16 kt + c16
+            float sc[4][4];
+            if (any) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float m = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
+                for (int kt = 0; kt < 4; ++kt) {
+                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-            mx[i] = m;
-        }
-        if (c16 == 0) {
+                    for (int s = 0; s < 4; ++s) acc = mfma16<S>(qf[s], kf[kt][s], acc);
+                    const int key = wkey0 + kt * 16 + c16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xm[wave][g4 * 4 + i] = mx[i];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = g4 * 4 + i;
-            mx[i] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
-        }
-        // probabilities, row sums, and the bf16 P tile
-        float ls[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ls[i] = 0.0f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+                    for (int i = 0; i < 4; ++i) {
+                        const bool vis = rowok[i] && key <= lastk[i];
+                        sc[kt][i] = vis ? acc[i] * sh.scale : -INFINITY;
+                    }
+                }
+            }
+            if (!any) continue;
+
+            // chunk max per row
+            float mx[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool vis = sc[kt][i] != -INFINITY;
-                const float pv = vis ? expf(sc[kt][i] - mx[i]) : 0.0f;
-                ls[i] = ls[i] + pv;
-                pl[wave][g4 * 4 + i][kt * 16 + c16] = S::narrow(pv);
+                float m = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+                mx[i] = m;
             }
+            if (c16 == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float l = ls[i];
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) l = l + __shfl_xor(l, off, kWave);
-            ls[i] = l;
-        }
-        if (c16 == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xl[wave][g4 * 4 + i] = ls[i];
-        }
-        __syncthreads();
-        // o partial of this wave: P (16 x 64) . V (64 x 128)
-        uint4 pf[2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) pf[s2] = *reinterpret_cast<const uint4 *>(&pl[wave][c16][s2 * 32 + g4 * 8]);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(pf[s2], vf[dt][s2], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ol[wave][g4 * 4 + i][dt * 16 + c16] = acc[i];
-        }
-        __syncthreads();
-        // combine the four wave partials in order and write this chunk's partial
-        for (int e = threadIdx.x; e < 16 * kHeadDim; e += kAttnWaves * kWave) {
-            const int rr = e / kHeadDim, d = e % kHeadDim;
-            const int r = mt * 16 + rr;
-            if (r >= R) continue;
-            const int j = r / sh.G;
-            if (row_last_key(kvlen, sh.Q, j, sh.causal) < key0) continue;
-            const int64_t h = (int64_t)hk * sh.G + (r - j * sh.G);
-            float* dst = part + (((b * sh.Q + j) * sh.Hq + h) * sh.nchunks + c) * kPartStride;
-            const float o = ((ol[0][rr][d] + ol[1][rr][d]) + ol[2][rr][d]) + ol[3][rr][d];
-            dst[d] = o;
-            if (d == 0) {
-                dst[kHeadDim] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
-                dst[kHeadDim + 1] = ((xl[0][rr] + xl[1][rr]) + xl[2][rr]) + xl[3][rr];
+                for (int i = 0; i < 4; ++i) xm[wave][g4 * 4 + i] = mx[i];
             }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = g4 * 4 + i;
+                mx[i] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
+            }
+            // probabilities, row sums, and the bf16 P tile
+            float ls[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ls[i] = 0.0f;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool vis = sc[kt][i] != -INFINITY;
+                    const float pv = vis ? expf(sc[kt][i] - mx[i]) : 0.0f;
+                    ls[i] = ls[i] + pv;
+                    pl[wave][g4 * 4 + i][kt * 16 + c16] = S::narrow(pv);
+                }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float l = ls[i];
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) l = l + __shfl_xor(l, off, kWave);
+                ls[i] = l;
+            }
+            if (c16 == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xl[wave][g4 * 4 + i] = ls[i];
+            }
+            __syncthreads();
+            // o partial of this wave: P (16 x 64) . V (64 x 128)
+            uint4 pf[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) pf[s2] = *reinterpret_cast<const uint4 *>(&pl[wave][c16][s2 * 32 + g4 * 8]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(pf[s2], vr[s2][j], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ol[wave][g4 * 4 + i][c16 * 8 + j] = acc[i];
+            }
+            __syncthreads();
+            // combine the four wave partials in order and write this chunk's
+            // partial: thread -> row t / 16 of the tile, d in [8 (t % 16), +8)
+            {
+                const int rr = threadIdx.x >> 4, dg = threadIdx.x & 15;
+                const int r = mt * 16 + rr;
+                if (r < R) {
+                    const int j = r / sh.G;
+                    if (last_key(it.kvlen, j) >= key0) {
+                        const int64_t h = (int64_t)it.hk * sh.G + (r - j * sh.G);
+                        float *dst = part + ((((int64_t)it.b * sh.Q + j) * sh.Hq + h) * sh.nchunks + it.c) * kPartStride;
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const int d = dg * 8 + half * 4;
+                            const float4 o0 = *reinterpret_cast<const float4 *>(&ol[0][rr][d]);
+                            const float4 o1 = *reinterpret_cast<const float4 *>(&ol[1][rr][d]);
+                            const float4 o2 = *reinterpret_cast<const float4 *>(&ol[2][rr][d]);
+                            const float4 o3 = *reinterpret_cast<const float4 *>(&ol[3][rr][d]);
+                            float4 o;
+                            o.x = ((o0.x + o1.x) + o2.x) + o3.x;
+                            o.y = ((o0.y + o1.y) + o2.y) + o3.y;
+                            o.z = ((o0.z + o1.z) + o2.z) + o3.z;
+                            o.w = ((o0.w + o1.w) + o2.w) + o3.w;
+                            *reinterpret_cast<float4 *>(dst + d) = o;
+                        }
+                        if (dg == 0) {
+                            dst[kHeadDim] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
+                            dst[kHeadDim + 1] = ((xl[0][rr] + xl[1][rr]) + xl[2][rr]) + xl[3][rr];
+                        }
+                    }
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
@@ -334,10 +408,12 @@ template <typename S>
 static void launch_attn(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len, float *part,
                         const AttnShape &sh, int64_t chunk, hipStream_t st)
 {
-    const int64_t groups = cdiv(sh.B * sh.nchunks, 8);
-    hipLaunchKernelGGL((attn_chunk_kernel<S>), dim3((unsigned)(groups * 8 * sh.Hkv)),
-                       dim3(kAttnWaves * kWave), 0, st, (const uint16_t *)q, (const uint16_t *)k,
-                       (const uint16_t *)v, kv_len, part, sh);
+    // item ids (padded to whole groups of 8); a persistent grid of two
+    // workgroups per CU, a multiple of 8 so that a workgroup stays on one XCD
+    const int64_t nid = cdiv(sh.B * sh.nchunks, 8) * 8 * sh.Hkv;
+    const int64_t grid = std::min<int64_t>(nid, (int64_t)device_cu_count() * 2 / 8 * 8);
+    hipLaunchKernelGGL((attn_chunk_kernel<S>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st,
+                       (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, part, sh, nid);
     const size_t smem = (size_t)sh.nchunks * 2 * sizeof(float);
     hipLaunchKernelGGL((attn_merge_kernel<S>), dim3((unsigned)(sh.B * sh.Q * sh.Hq)), dim3(kHeadDim), smem, st,
                        (const float *)part, kv_len, (uint16_t *)o, sh, chunk);
