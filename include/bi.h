@@ -93,7 +93,7 @@ bi_status bi_matmul(const void *x, const void *w, void *y,
  * Dense matmul with a caller workspace: bitwise the same y as bi_matmul.
  * Same source as bi_matmul.  The reduction tree of every output is bi_matmul's
  * (K blocks of 128 in eight slots, block b in slot b mod 8, each slot summed
- * in ascending block order, the slots added pairwise).  For M <= 64 with
+ * in ascending block order, the slots added pairwise).  For 16 < M <= 64 with
  * transposed 16-bit weights, K a multiple of 128 and 16-byte aligned x, w and
  * workspace, the slots of one output may be computed by different workgroups;
  * the partial sums of aligned slot groups meet in the workspace and are added

@@ -276,7 +276,7 @@ void dense_stream_kernel(const typename S::store_t *__restrict__ x, const typena
     using T = typename S::store_t;
     constexpr int P = kDenseWaves;
     constexpr int TR = MT * 16, TC = NS * 16;
-    constexpr int DEPTH = MT == 1 ? 3 : (MT == 2 ? 2 : 1);
+    constexpr int DEPTH = MT <= 2 ? 2 : 1;
     __shared__ float red[P][TR][TC + 1];
 
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -482,8 +482,11 @@ static bool try_launch_stream(const void *x, const void *w, void *y, int64_t M, 
 // sum to the workspace; the last workgroup of the tile to arrive (counted with
 // a device-scope atomic) reads all group sums, adds them by the rest of
 // slot_tree and stores y.  Arrival order decides only who adds, never how.
-template <typename S, int MT, int Q>
-__global__ __launch_bounds__(kDenseWaves * kWave, 2)
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
+
+template <typename S, int MT, int Q, int DW, int OCC>
+__global__ __launch_bounds__(kDenseWaves * kWave, OCC)
 void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typename S::store_t *__restrict__ w,
                         typename S::store_t *__restrict__ y, float *__restrict__ part,
                         unsigned *__restrict__ counters, int64_t M, int64_t N, int64_t K)
@@ -496,8 +499,8 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
     constexpr int XS = KB + 8;                     // LDS row stride: 272 bytes, 16-byte aligned, 4-bank shift per row
     constexpr int XCH = TR * (KB / 8);             // 16-byte chunks in one block of x
     constexpr int XPT = XCH > NT ? XCH / NT : 1;   // chunks staged per thread
-    constexpr int DX = 3, DW = 4;                  // x and W register ring depths
-    constexpr int U = Q <= 4 ? 12 : 24;            // unroll: a multiple of 3 (LDS ring), DX, DW and Q
+    constexpr int DX = 3;                          // x register ring depth (DW: W ring depth)
+    constexpr int U = lcm_c(lcm_c(3, DW), Q);       // unroll: a multiple of the LDS ring (3 = DX), DW and Q
     static_assert(G::CPB == 4 && XPT <= 2 && (XCH % NT == 0 || XPT == 1), "slot kernel geometry");
     __shared__ __attribute__((aligned(16))) T xs[3][TR][XS];
     __shared__ int s_last;
@@ -579,17 +582,15 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
             load_w(wb[(d + DW - 1) % DW], u + DW - 1);
             __syncthreads();
             if ((u / Q) * P + slot0 + (d % Q) < nb) {
-                uint4 a[4][MT];
 #pragma unroll
-                for (int st = 0; st < 4; ++st)
+                for (int st = 0; st < 4; ++st) {
+                    uint4 a[MT];
 #pragma unroll
                     for (int m = 0; m < MT; ++m)
-                        a[st][m] = *reinterpret_cast<const uint4 *>(&xs[d % 3][m * 16 + c][G::chunk_off(g, st)]);
-                __builtin_amdgcn_sched_barrier(0);
+                        a[m] = *reinterpret_cast<const uint4 *>(&xs[d % 3][m * 16 + c][G::chunk_off(g, st)]);
 #pragma unroll
-                for (int st = 0; st < 4; ++st)
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) acc[d % Q][m] = DenseMfma<S>::mma(a[st][m], wb[d % DW][st], acc[d % Q][m]);
+                    for (int m = 0; m < MT; ++m) acc[d % Q][m] = DenseMfma<S>::mma(a[m], wb[d % DW][st], acc[d % Q][m]);
+                }
             }
         };
         // Whole unrolled rounds run without item guards (exact load waits);
@@ -625,20 +626,21 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
     if constexpr (GRP == 1) {
         store_y(h);
     } else {
-        // group sum -> workspace, one contiguous 64-lane record per (register, wave)
-        constexpr int REC = MT * 4 * kWave;
-        float *base = part + (int64_t)ct * GRP * P * REC;
-        float *mine = base + ((int64_t)grp * P + wave) * REC;
-        // The group sums are written and read with device-scope accesses (they
-        // go through to the level all CUs share), so no cache-wide write-back
-        // or invalidate is needed: the barrier waits for this workgroup's
-        // stores to complete before thread 0 bumps the tile's counter, and the
-        // last workgroup reads the sums only after it has seen the count.
+        // Group sums go to the workspace as 16-byte records, m-major: record
+        // (tile, group, wave, m) holds lane l's four values at byte 16 l.
+        // Stores and loads are device scope (sc1: through to the level every
+        // CU sees), so no cache-wide write-back or invalidate is needed: the
+        // wait below and the barrier order this workgroup's stores before
+        // thread 0 bumps the tile's counter, and the last workgroup reads the
+        // sums only after it has seen the count.
+        constexpr int CPOL_DEVICE = 16;            // sc1
+        constexpr int REC = MT * kWave * 16;       // bytes per (group, wave)
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(part + (int64_t)ct * GRP * P * (REC / 4), (short)0, GRP * P * REC, 0x00020000);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                __hip_atomic_store(&mine[(m * 4 + r) * kWave + lane], h[m][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, h[m]), rsrc,
+                                                   (grp * P + wave) * REC + m * kWave * 16 + lane * 16, 0, CPOL_DEVICE);
         __builtin_amdgcn_s_waitcnt(0);             // every store of this wave acknowledged
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -654,10 +656,8 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
             f32x4 v[GRP];
 #pragma unroll
             for (int q = 0; q < GRP; ++q)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    v[q][r] = __hip_atomic_load(base + ((int64_t)q * P + wave) * REC + (m * 4 + r) * kWave + lane,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rsrc, (q * P + wave) * REC + m * kWave * 16 + lane * 16, 0, CPOL_DEVICE));
             if constexpr (GRP == 2) out[m] = v[0] + v[1];
             else if constexpr (GRP == 4) out[m] = (v[0] + v[1]) + (v[2] + v[3]);
             else out[m] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
@@ -675,7 +675,7 @@ constexpr int64_t kSlotTileCols = kDenseWaves * 16;
 constexpr int64_t kSlotMaxTiles = 16384;                    // N up to 2^21 columns
 constexpr size_t kSlotCounterBytes = kSlotMaxTiles * sizeof(unsigned);
 
-static int slot_mt(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+static int slot_mt(int64_t M) { return M <= 32 ? 2 : 4; }
 
 static size_t slot_ws_bytes(int64_t M, int64_t N, int groups)
 {
@@ -691,7 +691,11 @@ static void launch_slots_t(const void *x, const void *w, void *y, void *ws, int6
     const int64_t ntc = cdiv(N, kSlotTileCols);
     unsigned *counters = (unsigned *)ws;
     float *part = (float *)((char *)ws + kSlotCounterBytes);
-    hipLaunchKernelGGL((dense_slots_kernel<S, MT, Q>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
+    // W ring depth and waves per SIMD: two workgroups per CU (at most 128
+    // VGPRs) wherever the accumulators allow it.
+    constexpr int DW = MT == 4 ? 2 : 4;
+    constexpr int OCC = Q * MT <= 4 ? 4 : 2;
+    hipLaunchKernelGGL((dense_slots_kernel<S, MT, Q, DW, OCC>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
                        dim3(kDenseWaves * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, counters, M, N, K);
 }
 
@@ -718,12 +722,13 @@ static bool try_launch_slots(const void *x, const void *w, void *y, void *ws, si
                              int64_t N, int64_t K, hipStream_t st)
 {
     using G = DenseGeom<S>;
-    if (!ws || M > 64 || K % G::KB != 0 || !host_aligned16(x) || !host_aligned16(w) || !host_aligned16(ws))
+    // M <= 16: x is small, and bi_matmul's one-workgroup-per-tile kernel,
+    // which needs no exchange of partial sums, streams W faster.
+    if (!ws || M <= 16 || M > 64 || K % G::KB != 0 || !host_aligned16(x) || !host_aligned16(w) ||
+        !host_aligned16(ws))
         return false;
     if (ws_bytes < slot_ws_bytes(M, N, kDenseWaves)) return false;
-    const int mt = slot_mt(M);
-    if (mt == 1) launch_slots_mt<S, 1>(x, w, y, ws, M, N, K, st);
-    else if (mt == 2) launch_slots_mt<S, 2>(x, w, y, ws, M, N, K, st);
+    if (slot_mt(M) == 2) launch_slots_mt<S, 2>(x, w, y, ws, M, N, K, st);
     else launch_slots_mt<S, 4>(x, w, y, ws, M, N, K, st);
     return true;
 }
@@ -781,7 +786,7 @@ extern "C" bi_status bi_matmul(const void *x, const void *w, void *y, int64_t M,
 
 extern "C" size_t bi_matmul_ws_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t w_transposed)
 {
-    if (M < 1 || N < 1 || K < 1 || M > 64 || !w_transposed || (dtype != BI_BF16 && dtype != BI_F16) ||
+    if (M <= 16 || N < 1 || K < 1 || M > 64 || !w_transposed || (dtype != BI_BF16 && dtype != BI_F16) ||
         cdiv(N, kSlotTileCols) > kSlotMaxTiles)
         return 0;
     return slot_ws_bytes(M, N, kDenseWaves);

@@ -34,16 +34,16 @@ def same(a, b):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("M,N,K", [
-    (1, 96, 128),          # one block: slots 1..7 own nothing
-    (3, 1000, 896),        # 7 blocks, ragged column tile
+    (1, 96, 128),          # M <= 16: bi_matmul's kernels
+    (17, 96, 128),         # one block: slots 1..7 own nothing
+    (23, 1000, 896),       # 7 blocks, ragged column tile
     (16, 4096, 4096),
     (17, 6144, 4096),      # two row tiles of the 32-row form
     (33, 4096, 14336),     # the down projection, 112 blocks
     (64, 4096, 4096),
     (64, 1000, 4224),      # 33 blocks: uneven slots
     (64, 6144, 4096),
-    (16, 32768, 1024),     # enough column tiles for all eight slots in one workgroup
-    (32, 32768, 1024),
+    (32, 32768, 1024),     # enough column tiles for all eight slots in one workgroup
     (64, 32768, 1024),
     (65, 512, 4096),       # long M: bi_matmul's kernels
     (64, 512, 4100),       # K not a multiple of 128: bi_matmul's kernels
@@ -77,7 +77,7 @@ def test_decoder_shapes_and_every_m():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("M,N,K", [(64, 1000, 4224), (5, 300, 1024), (64, 128, 256)])
+@pytest.mark.parametrize("M,N,K", [(64, 1000, 4224), (25, 300, 1024), (64, 128, 256)])
 def test_oracle_parity(dtype, M, N, K):
     x, wt, _ = inputs.dense_case(M, N, K, dtype, seed=M + N + K)
     ws = bi.matmul_workspace(M, N, K, TD[dtype], device=dev())
