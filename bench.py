@@ -18,6 +18,7 @@ shape, and the cost of invariance against split-K comparison variants.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -56,6 +57,24 @@ def step_traffic(cfg, B, ctx):
     return dict(mm=mm, mm_bytes=mm_bytes, mm_flops=mm_flops, norm_bytes=norm_bytes, attn_bytes=attn_bytes,
                 attn_flops=attn_flops, glue_bytes=glue_bytes,
                 total_bytes=mm_bytes + norm_bytes + attn_bytes + glue_bytes, total_flops=mm_flops + attn_flops)
+
+
+def measured_traffic():
+    """HBM bytes per matmul launch from the committed counter runs
+    (profiles/dense_slots_kernel_decode_b64_traffic.json), or None when the
+    kernel sources have changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "dense_slots_kernel_decode_b64_traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest()[:16] != rec["source_sha256_16"]:
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids, budget_s):
@@ -152,17 +171,22 @@ def main():
     ms_step = (t1 - t0) * 1e3 / K
 
     # Roofline pass, right after: the same K steps again (the cache keeps
-    # growing as in the timed region), with HIP events on the launch stream
-    # around every matmul launch.  The events lengthen the step, not the
-    # launches they bracket.
+    # growing as in the timed region).  Every matmul launch carries a pair of
+    # HIP events on its stream that the launch itself records as the kernel
+    # starts and ends (bi_time_next_launch -> hipExtLaunchKernel), i.e. the
+    # kernel's own duration, as a kernel trace reports it.
+    L = bi.lib()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K * len(mm_idx))]
+    for s_, t_ in ev:                          # create the event handles
+        s_.record(stream)
+        t_.record(stream)
+    torch.cuda.synchronize()
     e = 0
     for _ in range(K):
         for i, (name, fn, a) in enumerate(plan):
             if name == "matmul":
-                ev[e][0].record(stream)
+                L.bi_time_next_launch(ctypes.c_void_p(ev[e][0].cuda_event), ctypes.c_void_p(ev[e][1].cuda_event))
                 rc = fn(*a)
-                ev[e][1].record(stream)
                 e += 1
             else:
                 rc = fn(*a)
@@ -196,7 +220,9 @@ def main():
                                "launches; achieved = all matmul algorithmic bytes / all matmul launch time)",
                      "bound": "hbm",
                      "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE, B=64 ctx 768 step mix)",
+                     "algorithmic_bytes_per_launch": round(tr["mm_bytes"] / len(mm_idx)),
                      "launches_per_step": len(mm_idx), "avg_launch_us": round(mm_avg_us, 2),
                      "share_of_step": round(mm_ms / K / ms_step, 3),
                      "per_shape": {f"{B}x{N}x{Kk}": {"us": round(1e3 * np.mean(v), 1),

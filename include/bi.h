@@ -254,6 +254,16 @@ bi_status bi_rmsnorm_split(const void *x, const void *w, void *y, int64_t rows, 
                            float eps, int32_t dtype, int32_t splits,
                            void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement hook (not part of any computation): the next kernel that a
+ * dense matmul entry point (bi_matmul, bi_matmul_ws, bi_matmul_split's
+ * partial pass) launches from the calling host thread records `start` when
+ * it begins executing and `stop` when it ends (hipExtLaunchKernel), so
+ * hipEventElapsedTime(start, stop) is that kernel's own duration without its
+ * dispatch.  Either event may be NULL.  One launch consumes the setting.
+ * ------------------------------------------------------------------------ */
+bi_status bi_time_next_launch(hipEvent_t start, hipEvent_t stop);
+
 /* ------------------------------------------------------------------------ */
 /* Human-readable status name (static string, never NULL). */
 const char *bi_status_str(int32_t status);

@@ -4,6 +4,7 @@
 // the library is built for gfx950 only.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,6 +91,32 @@ __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(th
 __device__ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline bool host_aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// One-shot launch timing: when set (bi_time_next_launch), the next kernel
+// the library launches on this host thread records `start` as it begins
+// executing and `stop` as it ends (hipExtLaunchKernel), so the pair brackets
+// the kernel itself rather than its dispatch.
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+inline LaunchTiming &launch_timing()
+{
+    static thread_local LaunchTiming t;
+    return t;
+}
+template <typename... Params, typename... Args>
+inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, size_t smem, hipStream_t st,
+                          Args... args)
+{
+    LaunchTiming &t = launch_timing();
+    if (t.start != nullptr || t.stop != nullptr) {
+        const LaunchTiming use = t;
+        t = LaunchTiming{};
+        hipExtLaunchKernelGGL(kernel, grid, block, smem, st, use.start, use.stop, 0, args...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, smem, st, args...);
+    }
+}
 
 // Compute units of the current device (cached per device; 256 if unknown).
 inline int device_cu_count()

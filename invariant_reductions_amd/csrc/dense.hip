@@ -419,10 +419,10 @@ static void launch_dense_t(const void *x, const void *w, void *y, float *part, i
     // The split comparison variant is its own instantiation, so profiles of the
     // invariant kernel never mix in its launches.
     if (part)
-        hipLaunchKernelGGL((dense_kernel<S, TRANS, VEC, MT, NS, true>), grid, dim3(kDenseWaves * kWave), 0, st,
+        launch_kernel((dense_kernel<S, TRANS, VEC, MT, NS, true>), grid, dim3(kDenseWaves * kWave), 0, st,
                            (const T *)x, (const T *)w, (T *)y, part, M, N, K, nblocks, splits);
     else
-        hipLaunchKernelGGL((dense_kernel<S, TRANS, VEC, MT, NS, false>), grid, dim3(kDenseWaves * kWave), 0, st,
+        launch_kernel((dense_kernel<S, TRANS, VEC, MT, NS, false>), grid, dim3(kDenseWaves * kWave), 0, st,
                            (const T *)x, (const T *)w, (T *)y, part, M, N, K, nblocks, splits);
 }
 
@@ -447,7 +447,7 @@ static void launch_stream_t(const void *x, const void *w, void *y, int64_t M, in
     const int64_t ntm = cdiv(M, MT * 16), ntn = cdiv(N, NS * 16);
     const int per_cu = (MT >= 4 && NS >= 2) ? 1 : 2;             // resident workgroups per CU at the register cap
     const int64_t grid = std::min<int64_t>(ntm * ntn, (int64_t)device_cu_count() * per_cu);
-    hipLaunchKernelGGL((dense_stream_kernel<S, MT, NS>), dim3((unsigned)grid), dim3(kDenseWaves * kWave), 0, st,
+    launch_kernel((dense_stream_kernel<S, MT, NS>), dim3((unsigned)grid), dim3(kDenseWaves * kWave), 0, st,
                        (const T *)x, (const T *)w, (T *)y, M, N, K, ntm, ntn);
 }
 
@@ -695,7 +695,7 @@ static void launch_slots_t(const void *x, const void *w, void *y, void *ws, int6
     // VGPRs) wherever the accumulators allow it.
     constexpr int DW = MT == 4 ? 2 : 4;
     constexpr int OCC = Q * MT <= 4 ? 4 : 2;
-    hipLaunchKernelGGL((dense_slots_kernel<S, MT, Q, DW, OCC>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
+    launch_kernel((dense_slots_kernel<S, MT, Q, DW, OCC>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
                        dim3(kDenseWaves * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, counters, M, N, K);
 }
 
@@ -832,8 +832,14 @@ extern "C" bi_status bi_matmul_split(const void *x, const void *w, void *y, int6
     dispatch_dense(x, w, y, part, M, N, K, dtype, w_transposed != 0, splits, stream);
     const int64_t MN = M * N;
     const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(MN, 256), 65536);
-    if (dtype == BI_BF16) hipLaunchKernelGGL(split_reduce_kernel<BF16>, dim3(blocks), dim3(256), 0, stream, part, (uint16_t *)y, MN, splits);
-    else if (dtype == BI_F16) hipLaunchKernelGGL(split_reduce_kernel<F16>, dim3(blocks), dim3(256), 0, stream, part, (uint16_t *)y, MN, splits);
-    else hipLaunchKernelGGL(split_reduce_kernel<F32>, dim3(blocks), dim3(256), 0, stream, part, (float *)y, MN, splits);
+    if (dtype == BI_BF16) launch_kernel(split_reduce_kernel<BF16>, dim3(blocks), dim3(256), 0, stream, part, (uint16_t *)y, MN, splits);
+    else if (dtype == BI_F16) launch_kernel(split_reduce_kernel<F16>, dim3(blocks), dim3(256), 0, stream, part, (uint16_t *)y, MN, splits);
+    else launch_kernel(split_reduce_kernel<F32>, dim3(blocks), dim3(256), 0, stream, part, (float *)y, MN, splits);
     return launch_status();
+}
+
+extern "C" bi_status bi_time_next_launch(hipEvent_t start, hipEvent_t stop)
+{
+    bi::launch_timing() = bi::LaunchTiming{start, stop};
+    return BI_OK;
 }

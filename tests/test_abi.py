@@ -150,6 +150,12 @@ def test_add_rmsnorm_validation():
     assert L.bi_add_rmsnorm(A, A, A, A, A, 4, 4096, 1e-6, 9, None) == DTYPE
 
 
+def test_time_next_launch_is_host_only():
+    """Setting and clearing the one-shot timing hook touches no device."""
+    L = bi.lib()
+    assert L.bi_time_next_launch(None, None) == OK
+
+
 def test_glue_validation():
     L = bi.lib()
     assert L.bi_embed(None, A, A, 1, 10, 64, None) == NULL
