@@ -22,7 +22,7 @@
 
 namespace bi {
 
-constexpr int kNormRowsPerBlock = 4;      // free: rows per workgroup (one per wave)
+constexpr int kNormRowsPerBlock = 1;      // free: rows per workgroup (one per wave); one row spreads short batches over more CUs
 constexpr int kNormCached = 8;            // free: chunks per lane kept in registers
 
 template <typename S>
@@ -136,8 +136,14 @@ void rmsnorm_kernel(const typename S::store_t *x, const typename S::store_t *__r
     const int64_t nch = cdiv(H, E);
 
     if (CACHED) {
-        uint4 cache[kNormCached];
+        uint4 cache[kNormCached], wc[kNormCached];
         float ss = 0.0f;
+        // the weight chunks are requested with the row, ahead of the sum
+#pragma unroll
+        for (int i = 0; i < kNormCached; ++i) {
+            const int64_t v = lane + (int64_t)i * kWave;
+            wc[i] = load_chunk<S, VEC>(w, v * E, H, v < nch);
+        }
 #pragma unroll
         for (int i = 0; i < kNormCached; ++i) {
             const int64_t v = lane + (int64_t)i * kWave;
@@ -155,7 +161,7 @@ void rmsnorm_kernel(const typename S::store_t *x, const typename S::store_t *__r
             if (v >= nch) break;
             float xv[E], wv[E], yv[E];
             chunk_vals<S>(cache[i], xv);
-            chunk_vals<S>(load_chunk<S, VEC>(w, v * E, H, true), wv);
+            chunk_vals<S>(wc[i], wv);
 #pragma unroll
             for (int e = 0; e < E; ++e) yv[e] = (xv[e] * inv) * wv[e];
             store_chunk<S, VEC>(yr, v * E, H, yv);
