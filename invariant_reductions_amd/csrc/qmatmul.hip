@@ -20,6 +20,8 @@
 // Bounds: a block that runs past K reads no packed word, scale or bias at or
 // beyond K and feeds exact zeros to the MFMA; a column n >= N reads nothing and
 // stores nothing.  The K % 32 == 16 shape (nvfp4) takes the word-granular path.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace bi {
@@ -77,14 +79,45 @@ __device__ inline uint16_t deq1(uint32_t q, const QGroup<QM> &g)
     return F16::narrow(v);
 }
 
-// Eight codes of one word -> one 16-byte MFMA operand chunk (element e = nibble e).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Eight codes of one word -> one 16-byte MFMA operand chunk (element e =
+// nibble e), the same values deq1 gives:
+//   affine: the nibbles are split into bytes (codes 0,2,4,6 and 1,3,5,7),
+//           converted exactly to fp32, w = fma(s, q, b) in fp32, and each
+//           pair rounded to binary16 (RNE) by one packed conversion;
+//   nvfp4 : code c = sign | e | m is placed as the binary16 pattern
+//           (sign << 15) | ((e, m) << 9), whose value is e2m1(c) * 2^-14
+//           exactly (e = 0 lands in the subnormal range, m * 2^-15); one
+//           packed multiply by 2^14 and one by the scale give e2m1 * scale,
+//           exact in binary16 (at most 6 significant bits, |w| <= 2688,
+//           smallest magnitude 2^-10).
 template <int QM>
 __device__ inline uint4 deq_word(uint32_t w, const QGroup<QM> &g)
 {
-    uint16_t h[8];
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    uint32_t out[4];
+    if constexpr (QM == BI_AFFINE) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = deq1<QM>((w >> (4 * e)) & 15u, g);
-    return __builtin_bit_cast(uint4, h);
+        for (int p = 0; p < 4; ++p) {
+            const float q0 = (float)((lo >> (8 * p)) & 0xffu), q1 = (float)((hi >> (8 * p)) & 0xffu);
+            const f32x2 v = f32x2{__builtin_fmaf(g.s, q0, g.b), __builtin_fmaf(g.s, q1, g.b)};
+            out[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+        }
+    } else {
+        const _Float16 sh = (_Float16)g.s;                 // e4m3 values are exact in binary16
+        const f16x2 sv = f16x2{sh, sh}, k14 = f16x2{(_Float16)16384.0f, (_Float16)16384.0f};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            // code 2p -> bits 0..3, code 2p + 1 -> bits 16..19
+            const uint32_t t = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | (uint32_t)p | ((uint32_t)(4 + p) << 16));
+            const uint32_t bits = ((t & 0x00080008u) << 12) | ((t & 0x00070007u) << 9);
+            const f16x2 v = (__builtin_bit_cast(f16x2, bits) * k14) * sv;
+            out[p] = __builtin_bit_cast(uint32_t, v);
+        }
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
 // Transposed weights [N, K/8]: lane (g, c) of block b supplies the 32 codes of
@@ -221,6 +254,154 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
     }
 }
 
+// Persistent streaming form of the same reduction for short M (at most 16
+// rows), transposed weights, K a multiple of the block and 16-byte aligned x
+// and wq.  A fixed grid walks the output tiles (16 rows x NS*16 columns) t =
+// blockIdx.x, blockIdx.x + gridDim.x, ...; each wave streams its (tile,
+// block) items -- packed words, group constants and x chunks -- through a
+// register ring of D items that runs across tile boundaries, and
+// dequantizes an item only when it multiplies it.  Per output the tree is
+// exactly qmatmul_kernel's: block b of K belongs to wave b mod 8, lane group
+// g supplies [32g, 32g + 32) of the block as four steps, wave partials are
+// added in wave order.
+template <int QM, int GS, int NS, int D>
+__global__ __launch_bounds__(kQWaves * kWave, 2)
+void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wq,
+                           const void *__restrict__ scales, const uint16_t *__restrict__ biases,
+                           uint16_t *__restrict__ y, int64_t M, int64_t N, int64_t K, int ntn)
+{
+    constexpr int P = kQWaves, TC = NS * 16;
+    __shared__ float red[P][16][TC + 1];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    const int nb = (int)(K / kQBlock);
+    const int nmine = wave < nb ? (nb - wave + P - 1) / P : 0;        // blocks of this wave per tile
+    const int mytiles = (int)blockIdx.x < ntn ? (ntn - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    const int items = mytiles * nmine;
+    const int64_t words = K / 8, groups = K / GS;
+    // x row of A-operand row c; rows >= M read row M - 1 and are never stored
+    const uint16_t *xr = x + (int64_t)(c < M ? c : M - 1) * K + g * 32;
+
+    uint4 Wr[D][NS], Xr[D][4];
+    uint32_t Sr[D][NS], Br[D][NS];
+    // prefetch cursor: item (pu, pj) = block wave + pj*P of tile pu; holds at the last item
+    int pu = 0, pj = 0;
+    auto load_next = [&](uint4 (&Wd)[NS], uint32_t (&Sd)[NS], uint32_t (&Bd)[NS], uint4 (&Xd)[4]) {
+        const int64_t t = (int64_t)blockIdx.x + (int64_t)pu * gridDim.x;
+        const int64_t kb = (int64_t)(wave + pj * P) * kQBlock + g * 32;     // this lane's first code
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            int64_t n = t * TC + j * 16 + c;
+            n = n < N ? n : N - 1;                                          // padding columns read a real row
+            Wd[j] = *reinterpret_cast<const uint4 *>(wq + n * words + kb / 8);
+            const int64_t gi = n * groups + kb / GS;
+            if (QM == BI_AFFINE) {
+                Sd[j] = ((const uint16_t *)scales)[gi];
+                Bd[j] = biases[gi];
+            } else {
+                Sd[j] = ((const uint16_t *)scales)[gi / 2];                 // the lane's two group bytes
+                Bd[j] = 0;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Xd[s] = *reinterpret_cast<const uint4 *>(xr + (kb - g * 32) + s * 8);
+        if (pj + 1 < nmine) {
+            ++pj;
+        } else if (pu + 1 < mytiles) {
+            pj = 0;
+            ++pu;
+        }
+    };
+    f32x4 acc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto finish_tile = [&](int u) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][j * 16 + c] = acc[j][r];
+            acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+        const int64_t n0 = ((int64_t)blockIdx.x + (int64_t)u * gridDim.x) * TC;
+        for (int o = threadIdx.x; o < 16 * TC; o += P * kWave) {
+            const int r = o / TC, cc = o % TC;
+            const int64_t col = n0 + cc;
+            if (r >= M || col >= N) continue;
+            float v = red[0][r][cc];
+#pragma unroll
+            for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+            y[(int64_t)r * N + col] = F16::narrow(v);
+        }
+        __syncthreads();
+    };
+
+    if (items > 0) {
+        int cu = 0, cj = 0;
+        static_for<0, D - 1>([&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+            load_next(Wr[d], Sr[d], Br[d], Xr[d]);
+        });
+        for (int i = 0; i < items; i += D) {
+            static_for<0, D>([&](auto dc) {
+                constexpr int d = decltype(dc)::value;
+                constexpr int dn = (d + D - 1) % D;
+                load_next(Wr[dn], Sr[dn], Br[dn], Xr[dn]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i + d < items) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                        for (int j = 0; j < NS; ++j) {
+                            QGroup<QM> gr;
+                            if (QM == BI_AFFINE) {
+                                gr.s = F16::widen((uint16_t)Sr[d][j]);
+                                gr.b = F16::widen((uint16_t)Br[d][j]);
+                            } else {
+                                gr.s = e4m3_to_f32((Sr[d][j] >> (s < 2 ? 0 : 8)) & 0xffu);
+                                gr.b = 0.0f;
+                            }
+                            const uint32_t wv = s == 0 ? Wr[d][j].x : s == 1 ? Wr[d][j].y : s == 2 ? Wr[d][j].z : Wr[d][j].w;
+                            acc[j] = qmfma(Xr[d][s], deq_word<QM>(wv, gr), acc[j]);
+                        }
+                    }
+                    if (++cj == nmine) {
+                        finish_tile(cu);
+                        cj = 0;
+                        ++cu;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+    } else {
+        // a wave that owns no block of K still takes part in every combine
+        for (int u = 0; u < mytiles; ++u) finish_tile(u);
+    }
+}
+
+template <int QM, int GS, int NS>
+static void launch_q_stream_t(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
+                              int64_t N, int64_t K, hipStream_t st)
+{
+    const int64_t ntn = cdiv(N, NS * 16);
+    const int64_t grid = std::min<int64_t>(ntn, (int64_t)device_cu_count() * 2);
+    hipLaunchKernelGGL((qmatmul_stream_kernel<QM, GS, NS, 3>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
+                       (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, M, N, K, (int)ntn);
+}
+
+template <int QM, int GS>
+static bool try_launch_q_stream(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
+                                int64_t N, int64_t K, hipStream_t st)
+{
+    if (M > 16 || K % kQBlock != 0 || !host_aligned16(x) || !host_aligned16(wq) || cdiv(N, 16) > (1ll << 30))
+        return false;
+    if (N >= 8192) launch_q_stream_t<QM, GS, 2>(x, wq, s, b, y, M, N, K, st);
+    else launch_q_stream_t<QM, GS, 1>(x, wq, s, b, y, M, N, K, st);
+    return true;
+}
+
 template <int QM, int GS, bool TRANS, bool WVEC, int MT>
 static void launch_q_t(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                        int64_t N, int64_t K, hipStream_t st)
@@ -245,6 +426,7 @@ static void launch_q(const void *x, const uint32_t *wq, const void *s, const voi
                      int64_t K, bool trans, hipStream_t st)
 {
     if (!trans) launch_q_mt<QM, GS, false, false>(x, wq, s, b, y, M, N, K, st);
+    else if (try_launch_q_stream<QM, GS>(x, wq, s, b, y, M, N, K, st)) return;
     else if (K % 32 == 0 && host_aligned16(wq)) launch_q_mt<QM, GS, true, true>(x, wq, s, b, y, M, N, K, st);
     else launch_q_mt<QM, GS, true, false>(x, wq, s, b, y, M, N, K, st);
 }
