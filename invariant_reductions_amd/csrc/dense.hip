@@ -706,11 +706,11 @@ static void launch_slots_mt(const void *x, const void *w, void *y, void *ws, int
                             hipStream_t st)
 {
     const int64_t ntc = cdiv(N, kSlotTileCols), cu = device_cu_count();
-    if constexpr (MT < 4) {
-        if (ntc >= cu) {
-            launch_slots_t<S, MT, 8>(x, w, y, ws, M, N, K, st);
-            return;
-        }
+    // All eight slots in one workgroup (no exchange) once the column tiles
+    // alone come close to one per CU.
+    if (ntc * 4 >= cu * 3) {
+        launch_slots_t<S, MT, 8>(x, w, y, ws, M, N, K, st);
+        return;
     }
     if (ntc * 2 >= cu) launch_slots_t<S, MT, 4>(x, w, y, ws, M, N, K, st);
     else if (ntc * 4 >= cu) launch_slots_t<S, MT, 2>(x, w, y, ws, M, N, K, st);
