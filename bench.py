@@ -4,8 +4,8 @@ One step = one greedy decode step of the 4-layer Llama-style decoder (hidden
 4096, 32 query / 8 KV heads, head_dim 128, SwiGLU 14336, vocab 32000, bf16,
 random init) for B sequences at a context of `--ctx` tokens: embedding,
 4 x (RMSNorm, QKV matmul, RoPE + KV-cache write, two-pass attention, O
-matmul, residual add, RMSNorm, gate/up matmul, SiLU*mul, down matmul,
-residual add), final RMSNorm, LM-head matmul, argmax -- every reduction
+matmul, residual add, RMSNorm, gate/up matmul with the SiLU*mul activation,
+down matmul, residual add), final RMSNorm, LM-head matmul, argmax -- every reduction
 through the invariant kernels.  Inputs (weights, KV cache, token ids) are
 seeded synthetic data resident in HBM before timing starts.
 
@@ -39,12 +39,15 @@ def step_traffic(cfg, B, ctx):
     written once, at its storage size)."""
     H, Hq, Hkv, D, F, V, L = (cfg[k] for k in ("hidden", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "n_layers"))
     qkvn = (Hq + 2 * Hkv) * D
-    mm = []                                                   # (M, N, K) of every matmul launch
+    # (M, N, K, columns stored) of every matmul launch; the gate/up product
+    # stores only its SwiGLU activation (F columns), fused into the matmul
+    mm = []
     for _ in range(L):
-        mm += [(B, qkvn, H), (B, H, Hq * D), (B, 2 * F, H), (B, H, F)]
-    mm.append((B, V, H))
-    mm_bytes = sum(2 * (N * K + M * K + M * N) for M, N, K in mm)
-    mm_flops = sum(2 * M * N * K for M, N, K in mm)
+        mm += [(B, qkvn, H, qkvn), (B, H, Hq * D, H), (B, 2 * F, H, F), (B, H, F, H)]
+    mm.append((B, V, H, V))
+    mm_bytes = sum(2 * (N * K + M * K + M * O) for M, N, K, O in mm)
+    swiglu_bytes = L * 2 * (2 * F * H + B * H + B * F)
+    mm_flops = sum(2 * M * N * K for M, N, K, _ in mm)
     # one plain RMSNorm (x -> h), then 2L residual adds fused with the norm that
     # follows them (x, r -> x, h)
     norm_bytes = (4 * B * H + 2 * H) + 2 * L * (8 * B * H + 2 * H)
@@ -52,10 +55,9 @@ def step_traffic(cfg, B, ctx):
     attn_flops = L * 4 * B * Hq * D * ctx
     glue_bytes = (2 * B * H * 2                              # embed
                   + L * (2 * B * qkvn + 2 * B * Hq * D + 4 * B * Hkv * D)   # rope + cache write
-                  + L * (2 * B * 2 * F + 2 * B * F)          # silu*mul
                   + 2 * B * V)                               # argmax
-    return dict(mm=mm, mm_bytes=mm_bytes, mm_flops=mm_flops, norm_bytes=norm_bytes, attn_bytes=attn_bytes,
-                attn_flops=attn_flops, glue_bytes=glue_bytes,
+    return dict(mm=mm, mm_bytes=mm_bytes, swiglu_bytes=swiglu_bytes, mm_flops=mm_flops, norm_bytes=norm_bytes,
+                attn_bytes=attn_bytes, attn_flops=attn_flops, glue_bytes=glue_bytes,
                 total_bytes=mm_bytes + norm_bytes + attn_bytes + glue_bytes, total_flops=mm_flops + attn_flops)
 
 
@@ -146,8 +148,12 @@ def main():
     calib2.copy_(calib)
     del calib, calib2
     plan = model.plan(B, 1, cap, stream)
-    mm_idx = [i for i, s in enumerate(plan) if s[0] == "matmul"]
-    mm_shape = [(plan[i][2][4], plan[i][2][5]) for i in mm_idx]          # (N, K) of each matmul launch
+    MM_OPS = ("matmul", "matmul_swiglu")
+    mm_idx = [i for i, s in enumerate(plan) if s[0] in MM_OPS]
+    # (N, K) of each matmul launch (the fused gate/up call passes F = N / 2)
+    mm_shape = [(plan[i][2][4] * (2 if plan[i][0] == "matmul_swiglu" else 1), plan[i][2][5]) for i in mm_idx]
+    mm_out = {(plan[i][2][4] * 2, plan[i][2][5]) if plan[i][0] == "matmul_swiglu" else (plan[i][2][4], plan[i][2][5]):
+              plan[i][2][4] for i in mm_idx}                                  # columns stored per shape
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -184,7 +190,7 @@ def main():
     e = 0
     for _ in range(K):
         for i, (name, fn, a) in enumerate(plan):
-            if name == "matmul":
+            if name in MM_OPS:
                 L.bi_time_next_launch(ctypes.c_void_p(ev[e][0].cuda_event), ctypes.c_void_p(ev[e][1].cuda_event))
                 rc = fn(*a)
                 e += 1
@@ -216,8 +222,9 @@ def main():
                    "batch": B, "context": ctx, "layers": cfg["n_layers"]},
         "tflops": round(tr["total_flops"] / (ms_step * 1e-3) / 1e12, 3),
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
-        "roofline": {"kernel": "bi_matmul_ws -> dense_slots_kernel<bf16, MT, Q> (every instantiation the step "
-                               "launches; achieved = all matmul algorithmic bytes / all matmul launch time)",
+        "roofline": {"kernel": "bi_matmul_ws / bi_matmul_swiglu -> dense_slots_kernel<bf16, MT, Q, EPI> (every "
+                               "instantiation the step launches; achieved = all matmul algorithmic bytes / all "
+                               "matmul launch time)",
                      "bound": "hbm",
                      "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
@@ -226,7 +233,8 @@ def main():
                      "launches_per_step": len(mm_idx), "avg_launch_us": round(mm_avg_us, 2),
                      "share_of_step": round(mm_ms / K / ms_step, 3),
                      "per_shape": {f"{B}x{N}x{Kk}": {"us": round(1e3 * np.mean(v), 1),
-                                                     "gbs": round(2 * (N * Kk + B * Kk + B * N) / (np.mean(v) * 1e-3) / 1e9, 1)}
+                                                     "gbs": round(2 * (N * Kk + B * Kk + B * mm_out[(N, Kk)])
+                                                                  / (np.mean(v) * 1e-3) / 1e9, 1)}
                                    for (N, Kk), v in per_shape.items()}},
         "setup_s": round(setup_s, 1),
     }
@@ -266,7 +274,8 @@ def op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch):
             tot[name] = tot.get(name, 0.0) + s.elapsed_time(t) / reps
     tr = step_traffic(cfg, B, ctx_mean)
     H, L = cfg["hidden"], cfg["n_layers"]
-    bytes_of = {"matmul": tr["mm_bytes"], "sdpa": tr["attn_bytes"], "rmsnorm": 4 * B * H + 2 * H,
+    bytes_of = {"matmul": tr["mm_bytes"] - tr["swiglu_bytes"], "matmul_swiglu": tr["swiglu_bytes"],
+                "sdpa": tr["attn_bytes"], "rmsnorm": 4 * B * H + 2 * H,
                 "add_rmsnorm": 2 * L * (8 * B * H + 2 * H)}
     res = {}
     for name, ms in tot.items():
@@ -297,7 +306,7 @@ def split_overhead(torch, bi, model, B, per_shape):
     dev = model.dev
     res = {}
     mats = {(model.qkvn, model.H): [L["wqkv"] for L in model.layers], (model.H, model.qn): [L["wo"] for L in model.layers],
-            (2 * model.F, model.H): [L["wgu"] for L in model.layers], (model.H, model.F): [L["wdown"] for L in model.layers],
+            (2 * model.F, model.H): [L["wgu_il"] for L in model.layers], (model.H, model.F): [L["wdown"] for L in model.layers],
             (model.V, model.H): [model.lm_head]}
     for (N, K), ws_list in mats.items():
         x = torch.randn(B, K, device=dev).to(torch.bfloat16)

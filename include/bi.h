@@ -115,6 +115,31 @@ bi_status bi_matmul_ws(const void *x, const void *w, void *y, int64_t M, int64_t
                        int32_t dtype, int32_t w_transposed, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Gate/up projection fused with the SwiGLU activation of a Llama-style MLP:
+ *   a[m, i] = RNE(silu(g) * u),  g = (x . Wg^T)[m, i] and u = (x . Wu^T)[m, i]
+ *   each rounded to bf16 first, silu(g) = g / (1 + exp(-g)) in fp32
+ * -- bitwise what bi_matmul (or bi_matmul_ws) followed by bi_silu_mul gives.
+ * Source: "Batch-invariant kernels ...", Mental model (pointwise ops are
+ * invariant, so fusing the activation into the reduction that produces its
+ * input changes no tree) and Case 6 (the decoder's MLP).
+ *   x    : [M, K] bf16.
+ *   w_il : [2F, K] bf16, the gate and up weights interleaved in blocks of 64
+ *          rows: rows [128 i, 128 i + 64) are gate rows [64 i, 64 i + 64),
+ *          rows [128 i + 64, 128 i + 128) are up rows [64 i, 64 i + 64).
+ *   a    : [M, F] bf16, 16-byte aligned.  F % 64 == 0.
+ *   ws   : at least bi_matmul_swiglu_workspace_bytes(M, F, K, dtype) bytes,
+ *          16-byte aligned, zero-filled before first use.  Its first 64 KiB
+ *          are counters that every call leaves zero (as in bi_matmul_ws, and
+ *          one workspace may serve both entry points in stream order); the
+ *          rest is scratch: the slot form's group sums, or for any other
+ *          shape the [M, 2F] gate/up product before the activation.
+ *   dtype: BI_BF16 only (BI_ERR_DTYPE otherwise).
+ * ------------------------------------------------------------------------ */
+size_t bi_matmul_swiglu_workspace_bytes(int64_t M, int64_t F, int64_t K, int32_t dtype);
+bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, int64_t M, int64_t F, int64_t K,
+                           int32_t dtype, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Group-quantized 4-bit matmul   y = x @ dequantize(W)^T
  * Source: "Fix fp quantized matmul corruption when the quantized dim is not a
  * multiple of 32", Problem (reference x @ dequantize(w).T; nvfp4 group size

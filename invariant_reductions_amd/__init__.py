@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "BIError", "library_path", "lib", "build_info",
-    "matmul", "matmul_ws", "matmul_workspace", "qmatmul", "rmsnorm", "add_rmsnorm", "sdpa", "sdpa_workspace_bytes",
+    "matmul", "matmul_ws", "matmul_workspace", "matmul_swiglu", "matmul_swiglu_workspace", "interleave_gate_up",
+    "qmatmul", "rmsnorm", "add_rmsnorm", "sdpa", "sdpa_workspace_bytes",
     "matmul_split", "rmsnorm_split",
     "embed", "rope_kv_write", "silu_mul", "add", "argmax",
     "BF16", "F16", "F32", "AFFINE", "NVFP4",
@@ -69,6 +70,7 @@ def lib():
             "bi_argmax": [P, P, I64, I64, P],
             "bi_matmul_split": [P, P, P, I64, I64, I64, I32, I32, I32, P, SZ, P],
             "bi_matmul_ws": [P, P, P, I64, I64, I64, I32, I32, P, SZ, P],
+            "bi_matmul_swiglu": [P, P, P, I64, I64, I64, I32, P, SZ, P],
             "bi_rmsnorm_split": [P, P, P, I64, I64, F, I32, I32, P, SZ, P],
         }
         for name, args in sig.items():
@@ -77,6 +79,8 @@ def lib():
             fn.restype = ctypes.c_int32
         L.bi_sdpa_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
         L.bi_sdpa_workspace_bytes.restype = SZ
+        L.bi_matmul_swiglu_workspace_bytes.argtypes = [I64, I64, I64, I32]
+        L.bi_matmul_swiglu_workspace_bytes.restype = SZ
         L.bi_matmul_ws_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
         L.bi_matmul_ws_workspace_bytes.restype = SZ
         L.bi_matmul_split_workspace_bytes.argtypes = [I64, I64, I32]
@@ -174,6 +178,35 @@ def matmul_ws(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, transposed: bo
     _check(lib().bi_matmul_ws(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dt(x), int(transposed), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "bi_matmul_ws")
     return y
+
+
+def interleave_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:
+    """[2F, K] weight for matmul_swiglu: gate and up rows interleaved in
+    blocks of 64 (a layout change done once, on any device)."""
+    F, K = w_gate.shape
+    if w_up.shape != (F, K) or F % 64:
+        raise ValueError("interleave_gate_up: gate/up must be [F, K] with F % 64 == 0")
+    return torch.stack([w_gate.view(F // 64, 64, K), w_up.view(F // 64, 64, K)], dim=1).reshape(2 * F, K).contiguous()
+
+
+def matmul_swiglu_workspace(M: int, F: int, K: int, device=None):
+    """A zero-filled workspace for matmul_swiglu at this shape."""
+    need = lib().bi_matmul_swiglu_workspace_bytes(M, F, K, BF16)
+    return torch.zeros(max(int(need), 16), dtype=torch.uint8, device=device)
+
+
+def matmul_swiglu(x: torch.Tensor, w_il: torch.Tensor, ws: torch.Tensor, out=None, stream=None):
+    """a = silu(x @ Wg^T) * (x @ Wu^T), bitwise matmul + silu_mul; w_il from
+    interleave_gate_up."""
+    _dev(x, w_il, out, ws)
+    M, K = x.shape
+    if w_il.shape[1] != K or w_il.shape[0] % 128 or x.dtype != torch.bfloat16 or w_il.dtype != x.dtype:
+        raise ValueError("matmul_swiglu: shape/dtype mismatch")
+    F = w_il.shape[0] // 2
+    a = out if out is not None else torch.empty((M, F), dtype=x.dtype, device=x.device)
+    _check(lib().bi_matmul_swiglu(_ptr(x), _ptr(w_il), _ptr(a), M, F, K, BF16, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)), "bi_matmul_swiglu")
+    return a
 
 
 def matmul_split(x, w, splits: int, transposed: bool = True, out=None, ws=None, stream=None):

@@ -72,6 +72,16 @@ __device__ inline uint4 load_chunk(const typename S::store_t *row, int64_t k, in
     return r;
 }
 
+// SwiGLU activation of one bf16 pair: RNE(silu(g) * u) with
+// silu(g) = g / (1 + exp(-g)), every step in fp32.  One definition for the
+// stand-alone kernel and the fused matmul epilogue, so both give these bits.
+__device__ inline uint16_t silu_mul1(uint16_t gb, uint16_t ub)
+{
+    const float g = BF16::widen(gb), u = BF16::widen(ub);
+    const float sg = g / (1.0f + expf(-g));
+    return BF16::narrow(sg * u);
+}
+
 // Calls f(std::integral_constant<int, I>{}) for I = B .. E-1: the index is a
 // compile-time constant inside f, so register arrays indexed by it stay in
 // registers.

@@ -485,7 +485,15 @@ static bool try_launch_stream(const void *x, const void *w, void *y, int64_t M, 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 
-template <typename S, int MT, int Q, int DW, int OCC>
+// What the slot kernel does with a finished tile: store y (EPI_Y), or the
+// SwiGLU activation of an interleaved gate/up tile (EPI_SWIGLU: the 128
+// columns of tile ct are gate columns 64ct .. 64ct + 63 followed by the up
+// columns of the same indices; a[m, 64ct + j] = silu_mul1(y[m, 128ct + j],
+// y[m, 128ct + 64 + j]), from the bf16-rounded y exactly as bi_silu_mul
+// would read it).
+enum SlotEpilogue { EPI_Y = 0, EPI_SWIGLU = 1 };
+
+template <typename S, int MT, int Q, int DW, int OCC, int EPI>
 __global__ __launch_bounds__(kDenseWaves * kWave, OCC)
 void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typename S::store_t *__restrict__ w,
                         typename S::store_t *__restrict__ y, float *__restrict__ part,
@@ -614,16 +622,40 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
     }
     // MFMA accumulator layout: lane (g, c), register r holds row 4g + r, column c.
     auto store_y = [&](const f32x4 (&v)[MT]) {
-        if (!nok) return;
+        if constexpr (EPI == EPI_Y) {
+            if (!nok) return;
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m * 16 + g * 4 + r;
-                if (row < M) y[row * N + n] = S::narrow(v[m][r]);
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = m * 16 + g * 4 + r;
+                    if (row < M) y[row * N + n] = S::narrow(v[m][r]);
+                }
+        } else {
+            // the tile's rounded y into LDS (the x ring is free by now), then
+            // each thread forms 8 consecutive activations of one row
+            T (*tile)[XS] = xs[0];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tile[m * 16 + g * 4 + r][wave * 16 + c] = S::narrow(v[m][r]);
+            __syncthreads();
+            const int F = (int)(N / 2);
+            for (int it = threadIdx.x; it < TR * 8; it += NT) {
+                const int row = it >> 3, jg = (it & 7) * 8;
+                if (row >= M) continue;
+                const uint4 gv = *reinterpret_cast<const uint4 *>(&tile[row][jg]);
+                const uint4 uv = *reinterpret_cast<const uint4 *>(&tile[row][64 + jg]);
+                const uint16_t *g8 = reinterpret_cast<const uint16_t *>(&gv), *u8 = reinterpret_cast<const uint16_t *>(&uv);
+                uint16_t o8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o8[e] = silu_mul1(g8[e], u8[e]);
+                *reinterpret_cast<uint4 *>(y + (int64_t)row * F + (int64_t)ct * 64 + jg) = __builtin_bit_cast(uint4, o8);
             }
+        }
     };
     if constexpr (GRP == 1) {
+        if constexpr (EPI != EPI_Y) __syncthreads();   // every wave is done reading the x ring
         store_y(h);
     } else {
         // Group sums go to the workspace as 16-byte records, m-major: record
@@ -683,7 +715,7 @@ static size_t slot_ws_bytes(int64_t M, int64_t N, int groups)
     return kSlotCounterBytes + (size_t)(cdiv(N, kSlotTileCols) * groups * kDenseWaves * rec);
 }
 
-template <typename S, int MT, int Q>
+template <typename S, int MT, int Q, int EPI>
 static void launch_slots_t(const void *x, const void *w, void *y, void *ws, int64_t M, int64_t N, int64_t K,
                            hipStream_t st)
 {
@@ -695,13 +727,13 @@ static void launch_slots_t(const void *x, const void *w, void *y, void *ws, int6
     // VGPRs) wherever the accumulators allow it.
     constexpr int DW = MT == 4 ? 2 : 4;
     constexpr int OCC = Q * MT <= 4 ? 4 : 2;
-    launch_kernel((dense_slots_kernel<S, MT, Q, DW, OCC>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
+    launch_kernel((dense_slots_kernel<S, MT, Q, DW, OCC, EPI>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
                        dim3(kDenseWaves * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, counters, M, N, K);
 }
 
 // Slots per workgroup: the largest group that still gives at least one
 // workgroup per CU (MT = 4 keeps at most four slots in registers).
-template <typename S, int MT>
+template <typename S, int MT, int EPI>
 static void launch_slots_mt(const void *x, const void *w, void *y, void *ws, int64_t M, int64_t N, int64_t K,
                             hipStream_t st)
 {
@@ -709,15 +741,15 @@ static void launch_slots_mt(const void *x, const void *w, void *y, void *ws, int
     // All eight slots in one workgroup (no exchange) once the column tiles
     // alone come close to one per CU.
     if (ntc * 4 >= cu * 3) {
-        launch_slots_t<S, MT, 8>(x, w, y, ws, M, N, K, st);
+        launch_slots_t<S, MT, 8, EPI>(x, w, y, ws, M, N, K, st);
         return;
     }
-    if (ntc * 2 >= cu) launch_slots_t<S, MT, 4>(x, w, y, ws, M, N, K, st);
-    else if (ntc * 4 >= cu) launch_slots_t<S, MT, 2>(x, w, y, ws, M, N, K, st);
-    else launch_slots_t<S, MT, 1>(x, w, y, ws, M, N, K, st);
+    if (ntc * 2 >= cu) launch_slots_t<S, MT, 4, EPI>(x, w, y, ws, M, N, K, st);
+    else if (ntc * 4 >= cu) launch_slots_t<S, MT, 2, EPI>(x, w, y, ws, M, N, K, st);
+    else launch_slots_t<S, MT, 1, EPI>(x, w, y, ws, M, N, K, st);
 }
 
-template <typename S>
+template <typename S, int EPI = EPI_Y>
 static bool try_launch_slots(const void *x, const void *w, void *y, void *ws, size_t ws_bytes, int64_t M,
                              int64_t N, int64_t K, hipStream_t st)
 {
@@ -728,8 +760,8 @@ static bool try_launch_slots(const void *x, const void *w, void *y, void *ws, si
         !host_aligned16(ws))
         return false;
     if (ws_bytes < slot_ws_bytes(M, N, kDenseWaves)) return false;
-    if (slot_mt(M) == 2) launch_slots_mt<S, 2>(x, w, y, ws, M, N, K, st);
-    else launch_slots_mt<S, 4>(x, w, y, ws, M, N, K, st);
+    if (slot_mt(M) == 2) launch_slots_mt<S, 2, EPI>(x, w, y, ws, M, N, K, st);
+    else launch_slots_mt<S, 4, EPI>(x, w, y, ws, M, N, K, st);
     return true;
 }
 
@@ -769,6 +801,26 @@ static void dispatch_dense(const void *x, const void *w, void *y, float *part, i
     else if (dtype == BI_F16) launch_dense<F16>(x, w, y, part, M, N, K, trans, splits, st);
     else launch_dense<F32>(x, w, y, part, M, N, K, trans, splits, st);
 }
+
+// SwiGLU activation of an interleaved gate/up product (the fallback of
+// bi_matmul_swiglu): in each row, columns 128 i + j and 128 i + 64 + j are
+// gate and up of activation 64 i + j.  Thread = 8 consecutive activations.
+__global__ void swiglu_il_kernel(const uint16_t *__restrict__ gu, uint16_t *__restrict__ a, int64_t rows, int64_t F)
+{
+    const int64_t fc = F / 8, n = rows * fc;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n; c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = c / fc, i = (c - r * fc) * 8;
+        const uint16_t *gp = gu + r * 2 * F + (i / 64) * 128 + (i % 64);
+        const uint4 gv = *reinterpret_cast<const uint4 *>(gp), uv = *reinterpret_cast<const uint4 *>(gp + 64);
+        const uint16_t *g8 = reinterpret_cast<const uint16_t *>(&gv), *u8 = reinterpret_cast<const uint16_t *>(&uv);
+        uint16_t o8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = silu_mul1(g8[e], u8[e]);
+        *reinterpret_cast<uint4 *>(a + r * F + i) = __builtin_bit_cast(uint4, o8);
+    }
+}
+
+static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace bi
 
@@ -842,4 +894,40 @@ extern "C" bi_status bi_time_next_launch(hipEvent_t start, hipEvent_t stop)
 {
     bi::launch_timing() = bi::LaunchTiming{start, stop};
     return BI_OK;
+}
+
+extern "C" size_t bi_matmul_swiglu_workspace_bytes(int64_t M, int64_t F, int64_t K, int32_t dtype)
+{
+    if (M < 1 || F < 1 || K < 1 || dtype != BI_BF16 || F % 64 || M > (1ll << 31) || F > (1ll << 30)) return 0;
+    // the slot form's counter area, then its group sums or (any other shape)
+    // the scratch product: never both in one call
+    const size_t slot = bi_matmul_ws_workspace_bytes(M, 2 * F, K, dtype, 1);
+    const size_t prod = align256((size_t)M * (size_t)(2 * F) * sizeof(uint16_t));
+    return kSlotCounterBytes + std::max(slot > 0 ? slot - kSlotCounterBytes : 0, prod);
+}
+
+extern "C" bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, int64_t M, int64_t F, int64_t K,
+                                      int32_t dtype, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (F < 1 || F > (1ll << 30)) return BI_ERR_SHAPE;
+    bi_status s = check_dense(x, w_il, a, M, 2 * F, K, dtype);
+    if (s != BI_OK) return s;
+    if (dtype != BI_BF16) return BI_ERR_DTYPE;
+    if (F % 64) return BI_ERR_SHAPE;
+    if (!host_aligned16(a)) return BI_ERR_ALIGN;
+    const size_t need = bi_matmul_swiglu_workspace_bytes(M, F, K, dtype);
+    if (!ws || ws_bytes < need) return BI_ERR_WORKSPACE;
+    if (!host_aligned16(ws)) return BI_ERR_ALIGN;
+    const size_t slot = bi_matmul_ws_workspace_bytes(M, 2 * F, K, dtype, 1);
+    (void)hipGetLastError();
+    if (slot > 0 && try_launch_slots<BF16, EPI_SWIGLU>(x, w_il, a, ws, slot, M, 2 * F, K, stream)) return launch_status();
+    // any other shape: the product into the scratch after the counter area
+    // (which stays zero for later slot-form calls on this workspace), then
+    // the activation
+    uint16_t *gu = (uint16_t *)((char *)ws + kSlotCounterBytes);
+    dispatch_dense(x, w_il, gu, nullptr, M, 2 * F, K, dtype, true, 1, stream);
+    const int64_t n = M * F / 8;
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n, 256), 65536);
+    hipLaunchKernelGGL(swiglu_il_kernel, dim3(blocks), dim3(256), 0, stream, (const uint16_t *)gu, (uint16_t *)a, M, F);
+    return launch_status();
 }

@@ -68,13 +68,6 @@ __global__ void rope_kv_kernel(const uint16_t *__restrict__ qkv, uint16_t *__res
     }
 }
 
-__device__ inline uint16_t silu_mul1(uint16_t gb, uint16_t ub)
-{
-    const float g = BF16::widen(gb), u = BF16::widen(ub);
-    const float sg = g / (1.0f + expf(-g));
-    return BF16::narrow(sg * u);
-}
-
 // VEC: F % 8 == 0 and 16-byte aligned rows; thread = 8 consecutive outputs.
 template <bool VEC>
 __global__ void silu_mul_kernel(const uint16_t *__restrict__ gu, uint16_t *__restrict__ out, int64_t rows, int64_t F)

@@ -24,8 +24,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (add_rmsnorm, argmax, embed, lib, matmul_ws, rmsnorm, rope_kv_write, sdpa, sdpa_workspace_bytes,
-               silu_mul)
+from . import (add_rmsnorm, argmax, embed, interleave_gate_up, lib, matmul_swiglu, matmul_ws, rmsnorm,
+               rope_kv_write, sdpa, sdpa_workspace_bytes)
 from .inputs import rope_tables
 
 
@@ -47,6 +47,12 @@ class Decoder:
         W = weights
         self.embed_w = _dev16(W["embed"], d)
         self.layers = [{k: _dev16(v, d) for k, v in lw.items()} for lw in W["layers"]]
+        # the gate/up weight [Wg; Wu] stored interleaved in blocks of 64 rows,
+        # the layout the fused projection + SwiGLU kernel reads
+        for lw in self.layers:
+            wgu = lw.pop("wgu")
+            lw["wgu_il"] = interleave_gate_up(wgu[:self.F], wgu[self.F:])
+            del wgu
         self.final_norm = _dev16(W["final_norm"], d)
         self.lm_head = _dev16(W["lm_head"], d)
         cos_t, sin_t = rope_tables(max_len, self.D, c.get("rope_theta", 10000.0))
@@ -60,7 +66,7 @@ class Decoder:
         self.vc = [z(max_batch, max_len, self.Hkv, self.D) for _ in range(self.L)]
         self.x, self.h, self.t1 = z(T, self.H), z(T, self.H), z(T, self.H)
         self.qkv, self.q, self.o = z(T, self.qkvn), z(T, self.qn), z(T, self.qn)
-        self.gu, self.a = z(T, 2 * self.F), z(T, self.F)
+        self.a = z(T, self.F)
         self.logits = z(T, self.V)
         self.ids = torch.zeros(T, dtype=torch.int32, device=d)
         self.next_ids = torch.zeros(T, dtype=torch.int32, device=d)
@@ -71,6 +77,10 @@ class Decoder:
         mshapes = [(self.qkvn, self.H), (self.H, self.qn), (2 * self.F, self.H), (self.H, self.F), (self.V, self.H)]
         need = max(lib().bi_matmul_ws_workspace_bytes(min(T, 64), n, k, 0, 1) for n, k in mshapes)
         self.mws = torch.zeros(max(int(need), 16), dtype=torch.uint8, device=d)
+        # the fused gate/up + SwiGLU call has its own (its size covers the
+        # scratch product of the shapes the fused kernel does not take)
+        sneed = max(lib().bi_matmul_swiglu_workspace_bytes(m, self.F, self.H, 0) for m in {min(T, 64), T})
+        self.sws = torch.zeros(max(int(sneed), 16), dtype=torch.uint8, device=d)
 
     # -- one forward over Q new tokens of each of B sequences -----------------
     def forward(self, B: int, Q: int, max_kv: int):
@@ -80,7 +90,7 @@ class Decoder:
         H, qn = self.H, self.qn
         x, h, t1 = self.x[:T], self.h[:T], self.t1[:T]
         qkv, q, o = self.qkv[:T], self.q[:T], self.o[:T]
-        gu, a = self.gu[:T], self.a[:T]
+        a = self.a[:T]
         kv = self.kv_len[:B]
         embed(self.ids[:T], self.embed_w, out=x)
         scale = 1.0 / float(np.sqrt(self.D))
@@ -95,8 +105,7 @@ class Decoder:
                  out=o.view(B, Q, self.Hq, self.D), ws=self.ws)
             matmul_ws(o, Lw["wo"], self.mws, True, out=t1)
             add_rmsnorm(x, t1, Lw["mlp_norm"], self.eps, x_out=x, out=h)
-            matmul_ws(h, Lw["wgu"], self.mws, True, out=gu)
-            silu_mul(gu, out=a)
+            matmul_swiglu(h, Lw["wgu_il"], self.sws, out=a)
             matmul_ws(a, Lw["wdown"], self.mws, True, out=t1)
             nxt = self.layers[li + 1]["attn_norm"] if li + 1 < self.L else self.final_norm
             add_rmsnorm(x, t1, nxt, self.eps, x_out=x, out=h)
@@ -120,7 +129,7 @@ class Decoder:
         H, qn = self.H, self.qn
         x, h, t1 = self.x[:T], self.h[:T], self.t1[:T]
         qkv, q, o = self.qkv[:T], self.q[:T], self.o[:T]
-        gu, a = self.gu[:T], self.a[:T]
+        a = self.a[:T]
         kv = self.kv_len[:B]
         scale = ctypes.c_float(1.0 / float(np.sqrt(self.D)))
         eps = ctypes.c_float(self.eps)
@@ -140,8 +149,8 @@ class Decoder:
                                      self.D, scale, 1, 0, p(self.ws), self.ws.numel(), st)),
                 mm(o, Lw["wo"], t1, H, qn),
                 ("add_rmsnorm", L.bi_add_rmsnorm, (p(x), p(t1), p(x), p(Lw["mlp_norm"]), p(h), T, H, eps, 0, st)),
-                mm(h, Lw["wgu"], gu, 2 * self.F, H),
-                ("silu_mul", L.bi_silu_mul, (p(gu), p(a), T, self.F, st)),
+                ("matmul_swiglu", L.bi_matmul_swiglu, (p(h), p(Lw["wgu_il"]), p(a), T, self.F, H, 0, p(self.sws),
+                                                       self.sws.numel(), st)),
                 mm(a, Lw["wdown"], t1, H, self.F),
                 ("add_rmsnorm", L.bi_add_rmsnorm, (p(x), p(t1), p(x), p(nxt), p(h), T, H, eps, 0, st)),
             ]

@@ -139,6 +139,27 @@ def test_matmul_ws_validation_and_workspace_size():
     assert L.bi_matmul_ws(A, A, A, 64, 4096, 4096, 7, 1, A, need, None) == DTYPE
 
 
+def test_matmul_swiglu_validation_and_workspace_size():
+    """bf16 only, F a multiple of 64, a 16-byte aligned output and a workspace
+    of the reported size; errors come before any launch."""
+    L = bi.lib()
+    need = L.bi_matmul_swiglu_workspace_bytes(64, 14336, 4096, 0)
+    # the 64 KiB counter area, then the slot form's group sums or a scratch [M, 2F] bf16 product
+    assert need == L.bi_matmul_ws_workspace_bytes(64, 2 * 14336, 4096, 0, 1)      # group sums are the larger
+    assert L.bi_matmul_swiglu_workspace_bytes(1, 64, 128, 0) == 65536 + 256       # 1 x 128 bf16, 256-byte rounded
+    assert L.bi_matmul_swiglu_workspace_bytes(65, 14336, 4096, 0) == 65536 + 65 * 2 * 14336 * 2
+    assert L.bi_matmul_swiglu_workspace_bytes(64, 14336, 4096, 1) == 0            # f16
+    assert L.bi_matmul_swiglu_workspace_bytes(64, 100, 4096, 0) == 0              # F % 64
+    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 0, None, 0, None) == WORKSPACE
+    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 0, A, need - 1, None) == WORKSPACE
+    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 1, A, need, None) == DTYPE
+    assert L.bi_matmul_swiglu(A, A, A, 64, 100, 4096, 0, A, need, None) == SHAPE
+    assert L.bi_matmul_swiglu(A, A, A, 0, 14336, 4096, 0, A, need, None) == SHAPE
+    assert L.bi_matmul_swiglu(A, A, P(0x10010 + 2), 64, 14336, 4096, 0, A, need, None) == ALIGN
+    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 0, P(0x10010 + 2), need, None) == ALIGN
+    assert L.bi_matmul_swiglu(None, A, A, 64, 14336, 4096, 0, A, need, None) == NULL
+
+
 def test_add_rmsnorm_validation():
     L = bi.lib()
     assert L.bi_add_rmsnorm(A, None, A, A, A, 4, 4096, 1e-6, 0, None) == NULL

@@ -119,3 +119,57 @@ def test_run_to_run_determinism():
     first = bi.matmul_ws(x, w, ws)
     for _ in range(50):
         assert same(bi.matmul_ws(x, w, ws), first)
+
+
+@pytest.mark.parametrize("M,F,K", [
+    (1, 14336, 4096),      # decode rows on the one-workgroup-per-tile kernel: fallback (product + activation)
+    (16, 64, 128),
+    (17, 14336, 4096),     # the fused slot kernel, 32-row form
+    (40, 192, 896),        # few column tiles: slot groups exchange partial sums
+    (64, 14336, 4096),     # the decoder's MLP at batch 64
+    (64, 640, 4224),
+    (65, 14336, 4096),     # long M: fallback
+    (64, 128, 4100),       # K not a multiple of 128: fallback
+])
+def test_swiglu_bits_equal_matmul_then_silu(M, F, K):
+    """Fused gate/up + SwiGLU equals bi_matmul followed by bi_silu_mul bit
+    for bit, whichever form the call takes."""
+    x = rand((M, K), "bf16", seed=M + F)
+    wg = rand((F, K), "bf16", seed=F + K, scale=0.02)
+    wu = rand((F, K), "bf16", seed=F + K + 1, scale=0.02)
+    ref = bi.silu_mul(bi.matmul(x, torch.cat([wg, wu], 0).contiguous()))
+    ws = bi.matmul_swiglu_workspace(M, F, K, device=dev())
+    a = bi.matmul_swiglu(x, bi.interleave_gate_up(wg, wu), ws)
+    assert same(a, ref), f"{M}x{F}x{K}"
+    assert int(ws[:65536].count_nonzero()) == 0          # counters left zero by either form
+
+
+def test_swiglu_rows_independent_and_canaries():
+    """Every prefix of the rows gives the full call's rows, with one workspace
+    shared by both forms of the call in stream order; stores stay in the
+    output."""
+    F, K = 1024, 4096
+    x = rand((64, K), "bf16", seed=3)
+    wil = bi.interleave_gate_up(rand((F, K), "bf16", seed=4, scale=0.02), rand((F, K), "bf16", seed=5, scale=0.02))
+    ws = bi.matmul_swiglu_workspace(64, F, K, device=dev())
+    full = bi.matmul_swiglu(x, wil, ws)
+    for M in (1, 9, 16, 17, 33, 63, 2, 40):
+        assert same(bi.matmul_swiglu(x[:M].contiguous(), wil, ws), full[:M]), f"M={M}"
+    ag = Guarded((37, F), torch.bfloat16, poison=0x5A)
+    bi.matmul_swiglu(x[:37].contiguous(), wil, ws, out=ag.view)
+    torch.cuda.synchronize()
+    assert ag.canaries_intact()
+    assert same(ag.view, full[:37])
+
+
+def test_swiglu_oracle_parity():
+    """Against the oracle's matmul (rounded to bf16, as the decoder stores
+    it) then SiLU*mul, to the bf16 parity tolerance."""
+    M, F, K = 48, 320, 1024
+    x, wt, _ = inputs.dense_case(M, 2 * F, K, "bf16", seed=21)
+    gu = oracle.round_to(oracle.matmul(x, wt, "bf16", True), "bf16")
+    ref = oracle.silu_mul(gu[:, :F].copy(), gu[:, F:].copy(), "bf16")
+    w = to_dev(wt, "bf16")
+    ws = bi.matmul_swiglu_workspace(M, F, K, device=dev())
+    a = to_np(bi.matmul_swiglu(to_dev(x, "bf16"), bi.interleave_gate_up(w[:F], w[F:]), ws))
+    assert_parity(a, ref, "bf16", "swiglu")
