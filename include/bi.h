@@ -69,6 +69,8 @@ typedef enum {
 } bi_status;
 
 typedef enum { BI_BF16 = 0, BI_F16 = 1, BI_F32 = 2 } bi_dtype;
+/* Weight layouts of the dense entry points (their w_layout argument). */
+typedef enum { BI_W_NATURAL = 0, BI_W_TRANSPOSED = 1, BI_W_PACKED = 2 } bi_wlayout;
 typedef enum { BI_AFFINE = 0, BI_NVFP4 = 1 } bi_qmode;
 
 /* ------------------------------------------------------------------------
@@ -78,16 +80,40 @@ typedef enum { BI_AFFINE = 0, BI_NVFP4 = 1 } bi_qmode;
  * orientations of the weight); "Batch-invariant kernels ...", Case 3 and
  * Case 6 (one tile configuration for every batch size, no split-K).
  *   x : [M,K] of `dtype`.
- *   w : [N,K] of `dtype` when w_transposed != 0, else [K,N].
+ *   w : by w_layout: BI_W_TRANSPOSED [N,K]; BI_W_NATURAL [K,N]; BI_W_PACKED
+ *       the tile-packed form of [N,K] written by bi_pack_weights (16-bit
+ *       dtypes, K % 128 == 0, x and w 16-byte aligned; BI_ERR_DTYPE,
+ *       BI_ERR_SHAPE, BI_ERR_ALIGN otherwise).  Any other w_layout value:
+ *       BI_ERR_SHAPE.
  *   y : [M,N] of `dtype` (fp32 accumulation, RNE to `dtype`).
  *   dtype: BI_BF16, BI_F16 or BI_F32.
  *   M >= 1, N >= 1, K >= 1.
- * Row m of y depends only on row m of x, on W and on K -- not on M, N, or
- * where row m sits in x.
+ * Row m of y depends only on row m of x, on W and on K -- not on M, N, the
+ * weight layout, or where row m sits in x.
  * ------------------------------------------------------------------------ */
 bi_status bi_matmul(const void *x, const void *w, void *y,
                     int64_t M, int64_t N, int64_t K,
-                    int32_t dtype, int32_t w_transposed, hipStream_t stream);
+                    int32_t dtype, int32_t w_layout, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Tile-packed weights (BI_W_PACKED): a one-time layout change of a [N,K]
+ * weight that every dense entry point reads with the same reduction tree,
+ * hence the same bits, as [N,K].  For row group r (rows 16r .. 16r + 15, rows
+ * >= N stored as zeros), K block b (128 elements) and step s (32 of them),
+ * 64 x 8 elements are contiguous, lane l = 16 g + c holding
+ * W[16r + c][128 b + 32 s + 8 g + e], e = 0..7, at element offset
+ * (((r * (K / 128) + b) * 4 + s) * 64 + l) * 8.  The 4 KiB a wave multiplies
+ * per block are one piece of memory instead of sixteen 256-byte pieces of
+ * sixteen rows, which streams the weight with fewer DRAM pages opened.  Same
+ * source as bi_matmul (the layout is free: only the tree is frozen).
+ *   bi_packed_weight_bytes: ceil(N / 16) * 16 * K * 2, or 0 when the shape or
+ *     dtype cannot be packed (K % 128 != 0, dtype not BI_BF16 / BI_F16).
+ *   bi_pack_weights: w [N,K] -> wp (that many bytes), both 16-byte aligned,
+ *     stream-ordered; the caller owns both buffers.  Errors: BI_ERR_NULL,
+ *     BI_ERR_DTYPE, BI_ERR_SHAPE, BI_ERR_ALIGN.
+ * ------------------------------------------------------------------------ */
+size_t bi_packed_weight_bytes(int64_t N, int64_t K, int32_t dtype);
+bi_status bi_pack_weights(const void *w, void *wp, int64_t N, int64_t K, int32_t dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Dense matmul with a caller workspace: bitwise the same y as bi_matmul.
@@ -98,9 +124,10 @@ bi_status bi_matmul(const void *x, const void *w, void *y,
  * workspace, the slots of one output may be computed by different workgroups;
  * the partial sums of aligned slot groups meet in the workspace and are added
  * in the fixed tree order by whichever workgroup finishes last.  Every other
- * call runs bi_matmul's kernels.
+ * call runs bi_matmul's kernels.  w and w_layout as in bi_matmul (the slot
+ * form takes BI_W_TRANSPOSED and BI_W_PACKED weights).
  *   ws, ws_bytes: device memory of at least
- *     bi_matmul_ws_workspace_bytes(M, N, K, dtype, w_transposed) bytes
+ *     bi_matmul_ws_workspace_bytes(M, N, K, dtype, w_layout) bytes
  *     (0 means no workspace is needed and ws may be NULL), 16-byte aligned,
  *     filled with zero bytes before its first use.  Its first 64 KiB hold
  *     per-column-tile counters that every call leaves at zero again, so one
@@ -110,9 +137,9 @@ bi_status bi_matmul(const void *x, const void *w, void *y,
  *   Errors: as bi_matmul, plus BI_ERR_WORKSPACE when ws is NULL or too small
  *   and BI_ERR_ALIGN when ws is misaligned.
  * ------------------------------------------------------------------------ */
-size_t bi_matmul_ws_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t w_transposed);
+size_t bi_matmul_ws_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t w_layout);
 bi_status bi_matmul_ws(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
-                       int32_t dtype, int32_t w_transposed, void *ws, size_t ws_bytes, hipStream_t stream);
+                       int32_t dtype, int32_t w_layout, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Gate/up projection fused with the SwiGLU activation of a Llama-style MLP:
@@ -123,10 +150,12 @@ bi_status bi_matmul_ws(const void *x, const void *w, void *y, int64_t M, int64_t
  * invariant, so fusing the activation into the reduction that produces its
  * input changes no tree) and Case 6 (the decoder's MLP).
  *   x    : [M, K] bf16.
- *   w_il : [2F, K] bf16, the gate and up weights interleaved in blocks of 64
- *          rows: rows [128 i, 128 i + 64) are gate rows [64 i, 64 i + 64),
- *          rows [128 i + 64, 128 i + 128) are up rows [64 i, 64 i + 64).
- *   a    : [M, F] bf16, 16-byte aligned.  F % 64 == 0.
+ *   w_il : [2F, K] bf16, the gate and up weights interleaved in blocks of 8
+ *          rows: rows [16 i, 16 i + 8) are gate rows [8 i, 8 i + 8),
+ *          rows [16 i + 8, 16 i + 16) are up rows [8 i, 8 i + 8); as such
+ *          (w_layout BI_W_TRANSPOSED) or tile-packed by bi_pack_weights
+ *          (BI_W_PACKED).  BI_W_NATURAL: BI_ERR_UNSUPPORTED.
+ *   a    : [M, F] bf16, 16-byte aligned.  F % 8 == 0 (BI_ERR_SHAPE otherwise).
  *   ws   : at least bi_matmul_swiglu_workspace_bytes(M, F, K, dtype) bytes,
  *          16-byte aligned, zero-filled before first use.  Its first 64 KiB
  *          are counters that every call leaves zero (as in bi_matmul_ws, and
@@ -137,7 +166,7 @@ bi_status bi_matmul_ws(const void *x, const void *w, void *y, int64_t M, int64_t
  * ------------------------------------------------------------------------ */
 size_t bi_matmul_swiglu_workspace_bytes(int64_t M, int64_t F, int64_t K, int32_t dtype);
 bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, int64_t M, int64_t F, int64_t K,
-                           int32_t dtype, void *ws, size_t ws_bytes, hipStream_t stream);
+                           int32_t dtype, int32_t w_layout, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Group-quantized 4-bit matmul   y = x @ dequantize(W)^T
@@ -268,10 +297,11 @@ bi_status bi_argmax(const void *x, int32_t *idx, int64_t rows, int64_t cols, hip
  * picks `splits` from the batch size gets batch-dependent bits.
  * Source: "Batch-invariant kernels ...", Case 2 (split-k), Case 3, Case 4,
  * Case 6 (Split-K / Split-KV); "Fix/speculative shape invariance", Problem.
+ * bi_matmul_split takes weights in any layout of bi_matmul.
  * ------------------------------------------------------------------------ */
 size_t bi_matmul_split_workspace_bytes(int64_t M, int64_t N, int32_t splits);
 bi_status bi_matmul_split(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
-                          int32_t dtype, int32_t w_transposed, int32_t splits,
+                          int32_t dtype, int32_t w_layout, int32_t splits,
                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 size_t bi_rmsnorm_split_workspace_bytes(int64_t rows, int32_t splits);

@@ -19,6 +19,7 @@ import torch
 __all__ = [
     "BIError", "library_path", "lib", "build_info",
     "matmul", "matmul_ws", "matmul_workspace", "matmul_swiglu", "matmul_swiglu_workspace", "interleave_gate_up",
+    "PackedWeight", "pack_weights",
     "qmatmul", "rmsnorm", "add_rmsnorm", "sdpa", "sdpa_workspace_bytes",
     "matmul_split", "rmsnorm_split",
     "embed", "rope_kv_write", "silu_mul", "add", "argmax",
@@ -70,7 +71,8 @@ def lib():
             "bi_argmax": [P, P, I64, I64, P],
             "bi_matmul_split": [P, P, P, I64, I64, I64, I32, I32, I32, P, SZ, P],
             "bi_matmul_ws": [P, P, P, I64, I64, I64, I32, I32, P, SZ, P],
-            "bi_matmul_swiglu": [P, P, P, I64, I64, I64, I32, P, SZ, P],
+            "bi_matmul_swiglu": [P, P, P, I64, I64, I64, I32, I32, P, SZ, P],
+            "bi_pack_weights": [P, P, I64, I64, I32, P],
             "bi_rmsnorm_split": [P, P, P, I64, I64, F, I32, I32, P, SZ, P],
         }
         for name, args in sig.items():
@@ -79,6 +81,8 @@ def lib():
             fn.restype = ctypes.c_int32
         L.bi_sdpa_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
         L.bi_sdpa_workspace_bytes.restype = SZ
+        L.bi_packed_weight_bytes.argtypes = [I64, I64, I32]
+        L.bi_packed_weight_bytes.restype = SZ
         L.bi_matmul_swiglu_workspace_bytes.argtypes = [I64, I64, I64, I32]
         L.bi_matmul_swiglu_workspace_bytes.restype = SZ
         L.bi_matmul_ws_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
@@ -145,16 +149,52 @@ def _check(rc: int, where: str):
 # the four reductions
 # ---------------------------------------------------------------------------
 
-def matmul(x: torch.Tensor, w: torch.Tensor, transposed: bool = True, out=None, stream=None):
-    """y = x @ w.T (w [N,K], transposed=True) or x @ w (w [K,N])."""
-    _dev(x, w, out)
-    M, K = x.shape
+W_NATURAL, W_TRANSPOSED, W_PACKED = 0, 1, 2
+
+
+class PackedWeight:
+    """A [N, K] weight in the tile-packed layout (bi_pack_weights): `data` is
+    the packed buffer (ceil(N/16)*16 x K elements of the weight's dtype)."""
+
+    def __init__(self, data: torch.Tensor, N: int, K: int):
+        self.data, self.N, self.K = data, N, K
+        self.dtype, self.device = data.dtype, data.device
+
+
+def pack_weights(w: torch.Tensor, stream=None) -> PackedWeight:
+    """[N, K] bf16/f16 (K % 128 == 0) -> PackedWeight (same bits in every
+    dense entry point, fewer DRAM pages per byte streamed)."""
+    _dev(w)
+    N, K = w.shape
+    nbytes = lib().bi_packed_weight_bytes(N, K, _dt(w))
+    if nbytes == 0:
+        raise ValueError("pack_weights: needs a bf16/f16 [N, K] weight with K % 128 == 0")
+    wp = torch.empty(nbytes // w.element_size(), dtype=w.dtype, device=w.device)
+    _check(lib().bi_pack_weights(_ptr(w), _ptr(wp), N, K, _dt(w), _stream(stream)), "bi_pack_weights")
+    return PackedWeight(wp, N, K)
+
+
+def _wargs(w, transposed: bool, K: int, dtype, where: str):
+    """(tensor, N, layout) of a weight argument: a PackedWeight, or a tensor
+    [N, K] (transposed) / [K, N]."""
+    if isinstance(w, PackedWeight):
+        if w.K != K or w.dtype != dtype:
+            raise ValueError(f"{where}: shape/dtype mismatch")
+        return w.data, w.N, W_PACKED
     N = w.shape[0] if transposed else w.shape[1]
-    if (w.shape[1] if transposed else w.shape[0]) != K or w.dtype != x.dtype:
-        raise ValueError("matmul: shape/dtype mismatch")
+    if (w.shape[1] if transposed else w.shape[0]) != K or w.dtype != dtype:
+        raise ValueError(f"{where}: shape/dtype mismatch")
+    return w, N, W_TRANSPOSED if transposed else W_NATURAL
+
+
+def matmul(x: torch.Tensor, w, transposed: bool = True, out=None, stream=None):
+    """y = x @ w.T (w [N,K], transposed=True), x @ w (w [K,N]), or with a
+    PackedWeight of [N,K]."""
+    M, K = x.shape
+    wt, N, layout = _wargs(w, transposed, K, x.dtype, "matmul")
+    _dev(x, wt, out)
     y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
-    _check(lib().bi_matmul(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dt(x), int(transposed), _stream(stream)),
-           "bi_matmul")
+    _check(lib().bi_matmul(_ptr(x), _ptr(wt), _ptr(y), M, N, K, _dt(x), layout, _stream(stream)), "bi_matmul")
     return y
 
 
@@ -165,28 +205,26 @@ def matmul_workspace(M: int, N: int, K: int, dtype=torch.bfloat16, transposed: b
     return torch.zeros(max(int(need), 16), dtype=torch.uint8, device=device)
 
 
-def matmul_ws(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, transposed: bool = True, out=None, stream=None):
+def matmul_ws(x: torch.Tensor, w, ws: torch.Tensor, transposed: bool = True, out=None, stream=None):
     """Same bits as `matmul`; `ws` from `matmul_workspace` (or any zero-filled
     buffer of at least the workspace size), reused across calls in stream
-    order."""
-    _dev(x, w, out, ws)
+    order.  `w` as in `matmul`."""
     M, K = x.shape
-    N = w.shape[0] if transposed else w.shape[1]
-    if (w.shape[1] if transposed else w.shape[0]) != K or w.dtype != x.dtype:
-        raise ValueError("matmul_ws: shape/dtype mismatch")
+    wt, N, layout = _wargs(w, transposed, K, x.dtype, "matmul_ws")
+    _dev(x, wt, out, ws)
     y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
-    _check(lib().bi_matmul_ws(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dt(x), int(transposed), _ptr(ws),
+    _check(lib().bi_matmul_ws(_ptr(x), _ptr(wt), _ptr(y), M, N, K, _dt(x), layout, _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "bi_matmul_ws")
     return y
 
 
 def interleave_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor) -> torch.Tensor:
     """[2F, K] weight for matmul_swiglu: gate and up rows interleaved in
-    blocks of 64 (a layout change done once, on any device)."""
+    blocks of 8 (a layout change done once, on any device)."""
     F, K = w_gate.shape
-    if w_up.shape != (F, K) or F % 64:
-        raise ValueError("interleave_gate_up: gate/up must be [F, K] with F % 64 == 0")
-    return torch.stack([w_gate.view(F // 64, 64, K), w_up.view(F // 64, 64, K)], dim=1).reshape(2 * F, K).contiguous()
+    if w_up.shape != (F, K) or F % 8:
+        raise ValueError("interleave_gate_up: gate/up must be [F, K] with F % 8 == 0")
+    return torch.stack([w_gate.view(F // 8, 8, K), w_up.view(F // 8, 8, K)], dim=1).reshape(2 * F, K).contiguous()
 
 
 def matmul_swiglu_workspace(M: int, F: int, K: int, device=None):
@@ -195,30 +233,33 @@ def matmul_swiglu_workspace(M: int, F: int, K: int, device=None):
     return torch.zeros(max(int(need), 16), dtype=torch.uint8, device=device)
 
 
-def matmul_swiglu(x: torch.Tensor, w_il: torch.Tensor, ws: torch.Tensor, out=None, stream=None):
+def matmul_swiglu(x: torch.Tensor, w_il, ws: torch.Tensor, out=None, stream=None):
     """a = silu(x @ Wg^T) * (x @ Wu^T), bitwise matmul + silu_mul; w_il from
-    interleave_gate_up."""
-    _dev(x, w_il, out, ws)
+    interleave_gate_up, as a [2F, K] tensor or packed by pack_weights."""
     M, K = x.shape
-    if w_il.shape[1] != K or w_il.shape[0] % 128 or x.dtype != torch.bfloat16 or w_il.dtype != x.dtype:
-        raise ValueError("matmul_swiglu: shape/dtype mismatch")
-    F = w_il.shape[0] // 2
+    if x.dtype != torch.bfloat16:
+        raise ValueError("matmul_swiglu: bf16 only")
+    wt, N2, layout = _wargs(w_il, True, K, x.dtype, "matmul_swiglu")
+    _dev(x, wt, out, ws)
+    if N2 % 16:
+        raise ValueError("matmul_swiglu: 2F must be a multiple of 16")
+    F = N2 // 2
     a = out if out is not None else torch.empty((M, F), dtype=x.dtype, device=x.device)
-    _check(lib().bi_matmul_swiglu(_ptr(x), _ptr(w_il), _ptr(a), M, F, K, BF16, _ptr(ws),
+    _check(lib().bi_matmul_swiglu(_ptr(x), _ptr(wt), _ptr(a), M, F, K, BF16, layout, _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)), "bi_matmul_swiglu")
     return a
 
 
 def matmul_split(x, w, splits: int, transposed: bool = True, out=None, ws=None, stream=None):
     """Non-invariant split-K comparison variant (see include/bi.h)."""
-    _dev(x, w, out, ws)
     M, K = x.shape
-    N = w.shape[0] if transposed else w.shape[1]
+    wt, N, layout = _wargs(w, transposed, K, x.dtype, "matmul_split")
+    _dev(x, wt, out, ws)
     y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
     need = lib().bi_matmul_split_workspace_bytes(M, N, splits)
     if ws is None and splits > 1:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    _check(lib().bi_matmul_split(_ptr(x), _ptr(w), _ptr(y), M, N, K, _dt(x), int(transposed), splits,
+    _check(lib().bi_matmul_split(_ptr(x), _ptr(wt), _ptr(y), M, N, K, _dt(x), layout, splits,
                                  _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "bi_matmul_split")
     return y

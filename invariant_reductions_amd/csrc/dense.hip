@@ -28,97 +28,17 @@
 // eight in one workgroup, or spread over several with the partials of each
 // aligned slot group combined through a workspace) is a launch choice that
 // the tree does not see.
-#include "common.hpp"
+#include "dense_common.hpp"
+
+#include <algorithm>
 
 namespace bi {
-
-constexpr int kDenseWaves = 8;   // P: K-block slots per output (frozen)
-
-// The frozen combine of the P = 8 slot partials, pairwise:
-//   ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)).
-// Every aligned group of 1, 2, 4 or 8 consecutive slots is a subtree of it, so
-// a workgroup that owns such a group may add its own slots first.
-template <typename F>
-__device__ inline float slot_tree(F p)
-{
-    return ((p(0) + p(1)) + (p(2) + p(3))) + ((p(4) + p(5)) + (p(6) + p(7)));
-}
-
-template <typename S> struct DenseMfma;
-
-template <> struct DenseMfma<BF16> {
-    static constexpr int CPB = 4;                 // 16-byte chunks per lane per block
-    __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-    __device__ static f32x4 step(const uint4 *a, const uint4 *b, int s, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s]),
-                                                       __builtin_bit_cast(bf16x8, b[s]), c, 0, 0, 0);
-    }
-};
-template <> struct DenseMfma<F16> {
-    static constexpr int CPB = 4;
-    __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-    __device__ static f32x4 step(const uint4 *a, const uint4 *b, int s, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[s]),
-                                                      __builtin_bit_cast(f16x8, b[s]), c, 0, 0, 0);
-    }
-};
-template <> struct DenseMfma<F32> {
-    static constexpr int CPB = 1;
-    __device__ static f32x4 step(const uint4 *a, const uint4 *b, int s, f32x4 c) {
-        const float av = __uint_as_float(s == 0 ? a[0].x : s == 1 ? a[0].y : s == 2 ? a[0].z : a[0].w);
-        const float bv = __uint_as_float(s == 0 ? b[0].x : s == 1 ? b[0].y : s == 2 ? b[0].z : b[0].w);
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
-    }
-};
-
-template <typename S>
-struct DenseGeom {
-    static constexpr int E = S::kElemsPer16B;            // elements per 16-byte chunk
-    static constexpr int CPB = DenseMfma<S>::CPB;
-    static constexpr int KB = 4 * CPB * E;               // elements per block
-    // element offset, within a block, of chunk ci of lane group g
-    __device__ static constexpr int chunk_off(int g, int ci) { return CPB == 4 ? ci * 32 + g * 8 : g * 4; }
-};
-
-// Loads the chunks lane (g, c) contributes to block b for one operand row.
-// Transposed operand: `row` points at the start of the K-contiguous row.
-template <typename S, bool VEC>
-__device__ inline void load_row_chunks(uint4 *dst, const typename S::store_t *row, int64_t kblk, int g,
-                                       int64_t K, bool ok)
-{
-    using G = DenseGeom<S>;
-#pragma unroll
-    for (int ci = 0; ci < G::CPB; ++ci) dst[ci] = load_chunk<S, VEC>(row, kblk + G::chunk_off(g, ci), K, ok);
-}
-
-// Natural-layout weight [K, N]: gathers column `col` at the same k positions.
-template <typename S>
-__device__ inline void load_col_chunks(uint4 *dst, const typename S::store_t *w, int64_t kblk, int g,
-                                       int64_t K, int64_t N, int64_t col, bool ok)
-{
-    using G = DenseGeom<S>;
-    using T = typename S::store_t;
-#pragma unroll
-    for (int ci = 0; ci < G::CPB; ++ci) {
-        T tmp[G::E];
-#pragma unroll
-        for (int e = 0; e < G::E; ++e) {
-            const int64_t k = kblk + G::chunk_off(g, ci) + e;
-            tmp[e] = (ok && k < K) ? w[k * N + col] : (T)0;
-        }
-        dst[ci] = __builtin_bit_cast(uint4, tmp);
-    }
-}
 
 // One workgroup: output tile of MT*16 rows x NS*16 columns, kDenseWaves waves.
 // blockIdx.z selects a K range for the split comparison variant (splits > 1,
 // partials written to `part` as fp32 [splits, M, N]); the invariant path runs
 // with splits == 1 and part == nullptr.
-template <typename S, bool TRANS, bool VEC, int MT, int NS, bool PART>
+template <typename S, bool TRANS, bool VEC, int MT, int NS, bool PART, bool PK>
 __global__ __launch_bounds__(kDenseWaves * kWave, (TRANS && VEC && !(MT >= 4 && NS >= 2)) ? 4 : 2)
 void dense_kernel(const typename S::store_t *__restrict__ x, const typename S::store_t *__restrict__ w,
                   typename S::store_t *__restrict__ y, float *__restrict__ part,
@@ -154,14 +74,17 @@ void dense_kernel(const typename S::store_t *__restrict__ x, const typename S::s
         xok[i] = r < M;
         xrow[i] = x + (xok[i] ? r : M - 1) * K;
     }
-    int64_t wcol[NS];
+    int64_t wcol[NS], wrg[NS];
     bool wok[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int64_t n = n0 + j * 16 + c;
         wok[j] = n < N;
         wcol[j] = wok[j] ? n : N - 1;
+        const int64_t rg = n0 / 16 + j, nrg = (N + 15) / 16;
+        wrg[j] = rg < nrg ? rg : nrg - 1;              // packed: row group (a whole padding group reads the last one)
     }
+    const int64_t nbk = K / G::KB;
 
     // Register ring of DEPTH block buffers: the wave keeps DEPTH - 1 blocks
     // of loads in flight while it multiplies the oldest one.
@@ -184,7 +107,11 @@ void dense_kernel(const typename S::store_t *__restrict__ x, const typename S::s
         const int64_t kblk = b * G::KB;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            if (TRANS) {
+            if constexpr (PK) {
+#pragma unroll
+                for (int ci = 0; ci < G::CPB; ++ci)
+                    B[j][ci] = *reinterpret_cast<const uint4 *>(w + packed_off(wrg[j], nbk, b, ci, lane));
+            } else if (TRANS) {
                 const typename S::store_t *wr = w + wcol[j] * K + kblk;
 #pragma unroll
                 for (int ci = 0; ci < G::CPB; ++ci)
@@ -266,7 +193,7 @@ void dense_kernel(const typename S::store_t *__restrict__ x, const typename S::s
 // flight while the current tile's eight partials are combined.  Per output
 // the tree is exactly that of dense_kernel: block b of K belongs to wave
 // b mod P, accumulated in ascending order, partials added by slot_tree.
-template <typename S, int MT, int NS>
+template <typename S, int MT, int NS, bool PK>
 __global__ __launch_bounds__(kDenseWaves * kWave, (MT >= 4 && NS >= 2) ? 2 : 4)
 void dense_stream_kernel(const typename S::store_t *__restrict__ x, const typename S::store_t *__restrict__ w,
                          typename S::store_t *__restrict__ y, int64_t M, int64_t N, int64_t K,
@@ -311,11 +238,19 @@ void dense_stream_kernel(const typename S::store_t *__restrict__ x, const typena
         const int64_t kblk = (int64_t)(wave + pj * P) * G::KB;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            int64_t n = (int64_t)ptn * TC + j * 16 + c;
-            n = n < N ? n : N - 1;                                // padding columns read a real row
-            const T *wr = w + n * K + kblk;
+            if constexpr (PK) {
+                int64_t rg = (int64_t)ptn * NS + j;
+                rg = rg < (N + 15) / 16 ? rg : (N + 15) / 16 - 1;   // a padding row group reads a real one
 #pragma unroll
-            for (int ci = 0; ci < G::CPB; ++ci) B[j][ci] = *reinterpret_cast<const uint4 *>(wr + G::chunk_off(g, ci));
+                for (int ci = 0; ci < G::CPB; ++ci)
+                    B[j][ci] = *reinterpret_cast<const uint4 *>(w + packed_off(rg, nb, wave + pj * P, ci, lane));
+            } else {
+                int64_t n = (int64_t)ptn * TC + j * 16 + c;
+                n = n < N ? n : N - 1;                            // padding columns read a real row
+                const T *wr = w + n * K + kblk;
+#pragma unroll
+                for (int ci = 0; ci < G::CPB; ++ci) B[j][ci] = *reinterpret_cast<const uint4 *>(wr + G::chunk_off(g, ci));
+            }
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
@@ -408,7 +343,7 @@ __global__ void split_reduce_kernel(const float *__restrict__ part, typename S::
     }
 }
 
-template <typename S, bool TRANS, bool VEC, int MT, int NS>
+template <typename S, bool TRANS, bool VEC, int MT, int NS, bool PK>
 static void launch_dense_t(const void *x, const void *w, void *y, float *part, int64_t M, int64_t N,
                            int64_t K, int splits, hipStream_t st)
 {
@@ -419,14 +354,14 @@ static void launch_dense_t(const void *x, const void *w, void *y, float *part, i
     // The split comparison variant is its own instantiation, so profiles of the
     // invariant kernel never mix in its launches.
     if (part)
-        launch_kernel((dense_kernel<S, TRANS, VEC, MT, NS, true>), grid, dim3(kDenseWaves * kWave), 0, st,
+        launch_kernel((dense_kernel<S, TRANS, VEC, MT, NS, true, PK>), grid, dim3(kDenseWaves * kWave), 0, st,
                            (const T *)x, (const T *)w, (T *)y, part, M, N, K, nblocks, splits);
     else
-        launch_kernel((dense_kernel<S, TRANS, VEC, MT, NS, false>), grid, dim3(kDenseWaves * kWave), 0, st,
+        launch_kernel((dense_kernel<S, TRANS, VEC, MT, NS, false, PK>), grid, dim3(kDenseWaves * kWave), 0, st,
                            (const T *)x, (const T *)w, (T *)y, part, M, N, K, nblocks, splits);
 }
 
-template <typename S, bool TRANS, bool VEC>
+template <typename S, bool TRANS, bool VEC, bool PK = false>
 static void launch_dense_mt(const void *x, const void *w, void *y, float *part, int64_t M, int64_t N,
                             int64_t K, int splits, hipStream_t st)
 {
@@ -434,342 +369,52 @@ static void launch_dense_mt(const void *x, const void *w, void *y, float *part, 
     // Wider N tiles once there are enough of them: every workgroup re-reads its
     // rows of x, so a tile of 2x16 columns halves that traffic.
     const int64_t mt = cdiv(M, 16);
-    if (mt <= 1) launch_dense_t<S, TRANS, VEC, 1, 1>(x, w, y, part, M, N, K, splits, st);
-    else if (mt <= 2) launch_dense_t<S, TRANS, VEC, 2, 1>(x, w, y, part, M, N, K, splits, st);
-    else if (N >= 8192) launch_dense_t<S, TRANS, VEC, 4, 2>(x, w, y, part, M, N, K, splits, st);
-    else launch_dense_t<S, TRANS, VEC, 4, 1>(x, w, y, part, M, N, K, splits, st);
+    if (mt <= 1) launch_dense_t<S, TRANS, VEC, 1, 1, PK>(x, w, y, part, M, N, K, splits, st);
+    else if (mt <= 2) launch_dense_t<S, TRANS, VEC, 2, 1, PK>(x, w, y, part, M, N, K, splits, st);
+    else if (N >= 8192) launch_dense_t<S, TRANS, VEC, 4, 2, PK>(x, w, y, part, M, N, K, splits, st);
+    else launch_dense_t<S, TRANS, VEC, 4, 1, PK>(x, w, y, part, M, N, K, splits, st);
 }
 
-template <typename S, int MT, int NS>
+template <typename S, int MT, int NS, bool PK>
 static void launch_stream_t(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K, hipStream_t st)
 {
     using T = typename S::store_t;
     const int64_t ntm = cdiv(M, MT * 16), ntn = cdiv(N, NS * 16);
     const int per_cu = (MT >= 4 && NS >= 2) ? 1 : 2;             // resident workgroups per CU at the register cap
     const int64_t grid = std::min<int64_t>(ntm * ntn, (int64_t)device_cu_count() * per_cu);
-    launch_kernel((dense_stream_kernel<S, MT, NS>), dim3((unsigned)grid), dim3(kDenseWaves * kWave), 0, st,
+    launch_kernel((dense_stream_kernel<S, MT, NS, PK>), dim3((unsigned)grid), dim3(kDenseWaves * kWave), 0, st,
                        (const T *)x, (const T *)w, (T *)y, M, N, K, ntm, ntn);
 }
 
-template <typename S>
+template <typename S, bool PK>
 static bool try_launch_stream(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
                               hipStream_t st)
 {
     using G = DenseGeom<S>;
     if (K % G::KB != 0 || !host_aligned16(x) || !host_aligned16(w)) return false;
     const int64_t mt = cdiv(M, 16);
-    if (mt <= 1) launch_stream_t<S, 1, 1>(x, w, y, M, N, K, st);
-    else if (mt <= 2) launch_stream_t<S, 2, 1>(x, w, y, M, N, K, st);
-    else if (N >= 16384) launch_stream_t<S, 4, 4>(x, w, y, M, N, K, st);
-    else if (N >= 6144) launch_stream_t<S, 4, 2>(x, w, y, M, N, K, st);
-    else launch_stream_t<S, 4, 1>(x, w, y, M, N, K, st);
-    return true;
-}
-
-// ---------------------------------------------------------------------------
-// Slot-group form for short M (at most 64 rows): transposed W, 16-bit types,
-// K a multiple of the block, x and W 16-byte aligned.
-//
-// Workgroup (ct, grp) owns the 128 output columns of tile ct (wave v: columns
-// 16v .. 16v + 15) and the Q consecutive slots grp*Q .. grp*Q + Q - 1.  It
-// walks its blocks as items u -> (step j = u / Q, slot grp*Q + u % Q), i.e.
-// block 8j + grp*Q + u % Q.  Each block of x (all rows of the M tile) is
-// staged once in LDS and read by all eight waves; each wave streams its 16
-// rows of W through a register ring.  Slot i of the group accumulates in its
-// own MFMA accumulator, block by block in ascending order, exactly as a wave
-// of the kernels above does, and the Q slot partials are added by their
-// subtree of slot_tree.  With 8/Q > 1 groups per tile, each group writes that
-// sum to the workspace; the last workgroup of the tile to arrive (counted with
-// a device-scope atomic) reads all group sums, adds them by the rest of
-// slot_tree and stores y.  Arrival order decides only who adds, never how.
-constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
-constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
-
-// What the slot kernel does with a finished tile: store y (EPI_Y), or the
-// SwiGLU activation of an interleaved gate/up tile (EPI_SWIGLU: the 128
-// columns of tile ct are gate columns 64ct .. 64ct + 63 followed by the up
-// columns of the same indices; a[m, 64ct + j] = silu_mul1(y[m, 128ct + j],
-// y[m, 128ct + 64 + j]), from the bf16-rounded y exactly as bi_silu_mul
-// would read it).
-enum SlotEpilogue { EPI_Y = 0, EPI_SWIGLU = 1 };
-
-template <typename S, int MT, int Q, int DW, int OCC, int EPI>
-__global__ __launch_bounds__(kDenseWaves * kWave, OCC)
-void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typename S::store_t *__restrict__ w,
-                        typename S::store_t *__restrict__ y, float *__restrict__ part,
-                        unsigned *__restrict__ counters, int64_t M, int64_t N, int64_t K)
-{
-    using G = DenseGeom<S>;
-    using T = typename S::store_t;
-    constexpr int P = kDenseWaves, NT = P * kWave;
-    constexpr int GRP = P / Q;                     // slot groups per column tile
-    constexpr int TR = MT * 16, KB = G::KB;
-    constexpr int XS = KB + 8;                     // LDS row stride: 272 bytes, 16-byte aligned, 4-bank shift per row
-    constexpr int XCH = TR * (KB / 8);             // 16-byte chunks in one block of x
-    constexpr int XPT = XCH > NT ? XCH / NT : 1;   // chunks staged per thread
-    constexpr int DX = 3;                          // x register ring depth (DW: W ring depth)
-    constexpr int U = lcm_c(lcm_c(3, DW), Q);       // unroll: a multiple of the LDS ring (3 = DX), DW and Q
-    static_assert(G::CPB == 4 && XPT <= 2 && (XCH % NT == 0 || XPT == 1), "slot kernel geometry");
-    __shared__ __attribute__((aligned(16))) T xs[3][TR][XS];
-    __shared__ int s_last;
-
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int g = lane >> 4, c = lane & 15;
-    const int ct = blockIdx.x, grp = blockIdx.y;
-    const int nb = (int)(K / KB);
-    const int slot0 = grp * Q;
-    const int nsteps = slot0 < nb ? (nb - slot0 + P - 1) / P : 0;
-    const int nitems = nsteps * Q;
-    // Block of item u.  Items past the last block re-read block slot0 (valid
-    // whenever nitems > 0) and are never multiplied.
-    auto block_of = [&](int u) {
-        const int b = (u / Q) * P + slot0 + (u % Q);
-        return b < nb ? b : slot0;
-    };
-
-    const int64_t n = (int64_t)ct * (P * 16) + wave * 16 + c;
-    const bool nok = n < N;
-    const T *wr = w + (nok ? n : N - 1) * K;     // padding columns read a real row, never stored
-    const int t = threadIdx.x, xc = t & 15;
-
-    struct XChunks { uint4 v0, v1; };
-    XChunks xr0, xr1, xr2;
-    auto xreg = [&](auto sc) -> XChunks & {
-        constexpr int sl = decltype(sc)::value % DX;
-        if constexpr (sl == 0) return xr0;
-        else if constexpr (sl == 1) return xr1;
-        else return xr2;
-    };
-    // thread t stages chunk (t + h*NT) mod XCH of the block: row / 16, 16 bytes at (chunk % 16) * 16
-    auto load_x = [&](XChunks &r, int u) {
-        const int64_t kb = (int64_t)block_of(u) * KB + xc * 8;
-        static_for<0, XPT>([&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            const int row = ((t + h * NT) % XCH) >> 4;
-            const uint4 v = *reinterpret_cast<const uint4 *>(x + (int64_t)(row < M ? row : M - 1) * K + kb);
-            if constexpr (h == 0) r.v0 = v;
-            else r.v1 = v;
-        });
-    };
-    auto store_x = [&](const XChunks &r, int buf) {
-        static_for<0, XPT>([&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            const int row = ((t + h * NT) % XCH) >> 4;
-            *reinterpret_cast<uint4 *>(&xs[buf][row][xc * 8]) = h == 0 ? r.v0 : r.v1;
-        });
-    };
-    uint4 wb[DW][G::CPB];
-    auto load_w = [&](uint4 (&B)[G::CPB], int u) {
-        const T *p = wr + (int64_t)block_of(u) * KB;
-#pragma unroll
-        for (int ci = 0; ci < G::CPB; ++ci) B[ci] = *reinterpret_cast<const uint4 *>(p + G::chunk_off(g, ci));
-    };
-
-    f32x4 acc[Q][MT];
-#pragma unroll
-    for (int i = 0; i < Q; ++i)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (nitems > 0) {
-        // Pipeline: x of item u + 1 goes to LDS slot (u + 1) % 3 at item u (its
-        // register slot is refilled with item u + 1 + DX); W runs DW - 1 items
-        // ahead.  Three LDS slots let one barrier per item separate the writers
-        // of slot (u + 1) % 3 from the last readers of that slot (item u - 2).
-        static_for<0, DX>([&](auto dc) { load_x(xreg(dc), decltype(dc)::value); });
-        store_x(xr0, 0);
-        load_x(xr0, DX);
-        static_for<0, DW - 1>([&](auto dc) { load_w(wb[decltype(dc)::value], decltype(dc)::value); });
-        // One item: stage x of item u + 1, refill the rings, wait for the
-        // workgroup, multiply item u (unless it lies past the last block).
-        auto item = [&](auto dc, int u) {
-            constexpr int d = decltype(dc)::value;
-            XChunks &nx = xreg(std::integral_constant<int, d + 1>{});
-            store_x(nx, (d + 1) % 3);
-            load_x(nx, u + 1 + DX);
-            load_w(wb[(d + DW - 1) % DW], u + DW - 1);
-            __syncthreads();
-            if ((u / Q) * P + slot0 + (d % Q) < nb) {
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    uint4 a[MT];
-#pragma unroll
-                    for (int m = 0; m < MT; ++m)
-                        a[m] = *reinterpret_cast<const uint4 *>(&xs[d % 3][m * 16 + c][G::chunk_off(g, st)]);
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) acc[d % Q][m] = DenseMfma<S>::mma(a[m], wb[d % DW][st], acc[d % Q][m]);
-                }
-            }
-        };
-        // Whole unrolled rounds run without item guards (exact load waits);
-        // the last partial round is guarded.
-        int u0 = 0;
-        for (; u0 + U <= nitems; u0 += U) static_for<0, U>([&](auto dc) { item(dc, u0 + decltype(dc)::value); });
-        if (u0 < nitems)
-            static_for<0, U>([&](auto dc) {
-                if (u0 + decltype(dc)::value < nitems) item(dc, u0 + decltype(dc)::value);
-            });
-    }
-
-    // the group's subtree of slot_tree
-    f32x4 h[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if constexpr (Q == 1) h[m] = acc[0][m];
-        else if constexpr (Q == 2) h[m] = acc[0][m] + acc[1][m];
-        else if constexpr (Q == 4) h[m] = (acc[0][m] + acc[1][m]) + (acc[2][m] + acc[3][m]);
-        else h[m] = ((acc[0][m] + acc[1][m]) + (acc[2][m] + acc[3][m])) + ((acc[4][m] + acc[5][m]) + (acc[6][m] + acc[7][m]));
-    }
-    // MFMA accumulator layout: lane (g, c), register r holds row 4g + r, column c.
-    auto store_y = [&](const f32x4 (&v)[MT]) {
-        if constexpr (EPI == EPI_Y) {
-            if (!nok) return;
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t row = m * 16 + g * 4 + r;
-                    if (row < M) y[row * N + n] = S::narrow(v[m][r]);
-                }
-        } else {
-            // the tile's rounded y into LDS (the x ring is free by now), then
-            // each thread forms 8 consecutive activations of one row
-            T (*tile)[XS] = xs[0];
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) tile[m * 16 + g * 4 + r][wave * 16 + c] = S::narrow(v[m][r]);
-            __syncthreads();
-            const int F = (int)(N / 2);
-            for (int it = threadIdx.x; it < TR * 8; it += NT) {
-                const int row = it >> 3, jg = (it & 7) * 8;
-                if (row >= M) continue;
-                const uint4 gv = *reinterpret_cast<const uint4 *>(&tile[row][jg]);
-                const uint4 uv = *reinterpret_cast<const uint4 *>(&tile[row][64 + jg]);
-                const uint16_t *g8 = reinterpret_cast<const uint16_t *>(&gv), *u8 = reinterpret_cast<const uint16_t *>(&uv);
-                uint16_t o8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o8[e] = silu_mul1(g8[e], u8[e]);
-                *reinterpret_cast<uint4 *>(y + (int64_t)row * F + (int64_t)ct * 64 + jg) = __builtin_bit_cast(uint4, o8);
-            }
-        }
-    };
-    if constexpr (GRP == 1) {
-        if constexpr (EPI != EPI_Y) __syncthreads();   // every wave is done reading the x ring
-        store_y(h);
-    } else {
-        // Group sums go to the workspace as 16-byte records, m-major: record
-        // (tile, group, wave, m) holds lane l's four values at byte 16 l.
-        // Stores and loads are device scope (sc1: through to the level every
-        // CU sees), so no cache-wide write-back or invalidate is needed: the
-        // wait below and the barrier order this workgroup's stores before
-        // thread 0 bumps the tile's counter, and the last workgroup reads the
-        // sums only after it has seen the count.
-        constexpr int CPOL_DEVICE = 16;            // sc1
-        constexpr int REC = MT * kWave * 16;       // bytes per (group, wave)
-        const __amdgpu_buffer_rsrc_t rsrc =
-            __builtin_amdgcn_make_buffer_rsrc(part + (int64_t)ct * GRP * P * (REC / 4), (short)0, GRP * P * REC, 0x00020000);
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, h[m]), rsrc,
-                                                   (grp * P + wave) * REC + m * kWave * 16 + lane * 16, 0, CPOL_DEVICE);
-        __builtin_amdgcn_s_waitcnt(0);             // every store of this wave acknowledged
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const unsigned prev = __hip_atomic_fetch_add(&counters[ct], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = prev == (unsigned)(GRP - 1);
-        }
-        __syncthreads();
-        if (!s_last) return;
-        if (threadIdx.x == 0) __hip_atomic_store(&counters[ct], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        f32x4 out[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            f32x4 v[GRP];
-#pragma unroll
-            for (int q = 0; q < GRP; ++q)
-                v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rsrc, (q * P + wave) * REC + m * kWave * 16 + lane * 16, 0, CPOL_DEVICE));
-            if constexpr (GRP == 2) out[m] = v[0] + v[1];
-            else if constexpr (GRP == 4) out[m] = (v[0] + v[1]) + (v[2] + v[3]);
-            else out[m] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-        }
-        store_y(out);
-    }
-}
-
-// Workspace of the slot-group form: a fixed counter area (one counter per
-// column tile, room for kSlotMaxTiles tiles, left zero by every call) followed
-// by the group sums.  The counter area has the same place and size for every
-// shape, so the group sums of one call never land on the counters of another
-// call that shares the workspace.
-constexpr int64_t kSlotTileCols = kDenseWaves * 16;
-constexpr int64_t kSlotMaxTiles = 16384;                    // N up to 2^21 columns
-constexpr size_t kSlotCounterBytes = kSlotMaxTiles * sizeof(unsigned);
-
-static int slot_mt(int64_t M) { return M <= 32 ? 2 : 4; }
-
-static size_t slot_ws_bytes(int64_t M, int64_t N, int groups)
-{
-    const int64_t rec = (int64_t)slot_mt(M) * 4 * kWave * (int64_t)sizeof(float);
-    return kSlotCounterBytes + (size_t)(cdiv(N, kSlotTileCols) * groups * kDenseWaves * rec);
-}
-
-template <typename S, int MT, int Q, int EPI>
-static void launch_slots_t(const void *x, const void *w, void *y, void *ws, int64_t M, int64_t N, int64_t K,
-                           hipStream_t st)
-{
-    using T = typename S::store_t;
-    const int64_t ntc = cdiv(N, kSlotTileCols);
-    unsigned *counters = (unsigned *)ws;
-    float *part = (float *)((char *)ws + kSlotCounterBytes);
-    // W ring depth and waves per SIMD: two workgroups per CU (at most 128
-    // VGPRs) wherever the accumulators allow it.
-    constexpr int DW = MT == 4 ? 2 : 4;
-    constexpr int OCC = Q * MT <= 4 ? 4 : 2;
-    launch_kernel((dense_slots_kernel<S, MT, Q, DW, OCC, EPI>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
-                       dim3(kDenseWaves * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, counters, M, N, K);
-}
-
-// Slots per workgroup: the largest group that still gives at least one
-// workgroup per CU (MT = 4 keeps at most four slots in registers).
-template <typename S, int MT, int EPI>
-static void launch_slots_mt(const void *x, const void *w, void *y, void *ws, int64_t M, int64_t N, int64_t K,
-                            hipStream_t st)
-{
-    const int64_t ntc = cdiv(N, kSlotTileCols), cu = device_cu_count();
-    // All eight slots in one workgroup (no exchange) once the column tiles
-    // alone come close to one per CU.
-    if (ntc * 4 >= cu * 3) {
-        launch_slots_t<S, MT, 8, EPI>(x, w, y, ws, M, N, K, st);
-        return;
-    }
-    if (ntc * 2 >= cu) launch_slots_t<S, MT, 4, EPI>(x, w, y, ws, M, N, K, st);
-    else if (ntc * 4 >= cu) launch_slots_t<S, MT, 2, EPI>(x, w, y, ws, M, N, K, st);
-    else launch_slots_t<S, MT, 1, EPI>(x, w, y, ws, M, N, K, st);
-}
-
-template <typename S, int EPI = EPI_Y>
-static bool try_launch_slots(const void *x, const void *w, void *y, void *ws, size_t ws_bytes, int64_t M,
-                             int64_t N, int64_t K, hipStream_t st)
-{
-    using G = DenseGeom<S>;
-    // M <= 16: x is small, and bi_matmul's one-workgroup-per-tile kernel,
-    // which needs no exchange of partial sums, streams W faster.
-    if (!ws || M <= 16 || M > 64 || K % G::KB != 0 || !host_aligned16(x) || !host_aligned16(w) ||
-        !host_aligned16(ws))
-        return false;
-    if (ws_bytes < slot_ws_bytes(M, N, kDenseWaves)) return false;
-    if (slot_mt(M) == 2) launch_slots_mt<S, 2, EPI>(x, w, y, ws, M, N, K, st);
-    else launch_slots_mt<S, 4, EPI>(x, w, y, ws, M, N, K, st);
+    if (mt <= 1) launch_stream_t<S, 1, 1, PK>(x, w, y, M, N, K, st);
+    else if (mt <= 2) launch_stream_t<S, 2, 1, PK>(x, w, y, M, N, K, st);
+    else if (N >= 16384) launch_stream_t<S, 4, 4, PK>(x, w, y, M, N, K, st);
+    else if (N >= 6144) launch_stream_t<S, 4, 2, PK>(x, w, y, M, N, K, st);
+    else launch_stream_t<S, 4, 1, PK>(x, w, y, M, N, K, st);
     return true;
 }
 
 template <typename S>
 static void launch_dense(const void *x, const void *w, void *y, float *part, int64_t M, int64_t N,
-                         int64_t K, bool trans, int splits, hipStream_t st)
+                         int64_t K, int32_t layout, int splits, hipStream_t st)
 {
-    if (trans && splits == 1 && part == nullptr && try_launch_stream<S>(x, w, y, M, N, K, st)) return;
+    const bool plain = splits == 1 && part == nullptr;
+    if constexpr (!std::is_same_v<S, F32>) {
+        if (layout == W_PACKED) {                  // K % 128 == 0 and 16-byte aligned operands (checked)
+            if (plain && try_launch_stream<S, true>(x, w, y, M, N, K, st)) return;
+            launch_dense_mt<S, true, true, true>(x, w, y, part, M, N, K, splits, st);
+            return;
+        }
+    }
+    const bool trans = layout != W_NATURAL;
+    if (trans && plain && try_launch_stream<S, false>(x, w, y, M, N, K, st)) return;
     // 16-byte chunk loads when K is a multiple of the chunk length (chunks then
     // never straddle K) and both operands start on 16-byte boundaries; the
     // element-wise path fills the same slots, so the tree is the same.
@@ -783,82 +428,59 @@ static void launch_dense(const void *x, const void *w, void *y, float *part, int
     }
 }
 
-static bi_status check_dense(const void *x, const void *w, const void *y, int64_t M, int64_t N, int64_t K,
-                             int32_t dtype)
+void dispatch_dense(const void *x, const void *w, void *y, float *part, int64_t M, int64_t N, int64_t K,
+                    int32_t dtype, int32_t layout, int splits, hipStream_t st)
 {
-    if (!x || !w || !y) return BI_ERR_NULL;
-    if (M < 1 || N < 1 || K < 1 || M > (1ll << 31) || N > (1ll << 31) || K > (1ll << 31)) return BI_ERR_SHAPE;
-    if (dtype != BI_BF16 && dtype != BI_F16 && dtype != BI_F32) return BI_ERR_DTYPE;
-    const size_t esz = dtype == BI_F32 ? 4 : 2;
-    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & (esz - 1)) return BI_ERR_ALIGN;
-    return BI_OK;
+    if (dtype == BI_BF16) launch_dense<BF16>(x, w, y, part, M, N, K, layout, splits, st);
+    else if (dtype == BI_F16) launch_dense<F16>(x, w, y, part, M, N, K, layout, splits, st);
+    else launch_dense<F32>(x, w, y, part, M, N, K, layout, splits, st);
 }
 
-static void dispatch_dense(const void *x, const void *w, void *y, float *part, int64_t M, int64_t N,
-                           int64_t K, int32_t dtype, bool trans, int splits, hipStream_t st)
+// [N, K] -> tile-packed (W_PACKED): thread = one 16-byte chunk of the packed
+// buffer; rows past N are written as zeros.
+__global__ void pack_weights_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ wp, int64_t N, int64_t K)
 {
-    if (dtype == BI_BF16) launch_dense<BF16>(x, w, y, part, M, N, K, trans, splits, st);
-    else if (dtype == BI_F16) launch_dense<F16>(x, w, y, part, M, N, K, trans, splits, st);
-    else launch_dense<F32>(x, w, y, part, M, N, K, trans, splits, st);
-}
-
-// SwiGLU activation of an interleaved gate/up product (the fallback of
-// bi_matmul_swiglu): in each row, columns 128 i + j and 128 i + 64 + j are
-// gate and up of activation 64 i + j.  Thread = 8 consecutive activations.
-__global__ void swiglu_il_kernel(const uint16_t *__restrict__ gu, uint16_t *__restrict__ a, int64_t rows, int64_t F)
-{
-    const int64_t fc = F / 8, n = rows * fc;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n; c += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = c / fc, i = (c - r * fc) * 8;
-        const uint16_t *gp = gu + r * 2 * F + (i / 64) * 128 + (i % 64);
-        const uint4 gv = *reinterpret_cast<const uint4 *>(gp), uv = *reinterpret_cast<const uint4 *>(gp + 64);
-        const uint16_t *g8 = reinterpret_cast<const uint16_t *>(&gv), *u8 = reinterpret_cast<const uint16_t *>(&uv);
-        uint16_t o8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] = silu_mul1(g8[e], u8[e]);
-        *reinterpret_cast<uint4 *>(a + r * F + i) = __builtin_bit_cast(uint4, o8);
+    const int64_t nb = K / 128, nrg = (N + 15) / 16, n = nrg * nb * 256;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(i & 63), s = (int)((i >> 6) & 3);
+        const int64_t rest = i >> 8, b = rest % nb, rg = rest / nb;
+        const int64_t row = rg * 16 + (lane & 15), k = b * 128 + s * 32 + (lane >> 4) * 8;
+        const uint4 v = row < N ? *reinterpret_cast<const uint4 *>(w + row * K + k) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(wp + packed_off(rg, nb, b, s, lane)) = v;
     }
 }
-
-static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace bi
 
 using namespace bi;
 
-extern "C" bi_status bi_matmul(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
-                               int32_t dtype, int32_t w_transposed, hipStream_t stream)
+extern "C" size_t bi_packed_weight_bytes(int64_t N, int64_t K, int32_t dtype)
 {
-    bi_status s = check_dense(x, w, y, M, N, K, dtype);
-    if (s != BI_OK) return s;
+    if (N < 1 || K < 1 || K % 128 || N > (1ll << 31) || K > (1ll << 31) || (dtype != BI_BF16 && dtype != BI_F16))
+        return 0;
+    return (size_t)cdiv(N, 16) * 16 * (size_t)K * 2;
+}
+
+extern "C" bi_status bi_pack_weights(const void *w, void *wp, int64_t N, int64_t K, int32_t dtype, hipStream_t stream)
+{
+    if (!w || !wp) return BI_ERR_NULL;
+    if (dtype != BI_BF16 && dtype != BI_F16) return BI_ERR_DTYPE;
+    if (bi_packed_weight_bytes(N, K, dtype) == 0) return BI_ERR_SHAPE;
+    if (!host_aligned16(w) || !host_aligned16(wp)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
-    dispatch_dense(x, w, y, nullptr, M, N, K, dtype, w_transposed != 0, 1, stream);
+    const int64_t chunks = cdiv(N, 16) * (K / 128) * 256;
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(chunks, 256), 65536);
+    launch_kernel(pack_weights_kernel, dim3(blocks), dim3(256), 0, stream, (const uint16_t *)w, (uint16_t *)wp, N, K);
     return launch_status();
 }
 
-extern "C" size_t bi_matmul_ws_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t w_transposed)
+extern "C" bi_status bi_matmul(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
+                               int32_t dtype, int32_t w_layout, hipStream_t stream)
 {
-    if (M <= 16 || N < 1 || K < 1 || M > 64 || !w_transposed || (dtype != BI_BF16 && dtype != BI_F16) ||
-        cdiv(N, kSlotTileCols) > kSlotMaxTiles)
-        return 0;
-    return slot_ws_bytes(M, N, kDenseWaves);
-}
-
-extern "C" bi_status bi_matmul_ws(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
-                                  int32_t dtype, int32_t w_transposed, void *ws, size_t ws_bytes, hipStream_t stream)
-{
-    bi_status s = check_dense(x, w, y, M, N, K, dtype);
+    bi_status s = check_dense(x, w, y, M, N, K, dtype, w_layout);
     if (s != BI_OK) return s;
-    const size_t need = bi_matmul_ws_workspace_bytes(M, N, K, dtype, w_transposed);
-    if (need > 0 && (!ws || ws_bytes < need)) return BI_ERR_WORKSPACE;
-    if (need > 0 && !host_aligned16(ws)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
-    bool done = false;
-    if (need > 0) {
-        if (dtype == BI_BF16) done = try_launch_slots<BF16>(x, w, y, ws, ws_bytes, M, N, K, stream);
-        else done = try_launch_slots<F16>(x, w, y, ws, ws_bytes, M, N, K, stream);
-    }
-    if (!done) dispatch_dense(x, w, y, nullptr, M, N, K, dtype, w_transposed != 0, 1, stream);
+    dispatch_dense(x, w, y, nullptr, M, N, K, dtype, w_layout, 1, stream);
     return launch_status();
 }
 
@@ -869,19 +491,19 @@ extern "C" size_t bi_matmul_split_workspace_bytes(int64_t M, int64_t N, int32_t 
 }
 
 extern "C" bi_status bi_matmul_split(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
-                                     int32_t dtype, int32_t w_transposed, int32_t splits, void *ws,
+                                     int32_t dtype, int32_t w_layout, int32_t splits, void *ws,
                                      size_t ws_bytes, hipStream_t stream)
 {
-    bi_status s = check_dense(x, w, y, M, N, K, dtype);
+    bi_status s = check_dense(x, w, y, M, N, K, dtype, w_layout);
     if (s != BI_OK) return s;
     if (splits < 1 || splits > 1024) return BI_ERR_SHAPE;
-    if (splits == 1) return bi_matmul(x, w, y, M, N, K, dtype, w_transposed, stream);
+    if (splits == 1) return bi_matmul(x, w, y, M, N, K, dtype, w_layout, stream);
     if (!ws) return BI_ERR_WORKSPACE;
     if (!host_aligned16(ws)) return BI_ERR_ALIGN;
     if (ws_bytes < bi_matmul_split_workspace_bytes(M, N, splits)) return BI_ERR_WORKSPACE;
     (void)hipGetLastError();
     float *part = (float *)ws;
-    dispatch_dense(x, w, y, part, M, N, K, dtype, w_transposed != 0, splits, stream);
+    dispatch_dense(x, w, y, part, M, N, K, dtype, w_layout, splits, stream);
     const int64_t MN = M * N;
     const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(MN, 256), 65536);
     if (dtype == BI_BF16) launch_kernel(split_reduce_kernel<BF16>, dim3(blocks), dim3(256), 0, stream, part, (uint16_t *)y, MN, splits);
@@ -896,38 +518,3 @@ extern "C" bi_status bi_time_next_launch(hipEvent_t start, hipEvent_t stop)
     return BI_OK;
 }
 
-extern "C" size_t bi_matmul_swiglu_workspace_bytes(int64_t M, int64_t F, int64_t K, int32_t dtype)
-{
-    if (M < 1 || F < 1 || K < 1 || dtype != BI_BF16 || F % 64 || M > (1ll << 31) || F > (1ll << 30)) return 0;
-    // the slot form's counter area, then its group sums or (any other shape)
-    // the scratch product: never both in one call
-    const size_t slot = bi_matmul_ws_workspace_bytes(M, 2 * F, K, dtype, 1);
-    const size_t prod = align256((size_t)M * (size_t)(2 * F) * sizeof(uint16_t));
-    return kSlotCounterBytes + std::max(slot > 0 ? slot - kSlotCounterBytes : 0, prod);
-}
-
-extern "C" bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, int64_t M, int64_t F, int64_t K,
-                                      int32_t dtype, void *ws, size_t ws_bytes, hipStream_t stream)
-{
-    if (F < 1 || F > (1ll << 30)) return BI_ERR_SHAPE;
-    bi_status s = check_dense(x, w_il, a, M, 2 * F, K, dtype);
-    if (s != BI_OK) return s;
-    if (dtype != BI_BF16) return BI_ERR_DTYPE;
-    if (F % 64) return BI_ERR_SHAPE;
-    if (!host_aligned16(a)) return BI_ERR_ALIGN;
-    const size_t need = bi_matmul_swiglu_workspace_bytes(M, F, K, dtype);
-    if (!ws || ws_bytes < need) return BI_ERR_WORKSPACE;
-    if (!host_aligned16(ws)) return BI_ERR_ALIGN;
-    const size_t slot = bi_matmul_ws_workspace_bytes(M, 2 * F, K, dtype, 1);
-    (void)hipGetLastError();
-    if (slot > 0 && try_launch_slots<BF16, EPI_SWIGLU>(x, w_il, a, ws, slot, M, 2 * F, K, stream)) return launch_status();
-    // any other shape: the product into the scratch after the counter area
-    // (which stays zero for later slot-form calls on this workspace), then
-    // the activation
-    uint16_t *gu = (uint16_t *)((char *)ws + kSlotCounterBytes);
-    dispatch_dense(x, w_il, gu, nullptr, M, 2 * F, K, dtype, true, 1, stream);
-    const int64_t n = M * F / 8;
-    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n, 256), 65536);
-    hipLaunchKernelGGL(swiglu_il_kernel, dim3(blocks), dim3(256), 0, stream, (const uint16_t *)gu, (uint16_t *)a, M, F);
-    return launch_status();
-}

@@ -24,8 +24,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (add_rmsnorm, argmax, embed, interleave_gate_up, lib, matmul_swiglu, matmul_ws, rmsnorm,
-               rope_kv_write, sdpa, sdpa_workspace_bytes)
+from . import (W_PACKED, add_rmsnorm, argmax, embed, interleave_gate_up, lib, matmul_swiglu, matmul_ws,
+               pack_weights, rmsnorm, rope_kv_write, sdpa, sdpa_workspace_bytes)
 from .inputs import rope_tables
 
 
@@ -47,14 +47,18 @@ class Decoder:
         W = weights
         self.embed_w = _dev16(W["embed"], d)
         self.layers = [{k: _dev16(v, d) for k, v in lw.items()} for lw in W["layers"]]
-        # the gate/up weight [Wg; Wu] stored interleaved in blocks of 64 rows,
-        # the layout the fused projection + SwiGLU kernel reads
+        # Projection weights are kept tile-packed (pack_weights: same bits,
+        # fewer DRAM pages per byte streamed); the gate/up weight [Wg; Wu] is
+        # first interleaved in blocks of 8 rows, the layout the fused
+        # projection + SwiGLU kernel reads.
         for lw in self.layers:
             wgu = lw.pop("wgu")
-            lw["wgu_il"] = interleave_gate_up(wgu[:self.F], wgu[self.F:])
+            lw["wgu_il"] = pack_weights(interleave_gate_up(wgu[:self.F], wgu[self.F:]))
             del wgu
+            for k in ("wqkv", "wo", "wdown"):
+                lw[k] = pack_weights(lw[k])
         self.final_norm = _dev16(W["final_norm"], d)
-        self.lm_head = _dev16(W["lm_head"], d)
+        self.lm_head = pack_weights(_dev16(W["lm_head"], d))
         cos_t, sin_t = rope_tables(max_len, self.D, c.get("rope_theta", 10000.0))
         self.cos_t = torch.from_numpy(cos_t).to(d)
         self.sin_t = torch.from_numpy(sin_t).to(d)
@@ -98,18 +102,18 @@ class Decoder:
         # (the next block's norm, or the final norm after the last layer).
         rmsnorm(x, self.layers[0]["attn_norm"], self.eps, out=h)
         for li, Lw in enumerate(self.layers):
-            matmul_ws(h, Lw["wqkv"], self.mws, True, out=qkv)
+            matmul_ws(h, Lw["wqkv"], self.mws, out=qkv)
             kc, vc = self.kc[li][:B], self.vc[li][:B]
             rope_kv_write(qkv, q, kc, vc, kv, self.cos_t, self.sin_t, B, Q, self.Hq, self.Hkv, self.D)
             sdpa(q.view(B, Q, self.Hq, self.D), kc, vc, kv, max_kv, scale, True,
                  out=o.view(B, Q, self.Hq, self.D), ws=self.ws)
-            matmul_ws(o, Lw["wo"], self.mws, True, out=t1)
+            matmul_ws(o, Lw["wo"], self.mws, out=t1)
             add_rmsnorm(x, t1, Lw["mlp_norm"], self.eps, x_out=x, out=h)
             matmul_swiglu(h, Lw["wgu_il"], self.sws, out=a)
-            matmul_ws(a, Lw["wdown"], self.mws, True, out=t1)
+            matmul_ws(a, Lw["wdown"], self.mws, out=t1)
             nxt = self.layers[li + 1]["attn_norm"] if li + 1 < self.L else self.final_norm
             add_rmsnorm(x, t1, nxt, self.eps, x_out=x, out=h)
-        matmul_ws(h, self.lm_head, self.mws, True, out=self.logits[:T])
+        matmul_ws(h, self.lm_head, self.mws, out=self.logits[:T])
         argmax(self.logits[:T], out=self.next_ids[:T])
         return self.logits[:T]
 
@@ -135,7 +139,8 @@ class Decoder:
         eps = ctypes.c_float(self.eps)
         steps = [("embed", L.bi_embed, (p(self.ids), p(self.embed_w), p(x), T, self.V, H, st))]
         mws, mwsb = p(self.mws), self.mws.numel()
-        mm = lambda xin, w, out, N, K: ("matmul", L.bi_matmul_ws, (p(xin), p(w), p(out), T, N, K, 0, 1, mws, mwsb, st))
+        mm = lambda xin, w, out, N, K: ("matmul", L.bi_matmul_ws, (p(xin), p(w.data), p(out), T, N, K, 0, W_PACKED, mws,
+                                                                    mwsb, st))
         steps.append(("rmsnorm", L.bi_rmsnorm, (p(x), p(self.layers[0]["attn_norm"]), p(h), T, H, eps, 0, st)))
         for li, Lw in enumerate(self.layers):
             kc, vc = self.kc[li], self.vc[li]
@@ -149,8 +154,8 @@ class Decoder:
                                      self.D, scale, 1, 0, p(self.ws), self.ws.numel(), st)),
                 mm(o, Lw["wo"], t1, H, qn),
                 ("add_rmsnorm", L.bi_add_rmsnorm, (p(x), p(t1), p(x), p(Lw["mlp_norm"]), p(h), T, H, eps, 0, st)),
-                ("matmul_swiglu", L.bi_matmul_swiglu, (p(h), p(Lw["wgu_il"]), p(a), T, self.F, H, 0, p(self.sws),
-                                                       self.sws.numel(), st)),
+                ("matmul_swiglu", L.bi_matmul_swiglu, (p(h), p(Lw["wgu_il"].data), p(a), T, self.F, H, 0, W_PACKED,
+                                                       p(self.sws), self.sws.numel(), st)),
                 mm(a, Lw["wdown"], t1, H, self.F),
                 ("add_rmsnorm", L.bi_add_rmsnorm, (p(x), p(t1), p(x), p(nxt), p(h), T, H, eps, 0, st)),
             ]

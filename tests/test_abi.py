@@ -147,17 +147,38 @@ def test_matmul_swiglu_validation_and_workspace_size():
     # the 64 KiB counter area, then the slot form's group sums or a scratch [M, 2F] bf16 product
     assert need == L.bi_matmul_ws_workspace_bytes(64, 2 * 14336, 4096, 0, 1)      # group sums are the larger
     assert L.bi_matmul_swiglu_workspace_bytes(1, 64, 128, 0) == 65536 + 256       # 1 x 128 bf16, 256-byte rounded
+    assert L.bi_matmul_swiglu_workspace_bytes(1, 8, 128, 0) == 65536 + 256        # F = 8: one interleave block
     assert L.bi_matmul_swiglu_workspace_bytes(65, 14336, 4096, 0) == 65536 + 65 * 2 * 14336 * 2
     assert L.bi_matmul_swiglu_workspace_bytes(64, 14336, 4096, 1) == 0            # f16
-    assert L.bi_matmul_swiglu_workspace_bytes(64, 100, 4096, 0) == 0              # F % 64
-    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 0, None, 0, None) == WORKSPACE
-    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 0, A, need - 1, None) == WORKSPACE
-    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 1, A, need, None) == DTYPE
-    assert L.bi_matmul_swiglu(A, A, A, 64, 100, 4096, 0, A, need, None) == SHAPE
-    assert L.bi_matmul_swiglu(A, A, A, 0, 14336, 4096, 0, A, need, None) == SHAPE
-    assert L.bi_matmul_swiglu(A, A, P(0x10010 + 2), 64, 14336, 4096, 0, A, need, None) == ALIGN
-    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 0, P(0x10010 + 2), need, None) == ALIGN
-    assert L.bi_matmul_swiglu(None, A, A, 64, 14336, 4096, 0, A, need, None) == NULL
+    assert L.bi_matmul_swiglu_workspace_bytes(64, 100, 4096, 0) == 0              # F % 8
+    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 0, 1, None, 0, None) == WORKSPACE
+    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 0, 1, A, need - 1, None) == WORKSPACE
+    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 1, 1, A, need, None) == DTYPE
+    assert L.bi_matmul_swiglu(A, A, A, 64, 100, 4096, 0, 1, A, need, None) == SHAPE
+    assert L.bi_matmul_swiglu(A, A, A, 0, 14336, 4096, 0, 1, A, need, None) == SHAPE
+    assert L.bi_matmul_swiglu(A, A, P(0x10010 + 2), 64, 14336, 4096, 0, 1, A, need, None) == ALIGN
+    assert L.bi_matmul_swiglu(A, A, A, 64, 14336, 4096, 0, 1, P(0x10010 + 2), need, None) == ALIGN
+    assert L.bi_matmul_swiglu(None, A, A, 64, 14336, 4096, 0, 1, A, need, None) == NULL
+
+
+def test_packed_weight_validation():
+    """Packing needs a 16-bit [N, K] weight with K % 128 == 0 and 16-byte
+    aligned buffers; the packed layout is refused where the kernels cannot
+    read it, before any launch."""
+    L = bi.lib()
+    assert L.bi_packed_weight_bytes(37, 384, 0) == 48 * 384 * 2
+    assert L.bi_packed_weight_bytes(16, 384, 1) == 16 * 384 * 2
+    assert L.bi_packed_weight_bytes(16, 100, 0) == 0        # K % 128
+    assert L.bi_packed_weight_bytes(16, 128, 2) == 0        # f32
+    assert L.bi_pack_weights(None, A, 16, 128, 0, None) == NULL
+    assert L.bi_pack_weights(A, A, 16, 100, 0, None) == SHAPE
+    assert L.bi_pack_weights(A, A, 16, 128, 2, None) == DTYPE
+    assert L.bi_pack_weights(A, P(0x10010 + 2), 16, 128, 0, None) == ALIGN
+    assert L.bi_matmul(A, A, A, 4, 16, 100, 0, 2, None) == SHAPE       # packed needs K % 128 == 0
+    assert L.bi_matmul(A, A, A, 4, 16, 128, 2, 2, None) == DTYPE       # packed f32
+    assert L.bi_matmul(A, P(0x10010 + 2), A, 4, 16, 128, 0, 2, None) == ALIGN
+    assert L.bi_matmul(A, A, A, 4, 16, 128, 0, 3, None) == SHAPE       # no such layout
+    assert L.bi_matmul_swiglu(A, A, A, 64, 64, 128, 0, 0, A, 1 << 30, None) == UNSUP
 
 
 def test_add_rmsnorm_validation():

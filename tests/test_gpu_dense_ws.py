@@ -45,6 +45,8 @@ def same(a, b):
     (64, 6144, 4096),
     (32, 32768, 1024),     # enough column tiles for all eight slots in one workgroup
     (64, 32768, 1024),
+    (64, 28656, 256),      # 7-wave (112-column) tiles fill 256 CUs; last tile ragged
+    (20, 28656, 384),
     (65, 512, 4096),       # long M: bi_matmul's kernels
     (64, 512, 4100),       # K not a multiple of 128: bi_matmul's kernels
 ])
@@ -128,6 +130,8 @@ def test_run_to_run_determinism():
     (40, 192, 896),        # few column tiles: slot groups exchange partial sums
     (64, 14336, 4096),     # the decoder's MLP at batch 64
     (64, 640, 4224),
+    (17, 14328, 256),      # 7-wave tiles, last tile ragged
+    (33, 200, 512),        # F not a multiple of 64: 8-row interleave blocks across tiles
     (65, 14336, 4096),     # long M: fallback
     (64, 128, 4100),       # K not a multiple of 128: fallback
 ])
@@ -173,3 +177,64 @@ def test_swiglu_oracle_parity():
     ws = bi.matmul_swiglu_workspace(M, F, K, device=dev())
     a = to_np(bi.matmul_swiglu(to_dev(x, "bf16"), bi.interleave_gate_up(w[:F], w[F:]), ws))
     assert_parity(a, ref, "bf16", "swiglu")
+
+
+# ---------------------------------------------------------------------------
+# tile-packed weights: same bits as [N, K] in every dense path
+# ---------------------------------------------------------------------------
+
+def test_pack_layout_matches_definition():
+    """Every element lands where the header's formula puts it; rows past N
+    are zero."""
+    N, K = 37, 384
+    w = torch.arange(N * K, dtype=torch.int32).remainder(30011).to(torch.int16).view(N, K)
+    wp = bi.pack_weights(w.view(torch.bfloat16).to(dev())).data.view(torch.int16).cpu().numpy()
+    nb, nrg = K // 128, (N + 15) // 16
+    assert wp.size == nrg * 16 * K
+    ref = np.zeros(nrg * 16 * K, np.int16)
+    wn = w.numpy()
+    for r in range(nrg):
+        for b in range(nb):
+            for s in range(4):
+                for lane in range(64):
+                    g, c = lane >> 4, lane & 15
+                    row = 16 * r + c
+                    off = (((r * nb + b) * 4 + s) * 64 + lane) * 8
+                    if row < N:
+                        ref[off:off + 8] = wn[row, 128 * b + 32 * s + 8 * g:128 * b + 32 * s + 8 * g + 8]
+    assert np.array_equal(wp, ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("N,K", [(96, 128), (1000, 896), (4096, 4096), (28656, 256), (6144, 4096)])
+def test_packed_bits_equal(dtype, N, K):
+    """bi_matmul and bi_matmul_ws on the packed weight give the [N, K]
+    weight's bits for every M form: the streaming kernel (M <= 16), the slot
+    form (16 < M <= 64) and the tiled kernel (M > 64)."""
+    w = rand((N, K), dtype, seed=N + K, scale=0.02)
+    wp = bi.pack_weights(w)
+    x = rand((96, K), dtype, seed=K + 1)
+    ws = bi.matmul_workspace(64, N, K, TD[dtype], device=dev())
+    full = bi.matmul(x, w)
+    assert same(bi.matmul(x, wp), full), "M=96 tiled"
+    for M in (1, 5, 16, 17, 40, 64):
+        xm = x[:M].contiguous()
+        assert same(bi.matmul(xm, wp), full[:M]), f"matmul M={M}"
+        assert same(bi.matmul_ws(xm, wp, ws), full[:M]), f"matmul_ws M={M}"
+    assert int(ws[:65536].count_nonzero()) == 0
+
+
+def test_packed_swiglu_and_split_variant():
+    F, K = 1024, 512
+    wg = rand((F, K), "bf16", seed=7, scale=0.02)
+    wu = rand((F, K), "bf16", seed=8, scale=0.02)
+    wil = bi.interleave_gate_up(wg, wu)
+    wilp = bi.pack_weights(wil)
+    ws = bi.matmul_swiglu_workspace(64, F, K, device=dev())
+    for M in (1, 17, 64, 70):
+        x = rand((M, K), "bf16", seed=M)
+        assert same(bi.matmul_swiglu(x, wilp, ws), bi.matmul_swiglu(x, wil, ws)), f"M={M}"
+    # the comparison variant reads packed weights too (same bits as on [N, K])
+    x = rand((8, K), "bf16", seed=3)
+    for s in (1, 2, 4):
+        assert same(bi.matmul_split(x, wilp, s), bi.matmul_split(x, wil, s)), f"splits={s}"
