@@ -55,7 +55,7 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
     constexpr int XPT = (XCH + NT - 1) / NT;       // chunks staged per thread (the last round may be partial)
     constexpr int DX = 3;                          // x register ring depth (DW: W ring depth)
     constexpr int U = lcm_c(lcm_c(3, DW), Q);       // unroll: a multiple of the LDS ring (3 = DX), DW and Q
-    static_assert(G::CPB == 4 && XPT <= 3, "slot kernel geometry");
+    static_assert(G::CPB == 4 && XPT <= 4, "slot kernel geometry");
     __shared__ __attribute__((aligned(16))) T xs[3][TR][XS];
     __shared__ int s_last;
 
@@ -80,7 +80,7 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
     const int64_t wrg = (int64_t)ct * NW + wave < nrg ? (int64_t)ct * NW + wave : nrg - 1;   // packed row group
     const int t = threadIdx.x, xc = t & 15;
 
-    struct XChunks { uint4 v0, v1, v2; };
+    struct XChunks { uint4 v0, v1, v2, v3; };
     XChunks xr0, xr1, xr2;
     auto xreg = [&](auto sc) -> XChunks & {
         constexpr int sl = decltype(sc)::value % DX;
@@ -100,7 +100,8 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
             const uint4 v = *reinterpret_cast<const uint4 *>(x + (int64_t)(row < M ? row : M - 1) * K + kb);
             if constexpr (h == 0) r.v0 = v;
             else if constexpr (h == 1) r.v1 = v;
-            else r.v2 = v;
+            else if constexpr (h == 2) r.v2 = v;
+            else r.v3 = v;
         });
     };
     auto store_x = [&](const XChunks &r, int buf) {
@@ -108,7 +109,7 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
             constexpr int h = decltype(hc)::value;
             if (XCH % NT == 0 || h + 1 < XPT || t + h * NT < XCH) {
                 const int row = (t + h * NT) >> 4;
-                *reinterpret_cast<uint4 *>(&xs[buf][row][xc * 8]) = h == 0 ? r.v0 : h == 1 ? r.v1 : r.v2;
+                *reinterpret_cast<uint4 *>(&xs[buf][row][xc * 8]) = h == 0 ? r.v0 : h == 1 ? r.v1 : h == 2 ? r.v2 : r.v3;
             }
         });
     };
@@ -263,7 +264,9 @@ static void launch_slots_t(const void *x, const void *w, void *y, void *ws, int6
                            hipStream_t st)
 {
     using T = typename S::store_t;
-    static_assert(NW == kDenseWaves || Q == kDenseWaves, "narrower tiles only without an exchange");
+    // group-sum records: (N / 16 NW tiles) x (8 / Q groups) x NW waves fit in
+    // slot_ws_bytes's (N / 128) x 8 x 8 whenever NW Q >= 8 or there is no exchange
+    static_assert(NW == kDenseWaves || Q == kDenseWaves || NW * Q >= kDenseWaves, "group sums exceed the workspace");
     const int64_t ntc = cdiv(N, NW * 16);
     unsigned *counters = (unsigned *)ws;
     float *part = (float *)((char *)ws + kSlotCounterBytes);
@@ -295,9 +298,18 @@ static void launch_slots_mt(const void *x, const void *w, void *y, void *ws, int
             launch_slots_t<S, MT, 8, EPI, PK>(x, w, y, ws, M, N, K, st);
         return;
     }
-    if (ntc * 2 >= cu) launch_slots_t<S, MT, 4, EPI, PK>(x, w, y, ws, M, N, K, st);
-    else if (ntc * 4 >= cu) launch_slots_t<S, MT, 2, EPI, PK>(x, w, y, ws, M, N, K, st);
-    else launch_slots_t<S, MT, 1, EPI, PK>(x, w, y, ws, M, N, K, st);
+    if (ntc * 2 >= cu) {
+        launch_slots_t<S, MT, 4, EPI, PK>(x, w, y, ws, M, N, K, st);
+    } else if constexpr (MT == 4) {
+        // Few column tiles: 64-column tiles with pairs of slots (four groups)
+        // give as many workgroups as 128-column tiles with single slots, but
+        // half the group sums to exchange and a quarter for the last arriver
+        // to read.
+        launch_slots_t<S, MT, 2, EPI, PK, 4>(x, w, y, ws, M, N, K, st);
+    } else {
+        if (ntc * 4 >= cu) launch_slots_t<S, MT, 2, EPI, PK>(x, w, y, ws, M, N, K, st);
+        else launch_slots_t<S, MT, 1, EPI, PK>(x, w, y, ws, M, N, K, st);
+    }
 }
 
 template <typename S, int EPI = EPI_Y>
