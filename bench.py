@@ -325,8 +325,10 @@ def split_overhead(torch, bi, model, B, per_shape):
 
 
 def qmatmul_decode(torch, bi, dev):
-    """Quantized matmul at a decode shape (M = 8, K = N = 4096 and the MLP
-    shape 28672 x 4096): weight stream in GB/s against the HBM peak."""
+    """Quantized matmul at decode shapes (M = 8; K = N = 4096 and the MLP
+    shape 28672 x 4096), cold: the seeded quantized weight plus bit-permuted
+    copies (distinct bytes, same sizes) rotated so no launch finds its weight
+    in a cache.  Transposed [N, K/8] weights and the tile-packed layout."""
     from invariant_reductions_amd import inputs
     res = {}
     for mode, gs in (("affine", 64), ("nvfp4", 16)):
@@ -334,17 +336,24 @@ def qmatmul_decode(torch, bi, dev):
             M = 8
             x, wq, s, b = inputs.qmatmul_case(M, K, N, mode, gs, True, seed=0)
             xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
-            wqd = torch.from_numpy(wq.view(np.int32)).to(dev)
+            wq0 = torch.from_numpy(wq.view(np.int32)).to(dev)
             sd = torch.from_numpy(s if s.dtype == np.uint8 else s.view(np.int16)).to(dev)
             bd = None if b is None else torch.from_numpy(b.view(np.int16)).to(dev)
-            y = torch.empty(M, N, dtype=torch.float16, device=dev)
+            copies = max(2, int(0.8e9 // (N * K // 2)))
+            wqs = [wq0] + [torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff) for r in range(1, copies)]
             qm = bi.AFFINE if mode == "affine" else bi.NVFP4
-            t = _time(torch, lambda: bi.qmatmul(xd, wqd, sd, bd, N, K, qm, gs, True, out=y))
+            wps = [bi.pack_qweights(w, sd, bd, N, K, qm, gs) for w in wqs]
+            y = torch.empty(M, N, dtype=torch.float16, device=dev)
             wbytes = N * K // 2 + N * (K // gs) * (4 if mode == "affine" else 1)
             tot = wbytes + 2 * M * K + 2 * M * N
-            gbs = tot / (t * 1e-3) / 1e9
-            res[f"{mode}-gs{gs} {M}x{N}x{K}"] = {"us": round(t * 1e3, 1), "gbs": round(gbs, 1),
-                                                  "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            for tag, fn in (("transposed", lambda r: bi.qmatmul(xd, wqs[r], sd, bd, N, K, qm, gs, True, out=y)),
+                            ("packed", lambda r: bi.qmatmul(xd, wps[r], None, None, N, K, qm, gs, out=y, packed=True))):
+                it = iter(range(1 << 30))
+                t = _time(torch, lambda: fn(next(it) % copies), reps=4 * copies)
+                gbs = tot / (t * 1e-3) / 1e9
+                res[f"{mode}-gs{gs} {M}x{N}x{K} {tag}"] = {"us": round(t * 1e3, 1), "gbs": round(gbs, 1),
+                                                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            del wqs, wps
     return res
 
 

@@ -176,10 +176,14 @@ bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, int64_t M, 
  * shape invariance", Problem (quantized matmul selected different paths by M).
  *   x      : [M,K] binary16.
  *   y      : [M,N] binary16.
- *   Transposed weights (w_transposed != 0), quantized along K:
+ *   w_layout BI_W_TRANSPOSED (1), quantized along K:
  *     wq [N, K/8] uint32, scales [N, K/gs], biases [N, K/gs].
- *   Natural weights (w_transposed == 0), quantized along N:
+ *   w_layout BI_W_NATURAL (0), quantized along N:
  *     wq [K, N/8] uint32, scales [K, N/gs], biases [K, N/gs].
+ *   w_layout BI_W_PACKED (2): wq is the buffer bi_pack_qweights wrote from
+ *     transposed weights (K % 128 == 0, 16-byte aligned; BI_ERR_SHAPE /
+ *     BI_ERR_ALIGN otherwise); scales and biases are not read (may be NULL).
+ *     Same bits as the transposed call.  Other w_layout values: BI_ERR_SHAPE.
  *   Packing: eight 4-bit codes per little-endian uint32; the element with the
  *   lowest index along the quantized axis is in bits 0..3.
  *   qmode BI_AFFINE: gs in {32, 64, 128}; binary16 scales s and biases b;
@@ -193,8 +197,30 @@ bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, int64_t M, 
  * ------------------------------------------------------------------------ */
 bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, const void *biases,
                      void *y, int64_t M, int64_t N, int64_t K,
-                     int32_t qmode, int32_t bits, int32_t group_size, int32_t w_transposed,
+                     int32_t qmode, int32_t bits, int32_t group_size, int32_t w_layout,
                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Tile-packed quantized weights (BI_W_PACKED for bi_qmatmul), a one-time
+ * layout change of transposed weights that bi_qmatmul multiplies with the
+ * same tree, hence the same bits.  Same source as bi_qmatmul (the layout is
+ * free).  For row group r (rows 16r .. 16r + 15; rows >= N are zeros) and K
+ * block b (128 codes): 1 KiB of codes in MFMA lane order, lane l = 16g + c
+ * holding the four words of row 16r + c for k in [128b + 32g, +32), at byte
+ * ((r * (K/128) + b) * 64 + l) * 16; after all code chunks, one constants
+ * chunk per (r, b) in the same order -- affine: 16 rows x (128/gs) entries
+ * scale | bias << 16 (4 bytes each, row-major); nvfp4: 16 rows x 8 scale
+ * bytes.  A wave reads its codes for a block as one 1 KiB piece and its
+ * constants as one small piece.
+ *   bi_packed_qweight_bytes: ceil(N/16) * (K/128) * (1024 + constants chunk),
+ *     or 0 for an illegal mode / group size / bits or K % 128 != 0.
+ *   bi_pack_qweights: transposed wq, scales, biases (as bi_qmatmul) -> wqp of
+ *     that many bytes; wq and wqp 16-byte aligned.  Stream-ordered; errors as
+ *     bi_qmatmul plus BI_ERR_SHAPE when K % 128 != 0.
+ * ------------------------------------------------------------------------ */
+size_t bi_packed_qweight_bytes(int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size);
+bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, const void *biases, void *wqp, int64_t N,
+                           int64_t K, int32_t qmode, int32_t bits, int32_t group_size, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * RMSNorm   y = (x * inv) * w,   inv = 1 / sqrt(sum_i x_i^2 / H + eps)

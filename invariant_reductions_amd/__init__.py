@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "BIError", "library_path", "lib", "build_info",
     "matmul", "matmul_ws", "matmul_workspace", "matmul_swiglu", "matmul_swiglu_workspace", "interleave_gate_up",
-    "PackedWeight", "pack_weights",
+    "PackedWeight", "pack_weights", "pack_qweights",
     "qmatmul", "rmsnorm", "add_rmsnorm", "sdpa", "sdpa_workspace_bytes",
     "matmul_split", "rmsnorm_split",
     "embed", "rope_kv_write", "silu_mul", "add", "argmax",
@@ -73,6 +73,7 @@ def lib():
             "bi_matmul_ws": [P, P, P, I64, I64, I64, I32, I32, P, SZ, P],
             "bi_matmul_swiglu": [P, P, P, I64, I64, I64, I32, I32, P, SZ, P],
             "bi_pack_weights": [P, P, I64, I64, I32, P],
+            "bi_pack_qweights": [P, P, P, P, I64, I64, I32, I32, I32, P],
             "bi_rmsnorm_split": [P, P, P, I64, I64, F, I32, I32, P, SZ, P],
         }
         for name, args in sig.items():
@@ -81,6 +82,8 @@ def lib():
             fn.restype = ctypes.c_int32
         L.bi_sdpa_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
         L.bi_sdpa_workspace_bytes.restype = SZ
+        L.bi_packed_qweight_bytes.argtypes = [I64, I64, I32, I32, I32]
+        L.bi_packed_qweight_bytes.restype = SZ
         L.bi_packed_weight_bytes.argtypes = [I64, I64, I32]
         L.bi_packed_weight_bytes.restype = SZ
         L.bi_matmul_swiglu_workspace_bytes.argtypes = [I64, I64, I64, I32]
@@ -266,8 +269,9 @@ def matmul_split(x, w, splits: int, transposed: bool = True, out=None, ws=None, 
 
 
 def qmatmul(x, wq, scales, biases, N: int, K: int, qmode: int, group_size: int, transposed: bool = True,
-            out=None, stream=None):
-    """y = x @ dequantize(W)^T; x float16 [M,K]; wq int32 (uint32 bit patterns)."""
+            out=None, stream=None, packed: bool = False):
+    """y = x @ dequantize(W)^T; x float16 [M,K]; wq int32 (uint32 bit patterns),
+    or (packed=True) the buffer of pack_qweights, with scales/biases None."""
     _dev(x, wq, scales, biases, out)
     if x.dtype != torch.float16:
         raise ValueError("qmatmul: x must be float16")
@@ -275,9 +279,22 @@ def qmatmul(x, wq, scales, biases, N: int, K: int, qmode: int, group_size: int, 
     if x.shape[1] != K:
         raise ValueError("qmatmul: x shape")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    layout = W_PACKED if packed else (W_TRANSPOSED if transposed else W_NATURAL)
     _check(lib().bi_qmatmul(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, qmode, 4,
-                            group_size, int(transposed), _stream(stream)), "bi_qmatmul")
+                            group_size, layout, _stream(stream)), "bi_qmatmul")
     return y
+
+
+def pack_qweights(wq, scales, biases, N: int, K: int, qmode: int, group_size: int, stream=None) -> torch.Tensor:
+    """Transposed quantized weights -> the packed buffer qmatmul(packed=True) reads."""
+    _dev(wq, scales, biases)
+    nbytes = lib().bi_packed_qweight_bytes(N, K, qmode, 4, group_size)
+    if nbytes == 0:
+        raise ValueError("pack_qweights: needs K % 128 == 0 and a legal mode / group size")
+    wqp = torch.empty(nbytes // 4, dtype=torch.int32, device=wq.device)
+    _check(lib().bi_pack_qweights(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(wqp), N, K, qmode, 4, group_size,
+                                  _stream(stream)), "bi_pack_qweights")
+    return wqp
 
 
 def rmsnorm(x, w, eps: float = 1e-6, out=None, stream=None):

@@ -70,6 +70,36 @@ __device__ inline QGroup<QM> load_group(const void *scales, const uint16_t *bias
     return g;
 }
 
+// Tile-packed quantized weight (w_layout 2; transposed source, K % 128 == 0).
+// Codes: for row group r (rows 16r .. 16r + 15; rows >= N zero) and K block b,
+// 1 KiB in MFMA lane order -- lane l = 16g + c holds the four words of row
+// 16r + c covering k in [128b + 32g, +32) -- at byte ((r * nb + b) * 64 + l) * 16.
+// Group constants follow all code chunks, one chunk of qconst_chunk_bytes per
+// (r, b) in the same order: affine, 16 rows x (128 / gs) groups of
+// (scale16 | bias16 << 16); nvfp4, 16 rows x 8 scale bytes.  A wave's codes
+// for one block are one 1 KiB piece and its constants one piece of at most
+// 256 bytes, where [N, K/8] + [N, K/gs] spread them over 16 rows each.  The
+// lane that reads a code is the lane that multiplies it, as before.
+__host__ __device__ constexpr int qconst_chunk_bytes(int qm, int gs) { return qm == BI_AFFINE ? 16 * (128 / gs) * 4 : 16 * 8; }
+
+// Lane (g, c)'s words and group constants of row group rg, block b (packed).
+template <int QM, int GS>
+__device__ inline void qload_packed_raw(const uint32_t *wqp, int64_t nrg, int64_t nb, int64_t rg, int64_t b, int lane,
+                                        uint4 &words, uint32_t &sc, uint32_t &bs)
+{
+    const int g = lane >> 4, c = lane & 15;
+    words = *reinterpret_cast<const uint4 *>(wqp + ((rg * nb + b) * 64 + lane) * 4);
+    const uint8_t *cb = reinterpret_cast<const uint8_t *>(wqp) + nrg * nb * 1024 + (rg * nb + b) * qconst_chunk_bytes(QM, GS);
+    if constexpr (QM == BI_AFFINE) {
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(cb + (c * (128 / GS) + (32 * g) / GS) * 4);
+        sc = v & 0xffffu;
+        bs = v >> 16;
+    } else {
+        sc = *reinterpret_cast<const uint16_t *>(cb + c * 8 + 2 * g);   // groups 2g (low byte) and 2g + 1
+        bs = 0;
+    }
+}
+
 template <int QM>
 __device__ inline uint16_t deq1(uint32_t q, const QGroup<QM> &g)
 {
@@ -176,7 +206,7 @@ __device__ inline void qload_nat(uint4 *dst, const uint32_t *wq, const void *sca
     }
 }
 
-template <int QM, int GS, bool TRANS, bool WVEC, int MT, int NS>
+template <int QM, int GS, bool TRANS, bool WVEC, int MT, int NS, bool PK>
 __global__ __launch_bounds__(kQWaves * kWave)
 void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wq, const void *__restrict__ scales,
                     const uint16_t *__restrict__ biases, uint16_t *__restrict__ y, int64_t M, int64_t N, int64_t K)
@@ -219,8 +249,30 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         uint4 A[MT][4], Bf[NS][4];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            if (TRANS) qload_trans<QM, GS, WVEC>(Bf[j], wq, scales, biases, wn[j], wok[j], K, kbase);
-            else qload_nat<QM, GS>(Bf[j], wq, scales, biases, wn[j], wok[j], N, K, kbase);
+            if constexpr (PK) {
+                // K % 128 == 0: every block is whole; padding columns multiply zeros
+                const int64_t nrg = (N + 15) / 16, rg0 = n0 / 16 + j;
+                uint4 wv;
+                uint32_t sc, bs;
+                qload_packed_raw<QM, GS>(wq, nrg, nblocks, rg0 < nrg ? rg0 : nrg - 1, b, lane, wv, sc, bs);
+                const uint32_t wa[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    QGroup<QM> gr;
+                    if constexpr (QM == BI_AFFINE) {
+                        gr.s = F16::widen((uint16_t)sc);
+                        gr.b = F16::widen((uint16_t)bs);
+                    } else {
+                        gr.s = e4m3_to_f32((sc >> (s < 2 ? 0 : 8)) & 0xffu);
+                        gr.b = 0.0f;
+                    }
+                    Bf[j][s] = deq_word<QM>(wa[s], gr);
+                }
+            } else if (TRANS) {
+                qload_trans<QM, GS, WVEC>(Bf[j], wq, scales, biases, wn[j], wok[j], K, kbase);
+            } else {
+                qload_nat<QM, GS>(Bf[j], wq, scales, biases, wn[j], wok[j], N, K, kbase);
+            }
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i)
@@ -264,7 +316,7 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
 // exactly qmatmul_kernel's: block b of K belongs to wave b mod 8, lane group
 // g supplies [32g, 32g + 32) of the block as four steps, wave partials are
 // added in wave order.
-template <int QM, int GS, int NS, int D>
+template <int QM, int GS, int NS, int D, bool PK>
 __global__ __launch_bounds__(kQWaves * kWave, 2)
 void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wq,
                            const void *__restrict__ scales, const uint16_t *__restrict__ biases,
@@ -291,20 +343,31 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
         const int64_t kb = (int64_t)(wave + pj * P) * kQBlock + g * 32;     // this lane's first code
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            int64_t n = t * TC + j * 16 + c;
-            n = n < N ? n : N - 1;                                          // padding columns read a real row
-            Wd[j] = *reinterpret_cast<const uint4 *>(wq + n * words + kb / 8);
-            const int64_t gi = n * groups + kb / GS;
-            if (QM == BI_AFFINE) {
-                Sd[j] = ((const uint16_t *)scales)[gi];
-                Bd[j] = biases[gi];
+            if constexpr (PK) {
+                const int64_t nrg = (N + 15) / 16, rg = t * NS + j;
+                qload_packed_raw<QM, GS>(wq, nrg, nb, rg < nrg ? rg : nrg - 1, wave + pj * P, lane, Wd[j], Sd[j], Bd[j]);
             } else {
-                Sd[j] = ((const uint16_t *)scales)[gi / 2];                 // the lane's two group bytes
-                Bd[j] = 0;
+                int64_t n = t * TC + j * 16 + c;
+                n = n < N ? n : N - 1;                                      // padding columns read a real row
+                Wd[j] = *reinterpret_cast<const uint4 *>(wq + n * words + kb / 8);
+                const int64_t gi = n * groups + kb / GS;
+                if (QM == BI_AFFINE) {
+                    Sd[j] = ((const uint16_t *)scales)[gi];
+                    Bd[j] = biases[gi];
+                } else {
+                    Sd[j] = ((const uint16_t *)scales)[gi / 2];             // the lane's two group bytes
+                    Bd[j] = 0;
+                }
             }
         }
+        // rows >= M (MFMA padding) load nothing: their products are never stored
+        if (c < M) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) Xd[s] = *reinterpret_cast<const uint4 *>(xr + (kb - g * 32) + s * 8);
+            for (int s = 0; s < 4; ++s) Xd[s] = *reinterpret_cast<const uint4 *>(xr + (kb - g * 32) + s * 8);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xd[s] = make_uint4(0, 0, 0, 0);
+        }
         if (pj + 1 < nmine) {
             ++pj;
         } else if (pu + 1 < mytiles) {
@@ -381,86 +444,166 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
     }
 }
 
-template <int QM, int GS, int NS>
+template <int QM, int GS, int NS, bool PK>
 static void launch_q_stream_t(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                               int64_t N, int64_t K, hipStream_t st)
 {
     const int64_t ntn = cdiv(N, NS * 16);
     const int64_t grid = std::min<int64_t>(ntn, (int64_t)device_cu_count() * 2);
-    hipLaunchKernelGGL((qmatmul_stream_kernel<QM, GS, NS, 3>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
+    hipLaunchKernelGGL((qmatmul_stream_kernel<QM, GS, NS, 3, PK>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
                        (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, M, N, K, (int)ntn);
 }
 
-template <int QM, int GS>
+template <int QM, int GS, bool PK>
 static bool try_launch_q_stream(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                                 int64_t N, int64_t K, hipStream_t st)
 {
     if (M > 16 || K % kQBlock != 0 || !host_aligned16(x) || !host_aligned16(wq) || cdiv(N, 16) > (1ll << 30))
         return false;
-    if (N >= 8192) launch_q_stream_t<QM, GS, 2>(x, wq, s, b, y, M, N, K, st);
-    else launch_q_stream_t<QM, GS, 1>(x, wq, s, b, y, M, N, K, st);
+    if (N >= 8192) launch_q_stream_t<QM, GS, 2, PK>(x, wq, s, b, y, M, N, K, st);
+    else launch_q_stream_t<QM, GS, 1, PK>(x, wq, s, b, y, M, N, K, st);
     return true;
 }
 
-template <int QM, int GS, bool TRANS, bool WVEC, int MT>
+template <int QM, int GS, bool TRANS, bool WVEC, int MT, bool PK>
 static void launch_q_t(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                        int64_t N, int64_t K, hipStream_t st)
 {
     dim3 grid((unsigned)cdiv(N, 16), (unsigned)cdiv(M, MT * 16));
-    hipLaunchKernelGGL((qmatmul_kernel<QM, GS, TRANS, WVEC, MT, 1>), grid, dim3(kQWaves * kWave), 0, st,
+    hipLaunchKernelGGL((qmatmul_kernel<QM, GS, TRANS, WVEC, MT, 1, PK>), grid, dim3(kQWaves * kWave), 0, st,
                        (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, M, N, K);
 }
 
-template <int QM, int GS, bool TRANS, bool WVEC>
+template <int QM, int GS, bool TRANS, bool WVEC, bool PK = false>
 static void launch_q_mt(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                         int64_t N, int64_t K, hipStream_t st)
 {
     const int64_t mt = cdiv(M, 16);
-    if (mt <= 1) launch_q_t<QM, GS, TRANS, WVEC, 1>(x, wq, s, b, y, M, N, K, st);
-    else if (mt <= 2) launch_q_t<QM, GS, TRANS, WVEC, 2>(x, wq, s, b, y, M, N, K, st);
-    else launch_q_t<QM, GS, TRANS, WVEC, 4>(x, wq, s, b, y, M, N, K, st);
+    if (mt <= 1) launch_q_t<QM, GS, TRANS, WVEC, 1, PK>(x, wq, s, b, y, M, N, K, st);
+    else if (mt <= 2) launch_q_t<QM, GS, TRANS, WVEC, 2, PK>(x, wq, s, b, y, M, N, K, st);
+    else launch_q_t<QM, GS, TRANS, WVEC, 4, PK>(x, wq, s, b, y, M, N, K, st);
 }
 
 template <int QM, int GS>
 static void launch_q(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M, int64_t N,
-                     int64_t K, bool trans, hipStream_t st)
+                     int64_t K, int layout, hipStream_t st)
 {
-    if (!trans) launch_q_mt<QM, GS, false, false>(x, wq, s, b, y, M, N, K, st);
-    else if (try_launch_q_stream<QM, GS>(x, wq, s, b, y, M, N, K, st)) return;
-    else if (K % 32 == 0 && host_aligned16(wq)) launch_q_mt<QM, GS, true, true>(x, wq, s, b, y, M, N, K, st);
-    else launch_q_mt<QM, GS, true, false>(x, wq, s, b, y, M, N, K, st);
+    if (layout == 2) {                              // packed: K % 128 == 0, wq 16-byte aligned (checked)
+        if (!try_launch_q_stream<QM, GS, true>(x, wq, s, b, y, M, N, K, st))
+            launch_q_mt<QM, GS, true, true, true>(x, wq, s, b, y, M, N, K, st);
+    } else if (layout == 0) {
+        launch_q_mt<QM, GS, false, false>(x, wq, s, b, y, M, N, K, st);
+    } else if (try_launch_q_stream<QM, GS, false>(x, wq, s, b, y, M, N, K, st)) {
+        return;
+    } else if (K % 32 == 0 && host_aligned16(wq)) {
+        launch_q_mt<QM, GS, true, true>(x, wq, s, b, y, M, N, K, st);
+    } else {
+        launch_q_mt<QM, GS, true, false>(x, wq, s, b, y, M, N, K, st);
+    }
+}
+
+// [N, K/8] codes + [N, K/gs] constants -> the packed layout; one thread per
+// 16-byte code chunk, then one per constant entry.
+template <int QM, int GS>
+__global__ void pack_q_kernel(const uint32_t *__restrict__ wq, const void *__restrict__ scales,
+                              const uint16_t *__restrict__ biases, uint32_t *__restrict__ wqp, int64_t N, int64_t K)
+{
+    const int64_t nb = K / kQBlock, nrg = (N + 15) / 16, words = K / 8, groups = K / GS;
+    constexpr int GPB = QM == BI_AFFINE ? 128 / GS : 8;          // constant entries per row per block
+    const int64_t ncode = nrg * nb * 64, nconst = nrg * nb * 16 * GPB;
+    uint8_t *cbase = reinterpret_cast<uint8_t *>(wqp) + nrg * nb * 1024;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ncode + nconst;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < ncode) {
+            const int lane = (int)(i & 63);
+            const int64_t rb = i >> 6, b = rb % nb, rg = rb / nb;
+            const int64_t row = rg * 16 + (lane & 15);
+            const uint4 v = row < N ? *reinterpret_cast<const uint4 *>(wq + row * words + b * 16 + (lane >> 4) * 4)
+                                    : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(wqp + i * 4) = v;
+        } else {
+            const int64_t e = i - ncode, q = e % GPB, cr = e / GPB, c = cr % 16, rb = cr / 16;
+            const int64_t b = rb % nb, rg = rb / nb, row = rg * 16 + c;
+            const int64_t gi = row * groups + b * GPB + q;
+            if constexpr (QM == BI_AFFINE) {
+                const uint32_t v = row < N ? (uint32_t)((const uint16_t *)scales)[gi] | ((uint32_t)biases[gi] << 16) : 0u;
+                *reinterpret_cast<uint32_t *>(cbase + e * 4) = v;
+            } else {
+                cbase[e] = row < N ? ((const uint8_t *)scales)[gi] : (uint8_t)0;
+            }
+        }
+    }
 }
 
 }  // namespace bi
 
 using namespace bi;
 
+static bi_status check_qmode(int32_t qmode, int32_t bits, int32_t group_size)
+{
+    if (bits != 4) return BI_ERR_GROUP;
+    if (qmode == BI_AFFINE) return (group_size == 32 || group_size == 64 || group_size == 128) ? BI_OK : BI_ERR_GROUP;
+    if (qmode == BI_NVFP4) return group_size == 16 ? BI_OK : BI_ERR_GROUP;
+    return BI_ERR_GROUP;
+}
+
 extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, const void *biases, void *y,
                                 int64_t M, int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size,
-                                int32_t w_transposed, hipStream_t stream)
+                                int32_t w_layout, hipStream_t stream)
 {
-    if (!x || !wq || !scales || !y) return BI_ERR_NULL;
+    const bool packed = w_layout == 2;
+    if (!x || !wq || !y || (!scales && !packed)) return BI_ERR_NULL;
     if (M < 1 || N < 1 || K < 1 || M > (1ll << 31) || N > (1ll << 31) || K > (1ll << 31)) return BI_ERR_SHAPE;
-    if (bits != 4) return BI_ERR_GROUP;
-    if (qmode == BI_AFFINE) {
-        if (group_size != 32 && group_size != 64 && group_size != 128) return BI_ERR_GROUP;
-        if (!biases) return BI_ERR_NULL;
-    } else if (qmode == BI_NVFP4) {
-        if (group_size != 16) return BI_ERR_GROUP;
-        if (biases) return BI_ERR_GROUP;
-    } else {
-        return BI_ERR_GROUP;
+    if (w_layout < 0 || w_layout > 2) return BI_ERR_SHAPE;
+    const bi_status qs = check_qmode(qmode, bits, group_size);
+    if (qs != BI_OK) return qs;
+    if (!packed) {
+        if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
+        if (qmode == BI_NVFP4 && biases) return BI_ERR_GROUP;
     }
-    const int64_t qdim = w_transposed ? K : N;
+    const int64_t qdim = w_layout ? K : N;
     if (qdim % group_size) return BI_ERR_GROUP;
-    if ((((uintptr_t)x | (uintptr_t)y) & 1u) || ((uintptr_t)wq & 3u) || ((uintptr_t)scales & 1u) ||
-        ((uintptr_t)biases & 1u))
+    if (packed && K % kQBlock) return BI_ERR_SHAPE;
+    if ((((uintptr_t)x | (uintptr_t)y) & 1u) || ((uintptr_t)wq & (packed ? 15u : 3u)) ||
+        (!packed && (((uintptr_t)scales & 1u) || ((uintptr_t)biases & 1u))))
         return BI_ERR_ALIGN;
     (void)hipGetLastError();
-    const bool t = w_transposed != 0;
-    if (qmode == BI_NVFP4) launch_q<BI_NVFP4, 16>(x, wq, scales, biases, y, M, N, K, t, stream);
-    else if (group_size == 32) launch_q<BI_AFFINE, 32>(x, wq, scales, biases, y, M, N, K, t, stream);
-    else if (group_size == 64) launch_q<BI_AFFINE, 64>(x, wq, scales, biases, y, M, N, K, t, stream);
-    else launch_q<BI_AFFINE, 128>(x, wq, scales, biases, y, M, N, K, t, stream);
+    if (qmode == BI_NVFP4) launch_q<BI_NVFP4, 16>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
+    else if (group_size == 32) launch_q<BI_AFFINE, 32>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
+    else if (group_size == 64) launch_q<BI_AFFINE, 64>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
+    else launch_q<BI_AFFINE, 128>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
+    return launch_status();
+}
+
+extern "C" size_t bi_packed_qweight_bytes(int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size)
+{
+    if (N < 1 || K < 1 || K % kQBlock || N > (1ll << 31) || K > (1ll << 31) || check_qmode(qmode, bits, group_size) != BI_OK)
+        return 0;
+    const size_t chunks = (size_t)cdiv(N, 16) * (size_t)(K / kQBlock);
+    return chunks * (1024 + (size_t)qconst_chunk_bytes(qmode, group_size));
+}
+
+extern "C" bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, const void *biases, void *wqp, int64_t N,
+                                      int64_t K, int32_t qmode, int32_t bits, int32_t group_size, hipStream_t stream)
+{
+    if (!wq || !scales || !wqp) return BI_ERR_NULL;
+    const bi_status qs = check_qmode(qmode, bits, group_size);
+    if (qs != BI_OK) return qs;
+    if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
+    if (qmode == BI_NVFP4 && biases) return BI_ERR_GROUP;
+    if (bi_packed_qweight_bytes(N, K, qmode, bits, group_size) == 0) return BI_ERR_SHAPE;
+    if (!host_aligned16(wq) || !host_aligned16(wqp) || ((uintptr_t)scales & 1u) || ((uintptr_t)biases & 1u))
+        return BI_ERR_ALIGN;
+    (void)hipGetLastError();
+    const int64_t nrg = cdiv(N, 16), nb = K / kQBlock;
+    const int64_t n = nrg * nb * 64 + nrg * nb * 16 * (qmode == BI_AFFINE ? 128 / group_size : 8);
+    const dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), block(256);
+    const uint32_t *w = wq;
+    const uint16_t *bz = (const uint16_t *)biases;
+    uint32_t *o = (uint32_t *)wqp;
+    if (qmode == BI_NVFP4) hipLaunchKernelGGL((pack_q_kernel<BI_NVFP4, 16>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    else if (group_size == 32) hipLaunchKernelGGL((pack_q_kernel<BI_AFFINE, 32>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    else if (group_size == 64) hipLaunchKernelGGL((pack_q_kernel<BI_AFFINE, 64>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    else hipLaunchKernelGGL((pack_q_kernel<BI_AFFINE, 128>), grid, block, 0, stream, w, scales, bz, o, N, K);
     return launch_status();
 }

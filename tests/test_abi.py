@@ -181,6 +181,23 @@ def test_packed_weight_validation():
     assert L.bi_matmul_swiglu(A, A, A, 64, 64, 128, 0, 0, A, 1 << 30, None) == UNSUP
 
 
+def test_packed_qweight_validation():
+    L = bi.lib()
+    assert L.bi_packed_qweight_bytes(20, 256, 0, 4, 64) == 2 * 2 * (1024 + 16 * 2 * 4)
+    assert L.bi_packed_qweight_bytes(16, 128, 1, 4, 16) == 1024 + 128
+    assert L.bi_packed_qweight_bytes(16, 192, 0, 4, 64) == 0           # K % 128
+    assert L.bi_packed_qweight_bytes(16, 128, 0, 4, 16) == 0           # affine gs 16
+    assert L.bi_pack_qweights(A, A, None, A, 16, 128, 0, 4, 64, None) == NULL    # affine needs biases
+    assert L.bi_pack_qweights(A, A, A, A, 16, 128, 1, 4, 16, None) == GROUP      # nvfp4 takes none
+    assert L.bi_pack_qweights(A, A, A, A, 16, 192, 0, 4, 64, None) == SHAPE
+    assert L.bi_pack_qweights(A, A, A, P(0x10010 + 4), 16, 128, 0, 4, 64, None) == ALIGN
+    # packed qmatmul: constants are inside the buffer (scales/biases may be NULL)
+    assert L.bi_qmatmul(A, A, None, None, A, 4, 16, 192, 0, 4, 64, 2, None) == SHAPE   # K % 128
+    assert L.bi_qmatmul(A, P(0x10010 + 4), None, None, A, 4, 16, 128, 0, 4, 64, 2, None) == ALIGN
+    assert L.bi_qmatmul(A, A, A, A, A, 4, 16, 128, 0, 4, 64, 3, None) == SHAPE         # no such layout
+    assert L.bi_qmatmul(A, A, None, None, A, 4, 16, 128, 0, 4, 64, 1, None) == NULL    # transposed needs scales
+
+
 def test_add_rmsnorm_validation():
     L = bi.lib()
     assert L.bi_add_rmsnorm(A, None, A, A, A, 4, 4096, 1e-6, 0, None) == NULL

@@ -158,3 +158,67 @@ def test_illegal_shapes_are_rejected_not_corrupted():
     wqd, sd, bd = dev_q(wq, s, b)
     with pytest.raises(bi.BIError):
         bi.qmatmul(to_dev(x, "f16"), wqd, sd, bd, 100, 128, bi.AFFINE, 32, False)   # natural N % gs != 0
+
+
+# ---------------------------------------------------------------------------
+# tile-packed quantized weights: the transposed call's bits on every path
+# ---------------------------------------------------------------------------
+
+def pack_dev(wq, s, b, N, K, mode, gs):
+    wqd, sd, bd = dev_q(wq, s, b)
+    return bi.pack_qweights(wqd, sd, bd, N, K, QM[mode], gs)
+
+
+@pytest.mark.parametrize("mode,gs", MODES)
+@pytest.mark.parametrize("N,K", [(512, 4096), (100, 384), (1000, 1024)])
+def test_packed_bits_equal_transposed(mode, gs, N, K):
+    """Streaming kernel (M <= 16) and tiled kernel (M > 16), ragged N."""
+    x, wq, s, b = inputs.qmatmul_case(40, K, N, mode, gs, True, seed=N + K)
+    wqd, sd, bd = dev_q(wq, s, b)
+    wqp = pack_dev(wq, s, b, N, K, mode, gs)
+    xd = to_dev(x, "f16")
+    for M in (1, 3, 8, 16, 17, 40):
+        xm = xd[:M].contiguous()
+        yt = to_np(bi.qmatmul(xm, wqd, sd, bd, N, K, QM[mode], gs, True))
+        yp = to_np(bi.qmatmul(xm, wqp, None, None, N, K, QM[mode], gs, packed=True))
+        assert bits_equal(yp, yt), f"{mode}{gs} {N}x{K} M={M}"
+
+
+def test_packed_oracle_parity_and_bounded_stores():
+    M, K, N = 8, 512, 200
+    for mode, gs in MODES:
+        x, wq, s, b = inputs.qmatmul_case(M, K, N, mode, gs, True, seed=5)
+        wqp = pack_dev(wq, s, b, N, K, mode, gs)
+        yg = Guarded((M, N), torch.float16, poison=0x3C)
+        bi.qmatmul(to_dev(x, "f16"), wqp, None, None, N, K, QM[mode], gs, packed=True, out=yg.view)
+        torch.cuda.synchronize()
+        assert yg.canaries_intact()
+        assert_parity(to_np(yg.view), ref(x, wq, s, b, M, N, K, mode, gs, True), "f16", f"{mode}{gs}")
+
+
+def test_packed_layout_matches_definition():
+    """Codes and constants land where the header's formula puts them."""
+    N, K, gs = 20, 256, 64
+    x, wq, s, b = inputs.qmatmul_case(1, K, N, "affine", gs, True, seed=9)
+    got = pack_dev(wq, s, b, N, K, "affine", gs).cpu().numpy().view(np.uint32)
+    nb, nrg = K // 128, (N + 15) // 16
+    wqu = np.ascontiguousarray(wq).view(np.uint32).reshape(N, K // 8)
+    su = np.ascontiguousarray(s).view(np.uint16).reshape(N, K // gs).astype(np.uint32)
+    bu = np.ascontiguousarray(b).view(np.uint16).reshape(N, K // gs).astype(np.uint32)
+    codes = np.zeros(nrg * nb * 256, np.uint32)
+    consts = np.zeros(nrg * nb * 16 * (128 // gs), np.uint32)
+    for r in range(nrg):
+        for blk in range(nb):
+            for lane in range(64):
+                row = 16 * r + (lane & 15)
+                if row < N:
+                    o = ((r * nb + blk) * 64 + lane) * 4
+                    codes[o:o + 4] = wqu[row, blk * 16 + (lane >> 4) * 4:blk * 16 + (lane >> 4) * 4 + 4]
+            for c in range(16):
+                for q in range(128 // gs):
+                    row = 16 * r + c
+                    if row < N:
+                        gi = blk * (128 // gs) + q
+                        consts[((r * nb + blk) * 16 + c) * (128 // gs) + q] = su[row, gi] | (bu[row, gi] << 16)
+    assert np.array_equal(got[:codes.size], codes)
+    assert np.array_equal(got[codes.size:], consts)
