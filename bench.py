@@ -132,8 +132,9 @@ def main():
     for li in range(cfg["n_layers"]):
         kh = inputs.normal(rng, (B, cap, Hkv, D))
         vh = inputs.normal(rng, (B, cap, Hkv, D))
-        model.kc[li].copy_(torch.from_numpy(kh.view(np.int16)).view(torch.bfloat16))
-        model.vc[li].copy_(torch.from_numpy(vh.view(np.int16)).view(torch.bfloat16))
+        # the decoder keeps its caches head-major [B, Hkv, cap, D]
+        model.kc[li].copy_(torch.from_numpy(kh.view(np.int16)).view(torch.bfloat16).transpose(1, 2))
+        model.vc[li].copy_(torch.from_numpy(vh.view(np.int16)).view(torch.bfloat16).transpose(1, 2))
         kc_host.append(kh)
         vc_host.append(vh)
     ids0 = rng.integers(0, cfg["vocab"], size=B).astype(np.int32)
@@ -324,11 +325,30 @@ def split_overhead(torch, bi, model, B, per_shape):
     return res
 
 
+def _time_kernel(torch, bi, fn, reps):
+    """Mean kernel execution time (ms) of the single bi launch `fn` makes: a
+    start/stop event pair recorded by the launch itself (bi_time_next_launch),
+    so host-side launch overhead is not counted."""
+    L = bi.lib()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for s_, t_ in ev:
+        s_.record()
+        t_.record()
+    fn(0)
+    torch.cuda.synchronize()
+    for i, (s_, t_) in enumerate(ev):
+        L.bi_time_next_launch(ctypes.c_void_p(s_.cuda_event), ctypes.c_void_p(t_.cuda_event))
+        fn(i)
+    torch.cuda.synchronize()
+    return float(np.mean([s_.elapsed_time(t_) for s_, t_ in ev]))
+
+
 def qmatmul_decode(torch, bi, dev):
     """Quantized matmul at decode shapes (M = 8; K = N = 4096 and the MLP
     shape 28672 x 4096), cold: the seeded quantized weight plus bit-permuted
     copies (distinct bytes, same sizes) rotated so no launch finds its weight
-    in a cache.  Transposed [N, K/8] weights and the tile-packed layout."""
+    in a cache.  Transposed [N, K/8] weights and the tile-packed layout;
+    kernel execution time (launch-recorded events)."""
     from invariant_reductions_amd import inputs
     res = {}
     for mode, gs in (("affine", 64), ("nvfp4", 16)):
@@ -348,8 +368,7 @@ def qmatmul_decode(torch, bi, dev):
             tot = wbytes + 2 * M * K + 2 * M * N
             for tag, fn in (("transposed", lambda r: bi.qmatmul(xd, wqs[r], sd, bd, N, K, qm, gs, True, out=y)),
                             ("packed", lambda r: bi.qmatmul(xd, wps[r], None, None, N, K, qm, gs, out=y, packed=True))):
-                it = iter(range(1 << 30))
-                t = _time(torch, lambda: fn(next(it) % copies), reps=4 * copies)
+                t = _time_kernel(torch, bi, lambda i: fn(i % copies), reps=4 * copies)
                 gbs = tot / (t * 1e-3) / 1e9
                 res[f"{mode}-gs{gs} {M}x{N}x{K} {tag}"] = {"us": round(t * 1e3, 1), "gbs": round(gbs, 1),
                                                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}

@@ -253,8 +253,11 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
  * short causal block); "Batch-invariant kernels ...", Case 6 (fixed split
  * size with a varying number of splits; cache updated before the kernel).
  *   q, o   : [B, Q, Hq, D] of `dtype` (BI_BF16 or BI_F16).
- *   k, v   : [B, Lcap, Hkv, D] of `dtype` (the KV cache, already holding the
- *            keys/values of the Q new tokens).
+ *   k, v   : the KV cache of `dtype`, already holding the keys/values of the
+ *            Q new tokens: [B, Lcap, Hkv, D] (kv_layout 0) or head-major
+ *            [B, Hkv, Lcap, D] (kv_layout 1, where the keys of one head are
+ *            contiguous and a chunk is one piece of memory); same bits in
+ *            both.  Other kv_layout values: BI_ERR_SHAPE.
  *   kv_len : device int32 [B]; sequence b holds kv_len[b] valid positions.
  *            Query j of sequence b sits at position p = kv_len[b] - Q + j.
  *            With causal != 0 it attends to keys 0..p, else to 0..kv_len[b]-1.
@@ -275,7 +278,7 @@ size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int32_t
 bi_status bi_sdpa(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len,
                   int64_t max_kv_len, int64_t B, int64_t Q, int64_t Lcap,
                   int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t causal,
-                  int32_t dtype, void *ws, size_t ws_bytes, hipStream_t stream);
+                  int32_t dtype, int32_t kv_layout, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Pointwise glue of a Llama-style decoder.  Pointwise ops are batch-invariant
@@ -293,15 +296,17 @@ bi_status bi_embed(const int32_t *ids, const void *table, void *out, int64_t T, 
  *   qkv   : [B*Q, (Hq + 2*Hkv) * D]; row (b, j) holds q | k | v of token j of
  *           sequence b.
  *   q_out : [B*Q, Hq*D]   rotated q.
- *   kc, vc: [B, Lcap, Hkv, D] caches; token j of sequence b is written at
- *           position kv_len[b] - Q + j (rotated k, and v unchanged).
+ *   kc, vc: caches, [B, Lcap, Hkv, D] (kv_layout 0) or [B, Hkv, Lcap, D]
+ *           (kv_layout 1), as bi_sdpa reads them; token j of sequence b is
+ *           written at position kv_len[b] - Q + j (rotated k, v unchanged).
  *   cos_t, sin_t: fp32 [max_pos, D/2] tables; positions must be < max_pos.
  *   out_i = x_i * c_i - x_{i+D/2} * s_i;  out_{i+D/2} = x_{i+D/2} * c_i + x_i * s_i
  *   (each product and the difference/sum rounded separately in fp32). */
 bi_status bi_rope_kv_write(const void *qkv, void *q_out, void *kc, void *vc,
                            const int32_t *kv_len, const float *cos_t, const float *sin_t,
                            int64_t B, int64_t Q, int64_t Lcap, int32_t Hq, int32_t Hkv,
-                           int32_t D, int64_t max_pos, hipStream_t stream);
+                           int32_t D, int64_t max_pos, int32_t kv_layout,
+                           hipStream_t stream);
 
 /* out[r, i] = silu(gu[r, i]) * gu[r, F + i],  silu(g) = g / (1 + exp(-g));
  * gu [rows, 2F], out [rows, F]. */

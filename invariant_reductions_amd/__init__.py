@@ -63,9 +63,9 @@ def lib():
             "bi_qmatmul": [P, P, P, P, P, I64, I64, I64, I32, I32, I32, I32, P],
             "bi_rmsnorm": [P, P, P, I64, I64, F, I32, P],
             "bi_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I32, P],
-            "bi_sdpa": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, P, SZ, P],
+            "bi_sdpa": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, I32, P, SZ, P],
             "bi_embed": [P, P, P, I64, I64, I64, P],
-            "bi_rope_kv_write": [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, I64, P],
+            "bi_rope_kv_write": [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, I64, I32, P],
             "bi_silu_mul": [P, P, I64, I64, P],
             "bi_add": [P, P, P, I64, P],
             "bi_argmax": [P, P, I64, I64, P],
@@ -332,11 +332,16 @@ def sdpa_workspace_bytes(B: int, Q: int, max_kv_len: int, Hq: int, D: int) -> in
     return lib().bi_sdpa_workspace_bytes(B, Q, max_kv_len, Hq, D)
 
 
-def sdpa(q, k, v, kv_len, max_kv_len: int, scale: float, causal: bool = True, out=None, ws=None, stream=None):
-    """q [B,Q,Hq,D]; k, v [B,Lcap,Hkv,D]; kv_len int32 [B] on the device."""
+def sdpa(q, k, v, kv_len, max_kv_len: int, scale: float, causal: bool = True, out=None, ws=None, stream=None,
+         head_major: bool = False):
+    """q [B,Q,Hq,D]; k, v [B,Lcap,Hkv,D] (or [B,Hkv,Lcap,D] with head_major);
+    kv_len int32 [B] on the device."""
     _dev(q, k, v, kv_len, out, ws)
     B, Q, Hq, D = q.shape
-    _, Lcap, Hkv, _ = k.shape
+    if head_major:
+        _, Hkv, Lcap, _ = k.shape
+    else:
+        _, Lcap, Hkv, _ = k.shape
     if kv_len.dtype != torch.int32:
         raise ValueError("kv_len must be int32")
     o = out if out is not None else torch.empty_like(q)
@@ -344,8 +349,8 @@ def sdpa(q, k, v, kv_len, max_kv_len: int, scale: float, causal: bool = True, ou
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check(lib().bi_sdpa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_len), max_kv_len, B, Q, Lcap, Hq, Hkv, D,
-                         scale, int(causal), _dt(q), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "bi_sdpa")
+                         scale, int(causal), _dt(q), int(head_major), _ptr(ws), ws.numel() * ws.element_size(),
+                         _stream(stream)), "bi_sdpa")
     return o
 
 
@@ -362,12 +367,14 @@ def embed(ids, table, out=None, stream=None):
     return y
 
 
-def rope_kv_write(qkv, q_out, kc, vc, kv_len, cos_t, sin_t, B: int, Q: int, Hq: int, Hkv: int, D: int, stream=None):
+def rope_kv_write(qkv, q_out, kc, vc, kv_len, cos_t, sin_t, B: int, Q: int, Hq: int, Hkv: int, D: int, stream=None,
+                  head_major: bool = False):
+    """Caches [B,Lcap,Hkv,D], or [B,Hkv,Lcap,D] with head_major."""
     _dev(qkv, q_out, kc, vc, kv_len, cos_t, sin_t)
-    Lcap = kc.shape[1]
+    Lcap = kc.shape[2] if head_major else kc.shape[1]
     _check(lib().bi_rope_kv_write(_ptr(qkv), _ptr(q_out), _ptr(kc), _ptr(vc), _ptr(kv_len), _ptr(cos_t),
-                                  _ptr(sin_t), B, Q, Lcap, Hq, Hkv, D, cos_t.shape[0], _stream(stream)),
-           "bi_rope_kv_write")
+                                  _ptr(sin_t), B, Q, Lcap, Hq, Hkv, D, cos_t.shape[0], int(head_major),
+                                  _stream(stream)), "bi_rope_kv_write")
 
 
 def silu_mul(gu, out=None, stream=None):

@@ -30,8 +30,12 @@ __global__ void rope_kv_kernel(const uint16_t *__restrict__ qkv, uint16_t *__res
                                uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
                                const int32_t *__restrict__ kv_len, const float *__restrict__ cos_t,
                                const float *__restrict__ sin_t, int64_t B, int64_t Q, int64_t Lcap,
-                               int Hq, int Hkv, int D, int64_t max_pos)
+                               int Hq, int Hkv, int D, int64_t max_pos, int head_major)
 {
+    // cache element offset of (sequence b, position pos, KV head h)
+    auto cache_at = [&](int64_t b, int64_t pos, int64_t h) {
+        return (head_major ? (b * Hkv + h) * Lcap + pos : (b * Lcap + pos) * Hkv + h) * (int64_t)D;
+    };
     typedef uint16_t vec_t __attribute__((ext_vector_type(G)));
     const int half = D / 2, ng = half / G;
     const int heads = Hq + 2 * Hkv;
@@ -48,7 +52,7 @@ __global__ void rope_kv_kernel(const uint16_t *__restrict__ qkv, uint16_t *__res
         const vec_t lo_in = *reinterpret_cast<const vec_t *>(src + i);
         const vec_t hi_in = *reinterpret_cast<const vec_t *>(src + i + half);
         if (hh >= Hq + Hkv) {                                      // v: copied to the cache unchanged
-            uint16_t *dst = vc + ((b * Lcap + pos) * Hkv + (hh - Hq - Hkv)) * (int64_t)D;
+            uint16_t *dst = vc + cache_at(b, pos, hh - Hq - Hkv);
             *reinterpret_cast<vec_t *>(dst + i) = lo_in;
             *reinterpret_cast<vec_t *>(dst + i + half) = hi_in;
             continue;
@@ -62,7 +66,7 @@ __global__ void rope_kv_kernel(const uint16_t *__restrict__ qkv, uint16_t *__res
             hi_out[e] = BF16::narrow(bb * c + a * sn);
         }
         uint16_t *dst = hh < Hq ? q_out + tok * (int64_t)Hq * D + (int64_t)hh * D
-                                : kc + ((b * Lcap + pos) * Hkv + (hh - Hq)) * (int64_t)D;
+                                : kc + cache_at(b, pos, hh - Hq);
         *reinterpret_cast<vec_t *>(dst + i) = lo_out;
         *reinterpret_cast<vec_t *>(dst + i + half) = hi_out;
     }
@@ -213,10 +217,12 @@ extern "C" bi_status bi_embed(const int32_t *ids, const void *table, void *out, 
 
 extern "C" bi_status bi_rope_kv_write(const void *qkv, void *q_out, void *kc, void *vc, const int32_t *kv_len,
                                       const float *cos_t, const float *sin_t, int64_t B, int64_t Q, int64_t Lcap,
-                                      int32_t Hq, int32_t Hkv, int32_t D, int64_t max_pos, hipStream_t stream)
+                                      int32_t Hq, int32_t Hkv, int32_t D, int64_t max_pos, int32_t kv_layout,
+                                      hipStream_t stream)
 {
     if (!qkv || !q_out || !kc || !vc || !kv_len || !cos_t || !sin_t) return BI_ERR_NULL;
     if (B < 1 || Q < 1 || Lcap < 1 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 || max_pos < 1) return BI_ERR_SHAPE;
+    if (kv_layout != 0 && kv_layout != 1) return BI_ERR_SHAPE;
     if (!host_aligned16(qkv) || !host_aligned16(q_out) || !host_aligned16(kc) || !host_aligned16(vc) ||
         !host_aligned16(cos_t) || !host_aligned16(sin_t) || ((uintptr_t)kv_len & 3u))
         return BI_ERR_ALIGN;
@@ -227,11 +233,11 @@ extern "C" bi_status bi_rope_kv_write(const void *qkv, void *q_out, void *kc, vo
     if (vec)
         hipLaunchKernelGGL(rope_kv_kernel<8>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)qkv,
                            (uint16_t *)q_out, (uint16_t *)kc, (uint16_t *)vc, kv_len, cos_t, sin_t, B, Q, Lcap,
-                           Hq, Hkv, D, max_pos);
+                           Hq, Hkv, D, max_pos, kv_layout);
     else
         hipLaunchKernelGGL(rope_kv_kernel<1>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)qkv,
                            (uint16_t *)q_out, (uint16_t *)kc, (uint16_t *)vc, kv_len, cos_t, sin_t, B, Q, Lcap,
-                           Hq, Hkv, D, max_pos);
+                           Hq, Hkv, D, max_pos, kv_layout);
     return launch_status();
 }
 

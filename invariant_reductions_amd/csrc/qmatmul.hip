@@ -450,7 +450,7 @@ static void launch_q_stream_t(const void *x, const uint32_t *wq, const void *s, 
 {
     const int64_t ntn = cdiv(N, NS * 16);
     const int64_t grid = std::min<int64_t>(ntn, (int64_t)device_cu_count() * 2);
-    hipLaunchKernelGGL((qmatmul_stream_kernel<QM, GS, NS, 3, PK>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
+    launch_kernel((qmatmul_stream_kernel<QM, GS, NS, 3, PK>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
                        (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, M, N, K, (int)ntn);
 }
 
@@ -470,7 +470,7 @@ static void launch_q_t(const void *x, const uint32_t *wq, const void *s, const v
                        int64_t N, int64_t K, hipStream_t st)
 {
     dim3 grid((unsigned)cdiv(N, 16), (unsigned)cdiv(M, MT * 16));
-    hipLaunchKernelGGL((qmatmul_kernel<QM, GS, TRANS, WVEC, MT, 1, PK>), grid, dim3(kQWaves * kWave), 0, st,
+    launch_kernel((qmatmul_kernel<QM, GS, TRANS, WVEC, MT, 1, PK>), grid, dim3(kQWaves * kWave), 0, st,
                        (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, M, N, K);
 }
 

@@ -61,6 +61,7 @@ struct AttnShape {
     int Hq, Hkv, G;
     float scale;
     int causal;
+    int64_t ks, hs;       // cache strides (elements) between consecutive keys and between KV heads
 };
 
 __device__ inline int64_t row_last_key(int64_t kvlen, int64_t Q, int64_t j, int causal)
@@ -157,9 +158,9 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
     // item's first key, which always exists (the item has work), and the
     // value is then replaced by zero.  Bases are wave-uniform; per-lane
     // offsets are 32-bit.
-    const int rs = sh.Hkv * kHeadDim;                                    // elements between keys
+    const int rs = (int)sh.ks;                                           // elements between keys
     auto item_base = [&](const uint16_t *p, const Item &it) {
-        return p + ((int64_t)it.b * sh.Lcap + (int64_t)it.c * kChunk) * rs + (int64_t)it.hk * kHeadDim;
+        return p + (int64_t)it.b * sh.Lcap * sh.Hkv * kHeadDim + (int64_t)it.c * kChunk * rs + (int64_t)it.hk * sh.hs;
     };
     // keys of this wave that exist
     auto wave_valid = [&](const Item &it) { return min(max(it.kvlen - (it.c * kChunk + wave * kKeysPerWave), 0), kKeysPerWave); };
@@ -431,15 +432,18 @@ extern "C" size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Q, int64_t max_kv_l
 
 extern "C" bi_status bi_sdpa(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len,
                              int64_t max_kv_len, int64_t B, int64_t Q, int64_t Lcap, int32_t Hq, int32_t Hkv,
-                             int32_t D, float scale, int32_t causal, int32_t dtype, void *ws, size_t ws_bytes,
-                             hipStream_t stream)
+                             int32_t D, float scale, int32_t causal, int32_t dtype, int32_t kv_layout, void *ws,
+                             size_t ws_bytes, hipStream_t stream)
 {
     bi_status s = check_attn(q, k, v, o, kv_len, max_kv_len, B, Q, Lcap, Hq, Hkv, D, dtype);
     if (s != BI_OK) return s;
+    if (kv_layout != 0 && kv_layout != 1) return BI_ERR_SHAPE;
     if (!ws) return BI_ERR_WORKSPACE;
     if (!host_aligned16(ws)) return BI_ERR_ALIGN;
     if (ws_bytes < bi_sdpa_workspace_bytes(B, Q, max_kv_len, Hq, D)) return BI_ERR_WORKSPACE;
-    AttnShape sh{B, Q, Lcap, cdiv(max_kv_len, kChunk), max_kv_len, Hq, Hkv, Hq / Hkv, scale, causal ? 1 : 0};
+    // kv_layout 0: [B, Lcap, Hkv, D]; 1: [B, Hkv, Lcap, D] (head-major)
+    const int64_t ks = kv_layout ? (int64_t)D : (int64_t)Hkv * D, hs = kv_layout ? Lcap * D : (int64_t)D;
+    AttnShape sh{B, Q, Lcap, cdiv(max_kv_len, kChunk), max_kv_len, Hq, Hkv, Hq / Hkv, scale, causal ? 1 : 0, ks, hs};
     (void)hipGetLastError();
     if (dtype == BI_BF16) launch_attn<BF16>(q, k, v, o, kv_len, (float *)ws, sh, kChunk, stream);
     else launch_attn<F16>(q, k, v, o, kv_len, (float *)ws, sh, kChunk, stream);

@@ -66,8 +66,9 @@ class Decoder:
         T = max_batch * max_q
         bf = torch.bfloat16
         z = lambda *s: torch.zeros(*s, dtype=bf, device=d)
-        self.kc = [z(max_batch, max_len, self.Hkv, self.D) for _ in range(self.L)]
-        self.vc = [z(max_batch, max_len, self.Hkv, self.D) for _ in range(self.L)]
+        # head-major KV caches [B, Hkv, Lcap, D]: each head's keys contiguous
+        self.kc = [z(max_batch, self.Hkv, max_len, self.D) for _ in range(self.L)]
+        self.vc = [z(max_batch, self.Hkv, max_len, self.D) for _ in range(self.L)]
         self.x, self.h, self.t1 = z(T, self.H), z(T, self.H), z(T, self.H)
         self.qkv, self.q, self.o = z(T, self.qkvn), z(T, self.qn), z(T, self.qn)
         self.a = z(T, self.F)
@@ -104,8 +105,8 @@ class Decoder:
         for li, Lw in enumerate(self.layers):
             matmul_ws(h, Lw["wqkv"], self.mws, out=qkv)
             kc, vc = self.kc[li][:B], self.vc[li][:B]
-            rope_kv_write(qkv, q, kc, vc, kv, self.cos_t, self.sin_t, B, Q, self.Hq, self.Hkv, self.D)
-            sdpa(q.view(B, Q, self.Hq, self.D), kc, vc, kv, max_kv, scale, True,
+            rope_kv_write(qkv, q, kc, vc, kv, self.cos_t, self.sin_t, B, Q, self.Hq, self.Hkv, self.D, head_major=True)
+            sdpa(q.view(B, Q, self.Hq, self.D), kc, vc, kv, max_kv, scale, True, head_major=True,
                  out=o.view(B, Q, self.Hq, self.D), ws=self.ws)
             matmul_ws(o, Lw["wo"], self.mws, out=t1)
             add_rmsnorm(x, t1, Lw["mlp_norm"], self.eps, x_out=x, out=h)
@@ -144,14 +145,14 @@ class Decoder:
         steps.append(("rmsnorm", L.bi_rmsnorm, (p(x), p(self.layers[0]["attn_norm"]), p(h), T, H, eps, 0, st)))
         for li, Lw in enumerate(self.layers):
             kc, vc = self.kc[li], self.vc[li]
-            Lcap = kc.shape[1]
+            Lcap = kc.shape[2]
             nxt = self.layers[li + 1]["attn_norm"] if li + 1 < self.L else self.final_norm
             steps += [
                 mm(h, Lw["wqkv"], qkv, self.qkvn, H),
                 ("rope_kv", L.bi_rope_kv_write, (p(qkv), p(q), p(kc), p(vc), p(kv), p(self.cos_t), p(self.sin_t),
-                                                 B, Q, Lcap, self.Hq, self.Hkv, self.D, self.cos_t.shape[0], st)),
+                                                 B, Q, Lcap, self.Hq, self.Hkv, self.D, self.cos_t.shape[0], 1, st)),
                 ("sdpa", L.bi_sdpa, (p(q), p(kc), p(vc), p(o), p(kv), max_kv, B, Q, Lcap, self.Hq, self.Hkv,
-                                     self.D, scale, 1, 0, p(self.ws), self.ws.numel(), st)),
+                                     self.D, scale, 1, 0, 1, p(self.ws), self.ws.numel(), st)),
                 mm(o, Lw["wo"], t1, H, qn),
                 ("add_rmsnorm", L.bi_add_rmsnorm, (p(x), p(t1), p(x), p(Lw["mlp_norm"]), p(h), T, H, eps, 0, st)),
                 ("matmul_swiglu", L.bi_matmul_swiglu, (p(h), p(Lw["wgu_il"].data), p(a), T, self.F, H, 0, W_PACKED,

@@ -97,8 +97,10 @@ def test_sdpa_validation_and_workspace_size():
                  scale=0.088, causal=1, dt=0, ws=A, wsb=10 ** 9)
         a.update(kw)
         return L.bi_sdpa(a["q"], a["k"], a["v"], a["o"], a["kv"], a["maxkv"], a["B"], a["Q"], a["Lcap"],
-                         a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["dt"], a["ws"], a["wsb"], None)
+                         a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["dt"], a.get("lay", 0), a["ws"],
+                         a["wsb"], None)
     assert call(kv=None) == NULL
+    assert call(lay=2) == SHAPE                     # no such cache layout
     assert call(Hkv=5) == SHAPE
     assert call(maxkv=4) == SHAPE                   # max_kv_len < Q
     assert call(maxkv=4096) == SHAPE                # max_kv_len > Lcap
@@ -219,7 +221,8 @@ def test_glue_validation():
     L = bi.lib()
     assert L.bi_embed(None, A, A, 1, 10, 64, None) == NULL
     assert L.bi_embed(A, A, A, 1, 10, 12, None) == SHAPE
-    assert L.bi_rope_kv_write(A, A, A, A, A, A, A, 1, 1, 16, 4, 2, 7, 16, None) == SHAPE
+    assert L.bi_rope_kv_write(A, A, A, A, A, A, A, 1, 1, 16, 4, 2, 7, 16, 0, None) == SHAPE
+    assert L.bi_rope_kv_write(A, A, A, A, A, A, A, 1, 1, 16, 4, 2, 8, 16, 2, None) == SHAPE   # no such layout
     assert L.bi_silu_mul(A, None, 4, 8, None) == NULL
     assert L.bi_add(A, A, ODD, 8, None) == ALIGN
     assert L.bi_argmax(A, A, 0, 8, None) == SHAPE

@@ -51,6 +51,14 @@ def test_rope_and_kv_write_bit_exact(D):
     for b in range(B):
         untouched[b, kv_len[b] - Q:kv_len[b]] = False
     assert np.all(kcn[untouched] == 0) and np.all(vcn[untouched] == 0)
+    # the head-major cache holds the same rows at [b, h, p]
+    kh = torch.zeros((B, Hkv, Lcap, D), dtype=torch.bfloat16, device=dev())
+    vh = torch.zeros((B, Hkv, Lcap, D), dtype=torch.bfloat16, device=dev())
+    bi.rope_kv_write(to_dev(qkv, "bf16"), qo, kh, vh, torch.from_numpy(kv_len).to(dev()),
+                     torch.from_numpy(cos_t).to(dev()), torch.from_numpy(sin_t).to(dev()), B, Q, Hq, Hkv, D,
+                     head_major=True)
+    assert bits_equal(to_np(kh.transpose(1, 2).contiguous()), kcn)
+    assert bits_equal(to_np(vh.transpose(1, 2).contiguous()), vcn)
 
 
 @pytest.mark.parametrize("F", [1000, 1001, 14336])

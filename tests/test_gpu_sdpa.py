@@ -143,3 +143,18 @@ def test_run_to_run_determinism():
     first = bi.sdpa(qd, kd, vd, kvd, 4100, SCALE, True)
     for _ in range(30):
         assert torch.equal(bi.sdpa(qd, kd, vd, kvd, 4100, SCALE, True).view(torch.int16), first.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,Q,Lk", [(1, 8, 1028), (3, 1, 783), (2, 5, 300), (4, 1, 4100)])
+def test_head_major_cache_same_bits(B, Q, Lk):
+    """The head-major cache [B, Hkv, Lcap, D] gives the [B, Lcap, Hkv, D]
+    cache's bits (only the strides change), ragged lengths included."""
+    q, k, v = inputs.sdpa_case(B, Q, Lk, HQ, HKV, D, seed=B + Q)
+    kv_len = np.array([Lk - 3 * b for b in range(B)], np.int32)
+    kd, vd = to_dev(k, "bf16"), to_dev(v, "bf16")
+    kvd = torch.tensor(kv_len, device=dev())
+    qd = to_dev(q, "bf16")
+    std = to_np(bi.sdpa(qd, kd, vd, kvd, Lk, SCALE, True))
+    hm = to_np(bi.sdpa(qd, kd.transpose(1, 2).contiguous(), vd.transpose(1, 2).contiguous(), kvd, Lk, SCALE, True,
+                       head_major=True))
+    assert bits_equal(hm, std)
