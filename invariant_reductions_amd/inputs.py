@@ -191,6 +191,26 @@ def quantize_nvfp4(w: np.ndarray):
     return pack_nibbles(codes), sb
 
 
+def quantize_mxfp4(w: np.ndarray):
+    """mxfp4-style quantization along the last axis of fp32 `w` [rows, cols]:
+    per 32 elements one e8m0 scale 2^(e - 127) with e = floor(log2(amax)) - 2
+    + 127 (the largest e2m1 magnitude is 6 = 1.5 * 2^2), clamped to [0, 254];
+    codes = e2m1(w / scale), saturating; a zero group gets e = 0 and zero
+    codes.  Returns (wq uint32 [rows, cols/8], scale bytes uint8 [rows, cols/32])."""
+    w = np.asarray(w, np.float32)
+    rows, cols = w.shape
+    assert cols % 32 == 0
+    g = w.reshape(rows, cols // 32, 32).astype(np.float64)
+    amax = np.abs(g).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2 + 127, 0)
+    e = np.clip(e, 0, 254).astype(np.int64)
+    scale = np.ldexp(1.0, (e - 127).astype(np.int32))
+    r = np.where(amax[:, :, None] > 0, g / scale[:, :, None], 0.0)
+    codes = encode_e2m1(r).reshape(rows, cols)
+    return pack_nibbles(codes), e.astype(np.uint8)
+
+
 def qmatmul_case(M: int, K: int, N: int, qmode: str, group_size: int, transposed: bool = True,
                  seed: int = 0):
     """W ~ N(0,1) drawn first, quantized along the matrix's stored minor axis
@@ -203,6 +223,10 @@ def qmatmul_case(M: int, K: int, N: int, qmode: str, group_size: int, transposed
     elif qmode == "nvfp4":
         assert group_size == 16
         wq, s = quantize_nvfp4(w)
+        b = None
+    elif qmode == "mxfp4":
+        assert group_size == 32
+        wq, s = quantize_mxfp4(w)
         b = None
     else:
         raise ValueError(qmode)

@@ -15,7 +15,9 @@ Sources followed (cited by page title and section):
     (the three reductions and their batch-invariant strategies).
   * "Fix fp quantized matmul corruption when the quantized dim is not a
     multiple of 32" -- Problem (the reference is x @ dequantize(W).T) and Fix
-    (group sizes; nvfp4 = e2m1 codes with one e4m3 scale per 16).
+    (group sizes; nvfp4 = e2m1 codes with one e4m3 scale per 16; mxfp4 has
+    group size 32 -- its e2m1 codes and power-of-two e8m0 scale follow the
+    OCP microscaling format, which the pages name but do not define).
   * "Fix/speculative shape invariance" -- Problem and Changes (dense matmul,
     quantized matmul and two-pass SDPA must reduce a token the same way alone
     or inside a verification block).
@@ -33,7 +35,7 @@ _SRC = os.path.join(_HERE, "bi_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 BF16, F16, F32 = 0, 1, 2
-AFFINE, NVFP4 = 0, 1
+AFFINE, NVFP4, MXFP4 = 0, 1, 2
 _DT = {"bf16": BF16, "f16": F16, "f32": F32}
 
 
@@ -66,6 +68,7 @@ def lib():
         L.bo_f32_to_f16.argtypes = [ctypes.c_float]; L.bo_f32_to_f16.restype = ctypes.c_uint16
         L.bo_e2m1_to_f32.argtypes = [ctypes.c_uint8]; L.bo_e2m1_to_f32.restype = ctypes.c_float
         L.bo_e4m3_to_f32.argtypes = [ctypes.c_uint8]; L.bo_e4m3_to_f32.restype = ctypes.c_float
+        L.bo_e8m0_to_f32.argtypes = [ctypes.c_uint8]; L.bo_e8m0_to_f32.restype = ctypes.c_float
         L.bo_round.argtypes = [P, P, I64, I32]
         L.bo_widen.argtypes = [P, P, I64, I32]
         L.bo_fold_seq_f32.argtypes = [P, I64]; L.bo_fold_seq_f32.restype = ctypes.c_float
@@ -129,6 +132,10 @@ def e2m1_value(code: int) -> float:
 
 def e4m3_value(code: int) -> float:
     return lib().bo_e4m3_to_f32(code)
+
+
+def e8m0_value(code: int) -> float:
+    return lib().bo_e8m0_to_f32(code)
 
 
 # --- folds (Case 1 / Case 2) -------------------------------------------------

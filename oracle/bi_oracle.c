@@ -34,7 +34,7 @@
 #endif
 
 enum { BO_BF16 = 0, BO_F16 = 1, BO_F32 = 2 };
-enum { BO_AFFINE = 0, BO_NVFP4 = 1 };
+enum { BO_AFFINE = 0, BO_NVFP4 = 1, BO_MXFP4 = 2 };
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                           */
@@ -116,6 +116,14 @@ float bo_e4m3_to_f32(uint8_t c)
     else if (e == 0) v = ldexpf((float)m / 8.0f, -6);
     else v = ldexpf(1.0f + (float)m / 8.0f, (int)e - 7);
     return s ? -v : v;
+}
+
+/* OCP MX e8m0 scale: an unsigned biased exponent, value 2^(e - 127); the
+ * byte 0xFF is NaN.  2^-127 is an fp32 subnormal, so every value is exact. */
+float bo_e8m0_to_f32(uint8_t e)
+{
+    if (e == 0xffu) return bits_to_f32(0x7fc00000u);
+    return ldexpf(1.0f, (int)e - 127);
 }
 
 static float load_elem(const void *p, int64_t i, int dtype)
@@ -273,6 +281,10 @@ int bo_matmul(const void *x, const void *w, float *y, int64_t M, int64_t N, int6
  *   binary16 (the activation type the weights are multiplied against).
  * NVFP4: w = e2m1(q) * e4m3(s), one scale byte per 16 elements; the product
  *   is exact in fp32 and exactly representable in binary16.
+ * MXFP4: w = e2m1(q) * e8m0(s), one scale byte per 32 elements; the product is
+ *   exact in fp32 (a power-of-two scaling of a 2-bit significand) and is then
+ *   rounded to binary16 (values beyond its range become +-inf, tiny ones
+ *   round to subnormals or zero).
  * Output: binary16 bits, same [rows, cols] layout as the stored matrix. */
 int bo_dequantize(const uint32_t *wq, const void *scales, const uint16_t *biases,
                   uint16_t *out, int64_t rows, int64_t cols, int qmode, int group_size)
@@ -283,6 +295,8 @@ int bo_dequantize(const uint32_t *wq, const void *scales, const uint16_t *biases
         if (!biases) return -1;
     } else if (qmode == BO_NVFP4) {
         if (group_size != 16) return -3;
+    } else if (qmode == BO_MXFP4) {
+        if (group_size != 32) return -3;
     } else {
         return -1;
     }
@@ -300,8 +314,10 @@ int bo_dequantize(const uint32_t *wq, const void *scales, const uint16_t *biases
                 float b = bo_f16_to_f32(biases[g]);
                 float sq = s * (float)q;
                 v = sq + b;
-            } else {
+            } else if (qmode == BO_NVFP4) {
                 v = bo_e2m1_to_f32((uint8_t)q) * bo_e4m3_to_f32(((const uint8_t *)scales)[g]);
+            } else {
+                v = bo_e2m1_to_f32((uint8_t)q) * bo_e8m0_to_f32(((const uint8_t *)scales)[g]);
             }
             out[r * cols + c] = bo_f32_to_f16(v);
         }

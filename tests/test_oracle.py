@@ -171,6 +171,21 @@ def test_e4m3_all_codes_vs_torch_and_spec():
             assert oracle.e4m3_value(int(k, 16)) == val
 
 
+def test_e8m0_all_codes_vs_torch_and_spec():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).float().numpy()
+    ours = np.array([oracle.e8m0_value(int(c)) for c in codes], np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 1
+    assert np.array_equal(ours[~nan], ref[~nan])
+    for k, val in golden("ocp_fp4_fp8_values.json")["e8m0"].items():
+        if k == "nan_codes":
+            for c in val:
+                assert np.isnan(oracle.e8m0_value(int(c, 16)))
+        else:
+            assert oracle.e8m0_value(int(k, 16)) == val
+
+
 # ---------------------------------------------------------------------------
 # dense matmul
 # ---------------------------------------------------------------------------
@@ -285,6 +300,43 @@ def test_nvfp4_scales_multiply_exactly():
     assert np.array_equal(deq.astype(np.float64), spec[None, :] * sval[:, None])
 
 
+def test_mxfp4_scales_multiply_then_round_to_binary16():
+    """Every (code, scale) pair: the dequantized value is the spec value times
+    2^(e-127) (exact in fp64) rounded once to binary16 by numpy -- overflow to
+    inf above the binary16 range, subnormals and zero below it."""
+    g = golden("ocp_fp4_fp8_values.json")
+    spec = np.array(g["e2m1_positive_codes_0_to_7"] + [-v for v in g["e2m1_positive_codes_0_to_7"]])
+    e = np.arange(255, dtype=np.uint8)
+    codes = np.tile(np.arange(16, dtype=np.uint32).repeat(2), (e.size, 1))   # 32 codes per row = 1 group
+    wq = inputs.pack_nibbles(codes)
+    deq = oracle.dequantize(wq, e[:, None].copy(), None, e.size, 32, oracle.MXFP4, 32)
+    want = (spec[codes] * np.ldexp(1.0, e.astype(np.int32) - 127)[:, None]).astype(np.float16)
+    assert np.array_equal(deq, want.view(np.uint16))
+
+
+def test_mxfp4_grid_values_round_trip_and_unit_scale_is_exact():
+    """Weights on the e2m1 grid times 2^k, group maximum 6 * 2^k, quantize to
+    scale 2^k and come back exactly; at scale 1 with integer x the product is
+    exact."""
+    g = golden("ocp_fp4_fp8_values.json")
+    spec = np.array(g["e2m1_positive_codes_0_to_7"] + [-v for v in g["e2m1_positive_codes_0_to_7"]])
+    rng = np.random.default_rng(6)
+    codes = rng.integers(0, 16, size=(16, 256))
+    codes[:, ::32] = 7
+    k = rng.integers(-8, 8, size=(16, 8))
+    w = (spec[codes] * np.repeat(2.0 ** k, 32, axis=1)).astype(np.float32)
+    wq, s = inputs.quantize_mxfp4(w)
+    assert np.array_equal(s.astype(np.int64), k + 127)
+    deq = inputs.from_storage(oracle.dequantize(wq, s, None, 16, 256, oracle.MXFP4, 32), "f16")
+    assert np.array_equal(deq, w)
+    M, K, N = 3, 256, 16
+    s1 = np.full((N, K // 32), 127, np.uint8)
+    x = inputs.integer_values(rng, (M, K), -8, 8, "f16")
+    exact = inputs.from_storage(x, "f16").astype(np.float64) @ spec[codes].T
+    y = oracle.qmatmul(x, wq, s1, None, M, N, K, oracle.MXFP4, 32, True)
+    assert np.array_equal(y.astype(np.float64), exact)
+
+
 @pytest.mark.parametrize("gs", [32, 64, 128])
 def test_affine_quantize_dequantize_error_bound(gs):
     rng = np.random.default_rng(9)
@@ -312,14 +364,14 @@ def test_nvfp4_grid_values_round_trip():
     assert np.array_equal(deq, w)
 
 
-@pytest.mark.parametrize("qmode,gs", [("affine", 32), ("affine", 128), ("nvfp4", 16)])
+@pytest.mark.parametrize("qmode,gs", [("affine", 32), ("affine", 128), ("nvfp4", 16), ("mxfp4", 32)])
 @pytest.mark.parametrize("transposed", [True, False])
 def test_qmatmul_tiny_brute_force(qmode, gs, transposed):
     """Tiny shapes, every output summed in fp64 from the dequantized weights:
     the oracle lies within the fp32 rounding bound."""
     M, K, N = 3, 256, 128
     x, wq, s, b = inputs.qmatmul_case(M, K, N, qmode, gs, transposed, seed=2)
-    qm = oracle.AFFINE if qmode == "affine" else oracle.NVFP4
+    qm = {"affine": oracle.AFFINE, "nvfp4": oracle.NVFP4, "mxfp4": oracle.MXFP4}[qmode]
     rows, cols = (N, K) if transposed else (K, N)
     deq = inputs.from_storage(oracle.dequantize(wq, s, b, rows, cols, qm, gs), "f16").astype(np.float64)
     wmat = deq if transposed else deq.T                                   # [N, K]
