@@ -351,7 +351,7 @@ def qmatmul_decode(torch, bi, dev):
     kernel execution time (launch-recorded events)."""
     from invariant_reductions_amd import inputs
     res = {}
-    for mode, gs in (("affine", 64), ("nvfp4", 16)):
+    for mode, gs in (("affine", 64), ("nvfp4", 16), ("mxfp4", 32)):
         for (N, K) in ((4096, 4096), (28672, 4096)):
             M = 8
             x, wq, s, b = inputs.qmatmul_case(M, K, N, mode, gs, True, seed=0)
@@ -361,7 +361,7 @@ def qmatmul_decode(torch, bi, dev):
             bd = None if b is None else torch.from_numpy(b.view(np.int16)).to(dev)
             copies = max(2, int(0.8e9 // (N * K // 2)))
             wqs = [wq0] + [torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff) for r in range(1, copies)]
-            qm = bi.AFFINE if mode == "affine" else bi.NVFP4
+            qm = {"affine": bi.AFFINE, "nvfp4": bi.NVFP4, "mxfp4": bi.MXFP4}[mode]
             wps = [bi.pack_qweights(w, sd, bd, N, K, qm, gs) for w in wqs]
             y = torch.empty(M, N, dtype=torch.float16, device=dev)
             wbytes = N * K // 2 + N * (K // gs) * (4 if mode == "affine" else 1)

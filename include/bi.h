@@ -71,7 +71,7 @@ typedef enum {
 typedef enum { BI_BF16 = 0, BI_F16 = 1, BI_F32 = 2 } bi_dtype;
 /* Weight layouts of the dense entry points (their w_layout argument). */
 typedef enum { BI_W_NATURAL = 0, BI_W_TRANSPOSED = 1, BI_W_PACKED = 2 } bi_wlayout;
-typedef enum { BI_AFFINE = 0, BI_NVFP4 = 1 } bi_qmode;
+typedef enum { BI_AFFINE = 0, BI_NVFP4 = 1, BI_MXFP4 = 2 } bi_qmode;
 
 /* ------------------------------------------------------------------------
  * Dense matmul   y[m,n] = sum_k x[m,k] * W[n,k]
@@ -191,6 +191,12 @@ bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, int64_t M, 
  *   qmode BI_NVFP4: gs == 16; codes are e2m1 (sign in bit 3), scales are one
  *     OCP e4m3fn byte per group; w = e2m1(q) * e4m3(s) (exact in binary16);
  *     biases must be NULL.
+ *   qmode BI_MXFP4: gs == 32; e2m1 codes, scales one OCP MX e8m0 byte per
+ *     group (2^(e - 127), 0xFF = NaN); w = binary16(e2m1(q) * 2^(e - 127)),
+ *     the exact fp32 product rounded once (RNE; beyond the binary16 range it
+ *     is +-inf); biases must be NULL.  (The pages name mxfp4 with group size
+ *     32 -- "Fix fp quantized matmul corruption ...", Fix -- and leave the
+ *     format to the OCP microscaling specification.)
  *   bits must be 4.  The quantized dimension must be a multiple of gs
  *   (BI_ERR_GROUP otherwise).  Any M >= 1 is legal, as is K % 32 == 16 at
  *   gs 16 and N % 32 != 0 -- tails are bounded on loads and stores.
@@ -209,8 +215,8 @@ bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, cons
  * holding the four words of row 16r + c for k in [128b + 32g, +32), at byte
  * ((r * (K/128) + b) * 64 + l) * 16; after all code chunks, one constants
  * chunk per (r, b) in the same order -- affine: 16 rows x (128/gs) entries
- * scale | bias << 16 (4 bytes each, row-major); nvfp4: 16 rows x 8 scale
- * bytes.  A wave reads its codes for a block as one 1 KiB piece and its
+ * scale | bias << 16 (4 bytes each, row-major); nvfp4 / mxfp4: 16 rows x
+ * (128/gs) scale bytes.  A wave reads its codes for a block as one 1 KiB piece and its
  * constants as one small piece.
  *   bi_packed_qweight_bytes: ceil(N/16) * (K/128) * (1024 + constants chunk),
  *     or 0 for an illegal mode / group size / bits or K % 128 != 0.

@@ -27,7 +27,7 @@ __all__ = [
 ]
 
 BF16, F16, F32 = 0, 1, 2
-AFFINE, NVFP4 = 0, 1
+AFFINE, NVFP4, MXFP4 = 0, 1, 2
 _TORCH_DT = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

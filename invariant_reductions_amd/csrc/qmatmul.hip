@@ -43,6 +43,13 @@ __device__ inline float e4m3_to_f32(uint32_t s)
     return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
 }
 
+// OCP MX e8m0 scale byte -> fp32 (exact): 2^(e - 127), 0xFF -> NaN.
+__device__ inline float e8m0_to_f32(uint32_t e)
+{
+    if (e == 0xffu) return __uint_as_float(0x7fc00000u);
+    return e == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);   // 2^-127 is subnormal
+}
+
 // e2m1 nibble -> fp32 (exact): magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6, sign in bit 3.
 __device__ inline float e2m1_to_f32(uint32_t c)
 {
@@ -54,18 +61,62 @@ __device__ inline float e2m1_to_f32(uint32_t c)
 template <int QM>
 struct QGroup {                      // per-group dequantization constants
     float s, b;
+    uint32_t m;                      // mxfp4: binary16 factors 2^k1 | 2^k2 << 16 (see mx_group)
 };
+
+
+// mxfp4 group of scale byte e (k = e - 127): s = 2^k in fp32 for the
+// element-wise path, and the binary16 pair (2^k1, 2^k2), k1 = clamp(k, -13,
+// 13), k2 = clamp(k - k1, -24, 15), for the packed path.  e2m1 * 2^k1 is
+// exact in binary16 (two significant bits, between 2^-14 and 49152), so the
+// second product is the only rounding: RNE(e2m1 * 2^k) whenever k1 + k2 = k,
+// i.e. for -37 <= k <= 28; below, every value rounds to +-0 either way, above
+// every nonzero value overflows to +-inf either way.  e = 0xFF: 2^k2 is NaN.
+__device__ inline QGroup<BI_MXFP4> mx_group(uint32_t e)
+{
+    QGroup<BI_MXFP4> g;
+    g.s = e8m0_to_f32(e);
+    g.b = 0.0f;
+    const int k = (int)e - 127;
+    const int k1 = k < -13 ? -13 : (k > 13 ? 13 : k);
+    const int k2r = k - k1, k2 = k2r < -24 ? -24 : (k2r > 15 ? 15 : k2r);
+    const uint32_t h1 = (uint32_t)(k1 + 15) << 10;
+    const uint32_t h2 = e == 0xffu ? 0x7e00u : (k2 >= -14 ? (uint32_t)(k2 + 15) << 10 : 1u << (k2 + 24));
+    g.m = h1 | (h2 << 16);
+    return g;
+}
 
 template <int QM>
 __device__ inline QGroup<QM> load_group(const void *scales, const uint16_t *biases, int64_t gi)
 {
     QGroup<QM> g;
-    if (QM == BI_AFFINE) {
+    if constexpr (QM == BI_AFFINE) {
         g.s = F16::widen(((const uint16_t *)scales)[gi]);
         g.b = F16::widen(biases[gi]);
-    } else {
+    } else if constexpr (QM == BI_NVFP4) {
         g.s = e4m3_to_f32(((const uint8_t *)scales)[gi]);
         g.b = 0.0f;
+    } else {
+        g = mx_group(((const uint8_t *)scales)[gi]);
+    }
+    return g;
+}
+
+// Constants of word s (of a lane's four) from the raw scale/bias a lane
+// loaded: affine binary16 scale and bias; nvfp4 the two e4m3 bytes of the
+// lane's two groups (words 0-1, 2-3); mxfp4 the one e8m0 byte.
+template <int QM>
+__device__ inline QGroup<QM> group_from_raw(uint32_t sc, uint32_t bs, int s)
+{
+    QGroup<QM> g;
+    if constexpr (QM == BI_AFFINE) {
+        g.s = F16::widen((uint16_t)sc);
+        g.b = F16::widen((uint16_t)bs);
+    } else if constexpr (QM == BI_NVFP4) {
+        g.s = e4m3_to_f32((sc >> (s < 2 ? 0 : 8)) & 0xffu);
+        g.b = 0.0f;
+    } else {
+        g = mx_group(sc & 0xffu);
     }
     return g;
 }
@@ -75,12 +126,12 @@ __device__ inline QGroup<QM> load_group(const void *scales, const uint16_t *bias
 // 1 KiB in MFMA lane order -- lane l = 16g + c holds the four words of row
 // 16r + c covering k in [128b + 32g, +32) -- at byte ((r * nb + b) * 64 + l) * 16.
 // Group constants follow all code chunks, one chunk of qconst_chunk_bytes per
-// (r, b) in the same order: affine, 16 rows x (128 / gs) groups of
-// (scale16 | bias16 << 16); nvfp4, 16 rows x 8 scale bytes.  A wave's codes
+// (r, b) in the same order: 16 rows x (128 / gs) groups of, for affine,
+// (scale16 | bias16 << 16), for nvfp4 and mxfp4 one scale byte.  A wave's codes
 // for one block are one 1 KiB piece and its constants one piece of at most
 // 256 bytes, where [N, K/8] + [N, K/gs] spread them over 16 rows each.  The
 // lane that reads a code is the lane that multiplies it, as before.
-__host__ __device__ constexpr int qconst_chunk_bytes(int qm, int gs) { return qm == BI_AFFINE ? 16 * (128 / gs) * 4 : 16 * 8; }
+__host__ __device__ constexpr int qconst_chunk_bytes(int qm, int gs) { return 16 * (128 / gs) * (qm == BI_AFFINE ? 4 : 1); }
 
 // Lane (g, c)'s words and group constants of row group rg, block b (packed).
 template <int QM, int GS>
@@ -94,8 +145,11 @@ __device__ inline void qload_packed_raw(const uint32_t *wqp, int64_t nrg, int64_
         const uint32_t v = *reinterpret_cast<const uint32_t *>(cb + (c * (128 / GS) + (32 * g) / GS) * 4);
         sc = v & 0xffffu;
         bs = v >> 16;
-    } else {
+    } else if constexpr (QM == BI_NVFP4) {
         sc = *reinterpret_cast<const uint16_t *>(cb + c * 8 + 2 * g);   // groups 2g (low byte) and 2g + 1
+        bs = 0;
+    } else {
+        sc = cb[c * 4 + g];                                             // the lane's one group
         bs = 0;
     }
 }
@@ -105,7 +159,7 @@ __device__ inline uint16_t deq1(uint32_t q, const QGroup<QM> &g)
 {
     float v;
     if (QM == BI_AFFINE) v = __builtin_fmaf(g.s, (float)q, g.b);
-    else v = e2m1_to_f32(q) * g.s;
+    else v = e2m1_to_f32(q) * g.s;                 // exact in fp32 for both fp modes
     return F16::narrow(v);
 }
 
@@ -134,6 +188,19 @@ __device__ inline uint4 deq_word(uint32_t w, const QGroup<QM> &g)
             const float q0 = (float)((lo >> (8 * p)) & 0xffu), q1 = (float)((hi >> (8 * p)) & 0xffu);
             const f32x2 v = f32x2{__builtin_fmaf(g.s, q0, g.b), __builtin_fmaf(g.s, q1, g.b)};
             out[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+        }
+    } else if constexpr (QM == BI_MXFP4) {
+        // e2m1 * 2^-14 from the code bits (as nvfp4), times 2^14 and 2^k1
+        // (both exact), times 2^k2 (the one rounding; see mx_group)
+        const f16x2 k14 = f16x2{(_Float16)16384.0f, (_Float16)16384.0f};
+        const f16x2 s1 = __builtin_bit_cast(f16x2, (g.m & 0xffffu) * 0x00010001u);
+        const f16x2 s2 = __builtin_bit_cast(f16x2, (g.m >> 16) * 0x00010001u);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t t = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | (uint32_t)p | ((uint32_t)(4 + p) << 16));
+            const uint32_t bits = ((t & 0x00080008u) << 12) | ((t & 0x00070007u) << 9);
+            const f16x2 v = ((__builtin_bit_cast(f16x2, bits) * k14) * s1) * s2;
+            out[p] = __builtin_bit_cast(uint32_t, v);
         }
     } else {
         const _Float16 sh = (_Float16)g.s;                 // e4m3 values are exact in binary16
@@ -257,17 +324,7 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
                 qload_packed_raw<QM, GS>(wq, nrg, nblocks, rg0 < nrg ? rg0 : nrg - 1, b, lane, wv, sc, bs);
                 const uint32_t wa[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    QGroup<QM> gr;
-                    if constexpr (QM == BI_AFFINE) {
-                        gr.s = F16::widen((uint16_t)sc);
-                        gr.b = F16::widen((uint16_t)bs);
-                    } else {
-                        gr.s = e4m3_to_f32((sc >> (s < 2 ? 0 : 8)) & 0xffu);
-                        gr.b = 0.0f;
-                    }
-                    Bf[j][s] = deq_word<QM>(wa[s], gr);
-                }
+                for (int s = 0; s < 4; ++s) Bf[j][s] = deq_word<QM>(wa[s], group_from_raw<QM>(sc, bs, s));
             } else if (TRANS) {
                 qload_trans<QM, GS, WVEC>(Bf[j], wq, scales, biases, wn[j], wok[j], K, kbase);
             } else {
@@ -354,8 +411,11 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
                 if (QM == BI_AFFINE) {
                     Sd[j] = ((const uint16_t *)scales)[gi];
                     Bd[j] = biases[gi];
-                } else {
+                } else if (QM == BI_NVFP4) {
                     Sd[j] = ((const uint16_t *)scales)[gi / 2];             // the lane's two group bytes
+                    Bd[j] = 0;
+                } else {
+                    Sd[j] = ((const uint8_t *)scales)[gi];                  // the lane's one group byte
                     Bd[j] = 0;
                 }
             }
@@ -417,14 +477,7 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
                     for (int s = 0; s < 4; ++s) {
 #pragma unroll
                         for (int j = 0; j < NS; ++j) {
-                            QGroup<QM> gr;
-                            if (QM == BI_AFFINE) {
-                                gr.s = F16::widen((uint16_t)Sr[d][j]);
-                                gr.b = F16::widen((uint16_t)Br[d][j]);
-                            } else {
-                                gr.s = e4m3_to_f32((Sr[d][j] >> (s < 2 ? 0 : 8)) & 0xffu);
-                                gr.b = 0.0f;
-                            }
+                            const QGroup<QM> gr = group_from_raw<QM>(Sr[d][j], Br[d][j], s);
                             const uint32_t wv = s == 0 ? Wr[d][j].x : s == 1 ? Wr[d][j].y : s == 2 ? Wr[d][j].z : Wr[d][j].w;
                             acc[j] = qmfma(Xr[d][s], deq_word<QM>(wv, gr), acc[j]);
                         }
@@ -509,7 +562,7 @@ __global__ void pack_q_kernel(const uint32_t *__restrict__ wq, const void *__res
                               const uint16_t *__restrict__ biases, uint32_t *__restrict__ wqp, int64_t N, int64_t K)
 {
     const int64_t nb = K / kQBlock, nrg = (N + 15) / 16, words = K / 8, groups = K / GS;
-    constexpr int GPB = QM == BI_AFFINE ? 128 / GS : 8;          // constant entries per row per block
+    constexpr int GPB = 128 / GS;                                // constant entries per row per block
     const int64_t ncode = nrg * nb * 64, nconst = nrg * nb * 16 * GPB;
     uint8_t *cbase = reinterpret_cast<uint8_t *>(wqp) + nrg * nb * 1024;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ncode + nconst;
@@ -544,6 +597,7 @@ static bi_status check_qmode(int32_t qmode, int32_t bits, int32_t group_size)
     if (bits != 4) return BI_ERR_GROUP;
     if (qmode == BI_AFFINE) return (group_size == 32 || group_size == 64 || group_size == 128) ? BI_OK : BI_ERR_GROUP;
     if (qmode == BI_NVFP4) return group_size == 16 ? BI_OK : BI_ERR_GROUP;
+    if (qmode == BI_MXFP4) return group_size == 32 ? BI_OK : BI_ERR_GROUP;
     return BI_ERR_GROUP;
 }
 
@@ -559,7 +613,7 @@ extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *s
     if (qs != BI_OK) return qs;
     if (!packed) {
         if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
-        if (qmode == BI_NVFP4 && biases) return BI_ERR_GROUP;
+        if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
     }
     const int64_t qdim = w_layout ? K : N;
     if (qdim % group_size) return BI_ERR_GROUP;
@@ -569,6 +623,7 @@ extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *s
         return BI_ERR_ALIGN;
     (void)hipGetLastError();
     if (qmode == BI_NVFP4) launch_q<BI_NVFP4, 16>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
+    else if (qmode == BI_MXFP4) launch_q<BI_MXFP4, 32>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
     else if (group_size == 32) launch_q<BI_AFFINE, 32>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
     else if (group_size == 64) launch_q<BI_AFFINE, 64>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
     else launch_q<BI_AFFINE, 128>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
@@ -590,18 +645,19 @@ extern "C" bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, co
     const bi_status qs = check_qmode(qmode, bits, group_size);
     if (qs != BI_OK) return qs;
     if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
-    if (qmode == BI_NVFP4 && biases) return BI_ERR_GROUP;
+    if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
     if (bi_packed_qweight_bytes(N, K, qmode, bits, group_size) == 0) return BI_ERR_SHAPE;
     if (!host_aligned16(wq) || !host_aligned16(wqp) || ((uintptr_t)scales & 1u) || ((uintptr_t)biases & 1u))
         return BI_ERR_ALIGN;
     (void)hipGetLastError();
     const int64_t nrg = cdiv(N, 16), nb = K / kQBlock;
-    const int64_t n = nrg * nb * 64 + nrg * nb * 16 * (qmode == BI_AFFINE ? 128 / group_size : 8);
+    const int64_t n = nrg * nb * 64 + nrg * nb * 16 * (128 / group_size);
     const dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), block(256);
     const uint32_t *w = wq;
     const uint16_t *bz = (const uint16_t *)biases;
     uint32_t *o = (uint32_t *)wqp;
     if (qmode == BI_NVFP4) hipLaunchKernelGGL((pack_q_kernel<BI_NVFP4, 16>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    else if (qmode == BI_MXFP4) hipLaunchKernelGGL((pack_q_kernel<BI_MXFP4, 32>), grid, block, 0, stream, w, scales, bz, o, N, K);
     else if (group_size == 32) hipLaunchKernelGGL((pack_q_kernel<BI_AFFINE, 32>), grid, block, 0, stream, w, scales, bz, o, N, K);
     else if (group_size == 64) hipLaunchKernelGGL((pack_q_kernel<BI_AFFINE, 64>), grid, block, 0, stream, w, scales, bz, o, N, K);
     else hipLaunchKernelGGL((pack_q_kernel<BI_AFFINE, 128>), grid, block, 0, stream, w, scales, bz, o, N, K);

@@ -69,7 +69,9 @@ def test_matmul_validation(args, code):
     (1, 512, 4096, 0, 4, 32, 1, None, NULL),        # affine needs biases
     (50, 128, 1040, 0, 4, 32, 1, A, GROUP),         # affine K % gs != 0 (transposed)
     (64, 100, 32768, 0, 4, 32, 0, A, GROUP),        # natural layout quantizes N: 100 % 32 != 0
-    (1, 512, 4096, 2, 4, 32, 1, A, GROUP),          # unknown mode
+    (1, 512, 4096, 2, 4, 16, 1, None, GROUP),       # mxfp4 needs gs 32
+    (1, 512, 4096, 2, 4, 32, 1, A, GROUP),          # mxfp4 takes no biases
+    (1, 512, 4096, 3, 4, 32, 1, None, GROUP),       # unknown mode
     (0, 512, 4096, 0, 4, 32, 1, A, SHAPE),
 ])
 def test_qmatmul_validation(M, N, K, qmode, bits, gs, trans, biases, code):

@@ -2,8 +2,8 @@
 matmul oracle, bitwise invariance over M, bounded tails.
 
 Workload: x fp16 ~ N(0,1); W ~ N(0,1) quantized per group -- affine int4 at
-group sizes 32/64/128 (fp16 scale and bias) and nvfp4 (e2m1 codes, one e4m3
-scale per 16); shapes (M, K, N) in {(1..8, 4096, 512), (50, 1040, 128),
+group sizes 32/64/128 (fp16 scale and bias), nvfp4 (e2m1 codes, one e4m3
+scale per 16) and mxfp4 (e2m1 codes, one e8m0 power-of-two scale per 32); shapes (M, K, N) in {(1..8, 4096, 512), (50, 1040, 128),
 (64, 32768, 100)} in both layouts where legal -- the shapes of "Fix fp
 quantized matmul corruption when the quantized dim is not a multiple of 32"
 (Problem reproducer; affine over-read reproducer; Validation) and the
@@ -19,8 +19,8 @@ from invariant_reductions_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-MODES = [("affine", 32), ("affine", 64), ("affine", 128), ("nvfp4", 16)]
-QM = {"affine": bi.AFFINE, "nvfp4": bi.NVFP4}
+MODES = [("affine", 32), ("affine", 64), ("affine", 128), ("nvfp4", 16), ("mxfp4", 32)]
+QM = {"affine": bi.AFFINE, "nvfp4": bi.NVFP4, "mxfp4": bi.MXFP4}
 
 
 def dev_q(wq, s, b):
@@ -38,8 +38,11 @@ def run(x, wq, s, b, N, K, mode, gs, transposed):
     return to_np(bi.qmatmul(to_dev(x, "f16"), wqd, sd, bd, N, K, QM[mode], gs, transposed))
 
 
+OQM = {"affine": oracle.AFFINE, "nvfp4": oracle.NVFP4, "mxfp4": oracle.MXFP4}
+
+
 def ref(x, wq, s, b, M, N, K, mode, gs, transposed):
-    return oracle.qmatmul(x, wq, s, b, M, N, K, QM[mode], gs, transposed)
+    return oracle.qmatmul(x, wq, s, b, M, N, K, OQM[mode], gs, transposed)
 
 
 @pytest.mark.parametrize("mode,gs", MODES)
@@ -116,6 +119,65 @@ def test_nvfp4_unit_scale_bit_exact(shape, transposed):
     x = inputs.integer_values(rng, (M, K), -8, 8, "f16")
     r = oracle.round_to(ref(x, wq, s, None, M, N, K, "nvfp4", 16, transposed), "f16")
     assert bits_equal(run(x, wq, s, None, N, K, "nvfp4", 16, transposed), r)
+
+
+@pytest.mark.parametrize("M,K,N", [(5, 4096, 100), (17, 512, 64)])
+@pytest.mark.parametrize("transposed", [True, False])
+def test_mxfp4_power_of_two_scales_bit_exact(M, K, N, transposed):
+    """Scales 2^(e-127) for e in 124..130 with integer x: every product and
+    partial sum is a multiple of 2^-4 below 2^20, so the GPU equals the oracle
+    bit for bit whatever the order of the sums."""
+    if not transposed and N % 32:
+        pytest.skip("natural layout quantizes N")
+    rng = np.random.default_rng(K + N)
+    rows, cols = (N, K) if transposed else (K, N)
+    codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint32)
+    wq = inputs.pack_nibbles(codes)
+    s = rng.integers(124, 131, size=(rows, cols // 32)).astype(np.uint8)
+    x = inputs.integer_values(rng, (M, K), -8, 8, "f16")
+    r = oracle.round_to(ref(x, wq, s, None, M, N, K, "mxfp4", 32, transposed), "f16")
+    assert bits_equal(run(x, wq, s, None, N, K, "mxfp4", 32, transposed), r)
+
+
+@pytest.mark.parametrize("M", [8, 32])
+def test_mxfp4_every_code_and_finite_scale(M):
+    """One-hot rows of x read single dequantized weights: every code at every
+    scale byte whose values stay finite in binary16 (e <= 140), through the
+    streaming (M <= 16) and tiled kernels, equals the oracle's binary16
+    rounding bit for bit -- subnormal and zero results included."""
+    es = np.arange(0, 141, dtype=np.uint8)
+    K, N = 32, es.size
+    codes = np.tile(np.arange(16, dtype=np.uint32).repeat(2), (N, 1))        # [N, 32]
+    wq, s = inputs.pack_nibbles(codes), es[:, None].copy()
+    transposed = True
+    x = np.zeros((M, K), np.float32)
+    x[np.arange(M), np.arange(M) % K] = 1.0
+    xb = inputs.to_storage(x, "f16")
+    r = oracle.round_to(ref(xb, wq, s, None, M, N, K, "mxfp4", 32, transposed), "f16")
+    assert bits_equal(run(xb, wq, s, None, N, K, "mxfp4", 32, transposed), r)
+
+
+def test_mxfp4_extreme_scales_match_oracle():
+    """Scales far outside binary16 (e = 0, 1, 100, 150, 254) and the NaN byte:
+    the dequantized weights overflow to inf, flush to zero or are NaN exactly
+    as the oracle rounds them.  Every finite output sums multiples of 1/2
+    (scale-1 groups, integer x) exactly, so outputs agree value for value,
+    inf for inf and NaN for NaN."""
+    M, K, N = 2, 256, 32
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.uint32)
+    s = np.full((N, K // 32), 127, np.uint8)
+    s[8:16, 2] = rng.choice(np.array([150, 254], np.uint8), size=8)      # overflow to +inf ...
+    codes[8:16, 64:96] = rng.integers(1, 8, size=(8, 32))               # ... from positive codes
+    s[16:24, 5] = 255                                                     # NaN scale
+    s[24:32, ::2] = rng.choice(np.array([0, 1, 100], np.uint8), size=(8, 4))   # flush to zero
+    wq = inputs.pack_nibbles(codes)
+    x = inputs.integer_values(rng, (M, K), 1, 2, "f16")                  # positive: no 0 * inf
+    r = oracle.round_to(ref(x, wq, s, None, M, N, K, "mxfp4", 32, True), "f16")
+    g = run(x, wq, s, None, N, K, "mxfp4", 32, True)
+    rf, gf = inputs.from_storage(r, "f16"), inputs.from_storage(g, "f16")
+    assert np.isnan(rf).any() and np.isinf(rf).any() and np.isfinite(rf).any()
+    assert np.array_equal(rf, gf, equal_nan=True)
 
 
 @pytest.mark.parametrize("mode,gs,M,K,N,transposed", [
