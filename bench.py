@@ -64,7 +64,8 @@ def step_traffic(cfg, B, ctx):
 def measured_traffic():
     """HBM bytes per matmul launch from the committed counter runs
     (profiles/dense_slots_kernel_decode_b64_traffic.json), or None when the
-    kernel sources have changed since those counters were taken."""
+    dense kernel sources it lists have changed since those counters were
+    taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "dense_slots_kernel_decode_b64_traffic.json")
     try:
