@@ -83,6 +83,8 @@ def lib():
         L.bo_rope.argtypes = [P, P, P, P, P, I64, I64, I64, I32]
         L.bo_silu_mul.argtypes = [P, P, P, I64, I32]
         L.bo_argmax.argtypes = [P, P, I64, I64, I32]
+        L.bo_log_softmax.argtypes = [P, P, I64, I64, I32]
+        L.bo_row_mean.argtypes = [P, P, I64, I64, I32]
         L.bo_num_threads.argtypes = []; L.bo_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -243,3 +245,24 @@ def argmax(x, dtype) -> np.ndarray:
     idx = np.empty(rows, np.int32)
     _check(lib().bo_argmax(_p(x), _p(idx), rows, cols, _dt(dtype)), "argmax")
     return idx
+
+
+def log_softmax(x, dtype) -> np.ndarray:
+    """fp32 [rows, cols]: (x - max) - log(sum exp(x - max)), the sum in
+    ascending column order ("Batch-invariant kernels ...", The trap and
+    Sources: the log-softmax / logprob outputs an RL trainer compares with its
+    sampler)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    y = np.empty((rows, cols), np.float32)
+    _check(lib().bo_log_softmax(_p(x), _p(y), rows, cols, _dt(dtype)), "log_softmax")
+    return y
+
+
+def row_mean(x, dtype) -> np.ndarray:
+    """fp32 [rows]: the ascending fp32 sum of each row divided by cols."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    y = np.empty(rows, np.float32)
+    _check(lib().bo_row_mean(_p(x), _p(y), rows, cols, _dt(dtype)), "row_mean")
+    return y

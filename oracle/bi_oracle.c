@@ -490,6 +490,43 @@ int bo_argmax(const void *x, int32_t *idx, int64_t rows, int64_t cols, int dtype
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Row log-softmax, token log-probability and row mean                     */
+/* ------------------------------------------------------------------------ */
+
+/* y[r, c] = (x[r, c] - m) - logf(s), m = max_c x[r, c], s = sum_c expf(x[r, c] - m)
+ * summed in ascending c in fp32 (the textbook log-softmax, written out). */
+int bo_log_softmax(const void *x, float *y, int64_t rows, int64_t cols, int dtype)
+{
+    if (!x || !y || cols < 1 || !valid_dtype(dtype)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float m = load_elem(x, r * cols, dtype);
+        for (int64_t c = 1; c < cols; ++c) {
+            float v = load_elem(x, r * cols + c, dtype);
+            if (v > m) m = v;
+        }
+        float s = 0.0f;
+        for (int64_t c = 0; c < cols; ++c) s = s + expf(load_elem(x, r * cols + c, dtype) - m);
+        const float ls = logf(s);
+        for (int64_t c = 0; c < cols; ++c) y[r * cols + c] = (load_elem(x, r * cols + c, dtype) - m) - ls;
+    }
+    return 0;
+}
+
+/* y[r] = (sum_c x[r, c], ascending c, fp32) / cols. */
+int bo_row_mean(const void *x, float *y, int64_t rows, int64_t cols, int dtype)
+{
+    if (!x || !y || cols < 1 || !valid_dtype(dtype)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float s = 0.0f;
+        for (int64_t c = 0; c < cols; ++c) s = s + load_elem(x, r * cols + c, dtype);
+        y[r] = s / (float)cols;
+    }
+    return 0;
+}
+
 int bo_num_threads(void)
 {
 #ifdef _OPENMP

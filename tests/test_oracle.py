@@ -654,3 +654,52 @@ def test_decode_step_reproduces_teacher_forced_forward():
         logits, ids = decoder.decode_step(W, c, toks[:, p], kc, vc, np.full(2, p + 1, np.int32), cos_t, sin_t)
         for b in range(2):
             assert np.array_equal(logits[b], full[b][p]), (b, p)
+
+
+# ---------------------------------------------------------------------------
+# log-softmax, token log-probabilities, row mean
+# ---------------------------------------------------------------------------
+
+def test_log_softmax_closed_forms():
+    """A constant row gives -ln(cols) everywhere (within an ulp of fp32 log);
+    one dominant logit (100 above the rest) gives exactly 0 there and exactly
+    -100 elsewhere, since exp(-100) * (cols - 1) vanishes next to 1 in fp32."""
+    for cols in (1, 7, 32000, 65536):
+        x = inputs.to_storage(np.full((2, cols), 3.0, np.float32), "bf16")
+        y = oracle.log_softmax(x, "bf16")
+        assert np.all(y == y[0, 0])
+        assert abs(float(y[0, 0]) + np.log(cols)) <= 2 * np.spacing(np.float32(np.log(cols)))
+    x = np.zeros((1, 1000), np.float32)
+    x[0, 417] = 100.0
+    y = oracle.log_softmax(x, "f32")
+    assert y[0, 417] == 0.0 and np.all(np.delete(y[0], 417) == -100.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_log_softmax_within_bound_of_torch_fp64(dtype):
+    """Against torch's fp64 log_softmax: the fp32 sequential sum of cols terms
+    and one rounding of x - m, log and the subtraction bound the error."""
+    rng = np.random.default_rng(11)
+    cols = 32000
+    x = inputs.to_storage((rng.standard_normal((4, cols)) * 4).astype(np.float32), dtype)
+    xf = inputs.from_storage(x, dtype).astype(np.float64)
+    ref = torch.log_softmax(torch.from_numpy(xf), dim=1).numpy()
+    y = oracle.log_softmax(x, dtype).astype(np.float64)
+    bound = (cols + 8) * 2.0 ** -24 + 4 * 2.0 ** -24 * (np.abs(ref) + np.abs(xf).max(axis=1, keepdims=True))
+    assert np.all(np.abs(y - ref) <= bound)
+    # and the probabilities sum to one within the same order of error
+    assert np.all(np.abs(np.exp(y).sum(axis=1) - 1.0) <= (cols + 8) * 2.0 ** -23)
+
+
+def test_row_mean_exact_and_bounded():
+    """Integer rows with a power-of-two length: every partial sum and the
+    division are exact; random rows: within the fp32 sequential-sum bound of
+    numpy's fp64 mean."""
+    rng = np.random.default_rng(12)
+    xi = rng.integers(-100, 100, size=(5, 4096)).astype(np.float32)
+    y = oracle.row_mean(inputs.to_storage(xi, "bf16"), "bf16")
+    assert np.array_equal(y.astype(np.float64), xi.astype(np.float64).mean(axis=1))
+    x = (rng.standard_normal((5, 3000)) * 2).astype(np.float32)
+    y = oracle.row_mean(x, "f32").astype(np.float64)
+    ref = x.astype(np.float64).mean(axis=1)
+    assert np.all(np.abs(y - ref) <= gamma(3000) * np.abs(x).astype(np.float64).sum(axis=1) / 3000 + 2.0 ** -24 * np.abs(ref))
