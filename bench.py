@@ -245,6 +245,7 @@ def main():
         out["ops"] = op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch)
         out["invariance_overhead"] = split_overhead(torch, bi, model, B, per_shape)
         out["qmatmul"] = qmatmul_decode(torch, bi, dev)
+        out["row_ops"] = row_ops(torch, bi, model, B)
 
     if not args.no_cpu_baseline:
         n, secs, cores = cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids0, args.cpu_budget)
@@ -342,6 +343,24 @@ def _time_kernel(torch, bi, fn, reps):
         fn(i)
     torch.cuda.synchronize()
     return float(np.mean([s_.elapsed_time(t_) for s_, t_ in ev]))
+
+
+def row_ops(torch, bi, model, B):
+    """Log-softmax, token log-probabilities and row mean over the step's own
+    logits [B, vocab] bf16 (kernel time, launch-recorded events)."""
+    x = model.logits[:B]
+    ids = model.next_ids[:B]
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    lp = torch.empty(B, dtype=torch.float32, device=x.device)
+    res = {}
+    V = x.shape[1]
+    for name, fn, nbytes in (("log_softmax", lambda i: bi.log_softmax(x, out=y), 2 * B * V + 4 * B * V),
+                             ("token_logprob", lambda i: bi.token_logprob(x, ids, out=lp), 2 * B * V + 8 * B),
+                             ("row_mean", lambda i: bi.row_mean(x, out=lp), 2 * B * V + 4 * B)):
+        t = _time_kernel(torch, bi, fn, reps=50)
+        gbs = nbytes / (t * 1e-3) / 1e9
+        res[f"{name} {B}x{V}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def qmatmul_decode(torch, bi, dev):

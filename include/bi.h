@@ -287,6 +287,29 @@ bi_status bi_sdpa(const void *q, const void *k, const void *v, void *o, const in
                   int32_t dtype, int32_t kv_layout, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Row log-softmax, token log-probabilities and row mean (the log-prob
+ * outputs a sampler and an RL trainer must agree on bit for bit).
+ * Source: "Batch-invariant kernels ...", The boring rule (item 1: one
+ * reduction strategy at every batch size), The trap (train/serve log-prob
+ * mismatch), Sources (the companion library's mean and log-softmax).
+ *   x   : [rows, cols] of `dtype` (BI_BF16, BI_F16, BI_F32).
+ *   bi_log_softmax  : y fp32 [rows, cols], y = (x - max) - log(sum exp(x - max)).
+ *   bi_token_logprob: out fp32 [rows], the same value at column ids[r]
+ *                     (ids device int32 [rows]; an id outside [0, cols) gives NaN).
+ *   bi_row_mean     : y fp32 [rows], the row sum divided by cols.
+ * Tree per row (depends on cols only): 8-element chunks dealt round-robin to
+ * 1024 threads, a sequential fold per thread, a xor butterfly per wave, the
+ * 16 wave sums in order; the max is exact.  A row's result does not depend
+ * on rows or on its position.  Errors: BI_ERR_NULL, BI_ERR_SHAPE (rows or
+ * cols < 1), BI_ERR_DTYPE, BI_ERR_ALIGN (x not element-aligned, y / ids not
+ * 4-byte aligned).
+ * ------------------------------------------------------------------------ */
+bi_status bi_log_softmax(const void *x, float *y, int64_t rows, int64_t cols, int32_t dtype, hipStream_t stream);
+bi_status bi_token_logprob(const void *x, const int32_t *ids, float *out, int64_t rows, int64_t cols,
+                           int32_t dtype, hipStream_t stream);
+bi_status bi_row_mean(const void *x, float *y, int64_t rows, int64_t cols, int32_t dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Pointwise glue of a Llama-style decoder.  Pointwise ops are batch-invariant
  * by construction ("Batch-invariant kernels ...", Mental model).  All tensors
  * are bf16 unless stated.

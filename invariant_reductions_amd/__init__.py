@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "BIError", "library_path", "lib", "build_info",
     "matmul", "matmul_ws", "matmul_workspace", "matmul_swiglu", "matmul_swiglu_workspace", "interleave_gate_up",
-    "PackedWeight", "pack_weights", "pack_qweights",
+    "PackedWeight", "pack_weights", "pack_qweights", "log_softmax", "token_logprob", "row_mean",
     "qmatmul", "rmsnorm", "add_rmsnorm", "sdpa", "sdpa_workspace_bytes",
     "matmul_split", "rmsnorm_split",
     "embed", "rope_kv_write", "silu_mul", "add", "argmax",
@@ -74,6 +74,9 @@ def lib():
             "bi_matmul_swiglu": [P, P, P, I64, I64, I64, I32, I32, P, SZ, P],
             "bi_pack_weights": [P, P, I64, I64, I32, P],
             "bi_pack_qweights": [P, P, P, P, I64, I64, I32, I32, I32, P],
+            "bi_log_softmax": [P, P, I64, I64, I32, P],
+            "bi_token_logprob": [P, P, P, I64, I64, I32, P],
+            "bi_row_mean": [P, P, I64, I64, I32, P],
             "bi_rmsnorm_split": [P, P, P, I64, I64, F, I32, I32, P, SZ, P],
         }
         for name, args in sig.items():
@@ -397,4 +400,38 @@ def argmax(x, out=None, stream=None):
     rows, cols = x.shape
     y = out if out is not None else torch.empty(rows, dtype=torch.int32, device=x.device)
     _check(lib().bi_argmax(_ptr(x), _ptr(y), rows, cols, _stream(stream)), "bi_argmax")
+    return y
+
+
+# ---------------------------------------------------------------------------
+# log-probabilities and means
+# ---------------------------------------------------------------------------
+
+def log_softmax(x, out=None, stream=None):
+    """fp32 [rows, cols] log-softmax of x [rows, cols] (bf16/f16/f32)."""
+    _dev(x, out)
+    rows, cols = x.shape
+    y = out if out is not None else torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    _check(lib().bi_log_softmax(_ptr(x), _ptr(y), rows, cols, _dt(x), _stream(stream)), "bi_log_softmax")
+    return y
+
+
+def token_logprob(x, ids, out=None, stream=None):
+    """fp32 [rows]: log_softmax(x)[r, ids[r]], bit for bit; ids int32 [rows] on the device."""
+    _dev(x, ids, out)
+    rows, cols = x.shape
+    if ids.dtype != torch.int32 or ids.numel() != rows:
+        raise ValueError("token_logprob: ids must be int32 [rows]")
+    y = out if out is not None else torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib().bi_token_logprob(_ptr(x), _ptr(ids), _ptr(y), rows, cols, _dt(x), _stream(stream)),
+           "bi_token_logprob")
+    return y
+
+
+def row_mean(x, out=None, stream=None):
+    """fp32 [rows] mean of each row of x [rows, cols]."""
+    _dev(x, out)
+    rows, cols = x.shape
+    y = out if out is not None else torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib().bi_row_mean(_ptr(x), _ptr(y), rows, cols, _dt(x), _stream(stream)), "bi_row_mean")
     return y

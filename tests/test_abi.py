@@ -202,6 +202,17 @@ def test_packed_qweight_validation():
     assert L.bi_qmatmul(A, A, None, None, A, 4, 16, 128, 0, 4, 64, 1, None) == NULL    # transposed needs scales
 
 
+def test_row_reduction_validation():
+    L = bi.lib()
+    assert L.bi_log_softmax(None, A, 4, 32000, 0, None) == NULL
+    assert L.bi_token_logprob(A, None, A, 4, 32000, 0, None) == NULL
+    assert L.bi_row_mean(A, A, 0, 32000, 0, None) == SHAPE
+    assert L.bi_log_softmax(A, A, 4, 0, 0, None) == SHAPE
+    assert L.bi_log_softmax(A, A, 4, 32000, 9, None) == DTYPE
+    assert L.bi_log_softmax(ODD, A, 4, 32000, 0, None) == ALIGN
+    assert L.bi_row_mean(A, P(0x10002), 4, 32000, 0, None) == ALIGN
+
+
 def test_add_rmsnorm_validation():
     L = bi.lib()
     assert L.bi_add_rmsnorm(A, None, A, A, A, 4, 4096, 1e-6, 0, None) == NULL
