@@ -158,3 +158,22 @@ def test_head_major_cache_same_bits(B, Q, Lk):
     hm = to_np(bi.sdpa(qd, kd.transpose(1, 2).contiguous(), vd.transpose(1, 2).contiguous(), kvd, Lk, SCALE, True,
                        head_major=True))
     assert bits_equal(hm, std)
+
+
+@pytest.mark.parametrize("L,chunk", [(1100, 256), (777, 100), (520, 1)])
+def test_prefill_chunking_invariance(L, chunk):
+    """A prompt prefilled in one causal call and the same prompt prefilled in
+    chunks over the growing cache give every token the same bits: a token's
+    tree depends on its position only, not on the prefill chunking or on how
+    much of the prefix was cached (the invariant-prefill property of chunked
+    prefill)."""
+    q, k, v = inputs.sdpa_case(1, L, L, HQ, HKV, D, seed=L)
+    kd, vd = to_dev(k, "bf16"), to_dev(v, "bf16")
+    qd = to_dev(q, "bf16")
+    one = bi.sdpa(qd, kd, vd, torch.tensor([L], dtype=torch.int32, device=dev()), L, SCALE, True)
+    parts = []
+    for s0 in range(0, L, chunk):
+        s1 = min(s0 + chunk, L)
+        parts.append(bi.sdpa(qd[:, s0:s1].contiguous(), kd, vd, torch.tensor([s1], dtype=torch.int32, device=dev()),
+                             s1, SCALE, True))
+    assert torch.equal(torch.cat(parts, dim=1).view(torch.int16), one.view(torch.int16))
