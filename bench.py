@@ -149,7 +149,9 @@ def main():
     calib2 = torch.empty_like(calib)
     calib2.copy_(calib)
     del calib, calib2
-    plan = model.plan(B, 1, cap, stream)
+    # the step's last launch (argmax) also feeds its tokens back as the next
+    # step's ids and grows kv_len: the plan is replayed as is, step after step
+    plan = model.plan(B, 1, cap, stream, advance=True)
     MM_OPS = ("matmul", "matmul_swiglu")
     mm_idx = [i for i, s in enumerate(plan) if s[0] in MM_OPS]
     # (N, K) of each matmul launch (the fused gate/up call passes F = N / 2)
@@ -159,13 +161,8 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
-    def advance():
-        model.ids[:B].copy_(model.next_ids[:B])
-        model.kv_len[:B].add_(1)
-
     for _ in range(Wm):
         model.run_plan(plan)
-        advance()
     # Timed region: K whole steps, nothing but the step's own launches (a HIP
     # event record costs several microseconds of idle GPU time, so none is
     # placed between the kernels here).
@@ -173,7 +170,6 @@ def main():
     t0 = time.perf_counter()
     for _ in range(K):
         model.run_plan(plan)
-        advance()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
@@ -200,7 +196,6 @@ def main():
                 rc = fn(*a)
             if rc != 0:
                 raise bi.BIError(rc, name)
-        advance()
     torch.cuda.synchronize()
     durs = [s.elapsed_time(t) for s, t in ev]
     mm_ms = sum(durs)

@@ -348,6 +348,15 @@ bi_status bi_add(const void *a, const void *b, void *out, int64_t n, hipStream_t
  * index wins ties; idx device int32 [rows]. */
 bi_status bi_argmax(const void *x, int32_t *idx, int64_t rows, int64_t cols, hipStream_t stream);
 
+/* Greedy decode step bookkeeping fused into the argmax of its logits (one
+ * new token per sequence, rows == sequences): idx[r] = argmax as bi_argmax,
+ * ids_next[r] = the same token (the sequence's next input) and kv_len[r] += 1
+ * (its cache grows by one position).  ids_next and kv_len: device int32
+ * [rows]; kv_len must not be read or written by other work in flight.
+ * Errors: as bi_argmax, BI_ERR_NULL for ids_next or kv_len. */
+bi_status bi_argmax_advance(const void *x, int32_t *idx, int32_t *ids_next, int32_t *kv_len, int64_t rows,
+                            int64_t cols, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Non-invariant comparison variants.  These reproduce the strategies the
  * pages identify as the source of batch dependence -- split-K matmul with a

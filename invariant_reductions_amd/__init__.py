@@ -75,6 +75,7 @@ def lib():
             "bi_pack_weights": [P, P, I64, I64, I32, P],
             "bi_pack_qweights": [P, P, P, P, I64, I64, I32, I32, I32, P],
             "bi_log_softmax": [P, P, I64, I64, I32, P],
+            "bi_argmax_advance": [P, P, P, P, I64, I64, P],
             "bi_token_logprob": [P, P, P, I64, I64, I32, P],
             "bi_row_mean": [P, P, I64, I64, I32, P],
             "bi_rmsnorm_split": [P, P, P, I64, I64, F, I32, I32, P, SZ, P],

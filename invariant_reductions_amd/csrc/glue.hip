@@ -139,7 +139,8 @@ __device__ inline void argmax_take(float v, int i, float &bv, int &bi, int none)
 // meet candidates in any order.
 template <bool VEC>
 __global__ __launch_bounds__(kArgmaxThreads)
-void argmax_kernel(const uint16_t *__restrict__ x, int32_t *__restrict__ idx, int64_t rows, int64_t cols)
+void argmax_kernel(const uint16_t *__restrict__ x, int32_t *__restrict__ idx, int64_t rows, int64_t cols,
+                   int32_t *__restrict__ ids_next, int32_t *__restrict__ kv_len)
 {
     __shared__ float sv[kArgmaxThreads / kWave];
     __shared__ int si[kArgmaxThreads / kWave];
@@ -189,7 +190,13 @@ void argmax_kernel(const uint16_t *__restrict__ x, int32_t *__restrict__ idx, in
             const int oi = __shfl_xor(bi, off, kWave);
             argmax_take(ov, oi, bv, bi, none);
         }
-        if (lane == 0) idx[blockIdx.x] = bi;
+        if (lane == 0) {
+            idx[blockIdx.x] = bi;
+            // greedy decode bookkeeping: the token is the sequence's next input
+            // and its cache grows by one position
+            if (ids_next) ids_next[blockIdx.x] = bi;
+            if (kv_len) kv_len[blockIdx.x] = kv_len[blockIdx.x] + 1;
+        }
     }
 }
 
@@ -271,19 +278,32 @@ extern "C" bi_status bi_add(const void *a, const void *b, void *out, int64_t n, 
     return launch_status();
 }
 
-extern "C" bi_status bi_argmax(const void *x, int32_t *idx, int64_t rows, int64_t cols, hipStream_t stream)
+static bi_status run_argmax(const void *x, int32_t *idx, int32_t *ids_next, int32_t *kv_len, int64_t rows,
+                            int64_t cols, hipStream_t stream)
 {
     if (!x || !idx) return BI_ERR_NULL;
     if (rows < 1 || cols < 1 || rows > (1ll << 31) - 1 || cols > (1ll << 31) - 1) return BI_ERR_SHAPE;
-    if (!host_aligned16(x) || ((uintptr_t)idx & 3u)) return BI_ERR_ALIGN;
+    if (!host_aligned16(x) || (((uintptr_t)idx | (uintptr_t)ids_next | (uintptr_t)kv_len) & 3u)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
     if (cols % 8 == 0)
         hipLaunchKernelGGL(argmax_kernel<true>, dim3((unsigned)rows), dim3(kArgmaxThreads), 0, stream,
-                           (const uint16_t *)x, idx, rows, cols);
+                           (const uint16_t *)x, idx, rows, cols, ids_next, kv_len);
     else
         hipLaunchKernelGGL(argmax_kernel<false>, dim3((unsigned)rows), dim3(kArgmaxThreads), 0, stream,
-                           (const uint16_t *)x, idx, rows, cols);
+                           (const uint16_t *)x, idx, rows, cols, ids_next, kv_len);
     return launch_status();
+}
+
+extern "C" bi_status bi_argmax(const void *x, int32_t *idx, int64_t rows, int64_t cols, hipStream_t stream)
+{
+    return run_argmax(x, idx, nullptr, nullptr, rows, cols, stream);
+}
+
+extern "C" bi_status bi_argmax_advance(const void *x, int32_t *idx, int32_t *ids_next, int32_t *kv_len, int64_t rows,
+                                       int64_t cols, hipStream_t stream)
+{
+    if (!ids_next || !kv_len) return BI_ERR_NULL;
+    return run_argmax(x, idx, ids_next, kv_len, rows, cols, stream);
 }
 
 extern "C" const char *bi_status_str(int32_t status)

@@ -119,12 +119,14 @@ class Decoder:
         return self.logits[:T]
 
     # -- launch plans -----------------------------------------------------------------
-    def plan(self, B: int, Q: int, max_kv: int, stream=None):
+    def plan(self, B: int, Q: int, max_kv: int, stream=None, advance: bool = False):
         """The forward as a list of (name, C entry point, argument tuple) over the
         fixed buffers, for callers that replay the same step many times (a
         serving loop, the benchmark) without re-marshalling arguments.  The
         device-side ids / kv_len buffers are read at run time, so one plan
-        serves every step whose lengths stay within max_kv."""
+        serves every step whose lengths stay within max_kv.  advance (greedy
+        decode, Q = 1): the final argmax also writes each token into ids and
+        grows kv_len by one, so the plan can be replayed step after step."""
         import ctypes
         from . import lib
         L = lib()
@@ -161,7 +163,10 @@ class Decoder:
                 ("add_rmsnorm", L.bi_add_rmsnorm, (p(x), p(t1), p(x), p(nxt), p(h), T, H, eps, 0, st)),
             ]
         steps += [mm(h, self.lm_head, self.logits, self.V, H),
-                  ("argmax", L.bi_argmax, (p(self.logits), p(self.next_ids), T, self.V, st))]
+                  ("argmax", L.bi_argmax, (p(self.logits), p(self.next_ids), T, self.V, st)) if not advance else
+                  ("argmax", L.bi_argmax_advance, (p(self.logits), p(self.next_ids), p(self.ids), p(kv), T, self.V, st))]
+        if advance and Q != 1:
+            raise ValueError("plan(advance=True) is the one-token greedy step (Q = 1)")
         return steps
 
     @staticmethod

@@ -202,6 +202,14 @@ def test_packed_qweight_validation():
     assert L.bi_qmatmul(A, A, None, None, A, 4, 16, 128, 0, 4, 64, 1, None) == NULL    # transposed needs scales
 
 
+def test_argmax_advance_validation():
+    L = bi.lib()
+    assert L.bi_argmax_advance(A, A, None, A, 4, 32000, None) == NULL
+    assert L.bi_argmax_advance(A, A, A, None, 4, 32000, None) == NULL
+    assert L.bi_argmax_advance(A, A, A, P(0x10002), 4, 32000, None) == ALIGN
+    assert L.bi_argmax_advance(A, A, A, A, 0, 32000, None) == SHAPE
+
+
 def test_row_reduction_validation():
     L = bi.lib()
     assert L.bi_log_softmax(None, A, 4, 32000, 0, None) == NULL

@@ -76,6 +76,24 @@ def test_tokens_and_logits_identical_across_batch_sizes(model, prompts, plain64,
     assert np.array_equal(cs.cs.cpu().numpy(), cs64[:B])
 
 
+def test_replayed_advancing_plan_equals_generate(model, prompts, plain64):
+    """The one-token plan with the argmax's own bookkeeping (next ids and kv
+    lengths written by the kernel), replayed step after step, produces the
+    plain decoding's tokens."""
+    B, n = 16, 24
+    first, _ = model.prefill(torch.from_numpy(prompts[:B]).to(dev()))
+    model.ids[:B].copy_(torch.from_numpy(first).to(dev()))
+    model.kv_len[:B].fill_(P + 1)
+    plan = model.plan(B, 1, P + STEPS, advance=True)
+    got = [first]
+    for _ in range(1, n):
+        model.run_plan(plan)
+        got.append(model.next_ids[:B].cpu().numpy())
+    assert np.array_equal(np.stack(got, axis=1), plain64[0][:B, :n])
+    assert np.array_equal(model.kv_len[:B].cpu().numpy(), np.full(B, P + n, np.int32))
+    assert np.array_equal(model.ids[:B].cpu().numpy(), got[-1])
+
+
 def test_tokens_vary_between_sequences(plain64):
     toks64, _ = plain64
     assert len({tuple(r) for r in toks64}) > 1
