@@ -123,8 +123,9 @@ bi_status bi_pack_weights(const void *w, void *wp, int64_t N, int64_t K, int32_t
  * transposed 16-bit weights, K a multiple of 128 and 16-byte aligned x, w and
  * workspace, the slots of one output may be computed by different workgroups;
  * the partial sums of aligned slot groups meet in the workspace and are added
- * in the fixed tree order by whichever workgroup finishes last.  Every other
- * call runs bi_matmul's kernels.  w and w_layout as in bi_matmul (the slot
+ * in the fixed tree order by whichever workgroup finishes last (also for
+ * 8 < M <= 16 when N >= 16384, and 12 < M <= 16 when N K > 4096 * 4096).
+ * Every other call runs bi_matmul's kernels.  w and w_layout as in bi_matmul (the slot
  * form takes BI_W_TRANSPOSED and BI_W_PACKED weights).
  *   ws, ws_bytes: device memory of at least
  *     bi_matmul_ws_workspace_bytes(M, N, K, dtype, w_layout) bytes

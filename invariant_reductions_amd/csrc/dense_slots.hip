@@ -251,7 +251,20 @@ constexpr int64_t kSlotTileCols = kDenseWaves * 16;
 constexpr int64_t kSlotMaxTiles = 16384;                    // N up to 2^21 columns
 constexpr size_t kSlotCounterBytes = kSlotMaxTiles * sizeof(unsigned);
 
-static int slot_mt(int64_t M) { return M <= 32 ? 2 : 4; }
+static int slot_mt(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
+// Row counts the slot form takes: 16 < M <= 64, and down to M = 9 or 13 when
+// the weight is large -- there the one-workgroup-per-tile kernel reads each
+// tile's x rows once per column tile from L2 and falls behind the LDS-shared
+// x of the slot form (measured on the decoder's projections; at M <= 8 and
+// on 4096 x 4096 the streaming kernel stays ahead).
+static bool slot_takes(int64_t M, int64_t N, int64_t K)
+{
+    if (M > 64 || M < 1) return false;
+    if (M > 16) return true;
+    if (N >= 16384) return M > 8;
+    return M > 12 && N * K > 4096ll * 4096ll;
+}
 
 static size_t slot_ws_bytes(int64_t M, int64_t N, int groups)
 {
@@ -317,17 +330,17 @@ static bool try_launch_slots(const void *x, const void *w, void *y, void *ws, si
                              int64_t N, int64_t K, bool packed, hipStream_t st)
 {
     using G = DenseGeom<S>;
-    // M <= 16: x is small, and bi_matmul's one-workgroup-per-tile kernel,
-    // which needs no exchange of partial sums, streams W faster.
-    if (!ws || M <= 16 || M > 64 || K % G::KB != 0 || !host_aligned16(x) || !host_aligned16(w) ||
+    if (!ws || !slot_takes(M, N, K) || K % G::KB != 0 || !host_aligned16(x) || !host_aligned16(w) ||
         !host_aligned16(ws))
         return false;
     if (ws_bytes < slot_ws_bytes(M, N, kDenseWaves)) return false;
     if (packed) {
-        if (slot_mt(M) == 2) launch_slots_mt<S, 2, EPI, true>(x, w, y, ws, M, N, K, st);
+        if (slot_mt(M) == 1) launch_slots_mt<S, 1, EPI, true>(x, w, y, ws, M, N, K, st);
+        else if (slot_mt(M) == 2) launch_slots_mt<S, 2, EPI, true>(x, w, y, ws, M, N, K, st);
         else launch_slots_mt<S, 4, EPI, true>(x, w, y, ws, M, N, K, st);
     } else {
-        if (slot_mt(M) == 2) launch_slots_mt<S, 2, EPI, false>(x, w, y, ws, M, N, K, st);
+        if (slot_mt(M) == 1) launch_slots_mt<S, 1, EPI, false>(x, w, y, ws, M, N, K, st);
+        else if (slot_mt(M) == 2) launch_slots_mt<S, 2, EPI, false>(x, w, y, ws, M, N, K, st);
         else launch_slots_mt<S, 4, EPI, false>(x, w, y, ws, M, N, K, st);
     }
     return true;
@@ -359,7 +372,7 @@ using namespace bi;
 
 extern "C" size_t bi_matmul_ws_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t w_layout)
 {
-    if (M <= 16 || N < 1 || K < 1 || M > 64 || (w_layout != W_TRANS && w_layout != W_PACKED) || (dtype != BI_BF16 && dtype != BI_F16) ||
+    if (N < 1 || K < 1 || !slot_takes(M, N, K) || (w_layout != W_TRANS && w_layout != W_PACKED) || (dtype != BI_BF16 && dtype != BI_F16) ||
         cdiv(N, kSlotTileCols) > kSlotMaxTiles)
         return 0;
     return slot_ws_bytes(M, N, kDenseWaves);

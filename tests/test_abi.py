@@ -131,6 +131,9 @@ def test_matmul_ws_validation_and_workspace_size():
     assert need == 65536 + 32 * 8 * 8 * 4 * 4 * 64 * 4
     assert L.bi_matmul_ws_workspace_bytes(17, 4096, 4096, 0, 1) == 65536 + 32 * 8 * 8 * 2 * 4 * 64 * 4
     assert L.bi_matmul_ws_workspace_bytes(16, 4096, 4096, 0, 1) == 0      # short M: bi_matmul's kernels
+    assert L.bi_matmul_ws_workspace_bytes(8, 28672, 4096, 0, 1) == 0
+    # 8 < M <= 16 on a large weight: the slot form, 16-row tiles (1 KiB records)
+    assert L.bi_matmul_ws_workspace_bytes(9, 28672, 4096, 0, 1) == 65536 + 224 * 8 * 8 * 1 * 4 * 64 * 4
     assert L.bi_matmul_ws_workspace_bytes(64, 128 * 16385, 128, 0, 1) == 0   # beyond the counter area
     assert L.bi_matmul_ws_workspace_bytes(65, 4096, 4096, 0, 1) == 0      # long M: bi_matmul's kernels
     assert L.bi_matmul_ws_workspace_bytes(64, 4096, 4096, 2, 1) == 0      # f32

@@ -35,6 +35,9 @@ def same(a, b):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("M,N,K", [
     (1, 96, 128),          # M <= 16: bi_matmul's kernels
+    (9, 28672, 512),       # 8 < M <= 16 on a large weight: the slot form (16-row tiles)
+    (13, 6144, 4096),
+    (12, 6144, 4096),      # ... but not here: bi_matmul's kernels
     (17, 96, 128),         # one block: slots 1..7 own nothing
     (23, 1000, 896),       # 7 blocks, ragged column tile
     (16, 4096, 4096),
@@ -67,7 +70,7 @@ def test_decoder_shapes_and_every_m():
         x = rand((64, K), "bf16", seed=N + 1)
         ws = bi.matmul_workspace(64, N, K, device=dev())
         full = bi.matmul(x, w)
-        for M in (1, 2, 5, 16, 17, 31, 32, 33, 48, 63, 64):
+        for M in (1, 2, 5, 9, 12, 13, 16, 17, 31, 32, 33, 48, 63, 64):
             assert same(bi.matmul_ws(x[:M].contiguous(), w, ws), full[:M]), f"N={N} M={M}"
         assert same(bi.matmul_ws(x[40:41].contiguous(), w, ws), full[40:41])
     w = rand((4096, 14336), "bf16", seed=5, scale=0.02)
