@@ -241,6 +241,7 @@ def main():
         out["invariance_overhead"] = split_overhead(torch, bi, model, B, per_shape)
         out["qmatmul"] = qmatmul_decode(torch, bi, dev)
         out["row_ops"] = row_ops(torch, bi, model, B)
+        out["sweep"] = op_sweep(torch, bi, dev)
 
     if not args.no_cpu_baseline:
         n, secs, cores = cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids0, args.cpu_budget)
@@ -322,10 +323,10 @@ def split_overhead(torch, bi, model, B, per_shape):
     return res
 
 
-def _time_kernel(torch, bi, fn, reps):
-    """Mean kernel execution time (ms) of the single bi launch `fn` makes: a
-    start/stop event pair recorded by the launch itself (bi_time_next_launch),
-    so host-side launch overhead is not counted."""
+def _time_kernel(torch, bi, fn, reps, launches=1):
+    """Mean execution time (ms) of the `launches` bi kernels `fn` launches: a
+    start/stop event pair recorded by the launches themselves
+    (bi_time_next_launches), so host-side launch overhead is not counted."""
     L = bi.lib()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for s_, t_ in ev:
@@ -334,10 +335,64 @@ def _time_kernel(torch, bi, fn, reps):
     fn(0)
     torch.cuda.synchronize()
     for i, (s_, t_) in enumerate(ev):
-        L.bi_time_next_launch(ctypes.c_void_p(s_.cuda_event), ctypes.c_void_p(t_.cuda_event))
+        L.bi_time_next_launches(ctypes.c_void_p(s_.cuda_event), ctypes.c_void_p(t_.cuda_event), launches)
         fn(i)
     torch.cuda.synchronize()
     return float(np.mean([s_.elapsed_time(t_) for s_, t_ in ev]))
+
+
+def op_sweep(torch, bi, dev):
+    """The four reductions at the measurement shapes, cold (rotated copies of
+    the streamed operand, at least 512 MiB in all), kernel time:
+      dense (packed weights): the pages' 4096 x 4096 and the decoder's
+        projections at M in 1..64;
+      RMSNorm: H = 4096 at B in {1, 8, 64, 512, 4096};
+      SDPA (two launches: chunks and merge): B = 1, Q in {1, 8} at
+        Lk in {1028, 8196, 16388, 65540}, and B in {4, 16, 64} at Q = 1,
+        Lk = 8196."""
+    res = {"matmul": {}, "rmsnorm": {}, "sdpa": {}}
+    bf = torch.bfloat16
+    for (N, K) in ((4096, 4096), (6144, 4096), (28672, 4096), (4096, 14336), (32000, 4096)):
+        copies = max(2, -(-(512 << 20) // (N * K * 2)))
+        wps = [bi.pack_weights((torch.randn(N, K, device=dev) * 0.02).to(bf)) for _ in range(copies)]
+        ws = bi.matmul_workspace(64, N, K, device=dev)
+        for M in (1, 2, 4, 8, 16, 32, 64):
+            x = torch.randn(M, K, device=dev).to(bf)
+            y = torch.empty(M, N, dtype=bf, device=dev)
+            t = _time_kernel(torch, bi, lambda i: bi.matmul_ws(x, wps[i % copies], ws, out=y), reps=3 * copies)
+            gbs = 2 * (N * K + M * K + M * N) / (t * 1e-3) / 1e9
+            res["matmul"][f"{M}x{N}x{K}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1),
+                                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del wps
+    H = 4096
+    w = torch.ones(H, dtype=bf, device=dev)
+    for Bn in (1, 8, 64, 512, 4096):
+        copies = max(2, min(64, -(-(512 << 20) // (Bn * H * 2))))
+        xs = [torch.randn(Bn, H, device=dev).to(bf) for _ in range(copies)]
+        y = torch.empty(Bn, H, dtype=bf, device=dev)
+        t = _time_kernel(torch, bi, lambda i: bi.rmsnorm(xs[i % copies], w, out=y), reps=3 * copies)
+        gbs = (4 * Bn * H + 2 * H) / (t * 1e-3) / 1e9
+        res["rmsnorm"][f"{Bn}x{H}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del xs
+    Hq, Hkv, D = 32, 8, 128
+    cases = [(1, Q, Lk) for Lk in (1028, 8196, 16388, 65540) for Q in (1, 8)] + [(Bn, 1, 8196) for Bn in (4, 16, 64)]
+    for Bn, Q, Lk in cases:
+        kvb = 4 * Bn * Lk * Hkv * D
+        copies = max(2, min(16, -(-(512 << 20) // kvb)))
+        ks = [torch.randn(Bn, Hkv, Lk, D, device=dev).to(bf) for _ in range(copies)]
+        vs = [torch.randn(Bn, Hkv, Lk, D, device=dev).to(bf) for _ in range(copies)]
+        q = torch.randn(Bn, Q, Hq, D, device=dev).to(bf)
+        kv = torch.full((Bn,), Lk, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        wsd = torch.empty(bi.sdpa_workspace_bytes(Bn, Q, Lk, Hq, D), dtype=torch.uint8, device=dev)
+        t = _time_kernel(torch, bi, lambda i: bi.sdpa(q, ks[i % copies], vs[i % copies], kv, Lk, 0.088, True, out=o,
+                                                      ws=wsd, head_major=True), reps=3 * copies, launches=2)
+        gbs = (kvb + 4 * Bn * Q * Hq * D) / (t * 1e-3) / 1e9
+        res["sdpa"][f"B{Bn} Q{Q} Lk{Lk}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1),
+                                              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del ks, vs
+    torch.cuda.empty_cache()
+    return res
 
 
 def row_ops(torch, bi, model, B):

@@ -380,14 +380,17 @@ bi_status bi_rmsnorm_split(const void *x, const void *w, void *y, int64_t rows, 
                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Measurement hook (not part of any computation): the next kernel that a
- * dense matmul entry point (bi_matmul, bi_matmul_ws, bi_matmul_split's
- * partial pass) launches from the calling host thread records `start` when
- * it begins executing and `stop` when it ends (hipExtLaunchKernel), so
- * hipEventElapsedTime(start, stop) is that kernel's own duration without its
- * dispatch.  Either event may be NULL.  One launch consumes the setting.
+ * Measurement hooks (not part of any computation): the next kernel (or the
+ * next `count` kernels) that the library's entry points launch from the
+ * calling host thread carry `start`, recorded when the first begins
+ * executing, and `stop`, recorded when the last ends (hipExtLaunchKernel), so
+ * hipEventElapsedTime(start, stop) is their own execution time without the
+ * host's launch overhead.  Either event may be NULL; the launches consume the
+ * setting (bi_time_next_launches with count 0 clears it; count < 0:
+ * BI_ERR_SHAPE).
  * ------------------------------------------------------------------------ */
 bi_status bi_time_next_launch(hipEvent_t start, hipEvent_t stop);
+bi_status bi_time_next_launches(hipEvent_t start, hipEvent_t stop, int32_t count);
 
 /* ------------------------------------------------------------------------ */
 /* Human-readable status name (static string, never NULL). */

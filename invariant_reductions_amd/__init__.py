@@ -100,6 +100,8 @@ def lib():
         L.bi_rmsnorm_split_workspace_bytes.restype = SZ
         L.bi_time_next_launch.argtypes = [P, P]
         L.bi_time_next_launch.restype = ctypes.c_int32
+        L.bi_time_next_launches.argtypes = [P, P, I32]
+        L.bi_time_next_launches.restype = ctypes.c_int32
         L.bi_status_str.argtypes = [I32]
         L.bi_status_str.restype = ctypes.c_char_p
         L.bi_build_info.argtypes = []

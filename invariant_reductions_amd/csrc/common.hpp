@@ -106,8 +106,12 @@ inline bool host_aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // the library launches on this host thread records `start` as it begins
 // executing and `stop` as it ends (hipExtLaunchKernel), so the pair brackets
 // the kernel itself rather than its dispatch.
+// Measurement hook: the next `count` kernel launches of the calling thread
+// carry `start` (recorded as the first one starts) and `stop` (as the last
+// one ends), through the extended launch.
 struct LaunchTiming {
     hipEvent_t start = nullptr, stop = nullptr;
+    int count = 0;
 };
 inline LaunchTiming &launch_timing()
 {
@@ -119,10 +123,14 @@ inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, size
                           Args... args)
 {
     LaunchTiming &t = launch_timing();
-    if (t.start != nullptr || t.stop != nullptr) {
-        const LaunchTiming use = t;
-        t = LaunchTiming{};
-        hipExtLaunchKernelGGL(kernel, grid, block, smem, st, use.start, use.stop, 0, args...);
+    if (t.count > 0) {
+        hipEvent_t start = t.start, stop = nullptr;
+        t.start = nullptr;
+        if (--t.count == 0) {
+            stop = t.stop;
+            t = LaunchTiming{};
+        }
+        hipExtLaunchKernelGGL(kernel, grid, block, smem, st, start, stop, 0, args...);
     } else {
         hipLaunchKernelGGL(kernel, grid, block, smem, st, args...);
     }

@@ -514,7 +514,14 @@ extern "C" bi_status bi_matmul_split(const void *x, const void *w, void *y, int6
 
 extern "C" bi_status bi_time_next_launch(hipEvent_t start, hipEvent_t stop)
 {
-    bi::launch_timing() = bi::LaunchTiming{start, stop};
+    bi::launch_timing() = bi::LaunchTiming{start, stop, (start || stop) ? 1 : 0};
+    return BI_OK;
+}
+
+extern "C" bi_status bi_time_next_launches(hipEvent_t start, hipEvent_t stop, int32_t count)
+{
+    if (count < 0) return BI_ERR_SHAPE;
+    bi::launch_timing() = bi::LaunchTiming{start, stop, count};
     return BI_OK;
 }
 

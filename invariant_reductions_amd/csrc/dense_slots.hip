@@ -432,6 +432,6 @@ extern "C" bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, 
     dispatch_dense(x, w_il, gu, nullptr, M, 2 * F, K, dtype, w_layout, 1, stream);
     const int64_t n = M * F / 8;
     const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(n, 256), 65536);
-    hipLaunchKernelGGL(swiglu_il_kernel, dim3(blocks), dim3(256), 0, stream, (const uint16_t *)gu, (uint16_t *)a, M, F);
+    launch_kernel(swiglu_il_kernel, dim3(blocks), dim3(256), 0, stream, (const uint16_t *)gu, (uint16_t *)a, M, F);
     return launch_status();
 }

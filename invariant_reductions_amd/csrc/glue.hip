@@ -217,7 +217,7 @@ extern "C" bi_status bi_embed(const int32_t *ids, const void *table, void *out, 
     if (T < 1 || V < 1 || H < 1 || H % 8 || T > (1ll << 31) - 1) return BI_ERR_SHAPE;
     if (!host_aligned16(table) || !host_aligned16(out) || ((uintptr_t)ids & 3u)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(embed_kernel, dim3((unsigned)T), dim3(256), 0, stream, ids, (const uint4 *)table,
+    launch_kernel(embed_kernel, dim3((unsigned)T), dim3(256), 0, stream, ids, (const uint4 *)table,
                        (uint4 *)out, T, V, H / 8);
     return launch_status();
 }
@@ -238,11 +238,11 @@ extern "C" bi_status bi_rope_kv_write(const void *qkv, void *q_out, void *kc, vo
     const bool vec = (D / 2) % 8 == 0;
     const int64_t n = B * Q * (Hq + 2 * Hkv) * (vec ? D / 16 : D / 2);
     if (vec)
-        hipLaunchKernelGGL(rope_kv_kernel<8>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)qkv,
+        launch_kernel(rope_kv_kernel<8>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)qkv,
                            (uint16_t *)q_out, (uint16_t *)kc, (uint16_t *)vc, kv_len, cos_t, sin_t, B, Q, Lcap,
                            Hq, Hkv, D, max_pos, kv_layout);
     else
-        hipLaunchKernelGGL(rope_kv_kernel<1>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)qkv,
+        launch_kernel(rope_kv_kernel<1>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)qkv,
                            (uint16_t *)q_out, (uint16_t *)kc, (uint16_t *)vc, kv_len, cos_t, sin_t, B, Q, Lcap,
                            Hq, Hkv, D, max_pos, kv_layout);
     return launch_status();
@@ -255,10 +255,10 @@ extern "C" bi_status bi_silu_mul(const void *gu, void *out, int64_t rows, int64_
     if (!host_aligned16(gu) || !host_aligned16(out)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
     if (F % 8 == 0)
-        hipLaunchKernelGGL(silu_mul_kernel<true>, dim3(grid_for(rows * F / 8, 256)), dim3(256), 0, stream,
+        launch_kernel(silu_mul_kernel<true>, dim3(grid_for(rows * F / 8, 256)), dim3(256), 0, stream,
                            (const uint16_t *)gu, (uint16_t *)out, rows, F);
     else
-        hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(grid_for(rows * F, 256)), dim3(256), 0, stream,
+        launch_kernel(silu_mul_kernel<false>, dim3(grid_for(rows * F, 256)), dim3(256), 0, stream,
                            (const uint16_t *)gu, (uint16_t *)out, rows, F);
     return launch_status();
 }
@@ -270,10 +270,10 @@ extern "C" bi_status bi_add(const void *a, const void *b, void *out, int64_t n, 
     if (!host_aligned16(a) || !host_aligned16(b) || !host_aligned16(out)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
     if (n % 8 == 0)
-        hipLaunchKernelGGL(add_kernel<true>, dim3(grid_for(n / 8, 256)), dim3(256), 0, stream, (const uint16_t *)a,
+        launch_kernel(add_kernel<true>, dim3(grid_for(n / 8, 256)), dim3(256), 0, stream, (const uint16_t *)a,
                            (const uint16_t *)b, (uint16_t *)out, n);
     else
-        hipLaunchKernelGGL(add_kernel<false>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)a,
+        launch_kernel(add_kernel<false>, dim3(grid_for(n, 256)), dim3(256), 0, stream, (const uint16_t *)a,
                            (const uint16_t *)b, (uint16_t *)out, n);
     return launch_status();
 }
@@ -286,10 +286,10 @@ static bi_status run_argmax(const void *x, int32_t *idx, int32_t *ids_next, int3
     if (!host_aligned16(x) || (((uintptr_t)idx | (uintptr_t)ids_next | (uintptr_t)kv_len) & 3u)) return BI_ERR_ALIGN;
     (void)hipGetLastError();
     if (cols % 8 == 0)
-        hipLaunchKernelGGL(argmax_kernel<true>, dim3((unsigned)rows), dim3(kArgmaxThreads), 0, stream,
+        launch_kernel(argmax_kernel<true>, dim3((unsigned)rows), dim3(kArgmaxThreads), 0, stream,
                            (const uint16_t *)x, idx, rows, cols, ids_next, kv_len);
     else
-        hipLaunchKernelGGL(argmax_kernel<false>, dim3((unsigned)rows), dim3(kArgmaxThreads), 0, stream,
+        launch_kernel(argmax_kernel<false>, dim3((unsigned)rows), dim3(kArgmaxThreads), 0, stream,
                            (const uint16_t *)x, idx, rows, cols, ids_next, kv_len);
     return launch_status();
 }

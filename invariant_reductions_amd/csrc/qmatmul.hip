@@ -656,10 +656,10 @@ extern "C" bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, co
     const uint32_t *w = wq;
     const uint16_t *bz = (const uint16_t *)biases;
     uint32_t *o = (uint32_t *)wqp;
-    if (qmode == BI_NVFP4) hipLaunchKernelGGL((pack_q_kernel<BI_NVFP4, 16>), grid, block, 0, stream, w, scales, bz, o, N, K);
-    else if (qmode == BI_MXFP4) hipLaunchKernelGGL((pack_q_kernel<BI_MXFP4, 32>), grid, block, 0, stream, w, scales, bz, o, N, K);
-    else if (group_size == 32) hipLaunchKernelGGL((pack_q_kernel<BI_AFFINE, 32>), grid, block, 0, stream, w, scales, bz, o, N, K);
-    else if (group_size == 64) hipLaunchKernelGGL((pack_q_kernel<BI_AFFINE, 64>), grid, block, 0, stream, w, scales, bz, o, N, K);
-    else hipLaunchKernelGGL((pack_q_kernel<BI_AFFINE, 128>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    if (qmode == BI_NVFP4) launch_kernel((pack_q_kernel<BI_NVFP4, 16>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    else if (qmode == BI_MXFP4) launch_kernel((pack_q_kernel<BI_MXFP4, 32>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    else if (group_size == 32) launch_kernel((pack_q_kernel<BI_AFFINE, 32>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    else if (group_size == 64) launch_kernel((pack_q_kernel<BI_AFFINE, 64>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    else launch_kernel((pack_q_kernel<BI_AFFINE, 128>), grid, block, 0, stream, w, scales, bz, o, N, K);
     return launch_status();
 }

@@ -223,10 +223,10 @@ static void launch_rmsnorm(const void *x, const void *r, void *xo, const void *w
     dim3 grid((unsigned)cdiv(rows, kNormRowsPerBlock)), block(kNormRowsPerBlock * kWave);
     const T *xt = (const T *)x, *rt = (const T *)r, *wt = (const T *)w;
     T *xot = (T *)xo, *yt = (T *)y;
-    if (vec && cached) hipLaunchKernelGGL((rmsnorm_kernel<S, true, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
-    else if (vec) hipLaunchKernelGGL((rmsnorm_kernel<S, true, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
-    else if (cached) hipLaunchKernelGGL((rmsnorm_kernel<S, false, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
-    else hipLaunchKernelGGL((rmsnorm_kernel<S, false, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
+    if (vec && cached) launch_kernel((rmsnorm_kernel<S, true, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
+    else if (vec) launch_kernel((rmsnorm_kernel<S, true, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
+    else if (cached) launch_kernel((rmsnorm_kernel<S, false, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
+    else launch_kernel((rmsnorm_kernel<S, false, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
 }
 
 template <typename S>
@@ -236,11 +236,11 @@ static void launch_rmsnorm_split(const void *x, const void *w, void *y, float *p
     using T = typename S::store_t;
     constexpr int E = S::kElemsPer16B;
     if ((H % E) == 0 && host_aligned16(x) && host_aligned16(w) && host_aligned16(y)) {
-        hipLaunchKernelGGL((rmsnorm_split_partial<S, true>), dim3((unsigned)rows, (unsigned)splits), dim3(kWave), 0, st, (const T *)x, part, rows, H, splits);
-        hipLaunchKernelGGL((rmsnorm_split_finish<S, true>), dim3((unsigned)cdiv(rows, kNormRowsPerBlock)), dim3(kNormRowsPerBlock * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, rows, H, eps, splits);
+        launch_kernel((rmsnorm_split_partial<S, true>), dim3((unsigned)rows, (unsigned)splits), dim3(kWave), 0, st, (const T *)x, part, rows, H, splits);
+        launch_kernel((rmsnorm_split_finish<S, true>), dim3((unsigned)cdiv(rows, kNormRowsPerBlock)), dim3(kNormRowsPerBlock * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, rows, H, eps, splits);
     } else {
-        hipLaunchKernelGGL((rmsnorm_split_partial<S, false>), dim3((unsigned)rows, (unsigned)splits), dim3(kWave), 0, st, (const T *)x, part, rows, H, splits);
-        hipLaunchKernelGGL((rmsnorm_split_finish<S, false>), dim3((unsigned)cdiv(rows, kNormRowsPerBlock)), dim3(kNormRowsPerBlock * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, rows, H, eps, splits);
+        launch_kernel((rmsnorm_split_partial<S, false>), dim3((unsigned)rows, (unsigned)splits), dim3(kWave), 0, st, (const T *)x, part, rows, H, splits);
+        launch_kernel((rmsnorm_split_finish<S, false>), dim3((unsigned)cdiv(rows, kNormRowsPerBlock)), dim3(kNormRowsPerBlock * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, rows, H, eps, splits);
     }
 }
 

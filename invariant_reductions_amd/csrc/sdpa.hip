@@ -413,10 +413,10 @@ static void launch_attn(const void *q, const void *k, const void *v, void *o, co
     // workgroups per CU, a multiple of 8 so that a workgroup stays on one XCD
     const int64_t nid = cdiv(sh.B * sh.nchunks, 8) * 8 * sh.Hkv;
     const int64_t grid = std::min<int64_t>(nid, (int64_t)device_cu_count() * 2 / 8 * 8);
-    hipLaunchKernelGGL((attn_chunk_kernel<S>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st,
+    launch_kernel((attn_chunk_kernel<S>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, part, sh, nid);
     const size_t smem = (size_t)sh.nchunks * 2 * sizeof(float);
-    hipLaunchKernelGGL((attn_merge_kernel<S>), dim3((unsigned)(sh.B * sh.Q * sh.Hq)), dim3(kHeadDim), smem, st,
+    launch_kernel((attn_merge_kernel<S>), dim3((unsigned)(sh.B * sh.Q * sh.Hq)), dim3(kHeadDim), smem, st,
                        (const float *)part, kv_len, (uint16_t *)o, sh, chunk);
 }
 

@@ -239,6 +239,8 @@ def test_time_next_launch_is_host_only():
     """Setting and clearing the one-shot timing hook touches no device."""
     L = bi.lib()
     assert L.bi_time_next_launch(None, None) == OK
+    assert L.bi_time_next_launches(None, None, 0) == OK
+    assert L.bi_time_next_launches(None, None, -1) == SHAPE
 
 
 def test_glue_validation():
