@@ -111,24 +111,47 @@ def pack_nibbles(codes: np.ndarray) -> np.ndarray:
     return out
 
 
-def quantize_affine(w: np.ndarray, group_size: int):
-    """Min-max affine 4-bit quantization along the last axis of fp32 `w`
-    [rows, cols]: per group s = (max-min)/15 and b = min, both rounded to
-    binary16; q = clamp(rint((w - b)/s), 0, 15), q = 0 where s == 0.
-    Returns (wq uint32 [rows, cols/8], scales f16 bits, biases f16 bits)."""
+def pack_bits(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[rows, cols] codes 0..2^bits-1 -> [rows, cols*bits/32] uint32: each row
+    a little-endian bit stream, code j in bits [j*bits, (j+1)*bits), stream bit
+    i in bit i % 32 of word i / 32.  At bits = 4 this equals pack_nibbles."""
+    codes = np.asarray(codes, dtype=np.uint64)
+    rows, cols = codes.shape
+    assert (cols * bits) % 32 == 0 and 1 <= bits <= 8
+    assert int(codes.max(initial=0)) < (1 << bits)
+    # 32 codes of `bits` bits fill exactly `bits` words
+    c = codes.reshape(rows, cols // 32, 32)
+    out = np.zeros((rows, cols // 32, bits), np.uint32)
+    for j in range(32):
+        o = j * bits
+        w, sh = o // 32, o % 32
+        v = c[:, :, j]
+        out[:, :, w] |= ((v << np.uint64(sh)) & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+        if sh + bits > 32:
+            out[:, :, w + 1] |= (v >> np.uint64(32 - sh)).astype(np.uint32)
+    return out.reshape(rows, cols * bits // 32)
+
+
+def quantize_affine(w: np.ndarray, group_size: int, bits: int = 4):
+    """Min-max affine quantization to `bits` bits along the last axis of fp32
+    `w` [rows, cols]: with L = 2^bits - 1, per group s = (max-min)/L and b =
+    min, both rounded to binary16; q = clamp(rint((w - b)/s), 0, L), q = 0
+    where s == 0.  Returns (wq uint32 [rows, cols*bits/32], scales f16 bits,
+    biases f16 bits)."""
     w = np.asarray(w, np.float32)
     rows, cols = w.shape
     assert cols % group_size == 0
+    L = (1 << bits) - 1
     g = w.reshape(rows, cols // group_size, group_size).astype(np.float64)
     lo, hi = g.min(axis=2), g.max(axis=2)
-    s16 = ((hi - lo) / 15.0).astype(np.float16)
+    s16 = ((hi - lo) / L).astype(np.float16)
     b16 = lo.astype(np.float16)
     s = s16.astype(np.float64)[:, :, None]
     b = b16.astype(np.float64)[:, :, None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.where(s > 0, np.rint((g - b) / np.where(s > 0, s, 1.0)), 0.0)
-    q = np.clip(q, 0, 15).astype(np.uint32).reshape(rows, cols)
-    return pack_nibbles(q), s16.view(np.uint16), b16.view(np.uint16)
+    q = np.clip(q, 0, L).astype(np.uint32).reshape(rows, cols)
+    return pack_bits(q, bits), s16.view(np.uint16), b16.view(np.uint16)
 
 
 _E2M1_GRID = None
@@ -211,15 +234,38 @@ def quantize_mxfp4(w: np.ndarray):
     return pack_nibbles(codes), e.astype(np.uint8)
 
 
+def quantize_mxfp8(w: np.ndarray):
+    """mxfp8-style quantization along the last axis of fp32 `w` [rows, cols]:
+    per 32 elements one e8m0 scale 2^(e - 127) with e = floor(log2(amax)) - 8
+    + 127 (the largest e4m3 magnitude is 448 = 1.75 * 2^8), clamped to [0,
+    254]; codes = e4m3(w / scale), round to nearest even, saturating; a zero
+    group gets e = 0 and zero codes.  Returns (wq uint32 [rows, cols/4], the
+    codes as the row's bytes in order, and scale bytes uint8 [rows, cols/32])."""
+    w = np.asarray(w, np.float32)
+    rows, cols = w.shape
+    assert cols % 32 == 0
+    g = w.reshape(rows, cols // 32, 32).astype(np.float64)
+    amax = np.abs(g).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8 + 127, 0)
+    e = np.clip(e, 0, 254).astype(np.int64)
+    scale = np.ldexp(1.0, (e - 127).astype(np.int32))
+    r = np.where(amax[:, :, None] > 0, g / scale[:, :, None], 0.0)
+    codes = encode_e4m3(r.astype(np.float32)).reshape(rows, cols)
+    return pack_bits(codes.astype(np.uint32), 8), e.astype(np.uint8)
+
+
 def qmatmul_case(M: int, K: int, N: int, qmode: str, group_size: int, transposed: bool = True,
-                 seed: int = 0):
+                 seed: int = 0, bits: int = 4):
     """W ~ N(0,1) drawn first, quantized along the matrix's stored minor axis
     ([N,K] along K when transposed, [K,N] along N when natural), then
-    x [M,K] ~ N(0,1) as binary16 bits.  Returns (x, wq, scales, biases)."""
+    x [M,K] ~ N(0,1) as binary16 bits.  `bits` is the affine code width (2 to
+    8); the fp modes have fixed widths (nvfp4 and mxfp4 4, mxfp8 8).  Returns
+    (x, wq, scales, biases)."""
     rng = np.random.default_rng(seed)
     w = rng.standard_normal((N, K) if transposed else (K, N)).astype(np.float32)
     if qmode == "affine":
-        wq, s, b = quantize_affine(w, group_size)
+        wq, s, b = quantize_affine(w, group_size, bits)
     elif qmode == "nvfp4":
         assert group_size == 16
         wq, s = quantize_nvfp4(w)
@@ -228,15 +274,15 @@ def qmatmul_case(M: int, K: int, N: int, qmode: str, group_size: int, transposed
         assert group_size == 32
         wq, s = quantize_mxfp4(w)
         b = None
+    elif qmode == "mxfp8":
+        assert group_size == 32
+        wq, s = quantize_mxfp8(w)
+        b = None
     else:
         raise ValueError(qmode)
     x = normal(rng, (M, K), dtype="f16")
     return x, wq, s, b
 
-
-# --------------------------------------------------------------------------
-# decoder (Llama-style) buffers
-# --------------------------------------------------------------------------
 
 def rope_tables(max_pos: int, head_dim: int, theta: float = 10000.0):
     """cos/sin [max_pos, head_dim/2] of pos * theta^(-2i/head_dim), computed in

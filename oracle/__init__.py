@@ -35,7 +35,7 @@ _SRC = os.path.join(_HERE, "bi_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 BF16, F16, F32 = 0, 1, 2
-AFFINE, NVFP4, MXFP4 = 0, 1, 2
+AFFINE, NVFP4, MXFP4, MXFP8 = 0, 1, 2, 3
 _DT = {"bf16": BF16, "f16": F16, "f32": F32}
 
 
@@ -76,8 +76,8 @@ def lib():
         L.bo_fold_pairwise_f32.argtypes = [P, I64]; L.bo_fold_pairwise_f32.restype = ctypes.c_float
         L.bo_fold_split_f32.argtypes = [P, I64, I64]; L.bo_fold_split_f32.restype = ctypes.c_float
         L.bo_matmul.argtypes = [P, P, P, I64, I64, I64, I32, I32]
-        L.bo_dequantize.argtypes = [P, P, P, P, I64, I64, I32, I32]
-        L.bo_qmatmul.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, I32]
+        L.bo_dequantize.argtypes = [P, P, P, P, I64, I64, I32, I32, I32]
+        L.bo_qmatmul.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, I32, I32]
         L.bo_rmsnorm.argtypes = [P, P, P, P, I64, I64, ctypes.c_float, I32]
         L.bo_sdpa.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, I32]
         L.bo_rope.argtypes = [P, P, P, P, P, I64, I64, I64, I32]
@@ -175,19 +175,20 @@ def matmul(x: np.ndarray, w: np.ndarray, dtype, w_transposed: bool = True) -> np
     return y
 
 
-def dequantize(wq, scales, biases, rows: int, cols: int, qmode: int, group_size: int) -> np.ndarray:
-    """Packed 4-bit weights -> binary16 bits [rows, cols]."""
+def dequantize(wq, scales, biases, rows: int, cols: int, qmode: int, group_size: int, bits: int = 4) -> np.ndarray:
+    """Packed `bits`-bit weights (each row a little-endian bit stream of codes
+    in 32-bit words) -> binary16 bits [rows, cols]."""
     wq = np.ascontiguousarray(wq, dtype=np.uint32)
     scales = np.ascontiguousarray(scales)
     b = None if biases is None else np.ascontiguousarray(biases, dtype=np.uint16)
     out = np.empty((rows, cols), np.uint16)
     _check(lib().bo_dequantize(_p(wq), _p(scales), None if b is None else _p(b), _p(out),
-                               rows, cols, qmode, group_size), "dequantize")
+                               rows, cols, qmode, bits, group_size), "dequantize")
     return out
 
 
 def qmatmul(x, wq, scales, biases, M: int, N: int, K: int, qmode: int, group_size: int,
-            w_transposed: bool = True) -> np.ndarray:
+            w_transposed: bool = True, bits: int = 4) -> np.ndarray:
     """y = x @ dequantize(W)^T with x binary16 bits [M,K]; fp32 [M,N]."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     wq = np.ascontiguousarray(wq, dtype=np.uint32)
@@ -195,7 +196,7 @@ def qmatmul(x, wq, scales, biases, M: int, N: int, K: int, qmode: int, group_siz
     b = None if biases is None else np.ascontiguousarray(biases, dtype=np.uint16)
     y = np.empty((M, N), np.float32)
     _check(lib().bo_qmatmul(_p(x), _p(wq), _p(scales), None if b is None else _p(b), _p(y),
-                            M, N, K, qmode, group_size, int(w_transposed)), "qmatmul")
+                            M, N, K, qmode, bits, group_size, int(w_transposed)), "qmatmul")
     return y
 
 

@@ -34,7 +34,7 @@
 #endif
 
 enum { BO_BF16 = 0, BO_F16 = 1, BO_F32 = 2 };
-enum { BO_AFFINE = 0, BO_NVFP4 = 1, BO_MXFP4 = 2 };
+enum { BO_AFFINE = 0, BO_NVFP4 = 1, BO_MXFP4 = 2, BO_MXFP8 = 3 };
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                           */
@@ -270,43 +270,61 @@ int bo_matmul(const void *x, const void *w, float *y, int64_t M, int64_t N, int6
 /* Group-quantized weights: dequantize, then the dense matmul above.         */
 /* ------------------------------------------------------------------------ */
 
-/* Packed layout: 8 four-bit codes per little-endian 32-bit word; the element
- * with the lowest index along the quantized axis sits in bits 0..3.
+/* Packed layout: every stored row is a little-endian bit stream of `bits`-bit
+ * codes in 32-bit words: code j of the row occupies bits [j*bits, (j+1)*bits)
+ * of the stream, bit i of the stream being bit i % 32 of word i / 32.  At 4
+ * bits this is 8 codes per word with the lowest index in bits 0..3; at 8 bits
+ * the codes are the row's bytes in order.
  * rows x cols is the weight matrix as stored, quantized along cols:
  *   transposed weights [N,K]: rows = N, cols = K;
  *   natural weights    [K,N]: rows = K, cols = N.
- * wq: [rows, cols/8] words; scales: [rows, cols/gs]; biases: [rows, cols/gs].
- * Affine: w = s*q + b with q in 0..15 and binary16 s, b.  The product s*q is
- *   exact in fp32; the add rounds once in fp32; the result is rounded to
- *   binary16 (the activation type the weights are multiplied against).
+ * wq: [rows, cols*bits/32] words; scales: [rows, cols/gs]; biases: [rows, cols/gs].
+ * Affine (2 to 8 bits): w = s*q + b with q in 0..2^bits-1 and binary16 s, b.
+ *   The product s*q is exact in fp32 (at most 11 + 8 significant bits); the
+ *   add rounds once in fp32; the result is rounded to binary16 (the
+ *   activation type the weights are multiplied against).
  * NVFP4: w = e2m1(q) * e4m3(s), one scale byte per 16 elements; the product
  *   is exact in fp32 and exactly representable in binary16.
  * MXFP4: w = e2m1(q) * e8m0(s), one scale byte per 32 elements; the product is
  *   exact in fp32 (a power-of-two scaling of a 2-bit significand) and is then
  *   rounded to binary16 (values beyond its range become +-inf, tiny ones
  *   round to subnormals or zero).
+ * MXFP8: w = e4m3(q) * e8m0(s), one byte code per element and one scale byte
+ *   per 32; the product is exact in fp32 (a 4-bit significand scaled by a
+ *   power of two, never below 2^-136) or overflows to inf, and is then
+ *   rounded to binary16 as for MXFP4.
  * Output: binary16 bits, same [rows, cols] layout as the stored matrix. */
 int bo_dequantize(const uint32_t *wq, const void *scales, const uint16_t *biases,
-                  uint16_t *out, int64_t rows, int64_t cols, int qmode, int group_size)
+                  uint16_t *out, int64_t rows, int64_t cols, int qmode, int bits, int group_size)
 {
     if (!wq || !scales || !out || rows < 0 || cols < 0) return -1;
     if (qmode == BO_AFFINE) {
+        if (bits < 2 || bits > 8) return -3;
         if (group_size != 32 && group_size != 64 && group_size != 128) return -3;
         if (!biases) return -1;
     } else if (qmode == BO_NVFP4) {
-        if (group_size != 16) return -3;
+        if (bits != 4 || group_size != 16) return -3;
     } else if (qmode == BO_MXFP4) {
-        if (group_size != 32) return -3;
+        if (bits != 4 || group_size != 32) return -3;
+    } else if (qmode == BO_MXFP8) {
+        if (bits != 8 || group_size != 32) return -3;
     } else {
         return -1;
     }
-    if (cols % group_size) return -3;
-    const int64_t words = cols / 8, groups = cols / group_size;
+    if (cols % group_size || (cols * bits) % 32) return -3;
+    const int64_t words = cols * bits / 32, groups = cols / group_size;
+    const uint32_t mask = (1u << bits) - 1u;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t c = 0; c < cols; ++c) {
-            uint32_t word = wq[r * words + c / 8];
-            uint32_t q = (word >> (4 * (c % 8))) & 0xfu;
+            /* the code's bits, one at a time from the row's stream */
+            uint32_t q = 0;
+            for (int i = 0; i < bits; ++i) {
+                int64_t bit = c * bits + i;
+                uint32_t word = wq[r * words + bit / 32];
+                q |= ((word >> (bit % 32)) & 1u) << i;
+            }
+            q &= mask;
             int64_t g = r * groups + c / group_size;
             float v;
             if (qmode == BO_AFFINE) {
@@ -316,8 +334,10 @@ int bo_dequantize(const uint32_t *wq, const void *scales, const uint16_t *biases
                 v = sq + b;
             } else if (qmode == BO_NVFP4) {
                 v = bo_e2m1_to_f32((uint8_t)q) * bo_e4m3_to_f32(((const uint8_t *)scales)[g]);
-            } else {
+            } else if (qmode == BO_MXFP4) {
                 v = bo_e2m1_to_f32((uint8_t)q) * bo_e8m0_to_f32(((const uint8_t *)scales)[g]);
+            } else {
+                v = bo_e4m3_to_f32((uint8_t)q) * bo_e8m0_to_f32(((const uint8_t *)scales)[g]);
             }
             out[r * cols + c] = bo_f32_to_f16(v);
         }
@@ -328,13 +348,13 @@ int bo_dequantize(const uint32_t *wq, const void *scales, const uint16_t *biases
 /* y = x @ dequantize(W)^T (transposed) or x @ dequantize(W) (natural);
  * x binary16 [M,K]; y fp32 [M,N]. */
 int bo_qmatmul(const uint16_t *x, const uint32_t *wq, const void *scales, const uint16_t *biases,
-               float *y, int64_t M, int64_t N, int64_t K, int qmode, int group_size, int w_transposed)
+               float *y, int64_t M, int64_t N, int64_t K, int qmode, int bits, int group_size, int w_transposed)
 {
     if (!x || !y || M < 0 || N < 0 || K < 0) return -1;
     int64_t rows = w_transposed ? N : K, cols = w_transposed ? K : N;
     uint16_t *wd = (uint16_t *)malloc((size_t)(rows * cols > 0 ? rows * cols : 1) * 2);
     if (!wd) return -2;
-    int rc = bo_dequantize(wq, scales, biases, wd, rows, cols, qmode, group_size);
+    int rc = bo_dequantize(wq, scales, biases, wd, rows, cols, qmode, bits, group_size);
     if (rc == 0) rc = bo_matmul(x, wd, y, M, N, K, BO_F16, w_transposed);
     free(wd);
     return rc;

@@ -337,6 +337,121 @@ def test_mxfp4_grid_values_round_trip_and_unit_scale_is_exact():
     assert np.array_equal(y.astype(np.float64), exact)
 
 
+def _stream_words(codes, bits):
+    """Row bit streams built with numpy.packbits: code j's bit i is stream
+    bit j*bits + i, eight stream bits per byte (lowest first), four bytes per
+    little-endian word."""
+    rows, cols = codes.shape
+    bitmat = (codes[:, :, None].astype(np.uint32) >> np.arange(bits, dtype=np.uint32)) & 1
+    by = np.packbits(bitmat.reshape(rows, cols * bits).astype(np.uint8), axis=1, bitorder="little")
+    return np.ascontiguousarray(by).view("<u4").astype(np.uint32)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("transposed", [True, False])
+def test_affine_any_width_unit_scale_is_exact(bits, transposed):
+    """Scale 1 and bias -2^(bits-1): every dequantized value is its code minus
+    the bias, read from a bit stream that numpy.packbits laid out; with integer
+    x the product is exact.  At 4 bits the stream is the nibble layout, at 8
+    bits it is the row's bytes."""
+    rng = np.random.default_rng(100 + bits)
+    M, N, K, gs = 5, 96, 256, 32
+    rows, cols = (N, K) if transposed else (K, N)
+    codes = rng.integers(0, 1 << bits, size=(rows, cols)).astype(np.uint32)
+    wq = _stream_words(codes, bits)
+    assert np.array_equal(wq, inputs.pack_bits(codes, bits))
+    if bits == 4:
+        assert np.array_equal(wq, inputs.pack_nibbles(codes))
+    if bits == 8:
+        assert np.array_equal(wq.view(np.uint8), codes.astype(np.uint8))
+    half = 1 << (bits - 1)
+    s = np.full((rows, cols // gs), 0x3C00, np.uint16)                          # binary16 1.0
+    b = np.full((rows, cols // gs), np.float16(-half).view(np.uint16), np.uint16)
+    deq = oracle.dequantize(wq, s, b, rows, cols, oracle.AFFINE, gs, bits=bits)
+    assert np.array_equal(inputs.from_storage(deq, "f16"), codes.astype(np.float32) - half)
+    x = inputs.integer_values(rng, (M, K), -4, 4, "f16")
+    wmat = codes.astype(np.int64) - half
+    wmat = wmat if transposed else wmat.T
+    exact = inputs.from_storage(x, "f16").astype(np.int64) @ wmat.T
+    y = oracle.qmatmul(x, wq, s, b, M, N, K, oracle.AFFINE, gs, transposed, bits=bits)
+    assert np.array_equal(y.astype(np.int64), exact)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 5, 6, 7, 8])
+def test_affine_any_width_error_bound(bits):
+    """Min-max quantization to `bits` bits comes back within half a step
+    (plus binary16 rounding of s, b and the result)."""
+    rng = np.random.default_rng(bits)
+    w = rng.standard_normal((32, 512)).astype(np.float32)
+    for gs in (32, 64, 128):
+        wq, s, b = inputs.quantize_affine(w, gs, bits)
+        deq = inputs.from_storage(oracle.dequantize(wq, s, b, 32, 512, oracle.AFFINE, gs, bits=bits), "f16")
+        sv = np.repeat(inputs.from_storage(s, "f16"), gs, axis=1)
+        L = (1 << bits) - 1
+        bound = 0.5 * sv + 2.0 ** -10 * (np.abs(w) + (L + 1) * sv) + 2.0 ** -11 * np.abs(deq)
+        assert np.all(np.abs(deq - w) <= bound), (bits, gs)
+
+
+def test_affine_rejects_widths_outside_2_to_8():
+    wq = np.zeros((4, 32), np.uint32)
+    s = np.zeros((4, 1), np.uint16)
+    for bits in (1, 9):
+        with pytest.raises(ValueError):
+            oracle.dequantize(wq, s, s, 4, 32, oracle.AFFINE, 32, bits=bits)
+
+
+def test_mxfp8_spec_values_at_unit_scale():
+    """Scale byte 127 (2^0): the dequantized codes are the OCP e4m3 values."""
+    g = golden("ocp_fp4_fp8_values.json")["e4m3"]
+    items = [(int(k, 16), v) for k, v in g.items() if k != "nan_codes"]
+    codes = np.zeros((1, 32), np.uint32)
+    codes[0, :len(items)] = [c for c, _ in items]
+    codes[0, len(items):len(items) + 2] = [int(c, 16) for c in g["nan_codes"]]
+    wq = _stream_words(codes, 8)
+    deq = inputs.from_storage(oracle.dequantize(wq, np.array([[127]], np.uint8), None, 1, 32, oracle.MXFP8, 32,
+                                                bits=8), "f16")
+    assert np.array_equal(deq[0, :len(items)], np.array([v for _, v in items], np.float32))
+    assert np.all(np.isnan(deq[0, len(items):len(items) + 2]))
+
+
+def test_mxfp8_codes_times_scales_round_once_to_binary16():
+    """Every (code, scale) pair: the e4m3 value (torch's decode) times
+    2^(e-127), exact in fp64, rounded once to binary16 by numpy; NaN codes and
+    the NaN scale 0xFF give NaN."""
+    e = np.arange(256, dtype=np.uint8)
+    allc = np.arange(256, dtype=np.uint32)
+    rows = []
+    for half in range(8):                                   # 256 codes = 8 groups of 32
+        codes = np.tile(allc[half * 32:(half + 1) * 32], (e.size, 1))
+        deq = oracle.dequantize(_stream_words(codes, 8), e[:, None].copy(), None, e.size, 32, oracle.MXFP8, 32,
+                                bits=8)
+        rows.append(inputs.from_storage(deq, "f16"))
+    got = np.concatenate(rows, axis=1)                      # [scale, code]
+    val = torch.from_numpy(allc.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = (val[None, :] * np.ldexp(1.0, e.astype(np.int32) - 127)[:, None]).astype(np.float16)
+    want[255, :] = np.nan
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan].astype(np.float32))
+
+
+def test_mxfp8_grid_values_round_trip():
+    """Weights on the e4m3 grid times 2^k, group maximum 448 * 2^k, quantize to
+    scale 2^k and come back exactly."""
+    rng = np.random.default_rng(8)
+    vals = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    finite = np.flatnonzero(np.isfinite(vals))
+    codes = rng.choice(finite, size=(16, 256))
+    codes[:, ::32] = 0x7E                                   # 448
+    k = rng.integers(-10, 4, size=(16, 8))
+    w = (vals[codes] * np.repeat(2.0 ** k, 32, axis=1)).astype(np.float32)
+    wq, s = inputs.quantize_mxfp8(w)
+    assert np.array_equal(s.astype(np.int64), k + 127)
+    deq = inputs.from_storage(oracle.dequantize(wq, s, None, 16, 256, oracle.MXFP8, 32, bits=8), "f16")
+    assert np.array_equal(deq, w)
+
+
 @pytest.mark.parametrize("gs", [32, 64, 128])
 def test_affine_quantize_dequantize_error_bound(gs):
     rng = np.random.default_rng(9)
@@ -364,16 +479,17 @@ def test_nvfp4_grid_values_round_trip():
     assert np.array_equal(deq, w)
 
 
-@pytest.mark.parametrize("qmode,gs", [("affine", 32), ("affine", 128), ("nvfp4", 16), ("mxfp4", 32)])
+@pytest.mark.parametrize("qmode,gs,bits", [("affine", 32, 4), ("affine", 128, 4), ("nvfp4", 16, 4), ("mxfp4", 32, 4),
+                                           ("affine", 64, 3), ("affine", 32, 8), ("mxfp8", 32, 8)])
 @pytest.mark.parametrize("transposed", [True, False])
-def test_qmatmul_tiny_brute_force(qmode, gs, transposed):
+def test_qmatmul_tiny_brute_force(qmode, gs, bits, transposed):
     """Tiny shapes, every output summed in fp64 from the dequantized weights:
     the oracle lies within the fp32 rounding bound."""
     M, K, N = 3, 256, 128
-    x, wq, s, b = inputs.qmatmul_case(M, K, N, qmode, gs, transposed, seed=2)
-    qm = {"affine": oracle.AFFINE, "nvfp4": oracle.NVFP4, "mxfp4": oracle.MXFP4}[qmode]
+    x, wq, s, b = inputs.qmatmul_case(M, K, N, qmode, gs, transposed, seed=2, bits=bits)
+    qm = {"affine": oracle.AFFINE, "nvfp4": oracle.NVFP4, "mxfp4": oracle.MXFP4, "mxfp8": oracle.MXFP8}[qmode]
     rows, cols = (N, K) if transposed else (K, N)
-    deq = inputs.from_storage(oracle.dequantize(wq, s, b, rows, cols, qm, gs), "f16").astype(np.float64)
+    deq = inputs.from_storage(oracle.dequantize(wq, s, b, rows, cols, qm, gs, bits=bits), "f16").astype(np.float64)
     wmat = deq if transposed else deq.T                                   # [N, K]
     xf = inputs.from_storage(x, "f16").astype(np.float64)
     exact = np.zeros((M, N))
@@ -382,7 +498,7 @@ def test_qmatmul_tiny_brute_force(qmode, gs, transposed):
         for n in range(N):
             exact[m, n] = sum(xf[m, k] * wmat[n, k] for k in range(K))
             absum[m, n] = sum(abs(xf[m, k] * wmat[n, k]) for k in range(K))
-    y = oracle.qmatmul(x, wq, s, b, M, N, K, qm, gs, transposed)
+    y = oracle.qmatmul(x, wq, s, b, M, N, K, qm, gs, transposed, bits=bits)
     assert np.all(np.abs(y - exact) <= gamma(K) * absum)
 
 
