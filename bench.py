@@ -417,32 +417,56 @@ def qmatmul_decode(torch, bi, dev):
     """Quantized matmul at decode shapes (M = 8; K = N = 4096 and the MLP
     shape 28672 x 4096), cold: the seeded quantized weight plus bit-permuted
     copies (distinct bytes, same sizes) rotated so no launch finds its weight
-    in a cache.  Transposed [N, K/8] weights and the tile-packed layout;
-    kernel execution time (launch-recorded events)."""
+    in a cache.  Transposed [N, K*bits/32] weights, and for the 4-bit modes
+    also the tile-packed layout; kernel execution time (launch-recorded
+    events)."""
     from invariant_reductions_amd import inputs
     res = {}
-    for mode, gs in (("affine", 64), ("nvfp4", 16), ("mxfp4", 32)):
+    for mode, gs, bits in (("affine", 64, 4), ("nvfp4", 16, 4), ("mxfp4", 32, 4),
+                           ("affine", 64, 3), ("affine", 64, 8), ("mxfp8", 32, 8)):
         for (N, K) in ((4096, 4096), (28672, 4096)):
             M = 8
-            x, wq, s, b = inputs.qmatmul_case(M, K, N, mode, gs, True, seed=0)
+            x, wq, s, b = inputs.qmatmul_case(M, K, N, mode, gs, True, seed=0, bits=bits)
             xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
             wq0 = torch.from_numpy(wq.view(np.int32)).to(dev)
             sd = torch.from_numpy(s if s.dtype == np.uint8 else s.view(np.int16)).to(dev)
             bd = None if b is None else torch.from_numpy(b.view(np.int16)).to(dev)
-            copies = max(2, int(0.8e9 // (N * K // 2)))
+            copies = max(2, int(0.8e9 // (N * K * bits // 8)))
             wqs = [wq0] + [torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff) for r in range(1, copies)]
-            qm = {"affine": bi.AFFINE, "nvfp4": bi.NVFP4, "mxfp4": bi.MXFP4}[mode]
-            wps = [bi.pack_qweights(w, sd, bd, N, K, qm, gs) for w in wqs]
+            qm = {"affine": bi.AFFINE, "nvfp4": bi.NVFP4, "mxfp4": bi.MXFP4, "mxfp8": bi.MXFP8}[mode]
             y = torch.empty(M, N, dtype=torch.float16, device=dev)
-            wbytes = N * K // 2 + N * (K // gs) * (4 if mode == "affine" else 1)
+            wbytes = N * K * bits // 8 + N * (K // gs) * (4 if mode == "affine" else 1)
             tot = wbytes + 2 * M * K + 2 * M * N
-            for tag, fn in (("transposed", lambda r: bi.qmatmul(xd, wqs[r], sd, bd, N, K, qm, gs, True, out=y)),
-                            ("packed", lambda r: bi.qmatmul(xd, wps[r], None, None, N, K, qm, gs, out=y, packed=True))):
+            runs = [("transposed", lambda r: bi.qmatmul(xd, wqs[r], sd, bd, N, K, qm, gs, True, out=y, bits=bits))]
+            wps = []
+            if bits == 4 and mode != "mxfp8":
+                wps = [bi.pack_qweights(w, sd, bd, N, K, qm, gs) for w in wqs]
+                runs.append(("packed", lambda r: bi.qmatmul(xd, wps[r], None, None, N, K, qm, gs, out=y, packed=True)))
+            name = f"{mode}-gs{gs}" + (f"-b{bits}" if mode == "affine" and bits != 4 else "")
+            for tag, fn in runs:
                 t = _time_kernel(torch, bi, lambda i: fn(i % copies), reps=4 * copies)
                 gbs = tot / (t * 1e-3) / 1e9
-                res[f"{mode}-gs{gs} {M}x{N}x{K} {tag}"] = {"us": round(t * 1e3, 1), "gbs": round(gbs, 1),
-                                                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                res[f"{name} {M}x{N}x{K} {tag}"] = {"us": round(t * 1e3, 1), "gbs": round(gbs, 1),
+                                                   "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             del wqs, wps
+    # a mixture-of-experts decode step: 8 tokens, top-2 of 8 experts, each
+    # expert 14336 x 4096 affine gs64; algorithmic bytes = the experts used
+    T, topk, E, N, K, gs = 8, 2, 8, 14336, 4096, 64
+    x, lhs, rhs, wq, s, b = inputs.gather_case(T, topk, K, N, E, "affine", gs, True, False, seed=0)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
+    ld, rd = torch.from_numpy(lhs).to(dev), torch.from_numpy(rhs).to(dev)
+    w0 = torch.from_numpy(wq.view(np.int32)).to(dev)
+    sd, bd = torch.from_numpy(s.view(np.int16)).to(dev), torch.from_numpy(b.view(np.int16)).to(dev)
+    copies = 3
+    ws = [w0] + [torch.bitwise_xor(w0, (0x01010101 * r) & 0x7fffffff) for r in range(1, copies)]
+    y = torch.empty(rhs.size, N, dtype=torch.float16, device=dev)
+    used = len(set(rhs.tolist()))
+    tot = used * (N * K // 2 + N * (K // gs) * 4) + 2 * T * K + 2 * rhs.size * N
+    t = _time_kernel(torch, bi, lambda i: bi.gather_qmatmul(xd, ld, rd, ws[i % copies], sd, bd, N, K, bi.AFFINE, gs,
+                                                            True, out=y), reps=4 * copies)
+    gbs = tot / (t * 1e-3) / 1e9
+    res[f"gather affine-gs64 T{T} top{topk} of E{E} ({used} used) {N}x{K}"] = {
+        "us": round(t * 1e3, 1), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     return res
 
 

@@ -71,7 +71,7 @@ typedef enum {
 typedef enum { BI_BF16 = 0, BI_F16 = 1, BI_F32 = 2 } bi_dtype;
 /* Weight layouts of the dense entry points (their w_layout argument). */
 typedef enum { BI_W_NATURAL = 0, BI_W_TRANSPOSED = 1, BI_W_PACKED = 2 } bi_wlayout;
-typedef enum { BI_AFFINE = 0, BI_NVFP4 = 1, BI_MXFP4 = 2 } bi_qmode;
+typedef enum { BI_AFFINE = 0, BI_NVFP4 = 1, BI_MXFP4 = 2, BI_MXFP8 = 3 } bi_qmode;
 
 /* ------------------------------------------------------------------------
  * Dense matmul   y[m,n] = sum_k x[m,k] * W[n,k]
@@ -170,42 +170,85 @@ bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, int64_t M, 
                            int32_t dtype, int32_t w_layout, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Group-quantized 4-bit matmul   y = x @ dequantize(W)^T
+ * Group-quantized matmul   y = x @ dequantize(W)^T
  * Source: "Fix fp quantized matmul corruption when the quantized dim is not a
  * multiple of 32", Problem (reference x @ dequantize(w).T; nvfp4 group size
- * 16), Fix (bounded K remainder and N tail; loader masks); "Fix/speculative
- * shape invariance", Problem (quantized matmul selected different paths by M).
+ * 16), Fix (bounded K remainder and N tail; loader masks; mxfp4 and mxfp8 at
+ * group size 32), Validation (the differential campaign over affine codes of
+ * 2 to 8 bits at group sizes 32/64/128, mxfp4, mxfp8 and nvfp4); "Fix/
+ * speculative shape invariance", Problem (quantized matmul selected different
+ * paths by M).
  *   x      : [M,K] binary16.
  *   y      : [M,N] binary16.
  *   w_layout BI_W_TRANSPOSED (1), quantized along K:
- *     wq [N, K/8] uint32, scales [N, K/gs], biases [N, K/gs].
+ *     wq [N, K*bits/32] uint32, scales [N, K/gs], biases [N, K/gs].
  *   w_layout BI_W_NATURAL (0), quantized along N:
- *     wq [K, N/8] uint32, scales [K, N/gs], biases [K, N/gs].
- *   w_layout BI_W_PACKED (2): wq is the buffer bi_pack_qweights wrote from
- *     transposed weights (K % 128 == 0, 16-byte aligned; BI_ERR_SHAPE /
- *     BI_ERR_ALIGN otherwise); scales and biases are not read (may be NULL).
- *     Same bits as the transposed call.  Other w_layout values: BI_ERR_SHAPE.
- *   Packing: eight 4-bit codes per little-endian uint32; the element with the
- *   lowest index along the quantized axis is in bits 0..3.
- *   qmode BI_AFFINE: gs in {32, 64, 128}; binary16 scales s and biases b;
- *     w = s*q + b (q in 0..15), evaluated in fp32 and rounded to binary16.
- *   qmode BI_NVFP4: gs == 16; codes are e2m1 (sign in bit 3), scales are one
- *     OCP e4m3fn byte per group; w = e2m1(q) * e4m3(s) (exact in binary16);
- *     biases must be NULL.
- *   qmode BI_MXFP4: gs == 32; e2m1 codes, scales one OCP MX e8m0 byte per
- *     group (2^(e - 127), 0xFF = NaN); w = binary16(e2m1(q) * 2^(e - 127)),
+ *     wq [K, N*bits/32] uint32, scales [K, N/gs], biases [K, N/gs].
+ *   w_layout BI_W_PACKED (2), 4-bit modes only (BI_ERR_UNSUPPORTED for the
+ *     others): wq is the buffer bi_pack_qweights wrote from transposed
+ *     weights (K % 128 == 0, 16-byte aligned; BI_ERR_SHAPE / BI_ERR_ALIGN
+ *     otherwise); scales and biases are not read (may be NULL).  Same bits as
+ *     the transposed call.  Other w_layout values: BI_ERR_SHAPE.
+ *   Packing: each stored row is a little-endian bit stream of `bits`-bit
+ *   codes: code j in bits [j*bits, (j+1)*bits) of the stream, stream bit i in
+ *   bit i % 32 of uint32 word i / 32.  At 4 bits: eight codes per word, the
+ *   lowest index along the quantized axis in bits 0..3; at 8 bits: the row's
+ *   bytes in order.
+ *   qmode BI_AFFINE: bits in 2..8, gs in {32, 64, 128}; binary16 scales s and
+ *     biases b; w = s*q + b (q in 0..2^bits-1), evaluated in fp32 (s*q is
+ *     exact) and rounded to binary16.
+ *   qmode BI_NVFP4: bits 4, gs == 16; codes are e2m1 (sign in bit 3), scales
+ *     are one OCP e4m3fn byte per group; w = e2m1(q) * e4m3(s) (exact in
+ *     binary16); biases must be NULL.
+ *   qmode BI_MXFP4: bits 4, gs == 32; e2m1 codes, scales one OCP MX e8m0 byte
+ *     per group (2^(e - 127), 0xFF = NaN); w = binary16(e2m1(q) * 2^(e - 127)),
  *     the exact fp32 product rounded once (RNE; beyond the binary16 range it
- *     is +-inf); biases must be NULL.  (The pages name mxfp4 with group size
- *     32 -- "Fix fp quantized matmul corruption ...", Fix -- and leave the
- *     format to the OCP microscaling specification.)
- *   bits must be 4.  The quantized dimension must be a multiple of gs
- *   (BI_ERR_GROUP otherwise).  Any M >= 1 is legal, as is K % 32 == 16 at
- *   gs 16 and N % 32 != 0 -- tails are bounded on loads and stores.
+ *     is +-inf); biases must be NULL.
+ *   qmode BI_MXFP8: bits 8, gs == 32; codes are OCP e4m3fn bytes (S.1111.111
+ *     = NaN), scales one e8m0 byte per group; w = binary16(e4m3(q) *
+ *     2^(e - 127)), rounded once as for mxfp4; biases must be NULL.
+ *   (The pages name the formats and group sizes; the element and scale
+ *   encodings are the OCP microscaling specification's.)
+ *   Other (qmode, bits, gs) combinations: BI_ERR_GROUP.  The quantized
+ *   dimension must be a multiple of gs (BI_ERR_GROUP otherwise).  Any M >= 1
+ *   is legal, as is K % 32 == 16 at gs 16, any K in the natural layout and
+ *   N % 32 != 0 in the transposed one -- tails are bounded on loads and
+ *   stores.  Every mode runs the same K tree.
  * ------------------------------------------------------------------------ */
 bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, const void *biases,
                      void *y, int64_t M, int64_t N, int64_t K,
                      int32_t qmode, int32_t bits, int32_t group_size, int32_t w_layout,
                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Expert ("gather") quantized matmul of a mixture-of-experts layer:
+ *   y[m, :] = x[lhs[m], :] @ dequantize(W[rhs[m]])^T
+ * Source: "Fix fp quantized matmul corruption when the quantized dim is not a
+ * multiple of 32", The three defects (the tiled gather shares the quantized
+ * matmul's K loop and loader, so the sorted and unsorted MoE paths must bound
+ * the K remainder and the column tail the same way) and Validation (sorted
+ * gather at T = 64, K = 1040; unsorted gather at M = 50, K = 1040).
+ * Every row is reduced exactly as bi_qmatmul reduces a row, so row m has the
+ * bits of bi_qmatmul(x[lhs[m]], W[rhs[m]]) -- whatever the other rows, their
+ * experts, whether the indices are sorted, or how many rows there are.
+ *   x      : [x_rows, K] binary16 (2-byte aligned).
+ *   lhs_idx: device int32 [M], the token row of each output row, or NULL for
+ *            row m (then x_rows >= M, BI_ERR_SHAPE otherwise).
+ *   rhs_idx: device int32 [M], the expert of each output row (any order).
+ *   wq, scales, biases: E matrices back to back, each laid out as bi_qmatmul
+ *            takes one (w_layout 1 transposed or 0 natural; packed:
+ *            BI_ERR_UNSUPPORTED); wq 4-byte aligned.
+ *   y      : [M, N] binary16.
+ *   Modes: the 4-bit ones (affine gs 32/64/128, nvfp4, mxfp4); others:
+ *   BI_ERR_UNSUPPORTED.  1 <= E <= 1023.  A row whose lhs or rhs index is out
+ *   of range (a device-side condition the host cannot check) is written as
+ *   binary16 NaN; the other rows are unaffected.  Stream-ordered, no
+ *   allocation; errors as bi_qmatmul.
+ * ------------------------------------------------------------------------ */
+bi_status bi_gather_qmatmul(const void *x, const int32_t *lhs_idx, const int32_t *rhs_idx, const uint32_t *wq,
+                            const void *scales, const void *biases, void *y, int64_t M, int64_t x_rows, int64_t N,
+                            int64_t K, int64_t E, int32_t qmode, int32_t bits, int32_t group_size, int32_t w_layout,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Tile-packed quantized weights (BI_W_PACKED for bi_qmatmul), a one-time
@@ -219,11 +262,14 @@ bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, cons
  * scale | bias << 16 (4 bytes each, row-major); nvfp4 / mxfp4: 16 rows x
  * (128/gs) scale bytes.  A wave reads its codes for a block as one 1 KiB piece and its
  * constants as one small piece.
+ *   The 4-bit modes only (affine at bits 4, nvfp4, mxfp4).
  *   bi_packed_qweight_bytes: ceil(N/16) * (K/128) * (1024 + constants chunk),
- *     or 0 for an illegal mode / group size / bits or K % 128 != 0.
+ *     or 0 for an illegal or non-4-bit mode / group size / bits or
+ *     K % 128 != 0.
  *   bi_pack_qweights: transposed wq, scales, biases (as bi_qmatmul) -> wqp of
  *     that many bytes; wq and wqp 16-byte aligned.  Stream-ordered; errors as
- *     bi_qmatmul plus BI_ERR_SHAPE when K % 128 != 0.
+ *     bi_qmatmul plus BI_ERR_SHAPE when K % 128 != 0 and BI_ERR_UNSUPPORTED
+ *     for a legal mode of other than 4 bits.
  * ------------------------------------------------------------------------ */
 size_t bi_packed_qweight_bytes(int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size);
 bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, const void *biases, void *wqp, int64_t N,

@@ -27,7 +27,7 @@ __all__ = [
 ]
 
 BF16, F16, F32 = 0, 1, 2
-AFFINE, NVFP4, MXFP4 = 0, 1, 2
+AFFINE, NVFP4, MXFP4, MXFP8 = 0, 1, 2, 3
 _TORCH_DT = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +61,7 @@ def lib():
         sig = {
             "bi_matmul": [P, P, P, I64, I64, I64, I32, I32, P],
             "bi_qmatmul": [P, P, P, P, P, I64, I64, I64, I32, I32, I32, I32, P],
+            "bi_gather_qmatmul": [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I32, I32, I32, I32, P],
             "bi_rmsnorm": [P, P, P, I64, I64, F, I32, P],
             "bi_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I32, P],
             "bi_sdpa": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, I32, P, SZ, P],
@@ -275,9 +276,11 @@ def matmul_split(x, w, splits: int, transposed: bool = True, out=None, ws=None, 
 
 
 def qmatmul(x, wq, scales, biases, N: int, K: int, qmode: int, group_size: int, transposed: bool = True,
-            out=None, stream=None, packed: bool = False):
-    """y = x @ dequantize(W)^T; x float16 [M,K]; wq int32 (uint32 bit patterns),
-    or (packed=True) the buffer of pack_qweights, with scales/biases None."""
+            out=None, stream=None, packed: bool = False, bits: int = 4):
+    """y = x @ dequantize(W)^T; x float16 [M,K]; wq int32 (uint32 bit patterns:
+    each stored row a little-endian stream of `bits`-bit codes), or
+    (packed=True, 4-bit modes) the buffer of pack_qweights, with scales/biases
+    None.  bits: 2..8 for AFFINE, 4 for NVFP4 and MXFP4, 8 for MXFP8."""
     _dev(x, wq, scales, biases, out)
     if x.dtype != torch.float16:
         raise ValueError("qmatmul: x must be float16")
@@ -286,8 +289,26 @@ def qmatmul(x, wq, scales, biases, N: int, K: int, qmode: int, group_size: int, 
         raise ValueError("qmatmul: x shape")
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
     layout = W_PACKED if packed else (W_TRANSPOSED if transposed else W_NATURAL)
-    _check(lib().bi_qmatmul(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, qmode, 4,
+    _check(lib().bi_qmatmul(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, qmode, bits,
                             group_size, layout, _stream(stream)), "bi_qmatmul")
+    return y
+
+
+def gather_qmatmul(x, lhs, rhs, wq, scales, biases, N: int, K: int, qmode: int, group_size: int,
+                   transposed: bool = True, out=None, stream=None, bits: int = 4):
+    """Expert matmul: y[m] = x[lhs[m]] @ dequantize(W[rhs[m]])^T; x float16
+    [x_rows, K]; lhs (or None: row m) and rhs int32 [M] on the device; wq,
+    scales, biases stacked over the experts on dim 0."""
+    _dev(x, lhs, rhs, wq, scales, biases, out)
+    if x.dtype != torch.float16 or rhs.dtype != torch.int32 or (lhs is not None and lhs.dtype != torch.int32):
+        raise ValueError("gather_qmatmul: x float16, indices int32")
+    if x.shape[1] != K:
+        raise ValueError("gather_qmatmul: x shape")
+    M, E = rhs.shape[0], wq.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _check(lib().bi_gather_qmatmul(_ptr(x), _ptr(lhs), _ptr(rhs), _ptr(wq), _ptr(scales), _ptr(biases), _ptr(y),
+                                   M, x.shape[0], N, K, E, qmode, bits, group_size,
+                                   W_TRANSPOSED if transposed else W_NATURAL, _stream(stream)), "bi_gather_qmatmul")
     return y
 
 

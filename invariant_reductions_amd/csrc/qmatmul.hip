@@ -22,33 +22,9 @@
 // stores nothing.  The K % 32 == 16 shape (nvfp4) takes the word-granular path.
 #include <algorithm>
 
-#include "common.hpp"
+#include "qmatmul_common.hpp"
 
 namespace bi {
-
-constexpr int kQWaves = 8;          // frozen: same K slicing as the dense kernel
-constexpr int kQBlock = 128;
-
-__device__ inline f32x4 qmfma(uint4 a, uint4 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// e4m3fn byte -> fp32 (exact); S.1111.111 -> NaN.
-__device__ inline float e4m3_to_f32(uint32_t s)
-{
-    const uint32_t sign = (s & 0x80u) << 24, e = (s >> 3) & 0xfu, m = s & 7u;
-    if (e == 0xfu && m == 7u) return __uint_as_float(0x7fc00000u);
-    if (e == 0) return __uint_as_float(sign) + (float)m * 0x1p-9f;   // subnormal m/8 * 2^-6 (exact)
-    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
-}
-
-// OCP MX e8m0 scale byte -> fp32 (exact): 2^(e - 127), 0xFF -> NaN.
-__device__ inline float e8m0_to_f32(uint32_t e)
-{
-    if (e == 0xffu) return __uint_as_float(0x7fc00000u);
-    return e == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);   // 2^-127 is subnormal
-}
 
 // e2m1 nibble -> fp32 (exact): magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6, sign in bit 3.
 __device__ inline float e2m1_to_f32(uint32_t c)
@@ -163,9 +139,6 @@ __device__ inline uint16_t deq1(uint32_t q, const QGroup<QM> &g)
     return F16::narrow(v);
 }
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
 // Eight codes of one word -> one 16-byte MFMA operand chunk (element e =
 // nibble e), the same values deq1 gives:
 //   affine: the nibbles are split into bytes (codes 0,2,4,6 and 1,3,5,7),
@@ -249,28 +222,33 @@ __device__ inline void qload_trans(uint4 *dst, const uint32_t *wq, const void *s
 }
 
 // Natural weights [K, N/8] quantized along N: column n's code at row k sits in
-// word (k, n/8), nibble n % 8.
+// word (k, n/8), nibble n % 8.  Eight consecutive k from k0 -> one operand chunk.
+template <int QM, int GS>
+__device__ inline uint4 qload_nat8(const uint32_t *wq, const void *scales, const uint16_t *biases, int64_t n,
+                                   bool nok, int64_t N, int64_t K, int64_t k0)
+{
+    const int64_t words = N / 8, groups = N / GS;
+    uint16_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int64_t k = k0 + e;
+        if (nok && k < K) {
+            const uint32_t q = (wq[k * words + n / 8] >> (4 * (n % 8))) & 15u;
+            const QGroup<QM> gr = load_group<QM>(scales, biases, k * groups + n / GS);
+            h[e] = deq1<QM>(q, gr);
+        } else {
+            h[e] = 0;
+        }
+    }
+    return __builtin_bit_cast(uint4, h);
+}
+
 template <int QM, int GS>
 __device__ inline void qload_nat(uint4 *dst, const uint32_t *wq, const void *scales, const uint16_t *biases,
                                  int64_t n, bool nok, int64_t N, int64_t K, int64_t kbase)
 {
-    const int64_t words = N / 8, groups = N / GS;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        uint16_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t k = kbase + s * 8 + e;
-            if (nok && k < K) {
-                const uint32_t q = (wq[k * words + n / 8] >> (4 * (n % 8))) & 15u;
-                const QGroup<QM> gr = load_group<QM>(scales, biases, k * groups + n / GS);
-                h[e] = deq1<QM>(q, gr);
-            } else {
-                h[e] = 0;
-            }
-        }
-        dst[s] = __builtin_bit_cast(uint4, h);
-    }
+    for (int s = 0; s < 4; ++s) dst[s] = qload_nat8<QM, GS>(wq, scales, biases, n, nok, N, K, kbase + s * 8);
 }
 
 template <int QM, int GS, bool TRANS, bool WVEC, int MT, int NS, bool PK>
@@ -588,18 +566,170 @@ __global__ void pack_q_kernel(const uint32_t *__restrict__ wq, const void *__res
     }
 }
 
+// Expert ("gather") matmul of a mixture-of-experts layer: row m of y is
+// x[lhs[m]] @ dequantize(W[rhs[m]])^T (or the natural-layout product).  One
+// workgroup per 16-column tile walks every row: a slab of up to kGatherSlab
+// rows is bucketed by expert in LDS (a counting sort), and each bucket runs
+// in chunks of up to 16 rows, so the rows of one MFMA tile share the weight
+// fragment and each used expert's columns are streamed once per slab.  A
+// chunk reduces exactly as qmatmul_kernel does (block b of K to wave b mod 8,
+// lane group g supplying [32g, 32g + 32) of the block, wave partials added in
+// order), so a row gets the bits of the plain quantized matmul of its token
+// with its expert -- whatever the other rows, their experts, their order or
+// which chunk it lands in.  Rows whose token or expert index is out of range
+// are written as NaN.
+constexpr int kGatherSlab = 4096;
+constexpr int kGatherMaxExperts = 1023;       // + 1 bucket for invalid rows
+
+template <int QM, int GS, bool TRANS, bool WVEC>
+__global__ __launch_bounds__(kQWaves * kWave)
+void gather_q_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ lhs, const int32_t *__restrict__ rhs,
+                     const uint32_t *__restrict__ wq, const void *__restrict__ scales,
+                     const uint16_t *__restrict__ biases, uint16_t *__restrict__ y, int64_t M, int64_t x_rows,
+                     int64_t N, int64_t K, int E)
+{
+    constexpr int P = kQWaves, NT = kQWaves * kWave;
+    constexpr int SB = QM == BI_AFFINE ? 2 : 1;                 // bytes per scale entry
+    __shared__ float red[P][16][17];
+    __shared__ int perm[kGatherSlab];
+    __shared__ int start[kGatherMaxExperts + 2];                // bucket starts; [E + 1] = slab size
+    __shared__ int cur[kGatherMaxExperts + 1];
+    __shared__ int wsum[P];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * 16, n = n0 + c;
+    const bool nok = n < N;
+    const int64_t nblocks = cdiv(K, kQBlock);
+    const bool xvec = (K % 8) == 0 && aligned16(x);
+    const int64_t words_e = N * K / 8, groups_e = N * K / GS;   // per expert
+
+    auto bucket = [&](int64_t m) -> int {
+        const int64_t e = rhs[m], xr = lhs ? (int64_t)lhs[m] : m;
+        return (e >= 0 && e < E && xr >= 0 && xr < x_rows) ? (int)e : E;
+    };
+
+    for (int64_t s0 = 0; s0 < M; s0 += kGatherSlab) {
+        const int ns = (int)(M - s0 < kGatherSlab ? M - s0 : kGatherSlab);
+        for (int i = tid; i <= E; i += NT) cur[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < ns; i += NT) atomicAdd(&cur[bucket(s0 + i)], 1);
+        __syncthreads();
+        // exclusive scan of the E + 1 counts: thread t owns entries 2t, 2t + 1
+        const int a0 = 2 * tid <= E ? cur[2 * tid] : 0, a1 = 2 * tid + 1 <= E ? cur[2 * tid + 1] : 0;
+        int inc = a0 + a1;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(inc, off, kWave);
+            if (lane >= off) inc += v;
+        }
+        if (lane == kWave - 1) wsum[wave] = inc;
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += wsum[w];
+        const int ex = base + inc - (a0 + a1);
+        if (2 * tid <= E) start[2 * tid] = ex;
+        if (2 * tid + 1 <= E) start[2 * tid + 1] = ex + a0;
+        if (tid == 0) start[E + 1] = ns;
+        __syncthreads();
+        for (int i = tid; i <= E; i += NT) cur[i] = start[i];
+        __syncthreads();
+        for (int i = tid; i < ns; i += NT) perm[atomicAdd(&cur[bucket(s0 + i)], 1)] = i;
+        __syncthreads();
+
+        for (int e = 0; e < E; ++e) {
+            const int b0 = start[e], b1 = start[e + 1];
+            if (b0 == b1) continue;
+            const uint32_t *we = wq + (int64_t)e * words_e;
+            const void *se = (const uint8_t *)scales + (int64_t)e * groups_e * SB;
+            const uint16_t *be = biases ? biases + (int64_t)e * groups_e : nullptr;
+            for (int r0 = b0; r0 < b1; r0 += 16) {
+                const int nr = b1 - r0 < 16 ? b1 - r0 : 16;
+                const bool rok = c < nr;
+                const int64_t m = s0 + perm[r0 + (rok ? c : 0)];
+                const uint16_t *xrow = x + (lhs ? (int64_t)lhs[m] : m) * K;
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int64_t b = wave; b < nblocks; b += P) {
+                    const int64_t kbase = b * kQBlock + (int64_t)g * 32;
+                    if constexpr (TRANS) {
+                        uint4 A[4], Bf[4];
+                        qload_trans<QM, GS, WVEC>(Bf, we, se, be, nok ? n : 0, nok, K, kbase);
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            A[s] = xvec ? load_chunk<F16, true>(xrow, kbase + s * 8, K, rok)
+                                        : load_chunk<F16, false>(xrow, kbase + s * 8, K, rok);
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) acc = qmfma(A[s], Bf[s], acc);
+                    } else {
+                        // element-wise gathers: one step of 8 at a time keeps the registers bounded
+#pragma unroll 1
+                        for (int s = 0; s < 4; ++s) {
+                            const uint4 Bs = qload_nat8<QM, GS>(we, se, be, nok ? n : 0, nok, N, K, kbase + s * 8);
+                            const uint4 As = xvec ? load_chunk<F16, true>(xrow, kbase + s * 8, K, rok)
+                                                  : load_chunk<F16, false>(xrow, kbase + s * 8, K, rok);
+                            acc = qmfma(As, Bs, acc);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][c] = acc[r];
+                __syncthreads();
+                if (tid < 256) {
+                    const int r = tid >> 4, cc = tid & 15;
+                    if (r < nr && n0 + cc < N) {
+                        float v = red[0][r][cc];
+#pragma unroll
+                        for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+                        y[(s0 + perm[r0 + r]) * N + n0 + cc] = F16::narrow(v);
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int i = start[E] * 16 + tid; i < ns * 16; i += NT) {      // invalid rows: NaN
+            const int64_t col = n0 + (i & 15);
+            if (col < N) y[(s0 + perm[i >> 4]) * N + col] = 0x7e00u;
+        }
+        __syncthreads();                                                // perm and start are reused
+    }
+}
+
+template <int QM, int GS>
+static void launch_gather(const void *x, const int32_t *lhs, const int32_t *rhs, const uint32_t *wq, const void *s,
+                          const void *b, void *y, int64_t M, int64_t x_rows, int64_t N, int64_t K, int E, int layout,
+                          hipStream_t st)
+{
+    const dim3 grid((unsigned)cdiv(N, 16)), block(kQWaves * kWave);
+    const uint16_t *bz = (const uint16_t *)b;
+    if (layout == 0)
+        launch_kernel((gather_q_kernel<QM, GS, false, false>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs, wq, s,
+                      bz, (uint16_t *)y, M, x_rows, N, K, E);
+    else if (K % 32 == 0 && host_aligned16(wq))     // then every expert's matrix starts 16-byte aligned too
+        launch_kernel((gather_q_kernel<QM, GS, true, true>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs, wq, s,
+                      bz, (uint16_t *)y, M, x_rows, N, K, E);
+    else
+        launch_kernel((gather_q_kernel<QM, GS, true, false>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs, wq, s,
+                      bz, (uint16_t *)y, M, x_rows, N, K, E);
+}
+
 }  // namespace bi
 
 using namespace bi;
 
 static bi_status check_qmode(int32_t qmode, int32_t bits, int32_t group_size)
 {
-    if (bits != 4) return BI_ERR_GROUP;
-    if (qmode == BI_AFFINE) return (group_size == 32 || group_size == 64 || group_size == 128) ? BI_OK : BI_ERR_GROUP;
-    if (qmode == BI_NVFP4) return group_size == 16 ? BI_OK : BI_ERR_GROUP;
-    if (qmode == BI_MXFP4) return group_size == 32 ? BI_OK : BI_ERR_GROUP;
+    if (qmode == BI_AFFINE)
+        return (bits >= 2 && bits <= 8 && (group_size == 32 || group_size == 64 || group_size == 128)) ? BI_OK
+                                                                                                      : BI_ERR_GROUP;
+    if (qmode == BI_NVFP4) return (bits == 4 && group_size == 16) ? BI_OK : BI_ERR_GROUP;
+    if (qmode == BI_MXFP4) return (bits == 4 && group_size == 32) ? BI_OK : BI_ERR_GROUP;
+    if (qmode == BI_MXFP8) return (bits == 8 && group_size == 32) ? BI_OK : BI_ERR_GROUP;
     return BI_ERR_GROUP;
 }
+
+// The formats this file's kernels (and the packed layout) serve; the rest go
+// to qmatmul_wide.hip.
+static bool four_bit_mode(int32_t qmode, int32_t bits) { return bits == 4 && qmode != BI_MXFP8; }
 
 extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, const void *biases, void *y,
                                 int64_t M, int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size,
@@ -611,6 +741,7 @@ extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *s
     if (w_layout < 0 || w_layout > 2) return BI_ERR_SHAPE;
     const bi_status qs = check_qmode(qmode, bits, group_size);
     if (qs != BI_OK) return qs;
+    if (packed && !four_bit_mode(qmode, bits)) return BI_ERR_UNSUPPORTED;
     if (!packed) {
         if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
         if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
@@ -622,6 +753,8 @@ extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *s
         (!packed && (((uintptr_t)scales & 1u) || ((uintptr_t)biases & 1u))))
         return BI_ERR_ALIGN;
     (void)hipGetLastError();
+    if (!four_bit_mode(qmode, bits))
+        return bi_qmatmul_wide(x, wq, scales, biases, y, M, N, K, qmode, bits, group_size, w_layout, stream);
     if (qmode == BI_NVFP4) launch_q<BI_NVFP4, 16>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
     else if (qmode == BI_MXFP4) launch_q<BI_MXFP4, 32>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
     else if (group_size == 32) launch_q<BI_AFFINE, 32>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
@@ -632,7 +765,8 @@ extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *s
 
 extern "C" size_t bi_packed_qweight_bytes(int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size)
 {
-    if (N < 1 || K < 1 || K % kQBlock || N > (1ll << 31) || K > (1ll << 31) || check_qmode(qmode, bits, group_size) != BI_OK)
+    if (N < 1 || K < 1 || K % kQBlock || N > (1ll << 31) || K > (1ll << 31) || check_qmode(qmode, bits, group_size) != BI_OK ||
+        !four_bit_mode(qmode, bits))
         return 0;
     const size_t chunks = (size_t)cdiv(N, 16) * (size_t)(K / kQBlock);
     return chunks * (1024 + (size_t)qconst_chunk_bytes(qmode, group_size));
@@ -644,6 +778,7 @@ extern "C" bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, co
     if (!wq || !scales || !wqp) return BI_ERR_NULL;
     const bi_status qs = check_qmode(qmode, bits, group_size);
     if (qs != BI_OK) return qs;
+    if (!four_bit_mode(qmode, bits)) return BI_ERR_UNSUPPORTED;
     if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
     if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
     if (bi_packed_qweight_bytes(N, K, qmode, bits, group_size) == 0) return BI_ERR_SHAPE;
@@ -661,5 +796,39 @@ extern "C" bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, co
     else if (group_size == 32) launch_kernel((pack_q_kernel<BI_AFFINE, 32>), grid, block, 0, stream, w, scales, bz, o, N, K);
     else if (group_size == 64) launch_kernel((pack_q_kernel<BI_AFFINE, 64>), grid, block, 0, stream, w, scales, bz, o, N, K);
     else launch_kernel((pack_q_kernel<BI_AFFINE, 128>), grid, block, 0, stream, w, scales, bz, o, N, K);
+    return launch_status();
+}
+
+extern "C" bi_status bi_gather_qmatmul(const void *x, const int32_t *lhs_idx, const int32_t *rhs_idx,
+                                       const uint32_t *wq, const void *scales, const void *biases, void *y,
+                                       int64_t M, int64_t x_rows, int64_t N, int64_t K, int64_t E, int32_t qmode,
+                                       int32_t bits, int32_t group_size, int32_t w_layout, hipStream_t stream)
+{
+    if (!x || !rhs_idx || !wq || !scales || !y) return BI_ERR_NULL;
+    if (M < 1 || x_rows < 1 || N < 1 || K < 1 || E < 1 || M > (1ll << 31) || x_rows > (1ll << 31) ||
+        N > (1ll << 31) || K > (1ll << 31) || E > kGatherMaxExperts || (!lhs_idx && x_rows < M))
+        return BI_ERR_SHAPE;
+    if (w_layout < 0 || w_layout > 2) return BI_ERR_SHAPE;
+    const bi_status qs = check_qmode(qmode, bits, group_size);
+    if (qs != BI_OK) return qs;
+    if (w_layout == 2 || !four_bit_mode(qmode, bits)) return BI_ERR_UNSUPPORTED;
+    if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
+    if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
+    if ((w_layout ? K : N) % group_size) return BI_ERR_GROUP;
+    if ((((uintptr_t)x | (uintptr_t)y | (uintptr_t)scales | (uintptr_t)biases) & 1u) ||
+        (((uintptr_t)wq | (uintptr_t)lhs_idx | (uintptr_t)rhs_idx) & 3u))
+        return BI_ERR_ALIGN;
+    (void)hipGetLastError();
+    const int e = (int)E;
+    if (qmode == BI_NVFP4)
+        launch_gather<BI_NVFP4, 16>(x, lhs_idx, rhs_idx, wq, scales, biases, y, M, x_rows, N, K, e, w_layout, stream);
+    else if (qmode == BI_MXFP4)
+        launch_gather<BI_MXFP4, 32>(x, lhs_idx, rhs_idx, wq, scales, biases, y, M, x_rows, N, K, e, w_layout, stream);
+    else if (group_size == 32)
+        launch_gather<BI_AFFINE, 32>(x, lhs_idx, rhs_idx, wq, scales, biases, y, M, x_rows, N, K, e, w_layout, stream);
+    else if (group_size == 64)
+        launch_gather<BI_AFFINE, 64>(x, lhs_idx, rhs_idx, wq, scales, biases, y, M, x_rows, N, K, e, w_layout, stream);
+    else
+        launch_gather<BI_AFFINE, 128>(x, lhs_idx, rhs_idx, wq, scales, biases, y, M, x_rows, N, K, e, w_layout, stream);
     return launch_status();
 }

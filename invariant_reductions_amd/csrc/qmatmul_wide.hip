@@ -1,0 +1,435 @@
+// qmatmul_wide.hip -- batch-invariant group-quantized matmul on gfx950 for the
+// code widths beyond the 4-bit formats: affine codes of 2 to 8 bits (other
+// than 4) and mxfp8 (OCP e4m3 codes, one e8m0 scale per 32).
+//
+// Sources: "Fix fp quantized matmul corruption when the quantized dim is not a
+// multiple of 32" (Validation: the differential campaign over affine codes of
+// 2 to 8 bits at group sizes 32/64/128 and the mx and nv fp formats; Fix:
+// mxfp8's group size is 32, a multiple of the K tile, so no group is cut by a
+// K remainder); "Fix/speculative shape invariance" (Problem: the quantized
+// matmul must not pick its reduction by M).
+//
+// What is computed: W is dequantized in registers to binary16 --
+//   affine: w = RNE16(fma(s, q, b)) with binary16 s, b (s*q is exact in fp32,
+//           at most 11 + 8 significant bits, so the fma rounds once, exactly
+//           like mul-then-add);
+//   mxfp8 : w = RNE16(e4m3(q) * 2^(e - 127)), the exact product rounded once --
+// and multiplied against binary16 x by the K tree of the 4-bit kernels: blocks
+// of 128 owned by wave b mod 8, lane group g supplying [32g, 32g + 32) of a
+// block as four v_mfma_f32_16x16x32_f16 steps, wave partials added in wave
+// order, RNE to binary16.  Group sizes are at least 32, so a lane's 32 codes
+// of a block share one group.  M, the M tile and the column tiling are free.
+//
+// Codes: every stored row is a little-endian bit stream of BITS-bit codes in
+// 32-bit words, so in the transposed layout a lane's 32 codes are exactly
+// BITS consecutive words.  In the natural layout column n's code in row k
+// starts at stream bit n * BITS of row k and may straddle two words.
+//
+// Bounds: transposed K is a multiple of the group size (>= 32), so a lane's 32
+// codes lie wholly below K or wholly at/after it; natural K is arbitrary and a
+// code at k >= K is not read; columns n >= N read nothing and store nothing.
+#include <algorithm>
+
+#include "qmatmul_common.hpp"
+
+namespace bi {
+
+// Code e (0..31; a compile-time constant once unrolled) of a lane's words.
+template <int BITS>
+__device__ inline uint32_t wcode(const uint32_t (&w)[BITS], int e)
+{
+    const int o = e * BITS, i = o >> 5, sh = o & 31;
+    uint32_t v = w[i] >> sh;
+    if (sh + BITS > 32) v |= w[i + 1] << (32 - sh);
+    return v & ((1u << BITS) - 1u);
+}
+
+// The BITS words of a lane: 16-byte loads when BITS % 4 == 0, 8-byte ones when
+// BITS is even (the offsets are multiples of those sizes whenever wq is
+// 16-byte aligned and K % 32 == 0), else single words.
+template <int BITS>
+__device__ inline void load_words(uint32_t (&w)[BITS], const uint32_t *src, bool vec)
+{
+    if (vec && BITS % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < BITS / 4; ++i) {
+            const uint4 v = reinterpret_cast<const uint4 *>(src)[i];
+            w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    } else if (vec && BITS % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < BITS / 2; ++i) {
+            const uint2 v = reinterpret_cast<const uint2 *>(src)[i];
+            w[2 * i] = v.x; w[2 * i + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) w[i] = src[i];
+    }
+}
+
+// mxfp8 scale of the register path: 2^(min(k, 25) + 8) with k = e - 127, NaN
+// for e = 0xFF.  Codes enter as binary16 patterns worth e4m3 * 2^-8, so the
+// fp32 product is e4m3 * 2^min(k, 25): exact (at least 2^-136 with four
+// significant bits).  For k >= 25 every nonzero code gives at least 2^16,
+// which rounds to +-inf in binary16 just as the exact value does.
+__device__ inline float mx8_scale(uint32_t e)
+{
+    if (e == 0xffu) return __uint_as_float(0x7fc00000u);
+    const int k = (int)e - 127;
+    return __uint_as_float((uint32_t)((k > 25 ? 25 : k) + 8 + 127) << 23);
+}
+
+// Group constants from the raw scale (and bias) a lane loaded.
+template <int QM>
+__device__ inline void wgroup(uint32_t sc, uint32_t bs, float &s, float &b)
+{
+    if constexpr (QM == BI_MXFP8) {
+        s = mx8_scale(sc);
+        b = 0.0f;
+    } else {
+        s = F16::widen((uint16_t)sc);
+        b = F16::widen((uint16_t)bs);
+    }
+}
+
+template <int QM>
+__device__ inline void load_raw_group(const void *scales, const uint16_t *biases, int64_t gi, uint32_t &sc,
+                                      uint32_t &bs)
+{
+    if constexpr (QM == BI_MXFP8) {
+        sc = ((const uint8_t *)scales)[gi];
+        bs = 0;
+    } else {
+        sc = ((const uint16_t *)scales)[gi];
+        bs = biases[gi];
+    }
+}
+
+// Codes 8s .. 8s + 7 of a lane's 32 -> one 16-byte MFMA operand chunk.
+//   affine: code -> fp32 (exact), fma(s, q, b), pairs rounded to binary16 by
+//           one packed conversion;
+//   mxfp8 : byte (sign | e | m) -> binary16 pattern (sign << 15) | ((e, m) <<
+//           7), whose value is e4m3 * 2^-8 exactly (e = 0 lands on binary16
+//           subnormals, m * 2^-17); widened to fp32, times mx8_scale, rounded
+//           once to binary16; the NaN codes (e, m all ones) get the binary16
+//           NaN exponent and top mantissa bit ORed in.
+template <int QM, int BITS>
+__device__ inline uint4 wdeq8(const uint32_t (&w)[BITS], int s, float gsv, float gbv)
+{
+    uint32_t out[4];
+    if constexpr (QM == BI_MXFP8) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t word = w[2 * s + (p >> 1)];
+            const uint32_t b0 = 2u * (uint32_t)(p & 1);
+            // code 2p -> bits 0..7, code 2p + 1 -> bits 16..23
+            const uint32_t t = __builtin_amdgcn_perm(word, word, 0x0C000C00u | b0 | ((b0 + 1u) << 16));
+            const uint32_t mag = t & 0x007f007fu;
+            const uint32_t h = (mag << 7) | ((t & 0x00800080u) << 8);
+            const uint32_t nan = ((mag + 0x00010001u) & 0x00800080u) * 0xFCu;   // 0x80 * 0xFC = 0x7E00
+            const f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, h), f32x2) * gsv;
+            out[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2)) | nan;
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const float q0 = (float)wcode<BITS>(w, 8 * s + 2 * p), q1 = (float)wcode<BITS>(w, 8 * s + 2 * p + 1);
+            const f32x2 v = f32x2{__builtin_fmaf(gsv, q0, gbv), __builtin_fmaf(gsv, q1, gbv)};
+            out[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+        }
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// One code of the natural layout -> binary16 bits (the same value wdeq8 gives).
+template <int QM>
+__device__ inline uint16_t wdeq1(uint32_t q, uint32_t sc, uint32_t bs)
+{
+    if constexpr (QM == BI_MXFP8) {
+        return F16::narrow(e4m3_to_f32(q) * e8m0_to_f32(sc));
+    } else {
+        return F16::narrow(__builtin_fmaf(F16::widen((uint16_t)sc), (float)q, F16::widen((uint16_t)bs)));
+    }
+}
+
+// General form: any M (tiles of 16*MT rows), 16 columns per workgroup, either
+// layout.  gshift = log2(group size).
+template <int QM, int BITS, bool TRANS, int MT>
+__global__ __launch_bounds__(kQWaves * kWave)
+void qwide_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wq, const void *__restrict__ scales,
+                  const uint16_t *__restrict__ biases, uint16_t *__restrict__ y, int64_t M, int64_t N, int64_t K,
+                  int gshift, int wvec)
+{
+    constexpr int P = kQWaves, TR = MT * 16, TC = 16;
+    __shared__ float red[P][TR][TC + 1];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * TC, m0 = (int64_t)blockIdx.y * TR;
+    const int64_t nblocks = cdiv(K, kQBlock);
+    const bool xvec = (K % 8) == 0 && aligned16(x);
+    const int64_t n = n0 + c;
+    const bool nok = n < N;
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t *xrow[MT];
+    bool xok[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int64_t r = m0 + i * 16 + c;
+        xok[i] = r < M;
+        xrow[i] = x + (xok[i] ? r : 0) * K;
+    }
+
+    for (int64_t b = wave; b < nblocks; b += P) {
+        const int64_t kbase = b * kQBlock + (int64_t)g * 32;
+        uint4 Bf[4];
+        if constexpr (TRANS) {
+            if (nok && kbase < K) {
+                const int64_t wpr = K / 32 * BITS;
+                uint32_t w[BITS];
+                load_words<BITS>(w, wq + n * wpr + (kbase / 32) * BITS, wvec != 0);
+                uint32_t sc, bs;
+                load_raw_group<QM>(scales, biases, n * (K >> gshift) + (kbase >> gshift), sc, bs);
+                float gsv, gbv;
+                wgroup<QM>(sc, bs, gsv, gbv);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) Bf[s] = wdeq8<QM, BITS>(w, s, gsv, gbv);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) Bf[s] = make_uint4(0, 0, 0, 0);
+            }
+        } else {
+            const int64_t wpr = N / 32 * BITS, groups = N >> gshift;
+            const int64_t bit = n * BITS, wi = bit >> 5;
+            const int sh = (int)(bit & 31);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                uint16_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int64_t k = kbase + s * 8 + e;
+                    h[e] = 0;
+                    if (nok && k < K) {
+                        const uint32_t *row = wq + k * wpr;
+                        uint32_t v = row[wi] >> sh;
+                        if (sh + BITS > 32) v |= row[wi + 1] << (32 - sh);   // the code ends inside the row
+                        uint32_t sc, bs;
+                        load_raw_group<QM>(scales, biases, k * groups + (n >> gshift), sc, bs);
+                        h[e] = wdeq1<QM>(v & ((1u << BITS) - 1u), sc, bs);
+                    }
+                }
+                Bf[s] = __builtin_bit_cast(uint4, h);
+            }
+        }
+        uint4 A[MT][4];
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                A[i][s] = xvec ? load_chunk<F16, true>(xrow[i], kbase + s * 8, K, xok[i])
+                               : load_chunk<F16, false>(xrow[i], kbase + s * 8, K, xok[i]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) acc[i] = qmfma(A[i][s], Bf[s], acc[i]);
+    }
+
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][i * 16 + g * 4 + r][c] = acc[i][r];
+    __syncthreads();
+    for (int o = threadIdx.x; o < TR * TC; o += P * kWave) {
+        const int r = o / TC, cc = o % TC;
+        const int64_t row = m0 + r, col = n0 + cc;
+        if (row >= M || col >= N) continue;
+        float v = red[0][r][cc];
+#pragma unroll
+        for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+        y[row * N + col] = F16::narrow(v);
+    }
+}
+
+// Persistent streaming form for short M (at most 16 rows), transposed
+// weights, K % 128 == 0 and 16-byte aligned x: a fixed grid walks the output
+// tiles (16 rows x NS*16 columns) t = blockIdx.x, blockIdx.x + gridDim.x, ...;
+// each wave streams its (tile, block) items -- a lane's code words, group
+// constants and x chunks -- through a D-deep register ring that runs across
+// tile boundaries.  Per output the tree is qwide_kernel's.
+template <int QM, int BITS, int NS, int D>
+__global__ __launch_bounds__(kQWaves * kWave, 2)
+void qwide_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wq,
+                         const void *__restrict__ scales, const uint16_t *__restrict__ biases,
+                         uint16_t *__restrict__ y, int64_t M, int64_t N, int64_t K, int ntn, int gshift, int wvec)
+{
+    constexpr int P = kQWaves, TC = NS * 16;
+    __shared__ float red[P][16][TC + 1];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    const int nb = (int)(K / kQBlock);
+    const int nmine = wave < nb ? (nb - wave + P - 1) / P : 0;        // blocks of this wave per tile
+    const int mytiles = (int)blockIdx.x < ntn ? (ntn - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    const int items = mytiles * nmine;
+    const int64_t wpr = K / 32 * BITS, groups = K >> gshift;
+    // x row of A-operand row c; rows >= M are not loaded and never stored
+    const uint16_t *xr = x + (int64_t)(c < M ? c : M - 1) * K;
+
+    uint32_t Wr[D][NS][BITS];
+    uint4 Xr[D][4];
+    uint32_t Sr[D][NS], Br[D][NS];
+    // prefetch cursor: item (pu, pj) = block wave + pj*P of tile pu; holds at the last item
+    int pu = 0, pj = 0;
+    auto load_next = [&](uint32_t (&Wd)[NS][BITS], uint32_t (&Sd)[NS], uint32_t (&Bd)[NS], uint4 (&Xd)[4]) {
+        const int64_t t = (int64_t)blockIdx.x + (int64_t)pu * gridDim.x;
+        const int64_t kb = (int64_t)(wave + pj * P) * kQBlock + g * 32;     // this lane's first code
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            int64_t n = t * TC + j * 16 + c;
+            n = n < N ? n : N - 1;                                          // padding columns read a real row
+            load_words<BITS>(Wd[j], wq + n * wpr + (kb / 32) * BITS, wvec != 0);
+            load_raw_group<QM>(scales, biases, n * groups + (kb >> gshift), Sd[j], Bd[j]);
+        }
+        if (c < M) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xd[s] = *reinterpret_cast<const uint4 *>(xr + kb + s * 8);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xd[s] = make_uint4(0, 0, 0, 0);
+        }
+        if (pj + 1 < nmine) {
+            ++pj;
+        } else if (pu + 1 < mytiles) {
+            pj = 0;
+            ++pu;
+        }
+    };
+    f32x4 acc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto finish_tile = [&](int u) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][j * 16 + c] = acc[j][r];
+            acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+        const int64_t n0 = ((int64_t)blockIdx.x + (int64_t)u * gridDim.x) * TC;
+        for (int o = threadIdx.x; o < 16 * TC; o += P * kWave) {
+            const int r = o / TC, cc = o % TC;
+            const int64_t col = n0 + cc;
+            if (r >= M || col >= N) continue;
+            float v = red[0][r][cc];
+#pragma unroll
+            for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+            y[(int64_t)r * N + col] = F16::narrow(v);
+        }
+        __syncthreads();
+    };
+
+    if (items > 0) {
+        int cu = 0, cj = 0;
+        static_for<0, D - 1>([&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+            load_next(Wr[d], Sr[d], Br[d], Xr[d]);
+        });
+        for (int i = 0; i < items; i += D) {
+            static_for<0, D>([&](auto dc) {
+                constexpr int d = decltype(dc)::value;
+                constexpr int dn = (d + D - 1) % D;
+                load_next(Wr[dn], Sr[dn], Br[dn], Xr[dn]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i + d < items) {
+                    float gsv[NS], gbv[NS];
+#pragma unroll
+                    for (int j = 0; j < NS; ++j) wgroup<QM>(Sr[d][j], Br[d][j], gsv[j], gbv[j]);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int j = 0; j < NS; ++j)
+                            acc[j] = qmfma(Xr[d][s], wdeq8<QM, BITS>(Wr[d][j], s, gsv[j], gbv[j]), acc[j]);
+                    if (++cj == nmine) {
+                        finish_tile(cu);
+                        cj = 0;
+                        ++cu;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+    } else {
+        // a wave that owns no block of K still takes part in every combine
+        for (int u = 0; u < mytiles; ++u) finish_tile(u);
+    }
+}
+
+template <int QM, int BITS, bool TRANS, int MT>
+static void launch_qw_t(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
+                        int64_t N, int64_t K, int gshift, int wvec, hipStream_t st)
+{
+    dim3 grid((unsigned)cdiv(N, 16), (unsigned)cdiv(M, MT * 16));
+    launch_kernel((qwide_kernel<QM, BITS, TRANS, MT>), grid, dim3(kQWaves * kWave), 0, st, (const uint16_t *)x, wq, s,
+                  (const uint16_t *)b, (uint16_t *)y, M, N, K, gshift, wvec);
+}
+
+template <int QM, int BITS, int NS>
+static void launch_qw_stream(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
+                             int64_t N, int64_t K, int gshift, int wvec, hipStream_t st)
+{
+    constexpr int D = BITS >= 6 ? 2 : 3;                 // register ring depth: wide codes hold more words
+    const int64_t ntn = cdiv(N, NS * 16);
+    const int64_t grid = std::min<int64_t>(ntn, (int64_t)device_cu_count() * 2);
+    launch_kernel((qwide_stream_kernel<QM, BITS, NS, D>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
+                  (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, M, N, K, (int)ntn, gshift, wvec);
+}
+
+template <int QM, int BITS>
+static void launch_qw(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M, int64_t N,
+                      int64_t K, int gs, int layout, hipStream_t st)
+{
+    const int gshift = gs == 32 ? 5 : (gs == 64 ? 6 : 7);
+    const int wvec = host_aligned16(wq) ? 1 : 0;         // row and lane offsets are then multiples of the load size
+    if (layout == 1 && M <= 16 && K % kQBlock == 0 && host_aligned16(x) && cdiv(N, 16) <= (1ll << 30)) {
+        if (N >= 8192) launch_qw_stream<QM, BITS, 2>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+        else launch_qw_stream<QM, BITS, 1>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+        return;
+    }
+    const int64_t mt = cdiv(M, 16);
+    if (layout == 1) {
+        if (mt <= 1) launch_qw_t<QM, BITS, true, 1>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+        else if (mt <= 2) launch_qw_t<QM, BITS, true, 2>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+        else launch_qw_t<QM, BITS, true, 4>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+    } else {
+        if (mt <= 1) launch_qw_t<QM, BITS, false, 1>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+        else if (mt <= 2) launch_qw_t<QM, BITS, false, 2>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+        else launch_qw_t<QM, BITS, false, 4>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+    }
+}
+
+}  // namespace bi
+
+using namespace bi;
+
+bi_status bi_qmatmul_wide(const void *x, const uint32_t *wq, const void *scales, const void *biases, void *y,
+                          int64_t M, int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size,
+                          int32_t w_layout, hipStream_t st)
+{
+    if (qmode == BI_MXFP8) {
+        launch_qw<BI_MXFP8, 8>(x, wq, scales, biases, y, M, N, K, group_size, w_layout, st);
+    } else {
+        switch (bits) {
+        case 2: launch_qw<BI_AFFINE, 2>(x, wq, scales, biases, y, M, N, K, group_size, w_layout, st); break;
+        case 3: launch_qw<BI_AFFINE, 3>(x, wq, scales, biases, y, M, N, K, group_size, w_layout, st); break;
+        case 5: launch_qw<BI_AFFINE, 5>(x, wq, scales, biases, y, M, N, K, group_size, w_layout, st); break;
+        case 6: launch_qw<BI_AFFINE, 6>(x, wq, scales, biases, y, M, N, K, group_size, w_layout, st); break;
+        case 7: launch_qw<BI_AFFINE, 7>(x, wq, scales, biases, y, M, N, K, group_size, w_layout, st); break;
+        case 8: launch_qw<BI_AFFINE, 8>(x, wq, scales, biases, y, M, N, K, group_size, w_layout, st); break;
+        default: return BI_ERR_GROUP;
+        }
+    }
+    return launch_status();
+}

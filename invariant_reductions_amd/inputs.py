@@ -284,6 +284,41 @@ def qmatmul_case(M: int, K: int, N: int, qmode: str, group_size: int, transposed
     return x, wq, s, b
 
 
+def gather_case(T: int, topk: int, K: int, N: int, E: int, qmode: str, group_size: int, transposed: bool = True,
+                sort_rows: bool = False, seed: int = 0, bits: int = 4):
+    """A mixture-of-experts expert matmul: E weight matrices W_e ~ N(0,1)
+    ([N,K] when transposed, else [K,N]), each quantized as qmatmul_case does,
+    then x [T,K] ~ N(0,1) binary16, then per token `topk` distinct experts
+    drawn uniformly.  Row m = t*topk + j reads token t and its j-th expert;
+    sort_rows orders the rows by expert (stable), as a sorted-index caller
+    would.  Returns (x, lhs int32 [M], rhs int32 [M], wq [E, ...], scales
+    [E, ...], biases [E, ...] or None)."""
+    rng = np.random.default_rng(seed)
+    parts = []
+    for _ in range(E):
+        w = rng.standard_normal((N, K) if transposed else (K, N)).astype(np.float32)
+        if qmode == "affine":
+            parts.append(quantize_affine(w, group_size, bits))
+        elif qmode == "nvfp4":
+            parts.append(quantize_nvfp4(w) + (None,))
+        elif qmode == "mxfp4":
+            parts.append(quantize_mxfp4(w) + (None,))
+        elif qmode == "mxfp8":
+            parts.append(quantize_mxfp8(w) + (None,))
+        else:
+            raise ValueError(qmode)
+    wq = np.stack([p[0] for p in parts])
+    sc = np.stack([p[1] for p in parts])
+    bs = None if parts[0][2] is None else np.stack([p[2] for p in parts])
+    x = normal(rng, (T, K), dtype="f16")
+    rhs = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(T)]).reshape(-1).astype(np.int32)
+    lhs = np.repeat(np.arange(T, dtype=np.int32), topk)
+    if sort_rows:
+        order = np.argsort(rhs, kind="stable")
+        lhs, rhs = lhs[order], rhs[order]
+    return x, lhs, rhs, wq, sc, bs
+
+
 def rope_tables(max_pos: int, head_dim: int, theta: float = 10000.0):
     """cos/sin [max_pos, head_dim/2] of pos * theta^(-2i/head_dim), computed in
     fp64 and stored as fp32 (model buffers, like the weights)."""

@@ -78,6 +78,7 @@ def lib():
         L.bo_matmul.argtypes = [P, P, P, I64, I64, I64, I32, I32]
         L.bo_dequantize.argtypes = [P, P, P, P, I64, I64, I32, I32, I32]
         L.bo_qmatmul.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, I32, I32]
+        L.bo_gather_qmatmul.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I32, I32, I32, I32]
         L.bo_rmsnorm.argtypes = [P, P, P, P, I64, I64, ctypes.c_float, I32]
         L.bo_sdpa.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, I32]
         L.bo_rope.argtypes = [P, P, P, P, P, I64, I64, I64, I32]
@@ -197,6 +198,24 @@ def qmatmul(x, wq, scales, biases, M: int, N: int, K: int, qmode: int, group_siz
     y = np.empty((M, N), np.float32)
     _check(lib().bo_qmatmul(_p(x), _p(wq), _p(scales), None if b is None else _p(b), _p(y),
                             M, N, K, qmode, bits, group_size, int(w_transposed)), "qmatmul")
+    return y
+
+
+def gather_qmatmul(x, lhs, rhs, wq, scales, biases, N: int, K: int, qmode: int, group_size: int,
+                   w_transposed: bool = True, bits: int = 4) -> np.ndarray:
+    """Expert matmul: y[m] = x[lhs[m]] @ dequantize(W[rhs[m]])^T (lhs None:
+    x[m]); wq, scales, biases stacked over the E experts on axis 0; fp32 [M,N]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    rhs = np.ascontiguousarray(rhs, dtype=np.int32)
+    lh = None if lhs is None else np.ascontiguousarray(lhs, dtype=np.int32)
+    wq = np.ascontiguousarray(wq, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales)
+    b = None if biases is None else np.ascontiguousarray(biases, dtype=np.uint16)
+    M, E = rhs.shape[0], wq.shape[0]
+    y = np.empty((M, N), np.float32)
+    _check(lib().bo_gather_qmatmul(_p(x), None if lh is None else _p(lh), _p(rhs), _p(wq), _p(scales),
+                                   None if b is None else _p(b), _p(y), M, x.shape[0], N, K, E, qmode, bits,
+                                   group_size, int(w_transposed)), "gather_qmatmul")
     return y
 
 

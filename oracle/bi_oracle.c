@@ -360,6 +360,56 @@ int bo_qmatmul(const uint16_t *x, const uint32_t *wq, const void *scales, const 
     return rc;
 }
 
+/* Expert ("gather") matmul of a mixture-of-experts layer:
+ *   y[m, :] = x[lhs[m], :] @ dequantize(W[rhs[m]])^T   (transposed weights)
+ *   y[m, :] = x[lhs[m], :] @ dequantize(W[rhs[m]])     (natural weights)
+ * W holds E quantized matrices back to back, each stored as bo_dequantize
+ * describes (codes, scales and biases each [E, ...]); lhs NULL reads x[m].
+ * Every row is its own sequential fp32 fold over k, so a row's value does not
+ * depend on the other rows or on their order.  A row whose lhs or rhs index is
+ * out of range is NaN.  x binary16 [x_rows, K]; y fp32 [M, N]. */
+int bo_gather_qmatmul(const uint16_t *x, const int32_t *lhs, const int32_t *rhs, const uint32_t *wq,
+                      const void *scales, const uint16_t *biases, float *y, int64_t M, int64_t x_rows,
+                      int64_t N, int64_t K, int64_t E, int qmode, int bits, int group_size, int w_transposed)
+{
+    if (!x || !rhs || !wq || !scales || !y || M < 0 || x_rows < 0 || N < 0 || K < 0 || E < 1) return -1;
+    if (!lhs && x_rows < M) return -1;
+    const int64_t rows = w_transposed ? N : K, cols = w_transposed ? K : N;
+    if (group_size < 1 || cols % group_size || (cols * bits) % 32) return -3;
+    const int64_t words_e = rows * cols * bits / 32, groups_e = rows * cols / group_size;
+    const size_t ssz = qmode == BO_AFFINE ? 2 : 1;
+    uint16_t *wd = (uint16_t *)malloc((size_t)(E * rows * cols > 0 ? E * rows * cols : 1) * 2);
+    if (!wd) return -2;
+    for (int64_t e = 0; e < E; ++e) {
+        int rc = bo_dequantize(wq + e * words_e, (const uint8_t *)scales + e * groups_e * ssz,
+                               biases ? biases + e * groups_e : NULL, wd + e * rows * cols, rows, cols, qmode, bits,
+                               group_size);
+        if (rc) {
+            free(wd);
+            return rc;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const int64_t xr = lhs ? lhs[m] : m, e = rhs[m];
+        if (xr < 0 || xr >= x_rows || e < 0 || e >= E) {
+            for (int64_t n = 0; n < N; ++n) y[m * N + n] = bits_to_f32(0x7fc00000u);
+            continue;
+        }
+        const uint16_t *w = wd + e * rows * cols;
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                const float wv = bo_f16_to_f32(w_transposed ? w[n * K + k] : w[k * N + n]);
+                acc = acc + bo_f16_to_f32(x[xr * K + k]) * wv;
+            }
+            y[m * N + n] = acc;
+        }
+    }
+    free(wd);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* RMSNorm  y = (x * inv) * w,  inv = 1 / sqrt(sum(x^2) / H + eps)          */
 /* ------------------------------------------------------------------------ */

@@ -61,7 +61,16 @@ def test_matmul_validation(args, code):
 
 
 @pytest.mark.parametrize("M,N,K,qmode,bits,gs,trans,biases,code", [
-    (1, 512, 4096, 0, 3, 32, 1, A, GROUP),          # bits must be 4
+    (1, 512, 4096, 0, 1, 32, 1, A, GROUP),          # affine bits 2..8
+    (1, 512, 4096, 0, 9, 32, 1, A, GROUP),
+    (1, 512, 4096, 1, 8, 16, 1, None, GROUP),       # nvfp4 is 4-bit
+    (1, 512, 4096, 2, 8, 32, 1, None, GROUP),       # mxfp4 is 4-bit
+    (1, 512, 4096, 3, 4, 32, 1, None, GROUP),       # mxfp8 is 8-bit
+    (1, 512, 4096, 3, 8, 16, 1, None, GROUP),       # mxfp8 needs gs 32
+    (1, 512, 4096, 3, 8, 32, 1, A, GROUP),          # mxfp8 takes no biases
+    (1, 512, 4096, 0, 3, 32, 1, None, NULL),        # affine needs biases at any width
+    (50, 128, 1040, 0, 8, 32, 1, A, GROUP),         # K % gs != 0 at 8 bits
+    (64, 100, 32768, 3, 8, 32, 0, None, GROUP),     # natural mxfp8: 100 % 32 != 0
     (1, 512, 4096, 0, 4, 48, 1, A, GROUP),          # illegal affine group size
     (1, 512, 4096, 0, 4, 16, 1, A, GROUP),          # 16 is nvfp4 only
     (1, 512, 4096, 1, 4, 32, 1, None, GROUP),       # nvfp4 needs gs 16
@@ -71,7 +80,7 @@ def test_matmul_validation(args, code):
     (64, 100, 32768, 0, 4, 32, 0, A, GROUP),        # natural layout quantizes N: 100 % 32 != 0
     (1, 512, 4096, 2, 4, 16, 1, None, GROUP),       # mxfp4 needs gs 32
     (1, 512, 4096, 2, 4, 32, 1, A, GROUP),          # mxfp4 takes no biases
-    (1, 512, 4096, 3, 4, 32, 1, None, GROUP),       # unknown mode
+    (1, 512, 4096, 4, 4, 32, 1, None, GROUP),       # unknown mode
     (0, 512, 4096, 0, 4, 32, 1, A, SHAPE),
 ])
 def test_qmatmul_validation(M, N, K, qmode, bits, gs, trans, biases, code):
@@ -188,12 +197,37 @@ def test_packed_weight_validation():
     assert L.bi_matmul_swiglu(A, A, A, 64, 64, 128, 0, 0, A, 1 << 30, None) == UNSUP
 
 
+@pytest.mark.parametrize("args,code", [
+    # x, lhs, rhs, wq, scales, biases, y, M, x_rows, N, K, E, qmode, bits, gs, layout
+    ((None, A, A, A, A, A, A, 4, 4, 64, 256, 8, 0, 4, 32, 1), NULL),
+    ((A, A, None, A, A, A, A, 4, 4, 64, 256, 8, 0, 4, 32, 1), NULL),
+    ((A, A, A, A, A, None, A, 4, 4, 64, 256, 8, 0, 4, 32, 1), NULL),       # affine needs biases
+    ((A, None, A, A, A, A, A, 8, 4, 64, 256, 8, 0, 4, 32, 1), SHAPE),      # no lhs: x_rows >= M
+    ((A, A, A, A, A, A, A, 4, 4, 64, 256, 0, 0, 4, 32, 1), SHAPE),         # no experts
+    ((A, A, A, A, A, A, A, 4, 4, 64, 256, 1024, 0, 4, 32, 1), SHAPE),      # too many experts
+    ((A, A, A, A, A, A, A, 4, 4, 64, 256, 8, 0, 4, 32, 2), UNSUP),         # packed layout
+    ((A, A, A, A, A, None, A, 4, 4, 64, 256, 8, 3, 8, 32, 1), UNSUP),      # mxfp8
+    ((A, A, A, A, A, A, A, 4, 4, 64, 256, 8, 0, 8, 32, 1), UNSUP),         # affine 8-bit
+    ((A, A, A, A, A, A, A, 4, 4, 64, 1040, 8, 0, 4, 32, 1), GROUP),        # K % gs
+    ((A, A, A, A, A, A, A, 4, 4, 64, 256, 8, 1, 4, 16, 1), GROUP),         # nvfp4 takes no biases
+    ((A, P(0x10002), A, A, A, A, A, 4, 4, 64, 256, 8, 0, 4, 32, 1), ALIGN),
+])
+def test_gather_qmatmul_validation(args, code):
+    assert bi.lib().bi_gather_qmatmul(*args, None) == code
+
+
 def test_packed_qweight_validation():
     L = bi.lib()
     assert L.bi_packed_qweight_bytes(20, 256, 0, 4, 64) == 2 * 2 * (1024 + 16 * 2 * 4)
     assert L.bi_packed_qweight_bytes(16, 128, 1, 4, 16) == 1024 + 128
     assert L.bi_packed_qweight_bytes(16, 192, 0, 4, 64) == 0           # K % 128
     assert L.bi_packed_qweight_bytes(16, 128, 0, 4, 16) == 0           # affine gs 16
+    assert L.bi_packed_qweight_bytes(16, 128, 0, 8, 32) == 0           # 4-bit modes only
+    assert L.bi_packed_qweight_bytes(16, 128, 3, 8, 32) == 0
+    assert L.bi_pack_qweights(A, A, A, A, 16, 128, 0, 3, 32, None) == UNSUP
+    assert L.bi_pack_qweights(A, A, None, A, 16, 128, 3, 8, 32, None) == UNSUP
+    assert L.bi_qmatmul(A, A, None, None, A, 4, 16, 128, 3, 8, 32, 2, None) == UNSUP
+    assert L.bi_qmatmul(A, A, None, None, A, 4, 16, 128, 0, 6, 64, 2, None) == UNSUP
     assert L.bi_pack_qweights(A, A, None, A, 16, 128, 0, 4, 64, None) == NULL    # affine needs biases
     assert L.bi_pack_qweights(A, A, A, A, 16, 128, 1, 4, 16, None) == GROUP      # nvfp4 takes none
     assert L.bi_pack_qweights(A, A, A, A, 16, 192, 0, 4, 64, None) == SHAPE

@@ -157,6 +157,30 @@ def test_mxfp4_every_code_and_finite_scale(M):
     assert bits_equal(run(xb, wq, s, None, N, K, "mxfp4", 32, transposed), r)
 
 
+@pytest.mark.parametrize("transposed", [True, False])
+def test_nvfp4_every_code_at_every_scale_byte(transposed):
+    """One-hot rows of x read single dequantized weights: all 16 e2m1 codes
+    times every non-NaN e4m3 scale byte -- negative and subnormal scales
+    included -- equal the oracle bit for bit (each product is exact in
+    binary16).  Transposed: the streaming kernel (K = 128); natural: the
+    element-wise decode."""
+    scales = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    if transposed:
+        K, N = 128, scales.size
+        codes = np.tile(np.arange(16, dtype=np.uint32), (N, K // 16))          # [N, K]
+        s = np.repeat(scales[:, None], K // 16, axis=1)
+        M = 16
+    else:
+        K, N = 16, 16 * scales.size
+        codes = np.repeat(np.arange(16, dtype=np.uint32)[:, None], N, axis=1)  # row k = code k
+        s = np.tile(scales[None, :], (K, 1))
+        M = 16
+    wq = inputs.pack_nibbles(codes)
+    x = inputs.to_storage(np.eye(M, K, dtype=np.float32), "f16")
+    r = oracle.round_to(ref(x, wq, s, None, M, N, K, "nvfp4", 16, transposed), "f16")
+    assert bits_equal(run(x, wq, s, None, N, K, "nvfp4", 16, transposed), r)
+
+
 def test_mxfp4_extreme_scales_match_oracle():
     """Scales far outside binary16 (e = 0, 1, 100, 150, 254) and the NaN byte:
     the dequantized weights overflow to inf, flush to zero or are NaN exactly

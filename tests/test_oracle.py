@@ -452,6 +452,57 @@ def test_mxfp8_grid_values_round_trip():
     assert np.array_equal(deq, w)
 
 
+@pytest.mark.parametrize("transposed", [True, False])
+@pytest.mark.parametrize("sort_rows", [False, True])
+def test_gather_unit_scale_is_exact_per_expert(transposed, sort_rows):
+    """Expert matmul with scale 1 and bias -8 per expert and integer x: row m
+    equals x[lhs[m]] @ (codes[rhs[m]] - 8)^T in exact integer arithmetic."""
+    rng = np.random.default_rng(21)
+    T, topk, E, K, N, gs = 6, 2, 4, 256, 64, 32
+    rows, cols = (N, K) if transposed else (K, N)
+    codes = rng.integers(0, 16, size=(E, rows, cols)).astype(np.uint32)
+    wq = np.stack([inputs.pack_nibbles(c) for c in codes])
+    s = np.full((E, rows, cols // gs), 0x3C00, np.uint16)
+    b = np.full((E, rows, cols // gs), 0xC800, np.uint16)
+    x = inputs.integer_values(rng, (T, K), -4, 4, "f16")
+    rhs = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(T)]).reshape(-1).astype(np.int32)
+    lhs = np.repeat(np.arange(T, dtype=np.int32), topk)
+    if sort_rows:
+        order = np.argsort(rhs, kind="stable")
+        lhs, rhs = lhs[order], rhs[order]
+    y = oracle.gather_qmatmul(x, lhs, rhs, wq, s, b, N, K, oracle.AFFINE, gs, transposed)
+    xi = inputs.from_storage(x, "f16").astype(np.int64)
+    for m in range(rhs.size):
+        wmat = codes[rhs[m]].astype(np.int64) - 8
+        wmat = wmat if transposed else wmat.T
+        assert np.array_equal(y[m].astype(np.int64), xi[lhs[m]] @ wmat.T), m
+
+
+@pytest.mark.parametrize("qmode,gs,bits", [("nvfp4", 16, 4), ("affine", 64, 4), ("mxfp8", 32, 8)])
+def test_gather_rows_follow_their_expert_and_not_their_neighbours(qmode, gs, bits):
+    """Each row is the quantized matmul of its token with its expert (the
+    pinned qmatmul, bit for bit); permuting the rows permutes the outputs;
+    an out-of-range index gives a NaN row and leaves the others alone."""
+    T, topk, E, K, N = 5, 2, 3, 1040 if qmode == "nvfp4" else 1024, 48
+    qm = {"affine": oracle.AFFINE, "nvfp4": oracle.NVFP4, "mxfp8": oracle.MXFP8}[qmode]
+    x, lhs, rhs, wq, s, b = inputs.gather_case(T, topk, K, N, E, qmode, gs, True, seed=2, bits=bits)
+    y = oracle.gather_qmatmul(x, lhs, rhs, wq, s, b, N, K, qm, gs, True, bits=bits)
+    for m in range(rhs.size):
+        e = rhs[m]
+        one = oracle.qmatmul(x[lhs[m]:lhs[m] + 1], wq[e], s[e], None if b is None else b[e], 1, N, K, qm, gs, True,
+                             bits=bits)
+        assert np.array_equal(y[m:m + 1].view(np.uint32), one.view(np.uint32)), m
+    perm = np.random.default_rng(0).permutation(rhs.size)
+    yp = oracle.gather_qmatmul(x, lhs[perm], rhs[perm], wq, s, b, N, K, qm, gs, True, bits=bits)
+    assert np.array_equal(yp.view(np.uint32), y[perm].view(np.uint32))
+    bad = rhs.copy()
+    bad[3] = E
+    yb = oracle.gather_qmatmul(x, lhs, bad, wq, s, b, N, K, qm, gs, True, bits=bits)
+    assert np.all(np.isnan(yb[3]))
+    keep = np.arange(rhs.size) != 3
+    assert np.array_equal(yb[keep].view(np.uint32), y[keep].view(np.uint32))
+
+
 @pytest.mark.parametrize("gs", [32, 64, 128])
 def test_affine_quantize_dequantize_error_bound(gs):
     rng = np.random.default_rng(9)
