@@ -567,19 +567,20 @@ __global__ void pack_q_kernel(const uint32_t *__restrict__ wq, const void *__res
 }
 
 // Expert ("gather") matmul of a mixture-of-experts layer: row m of y is
-// x[lhs[m]] @ dequantize(W[rhs[m]])^T (or the natural-layout product).  One
-// workgroup per 16-column tile walks every row: a slab of up to kGatherSlab
-// rows is bucketed by expert in LDS (a counting sort), and each bucket runs
-// in chunks of up to 16 rows, so the rows of one MFMA tile share the weight
-// fragment and each used expert's columns are streamed once per slab.  A
-// chunk reduces exactly as qmatmul_kernel does (block b of K to wave b mod 8,
-// lane group g supplying [32g, 32g + 32) of the block, wave partials added in
-// order), so a row gets the bits of the plain quantized matmul of its token
-// with its expert -- whatever the other rows, their experts, their order or
-// which chunk it lands in.  Rows whose token or expert index is out of range
-// are written as NaN.
+// x[lhs[m]] @ dequantize(W[rhs[m]])^T (or the natural-layout product).
+// Workgroup (t, e) owns the 16 columns of tile t for expert e: it compacts the
+// rows routed to e (in ascending row order, a slab of up to kGatherSlab rows
+// at a time) into LDS and runs them 16 at a time, so the rows of one MFMA
+// tile share the weight fragment, each used expert's columns stream once per
+// slab, and the experts proceed in parallel.  A chunk reduces exactly as
+// qmatmul_kernel does (block b of K to wave b mod 8, lane group g supplying
+// [32g, 32g + 32) of the block, wave partials added in order), so a row gets
+// the bits of the plain quantized matmul of its token with its expert --
+// whatever the other rows, their experts, their order or which chunk it lands
+// in.  The workgroups of e = E write NaN to the rows whose token or expert
+// index is out of range.
 constexpr int kGatherSlab = 4096;
-constexpr int kGatherMaxExperts = 1023;       // + 1 bucket for invalid rows
+constexpr int kGatherMaxExperts = 1023;
 
 template <int QM, int GS, bool TRANS, bool WVEC>
 __global__ __launch_bounds__(kQWaves * kWave)
@@ -592,106 +593,259 @@ void gather_q_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__
     constexpr int SB = QM == BI_AFFINE ? 2 : 1;                 // bytes per scale entry
     __shared__ float red[P][16][17];
     __shared__ int perm[kGatherSlab];
-    __shared__ int start[kGatherMaxExperts + 2];                // bucket starts; [E + 1] = slab size
-    __shared__ int cur[kGatherMaxExperts + 1];
-    __shared__ int wsum[P];
+    __shared__ int wcnt[P];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
+    const int e = (int)blockIdx.y;
     const int64_t n0 = (int64_t)blockIdx.x * 16, n = n0 + c;
     const bool nok = n < N;
     const int64_t nblocks = cdiv(K, kQBlock);
     const bool xvec = (K % 8) == 0 && aligned16(x);
     const int64_t words_e = N * K / 8, groups_e = N * K / GS;   // per expert
+    const uint32_t *we = wq + (int64_t)(e < E ? e : 0) * words_e;
+    const void *se = (const uint8_t *)scales + (int64_t)(e < E ? e : 0) * groups_e * SB;
+    const uint16_t *be = biases ? biases + (int64_t)(e < E ? e : 0) * groups_e : nullptr;
 
     auto bucket = [&](int64_t m) -> int {
-        const int64_t e = rhs[m], xr = lhs ? (int64_t)lhs[m] : m;
-        return (e >= 0 && e < E && xr >= 0 && xr < x_rows) ? (int)e : E;
+        const int64_t r = rhs[m], xr = lhs ? (int64_t)lhs[m] : m;
+        return (r >= 0 && r < E && xr >= 0 && xr < x_rows) ? (int)r : E;
     };
 
     for (int64_t s0 = 0; s0 < M; s0 += kGatherSlab) {
         const int ns = (int)(M - s0 < kGatherSlab ? M - s0 : kGatherSlab);
-        for (int i = tid; i <= E; i += NT) cur[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < ns; i += NT) atomicAdd(&cur[bucket(s0 + i)], 1);
-        __syncthreads();
-        // exclusive scan of the E + 1 counts: thread t owns entries 2t, 2t + 1
-        const int a0 = 2 * tid <= E ? cur[2 * tid] : 0, a1 = 2 * tid + 1 <= E ? cur[2 * tid + 1] : 0;
-        int inc = a0 + a1;
+        // compact the slab's rows of bucket e into perm, in ascending order
+        int found = 0;
+        for (int i0 = 0; i0 < ns; i0 += NT) {
+            const int i = i0 + tid;
+            const bool hit = i < ns && bucket(s0 + i) == e;
+            const uint64_t mask = __ballot(hit);
+            if (lane == 0) wcnt[wave] = __popcll(mask);
+            __syncthreads();
+            int off = found, tot = 0;
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int v = __shfl_up(inc, off, kWave);
-            if (lane >= off) inc += v;
+            for (int w = 0; w < P; ++w) {
+                const int cw = wcnt[w];
+                off += w < wave ? cw : 0;
+                tot += cw;
+            }
+            if (hit) perm[off + __popcll(mask & ((1ull << lane) - 1ull))] = i;
+            found += tot;
+            __syncthreads();                                    // wcnt is rewritten next round
         }
-        if (lane == kWave - 1) wsum[wave] = inc;
-        __syncthreads();
-        int base = 0;
-        for (int w = 0; w < wave; ++w) base += wsum[w];
-        const int ex = base + inc - (a0 + a1);
-        if (2 * tid <= E) start[2 * tid] = ex;
-        if (2 * tid + 1 <= E) start[2 * tid + 1] = ex + a0;
-        if (tid == 0) start[E + 1] = ns;
-        __syncthreads();
-        for (int i = tid; i <= E; i += NT) cur[i] = start[i];
-        __syncthreads();
-        for (int i = tid; i < ns; i += NT) perm[atomicAdd(&cur[bucket(s0 + i)], 1)] = i;
-        __syncthreads();
-
-        for (int e = 0; e < E; ++e) {
-            const int b0 = start[e], b1 = start[e + 1];
-            if (b0 == b1) continue;
-            const uint32_t *we = wq + (int64_t)e * words_e;
-            const void *se = (const uint8_t *)scales + (int64_t)e * groups_e * SB;
-            const uint16_t *be = biases ? biases + (int64_t)e * groups_e : nullptr;
-            for (int r0 = b0; r0 < b1; r0 += 16) {
-                const int nr = b1 - r0 < 16 ? b1 - r0 : 16;
-                const bool rok = c < nr;
-                const int64_t m = s0 + perm[r0 + (rok ? c : 0)];
-                const uint16_t *xrow = x + (lhs ? (int64_t)lhs[m] : m) * K;
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int64_t b = wave; b < nblocks; b += P) {
-                    const int64_t kbase = b * kQBlock + (int64_t)g * 32;
-                    if constexpr (TRANS) {
-                        uint4 A[4], Bf[4];
-                        qload_trans<QM, GS, WVEC>(Bf, we, se, be, nok ? n : 0, nok, K, kbase);
+        if (e == E) {                                           // rows with a bad index: NaN
+            for (int i = tid; i < found * 16; i += NT) {
+                const int64_t col = n0 + (i & 15);
+                if (col < N) y[(s0 + perm[i >> 4]) * N + col] = 0x7e00u;
+            }
+            __syncthreads();
+            continue;
+        }
+        for (int r0 = 0; r0 < found; r0 += 16) {
+            const int nr = found - r0 < 16 ? found - r0 : 16;
+            const bool rok = c < nr;
+            const int64_t m = s0 + perm[r0 + (rok ? c : 0)];
+            const uint16_t *xrow = x + (lhs ? (int64_t)lhs[m] : m) * K;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int64_t b = wave; b < nblocks; b += P) {
+                const int64_t kbase = b * kQBlock + (int64_t)g * 32;
+                if constexpr (TRANS) {
+                    uint4 A[4], Bf[4];
+                    qload_trans<QM, GS, WVEC>(Bf, we, se, be, nok ? n : 0, nok, K, kbase);
 #pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            A[s] = xvec ? load_chunk<F16, true>(xrow, kbase + s * 8, K, rok)
-                                        : load_chunk<F16, false>(xrow, kbase + s * 8, K, rok);
+                    for (int s = 0; s < 4; ++s)
+                        A[s] = xvec ? load_chunk<F16, true>(xrow, kbase + s * 8, K, rok)
+                                    : load_chunk<F16, false>(xrow, kbase + s * 8, K, rok);
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) acc = qmfma(A[s], Bf[s], acc);
-                    } else {
-                        // element-wise gathers: one step of 8 at a time keeps the registers bounded
+                    for (int s = 0; s < 4; ++s) acc = qmfma(A[s], Bf[s], acc);
+                } else {
+                    // element-wise gathers: one step of 8 at a time keeps the registers bounded
 #pragma unroll 1
-                        for (int s = 0; s < 4; ++s) {
-                            const uint4 Bs = qload_nat8<QM, GS>(we, se, be, nok ? n : 0, nok, N, K, kbase + s * 8);
-                            const uint4 As = xvec ? load_chunk<F16, true>(xrow, kbase + s * 8, K, rok)
-                                                  : load_chunk<F16, false>(xrow, kbase + s * 8, K, rok);
-                            acc = qmfma(As, Bs, acc);
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
+                    for (int s = 0; s < 4; ++s) {
+                        const uint4 Bs = qload_nat8<QM, GS>(we, se, be, nok ? n : 0, nok, N, K, kbase + s * 8);
+                        const uint4 As = xvec ? load_chunk<F16, true>(xrow, kbase + s * 8, K, rok)
+                                              : load_chunk<F16, false>(xrow, kbase + s * 8, K, rok);
+                        acc = qmfma(As, Bs, acc);
                     }
                 }
+            }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][c] = acc[r];
-                __syncthreads();
-                if (tid < 256) {
-                    const int r = tid >> 4, cc = tid & 15;
-                    if (r < nr && n0 + cc < N) {
-                        float v = red[0][r][cc];
+            for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][c] = acc[r];
+            __syncthreads();
+            if (tid < 256) {
+                const int r = tid >> 4, cc = tid & 15;
+                if (r < nr && n0 + cc < N) {
+                    float v = red[0][r][cc];
 #pragma unroll
-                        for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
-                        y[(s0 + perm[r0 + r]) * N + n0 + cc] = F16::narrow(v);
-                    }
+                    for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+                    y[(s0 + perm[r0 + r]) * N + n0 + cc] = F16::narrow(v);
                 }
-                __syncthreads();
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Streaming form of the expert matmul for at most 16 rows (a decode step),
+// transposed weights, K % 128 == 0, 16-byte aligned x and wq.  The workgroup
+// lists the distinct experts of the rows (ascending) and walks the tiles
+// (expert, 16*NS columns) of that list as qmatmul_stream_kernel walks its
+// column tiles: each wave streams its (tile, block) items -- packed words,
+// group constants and x chunks -- through a D-deep register ring.  A-operand
+// row c is row c of the call, its x chunk zero unless the row is routed to
+// the tile's expert; only such rows are stored.  Per row the tree is
+// qmatmul_stream_kernel's, hence the plain quantized matmul's bits.
+template <int QM, int GS, int NS, int D>
+__global__ __launch_bounds__(kQWaves * kWave, 2)
+void gather_q_stream_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ lhs,
+                            const int32_t *__restrict__ rhs, const uint32_t *__restrict__ wq,
+                            const void *__restrict__ scales, const uint16_t *__restrict__ biases,
+                            uint16_t *__restrict__ y, int64_t M, int64_t x_rows, int64_t N, int64_t K, int E, int ntn)
+{
+    constexpr int P = kQWaves, TC = NS * 16, NT = kQWaves * kWave;
+    constexpr int SB = QM == BI_AFFINE ? 2 : 1;                 // bytes per scale entry
+    __shared__ float red[P][16][TC + 1];
+    __shared__ int s_bucket[16], s_active[16], s_nact;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    if (tid < 16) {
+        int bk = -1;                                            // -1: no such row; E: a bad index
+        if (tid < M) {
+            const int64_t r = rhs[tid], xi = lhs ? (int64_t)lhs[tid] : tid;
+            bk = (r >= 0 && r < E && xi >= 0 && xi < x_rows) ? (int)r : E;
+        }
+        s_bucket[tid] = bk;
+    }
+    __syncthreads();
+    if (tid == 0) {                                             // distinct experts, ascending
+        int na = 0, last = -1;
+        for (;;) {
+            int best = E;
+            for (int r = 0; r < 16; ++r) {
+                const int b = s_bucket[r];
+                if (b > last && b < best) best = b;
+            }
+            if (best == E) break;
+            s_active[na++] = best;
+            last = best;
+        }
+        s_nact = na;
+    }
+    __syncthreads();
+    const int ntiles = s_nact * ntn;
+    const int nb = (int)(K / kQBlock);
+    const int nmine = wave < nb ? (nb - wave + P - 1) / P : 0;        // blocks of this wave per tile
+    const int mytiles = (int)blockIdx.x < ntiles ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    const int items = mytiles * nmine;
+    const int64_t words = K / 8, groups = K / GS, words_e = N * K / 8, groups_e = N * K / GS;
+    const int mybk = s_bucket[c];
+    const bool myok = mybk >= 0 && mybk < E;
+    // x row of A-operand row c (rows without a valid expert read row 0 and are never stored)
+    const uint16_t *xr = x + (myok ? (lhs ? (int64_t)lhs[c] : (int64_t)c) : 0) * K + g * 32;
+
+    uint4 Wr[D][NS], Xr[D][4];
+    uint32_t Sr[D][NS], Br[D][NS];
+    int pu = 0, pj = 0;
+    auto load_next = [&](uint4 (&Wd)[NS], uint32_t (&Sd)[NS], uint32_t (&Bd)[NS], uint4 (&Xd)[4]) {
+        const int t = (int)blockIdx.x + pu * (int)gridDim.x;
+        const int e = s_active[t / ntn], ct = t % ntn;
+        const uint32_t *we = wq + (int64_t)e * words_e;
+        const uint8_t *se = (const uint8_t *)scales + (int64_t)e * groups_e * SB;
+        const int64_t kb = (int64_t)(wave + pj * P) * kQBlock + g * 32;     // this lane's first code
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            int64_t n = (int64_t)ct * TC + j * 16 + c;
+            n = n < N ? n : N - 1;                                      // padding columns read a real row
+            Wd[j] = *reinterpret_cast<const uint4 *>(we + n * words + kb / 8);
+            const int64_t gi = n * groups + kb / GS;
+            if (QM == BI_AFFINE) {
+                Sd[j] = ((const uint16_t *)se)[gi];
+                Bd[j] = (biases + (int64_t)e * groups_e)[gi];
+            } else if (QM == BI_NVFP4) {
+                Sd[j] = ((const uint16_t *)se)[gi / 2];                 // the lane's two group bytes
+                Bd[j] = 0;
+            } else {
+                Sd[j] = se[gi];                                         // the lane's one group byte
+                Bd[j] = 0;
             }
         }
-        for (int i = start[E] * 16 + tid; i < ns * 16; i += NT) {      // invalid rows: NaN
-            const int64_t col = n0 + (i & 15);
-            if (col < N) y[(s0 + perm[i >> 4]) * N + col] = 0x7e00u;
+        if (mybk == e) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xd[s] = *reinterpret_cast<const uint4 *>(xr + (kb - g * 32) + s * 8);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xd[s] = make_uint4(0, 0, 0, 0);
         }
-        __syncthreads();                                                // perm and start are reused
+        if (pj + 1 < nmine) {
+            ++pj;
+        } else if (pu + 1 < mytiles) {
+            pj = 0;
+            ++pu;
+        }
+    };
+    f32x4 acc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto finish_tile = [&](int u) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][j * 16 + c] = acc[j][r];
+            acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+        const int t = (int)blockIdx.x + u * (int)gridDim.x;
+        const int e = s_active[t / ntn];
+        const int64_t n0 = (int64_t)(t % ntn) * TC;
+        for (int o = tid; o < 16 * TC; o += NT) {
+            const int r = o / TC, cc = o % TC;
+            const int64_t col = n0 + cc;
+            if (s_bucket[r] != e || col >= N) continue;
+            float v = red[0][r][cc];
+#pragma unroll
+            for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+            y[(int64_t)r * N + col] = F16::narrow(v);
+        }
+        __syncthreads();
+    };
+
+    if (items > 0) {
+        int cu = 0, cj = 0;
+        static_for<0, D - 1>([&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+            load_next(Wr[d], Sr[d], Br[d], Xr[d]);
+        });
+        for (int i = 0; i < items; i += D) {
+            static_for<0, D>([&](auto dc) {
+                constexpr int d = decltype(dc)::value;
+                constexpr int dn = (d + D - 1) % D;
+                load_next(Wr[dn], Sr[dn], Br[dn], Xr[dn]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i + d < items) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                        for (int j = 0; j < NS; ++j) {
+                            const QGroup<QM> gr = group_from_raw<QM>(Sr[d][j], Br[d][j], s);
+                            const uint32_t wv = s == 0 ? Wr[d][j].x : s == 1 ? Wr[d][j].y : s == 2 ? Wr[d][j].z : Wr[d][j].w;
+                            acc[j] = qmfma(Xr[d][s], deq_word<QM>(wv, gr), acc[j]);
+                        }
+                    }
+                    if (++cj == nmine) {
+                        finish_tile(cu);
+                        cj = 0;
+                        ++cu;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+    } else {
+        for (int u = 0; u < mytiles; ++u) finish_tile(u);
     }
+    // rows with a bad index: NaN
+    for (int64_t i = (int64_t)blockIdx.x * NT + tid; i < M * N; i += (int64_t)gridDim.x * NT)
+        if (s_bucket[i / N] == E) y[i] = 0x7e00u;
 }
 
 template <int QM, int GS>
@@ -699,8 +853,23 @@ static void launch_gather(const void *x, const int32_t *lhs, const int32_t *rhs,
                           const void *b, void *y, int64_t M, int64_t x_rows, int64_t N, int64_t K, int E, int layout,
                           hipStream_t st)
 {
-    const dim3 grid((unsigned)cdiv(N, 16)), block(kQWaves * kWave);
+    // one workgroup per (16-column tile, expert), plus one per tile for the rows with a bad index
+    const dim3 grid((unsigned)cdiv(N, 16), (unsigned)(E + 1)), block(kQWaves * kWave);
     const uint16_t *bz = (const uint16_t *)b;
+    if (layout == 1 && M <= 16 && K % kQBlock == 0 && host_aligned16(x) && host_aligned16(wq) &&
+        cdiv(N, 16) <= (1ll << 24)) {
+        const int ns = N >= 8192 ? 2 : 1;
+        const int64_t ntn = cdiv(N, 16 * ns);
+        const int64_t tiles = std::min<int64_t>(M, E) * ntn;            // at most this many (expert, tile) pairs
+        const int64_t g = std::min<int64_t>(tiles, (int64_t)device_cu_count() * 2);
+        if (ns == 2)
+            launch_kernel((gather_q_stream_kernel<QM, GS, 2, 3>), dim3((unsigned)g), block, 0, st, (const uint16_t *)x,
+                          lhs, rhs, wq, s, bz, (uint16_t *)y, M, x_rows, N, K, E, (int)ntn);
+        else
+            launch_kernel((gather_q_stream_kernel<QM, GS, 1, 3>), dim3((unsigned)g), block, 0, st, (const uint16_t *)x,
+                          lhs, rhs, wq, s, bz, (uint16_t *)y, M, x_rows, N, K, E, (int)ntn);
+        return;
+    }
     if (layout == 0)
         launch_kernel((gather_q_kernel<QM, GS, false, false>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs, wq, s,
                       bz, (uint16_t *)y, M, x_rows, N, K, E);

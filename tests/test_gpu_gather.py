@@ -48,7 +48,8 @@ CASES = [
     # mode, gs, T, topk, E, K, N, transposed, sorted
     ("nvfp4", 16, 32, 2, 8, 1040, 128, True, True),       # sorted gather, 64 rows, K % 32 == 16
     ("nvfp4", 16, 25, 2, 8, 1040, 128, True, False),      # unsorted gather, 50 rows
-    ("affine", 64, 8, 2, 8, 4096, 512, True, False),      # decode-sized MoE step
+    ("affine", 64, 8, 2, 8, 4096, 512, True, False),      # decode-sized MoE step (streaming form, M <= 16)
+    ("nvfp4", 16, 6, 2, 8, 2048, 8192, True, True),       # streaming form, two column groups per tile
     ("mxfp4", 32, 16, 4, 16, 2048, 256, True, True),
     ("affine", 32, 12, 2, 4, 512, 96, False, False),      # natural layout
     ("nvfp4", 16, 10, 2, 4, 1040, 64, False, True),
@@ -100,10 +101,11 @@ def test_gather_more_rows_than_one_slab():
     assert bits_equal(gather(x, lhs[pick], rhs[pick], w, N, K, mode, gs, True), y[pick])
 
 
-def test_gather_out_of_range_rows_are_nan_and_fenced():
+@pytest.mark.parametrize("K", [1040, 1024])
+def test_gather_out_of_range_rows_are_nan_and_fenced(K):
     """Rows with a bad expert or token index are NaN; the others keep their
-    bits; nothing is written outside y."""
-    mode, gs, T, topk, E, K, N = "nvfp4", 16, 6, 2, 4, 1040, 80
+    bits; nothing is written outside y (K = 1024: the streaming form)."""
+    mode, gs, T, topk, E, N = "nvfp4", 16, 6, 2, 4, 80
     x, lhs, rhs, wq, s, b = inputs.gather_case(T, topk, K, N, E, mode, gs, True, False, seed=3)
     w = dev_w(wq, s, b)
     y = gather(x, lhs, rhs, w, N, K, mode, gs, True)
@@ -120,6 +122,14 @@ def test_gather_out_of_range_rows_are_nan_and_fenced():
     bad[[2, 5, 7]] = True
     assert np.all(np.isnan(g[bad]))
     assert bits_equal(to_np(yg.view)[~bad], y[~bad])
+
+
+def test_gather_every_row_bad_is_all_nan():
+    mode, gs, T, topk, E, K, N = "affine", 32, 4, 2, 3, 512, 64
+    x, lhs, rhs, wq, s, b = inputs.gather_case(T, topk, K, N, E, mode, gs, True, False, seed=8)
+    w = dev_w(wq, s, b)
+    y = gather(x, lhs, np.full_like(rhs, E), w, N, K, mode, gs, True)
+    assert np.all(np.isnan(inputs.from_storage(y, "f16")))
 
 
 def test_gather_200_runs_one_result():
