@@ -391,6 +391,23 @@ def op_sweep(torch, bi, dev):
         res["sdpa"][f"B{Bn} Q{Q} Lk{Lk}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1),
                                               "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
         del ks, vs
+    # causal prefill: Q = Lk (a whole prompt in one call), flops over the visible (query, key) pairs
+    res["prefill"] = {}
+    for Bn, Q in ((1, 512), (1, 2048), (8, 512), (64, 512)):
+        Lk = Q
+        ks = torch.randn(Bn, Hkv, Lk, D, device=dev).to(bf)
+        vs = torch.randn(Bn, Hkv, Lk, D, device=dev).to(bf)
+        q = torch.randn(Bn, Q, Hq, D, device=dev).to(bf)
+        kv = torch.full((Bn,), Lk, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        wsd = torch.empty(bi.sdpa_workspace_bytes(Bn, Q, Lk, Hq, D), dtype=torch.uint8, device=dev)
+        t = _time_kernel(torch, bi, lambda i: bi.sdpa(q, ks, vs, kv, Lk, 0.088, True, out=o, ws=wsd, head_major=True),
+                         reps=5, launches=2)
+        pairs = Q * (Q + 1) // 2
+        tf = 4 * Bn * Hq * D * pairs / (t * 1e-3) / 1e12
+        res["prefill"][f"B{Bn} Q{Q} Lk{Lk} causal"] = {"us": round(t * 1e3, 2), "tflops": round(tf, 2),
+                                                       "frac_mfma": round(tf / 2500.0, 4)}
+        del ks, vs, wsd
     torch.cuda.empty_cache()
     return res
 

@@ -30,6 +30,8 @@
 // independent there), so the number of queries Q, the GQA group, the batch and
 // where the row sits in its tile leave its bits unchanged; a query of a causal
 // verify block and a lone query at the same position reduce identically.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace bi {
@@ -41,6 +43,7 @@ constexpr int kKeysPerWave = kChunk / kAttnWaves;
 constexpr int kPartStride = kHeadDim + 4;   // floats per (row, chunk) partial: o[D], m, l, pad
 constexpr int kVStride = kHeadDim + 2;      // LDS row stride (elements) of the staged V tile
 constexpr int64_t kMaxKv = 1ll << 20;     // keeps pass 2's per-chunk weights within 32 KiB of LDS
+constexpr int kAttnMinTiles = 4;     // fewest query-row tiles (of 16) per work item when a prompt is split
 
 __device__ inline f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c)
 {
@@ -57,8 +60,8 @@ template <> __device__ inline f32x4 mfma16<BF16>(uint4 a, uint4 b, f32x4 c) { re
 template <> __device__ inline f32x4 mfma16<F16>(uint4 a, uint4 b, f32x4 c) { return mfma_f16(a, b, c); }
 
 struct AttnShape {
-    int64_t B, Q, Lcap, nchunks, max_kv;
-    int Hq, Hkv, G;
+    int64_t B, Q, Lcap, nchunks, max_kv, nmg;     // nmg: row groups of mgt 16-row tiles per (b, c, hk)
+    int Hq, Hkv, G, mgt;
     float scale;
     int causal;
     int64_t ks, hs;       // cache strides (elements) between consecutive keys and between KV heads
@@ -95,11 +98,15 @@ __device__ inline void transpose8x8_b16(uint4 (&m)[8])
 }
 
 // Pass 1 as a persistent, software-pipelined kernel.  Work item = (sequence
-// b, chunk c, KV head hk); a fixed grid of workgroups walks the item ids
-// t = blockIdx.x, blockIdx.x + gridDim.x, ...  The ids are ordered so that
-// the items of all KV heads of one (b, c) are processed together on one XCD:
-// id t -> XCD t % 8 (the hardware's round-robin when gridDim.x % 8 == 0),
-// hk = (t / 8) % Hkv, (b, c) = (t / (8 Hkv)) * 8 + t % 8; their key rows
+// b, chunk c, KV head hk, row group mg) -- mg picks sh.mgt of the 16-row query
+// tiles, so a long prompt with few sequences spreads over many workgroups (at
+// decode and verify sizes there is one group); a fixed grid of workgroups
+// walks the item ids
+// t = blockIdx.x, blockIdx.x + gridDim.x, ...  With u = t / nmg and mg = t %
+// nmg, the ids are ordered so that the items of all KV heads of one (b, c)
+// are processed together on one XCD at decode sizes (nmg = 1): id u -> XCD u
+// % 8 (the hardware's round-robin when gridDim.x % 8 == 0), hk = (u / 8) %
+// Hkv, (b, c) = (u / (8 Hkv)) * 8 + u % 8; their key rows
 // [b][pos][0..Hkv)[0..D) are contiguous in the cache.  Inside an item, wave w
 // owns keys [64w, 64w + 64) of the chunk (the frozen tree above).  The
 // resident workgroups drift out of step, so the cache streams without the
@@ -111,7 +118,7 @@ __device__ inline void transpose8x8_b16(uint4 (&m)[8])
 //        transposed in place to vr[s2][j] = those 8 keys at d = 8 c16 + j,
 //        the MFMA B operand of P . V (k slot 8 g4 + e of step s2 = key
 //        32 s2 + 8 g4 + e, column c16 = d 8 c16 + j of output tile j).
-template <typename S>
+template <typename S, bool MG>
 __global__ __launch_bounds__(kAttnWaves * kWave, 2)
 void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                        const uint16_t *__restrict__ v, const int32_t *__restrict__ kv_len,
@@ -133,10 +140,12 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
     // host cannot validate, so it is clamped to max_kv, which keeps every
     // access inside the cache and the workspace even for a bad value.
     struct Item {
-        int b, c, hk, kvlen;
+        int b, c, hk, kvlen, mg;
     };
-    auto decode = [&](int64_t t) {
+    auto decode = [&](int64_t t0) {
         Item it;
+        const int64_t t = MG ? t0 / sh.nmg : t0;
+        it.mg = MG ? (int)(t0 - t * sh.nmg) : 0;
         it.hk = (int)((t >> 3) % sh.Hkv);
         const int64_t bc = (t >> 3) / sh.Hkv * 8 + (t & 7);
         const bool exists = bc < nitems;
@@ -147,8 +156,12 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
     };
     const int Qi = (int)sh.Q;
     auto last_key = [&](int kvlen, int j) { return sh.causal ? kvlen - Qi + j : kvlen - 1; };
-    // an item has work when it exists and its first key is visible to the last row
-    auto has_work = [&](const Item &it) { return it.c >= 0 && it.c * kChunk <= last_key(it.kvlen, Qi - 1); };
+    // an item has work when it exists and its first key is visible to the last row of its group
+    auto has_work = [&](const Item &it) {
+        if (!MG) return it.c >= 0 && it.c * kChunk <= last_key(it.kvlen, Qi - 1);
+        const int rl = min(R, (it.mg + 1) * sh.mgt * 16) - 1;
+        return it.c >= 0 && it.c * kChunk <= last_key(it.kvlen, rl / sh.G);
+    };
     auto next_id = [&](int64_t t) {
         for (; t < nid; t += gridDim.x)
             if (has_work(decode(t))) break;
@@ -212,13 +225,14 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
         const Item it = decode(t);
         const int key0 = it.c * kChunk;
         const int wkey0 = key0 + wave * kKeysPerWave;
-        load_q(it, 0, qf);
+        const int mt0 = MG ? it.mg * sh.mgt : 0, mt1 = MG ? min(ntm, mt0 + sh.mgt) : ntm;
+        load_q(it, mt0, qf);
         load_k(it, kf);
         load_v(it, vr);
         transpose8x8_b16(vr[0]);                       // this item's V as the P . V B operand
         transpose8x8_b16(vr[1]);
 
-        for (int mt = 0; mt < ntm; ++mt) {
+        for (int mt = mt0; mt < mt1; ++mt) {
             // Rows of the accumulator layout held by this lane: 4 g4 + i.
             int lastk[4];
             bool rowok[4];
@@ -232,7 +246,7 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
             // Tile-uniform skip: no row of this tile reaches this chunk.
             const int rlast = mt * 16 + 15 < R ? mt * 16 + 15 : R - 1;
             const bool any = last_key(it.kvlen, rlast / sh.G) >= key0;
-            if (mt > 0) load_q(it, mt, qf);
+            if (mt > mt0) load_q(it, mt, qf);
 
             // scores: tile kt -> lane (g4, c16) reg i = row 4 g4 + i, key wkey0 + 16 kt + c16
             float sc[4][4];
@@ -411,10 +425,14 @@ static void launch_attn(const void *q, const void *k, const void *v, void *o, co
 {
     // item ids (padded to whole groups of 8); a persistent grid of two
     // workgroups per CU, a multiple of 8 so that a workgroup stays on one XCD
-    const int64_t nid = cdiv(sh.B * sh.nchunks, 8) * 8 * sh.Hkv;
+    const int64_t nid = cdiv(sh.B * sh.nchunks, 8) * 8 * sh.Hkv * sh.nmg;
     const int64_t grid = std::min<int64_t>(nid, (int64_t)device_cu_count() * 2 / 8 * 8);
-    launch_kernel((attn_chunk_kernel<S>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st,
-                       (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, part, sh, nid);
+    if (sh.nmg > 1)
+        launch_kernel((attn_chunk_kernel<S, true>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st,
+                      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, part, sh, nid);
+    else
+        launch_kernel((attn_chunk_kernel<S, false>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st,
+                      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, part, sh, nid);
     const size_t smem = (size_t)sh.nchunks * 2 * sizeof(float);
     launch_kernel((attn_merge_kernel<S>), dim3((unsigned)(sh.B * sh.Q * sh.Hq)), dim3(kHeadDim), smem, st,
                        (const float *)part, kv_len, (uint16_t *)o, sh, chunk);
@@ -443,7 +461,15 @@ extern "C" bi_status bi_sdpa(const void *q, const void *k, const void *v, void *
     if (ws_bytes < bi_sdpa_workspace_bytes(B, Q, max_kv_len, Hq, D)) return BI_ERR_WORKSPACE;
     // kv_layout 0: [B, Lcap, Hkv, D]; 1: [B, Hkv, Lcap, D] (head-major)
     const int64_t ks = kv_layout ? (int64_t)D : (int64_t)Hkv * D, hs = kv_layout ? Lcap * D : (int64_t)D;
-    AttnShape sh{B, Q, Lcap, cdiv(max_kv_len, kChunk), max_kv_len, Hq, Hkv, Hq / Hkv, scale, causal ? 1 : 0, ks, hs};
+    // query-row groups: when the (sequence, chunk, head) items alone give fewer
+    // than two per workgroup slot, split the rows so that about 4096 ids exist
+    // (half of a causal prompt's (chunk, rows) pairs being empty), never under
+    // kAttnMinTiles tiles each; otherwise one group
+    const int64_t ntm = cdiv(Q * (Hq / Hkv), 16), nbase = cdiv(B * cdiv(max_kv_len, kChunk), 8) * 8 * Hkv;
+    const int64_t ngroups = nbase >= 1024 ? 1 : std::max<int64_t>(1, cdiv(4096, nbase));
+    const int64_t mgt = std::max<int64_t>(kAttnMinTiles, cdiv(ntm, ngroups));
+    AttnShape sh{B, Q, Lcap, cdiv(max_kv_len, kChunk), max_kv_len, cdiv(ntm, mgt), Hq, Hkv, Hq / Hkv, (int)std::min<int64_t>(mgt, ntm),
+                 scale, causal ? 1 : 0, ks, hs};
     (void)hipGetLastError();
     if (dtype == BI_BF16) launch_attn<BF16>(q, k, v, o, kv_len, (float *)ws, sh, kChunk, stream);
     else launch_attn<F16>(q, k, v, o, kv_len, (float *)ws, sh, kChunk, stream);
