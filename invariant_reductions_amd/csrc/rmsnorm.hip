@@ -144,14 +144,43 @@ void rmsnorm_kernel(const typename S::store_t *x, const typename S::store_t *__r
             const int64_t v = lane + (int64_t)i * kWave;
             wc[i] = load_chunk<S, VEC>(w, v * E, H, v < nch);
         }
+        if constexpr (ADD) {
+            // every load of x and r is issued before the first store to xo: xo
+            // may alias x, so a store would otherwise hold back the loads after it
+            uint4 ra[kNormCached];
 #pragma unroll
-        for (int i = 0; i < kNormCached; ++i) {
-            const int64_t v = lane + (int64_t)i * kWave;
-            cache[i] = row_chunk<S, VEC, ADD>(xr, rr, xor_, v, H, v < nch);
-            float xv[E];
-            chunk_vals<S>(cache[i], xv);
+            for (int i = 0; i < kNormCached; ++i) {
+                const int64_t v = lane + (int64_t)i * kWave;
+                cache[i] = load_chunk<S, VEC>(xr, v * E, H, v < nch);
+                ra[i] = load_chunk<S, VEC>(rr, v * E, H, v < nch);
+            }
 #pragma unroll
-            for (int e = 0; e < E; ++e) ss = __builtin_fmaf(xv[e], xv[e], ss);
+            for (int i = 0; i < kNormCached; ++i) {
+                const int64_t v = lane + (int64_t)i * kWave;
+                float av[E], bv[E], sv[E];
+                chunk_vals<S>(cache[i], av);
+                chunk_vals<S>(ra[i], bv);
+                typename S::store_t tmp[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    tmp[e] = S::narrow(av[e] + bv[e]);
+                    sv[e] = S::widen(tmp[e]);
+                }
+                if (v < nch) store_chunk<S, VEC>(xor_, v * E, H, sv);
+                cache[i] = __builtin_bit_cast(uint4, tmp);
+#pragma unroll
+                for (int e = 0; e < E; ++e) ss = __builtin_fmaf(sv[e], sv[e], ss);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kNormCached; ++i) {
+                const int64_t v = lane + (int64_t)i * kWave;
+                cache[i] = row_chunk<S, VEC, ADD>(xr, rr, xor_, v, H, v < nch);
+                float xv[E];
+                chunk_vals<S>(cache[i], xv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) ss = __builtin_fmaf(xv[e], xv[e], ss);
+            }
         }
         ss = wave_sum_butterfly(ss);
         const float inv = 1.0f / sqrtf(ss / (float)H + eps);
