@@ -82,7 +82,7 @@ def measured_traffic():
 
 def cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids, budget_s):
     """The oracle's decode step on the host, repeated until `budget_s` seconds
-    have passed (at least one step, at most four)."""
+    have passed (at least one step, at most sixteen)."""
     import oracle
     from oracle import decoder as odec
     from invariant_reductions_amd.inputs import rope_tables
@@ -90,7 +90,7 @@ def cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids, budget_s):
     kv = np.full(B, ctx, np.int32)
     t0 = time.perf_counter()
     n = 0
-    while n < 4:
+    while n < 16:
         odec.decode_step(W, cfg, ids, kc_host, vc_host, kv, cos_t, sin_t)
         n += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -434,9 +434,8 @@ def qmatmul_decode(torch, bi, dev):
     """Quantized matmul at decode shapes (M = 8; K = N = 4096 and the MLP
     shape 28672 x 4096), cold: the seeded quantized weight plus bit-permuted
     copies (distinct bytes, same sizes) rotated so no launch finds its weight
-    in a cache.  Transposed [N, K*bits/32] weights, and for the 4-bit modes
-    also the tile-packed layout; kernel execution time (launch-recorded
-    events)."""
+    in a cache.  Transposed [N, K*bits/32] weights and the tile-packed
+    layout; kernel execution time (launch-recorded events)."""
     from invariant_reductions_amd import inputs
     res = {}
     for mode, gs, bits in (("affine", 64, 4), ("nvfp4", 16, 4), ("mxfp4", 32, 4),
@@ -455,10 +454,9 @@ def qmatmul_decode(torch, bi, dev):
             wbytes = N * K * bits // 8 + N * (K // gs) * (4 if mode == "affine" else 1)
             tot = wbytes + 2 * M * K + 2 * M * N
             runs = [("transposed", lambda r: bi.qmatmul(xd, wqs[r], sd, bd, N, K, qm, gs, True, out=y, bits=bits))]
-            wps = []
-            if bits == 4 and mode != "mxfp8":
-                wps = [bi.pack_qweights(w, sd, bd, N, K, qm, gs) for w in wqs]
-                runs.append(("packed", lambda r: bi.qmatmul(xd, wps[r], None, None, N, K, qm, gs, out=y, packed=True)))
+            wps = [bi.pack_qweights(w, sd, bd, N, K, qm, gs, bits=bits) for w in wqs]
+            runs.append(("packed", lambda r: bi.qmatmul(xd, wps[r], None, None, N, K, qm, gs, out=y, packed=True,
+                                                        bits=bits)))
             name = f"{mode}-gs{gs}" + (f"-b{bits}" if mode == "affine" and bits != 4 else "")
             for tag, fn in runs:
                 t = _time_kernel(torch, bi, lambda i: fn(i % copies), reps=4 * copies)

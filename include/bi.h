@@ -184,11 +184,10 @@ bi_status bi_matmul_swiglu(const void *x, const void *w_il, void *a, int64_t M, 
  *     wq [N, K*bits/32] uint32, scales [N, K/gs], biases [N, K/gs].
  *   w_layout BI_W_NATURAL (0), quantized along N:
  *     wq [K, N*bits/32] uint32, scales [K, N/gs], biases [K, N/gs].
- *   w_layout BI_W_PACKED (2), 4-bit modes only (BI_ERR_UNSUPPORTED for the
- *     others): wq is the buffer bi_pack_qweights wrote from transposed
- *     weights (K % 128 == 0, 16-byte aligned; BI_ERR_SHAPE / BI_ERR_ALIGN
- *     otherwise); scales and biases are not read (may be NULL).  Same bits as
- *     the transposed call.  Other w_layout values: BI_ERR_SHAPE.
+ *   w_layout BI_W_PACKED (2): wq is the buffer bi_pack_qweights wrote from
+ *     transposed weights (K % 128 == 0, 16-byte aligned; BI_ERR_SHAPE /
+ *     BI_ERR_ALIGN otherwise); scales and biases are not read (may be NULL).
+ *     Same bits as the transposed call.  Other w_layout values: BI_ERR_SHAPE.
  *   Packing: each stored row is a little-endian bit stream of `bits`-bit
  *   codes: code j in bits [j*bits, (j+1)*bits) of the stream, stream bit i in
  *   bit i % 32 of uint32 word i / 32.  At 4 bits: eight codes per word, the
@@ -255,21 +254,19 @@ bi_status bi_gather_qmatmul(const void *x, const int32_t *lhs_idx, const int32_t
  * layout change of transposed weights that bi_qmatmul multiplies with the
  * same tree, hence the same bits.  Same source as bi_qmatmul (the layout is
  * free).  For row group r (rows 16r .. 16r + 15; rows >= N are zeros) and K
- * block b (128 codes): 1 KiB of codes in MFMA lane order, lane l = 16g + c
- * holding the four words of row 16r + c for k in [128b + 32g, +32), at byte
- * ((r * (K/128) + b) * 64 + l) * 16; after all code chunks, one constants
- * chunk per (r, b) in the same order -- affine: 16 rows x (128/gs) entries
- * scale | bias << 16 (4 bytes each, row-major); nvfp4 / mxfp4: 16 rows x
- * (128/gs) scale bytes.  A wave reads its codes for a block as one 1 KiB piece and its
- * constants as one small piece.
- *   The 4-bit modes only (affine at bits 4, nvfp4, mxfp4).
- *   bi_packed_qweight_bytes: ceil(N/16) * (K/128) * (1024 + constants chunk),
- *     or 0 for an illegal or non-4-bit mode / group size / bits or
- *     K % 128 != 0.
+ * block b (128 codes): 64 lanes x `bits` words of codes in MFMA lane order,
+ * lane l = 16g + c holding the `bits` words of row 16r + c for k in
+ * [128b + 32g, +32), at word ((r * (K/128) + b) * 64 + l) * bits (at 4 bits:
+ * a 1 KiB chunk of four words per lane); after all code chunks, one
+ * constants chunk per (r, b) in the same order -- affine: 16 rows x (128/gs)
+ * entries scale | bias << 16 (4 bytes each, row-major); nvfp4 / mxfp4 /
+ * mxfp8: 16 rows x (128/gs) scale bytes.  A wave reads its codes for a block
+ * as one piece and its constants as one small piece.
+ *   bi_packed_qweight_bytes: ceil(N/16) * (K/128) * (256 * bits + constants
+ *     chunk), or 0 for an illegal mode / group size / bits or K % 128 != 0.
  *   bi_pack_qweights: transposed wq, scales, biases (as bi_qmatmul) -> wqp of
  *     that many bytes; wq and wqp 16-byte aligned.  Stream-ordered; errors as
- *     bi_qmatmul plus BI_ERR_SHAPE when K % 128 != 0 and BI_ERR_UNSUPPORTED
- *     for a legal mode of other than 4 bits.
+ *     bi_qmatmul plus BI_ERR_SHAPE when K % 128 != 0.
  * ------------------------------------------------------------------------ */
 size_t bi_packed_qweight_bytes(int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size);
 bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, const void *biases, void *wqp, int64_t N,

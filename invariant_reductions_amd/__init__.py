@@ -312,14 +312,15 @@ def gather_qmatmul(x, lhs, rhs, wq, scales, biases, N: int, K: int, qmode: int, 
     return y
 
 
-def pack_qweights(wq, scales, biases, N: int, K: int, qmode: int, group_size: int, stream=None) -> torch.Tensor:
+def pack_qweights(wq, scales, biases, N: int, K: int, qmode: int, group_size: int, stream=None,
+                  bits: int = 4) -> torch.Tensor:
     """Transposed quantized weights -> the packed buffer qmatmul(packed=True) reads."""
     _dev(wq, scales, biases)
-    nbytes = lib().bi_packed_qweight_bytes(N, K, qmode, 4, group_size)
+    nbytes = lib().bi_packed_qweight_bytes(N, K, qmode, bits, group_size)
     if nbytes == 0:
         raise ValueError("pack_qweights: needs K % 128 == 0 and a legal mode / group size")
     wqp = torch.empty(nbytes // 4, dtype=torch.int32, device=wq.device)
-    _check(lib().bi_pack_qweights(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(wqp), N, K, qmode, 4, group_size,
+    _check(lib().bi_pack_qweights(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(wqp), N, K, qmode, bits, group_size,
                                   _stream(stream)), "bi_pack_qweights")
     return wqp
 

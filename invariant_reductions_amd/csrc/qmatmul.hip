@@ -107,7 +107,6 @@ __device__ inline QGroup<QM> group_from_raw(uint32_t sc, uint32_t bs, int s)
 // for one block are one 1 KiB piece and its constants one piece of at most
 // 256 bytes, where [N, K/8] + [N, K/gs] spread them over 16 rows each.  The
 // lane that reads a code is the lane that multiplies it, as before.
-__host__ __device__ constexpr int qconst_chunk_bytes(int qm, int gs) { return 16 * (128 / gs) * (qm == BI_AFFINE ? 4 : 1); }
 
 // Lane (g, c)'s words and group constants of row group rg, block b (packed).
 template <int QM, int GS>
@@ -910,7 +909,6 @@ extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *s
     if (w_layout < 0 || w_layout > 2) return BI_ERR_SHAPE;
     const bi_status qs = check_qmode(qmode, bits, group_size);
     if (qs != BI_OK) return qs;
-    if (packed && !four_bit_mode(qmode, bits)) return BI_ERR_UNSUPPORTED;
     if (!packed) {
         if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
         if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
@@ -934,11 +932,10 @@ extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *s
 
 extern "C" size_t bi_packed_qweight_bytes(int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size)
 {
-    if (N < 1 || K < 1 || K % kQBlock || N > (1ll << 31) || K > (1ll << 31) || check_qmode(qmode, bits, group_size) != BI_OK ||
-        !four_bit_mode(qmode, bits))
+    if (N < 1 || K < 1 || K % kQBlock || N > (1ll << 31) || K > (1ll << 31) || check_qmode(qmode, bits, group_size) != BI_OK)
         return 0;
     const size_t chunks = (size_t)cdiv(N, 16) * (size_t)(K / kQBlock);
-    return chunks * (1024 + (size_t)qconst_chunk_bytes(qmode, group_size));
+    return chunks * ((size_t)256 * bits + (size_t)qconst_chunk_bytes(qmode, group_size));   // 64 lanes x bits words
 }
 
 extern "C" bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, const void *biases, void *wqp, int64_t N,
@@ -947,13 +944,13 @@ extern "C" bi_status bi_pack_qweights(const uint32_t *wq, const void *scales, co
     if (!wq || !scales || !wqp) return BI_ERR_NULL;
     const bi_status qs = check_qmode(qmode, bits, group_size);
     if (qs != BI_OK) return qs;
-    if (!four_bit_mode(qmode, bits)) return BI_ERR_UNSUPPORTED;
     if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
     if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
     if (bi_packed_qweight_bytes(N, K, qmode, bits, group_size) == 0) return BI_ERR_SHAPE;
     if (!host_aligned16(wq) || !host_aligned16(wqp) || ((uintptr_t)scales & 1u) || ((uintptr_t)biases & 1u))
         return BI_ERR_ALIGN;
     (void)hipGetLastError();
+    if (!four_bit_mode(qmode, bits)) return bi_pack_qweights_wide(wq, scales, biases, wqp, N, K, qmode, bits, group_size, stream);
     const int64_t nrg = cdiv(N, 16), nb = K / kQBlock;
     const int64_t n = nrg * nb * 64 + nrg * nb * 16 * (128 / group_size);
     const dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), block(256);

@@ -34,14 +34,21 @@ __device__ inline float e8m0_to_f32(uint32_t e)
     return e == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);   // 2^-127 is subnormal
 }
 
+// Bytes of one (16-row group, K block) constants chunk of the tile-packed
+// layout: 16 rows x (128 / gs) entries of scale | bias << 16 (affine, 4 bytes)
+// or one scale byte (the fp formats).
+__host__ __device__ constexpr int qconst_chunk_bytes(int qm, int gs) { return 16 * (128 / gs) * (qm == BI_AFFINE ? 4 : 1); }
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 }  // namespace bi
 
-// The wide-code entry (qmatmul_wide.hip); arguments already validated by
-// bi_qmatmul: qmode affine with bits in 2..8 other than 4, or mxfp8; layout 0
-// (natural) or 1 (transposed).
+// The wide-code entries (qmatmul_wide.hip); arguments already validated by
+// bi_qmatmul / bi_pack_qweights: qmode affine with bits in 2..8 other than 4,
+// or mxfp8; layout 0 (natural), 1 (transposed) or 2 (packed, K % 128 == 0).
 bi_status bi_qmatmul_wide(const void *x, const uint32_t *wq, const void *scales, const void *biases, void *y,
                           int64_t M, int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size,
                           int32_t w_layout, hipStream_t stream);
+bi_status bi_pack_qweights_wide(const uint32_t *wq, const void *scales, const void *biases, void *wqp, int64_t N,
+                                int64_t K, int32_t qmode, int32_t bits, int32_t group_size, hipStream_t stream);

@@ -25,6 +25,12 @@
 // BITS consecutive words.  In the natural layout column n's code in row k
 // starts at stream bit n * BITS of row k and may straddle two words.
 //
+// Packed layout (bi_pack_qweights, K % 128 == 0): the 4-bit layout with BITS
+// words per lane -- for row group r and K block b, 64 lanes x BITS words in
+// MFMA lane order at word ((r * nb + b) * 64 + lane) * BITS (lane 16g + c:
+// row 16r + c, k in [128b + 32g, +32)), then after all code chunks one
+// constants chunk per (r, b) as in the 4-bit layout.
+//
 // Bounds: transposed K is a multiple of the group size (>= 32), so a lane's 32
 // codes lie wholly below K or wholly at/after it; natural K is arbitrary and a
 // code at k >= K is not read; columns n >= N read nothing and store nothing.
@@ -106,6 +112,27 @@ __device__ inline void load_raw_group(const void *scales, const uint16_t *biases
     }
 }
 
+// Lane (g, c)'s words and raw group constants of row group rg, block b in the
+// packed layout (gshift = log2 gs).
+template <int QM, int BITS>
+__device__ inline void load_packed(const uint32_t *wqp, int64_t nrg, int64_t nb, int64_t rg, int64_t b, int lane,
+                                   int gshift, uint32_t (&w)[BITS], uint32_t &sc, uint32_t &bs)
+{
+    const int g = lane >> 4, c = lane & 15, gpb = 128 >> gshift;
+    load_words<BITS>(w, wqp + ((rg * nb + b) * 64 + lane) * BITS, true);
+    const uint8_t *cb = reinterpret_cast<const uint8_t *>(wqp) + nrg * nb * 256 * BITS +
+                        (rg * nb + b) * (int64_t)(16 * gpb * (QM == BI_MXFP8 ? 1 : 4));
+    const int ei = c * gpb + ((32 * g) >> gshift);
+    if constexpr (QM == BI_MXFP8) {
+        sc = cb[ei];
+        bs = 0;
+    } else {
+        const uint32_t v = reinterpret_cast<const uint32_t *>(cb)[ei];
+        sc = v & 0xffffu;
+        bs = v >> 16;
+    }
+}
+
 // Codes 8s .. 8s + 7 of a lane's 32 -> one 16-byte MFMA operand chunk.
 //   affine: code -> fp32 (exact), fma(s, q, b), pairs rounded to binary16 by
 //           one packed conversion;
@@ -155,7 +182,7 @@ __device__ inline uint16_t wdeq1(uint32_t q, uint32_t sc, uint32_t bs)
 
 // General form: any M (tiles of 16*MT rows), 16 columns per workgroup, either
 // layout.  gshift = log2(group size).
-template <int QM, int BITS, bool TRANS, int MT>
+template <int QM, int BITS, bool TRANS, int MT, bool PK>
 __global__ __launch_bounds__(kQWaves * kWave)
 void qwide_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wq, const void *__restrict__ scales,
                   const uint16_t *__restrict__ biases, uint16_t *__restrict__ y, int64_t M, int64_t N, int64_t K,
@@ -186,7 +213,15 @@ void qwide_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ w
     for (int64_t b = wave; b < nblocks; b += P) {
         const int64_t kbase = b * kQBlock + (int64_t)g * 32;
         uint4 Bf[4];
-        if constexpr (TRANS) {
+        if constexpr (PK) {
+            // K % 128 == 0: every block is whole; padding rows of the group are zeros
+            uint32_t w[BITS], sc, bs;
+            load_packed<QM, BITS>(wq, cdiv(N, 16), nblocks, (int64_t)blockIdx.x, b, lane, gshift, w, sc, bs);
+            float gsv, gbv;
+            wgroup<QM>(sc, bs, gsv, gbv);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Bf[s] = wdeq8<QM, BITS>(w, s, gsv, gbv);
+        } else if constexpr (TRANS) {
             if (nok && kbase < K) {
                 const int64_t wpr = K / 32 * BITS;
                 uint32_t w[BITS];
@@ -259,7 +294,7 @@ void qwide_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ w
 // each wave streams its (tile, block) items -- a lane's code words, group
 // constants and x chunks -- through a D-deep register ring that runs across
 // tile boundaries.  Per output the tree is qwide_kernel's.
-template <int QM, int BITS, int NS, int D>
+template <int QM, int BITS, int NS, int D, bool PK>
 __global__ __launch_bounds__(kQWaves * kWave, 2)
 void qwide_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wq,
                          const void *__restrict__ scales, const uint16_t *__restrict__ biases,
@@ -287,10 +322,16 @@ void qwide_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restr
         const int64_t kb = (int64_t)(wave + pj * P) * kQBlock + g * 32;     // this lane's first code
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            int64_t n = t * TC + j * 16 + c;
-            n = n < N ? n : N - 1;                                          // padding columns read a real row
-            load_words<BITS>(Wd[j], wq + n * wpr + (kb / 32) * BITS, wvec != 0);
-            load_raw_group<QM>(scales, biases, n * groups + (kb >> gshift), Sd[j], Bd[j]);
+            if constexpr (PK) {
+                const int64_t nrg = (N + 15) / 16, rg = t * NS + j;
+                load_packed<QM, BITS>(wq, nrg, nb, rg < nrg ? rg : nrg - 1, wave + pj * P, lane, gshift, Wd[j], Sd[j],
+                                      Bd[j]);
+            } else {
+                int64_t n = t * TC + j * 16 + c;
+                n = n < N ? n : N - 1;                                      // padding columns read a real row
+                load_words<BITS>(Wd[j], wq + n * wpr + (kb / 32) * BITS, wvec != 0);
+                load_raw_group<QM>(scales, biases, n * groups + (kb >> gshift), Sd[j], Bd[j]);
+            }
         }
         if (c < M) {
 #pragma unroll
@@ -367,24 +408,34 @@ void qwide_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restr
     }
 }
 
-template <int QM, int BITS, bool TRANS, int MT>
+template <int QM, int BITS, bool TRANS, int MT, bool PK = false>
 static void launch_qw_t(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                         int64_t N, int64_t K, int gshift, int wvec, hipStream_t st)
 {
     dim3 grid((unsigned)cdiv(N, 16), (unsigned)cdiv(M, MT * 16));
-    launch_kernel((qwide_kernel<QM, BITS, TRANS, MT>), grid, dim3(kQWaves * kWave), 0, st, (const uint16_t *)x, wq, s,
-                  (const uint16_t *)b, (uint16_t *)y, M, N, K, gshift, wvec);
+    launch_kernel((qwide_kernel<QM, BITS, TRANS, MT, PK>), grid, dim3(kQWaves * kWave), 0, st, (const uint16_t *)x, wq,
+                  s, (const uint16_t *)b, (uint16_t *)y, M, N, K, gshift, wvec);
 }
 
-template <int QM, int BITS, int NS>
+template <int QM, int BITS, int NS, bool PK>
 static void launch_qw_stream(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                              int64_t N, int64_t K, int gshift, int wvec, hipStream_t st)
 {
     constexpr int D = BITS >= 6 ? 2 : 3;                 // register ring depth: wide codes hold more words
     const int64_t ntn = cdiv(N, NS * 16);
     const int64_t grid = std::min<int64_t>(ntn, (int64_t)device_cu_count() * 2);
-    launch_kernel((qwide_stream_kernel<QM, BITS, NS, D>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
+    launch_kernel((qwide_stream_kernel<QM, BITS, NS, D, PK>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
                   (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, M, N, K, (int)ntn, gshift, wvec);
+}
+
+template <int QM, int BITS, bool TRANS, bool PK>
+static void launch_qw_mt(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
+                         int64_t N, int64_t K, int gshift, int wvec, hipStream_t st)
+{
+    const int64_t mt = cdiv(M, 16);
+    if (mt <= 1) launch_qw_t<QM, BITS, TRANS, 1, PK>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+    else if (mt <= 2) launch_qw_t<QM, BITS, TRANS, 2, PK>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+    else launch_qw_t<QM, BITS, TRANS, 4, PK>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
 }
 
 template <int QM, int BITS>
@@ -393,20 +444,52 @@ static void launch_qw(const void *x, const uint32_t *wq, const void *s, const vo
 {
     const int gshift = gs == 32 ? 5 : (gs == 64 ? 6 : 7);
     const int wvec = host_aligned16(wq) ? 1 : 0;         // row and lane offsets are then multiples of the load size
-    if (layout == 1 && M <= 16 && K % kQBlock == 0 && host_aligned16(x) && cdiv(N, 16) <= (1ll << 30)) {
-        if (N >= 8192) launch_qw_stream<QM, BITS, 2>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
-        else launch_qw_stream<QM, BITS, 1>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+    const bool stream = layout >= 1 && M <= 16 && K % kQBlock == 0 && host_aligned16(x) && cdiv(N, 16) <= (1ll << 30);
+    if (stream) {
+        if (layout == 2) {                               // packed: 16-byte aligned (checked)
+            if (N >= 8192) launch_qw_stream<QM, BITS, 2, true>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+            else launch_qw_stream<QM, BITS, 1, true>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+        } else {
+            if (N >= 8192) launch_qw_stream<QM, BITS, 2, false>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+            else launch_qw_stream<QM, BITS, 1, false>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+        }
         return;
     }
-    const int64_t mt = cdiv(M, 16);
-    if (layout == 1) {
-        if (mt <= 1) launch_qw_t<QM, BITS, true, 1>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
-        else if (mt <= 2) launch_qw_t<QM, BITS, true, 2>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
-        else launch_qw_t<QM, BITS, true, 4>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
-    } else {
-        if (mt <= 1) launch_qw_t<QM, BITS, false, 1>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
-        else if (mt <= 2) launch_qw_t<QM, BITS, false, 2>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
-        else launch_qw_t<QM, BITS, false, 4>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+    if (layout == 2) launch_qw_mt<QM, BITS, true, true>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+    else if (layout == 1) launch_qw_mt<QM, BITS, true, false>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+    else launch_qw_mt<QM, BITS, false, false>(x, wq, s, b, y, M, N, K, gshift, wvec, st);
+}
+
+// [N, K*bits/32] codes + [N, K/gs] constants -> the packed layout; one thread
+// per lane chunk of `bits` words, then one per constant entry.
+template <int QM>
+__global__ void pack_qwide_kernel(const uint32_t *__restrict__ wq, const void *__restrict__ scales,
+                                  const uint16_t *__restrict__ biases, uint32_t *__restrict__ wqp, int64_t N,
+                                  int64_t K, int bits, int gshift)
+{
+    const int64_t nb = K / kQBlock, nrg = (N + 15) / 16, wpr = K / 32 * bits, groups = K >> gshift;
+    const int gpb = 128 >> gshift;                               // constant entries per row per block
+    const int64_t ncode = nrg * nb * 64, nconst = nrg * nb * 16 * gpb;
+    uint8_t *cbase = reinterpret_cast<uint8_t *>(wqp) + nrg * nb * 256 * bits;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ncode + nconst;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < ncode) {
+            const int lane = (int)(i & 63);
+            const int64_t rb = i >> 6, b = rb % nb, rg = rb / nb;
+            const int64_t row = rg * 16 + (lane & 15);
+            const uint32_t *src = wq + row * wpr + (4 * b + (lane >> 4)) * bits;
+            for (int w = 0; w < bits; ++w) wqp[i * bits + w] = row < N ? src[w] : 0u;
+        } else {
+            const int64_t e = i - ncode, q = e % gpb, cr = e / gpb, c = cr % 16, rb = cr / 16;
+            const int64_t b = rb % nb, rg = rb / nb, row = rg * 16 + c;
+            const int64_t gi = row * groups + b * gpb + q;
+            if constexpr (QM == BI_AFFINE) {
+                const uint32_t v = row < N ? (uint32_t)((const uint16_t *)scales)[gi] | ((uint32_t)biases[gi] << 16) : 0u;
+                *reinterpret_cast<uint32_t *>(cbase + e * 4) = v;
+            } else {
+                cbase[e] = row < N ? ((const uint8_t *)scales)[gi] : (uint8_t)0;
+            }
+        }
     }
 }
 
@@ -431,5 +514,21 @@ bi_status bi_qmatmul_wide(const void *x, const uint32_t *wq, const void *scales,
         default: return BI_ERR_GROUP;
         }
     }
+    return launch_status();
+}
+
+bi_status bi_pack_qweights_wide(const uint32_t *wq, const void *scales, const void *biases, void *wqp, int64_t N,
+                                int64_t K, int32_t qmode, int32_t bits, int32_t group_size, hipStream_t st)
+{
+    const int gshift = group_size == 32 ? 5 : (group_size == 64 ? 6 : 7);
+    const int64_t nrg = cdiv(N, 16), nb = K / kQBlock;
+    const int64_t n = nrg * nb * 64 + nrg * nb * 16 * (128 / group_size);
+    const dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), block(256);
+    if (qmode == BI_MXFP8)
+        launch_kernel((pack_qwide_kernel<BI_MXFP8>), grid, block, 0, st, wq, scales, (const uint16_t *)biases,
+                      (uint32_t *)wqp, N, K, (int)bits, gshift);
+    else
+        launch_kernel((pack_qwide_kernel<BI_AFFINE>), grid, block, 0, st, wq, scales, (const uint16_t *)biases,
+                      (uint32_t *)wqp, N, K, (int)bits, gshift);
     return launch_status();
 }

@@ -222,12 +222,16 @@ def test_packed_qweight_validation():
     assert L.bi_packed_qweight_bytes(16, 128, 1, 4, 16) == 1024 + 128
     assert L.bi_packed_qweight_bytes(16, 192, 0, 4, 64) == 0           # K % 128
     assert L.bi_packed_qweight_bytes(16, 128, 0, 4, 16) == 0           # affine gs 16
-    assert L.bi_packed_qweight_bytes(16, 128, 0, 8, 32) == 0           # 4-bit modes only
-    assert L.bi_packed_qweight_bytes(16, 128, 3, 8, 32) == 0
-    assert L.bi_pack_qweights(A, A, A, A, 16, 128, 0, 3, 32, None) == UNSUP
-    assert L.bi_pack_qweights(A, A, None, A, 16, 128, 3, 8, 32, None) == UNSUP
-    assert L.bi_qmatmul(A, A, None, None, A, 4, 16, 128, 3, 8, 32, 2, None) == UNSUP
-    assert L.bi_qmatmul(A, A, None, None, A, 4, 16, 128, 0, 6, 64, 2, None) == UNSUP
+    # other widths: 64 lanes x bits words per chunk, then the same constants
+    assert L.bi_packed_qweight_bytes(16, 128, 0, 8, 32) == 64 * 8 * 4 + 16 * 4 * 4
+    assert L.bi_packed_qweight_bytes(20, 256, 3, 8, 32) == 2 * 2 * (64 * 8 * 4 + 16 * 4)
+    assert L.bi_packed_qweight_bytes(16, 128, 0, 3, 128) == 64 * 3 * 4 + 16 * 1 * 4
+    assert L.bi_packed_qweight_bytes(16, 128, 0, 9, 32) == 0
+    assert L.bi_pack_qweights(A, A, A, A, 16, 192, 0, 3, 32, None) == SHAPE       # K % 128
+    assert L.bi_pack_qweights(A, A, None, P(0x10010 + 4), 16, 128, 3, 8, 32, None) == ALIGN
+    assert L.bi_pack_qweights(A, A, A, A, 16, 128, 3, 8, 32, None) == GROUP       # mxfp8 takes no biases
+    assert L.bi_qmatmul(A, A, None, None, A, 4, 16, 192, 3, 8, 32, 2, None) == SHAPE    # K % 128
+    assert L.bi_qmatmul(A, P(0x10010 + 4), None, None, A, 4, 16, 128, 0, 6, 64, 2, None) == ALIGN
     assert L.bi_pack_qweights(A, A, None, A, 16, 128, 0, 4, 64, None) == NULL    # affine needs biases
     assert L.bi_pack_qweights(A, A, A, A, 16, 128, 1, 4, 16, None) == GROUP      # nvfp4 takes none
     assert L.bi_pack_qweights(A, A, A, A, 16, 192, 0, 4, 64, None) == SHAPE

@@ -241,3 +241,51 @@ def test_bounded_loads_and_stores(mode, gs, bits, M, K, N, transposed):
     torch.cuda.synchronize()
     assert yg.canaries_intact()
     assert_parity(to_np(yg.view), ref(x, wq, s, b, M, N, K, mode, gs, bits, transposed), "f16")
+
+
+@pytest.mark.parametrize("mode,gs,bits", WIDE)
+@pytest.mark.parametrize("M,N", [(8, 512), (40, 200), (4, 8192)])
+def test_packed_bits_equal_transposed(mode, gs, bits, M, N):
+    """The tile-packed layout (streaming kernel at M <= 16, tiled above, a
+    padded last row group at N = 200) gives the transposed call's bits."""
+    K = 1024
+    x, wq, s, b = inputs.qmatmul_case(M, K, N, mode, gs, True, seed=M + bits, bits=bits)
+    wqd, sd, bd = dev_q(wq, s, b)
+    wp = bi.pack_qweights(wqd, sd, bd, N, K, QM[mode], gs, bits=bits)
+    xd = to_dev(x, "f16")
+    a = to_np(bi.qmatmul(xd, wqd, sd, bd, N, K, QM[mode], gs, True, bits=bits))
+    p = to_np(bi.qmatmul(xd, wp, None, None, N, K, QM[mode], gs, packed=True, bits=bits))
+    assert bits_equal(a, p)
+
+
+@pytest.mark.parametrize("mode,gs,bits", [("affine", 64, 3), ("mxfp8", 32, 8), ("affine", 128, 6)])
+def test_packed_buffer_layout(mode, gs, bits):
+    """The packed buffer is the documented layout: for row group r and K block
+    b, lane 16g + c holds the `bits` words of row 16r + c for k in [128b + 32g,
+    +32); then one constants chunk per (r, b): 16 rows x 128/gs entries."""
+    N, K = 40, 256
+    _, wq, s, b = inputs.qmatmul_case(1, K, N, mode, gs, True, seed=2, bits=bits)
+    wqd, sd, bd = dev_q(wq, s, b)
+    got = bi.pack_qweights(wqd, sd, bd, N, K, QM[mode], gs, bits=bits).cpu().numpy().view(np.uint32)
+    nrg, nb, gpb = (N + 15) // 16, K // 128, 128 // gs
+    rows = np.zeros((nrg * 16, wq.shape[1]), np.uint32)
+    rows[:N] = wq
+    codes = np.zeros((nrg, nb, 64, bits), np.uint32)
+    for r in range(nrg):
+        for blk in range(nb):
+            for lane in range(64):
+                g, c = lane >> 4, lane & 15
+                codes[r, blk, lane] = rows[16 * r + c, (4 * blk + g) * bits:(4 * blk + g + 1) * bits]
+    ncode = codes.size
+    assert np.array_equal(got[:ncode], codes.reshape(-1))
+    cbytes = got[ncode:].view(np.uint8)
+    if mode == "affine":
+        sv = np.zeros((nrg * 16, K // gs), np.uint32)
+        sv[:N] = s.astype(np.uint32) | (b.astype(np.uint32) << 16)
+        want = np.stack([sv[16 * r:16 * r + 16, blk * gpb:(blk + 1) * gpb] for r in range(nrg) for blk in range(nb)])
+        assert np.array_equal(cbytes.view(np.uint32), want.reshape(-1))
+    else:
+        sv = np.zeros((nrg * 16, K // gs), np.uint8)
+        sv[:N] = s
+        want = np.stack([sv[16 * r:16 * r + 16, blk * gpb:(blk + 1) * gpb] for r in range(nrg) for blk in range(nb)])
+        assert np.array_equal(cbytes, want.reshape(-1))
