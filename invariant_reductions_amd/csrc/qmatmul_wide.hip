@@ -13,7 +13,9 @@
 //   affine: w = RNE16(fma(s, q, b)) with binary16 s, b (s*q is exact in fp32,
 //           at most 11 + 8 significant bits, so the fma rounds once, exactly
 //           like mul-then-add);
-//   mxfp8 : w = RNE16(e4m3(q) * 2^(e - 127)), the exact product rounded once --
+//   mxfp8 : w = RNE16(e4m3(q) * 2^(e - 127)), the exact product rounded once
+//           (the e4m3 decode is the hardware's OCP conversion, checked for
+//           every code at every scale against the oracle) --
 // and multiplied against binary16 x by the K tree of the 4-bit kernels: blocks
 // of 128 owned by wave b mod 8, lane group g supplying [32g, 32g + 32) of a
 // block as four v_mfma_f32_16x16x32_f16 steps, wave partials added in wave
@@ -74,24 +76,12 @@ __device__ inline void load_words(uint32_t (&w)[BITS], const uint32_t *src, bool
     }
 }
 
-// mxfp8 scale of the register path: 2^(min(k, 25) + 8) with k = e - 127, NaN
-// for e = 0xFF.  Codes enter as binary16 patterns worth e4m3 * 2^-8, so the
-// fp32 product is e4m3 * 2^min(k, 25): exact (at least 2^-136 with four
-// significant bits).  For k >= 25 every nonzero code gives at least 2^16,
-// which rounds to +-inf in binary16 just as the exact value does.
-__device__ inline float mx8_scale(uint32_t e)
-{
-    if (e == 0xffu) return __uint_as_float(0x7fc00000u);
-    const int k = (int)e - 127;
-    return __uint_as_float((uint32_t)((k > 25 ? 25 : k) + 8 + 127) << 23);
-}
-
 // Group constants from the raw scale (and bias) a lane loaded.
 template <int QM>
 __device__ inline void wgroup(uint32_t sc, uint32_t bs, float &s, float &b)
 {
     if constexpr (QM == BI_MXFP8) {
-        s = mx8_scale(sc);
+        s = e8m0_to_f32(sc);
         b = 0.0f;
     } else {
         s = F16::widen((uint16_t)sc);
@@ -136,11 +126,11 @@ __device__ inline void load_packed(const uint32_t *wqp, int64_t nrg, int64_t nb,
 // Codes 8s .. 8s + 7 of a lane's 32 -> one 16-byte MFMA operand chunk.
 //   affine: code -> fp32 (exact), fma(s, q, b), pairs rounded to binary16 by
 //           one packed conversion;
-//   mxfp8 : byte (sign | e | m) -> binary16 pattern (sign << 15) | ((e, m) <<
-//           7), whose value is e4m3 * 2^-8 exactly (e = 0 lands on binary16
-//           subnormals, m * 2^-17); widened to fp32, times mx8_scale, rounded
-//           once to binary16; the NaN codes (e, m all ones) get the binary16
-//           NaN exponent and top mantissa bit ORed in.
+//   mxfp8 : two codes at a time to fp32 by the OCP e4m3 conversion
+//           (v_cvt_pk_f32_fp8: exact, NaN codes give NaN), times the scale
+//           2^(e - 127) -- exact in fp32, or +-inf where binary16 overflows
+//           anyway, and where fp32 is subnormal binary16 rounds to zero
+//           anyway -- then rounded once to binary16.
 template <int QM, int BITS>
 __device__ inline uint4 wdeq8(const uint32_t (&w)[BITS], int s, float gsv, float gbv)
 {
@@ -148,15 +138,11 @@ __device__ inline uint4 wdeq8(const uint32_t (&w)[BITS], int s, float gsv, float
     if constexpr (QM == BI_MXFP8) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const uint32_t word = w[2 * s + (p >> 1)];
-            const uint32_t b0 = 2u * (uint32_t)(p & 1);
-            // code 2p -> bits 0..7, code 2p + 1 -> bits 16..23
-            const uint32_t t = __builtin_amdgcn_perm(word, word, 0x0C000C00u | b0 | ((b0 + 1u) << 16));
-            const uint32_t mag = t & 0x007f007fu;
-            const uint32_t h = (mag << 7) | ((t & 0x00800080u) << 8);
-            const uint32_t nan = ((mag + 0x00010001u) & 0x00800080u) * 0xFCu;   // 0x80 * 0xFC = 0x7E00
-            const f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, h), f32x2) * gsv;
-            out[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2)) | nan;
+            const int word = (int)w[2 * s + (p >> 1)];
+            const f32x2 e = (p & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)      // codes 2p, 2p + 1
+                                    : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+            const f32x2 v = e * gsv;
+            out[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
         }
     } else {
 #pragma unroll
