@@ -480,7 +480,13 @@ def qmatmul_decode(torch, bi, dev):
     t = _time_kernel(torch, bi, lambda i: bi.gather_qmatmul(xd, ld, rd, ws[i % copies], sd, bd, N, K, bi.AFFINE, gs,
                                                             True, out=y), reps=4 * copies)
     gbs = tot / (t * 1e-3) / 1e9
-    res[f"gather affine-gs64 T{T} top{topk} of E{E} ({used} used) {N}x{K}"] = {
+    res[f"gather affine-gs64 T{T} top{topk} of E{E} ({used} used) {N}x{K} transposed"] = {
+        "us": round(t * 1e3, 1), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    wps = [torch.stack([bi.pack_qweights(w[e], sd[e], bd[e], N, K, bi.AFFINE, gs) for e in range(E)]) for w in ws]
+    t = _time_kernel(torch, bi, lambda i: bi.gather_qmatmul(xd, ld, rd, wps[i % copies], None, None, N, K, bi.AFFINE,
+                                                            gs, out=y, packed=True), reps=4 * copies)
+    gbs = tot / (t * 1e-3) / 1e9
+    res[f"gather affine-gs64 T{T} top{topk} of E{E} ({used} used) {N}x{K} packed"] = {
         "us": round(t * 1e3, 1), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     return res
 

@@ -235,8 +235,10 @@ bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, cons
  *            row m (then x_rows >= M, BI_ERR_SHAPE otherwise).
  *   rhs_idx: device int32 [M], the expert of each output row (any order).
  *   wq, scales, biases: E matrices back to back, each laid out as bi_qmatmul
- *            takes one (w_layout 1 transposed or 0 natural; packed:
- *            BI_ERR_UNSUPPORTED); wq 4-byte aligned.
+ *            takes one (w_layout 1 transposed or 0 natural; wq 4-byte
+ *            aligned), or w_layout 2: E buffers of bi_pack_qweights back to
+ *            back (each bi_packed_qweight_bytes long; K % 128 == 0, wq
+ *            16-byte aligned), scales and biases not read (may be NULL).
  *   y      : [M, N] binary16.
  *   Modes: the 4-bit ones (affine gs 32/64/128, nvfp4, mxfp4); others:
  *   BI_ERR_UNSUPPORTED.  1 <= E <= 1023.  A row whose lhs or rhs index is out

@@ -295,10 +295,11 @@ def qmatmul(x, wq, scales, biases, N: int, K: int, qmode: int, group_size: int, 
 
 
 def gather_qmatmul(x, lhs, rhs, wq, scales, biases, N: int, K: int, qmode: int, group_size: int,
-                   transposed: bool = True, out=None, stream=None, bits: int = 4):
+                   transposed: bool = True, out=None, stream=None, bits: int = 4, packed: bool = False):
     """Expert matmul: y[m] = x[lhs[m]] @ dequantize(W[rhs[m]])^T; x float16
     [x_rows, K]; lhs (or None: row m) and rhs int32 [M] on the device; wq,
-    scales, biases stacked over the experts on dim 0."""
+    scales, biases stacked over the experts on dim 0 -- or (packed=True) wq
+    the experts' pack_qweights buffers stacked on dim 0, scales/biases None."""
     _dev(x, lhs, rhs, wq, scales, biases, out)
     if x.dtype != torch.float16 or rhs.dtype != torch.int32 or (lhs is not None and lhs.dtype != torch.int32):
         raise ValueError("gather_qmatmul: x float16, indices int32")
@@ -308,7 +309,8 @@ def gather_qmatmul(x, lhs, rhs, wq, scales, biases, N: int, K: int, qmode: int, 
     y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
     _check(lib().bi_gather_qmatmul(_ptr(x), _ptr(lhs), _ptr(rhs), _ptr(wq), _ptr(scales), _ptr(biases), _ptr(y),
                                    M, x.shape[0], N, K, E, qmode, bits, group_size,
-                                   W_TRANSPOSED if transposed else W_NATURAL, _stream(stream)), "bi_gather_qmatmul")
+                                   W_PACKED if packed else (W_TRANSPOSED if transposed else W_NATURAL),
+                                   _stream(stream)), "bi_gather_qmatmul")
     return y
 
 

@@ -581,7 +581,7 @@ __global__ void pack_q_kernel(const uint32_t *__restrict__ wq, const void *__res
 constexpr int kGatherSlab = 4096;
 constexpr int kGatherMaxExperts = 1023;
 
-template <int QM, int GS, bool TRANS, bool WVEC>
+template <int QM, int GS, bool TRANS, bool WVEC, bool PK>
 __global__ __launch_bounds__(kQWaves * kWave)
 void gather_q_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ lhs, const int32_t *__restrict__ rhs,
                      const uint32_t *__restrict__ wq, const void *__restrict__ scales,
@@ -600,7 +600,10 @@ void gather_q_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__
     const bool nok = n < N;
     const int64_t nblocks = cdiv(K, kQBlock);
     const bool xvec = (K % 8) == 0 && aligned16(x);
-    const int64_t words_e = N * K / 8, groups_e = N * K / GS;   // per expert
+    const int64_t nrg = (N + 15) / 16;
+    // per expert: codes [N, K/8] and constants [N, K/gs], or one packed buffer
+    const int64_t words_e = PK ? nrg * nblocks * (256 + qconst_chunk_bytes(QM, GS) / 4) : N * K / 8;
+    const int64_t groups_e = N * K / GS;
     const uint32_t *we = wq + (int64_t)(e < E ? e : 0) * words_e;
     const void *se = (const uint8_t *)scales + (int64_t)(e < E ? e : 0) * groups_e * SB;
     const uint16_t *be = biases ? biases + (int64_t)(e < E ? e : 0) * groups_e : nullptr;
@@ -647,7 +650,19 @@ void gather_q_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int64_t b = wave; b < nblocks; b += P) {
                 const int64_t kbase = b * kQBlock + (int64_t)g * 32;
-                if constexpr (TRANS) {
+                if constexpr (PK) {
+                    // K % 128 == 0: every block is whole; padding rows of the group are zeros
+                    uint4 A[4], wv;
+                    uint32_t sc, bs;
+                    qload_packed_raw<QM, GS>(we, nrg, nblocks, (int64_t)blockIdx.x, b, lane, wv, sc, bs);
+                    const uint32_t wa[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        A[s] = xvec ? load_chunk<F16, true>(xrow, kbase + s * 8, K, rok)
+                                    : load_chunk<F16, false>(xrow, kbase + s * 8, K, rok);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) acc = qmfma(A[s], deq_word<QM>(wa[s], group_from_raw<QM>(sc, bs, s)), acc);
+                } else if constexpr (TRANS) {
                     uint4 A[4], Bf[4];
                     qload_trans<QM, GS, WVEC>(Bf, we, se, be, nok ? n : 0, nok, K, kbase);
 #pragma unroll
@@ -693,7 +708,7 @@ void gather_q_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__
 // row c is row c of the call, its x chunk zero unless the row is routed to
 // the tile's expert; only such rows are stored.  Per row the tree is
 // qmatmul_stream_kernel's, hence the plain quantized matmul's bits.
-template <int QM, int GS, int NS, int D>
+template <int QM, int GS, int NS, int D, bool PK>
 __global__ __launch_bounds__(kQWaves * kWave, 2)
 void gather_q_stream_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ lhs,
                             const int32_t *__restrict__ rhs, const uint32_t *__restrict__ wq,
@@ -735,7 +750,9 @@ void gather_q_stream_kernel(const uint16_t *__restrict__ x, const int32_t *__res
     const int nmine = wave < nb ? (nb - wave + P - 1) / P : 0;        // blocks of this wave per tile
     const int mytiles = (int)blockIdx.x < ntiles ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
     const int items = mytiles * nmine;
-    const int64_t words = K / 8, groups = K / GS, words_e = N * K / 8, groups_e = N * K / GS;
+    const int64_t nrg = (N + 15) / 16;
+    const int64_t words = K / 8, groups = K / GS, groups_e = N * K / GS;
+    const int64_t words_e = PK ? nrg * nb * (256 + qconst_chunk_bytes(QM, GS) / 4) : N * K / 8;
     const int mybk = s_bucket[c];
     const bool myok = mybk >= 0 && mybk < E;
     // x row of A-operand row c (rows without a valid expert read row 0 and are never stored)
@@ -752,6 +769,11 @@ void gather_q_stream_kernel(const uint16_t *__restrict__ x, const int32_t *__res
         const int64_t kb = (int64_t)(wave + pj * P) * kQBlock + g * 32;     // this lane's first code
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
+            if constexpr (PK) {
+                const int64_t rg = (int64_t)ct * NS + j;
+                qload_packed_raw<QM, GS>(we, nrg, nb, rg < nrg ? rg : nrg - 1, wave + pj * P, lane, Wd[j], Sd[j], Bd[j]);
+                continue;
+            }
             int64_t n = (int64_t)ct * TC + j * 16 + c;
             n = n < N ? n : N - 1;                                      // padding columns read a real row
             Wd[j] = *reinterpret_cast<const uint4 *>(we + n * words + kb / 8);
@@ -855,29 +877,41 @@ static void launch_gather(const void *x, const int32_t *lhs, const int32_t *rhs,
     // one workgroup per (16-column tile, expert), plus one per tile for the rows with a bad index
     const dim3 grid((unsigned)cdiv(N, 16), (unsigned)(E + 1)), block(kQWaves * kWave);
     const uint16_t *bz = (const uint16_t *)b;
-    if (layout == 1 && M <= 16 && K % kQBlock == 0 && host_aligned16(x) && host_aligned16(wq) &&
+    const bool packed = layout == 2;                     // K % 128 == 0 and 16-byte aligned (checked)
+    if (layout >= 1 && M <= 16 && K % kQBlock == 0 && host_aligned16(x) && host_aligned16(wq) &&
         cdiv(N, 16) <= (1ll << 24)) {
         const int ns = N >= 8192 ? 2 : 1;
         const int64_t ntn = cdiv(N, 16 * ns);
         const int64_t tiles = std::min<int64_t>(M, E) * ntn;            // at most this many (expert, tile) pairs
-        const int64_t g = std::min<int64_t>(tiles, (int64_t)device_cu_count() * 2);
-        if (ns == 2)
-            launch_kernel((gather_q_stream_kernel<QM, GS, 2, 3>), dim3((unsigned)g), block, 0, st, (const uint16_t *)x,
-                          lhs, rhs, wq, s, bz, (uint16_t *)y, M, x_rows, N, K, E, (int)ntn);
+        const dim3 g((unsigned)std::min<int64_t>(tiles, (int64_t)device_cu_count() * 2));
+        const uint16_t *xx = (const uint16_t *)x;
+        uint16_t *yy = (uint16_t *)y;
+        if (ns == 2 && packed)
+            launch_kernel((gather_q_stream_kernel<QM, GS, 2, 3, true>), g, block, 0, st, xx, lhs, rhs, wq, s, bz, yy, M,
+                          x_rows, N, K, E, (int)ntn);
+        else if (ns == 2)
+            launch_kernel((gather_q_stream_kernel<QM, GS, 2, 3, false>), g, block, 0, st, xx, lhs, rhs, wq, s, bz, yy, M,
+                          x_rows, N, K, E, (int)ntn);
+        else if (packed)
+            launch_kernel((gather_q_stream_kernel<QM, GS, 1, 3, true>), g, block, 0, st, xx, lhs, rhs, wq, s, bz, yy, M,
+                          x_rows, N, K, E, (int)ntn);
         else
-            launch_kernel((gather_q_stream_kernel<QM, GS, 1, 3>), dim3((unsigned)g), block, 0, st, (const uint16_t *)x,
-                          lhs, rhs, wq, s, bz, (uint16_t *)y, M, x_rows, N, K, E, (int)ntn);
+            launch_kernel((gather_q_stream_kernel<QM, GS, 1, 3, false>), g, block, 0, st, xx, lhs, rhs, wq, s, bz, yy, M,
+                          x_rows, N, K, E, (int)ntn);
         return;
     }
-    if (layout == 0)
-        launch_kernel((gather_q_kernel<QM, GS, false, false>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs, wq, s,
-                      bz, (uint16_t *)y, M, x_rows, N, K, E);
+    if (packed)
+        launch_kernel((gather_q_kernel<QM, GS, true, true, true>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs, wq,
+                      s, bz, (uint16_t *)y, M, x_rows, N, K, E);
+    else if (layout == 0)
+        launch_kernel((gather_q_kernel<QM, GS, false, false, false>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs,
+                      wq, s, bz, (uint16_t *)y, M, x_rows, N, K, E);
     else if (K % 32 == 0 && host_aligned16(wq))     // then every expert's matrix starts 16-byte aligned too
-        launch_kernel((gather_q_kernel<QM, GS, true, true>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs, wq, s,
-                      bz, (uint16_t *)y, M, x_rows, N, K, E);
+        launch_kernel((gather_q_kernel<QM, GS, true, true, false>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs,
+                      wq, s, bz, (uint16_t *)y, M, x_rows, N, K, E);
     else
-        launch_kernel((gather_q_kernel<QM, GS, true, false>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs, wq, s,
-                      bz, (uint16_t *)y, M, x_rows, N, K, E);
+        launch_kernel((gather_q_kernel<QM, GS, true, false, false>), grid, block, 0, st, (const uint16_t *)x, lhs, rhs,
+                      wq, s, bz, (uint16_t *)y, M, x_rows, N, K, E);
 }
 
 }  // namespace bi
@@ -970,19 +1004,24 @@ extern "C" bi_status bi_gather_qmatmul(const void *x, const int32_t *lhs_idx, co
                                        int64_t M, int64_t x_rows, int64_t N, int64_t K, int64_t E, int32_t qmode,
                                        int32_t bits, int32_t group_size, int32_t w_layout, hipStream_t stream)
 {
-    if (!x || !rhs_idx || !wq || !scales || !y) return BI_ERR_NULL;
+    const bool packed = w_layout == 2;
+    if (!x || !rhs_idx || !wq || (!scales && !packed) || !y) return BI_ERR_NULL;
     if (M < 1 || x_rows < 1 || N < 1 || K < 1 || E < 1 || M > (1ll << 31) || x_rows > (1ll << 31) ||
         N > (1ll << 31) || K > (1ll << 31) || E > kGatherMaxExperts || (!lhs_idx && x_rows < M))
         return BI_ERR_SHAPE;
     if (w_layout < 0 || w_layout > 2) return BI_ERR_SHAPE;
     const bi_status qs = check_qmode(qmode, bits, group_size);
     if (qs != BI_OK) return qs;
-    if (w_layout == 2 || !four_bit_mode(qmode, bits)) return BI_ERR_UNSUPPORTED;
-    if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
-    if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
+    if (!four_bit_mode(qmode, bits)) return BI_ERR_UNSUPPORTED;
+    if (!packed) {
+        if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
+        if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
+    }
     if ((w_layout ? K : N) % group_size) return BI_ERR_GROUP;
-    if ((((uintptr_t)x | (uintptr_t)y | (uintptr_t)scales | (uintptr_t)biases) & 1u) ||
-        (((uintptr_t)wq | (uintptr_t)lhs_idx | (uintptr_t)rhs_idx) & 3u))
+    if (packed && K % kQBlock) return BI_ERR_SHAPE;
+    if ((((uintptr_t)x | (uintptr_t)y) & 1u) || ((uintptr_t)wq & (packed ? 15u : 3u)) ||
+        (!packed && (((uintptr_t)scales | (uintptr_t)biases) & 1u)) ||
+        (((uintptr_t)lhs_idx | (uintptr_t)rhs_idx) & 3u))
         return BI_ERR_ALIGN;
     (void)hipGetLastError();
     const int e = (int)E;

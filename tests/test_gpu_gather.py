@@ -140,3 +140,21 @@ def test_gather_200_runs_one_result():
     first = bi.gather_qmatmul(xd, ld, rd, wqd, sd, bd, N, K, QM[mode], gs, True)
     outs = [bi.gather_qmatmul(xd, ld, rd, wqd, sd, bd, N, K, QM[mode], gs, True) for _ in range(200)]
     assert all(torch.equal(o.view(torch.int16), first.view(torch.int16)) for o in outs)
+
+
+@pytest.mark.parametrize("mode,gs,T,topk,E,K,N", [
+    ("affine", 64, 8, 2, 8, 1024, 512),       # streaming form (16 rows)
+    ("nvfp4", 16, 6, 2, 8, 1024, 8192),       # streaming form, two column groups per tile
+    ("mxfp4", 32, 20, 2, 4, 512, 200),        # tiled form (40 rows), padded last row group
+])
+def test_gather_packed_bits_equal_transposed(mode, gs, T, topk, E, K, N):
+    """Experts packed one by one with pack_qweights and stacked give the
+    transposed gather's bits."""
+    x, lhs, rhs, wq, s, b = inputs.gather_case(T, topk, K, N, E, mode, gs, True, False, seed=T + N)
+    wqd, sd, bd = dev_w(wq, s, b)
+    wp = torch.stack([bi.pack_qweights(wqd[e], sd[e], None if bd is None else bd[e], N, K, QM[mode], gs)
+                      for e in range(E)])
+    y = gather(x, lhs, rhs, (wqd, sd, bd), N, K, mode, gs, True)
+    yp = to_np(bi.gather_qmatmul(to_dev(x, "f16"), idx(lhs), idx(rhs), wp, None, None, N, K, QM[mode], gs,
+                                 packed=True))
+    assert bits_equal(yp, y)
