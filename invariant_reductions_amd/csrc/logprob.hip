@@ -19,7 +19,8 @@
 //   same expression at its column; mean = sum / cols.
 // A row is one workgroup and no other row enters it, so the number of rows
 // and a row's place among them leave its bits unchanged.  Whether a chunk is
-// read as one 16-byte load or element by element changes no sum.
+// read as one 16-byte load or element by element, once or once per pass,
+// changes no sum.
 #include "common.hpp"
 
 #include <cmath>
@@ -55,7 +56,11 @@ __device__ inline int row_chunk8(const typename S::store_t *xr, int64_t k, int64
     return n;
 }
 
-template <typename S, int OP>
+// NC > 0: the row fits in NC chunks per thread (cols <= 8 * 1024 * NC) and is
+// read from memory once, kept in registers for the later passes; NC == 0:
+// every pass re-reads the row.  Either way each value enters the same fold in
+// the same place.
+template <typename S, int OP, int NC>
 __global__ __launch_bounds__(kLsThreads)
 void row_reduce_kernel(const typename S::store_t *__restrict__ x, float *__restrict__ y,
                        const int32_t *__restrict__ ids, int64_t cols, int vec)
@@ -65,14 +70,42 @@ void row_reduce_kernel(const typename S::store_t *__restrict__ x, float *__restr
     const int64_t r = blockIdx.x;
     const typename S::store_t *xr = x + r * cols;
     const int64_t nch = (cols + 7) / 8;
+    float cache[NC > 0 ? NC : 1][8];
+    int ncache[NC > 0 ? NC : 1];
+    if constexpr (NC > 0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int64_t k = t + (int64_t)i * kLsThreads;
+            ncache[i] = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cache[i][e] = 0.0f;
+            if (k < nch) ncache[i] = row_chunk8<S>(xr, k, cols, vec != 0, cache[i]);
+        }
+    }
+    // f(k, n, v) for this thread's chunks k = t, t + 1024, ... in ascending order
+    auto visit = [&](auto &&f) {
+        if constexpr (NC > 0) {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int64_t k = t + (int64_t)i * kLsThreads;
+                if (k < nch) f(k, ncache[i], cache[i]);
+            }
+        } else {
+            for (int64_t k = t; k < nch; k += kLsThreads) {
+                float v[8];
+                const int n = row_chunk8<S>(xr, k, cols, vec != 0, v);
+                f(k, n, v);
+            }
+        }
+    };
 
     float m = -INFINITY;
     if constexpr (OP != ROW_MEAN) {
-        for (int64_t k = t; k < nch; k += kLsThreads) {
-            float v[8];
-            const int n = row_chunk8<S>(xr, k, cols, vec != 0, v);
-            for (int e = 0; e < n; ++e) m = fmaxf(m, v[e]);
-        }
+        visit([&](int64_t, int n, const float (&v)[8]) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e < n) m = fmaxf(m, v[e]);
+        });
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
         if (lane == 0) part[wave] = m;
@@ -84,11 +117,11 @@ void row_reduce_kernel(const typename S::store_t *__restrict__ x, float *__restr
     }
 
     float s = 0.0f;
-    for (int64_t k = t; k < nch; k += kLsThreads) {
-        float v[8];
-        const int n = row_chunk8<S>(xr, k, cols, vec != 0, v);
-        for (int e = 0; e < n; ++e) s = s + (OP == ROW_MEAN ? v[e] : expf(v[e] - m));
-    }
+    visit([&](int64_t, int n, const float (&v)[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e < n) s = s + (OP == ROW_MEAN ? v[e] : expf(v[e] - m));
+    });
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s = s + __shfl_xor(s, off, kWave);
     if (lane == 0) part[wave] = s;
@@ -110,16 +143,16 @@ void row_reduce_kernel(const typename S::store_t *__restrict__ x, float *__restr
         return;
     }
     float *yr = y + r * cols;
-    for (int64_t k = t; k < nch; k += kLsThreads) {
-        float v[8];
-        const int n = row_chunk8<S>(xr, k, cols, vec != 0, v);
+    visit([&](int64_t k, int n, const float (&v)[8]) {
         if (vec && n == 8) {
             *reinterpret_cast<float4 *>(yr + k * 8) = make_float4((v[0] - m) - ls, (v[1] - m) - ls, (v[2] - m) - ls, (v[3] - m) - ls);
             *reinterpret_cast<float4 *>(yr + k * 8 + 4) = make_float4((v[4] - m) - ls, (v[5] - m) - ls, (v[6] - m) - ls, (v[7] - m) - ls);
         } else {
-            for (int e = 0; e < n; ++e) yr[k * 8 + e] = (v[e] - m) - ls;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e < n) yr[k * 8 + e] = (v[e] - m) - ls;
         }
-    }
+    });
 }
 
 template <typename S, int OP>
@@ -127,8 +160,16 @@ static void launch_row(const void *x, float *y, const int32_t *ids, int64_t rows
 {
     // 16-byte loads (and stores) need every row to start on a 16-byte boundary
     const int vec = (cols % 8 == 0) && host_aligned16(x) && (OP != ROW_LOG_SOFTMAX || host_aligned16(y));
-    launch_kernel((row_reduce_kernel<S, OP>), dim3((unsigned)rows), dim3(kLsThreads), 0, st,
-                  (const typename S::store_t *)x, y, ids, cols, vec);
+    const int64_t nch = (cols + 7) / 8;
+    if (nch <= (int64_t)kLsThreads * 4)
+        launch_kernel((row_reduce_kernel<S, OP, 4>), dim3((unsigned)rows), dim3(kLsThreads), 0, st,
+                      (const typename S::store_t *)x, y, ids, cols, vec);
+    else if (nch <= (int64_t)kLsThreads * 8)
+        launch_kernel((row_reduce_kernel<S, OP, 8>), dim3((unsigned)rows), dim3(kLsThreads), 0, st,
+                      (const typename S::store_t *)x, y, ids, cols, vec);
+    else
+        launch_kernel((row_reduce_kernel<S, OP, 0>), dim3((unsigned)rows), dim3(kLsThreads), 0, st,
+                      (const typename S::store_t *)x, y, ids, cols, vec);
 }
 
 template <int OP>
