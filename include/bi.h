@@ -240,8 +240,7 @@ bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *scales, cons
  *            back (each bi_packed_qweight_bytes long; K % 128 == 0, wq
  *            16-byte aligned), scales and biases not read (may be NULL).
  *   y      : [M, N] binary16.
- *   Modes: the 4-bit ones (affine gs 32/64/128, nvfp4, mxfp4); others:
- *   BI_ERR_UNSUPPORTED.  1 <= E <= 1023.  A row whose lhs or rhs index is out
+ *   Modes and code widths: as bi_qmatmul.  1 <= E <= 1023.  A row whose lhs or rhs index is out
  *   of range (a device-side condition the host cannot check) is written as
  *   binary16 NaN; the other rows are unaffected.  Stream-ordered, no
  *   allocation; errors as bi_qmatmul.

@@ -1012,7 +1012,6 @@ extern "C" bi_status bi_gather_qmatmul(const void *x, const int32_t *lhs_idx, co
     if (w_layout < 0 || w_layout > 2) return BI_ERR_SHAPE;
     const bi_status qs = check_qmode(qmode, bits, group_size);
     if (qs != BI_OK) return qs;
-    if (!four_bit_mode(qmode, bits)) return BI_ERR_UNSUPPORTED;
     if (!packed) {
         if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
         if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
@@ -1024,6 +1023,9 @@ extern "C" bi_status bi_gather_qmatmul(const void *x, const int32_t *lhs_idx, co
         (((uintptr_t)lhs_idx | (uintptr_t)rhs_idx) & 3u))
         return BI_ERR_ALIGN;
     (void)hipGetLastError();
+    if (!four_bit_mode(qmode, bits))
+        return bi_gather_qmatmul_wide(x, lhs_idx, rhs_idx, wq, scales, biases, y, M, x_rows, N, K, E, qmode, bits,
+                                      group_size, w_layout, stream);
     const int e = (int)E;
     if (qmode == BI_NVFP4)
         launch_gather<BI_NVFP4, 16>(x, lhs_idx, rhs_idx, wq, scales, biases, y, M, x_rows, N, K, e, w_layout, stream);

@@ -52,3 +52,7 @@ bi_status bi_qmatmul_wide(const void *x, const uint32_t *wq, const void *scales,
                           int32_t w_layout, hipStream_t stream);
 bi_status bi_pack_qweights_wide(const uint32_t *wq, const void *scales, const void *biases, void *wqp, int64_t N,
                                 int64_t K, int32_t qmode, int32_t bits, int32_t group_size, hipStream_t stream);
+bi_status bi_gather_qmatmul_wide(const void *x, const int32_t *lhs, const int32_t *rhs, const uint32_t *wq,
+                                 const void *scales, const void *biases, void *y, int64_t M, int64_t x_rows,
+                                 int64_t N, int64_t K, int64_t E, int32_t qmode, int32_t bits, int32_t group_size,
+                                 int32_t w_layout, hipStream_t stream);

@@ -479,6 +479,176 @@ __global__ void pack_qwide_kernel(const uint32_t *__restrict__ wq, const void *_
     }
 }
 
+// Expert ("gather") matmul at these widths: workgroup (t, e) owns the 16
+// columns of tile t for expert e, compacts the rows routed to e (ascending, a
+// slab of up to kWideGatherSlab rows at a time) into LDS and runs them 16 at a
+// time through qwide_kernel's reduction, so each row has the bits of the
+// plain quantized matmul of its token with its expert.  The workgroups of
+// e = E write NaN to the rows whose token or expert index is out of range.
+// Per expert: codes [N, K*BITS/32] (or [K, N*BITS/32]) and constants, or one
+// packed buffer (PK).
+constexpr int kWideGatherSlab = 4096;
+
+template <int QM, int BITS, bool TRANS, bool PK>
+__global__ __launch_bounds__(kQWaves * kWave)
+void qwide_gather_kernel(const uint16_t *__restrict__ x, const int32_t *__restrict__ lhs,
+                         const int32_t *__restrict__ rhs, const uint32_t *__restrict__ wq,
+                         const void *__restrict__ scales, const uint16_t *__restrict__ biases,
+                         uint16_t *__restrict__ y, int64_t M, int64_t x_rows, int64_t N, int64_t K, int E, int gshift)
+{
+    constexpr int P = kQWaves, NT = kQWaves * kWave;
+    constexpr int SB = QM == BI_AFFINE ? 2 : 1;
+    __shared__ float red[P][16][17];
+    __shared__ int perm[kWideGatherSlab];
+    __shared__ int wcnt[P];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int g = lane >> 4, c = lane & 15;
+    const int e = (int)blockIdx.y;
+    const int64_t n0 = (int64_t)blockIdx.x * 16, n = n0 + c;
+    const bool nok = n < N;
+    const int64_t nblocks = cdiv(K, kQBlock), nrg = cdiv(N, 16);
+    const bool xvec = (K % 8) == 0 && aligned16(x);
+    const int gpb = 128 >> gshift;
+    const int64_t words_e = PK ? nrg * nblocks * (64 * BITS + 4 * gpb * (QM == BI_MXFP8 ? 1 : 4))
+                               : N * K / 32 * BITS;
+    const int64_t groups_e = N * K >> gshift;
+    const int ee = e < E ? e : 0;
+    const uint32_t *we = wq + (int64_t)ee * words_e;
+    const void *se = (const uint8_t *)scales + (int64_t)ee * groups_e * SB;
+    const uint16_t *be = biases ? biases + (int64_t)ee * groups_e : nullptr;
+
+    auto bucket = [&](int64_t m) -> int {
+        const int64_t r = rhs[m], xr = lhs ? (int64_t)lhs[m] : m;
+        return (r >= 0 && r < E && xr >= 0 && xr < x_rows) ? (int)r : E;
+    };
+
+    for (int64_t s0 = 0; s0 < M; s0 += kWideGatherSlab) {
+        const int ns = (int)(M - s0 < kWideGatherSlab ? M - s0 : kWideGatherSlab);
+        int found = 0;
+        for (int i0 = 0; i0 < ns; i0 += NT) {
+            const int i = i0 + tid;
+            const bool hit = i < ns && bucket(s0 + i) == e;
+            const uint64_t mask = __ballot(hit);
+            if (lane == 0) wcnt[wave] = __popcll(mask);
+            __syncthreads();
+            int off = found, tot = 0;
+#pragma unroll
+            for (int w = 0; w < P; ++w) {
+                const int cw = wcnt[w];
+                off += w < wave ? cw : 0;
+                tot += cw;
+            }
+            if (hit) perm[off + __popcll(mask & ((1ull << lane) - 1ull))] = i;
+            found += tot;
+            __syncthreads();
+        }
+        if (e == E) {
+            for (int i = tid; i < found * 16; i += NT) {
+                const int64_t col = n0 + (i & 15);
+                if (col < N) y[(s0 + perm[i >> 4]) * N + col] = 0x7e00u;
+            }
+            __syncthreads();
+            continue;
+        }
+        for (int r0 = 0; r0 < found; r0 += 16) {
+            const int nr = found - r0 < 16 ? found - r0 : 16;
+            const bool rok = c < nr;
+            const int64_t m = s0 + perm[r0 + (rok ? c : 0)];
+            const uint16_t *xrow = x + (lhs ? (int64_t)lhs[m] : m) * K;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int64_t b = wave; b < nblocks; b += P) {
+                const int64_t kbase = b * kQBlock + (int64_t)g * 32;
+                if constexpr (PK || TRANS) {
+                    uint4 Bf[4];
+                    uint32_t w[BITS], sc = 0, bs = 0;
+                    bool have = true;
+                    if constexpr (PK) {
+                        load_packed<QM, BITS>(we, nrg, nblocks, (int64_t)blockIdx.x, b, lane, gshift, w, sc, bs);
+                    } else {
+                        have = nok && kbase < K;
+                        if (have) {
+                            load_words<BITS>(w, we + n * (K / 32 * BITS) + (kbase / 32) * BITS, false);
+                            load_raw_group<QM>(se, be, n * (K >> gshift) + (kbase >> gshift), sc, bs);
+                        }
+                    }
+                    if (have) {
+                        float gsv, gbv;
+                        wgroup<QM>(sc, bs, gsv, gbv);
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) Bf[s] = wdeq8<QM, BITS>(w, s, gsv, gbv);
+                    } else {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) Bf[s] = make_uint4(0, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const uint4 As = xvec ? load_chunk<F16, true>(xrow, kbase + s * 8, K, rok)
+                                              : load_chunk<F16, false>(xrow, kbase + s * 8, K, rok);
+                        acc = qmfma(As, Bf[s], acc);
+                    }
+                } else {
+                    const int64_t wpr = N / 32 * BITS, groups = N >> gshift;
+                    const int64_t bit = n * BITS, wi = bit >> 5;
+                    const int sh = (int)(bit & 31);
+#pragma unroll 1
+                    for (int s = 0; s < 4; ++s) {
+                        uint16_t h[8];
+#pragma unroll
+                        for (int ei = 0; ei < 8; ++ei) {
+                            const int64_t k = kbase + s * 8 + ei;
+                            h[ei] = 0;
+                            if (nok && k < K) {
+                                const uint32_t *row = we + k * wpr;
+                                uint32_t v = row[wi] >> sh;
+                                if (sh + BITS > 32) v |= row[wi + 1] << (32 - sh);
+                                uint32_t sc, bs;
+                                load_raw_group<QM>(se, be, k * groups + (n >> gshift), sc, bs);
+                                h[ei] = wdeq1<QM>(v & ((1u << BITS) - 1u), sc, bs);
+                            }
+                        }
+                        const uint4 As = xvec ? load_chunk<F16, true>(xrow, kbase + s * 8, K, rok)
+                                              : load_chunk<F16, false>(xrow, kbase + s * 8, K, rok);
+                        acc = qmfma(As, __builtin_bit_cast(uint4, h), acc);
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][c] = acc[r];
+            __syncthreads();
+            if (tid < 256) {
+                const int r = tid >> 4, cc = tid & 15;
+                if (r < nr && n0 + cc < N) {
+                    float v = red[0][r][cc];
+#pragma unroll
+                    for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
+                    y[(s0 + perm[r0 + r]) * N + n0 + cc] = F16::narrow(v);
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <int QM, int BITS>
+static void launch_qw_gather(const void *x, const int32_t *lhs, const int32_t *rhs, const uint32_t *wq, const void *s,
+                             const void *b, void *y, int64_t M, int64_t x_rows, int64_t N, int64_t K, int E, int gs,
+                             int layout, hipStream_t st)
+{
+    const int gshift = gs == 32 ? 5 : (gs == 64 ? 6 : 7);
+    const dim3 grid((unsigned)cdiv(N, 16), (unsigned)(E + 1)), block(kQWaves * kWave);
+    const uint16_t *xx = (const uint16_t *)x, *bz = (const uint16_t *)b;
+    uint16_t *yy = (uint16_t *)y;
+    if (layout == 2)
+        launch_kernel((qwide_gather_kernel<QM, BITS, true, true>), grid, block, 0, st, xx, lhs, rhs, wq, s, bz, yy, M,
+                      x_rows, N, K, E, gshift);
+    else if (layout == 1)
+        launch_kernel((qwide_gather_kernel<QM, BITS, true, false>), grid, block, 0, st, xx, lhs, rhs, wq, s, bz, yy, M,
+                      x_rows, N, K, E, gshift);
+    else
+        launch_kernel((qwide_gather_kernel<QM, BITS, false, false>), grid, block, 0, st, xx, lhs, rhs, wq, s, bz, yy, M,
+                      x_rows, N, K, E, gshift);
+}
+
 }  // namespace bi
 
 using namespace bi;
@@ -516,5 +686,27 @@ bi_status bi_pack_qweights_wide(const uint32_t *wq, const void *scales, const vo
     else
         launch_kernel((pack_qwide_kernel<BI_AFFINE>), grid, block, 0, st, wq, scales, (const uint16_t *)biases,
                       (uint32_t *)wqp, N, K, (int)bits, gshift);
+    return launch_status();
+}
+
+bi_status bi_gather_qmatmul_wide(const void *x, const int32_t *lhs, const int32_t *rhs, const uint32_t *wq,
+                                 const void *scales, const void *biases, void *y, int64_t M, int64_t x_rows,
+                                 int64_t N, int64_t K, int64_t E, int32_t qmode, int32_t bits, int32_t group_size,
+                                 int32_t w_layout, hipStream_t st)
+{
+    const int e = (int)E;
+    if (qmode == BI_MXFP8) {
+        launch_qw_gather<BI_MXFP8, 8>(x, lhs, rhs, wq, scales, biases, y, M, x_rows, N, K, e, group_size, w_layout, st);
+    } else {
+        switch (bits) {
+        case 2: launch_qw_gather<BI_AFFINE, 2>(x, lhs, rhs, wq, scales, biases, y, M, x_rows, N, K, e, group_size, w_layout, st); break;
+        case 3: launch_qw_gather<BI_AFFINE, 3>(x, lhs, rhs, wq, scales, biases, y, M, x_rows, N, K, e, group_size, w_layout, st); break;
+        case 5: launch_qw_gather<BI_AFFINE, 5>(x, lhs, rhs, wq, scales, biases, y, M, x_rows, N, K, e, group_size, w_layout, st); break;
+        case 6: launch_qw_gather<BI_AFFINE, 6>(x, lhs, rhs, wq, scales, biases, y, M, x_rows, N, K, e, group_size, w_layout, st); break;
+        case 7: launch_qw_gather<BI_AFFINE, 7>(x, lhs, rhs, wq, scales, biases, y, M, x_rows, N, K, e, group_size, w_layout, st); break;
+        case 8: launch_qw_gather<BI_AFFINE, 8>(x, lhs, rhs, wq, scales, biases, y, M, x_rows, N, K, e, group_size, w_layout, st); break;
+        default: return BI_ERR_GROUP;
+        }
+    }
     return launch_status();
 }

@@ -207,8 +207,9 @@ def test_packed_weight_validation():
     ((A, A, A, A, A, A, A, 4, 4, 64, 256, 1024, 0, 4, 32, 1), SHAPE),      # too many experts
     ((A, A, A, A, None, None, A, 4, 4, 64, 192, 8, 0, 4, 32, 2), SHAPE),   # packed: K % 128
     ((A, A, A, P(0x10014), None, None, A, 4, 4, 64, 256, 8, 0, 4, 32, 2), ALIGN),   # packed: 16-byte wq
-    ((A, A, A, A, A, None, A, 4, 4, 64, 256, 8, 3, 8, 32, 1), UNSUP),      # mxfp8
-    ((A, A, A, A, A, A, A, 4, 4, 64, 256, 8, 0, 8, 32, 1), UNSUP),         # affine 8-bit
+    ((A, A, A, A, A, A, A, 4, 4, 64, 256, 8, 3, 8, 32, 1), GROUP),         # mxfp8 takes no biases
+    ((A, A, A, A, A, A, A, 4, 4, 64, 1040, 8, 0, 8, 32, 1), GROUP),        # affine 8-bit: K % gs
+    ((A, A, A, A, A, A, A, 4, 4, 64, 256, 8, 0, 9, 32, 1), GROUP),         # affine bits 2..8
     ((A, A, A, A, A, A, A, 4, 4, 64, 1040, 8, 0, 4, 32, 1), GROUP),        # K % gs
     ((A, A, A, A, A, A, A, 4, 4, 64, 256, 8, 1, 4, 16, 1), GROUP),         # nvfp4 takes no biases
     ((A, P(0x10002), A, A, A, A, A, 4, 4, 64, 256, 8, 0, 4, 32, 1), ALIGN),

@@ -158,3 +158,30 @@ def test_gather_packed_bits_equal_transposed(mode, gs, T, topk, E, K, N):
     yp = to_np(bi.gather_qmatmul(to_dev(x, "f16"), idx(lhs), idx(rhs), wp, None, None, N, K, QM[mode], gs,
                                  packed=True))
     assert bits_equal(yp, y)
+
+
+@pytest.mark.parametrize("mode,gs,bits", [("affine", 64, 3), ("affine", 32, 8), ("mxfp8", 32, 8), ("affine", 128, 6)])
+@pytest.mark.parametrize("layout", ["transposed", "natural", "packed"])
+def test_gather_other_widths(mode, gs, bits, layout):
+    """Affine codes of 2 to 8 bits and mxfp8: parity with the oracle, and
+    every row the plain quantized matmul of its token with its expert (the
+    packed experts: the transposed call's bits)."""
+    T, topk, E, K, N = 10, 2, 4, 512 if layout != "natural" else 520, 128
+    transposed = layout != "natural"
+    qm = {"affine": bi.AFFINE, "mxfp8": bi.MXFP8}[mode]
+    oqm = {"affine": oracle.AFFINE, "mxfp8": oracle.MXFP8}[mode]
+    x, lhs, rhs, wq, s, b = inputs.gather_case(T, topk, K, N, E, mode, gs, transposed, False, seed=bits, bits=bits)
+    wqd, sd, bd = dev_w(wq, s, b)
+    xd = to_dev(x, "f16")
+    if layout == "packed":
+        wp = torch.stack([bi.pack_qweights(wqd[e], sd[e], None if bd is None else bd[e], N, K, qm, gs, bits=bits)
+                          for e in range(E)])
+        y = to_np(bi.gather_qmatmul(xd, idx(lhs), idx(rhs), wp, None, None, N, K, qm, gs, packed=True, bits=bits))
+    else:
+        y = to_np(bi.gather_qmatmul(xd, idx(lhs), idx(rhs), wqd, sd, bd, N, K, qm, gs, transposed, bits=bits))
+    assert_parity(y, oracle.gather_qmatmul(x, lhs, rhs, wq, s, b, N, K, oqm, gs, transposed, bits=bits), "f16")
+    for m in (0, 7, 19):
+        e = int(rhs[m])
+        one = to_np(bi.qmatmul(xd[lhs[m]:lhs[m] + 1].contiguous(), wqd[e], sd[e], None if bd is None else bd[e], N, K,
+                               qm, gs, transposed, bits=bits))
+        assert bits_equal(y[m:m + 1], one), f"row {m} (expert {e})"
