@@ -10,7 +10,10 @@
 // What is computed: W is dequantized in registers to binary16 --
 //   affine: w = RNE16(fma(s, q, b)) with binary16 s, b (the product s*q is
 //           exact in fp32, so the fma rounds once, exactly like mul-then-add);
-//   nvfp4 : w = e2m1(q) * e4m3(s), exact in fp32 and in binary16 --
+//   nvfp4 : w = e2m1(q) * e4m3(s), exact in fp32 and in binary16;
+//   mxfp4 : w = RNE16(e2m1(q) * 2^(e - 127)), the exact product rounded once
+//           (in registers by gfx950's OCP scaled fp4 conversion, checked for
+//           every code at every scale byte against the oracle) --
 // and multiplied against binary16 x by the same MFMA tree as the dense
 // kernel: K blocks of 128, block b owned by wave b mod 8, lane group g
 // supplying elements [32g, 32g + 32) of a block as four v_mfma_f32_16x16x32_f16
@@ -37,28 +40,15 @@ __device__ inline float e2m1_to_f32(uint32_t c)
 template <int QM>
 struct QGroup {                      // per-group dequantization constants
     float s, b;
-    uint32_t m;                      // mxfp4: binary16 factors 2^k1 | 2^k2 << 16 (see mx_group)
 };
 
 
-// mxfp4 group of scale byte e (k = e - 127): s = 2^k in fp32 for the
-// element-wise path, and the binary16 pair (2^k1, 2^k2), k1 = clamp(k, -13,
-// 13), k2 = clamp(k - k1, -24, 15), for the packed path.  e2m1 * 2^k1 is
-// exact in binary16 (two significant bits, between 2^-14 and 49152), so the
-// second product is the only rounding: RNE(e2m1 * 2^k) whenever k1 + k2 = k,
-// i.e. for -37 <= k <= 28; below, every value rounds to +-0 either way, above
-// every nonzero value overflows to +-inf either way.  e = 0xFF: 2^k2 is NaN.
+// mxfp4 group of scale byte e: s = 2^(e - 127) in fp32 (NaN for 0xFF).
 __device__ inline QGroup<BI_MXFP4> mx_group(uint32_t e)
 {
     QGroup<BI_MXFP4> g;
     g.s = e8m0_to_f32(e);
     g.b = 0.0f;
-    const int k = (int)e - 127;
-    const int k1 = k < -13 ? -13 : (k > 13 ? 13 : k);
-    const int k2r = k - k1, k2 = k2r < -24 ? -24 : (k2r > 15 ? 15 : k2r);
-    const uint32_t h1 = (uint32_t)(k1 + 15) << 10;
-    const uint32_t h2 = e == 0xffu ? 0x7e00u : (k2 >= -14 ? (uint32_t)(k2 + 15) << 10 : 1u << (k2 + 24));
-    g.m = h1 | (h2 << 16);
     return g;
 }
 
@@ -162,18 +152,13 @@ __device__ inline uint4 deq_word(uint32_t w, const QGroup<QM> &g)
             out[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
         }
     } else if constexpr (QM == BI_MXFP4) {
-        // e2m1 * 2^-14 from the code bits (as nvfp4), times 2^14 and 2^k1
-        // (both exact), times 2^k2 (the one rounding; see mx_group)
-        const f16x2 k14 = f16x2{(_Float16)16384.0f, (_Float16)16384.0f};
-        const f16x2 s1 = __builtin_bit_cast(f16x2, (g.m & 0xffffu) * 0x00010001u);
-        const f16x2 s2 = __builtin_bit_cast(f16x2, (g.m >> 16) * 0x00010001u);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t t = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | (uint32_t)p | ((uint32_t)(4 + p) << 16));
-            const uint32_t bits = ((t & 0x00080008u) << 12) | ((t & 0x00070007u) << 9);
-            const f16x2 v = ((__builtin_bit_cast(f16x2, bits) * k14) * s1) * s2;
-            out[p] = __builtin_bit_cast(uint32_t, v);
-        }
+        // two codes (one byte, low nibble first) at a time through the OCP
+        // scaled fp4 conversion with the e8m0 scale 2^k: e2m1 * 2^k rounded
+        // once to binary16
+        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, g.s, 0));
+        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, g.s, 1));
+        out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, g.s, 2));
+        out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, g.s, 3));
     } else {
         const _Float16 sh = (_Float16)g.s;                 // e4m3 values are exact in binary16
         const f16x2 sv = f16x2{sh, sh}, k14 = f16x2{(_Float16)16384.0f, (_Float16)16384.0f};
