@@ -133,12 +133,11 @@ __device__ inline uint16_t deq1(uint32_t q, const QGroup<QM> &g)
 //   affine: the nibbles are split into bytes (codes 0,2,4,6 and 1,3,5,7),
 //           converted exactly to fp32, w = fma(s, q, b) in fp32, and each
 //           pair rounded to binary16 (RNE) by one packed conversion;
-//   nvfp4 : code c = sign | e | m is placed as the binary16 pattern
-//           (sign << 15) | ((e, m) << 9), whose value is e2m1(c) * 2^-14
-//           exactly (e = 0 lands in the subnormal range, m * 2^-15); one
-//           packed multiply by 2^14 and one by the scale give e2m1 * scale,
-//           exact in binary16 (at most 6 significant bits, |w| <= 2688,
-//           smallest magnitude 2^-10).
+//   nvfp4 : the e4m3 scale split as 2^E * f (f = +-1.mmm); e2m1 * 2^E by
+//           the OCP scaled fp4 conversion, two codes per instruction, then one
+//           packed binary16 multiply by f; both steps exact (at most 6
+//           significant bits, |w| <= 2688, smallest magnitude 2^-10), so the
+//           result is e2m1 * scale exactly.
 template <int QM>
 __device__ inline uint4 deq_word(uint32_t w, const QGroup<QM> &g)
 {
@@ -160,16 +159,20 @@ __device__ inline uint4 deq_word(uint32_t w, const QGroup<QM> &g)
         out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, g.s, 2));
         out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, g.s, 3));
     } else {
-        const _Float16 sh = (_Float16)g.s;                 // e4m3 values are exact in binary16
-        const f16x2 sv = f16x2{sh, sh}, k14 = f16x2{(_Float16)16384.0f, (_Float16)16384.0f};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            // code 2p -> bits 0..3, code 2p + 1 -> bits 16..19
-            const uint32_t t = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | (uint32_t)p | ((uint32_t)(4 + p) << 16));
-            const uint32_t bits = ((t & 0x00080008u) << 12) | ((t & 0x00070007u) << 9);
-            const f16x2 v = (__builtin_bit_cast(f16x2, bits) * k14) * sv;
-            out[p] = __builtin_bit_cast(uint32_t, v);
-        }
+        // scale = 2^E * f with f = +-1.mmm: e2m1 * 2^E by the OCP scaled fp4
+        // conversion (exact: |e2m1 * 2^E| in [2^-10, 1536] or zero), then one
+        // packed binary16 multiply by f (exact: at most 6 significant bits);
+        // a NaN scale makes f NaN
+        const uint32_t vb = __float_as_uint(g.s);
+        const float s2 = __uint_as_float(vb & 0x7f800000u);
+        const bool nan = (vb & 0x7fffffffu) > 0x7f800000u;
+        const _Float16 fh = nan ? (_Float16)__uint_as_float(0x7fc00000u)
+                                : (_Float16)__uint_as_float((vb & 0x807fffffu) | 0x3f800000u);
+        const f16x2 fv = f16x2{fh, fh};
+        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s2, 0) * fv);
+        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s2, 1) * fv);
+        out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s2, 2) * fv);
+        out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s2, 3) * fv);
     }
     return make_uint4(out[0], out[1], out[2], out[3]);
 }

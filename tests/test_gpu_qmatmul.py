@@ -181,6 +181,31 @@ def test_nvfp4_every_code_at_every_scale_byte(transposed):
     assert bits_equal(run(x, wq, s, None, N, K, "nvfp4", 16, transposed), r)
 
 
+@pytest.mark.parametrize("transposed", [True, False])
+def test_nvfp4_nan_and_zero_scales_match_oracle(transposed):
+    """NaN scale bytes (0x7F, 0xFF) make their group's weights NaN and signed
+    zero scales (0x00, 0x80) make them zeros, as in the oracle; the rest of
+    the output is unaffected (unit scales, integer x: exact sums)."""
+    M, K, N = 3, 256, 64
+    rng = np.random.default_rng(12)
+    rows, cols = (N, K) if transposed else (K, N)
+    codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint32)
+    s = np.full((rows, cols // 16), 0x38, np.uint8)
+    if transposed:
+        s[5, 3], s[9, 10] = 0x7F, 0xFF
+        s[20:24, 2], s[30, :] = 0x00, 0x80
+    else:
+        s[17, 1], s[100, 3] = 0x7F, 0xFF
+        s[40:44, 2], s[60, :] = 0x00, 0x80
+    wq = inputs.pack_nibbles(codes)
+    x = inputs.integer_values(rng, (M, K), 1, 2, "f16")
+    r = oracle.round_to(ref(x, wq, s, None, M, N, K, "nvfp4", 16, transposed), "f16")
+    g = run(x, wq, s, None, N, K, "nvfp4", 16, transposed)
+    rf, gf = inputs.from_storage(r, "f16"), inputs.from_storage(g, "f16")
+    assert np.isnan(rf).any() and np.isfinite(rf).any()
+    assert np.array_equal(rf, gf, equal_nan=True)
+
+
 def test_mxfp4_extreme_scales_match_oracle():
     """Scales far outside binary16 (e = 0, 1, 100, 150, 254) and the NaN byte:
     the dequantized weights overflow to inf, flush to zero or are NaN exactly
