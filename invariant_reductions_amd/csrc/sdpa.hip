@@ -376,6 +376,12 @@ void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict
     float *wts = smem;                                    // [nchunks]
     float *lws = smem + sh.nchunks;                       // [nchunks]
     __shared__ float red[kHeadDim / kWave];
+    // the first kMergeEarly chunks' o values do not depend on the max: request
+    // them now, with the m values, rather than after the weights are known
+    constexpr int kMergeEarly = 8;
+    float oe[kMergeEarly];
+#pragma unroll
+    for (int cc = 0; cc < kMergeEarly; ++cc) oe[cc] = cc <= last ? pr[cc * kPartStride + d] : 0.0f;
 
     float m = -INFINITY;
     for (int64_t cc = d; cc <= last; cc += kHeadDim) m = fmaxf(m, pr[cc * kPartStride + kHeadDim]);
@@ -393,8 +399,15 @@ void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict
     }
     __syncthreads();
     float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < kMergeEarly; ++cc) {
+        if (cc <= last) {
+            o = o + oe[cc] * wts[cc];
+            l = l + lws[cc];
+        }
+    }
 #pragma unroll 8
-    for (int64_t cc = 0; cc <= last; ++cc) {
+    for (int64_t cc = kMergeEarly; cc <= last; ++cc) {
         o = o + pr[cc * kPartStride + d] * wts[cc];
         l = l + lws[cc];
     }
