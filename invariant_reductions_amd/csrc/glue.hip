@@ -46,11 +46,12 @@ __global__ void rope_kv_kernel(const uint16_t *__restrict__ qkv, uint16_t *__res
         const int rem = (int)(it - tok * per_tok);
         const int hh = rem / ng, i = (rem - hh * ng) * G;
         const int64_t b = tok / Q, j = tok - b * Q;
-        const int64_t pos = (int64_t)kv_len[b] - Q + j;
-        if (pos < 0 || pos >= Lcap || pos >= max_pos) continue;   // out-of-range positions write nothing
+        // the qkv row is requested before the position is known (it is in bounds either way)
         const uint16_t *src = qkv + tok * (int64_t)heads * D + (int64_t)hh * D;
         const vec_t lo_in = *reinterpret_cast<const vec_t *>(src + i);
         const vec_t hi_in = *reinterpret_cast<const vec_t *>(src + i + half);
+        const int64_t pos = (int64_t)kv_len[b] - Q + j;
+        if (pos < 0 || pos >= Lcap || pos >= max_pos) continue;   // out-of-range positions write nothing
         if (hh >= Hq + Hkv) {                                      // v: copied to the cache unchanged
             uint16_t *dst = vc + cache_at(b, pos, hh - Hq - Hkv);
             *reinterpret_cast<vec_t *>(dst + i) = lo_in;
