@@ -41,7 +41,6 @@ constexpr int kHeadDim = 128;        // D supported by this build
 constexpr int kAttnWaves = 4;        // waves per chunk workgroup (frozen: 64 keys each)
 constexpr int kKeysPerWave = kChunk / kAttnWaves;
 constexpr int kPartStride = kHeadDim + 4;   // floats per (row, chunk) partial: o[D], m, l, pad
-constexpr int kVStride = kHeadDim + 2;      // LDS row stride (elements) of the staged V tile
 constexpr int64_t kMaxKv = 1ll << 20;     // keeps pass 2's per-chunk weights within 32 KiB of LDS
 constexpr int kAttnMinTiles = 4;     // fewest query-row tiles (of 16) per work item when a prompt is split
 
