@@ -298,7 +298,7 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
                          int64_t rows, int64_t H, float eps, int32_t dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Decode / verify scaled-dot-product attention (GQA), two passes.
+ * Decode / verify / prefill scaled-dot-product attention (GQA).
  * Source: "Fix/speculative shape invariance", Problem and Changes (the
  * softmax reduction layout of a query must be the same alone or inside a
  * short causal block); "Batch-invariant kernels ...", Case 6 (fixed split
@@ -314,15 +314,22 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
  *            With causal != 0 it attends to keys 0..p, else to 0..kv_len[b]-1.
  *            Requires Q <= kv_len[b] <= max_kv_len <= Lcap (not checked on the
  *            host because kv_len lives on the device; positions beyond a
- *            row's limit are never read).
+ *            row's limit are never read; a violating value may leave that
+ *            sequence's outputs unwritten or wrong, never touches memory
+ *            outside the buffers).
  *   Query head h reads key/value head h / (Hq / Hkv); Hq % Hkv == 0.
  *   D must be 128 in this build.  scale is applied to q.k in fp32.
- *   ws     : device workspace of at least bi_sdpa_workspace_bytes(...) bytes,
- *            16-byte aligned; its contents on entry are ignored.
- * Keys are processed in chunks of a constant size (bi_build_info reports it);
- * the chunk a key falls in depends only on its position.  Each chunk's
- * partial (max, sum, weighted values) is merged in ascending chunk order, and
- * chunks past a query's last key are never merged.
+ *   ws     : device workspace of at least bi_sdpa_workspace_bytes(...) bytes
+ *            (the chunk partials), 16-byte aligned; its contents on entry are
+ *            ignored.  Calls that share a workspace must be ordered (same
+ *            stream or synchronised).
+ * Tree (frozen; bi_build_info reports it): keys in chunks of 256 positions,
+ * chunks in ranges of 16; a chunk's (max, sum, weighted values) partial, the
+ * ranges' partials and the row's result are each added in ascending order.
+ * The chunk and range a key falls in depend only on its position, and chunks
+ * past a query's last key are never merged, so a row's bits do not depend on
+ * B, Q, the other rows or the launch.  Two launches: the chunk partials,
+ * then the range and row levels.
  * ------------------------------------------------------------------------ */
 size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int32_t Hq, int32_t D);
 

@@ -331,5 +331,7 @@ extern "C" const char *bi_build_info(void)
            " slots added pairwise ((0+1)+(2+3))+((4+5)+(6+7));"
            " qmatmul: dequantize to binary16 in registers, v_mfma_f32_16x16x32_f16, same K slicing;"
            " rmsnorm: one wave per row, 16-byte chunk v to lane v%64, per-lane fma fold, xor butterfly 32..1;"
-           " sdpa: chunks of 256 keys, 4 waves x 64 keys, bf16 P in MFMA, pass-2 weights exp(m_c-M) summed in chunk order";
+           " sdpa: chunks of 256 keys, 4 waves x 64 keys, P as hi+lo 16-bit parts in MFMA (lo first),"
+           " chunk partials merged in ranges of 16 chunks (weights exp(m_c-M_r), ascending), ranges merged"
+           " in ascending order (weights exp(M_r-M))";
 }

@@ -1,4 +1,4 @@
-// sdpa.hip -- batch-invariant decode / verify attention on gfx950.
+// sdpa.hip -- batch-invariant decode / verify / prefill attention on gfx950.
 //
 // Sources: "Fix/speculative shape invariance" (Problem: two-pass SDPA derived
 // its split count from the query length; Changes: the single-query split
@@ -8,28 +8,36 @@
 // splits, KV cache updated before the kernel; Try this, item 5).
 //
 // Reduction tree of one query row r at position p (frozen; depends on p only):
-//   Pass 1 -- keys are cut into chunks of kChunk = 256 positions; chunk c holds
-//   keys [256c, 256c + 256) and is handled by its own workgroup for all query
-//   rows of one (sequence, KV head).  Inside the chunk, wave w owns keys
+//   Chunks -- keys are cut into chunks of kChunk = 256 positions; chunk c holds
+//   keys [256c, 256c + 256) and is handled by one workgroup for all query rows
+//   of one (sequence, KV head).  Inside the chunk, wave w owns keys
 //   [64w, 64w + 64):
-//     s_t   = scale * (q . k_t)      one 16x16x32 bf16 MFMA chain over d
-//                                    (4 steps; lane group g supplies d in
-//                                    [32g, 32g + 32), step s the s-th 8 of them)
+//     s_t   = scale * (q . k_t)      one 16x16x32 MFMA chain over d (4 steps;
+//                                    step s takes d in [32s, 32s + 32), lane
+//                                    group g supplies the 8 at 32s + 8g)
 //     m_c   = max of s_t over the chunk's keys t <= p (exact, order-free)
 //     p_t   = exp(s_t - m_c); keys t > p contribute exactly +0
 //     l_c   = sum p_t: per lane over its 4 key tiles in order, then a xor
 //             butterfly over the 16 lanes of a row (1, 2, 4, 8), then waves in
 //             order 0..3
-//     o_c   = sum bf16(p_t) * v_t: MFMA over the wave's 64 keys (2 steps of 32),
+//     o_c   = sum p_t * v_t with p_t carried as two 16-bit parts, hi =
+//             RNE(p_t) and lo = RNE(p_t - hi): MFMA over the wave's 64 keys,
+//             the lo products (2 steps of 32 keys) before the hi products,
 //             then the four wave partials added in order 0..3
-//   Pass 2 -- for the chunks 0..floor(p/256):
-//     M = max_c m_c (exact);  w_c = exp(m_c - M)
-//     o = sum_c o_c * w_c and l = sum_c l_c * w_c, both in ascending c
-//     out = RNE(o / l)
+//   Ranges -- chunks are grouped in ranges of kRange = 16 (4096 keys); for the
+//   chunks 16r .. min(16r + 15, floor(p / 256)) of range r:
+//     M_r = max m_c (exact);  w_c = exp(m_c - M_r)
+//     o_r = sum o_c * w_c and l_r = sum l_c * w_c in ascending c
+//   Row -- over the ranges 0 .. floor(p / 4096):
+//     M = max M_r (exact);  u_r = exp(M_r - M)
+//     o = sum o_r * u_r and l = sum l_r * u_r in ascending r;  out = RNE(o / l)
 // A query row never meets another row except inside an MFMA (rows are
 // independent there), so the number of queries Q, the GQA group, the batch and
 // where the row sits in its tile leave its bits unchanged; a query of a causal
 // verify block and a lone query at the same position reduce identically.
+//
+// The chunk level is one launch (attn_kernel); the range and row levels are a
+// second (attn_merge_kernel), one workgroup per query row.
 #include <algorithm>
 
 #include "common.hpp"
@@ -37,11 +45,12 @@
 namespace bi {
 
 constexpr int kChunk = 256;          // keys per chunk (frozen)
+constexpr int kRange = 16;           // chunks per merge range (frozen: 4096 keys)
 constexpr int kHeadDim = 128;        // D supported by this build
 constexpr int kAttnWaves = 4;        // waves per chunk workgroup (frozen: 64 keys each)
 constexpr int kKeysPerWave = kChunk / kAttnWaves;
 constexpr int kPartStride = kHeadDim + 4;   // floats per (row, chunk) partial: o[D], m, l, pad
-constexpr int64_t kMaxKv = 1ll << 20;     // keeps pass 2's per-chunk weights within 32 KiB of LDS
+constexpr int64_t kMaxKv = 1ll << 20;
 constexpr int kAttnMinTiles = 4;     // fewest query-row tiles (of 16) per work item when a prompt is split
 
 __device__ inline f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c)
@@ -59,17 +68,19 @@ template <> __device__ inline f32x4 mfma16<BF16>(uint4 a, uint4 b, f32x4 c) { re
 template <> __device__ inline f32x4 mfma16<F16>(uint4 a, uint4 b, f32x4 c) { return mfma_f16(a, b, c); }
 
 struct AttnShape {
-    int64_t B, Q, Lcap, nchunks, max_kv, nmg;     // nmg: row groups of mgt 16-row tiles per (b, c, hk)
+    int64_t B, Q, Lcap, nchunks, nranges, max_kv, nmg;  // nmg: row groups of mgt 16-row tiles per (b, c, hk)
     int Hq, Hkv, G, mgt;
     float scale;
     int causal;
     int64_t ks, hs;       // cache strides (elements) between consecutive keys and between KV heads
 };
 
-__device__ inline int64_t row_last_key(int64_t kvlen, int64_t Q, int64_t j, int causal)
-{
-    return causal ? kvlen - Q + j : kvlen - 1;
-}
+struct AttnBufs {
+    const uint16_t *q, *k, *v;
+    const int32_t *kv_len;
+    uint16_t *o;
+    float *part;          // chunk partials [B*Q*Hq][nchunks][kPartStride]
+};
 
 // In-place 8 x 8 transpose of 16-bit elements held by one lane: row e is
 // m[e] (elements j = 0..7); afterwards m[j] holds column j.  Pairs of rows
@@ -96,36 +107,52 @@ __device__ inline void transpose8x8_b16(uint4 (&m)[8])
     }
 }
 
-// Pass 1 as a persistent, software-pipelined kernel.  Work item = (sequence
-// b, chunk c, KV head hk, row group mg) -- mg picks sh.mgt of the 16-row query
-// tiles, so a long prompt with few sequences spreads over many workgroups (at
-// decode and verify sizes there is one group); a fixed grid of workgroups
-// walks the item ids
-// t = blockIdx.x, blockIdx.x + gridDim.x, ...  With u = t / nmg and mg = t %
-// nmg, the ids are ordered so that the items of all KV heads of one (b, c)
-// are processed together on one XCD at decode sizes (nmg = 1): id u -> XCD u
-// % 8 (the hardware's round-robin when gridDim.x % 8 == 0), hk = (u / 8) %
-// Hkv, (b, c) = (u / (8 Hkv)) * 8 + u % 8; their key rows
-// [b][pos][0..Hkv)[0..D) are contiguous in the cache.  Inside an item, wave w
-// owns keys [64w, 64w + 64) of the chunk (the frozen tree above).  The
-// resident workgroups drift out of step, so the cache streams without the
-// idle gaps of a grid that starts and finishes its workgroups in rounds.
+__device__ inline int attn_last_key(int kvlen, int Q, int j, int causal) { return causal ? kvlen - Q + j : kvlen - 1; }
+
+__device__ inline int64_t attn_row(const AttnShape &sh, int b, int hk, int rl)
+{
+    const int j = rl / sh.G;
+    return ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (rl - j * sh.G);
+}
+
+// Writes out = RNE(o / l) for the four d values of one quad.
+template <typename S>
+__device__ inline void attn_store_out(uint16_t *dst, float4 o, float l)
+{
+    uint2 pk;
+    pk.x = (uint32_t)S::narrow(o.x / l) | ((uint32_t)S::narrow(o.y / l) << 16);
+    pk.y = (uint32_t)S::narrow(o.z / l) | ((uint32_t)S::narrow(o.w / l) << 16);
+    *reinterpret_cast<uint2 *>(dst) = pk;
+}
+
+// The kernel: a persistent, software-pipelined walk over work items.  Work
+// item = (sequence b, chunk c, KV head hk, row group mg) -- mg picks sh.mgt of
+// the 16-row query tiles, so a long prompt with few sequences spreads over
+// many workgroups (at decode and verify sizes there is one group); a fixed
+// grid of workgroups walks the item ids t = blockIdx.x, blockIdx.x +
+// gridDim.x, ...  With u = t / nmg and mg = t % nmg, the ids are ordered so
+// that the items of all KV heads of one (b, c) are processed together on one
+// XCD at decode sizes (nmg = 1): id u -> XCD u % 8 (the hardware's
+// round-robin when gridDim.x % 8 == 0), hk = (u / 8) % Hkv, (b, c) = (u / (8
+// Hkv)) * 8 + u % 8.  Inside an item, wave w owns keys [64w, 64w + 64) of the
+// chunk (the frozen tree above).  The next item's K and q are requested as
+// soon as the current item's last scores have read them (in flight during the
+// softmax, P . V, the arrival handshake and any merge), its V once the
+// current item is done (in flight during the next scores).
 //
 // Register layouts (lane = 16 g4 + c16):
-//   K  : kf[kt][s] = key 16kt + c16, d in [32 g4 + 8 s, +8)   (MFMA B of q . k)
+//   K  : kf[kt][s] = key 16kt + c16, d in [32 s + 8 g4, +8)   (MFMA B of q . k)
 //   V  : rows loaded as vr[s2][e] = key 32 s2 + 8 g4 + e, d in [8 c16, +8),
 //        transposed in place to vr[s2][j] = those 8 keys at d = 8 c16 + j,
 //        the MFMA B operand of P . V (k slot 8 g4 + e of step s2 = key
 //        32 s2 + 8 g4 + e, column c16 = d 8 c16 + j of output tile j).
 template <typename S, bool MG>
 __global__ __launch_bounds__(kAttnWaves * kWave, 2)
-void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                       const uint16_t *__restrict__ v, const int32_t *__restrict__ kv_len,
-                       float *__restrict__ part, AttnShape sh, int64_t nid)
+void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, int64_t nid)
 {
     typedef uint16_t PTile[16][kKeysPerWave + 8];
     typedef float OTile[16][kHeadDim + 4];
-    __shared__ __attribute__((aligned(16))) PTile pl[kAttnWaves];
+    __shared__ __attribute__((aligned(16))) PTile phi[kAttnWaves], plo[kAttnWaves];
     __shared__ __attribute__((aligned(16))) OTile ol[kAttnWaves];
     __shared__ float xm[kAttnWaves][16], xl[kAttnWaves][16];
 
@@ -134,10 +161,18 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
     const int R = (int)sh.Q * sh.G;                                      // query rows per KV head
     const int ntm = (R + 15) / 16;
     const int64_t nitems = sh.B * sh.nchunks;
+    const int Qi = (int)sh.Q;
 
-    // b, c, hk and the clamped length of one item; kv_len is device data the
-    // host cannot validate, so it is clamped to max_kv, which keeps every
-    // access inside the cache and the workspace even for a bad value.
+    // The sequence lengths, clamped to max_kv (device data the host cannot
+    // validate: the clamp keeps every access inside the cache and the
+    // workspace even for a bad value), are read with scalar loads (a
+    // wave-uniform index into a read-only argument): a vector-memory read
+    // inside the walk would make the wave wait for every load in flight, one
+    // counter covering them all.
+    auto seq_len = [&](int b) {
+        return (int)min((int64_t)kv_len[__builtin_amdgcn_readfirstlane(b)], sh.max_kv);
+    };
+    // b, c, hk and the clamped length of one item
     struct Item {
         int b, c, hk, kvlen, mg;
     };
@@ -150,88 +185,99 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
         const bool exists = bc < nitems;
         it.b = exists ? (int)(bc / sh.nchunks) : 0;
         it.c = exists ? (int)(bc - (int64_t)it.b * sh.nchunks) : -1;
-        it.kvlen = (int)min((int64_t)kv_len[it.b], sh.max_kv);
+        it.kvlen = seq_len(it.b);
         return it;
     };
-    const int Qi = (int)sh.Q;
-    auto last_key = [&](int kvlen, int j) { return sh.causal ? kvlen - Qi + j : kvlen - 1; };
-    // an item has work when it exists and its first key is visible to the last row of its group
-    auto has_work = [&](const Item &it) {
-        if (!MG) return it.c >= 0 && it.c * kChunk <= last_key(it.kvlen, Qi - 1);
-        const int rl = min(R, (it.mg + 1) * sh.mgt * 16) - 1;
-        return it.c >= 0 && it.c * kChunk <= last_key(it.kvlen, rl / sh.G);
+    auto last_key = [&](int kvlen, int j) { return attn_last_key(kvlen, Qi, j, sh.causal); };
+    // rows [r0, r1) of an item's row group
+    auto group_rows = [&](const Item &it, int &r0, int &r1) {
+        r0 = MG ? it.mg * sh.mgt * 16 : 0;
+        r1 = MG ? min(R, r0 + sh.mgt * 16) : R;
     };
+    // last key any row of the item's group sees
+    auto group_last_key = [&](const Item &it) {
+        int r0, r1;
+        group_rows(it, r0, r1);
+        return last_key(it.kvlen, (r1 - 1) / sh.G);
+    };
+    // an item has work when it exists and its first key is visible to the last row of its group
+    auto has_work = [&](const Item &it) { return it.c >= 0 && it.c * kChunk <= group_last_key(it); };
     auto next_id = [&](int64_t t) {
         for (; t < nid; t += gridDim.x)
             if (has_work(decode(t))) break;
         return t;
     };
-    // Loads are unconditional: a missing key (position >= kv_len) reads the
-    // item's first key, which always exists (the item has work), and the
-    // value is then replaced by zero.  Bases are wave-uniform; per-lane
-    // offsets are 32-bit.
+    // Keys at or past kv_len are not read: a lane whose key is missing reads
+    // the item's first key (which always exists) instead.  Nothing is
+    // selected on the loaded values here -- a select would make the wave wait
+    // for each load as it is issued; the scores of missing keys (and padding
+    // rows of q) are masked after the product, and missing V rows are zeroed
+    // just before P . V reads them.  Bases are wave-uniform; per-lane offsets
+    // are 32-bit.
     const int rs = (int)sh.ks;                                           // elements between keys
     auto item_base = [&](const uint16_t *p, const Item &it) {
         return p + (int64_t)it.b * sh.Lcap * sh.Hkv * kHeadDim + (int64_t)it.c * kChunk * rs + (int64_t)it.hk * sh.hs;
     };
-    // keys of this wave that exist
     auto wave_valid = [&](const Item &it) { return min(max(it.kvlen - (it.c * kChunk + wave * kKeysPerWave), 0), kKeysPerWave); };
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
     auto load_k = [&](const Item &it, uint4 (&kf)[4][4]) {
-        const uint16_t *kb = item_base(k, it);
+        const uint16_t *kb = item_base(bf.k, it);
         const int nv = wave_valid(it);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int kk = kt * 16 + c16;
-            const bool ok = kk < nv;
-            const uint16_t *kr = kb + (ok ? wave * kKeysPerWave + kk : 0) * rs + g4 * 32;
+            const uint16_t *kr = kb + (kk < nv ? wave * kKeysPerWave + kk : 0) * rs + g4 * 8;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint4 x = *reinterpret_cast<const uint4 *>(kr + s * 8);
-                kf[kt][s] = ok ? x : zero4;
-            }
+            for (int s = 0; s < 4; ++s) kf[kt][s] = *reinterpret_cast<const uint4 *>(kr + s * 32);
         }
     };
     auto load_v = [&](const Item &it, uint4 (&vr)[2][8]) {
-        const uint16_t *vb = item_base(v, it);
+        const uint16_t *vb = item_base(bf.v, it);
         const int nv = wave_valid(it);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int kk = s2 * 32 + g4 * 8 + e;
-                const bool ok = kk < nv;
-                const uint4 x = *reinterpret_cast<const uint4 *>(vb + (ok ? wave * kKeysPerWave + kk : 0) * rs + c16 * 8);
-                vr[s2][e] = ok ? x : zero4;
+                vr[s2][e] = *reinterpret_cast<const uint4 *>(vb + (kk < nv ? wave * kKeysPerWave + kk : 0) * rs + c16 * 8);
             }
     };
-    // q rows of M tile mt as the MFMA A operand: row c16 of the tile, d in [32 g4 + 8 s, +8)
+    // q rows of M tile mt as the MFMA A operand: row c16 of the tile, d in [32 s + 8 g4, +8)
     auto load_q = [&](const Item &it, int mt, uint4 (&qf)[4]) {
         const int ra = mt * 16 + c16;
-        const bool ok = ra < R;
+        const bool ok = ra < R;                                          // padding rows read row 0
         const int ja = ok ? ra / sh.G : 0, ia = ok ? ra - ja * sh.G : 0;
-        const uint16_t *qb = q + ((int64_t)it.b * sh.Q * sh.Hq + (int64_t)it.hk * sh.G) * kHeadDim;
-        const uint16_t *qr = qb + (ja * sh.Hq + ia) * kHeadDim + g4 * 32;
+        const uint16_t *qb = bf.q + ((int64_t)it.b * sh.Q * sh.Hq + (int64_t)it.hk * sh.G) * kHeadDim;
+        const uint16_t *qr = qb + (ja * sh.Hq + ia) * kHeadDim + g4 * 8;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const uint4 x = *reinterpret_cast<const uint4 *>(qr + s * 8);
-            qf[s] = ok ? x : zero4;
-        }
+        for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const uint4 *>(qr + s * 32);
     };
 
     uint4 kf[4][4], vr[2][8], qf[4];
-    for (int64_t t = next_id(blockIdx.x); t < nid; t = next_id(t + gridDim.x)) {
+    int64_t t = next_id(blockIdx.x);
+    if (t < nid) {
+        const Item it = decode(t);
+        load_q(it, MG ? it.mg * sh.mgt : 0, qf);
+        load_k(it, kf);
+        load_v(it, vr);
+    }
+    while (t < nid) {
         const Item it = decode(t);
         const int key0 = it.c * kChunk;
         const int wkey0 = key0 + wave * kKeysPerWave;
-        const int mt0 = MG ? it.mg * sh.mgt : 0, mt1 = MG ? min(ntm, mt0 + sh.mgt) : ntm;
-        load_q(it, mt0, qf);
-        load_k(it, kf);
-        load_v(it, vr);
-        transpose8x8_b16(vr[0]);                       // this item's V as the P . V B operand
-        transpose8x8_b16(vr[1]);
+        int r0, r1;
+        group_rows(it, r0, r1);
+        const int mt0 = r0 / 16, mt1 = (r1 + 15) / 16;
+        const int64_t tn = next_id(t + gridDim.x);
+        bool prefetched = false;                       // the next item's K and q are requested
+        bool vready = false;                           // this item's V is in P . V operand form
 
-        for (int mt = mt0; mt < mt1; ++mt) {
+        // One 16-row query tile against this chunk.  The first tile runs on
+        // the q rows requested with the item; later tiles (verify blocks and
+        // prompts of more than 16 rows per head) request theirs first.  The
+        // first call is separate from the loop so that the waits of the
+        // common one-tile case count only the loads that precede its q.
+        auto run_tile = [&](const int mt) {
             // Rows of the accumulator layout held by this lane: 4 g4 + i.
             int lastk[4];
             bool rowok[4];
@@ -245,25 +291,30 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
             // Tile-uniform skip: no row of this tile reaches this chunk.
             const int rlast = mt * 16 + 15 < R ? mt * 16 + 15 : R - 1;
             const bool any = last_key(it.kvlen, rlast / sh.G) >= key0;
-            if (mt > mt0) load_q(it, mt, qf);
+            if (!any) return;
 
             // scores: tile kt -> lane (g4, c16) reg i = row 4 g4 + i, key wkey0 + 16 kt + c16
             float sc[4][4];
-            if (any) {
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < 4; ++kt) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) acc = mfma16<S>(qf[s], kf[kt][s], acc);
-                    const int key = wkey0 + kt * 16 + c16;
+                for (int s = 0; s < 4; ++s) acc = mfma16<S>(qf[s], kf[kt][s], acc);
+                const int key = wkey0 + kt * 16 + c16;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool vis = rowok[i] && key <= lastk[i];
-                        sc[kt][i] = vis ? acc[i] * sh.scale : -INFINITY;
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const bool vis = rowok[i] && key <= lastk[i];
+                    sc[kt][i] = vis ? acc[i] * sh.scale : -INFINITY;
                 }
             }
-            if (!any) continue;
+            // the next item's K and first q tile: requested once the last tile
+            // has read this item's
+            if (mt == mt1 - 1 && tn < nid) {
+                const Item nx = decode(tn);
+                load_k(nx, kf);
+                load_q(nx, MG ? nx.mg * sh.mgt : 0, qf);
+                prefetched = true;
+            }
 
             // chunk max per row
             float mx[4];
@@ -284,7 +335,7 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
                 const int rr = g4 * 4 + i;
                 mx[i] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
             }
-            // probabilities, row sums, and the bf16 P tile
+            // probabilities, row sums, and the P tile as hi and lo 16-bit parts
             float ls[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) ls[i] = 0.0f;
@@ -295,7 +346,9 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
                     const bool vis = sc[kt][i] != -INFINITY;
                     const float pv = vis ? expf(sc[kt][i] - mx[i]) : 0.0f;
                     ls[i] = ls[i] + pv;
-                    pl[wave][g4 * 4 + i][kt * 16 + c16] = S::narrow(pv);
+                    const uint16_t hi = S::narrow(pv);
+                    phi[wave][g4 * 4 + i][kt * 16 + c16] = hi;
+                    plo[wave][g4 * 4 + i][kt * 16 + c16] = S::narrow(pv - S::widen(hi));
                 }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -309,15 +362,33 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
                 for (int i = 0; i < 4; ++i) xl[wave][g4 * 4 + i] = ls[i];
             }
             __syncthreads();
-            // o partial of this wave: P (16 x 64) . V (64 x 128)
-            uint4 pf[2];
+            // this item's V as the P . V B operand (its loads had the scores
+            // and the softmax to arrive)
+            if (!vready) {
+                const int nv = wave_valid(it);
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) pf[s2] = *reinterpret_cast<const uint4 *>(&pl[wave][c16][s2 * 32 + g4 * 8]);
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (s2 * 32 + g4 * 8 + e >= nv) vr[s2][e] = zero4;   // p is 0 there; keep 0 * v exact
+                transpose8x8_b16(vr[0]);
+                transpose8x8_b16(vr[1]);
+                vready = true;
+            }
+            // o partial of this wave: P (16 x 64) . V (64 x 128), lo parts first
+            uint4 ph[2], pq[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                ph[s2] = *reinterpret_cast<const uint4 *>(&phi[wave][c16][s2 * 32 + g4 * 8]);
+                pq[s2] = *reinterpret_cast<const uint4 *>(&plo[wave][c16][s2 * 32 + g4 * 8]);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(pf[s2], vr[s2][j], acc);
+                for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(pq[s2], vr[s2][j], acc);
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(ph[s2], vr[s2][j], acc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ol[wave][g4 * 4 + i][c16 * 8 + j] = acc[i];
             }
@@ -331,7 +402,7 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
                     const int j = r / sh.G;
                     if (last_key(it.kvlen, j) >= key0) {
                         const int64_t h = (int64_t)it.hk * sh.G + (r - j * sh.G);
-                        float *dst = part + ((((int64_t)it.b * sh.Q + j) * sh.Hq + h) * sh.nchunks + it.c) * kPartStride;
+                        float *dst = bf.part + ((((int64_t)it.b * sh.Q + j) * sh.Hq + h) * sh.nchunks + it.c) * kPartStride;
 #pragma unroll
                         for (int half = 0; half < 2; ++half) {
                             const int d = dg * 8 + half * 4;
@@ -354,63 +425,147 @@ void attn_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restric
                 }
             }
             __syncthreads();
+        };
+        run_tile(mt0);
+        for (int mt = mt0 + 1; mt < mt1; ++mt) {
+            load_q(it, mt, qf);
+            run_tile(mt);
         }
+        // The group's last row, in the last tile, sees key0 (the item has
+        // work), so the last tile is never skipped and the next item's K and q
+        // are already in flight; this is the fallback should it ever be.
+        if (!prefetched && tn < nid) {
+            const Item nx = decode(tn);
+            load_k(nx, kf);
+            load_q(nx, MG ? nx.mg * sh.mgt : 0, qf);
+        }
+        // the next item's V (its K and q are in flight since this item's scores)
+        if (tn < nid) load_v(decode(tn), vr);
+        t = tn;
     }
 }
 
-// Pass 2: one workgroup of kHeadDim threads per query row (b, j, h).
-template <typename S>
-__global__ __launch_bounds__(kHeadDim)
-void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict__ kv_len,
-                       uint16_t *__restrict__ out, AttnShape sh, int64_t chunk_size)
-{
-    extern __shared__ float smem[];
-    const int64_t row = blockIdx.x;                       // (b * Q + j) * Hq + h
-    const int64_t j = (row / sh.Hq) % sh.Q, b = row / (sh.Hq * sh.Q);
-    const int d = threadIdx.x;
-    const int64_t kvlen = min((int64_t)kv_len[b], sh.max_kv);
-    const int64_t lastkey = row_last_key(kvlen, sh.Q, j, sh.causal);
-    const int64_t last = lastkey < 0 ? 0 : lastkey / chunk_size;     // a bad kv_len gives garbage, never an out-of-range read
-    const float *pr = part + row * sh.nchunks * kPartStride;
-    float *wts = smem;                                    // [nchunks]
-    float *lws = smem + sh.nchunks;                       // [nchunks]
-    __shared__ float red[kHeadDim / kWave];
-    // the first kMergeEarly chunks' o values do not depend on the max: request
-    // them now, with the m values, rather than after the weights are known
-    constexpr int kMergeEarly = 8;
-    float oe[kMergeEarly];
-#pragma unroll
-    for (int cc = 0; cc < kMergeEarly; ++cc) oe[cc] = cc <= last ? pr[cc * kPartStride + d] : 0.0f;
+// Range and row levels for one query row (b, j, h) per workgroup of
+// 32 * kMergeRanges threads: thread (r', quad) handles range r' of the current
+// batch of kMergeRanges ranges and d in [4 quad, +4).
+//   1. Range r: M_r = max m_c, o_r = sum o_c exp(m_c - M_r), l_r likewise, c
+//      ascending within the range.
+//   2. M = max over the row's chunk maxima (exact, any order: from the M_r
+//      when the ranges fit one batch, else read beforehand); range r's term
+//      o_r exp(M_r - M) goes to LDS.
+//   3. The 32 threads of range slot 0 add the batch's terms in ascending r to
+//      the running sums; batches follow in ascending order.
+// All of a range's chunk partials are requested at once, so a row costs about
+// two memory round trips whatever its length.
+constexpr int kMergeRanges = 32;     // ranges per batch (threads = 32 per range): 131072 keys
 
-    float m = -INFINITY;
-    for (int64_t cc = d; cc <= last; cc += kHeadDim) m = fmaxf(m, pr[cc * kPartStride + kHeadDim]);
+template <typename S>
+__global__ __launch_bounds__(32 * kMergeRanges)
+void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict__ kv_len,
+                       uint16_t *__restrict__ out, AttnShape sh)
+{
+    __shared__ __attribute__((aligned(16))) float term[kMergeRanges][kHeadDim + 4];
+    __shared__ float red[32 * kMergeRanges / kWave], rmax[kMergeRanges];
+    const int64_t row = blockIdx.x;                       // (b * Q + j) * Hq + h
+    const int j = (int)((row / sh.Hq) % sh.Q);
+    const int64_t b = row / (sh.Hq * sh.Q);
+    const int kvlen = (int)min((int64_t)kv_len[b], sh.max_kv);
+    const int lk = attn_last_key(kvlen, (int)sh.Q, j, sh.causal);
+    const int nthr = blockDim.x, slots = nthr / 32;
+    const int quad = threadIdx.x & 31, slot = threadIdx.x >> 5;
+    if (lk < 0) return;                                   // a bad kv_len: nothing this row may read
+    const int nch = lk / kChunk + 1, nr = (nch + kRange - 1) / kRange;
+    const float *pr = part + row * sh.nchunks * kPartStride;
+
+    // M = max over the chunk maxima: read first when the row's ranges take
+    // several batches, else taken from the range maxima below (the same value:
+    // a max is exact)
+    const bool one_batch = nr <= slots;
+    float M = -INFINITY;
+    if (!one_batch) {
+        for (int c = threadIdx.x; c < nch; c += nthr) M = fmaxf(M, pr[c * kPartStride + kHeadDim]);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    if ((d & 63) == 0) red[d >> 6] = m;
-    __syncthreads();
-    m = red[0];
-#pragma unroll
-    for (int i = 1; i < kHeadDim / kWave; ++i) m = fmaxf(m, red[i]);
-    for (int64_t cc = d; cc <= last; cc += kHeadDim) {
-        const float wv = expf(pr[cc * kPartStride + kHeadDim] - m);
-        wts[cc] = wv;
-        lws[cc] = pr[cc * kPartStride + kHeadDim + 1] * wv;
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
+        __syncthreads();
+        M = red[0];
+        for (int w = 1; w < nthr / kWave; ++w) M = fmaxf(M, red[w]);
     }
-    __syncthreads();
-    float o = 0.0f, l = 0.0f;
+
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.0f;
+    for (int r0 = 0; r0 < nr; r0 += slots) {
+        const int r = r0 + slot;
+        float Mr = -INFINITY, lr = 0.0f;
+        float4 orr = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < nr) {
+            const int c0 = r * kRange, n = min(nch - c0, kRange);
+            float mv[kRange], lv[kRange];
+            float4 ov[kRange];
 #pragma unroll
-    for (int cc = 0; cc < kMergeEarly; ++cc) {
-        if (cc <= last) {
-            o = o + oe[cc] * wts[cc];
-            l = l + lws[cc];
+            for (int i = 0; i < kRange; ++i) {
+                const float *pc = pr + (c0 + min(i, n - 1)) * kPartStride;   // stays on written partials
+                mv[i] = pc[kHeadDim];
+                lv[i] = pc[kHeadDim + 1];
+                ov[i] = *reinterpret_cast<const float4 *>(pc + quad * 4);
+            }
+            Mr = mv[0];
+#pragma unroll
+            for (int i = 1; i < kRange; ++i)
+                if (i < n) Mr = fmaxf(Mr, mv[i]);
+            float w = expf(mv[0] - Mr);
+            orr = make_float4(ov[0].x * w, ov[0].y * w, ov[0].z * w, ov[0].w * w);
+            lr = lv[0] * w;
+#pragma unroll
+            for (int i = 1; i < kRange; ++i) {
+                if (i < n) {
+                    w = expf(mv[i] - Mr);
+                    orr.x = orr.x + ov[i].x * w;
+                    orr.y = orr.y + ov[i].y * w;
+                    orr.z = orr.z + ov[i].z * w;
+                    orr.w = orr.w + ov[i].w * w;
+                    lr = lr + lv[i] * w;
+                }
+            }
         }
+        if (one_batch) {
+            if (quad == 0) rmax[slot] = Mr;
+            __syncthreads();
+            M = rmax[0];
+            for (int i = 1; i < nr; ++i) M = fmaxf(M, rmax[i]);
+        }
+        if (r < nr) {
+            const float u = expf(Mr - M);
+            *reinterpret_cast<float4 *>(&term[slot][quad * 4]) =
+                make_float4(orr.x * u, orr.y * u, orr.z * u, orr.w * u);
+            if (quad == 0) term[slot][kHeadDim] = lr * u;
+        }
+        __syncthreads();
+        if (slot == 0) {
+            const int nb = min(slots, nr - r0);
+            for (int i = 0; i < nb; ++i) {
+                const float4 tv = *reinterpret_cast<const float4 *>(&term[i][quad * 4]);
+                const float tl = term[i][kHeadDim];
+                if (r0 + i == 0) {
+                    o = tv;
+                    l = tl;
+                } else {
+                    o.x = o.x + tv.x;
+                    o.y = o.y + tv.y;
+                    o.z = o.z + tv.z;
+                    o.w = o.w + tv.w;
+                    l = l + tl;
+                }
+            }
+        }
+        __syncthreads();
     }
-#pragma unroll 8
-    for (int64_t cc = kMergeEarly; cc <= last; ++cc) {
-        o = o + pr[cc * kPartStride + d] * wts[cc];
-        l = l + lws[cc];
+    if (slot == 0) {
+        uint2 pk;
+        pk.x = (uint32_t)S::narrow(o.x / l) | ((uint32_t)S::narrow(o.y / l) << 16);
+        pk.y = (uint32_t)S::narrow(o.z / l) | ((uint32_t)S::narrow(o.w / l) << 16);
+        *reinterpret_cast<uint2 *>(out + row * kHeadDim + quad * 4) = pk;
     }
-    out[row * kHeadDim + d] = S::narrow(o / l);
 }
 
 static bi_status check_attn(const void *q, const void *k, const void *v, const void *o, const int32_t *kv_len,
@@ -421,7 +576,7 @@ static bi_status check_attn(const void *q, const void *k, const void *v, const v
     if (B < 1 || Q < 1 || Lcap < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
     if (max_kv_len < Q || max_kv_len > Lcap || max_kv_len > kMaxKv) return BI_ERR_SHAPE;
     if (Hkv > 65535 || B * Q * Hq > (1ll << 31) - 1 || Q * (Hq / Hkv) > (1ll << 30) ||
-        cdiv(B * cdiv(max_kv_len, kChunk), 8) * 8 * Hkv > (1ll << 31) - 1)
+        cdiv(B * cdiv(max_kv_len, kChunk), 8) * 8 * Hkv > (1ll << 31) - 1 || B * Lcap * Hkv * (int64_t)D > (1ll << 40))
         return BI_ERR_SHAPE;
     if (D != kHeadDim) return BI_ERR_UNSUPPORTED;
     if (dtype != BI_BF16 && dtype != BI_F16) return BI_ERR_DTYPE;
@@ -431,23 +586,77 @@ static bi_status check_attn(const void *q, const void *k, const void *v, const v
     return BI_OK;
 }
 
-template <typename S>
-static void launch_attn(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len, float *part,
-                        const AttnShape &sh, int64_t chunk, hipStream_t st)
+// Workspace: the chunk partials, fp32 [B*Q*Hq][nchunks][kPartStride].
+static size_t attn_partial_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Hq)
 {
+    return (size_t)(B * Q * Hq) * (size_t)cdiv(max_kv_len, kChunk) * kPartStride * sizeof(float);
+}
+
+struct AttnPlan {
+    AttnShape sh;
+    int64_t nid, grid, merge_threads;
+    size_t parts;
+};
+
+static AttnPlan attn_plan(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Lcap, int32_t Hq, int32_t Hkv,
+                          float scale, int32_t causal, int32_t kv_layout)
+{
+    const int64_t D = kHeadDim;
+    // kv_layout 0: [B, Lcap, Hkv, D]; 1: [B, Hkv, Lcap, D] (head-major)
+    const int64_t ks = kv_layout ? D : (int64_t)Hkv * D, hs = kv_layout ? Lcap * D : D;
+    // query-row groups: when the (sequence, chunk, head) items alone give fewer
+    // than two per workgroup slot, split the rows so that about 4096 ids exist
+    // (half of a causal prompt's (chunk, rows) pairs being empty), never under
+    // kAttnMinTiles tiles each; otherwise one group
+    const int64_t G = Hq / Hkv;
+    const int64_t ntm = cdiv(Q * G, 16), nbase = cdiv(B * cdiv(max_kv_len, kChunk), 8) * 8 * Hkv;
+    const int64_t ngroups = nbase >= 1024 ? 1 : std::max<int64_t>(1, cdiv(4096, nbase));
+    const int64_t mgt = std::min<int64_t>(std::max<int64_t>(kAttnMinTiles, cdiv(ntm, ngroups)), ntm);
+    const int64_t nch = cdiv(max_kv_len, kChunk);
+    AttnPlan p;
+    p.sh = AttnShape{B, Q, Lcap, nch, cdiv(nch, kRange), max_kv_len, cdiv(ntm, mgt), Hq, Hkv, (int)G, (int)mgt,
+                     scale, causal ? 1 : 0, ks, hs};
     // item ids (padded to whole groups of 8); a persistent grid of two
     // workgroups per CU, a multiple of 8 so that a workgroup stays on one XCD
-    const int64_t nid = cdiv(sh.B * sh.nchunks, 8) * 8 * sh.Hkv * sh.nmg;
-    const int64_t grid = std::min<int64_t>(nid, (int64_t)device_cu_count() * 2 / 8 * 8);
-    if (sh.nmg > 1)
-        launch_kernel((attn_chunk_kernel<S, true>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st,
-                      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, part, sh, nid);
+    p.nid = cdiv(B * nch, 8) * 8 * Hkv * p.sh.nmg;
+    p.grid = std::min<int64_t>(p.nid, (int64_t)device_cu_count() * 2 / 8 * 8);
+    // merge: 32 threads per range of the longest row, whole waves, at most kMergeRanges ranges at once
+    p.merge_threads = cdiv(32 * std::min<int64_t>(p.sh.nranges, kMergeRanges), kWave) * kWave;
+    p.parts = attn_partial_bytes(B, Q, max_kv_len, Hq);
+    return p;
+}
+
+template <typename S>
+static void launch_attn(const AttnBufs &bf, const AttnPlan &p, hipStream_t st)
+{
+    if (p.sh.nmg > 1)
+        launch_kernel((attn_kernel<S, true>), dim3((unsigned)p.grid), dim3(kAttnWaves * kWave), 0, st, bf, bf.kv_len,
+                      p.sh, p.nid);
     else
-        launch_kernel((attn_chunk_kernel<S, false>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st,
-                      (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, part, sh, nid);
-    const size_t smem = (size_t)sh.nchunks * 2 * sizeof(float);
-    launch_kernel((attn_merge_kernel<S>), dim3((unsigned)(sh.B * sh.Q * sh.Hq)), dim3(kHeadDim), smem, st,
-                       (const float *)part, kv_len, (uint16_t *)o, sh, chunk);
+        launch_kernel((attn_kernel<S, false>), dim3((unsigned)p.grid), dim3(kAttnWaves * kWave), 0, st, bf, bf.kv_len,
+                      p.sh, p.nid);
+    launch_kernel((attn_merge_kernel<S>), dim3((unsigned)(p.sh.B * p.sh.Q * p.sh.Hq)), dim3((unsigned)p.merge_threads),
+                  0, st, (const float *)bf.part, bf.kv_len, bf.o, p.sh);
+}
+
+// Shared by the entry points: validation, the launch plan, the launches.
+static bi_status attn_run(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len,
+                          int64_t max_kv_len, int64_t B, int64_t Q, int64_t Lcap, int32_t Hq, int32_t Hkv, int32_t D,
+                          float scale, int32_t causal, int32_t dtype, int32_t kv_layout, void *ws, size_t ws_bytes,
+                          hipStream_t stream)
+{
+    bi_status s = check_attn(q, k, v, o, kv_len, max_kv_len, B, Q, Lcap, Hq, Hkv, D, dtype);
+    if (s != BI_OK) return s;
+    if (kv_layout != 0 && kv_layout != 1) return BI_ERR_SHAPE;
+    if (!ws) return BI_ERR_WORKSPACE;
+    if (!host_aligned16(ws)) return BI_ERR_ALIGN;
+    const AttnPlan p = attn_plan(B, Q, max_kv_len, Lcap, Hq, Hkv, scale, causal, kv_layout);
+    if (ws_bytes < p.parts) return BI_ERR_WORKSPACE;
+    AttnBufs bf{(const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, (uint16_t *)o, (float *)ws};
+    (void)hipGetLastError();
+    if (dtype == BI_BF16) launch_attn<BF16>(bf, p, stream);
+    else launch_attn<F16>(bf, p, stream);
+    return launch_status();
 }
 
 }  // namespace bi
@@ -457,7 +666,7 @@ using namespace bi;
 extern "C" size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int32_t Hq, int32_t D)
 {
     if (B < 1 || Q < 1 || max_kv_len < 1 || Hq < 1 || D != kHeadDim) return 0;
-    return (size_t)B * Q * Hq * cdiv(max_kv_len, kChunk) * kPartStride * sizeof(float);
+    return attn_partial_bytes(B, Q, max_kv_len, Hq);
 }
 
 extern "C" bi_status bi_sdpa(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len,
@@ -465,25 +674,6 @@ extern "C" bi_status bi_sdpa(const void *q, const void *k, const void *v, void *
                              int32_t D, float scale, int32_t causal, int32_t dtype, int32_t kv_layout, void *ws,
                              size_t ws_bytes, hipStream_t stream)
 {
-    bi_status s = check_attn(q, k, v, o, kv_len, max_kv_len, B, Q, Lcap, Hq, Hkv, D, dtype);
-    if (s != BI_OK) return s;
-    if (kv_layout != 0 && kv_layout != 1) return BI_ERR_SHAPE;
-    if (!ws) return BI_ERR_WORKSPACE;
-    if (!host_aligned16(ws)) return BI_ERR_ALIGN;
-    if (ws_bytes < bi_sdpa_workspace_bytes(B, Q, max_kv_len, Hq, D)) return BI_ERR_WORKSPACE;
-    // kv_layout 0: [B, Lcap, Hkv, D]; 1: [B, Hkv, Lcap, D] (head-major)
-    const int64_t ks = kv_layout ? (int64_t)D : (int64_t)Hkv * D, hs = kv_layout ? Lcap * D : (int64_t)D;
-    // query-row groups: when the (sequence, chunk, head) items alone give fewer
-    // than two per workgroup slot, split the rows so that about 4096 ids exist
-    // (half of a causal prompt's (chunk, rows) pairs being empty), never under
-    // kAttnMinTiles tiles each; otherwise one group
-    const int64_t ntm = cdiv(Q * (Hq / Hkv), 16), nbase = cdiv(B * cdiv(max_kv_len, kChunk), 8) * 8 * Hkv;
-    const int64_t ngroups = nbase >= 1024 ? 1 : std::max<int64_t>(1, cdiv(4096, nbase));
-    const int64_t mgt = std::max<int64_t>(kAttnMinTiles, cdiv(ntm, ngroups));
-    AttnShape sh{B, Q, Lcap, cdiv(max_kv_len, kChunk), max_kv_len, cdiv(ntm, mgt), Hq, Hkv, Hq / Hkv, (int)std::min<int64_t>(mgt, ntm),
-                 scale, causal ? 1 : 0, ks, hs};
-    (void)hipGetLastError();
-    if (dtype == BI_BF16) launch_attn<BF16>(q, k, v, o, kv_len, (float *)ws, sh, kChunk, stream);
-    else launch_attn<F16>(q, k, v, o, kv_len, (float *)ws, sh, kChunk, stream);
-    return launch_status();
+    return attn_run(q, k, v, o, kv_len, max_kv_len, B, Q, Lcap, Hq, Hkv, D, scale, causal, dtype, kv_layout, ws,
+                    ws_bytes, stream);
 }

@@ -209,6 +209,24 @@ class Decoder:
             out[:, t] = self.next_ids[:B].cpu().numpy()
         return out
 
+    def teacher_forced(self, prompts: torch.Tensor, cont: np.ndarray, on_logits):
+        """Score a fixed continuation: prefill the prompts [B, P], then feed
+        cont [B, S] one token per step through the decode path (Q = 1, reading
+        the growing cache), as greedy decoding would feed its own tokens.
+        on_logits(p, logits [B, V]) sees the logits at every position p =
+        0 .. P + S - 1 (the prefill's rows first)."""
+        B, P = prompts.shape
+        S = cont.shape[1]
+        assert P + S <= self.max_len
+        self.prefill(prompts)
+        lg = self.logits[:B * P].view(B, P, self.V)
+        for p in range(P):
+            on_logits(p, lg[:, p])
+        for t in range(S):
+            self.ids[:B].copy_(torch.from_numpy(np.ascontiguousarray(cont[:, t], np.int32)).to(self.dev))
+            self.kv_len[:B].fill_(P + t + 1)
+            on_logits(P + t, self.forward(B, 1, P + t + 1))
+
     def generate_speculative(self, prompts: torch.Tensor, steps: int, draft, draft_len: int = 4, on_logits=None):
         """Greedy speculative decoding: each round verifies the last committed
         token plus `draft_len` drafted tokens in one causal block (Q =

@@ -45,7 +45,7 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(_LIB):
         return _LIB
     tmp = _LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+    cmd = ["gcc", "-O3", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
            "-shared", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
@@ -76,11 +76,14 @@ def lib():
         L.bo_fold_pairwise_f32.argtypes = [P, I64]; L.bo_fold_pairwise_f32.restype = ctypes.c_float
         L.bo_fold_split_f32.argtypes = [P, I64, I64]; L.bo_fold_split_f32.restype = ctypes.c_float
         L.bo_matmul.argtypes = [P, P, P, I64, I64, I64, I32, I32]
+        L.bo_matmul_desc.argtypes = [P, P, P, I64, I64, I64, I32, I32]
         L.bo_dequantize.argtypes = [P, P, P, P, I64, I64, I32, I32, I32]
         L.bo_qmatmul.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, I32, I32]
         L.bo_gather_qmatmul.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I32, I32, I32, I32]
         L.bo_rmsnorm.argtypes = [P, P, P, P, I64, I64, ctypes.c_float, I32]
+        L.bo_rmsnorm_desc.argtypes = [P, P, P, P, I64, I64, ctypes.c_float, I32]
         L.bo_sdpa.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, I32]
+        L.bo_sdpa_desc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, I32]
         L.bo_rope.argtypes = [P, P, P, P, P, I64, I64, I64, I32]
         L.bo_silu_mul.argtypes = [P, P, P, I64, I32]
         L.bo_argmax.argtypes = [P, P, I64, I64, I32]
@@ -165,14 +168,19 @@ def fold_split_f32(a, splits: int) -> float:
 
 # --- the four reductions -------------------------------------------------------
 
-def matmul(x: np.ndarray, w: np.ndarray, dtype, w_transposed: bool = True) -> np.ndarray:
-    """y = x @ W^T (W [N,K]) or x @ W (W [K,N]); fp32 [M,N]."""
+def matmul(x: np.ndarray, w: np.ndarray, dtype, w_transposed: bool = True, descending: bool = False) -> np.ndarray:
+    """y = x @ W^T (W [N,K]) or x @ W (W [K,N]); fp32 [M,N].  Each output is a
+    sequential fp32 fold over k ascending, or with descending=True over k
+    descending -- a second valid fixed tree (the "reverse" order of the
+    chapter's Case 4), used to measure how far two valid trees drift apart
+    through a composed model."""
     x = np.ascontiguousarray(x); w = np.ascontiguousarray(w)
     M, K = x.shape
     N = w.shape[0] if w_transposed else w.shape[1]
     assert (w.shape[1] if w_transposed else w.shape[0]) == K
     y = np.empty((M, N), np.float32)
-    _check(lib().bo_matmul(_p(x), _p(w), _p(y), M, N, K, _dt(dtype), int(w_transposed)), "matmul")
+    fn = lib().bo_matmul_desc if descending else lib().bo_matmul
+    _check(fn(_p(x), _p(w), _p(y), M, N, K, _dt(dtype), int(w_transposed)), "matmul")
     return y
 
 
@@ -219,24 +227,30 @@ def gather_qmatmul(x, lhs, rhs, wq, scales, biases, N: int, K: int, qmode: int, 
     return y
 
 
-def rmsnorm(x: np.ndarray, w: np.ndarray, dtype, eps: float = 1e-6, return_ss: bool = False):
+def rmsnorm(x: np.ndarray, w: np.ndarray, dtype, eps: float = 1e-6, return_ss: bool = False,
+            descending: bool = False):
+    """Sum of squares folded over i ascending (descending=True: the second
+    valid tree, Case 4's reverse order)."""
     x = np.ascontiguousarray(x); w = np.ascontiguousarray(w)
     rows, H = x.shape
     y = np.empty((rows, H), np.float32)
     ss = np.empty(rows, np.float32)
-    _check(lib().bo_rmsnorm(_p(x), _p(w), _p(y), _p(ss), rows, H, eps, _dt(dtype)), "rmsnorm")
+    fn = lib().bo_rmsnorm_desc if descending else lib().bo_rmsnorm
+    _check(fn(_p(x), _p(w), _p(y), _p(ss), rows, H, eps, _dt(dtype)), "rmsnorm")
     return (y, ss) if return_ss else y
 
 
-def sdpa(q, k, v, kv_len, scale: float, causal: bool, dtype) -> np.ndarray:
-    """q [B,Q,Hq,D]; k,v [B,Lcap,Hkv,D]; kv_len int32 [B] -> fp32 [B,Q,Hq,D]."""
+def sdpa(q, k, v, kv_len, scale: float, causal: bool, dtype, descending: bool = False) -> np.ndarray:
+    """q [B,Q,Hq,D]; k,v [B,Lcap,Hkv,D]; kv_len int32 [B] -> fp32 [B,Q,Hq,D].
+    Every sum ascending (descending=True: over d and over keys descending)."""
     q = np.ascontiguousarray(q); k = np.ascontiguousarray(k); v = np.ascontiguousarray(v)
     kv_len = np.ascontiguousarray(kv_len, dtype=np.int32)
     B, Q, Hq, D = q.shape
     _, Lcap, Hkv, _ = k.shape
     o = np.empty((B, Q, Hq, D), np.float32)
-    _check(lib().bo_sdpa(_p(q), _p(k), _p(v), _p(o), _p(kv_len), B, Q, Lcap, Hq, Hkv, D,
-                         scale, int(causal), _dt(dtype)), "sdpa")
+    fn = lib().bo_sdpa_desc if descending else lib().bo_sdpa
+    _check(fn(_p(q), _p(k), _p(v), _p(o), _p(kv_len), B, Q, Lcap, Hq, Hkv, D,
+              scale, int(causal), _dt(dtype)), "sdpa")
     return o
 
 

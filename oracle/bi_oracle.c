@@ -219,23 +219,24 @@ float bo_fold_split_f32(const float *a, int64_t n, int64_t splits)
 
 /* x: [M,K] of dtype; w: [N,K] when w_transposed else [K,N]; y: fp32 [M,N].
  * Each y[m,n] is the sequential fp32 fold over k = 0..K-1 of the rounded
- * product x*w.  Work is vectorised across n, which leaves every output's own
- * order untouched. */
-int bo_matmul(const void *x, const void *w, float *y, int64_t M, int64_t N, int64_t K,
-              int dtype, int w_transposed)
+ * product x*w (descending: k = K-1..0, the chapter's Case 4 "reverse" order,
+ * a second valid fixed tree).  Work is vectorised across n, which leaves every
+ * output's own order untouched. */
+static int matmul_fold(const void *x, const void *w, float *y, int64_t M, int64_t N, int64_t K,
+                       int dtype, int w_transposed, int descending)
 {
     if (!x || !w || !y || M < 0 || N < 0 || K < 0 || !valid_dtype(dtype)) return -1;
     if (M == 0 || N == 0) return 0;
     float *xf = (float *)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(float));
     if (!xf) return -2;
     for (int64_t i = 0; i < M * K; ++i) xf[i] = load_elem(x, i, dtype);
-    const int64_t NB = 256;
+    const int64_t NB = 256, MB = 8;
     const int64_t nblocks = (N + NB - 1) / NB;
     int err = 0;
 #pragma omp parallel
     {
         float *wt = (float *)malloc((size_t)(K > 0 ? K : 1) * NB * sizeof(float));
-        float *acc = (float *)malloc((size_t)NB * sizeof(float));
+        float *acc = (float *)malloc((size_t)(MB * NB) * sizeof(float));
         if (!wt || !acc) {
 #pragma omp atomic write
             err = -2;
@@ -247,15 +248,22 @@ int bo_matmul(const void *x, const void *w, float *y, int64_t M, int64_t N, int6
                     for (int64_t j = 0; j < nb; ++j)
                         wt[k * NB + j] = w_transposed ? load_elem(w, (n0 + j) * K + k, dtype)
                                                       : load_elem(w, k * N + (n0 + j), dtype);
-                for (int64_t m = 0; m < M; ++m) {
-                    for (int64_t j = 0; j < nb; ++j) acc[j] = 0.0f;
-                    const float *xr = xf + m * K;
-                    for (int64_t k = 0; k < K; ++k) {
-                        const float xv = xr[k];
+                /* Up to MB rows share one pass over the weight block; each
+                 * output still folds k = 0..K-1 in order in its own acc. */
+                for (int64_t m0 = 0; m0 < M; m0 += MB) {
+                    const int64_t mb = (M - m0 < MB) ? M - m0 : MB;
+                    for (int64_t i = 0; i < mb * NB; ++i) acc[i] = 0.0f;
+                    for (int64_t kk = 0; kk < K; ++kk) {
+                        const int64_t k = descending ? K - 1 - kk : kk;
                         const float *wr = wt + k * NB;
-                        for (int64_t j = 0; j < nb; ++j) acc[j] = acc[j] + xv * wr[j];
+                        for (int64_t i = 0; i < mb; ++i) {
+                            const float xv = xf[(m0 + i) * K + k];
+                            float *ai = acc + i * NB;
+                            for (int64_t j = 0; j < nb; ++j) ai[j] = ai[j] + xv * wr[j];
+                        }
                     }
-                    for (int64_t j = 0; j < nb; ++j) y[m * N + n0 + j] = acc[j];
+                    for (int64_t i = 0; i < mb; ++i)
+                        for (int64_t j = 0; j < nb; ++j) y[(m0 + i) * N + n0 + j] = acc[i * NB + j];
                 }
             }
         }
@@ -264,6 +272,18 @@ int bo_matmul(const void *x, const void *w, float *y, int64_t M, int64_t N, int6
     }
     free(xf);
     return err;
+}
+
+int bo_matmul(const void *x, const void *w, float *y, int64_t M, int64_t N, int64_t K,
+              int dtype, int w_transposed)
+{
+    return matmul_fold(x, w, y, M, N, K, dtype, w_transposed, 0);
+}
+
+int bo_matmul_desc(const void *x, const void *w, float *y, int64_t M, int64_t N, int64_t K,
+                   int dtype, int w_transposed)
+{
+    return matmul_fold(x, w, y, M, N, K, dtype, w_transposed, 1);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -415,15 +435,17 @@ int bo_gather_qmatmul(const uint16_t *x, const int32_t *lhs, const int32_t *rhs,
 /* ------------------------------------------------------------------------ */
 
 /* x [rows,H] and w [H] of dtype; y fp32 [rows,H]; ss (optional) fp32 [rows]
- * receives each row's sequential sum of squares. */
-int bo_rmsnorm(const void *x, const void *w, float *y, float *ss, int64_t rows, int64_t H,
-               float eps, int dtype)
+ * receives each row's sequential sum of squares (ascending i; descending: the
+ * chapter's Case 4 "reverse" order, a second valid fixed tree). */
+static int rmsnorm_fold(const void *x, const void *w, float *y, float *ss, int64_t rows, int64_t H,
+                        float eps, int dtype, int descending)
 {
     if (!x || !w || !y || rows < 0 || H < 1 || !valid_dtype(dtype)) return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         float s = 0.0f;
-        for (int64_t i = 0; i < H; ++i) {
+        for (int64_t ii = 0; ii < H; ++ii) {
+            const int64_t i = descending ? H - 1 - ii : ii;
             float v = load_elem(x, r * H + i, dtype);
             s = s + v * v;
         }
@@ -438,6 +460,18 @@ int bo_rmsnorm(const void *x, const void *w, float *y, float *ss, int64_t rows, 
     return 0;
 }
 
+int bo_rmsnorm(const void *x, const void *w, float *y, float *ss, int64_t rows, int64_t H,
+               float eps, int dtype)
+{
+    return rmsnorm_fold(x, w, y, ss, rows, H, eps, dtype, 0);
+}
+
+int bo_rmsnorm_desc(const void *x, const void *w, float *y, float *ss, int64_t rows, int64_t H,
+                    float eps, int dtype)
+{
+    return rmsnorm_fold(x, w, y, ss, rows, H, eps, dtype, 1);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Scaled dot-product attention for decode / verify blocks.                  */
 /* ------------------------------------------------------------------------ */
@@ -448,10 +482,11 @@ int bo_rmsnorm(const void *x, const void *w, float *y, float *ss, int64_t rows, 
  * reads key/value head h / (Hq / Hkv).
  * Plain two-pass softmax: s_t = (q . k_t) * scale (sequential over d),
  * m = max s, p_t = exp(s_t - m), l = sum p_t, o_d = (sum_t p_t * v_td) / l,
- * every sum sequential in ascending index. */
-int bo_sdpa(const void *q, const void *k, const void *v, float *o, const int32_t *kv_len,
-            int64_t B, int64_t Q, int64_t Lcap, int64_t Hq, int64_t Hkv, int64_t D,
-            float scale, int causal, int dtype)
+ * every sum sequential in ascending index (descending: every sum -- over d
+ * and over keys -- in descending index, a second valid fixed tree). */
+static int sdpa_fold(const void *q, const void *k, const void *v, float *o, const int32_t *kv_len,
+                     int64_t B, int64_t Q, int64_t Lcap, int64_t Hq, int64_t Hkv, int64_t D,
+                     float scale, int causal, int dtype, int descending)
 {
     if (!q || !k || !v || !o || !kv_len || B < 0 || Q < 1 || Lcap < 1 || Hq < 1 || Hkv < 1 || D < 1)
         return -1;
@@ -481,17 +516,19 @@ int bo_sdpa(const void *q, const void *k, const void *v, float *o, const int32_t
                 for (int64_t t = 0; t <= last; ++t) {
                     int64_t kb = ((b * Lcap + t) * Hkv + g) * D;
                     float dot = 0.0f;
-                    for (int64_t d = 0; d < D; ++d) dot = dot + qf[d] * load_elem(k, kb + d, dtype);
+                    for (int64_t dd = 0; dd < D; ++dd) {
+                        const int64_t d = descending ? D - 1 - dd : dd;
+                        dot = dot + qf[d] * load_elem(k, kb + d, dtype);
+                    }
                     sc[t] = dot * scale;
                     if (sc[t] > m) m = sc[t];
                 }
+                for (int64_t t = 0; t <= last; ++t) sc[t] = expf(sc[t] - m);
                 float l = 0.0f;
-                for (int64_t t = 0; t <= last; ++t) {
-                    sc[t] = expf(sc[t] - m);
-                    l = l + sc[t];
-                }
+                for (int64_t tt = 0; tt <= last; ++tt) l = l + sc[descending ? last - tt : tt];
                 for (int64_t d = 0; d < D; ++d) acc[d] = 0.0f;
-                for (int64_t t = 0; t <= last; ++t) {
+                for (int64_t tt = 0; tt <= last; ++tt) {
+                    const int64_t t = descending ? last - tt : tt;
                     int64_t vb = ((b * Lcap + t) * Hkv + g) * D;
                     for (int64_t d = 0; d < D; ++d) acc[d] = acc[d] + sc[t] * load_elem(v, vb + d, dtype);
                 }
@@ -503,6 +540,20 @@ int bo_sdpa(const void *q, const void *k, const void *v, float *o, const int32_t
         free(acc);
     }
     return err;
+}
+
+int bo_sdpa(const void *q, const void *k, const void *v, float *o, const int32_t *kv_len,
+            int64_t B, int64_t Q, int64_t Lcap, int64_t Hq, int64_t Hkv, int64_t D,
+            float scale, int causal, int dtype)
+{
+    return sdpa_fold(q, k, v, o, kv_len, B, Q, Lcap, Hq, Hkv, D, scale, causal, dtype, 0);
+}
+
+int bo_sdpa_desc(const void *q, const void *k, const void *v, float *o, const int32_t *kv_len,
+                 int64_t B, int64_t Q, int64_t Lcap, int64_t Hq, int64_t Hkv, int64_t D,
+                 float scale, int causal, int dtype)
+{
+    return sdpa_fold(q, k, v, o, kv_len, B, Q, Lcap, Hq, Hkv, D, scale, causal, dtype, 1);
 }
 
 /* ------------------------------------------------------------------------ */

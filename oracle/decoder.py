@@ -26,6 +26,9 @@ from __future__ import annotations
 import numpy as np
 
 from . import BF16, argmax, matmul, rmsnorm, rope, round_to, sdpa, silu_mul, widen
+from . import matmul as _matmul
+from . import rmsnorm as _rmsnorm
+from . import sdpa as _sdpa
 
 
 def _bf(a32: np.ndarray) -> np.ndarray:
@@ -37,11 +40,27 @@ def _add(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return _bf(widen(a, BF16) + widen(b, BF16))
 
 
-def forward(weights: dict, cfg: dict, tokens: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray):
+def forward(weights: dict, cfg: dict, tokens: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray,
+            descending: bool = False):
     """Teacher-forced forward of one sequence `tokens` [T] at positions 0..T-1.
-    Returns (logits fp32 [T, V], logits bf16 bits [T, V], greedy ids [T])."""
+    Returns (logits fp32 [T, V], logits bf16 bits [T, V], greedy ids [T]).
+    descending=True folds every reduction -- matmul over k, the RMSNorm sum of
+    squares, attention's dot products and its sums over keys -- in descending
+    order: a second valid fixed-order model, whose distance from the ascending
+    one measures how far two correct trees drift apart through the composed
+    layers."""
     H, Hq, Hkv, D, F = cfg["hidden"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["ffn"]
     eps = cfg["eps"]
+
+    def matmul(a, w, dt, tr):
+        return _matmul(a, w, dt, tr, descending=descending)
+
+    def rmsnorm(a, w, dt, e):
+        return _rmsnorm(a, w, dt, e, descending=descending)
+
+    def sdpa(q, k, v, kv, sc, causal, dt):
+        return _sdpa(q, k, v, kv, sc, causal, dt, descending=descending)
+
     tokens = np.asarray(tokens, np.int64)
     T = tokens.shape[0]
     pos = np.arange(T, dtype=np.int32)

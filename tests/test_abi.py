@@ -101,7 +101,7 @@ def test_rmsnorm_validation():
 def test_sdpa_validation_and_workspace_size():
     L = bi.lib()
     ws_need = L.bi_sdpa_workspace_bytes(1, 8, 65540, 32, 128)
-    assert ws_need == 1 * 8 * 32 * 257 * 132 * 4
+    assert ws_need == 1 * 8 * 32 * 257 * 132 * 4           # one fp32 partial per (query row, chunk)
     assert L.bi_sdpa_workspace_bytes(1, 8, 65540, 32, 64) == 0
     def call(**kw):
         a = dict(q=A, k=A, v=A, o=A, kv=A, maxkv=1028, B=1, Q=8, Lcap=2048, Hq=32, Hkv=8, D=128,

@@ -119,37 +119,68 @@ def test_speculative_equals_plain(model, prompts, plain64, B, mode):
         assert model.rounds <= (STEPS + 3) // 5 + 1          # every draft accepted: 5 tokens per round
 
 
-def test_logits_match_oracle_teacher_forced(weights):
-    """Short run (prompt 48, 12 steps, B = 1) against the oracle's forward over
-    the prompt plus the GPU's tokens.
+def test_logits_match_oracle_teacher_forced(weights, prompts):
+    """Config 5's 768 positions at B = 1 against the oracle: the 512-token
+    prompt, then 256 more tokens fed one per step through the decode path (a
+    seeded continuation, so no oracle input comes from the GPU; the decode
+    steps run exactly as in greedy decoding).
 
-    Gate: the 2e-2 bf16 tolerance bounds ONE op's output and is enforced per op
-    (the op tests, including the decoder's own projection shapes).  The logits
-    here sit about 47 bf16-rounded ops deep, and two valid fp32 trees drift
-    apart through them: the oracle with its sequential matmul fold and the same
-    oracle with BLAS matmuls differ by ~1.5e-2.  The composed logits are
-    therefore gated at 5e-2 (per position, max |g - o| / max |o|); greedy
-    tokens must agree wherever the oracle's top-2 margin clears the noise."""
-    Pp, S = 48, 12
-    m = Decoder(CFG, weights, max_batch=1, max_q=Pp, max_len=Pp + S + 8, device=dev())
-    pr = inputs.prompts(1, Pp, CFG["vocab"], seed=3)
-    got = []
-    toks = m.generate(torch.from_numpy(pr).to(dev()), S, on_logits=lambda i, lg: got.append(lg[0].float().cpu().numpy()))
-    seq = np.concatenate([pr[0], toks[0, :-1]])
-    cos_t, sin_t = inputs.rope_tables(Pp + S + 8, CFG["head_dim"])
+    Gate.  The 2e-2 bf16 tolerance bounds one op's output and every op is held
+    to it by its own tests.  The logits here sit ~47 bf16-rounded ops deep,
+    where the oracle itself is only defined up to the choice of fixed order:
+    the same oracle with every reduction folded descending instead of
+    ascending (tests/golden/decoder_tree_spread.json, written by
+    tests/golden/make_decoder_spread.py from oracle/ alone) differs from the
+    ascending one by up to 1.85e-2 per position (median 1.33e-2) on these
+    very inputs, and picks a different greedy token at 24 of the 768
+    positions ("Batch-invariant kernels", Case 5 and The trap: close is not
+    identical -- identity is checked GPU-vs-GPU above).  The GPU, a third
+    fixed order, must sit no further from the oracle than that spread allows:
+    every position within 1.25x the spread's maximum, the median within 1.25x
+    its median (1.25: the sampling noise of a maximum over 768 positions),
+    and at least 99% of positions within the per-op 2e-2.  Where the
+    oracle's top-2 margin exceeds 5e-2 of max |logit| (more than twice the
+    gate), the GPU's greedy token (its own argmax kernel on its own logits)
+    must be the oracle's: an error within the gate cannot reorder that pair."""
+    import json
+    import os
+    S = STEPS
+    with open(os.path.join(os.path.dirname(__file__), "golden", "decoder_tree_spread.json")) as f:
+        spread = json.load(f)
+    m = Decoder(CFG, weights, max_batch=1, max_q=P, max_len=P + S + 8, device=dev())
+    pr = prompts[:1]
+    cont = inputs.prompts(1, S, CFG["vocab"], seed=5)
+    got = np.zeros((P + S, CFG["vocab"]), np.float32)
+    gtok = np.zeros(P + S, np.int64)
+
+    def keep(p, lg):
+        got[p] = lg[0].float().cpu().numpy()
+        if p == 0:                                   # the prefill's argmax of every prompt position
+            gtok[:P] = m.next_ids[:P].cpu().numpy()
+        elif p >= P:
+            gtok[p] = int(m.next_ids[0].item())
+
+    m.teacher_forced(torch.from_numpy(pr).to(dev()), cont, keep)
+    seq = np.concatenate([pr[0], cont[0]])
+    cos_t, sin_t = inputs.rope_tables(P + S + 8, CFG["head_dim"])
     from oracle import decoder as odec
     ref32, _, ref_tok = odec.forward(weights, CFG, seq, cos_t, sin_t)
-    worst = 0.0
-    for i in range(S):
-        r = ref32[Pp - 1 + i].astype(np.float64)
-        g = got[i].astype(np.float64)
-        rel = np.abs(g - r).max() / np.abs(r).max()
-        worst = max(worst, rel)
-        assert rel <= 5e-2, (i, rel)
-        top = np.sort(r)[-2:]
-        if top[1] - top[0] > 0.1 * np.abs(r).max():
-            assert toks[0, i] == ref_tok[Pp - 1 + i], i
-    print(f"decoder logits vs oracle: worst per-position relative error {worst:.4f}")
+    r = ref32.astype(np.float64)
+    scale = np.abs(r).max(1)
+    rel = np.abs(got - r).max(1) / scale
+    top = np.sort(r, 1)[:, -2:]
+    decisive = (top[:, 1] - top[:, 0]) > 0.05 * scale
+    within = float(np.mean(rel <= 2e-2))
+    print(f"decoder logits vs oracle over {P + S} positions: worst {rel.max():.4e} at {int(rel.argmax())}, "
+          f"median {np.median(rel):.4e}, p99 {np.quantile(rel, 0.99):.4e}, within 2e-2 {within:.4f}; "
+          f"oracle tree spread max {spread['max']:.4e} median {spread['median']:.4e}; "
+          f"decisive positions {int(decisive.sum())}")
+    assert spread["positions"] == P + S
+    assert rel.max() <= 1.25 * spread["max"], (int(rel.argmax()), float(rel.max()))
+    assert np.median(rel) <= 1.25 * spread["median"], float(np.median(rel))
+    assert within >= 0.99, within
+    bad = np.nonzero(decisive & (gtok != ref_tok))[0]
+    assert bad.size == 0, bad[:10]
 
 
 @pytest.mark.parametrize("N,K", [(6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336), (32000, 4096)])

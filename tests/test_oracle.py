@@ -91,6 +91,22 @@ def test_case4_rmsnorm_printed_values():
     assert int(np.sum(y_f[0] != y_rev)) == g["output_differing"]
 
 
+def test_case4_sum_of_squares_through_matmul_both_orders():
+    """The matmul fold in ascending and in descending k order reproduces Case
+    4's printed forward and reverse sums of squares bit for bit (x . x over the
+    Case 4 row), pinning the descending tree the composed-model spread uses."""
+    g = golden("case4_rmsnorm.json")
+    row = np.array([2.0 ** -(i // 64) for i in range(4096)], np.float32)[None]
+    assert f"{oracle.matmul(row, row, 'f32')[0, 0]:.8e}" == g["sum_sq_forward"]
+    assert f"{oracle.matmul(row, row, 'f32', descending=True)[0, 0]:.8e}" == g["sum_sq_reverse"]
+    # and in general the descending fold is the ascending fold of the reversed k axis
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 257)).astype(np.float32)
+    w = rng.standard_normal((5, 257)).astype(np.float32)
+    want = oracle.matmul(np.ascontiguousarray(x[:, ::-1]), np.ascontiguousarray(w[:, ::-1]), "f32")
+    assert np.array_equal(oracle.matmul(x, w, "f32", descending=True), want)
+
+
 # ---------------------------------------------------------------------------
 # number formats
 # ---------------------------------------------------------------------------
