@@ -339,6 +339,27 @@ bi_status bi_sdpa(const void *q, const void *k, const void *v, void *o, const in
                   int32_t dtype, int32_t kv_layout, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * bi_sdpa without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, kernels and bits as bi_sdpa minus ws /
+ * ws_bytes: the chunk partials go to a fixed scratch array of
+ * bi_sdpa_noalloc_max_bytes() bytes (64 MiB) that the library holds on each
+ * GPU it runs on until the process ends.  A shape whose
+ * bi_sdpa_workspace_bytes exceeds that returns BI_ERR_WORKSPACE before
+ * anything is launched.  Nothing is allocated: the scratch address is looked
+ * up (hipGetSymbolAddress) once per device, on the first call made with that
+ * device current.  Every call on one GPU shares that GPU's scratch, so calls
+ * that overlap in time on one GPU (different streams, no ordering) race;
+ * stream-ordered calls are safe.  Errors: as bi_sdpa, plus BI_ERR_LAUNCH if
+ * the scratch address cannot be obtained.
+ * ------------------------------------------------------------------------ */
+size_t bi_sdpa_noalloc_max_bytes(void);
+bi_status bi_sdpa_noalloc(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len,
+                          int64_t max_kv_len, int64_t B, int64_t Q, int64_t Lcap,
+                          int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t causal,
+                          int32_t dtype, int32_t kv_layout, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Row log-softmax, token log-probabilities and row mean (the log-prob
  * outputs a sampler and an RL trainer must agree on bit for bit).
  * Source: "Batch-invariant kernels ...", The boring rule (item 1: one

@@ -20,7 +20,7 @@ __all__ = [
     "BIError", "library_path", "lib", "build_info",
     "matmul", "matmul_ws", "matmul_workspace", "matmul_swiglu", "matmul_swiglu_workspace", "interleave_gate_up",
     "PackedWeight", "pack_weights", "pack_qweights", "log_softmax", "token_logprob", "row_mean",
-    "qmatmul", "rmsnorm", "add_rmsnorm", "sdpa", "sdpa_workspace_bytes",
+    "qmatmul", "rmsnorm", "add_rmsnorm", "sdpa", "sdpa_workspace_bytes", "sdpa_noalloc",
     "matmul_split", "rmsnorm_split",
     "embed", "rope_kv_write", "silu_mul", "add", "argmax",
     "BF16", "F16", "F32", "AFFINE", "NVFP4",
@@ -65,6 +65,7 @@ def lib():
             "bi_rmsnorm": [P, P, P, I64, I64, F, I32, P],
             "bi_add_rmsnorm": [P, P, P, P, P, I64, I64, F, I32, P],
             "bi_sdpa": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, I32, P, SZ, P],
+            "bi_sdpa_noalloc": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, I32, P],
             "bi_embed": [P, P, P, I64, I64, I64, P],
             "bi_rope_kv_write": [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, I64, I32, P],
             "bi_silu_mul": [P, P, I64, I64, P],
@@ -87,6 +88,8 @@ def lib():
             fn.restype = ctypes.c_int32
         L.bi_sdpa_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
         L.bi_sdpa_workspace_bytes.restype = SZ
+        L.bi_sdpa_noalloc_max_bytes.argtypes = []
+        L.bi_sdpa_noalloc_max_bytes.restype = SZ
         L.bi_packed_qweight_bytes.argtypes = [I64, I64, I32, I32, I32]
         L.bi_packed_qweight_bytes.restype = SZ
         L.bi_packed_weight_bytes.argtypes = [I64, I64, I32]
@@ -381,6 +384,24 @@ def sdpa(q, k, v, kv_len, max_kv_len: int, scale: float, causal: bool = True, ou
     _check(lib().bi_sdpa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_len), max_kv_len, B, Q, Lcap, Hq, Hkv, D,
                          scale, int(causal), _dt(q), int(head_major), _ptr(ws), ws.numel() * ws.element_size(),
                          _stream(stream)), "bi_sdpa")
+    return o
+
+
+def sdpa_noalloc(q, k, v, kv_len, max_kv_len: int, scale: float, causal: bool = True, out=None, stream=None,
+                 head_major: bool = False):
+    """bi_sdpa on the library's fixed per-GPU scratch (no workspace, nothing
+    allocated by the call itself except `out` when it is not given)."""
+    _dev(q, k, v, kv_len, out)
+    B, Q, Hq, D = q.shape
+    if head_major:
+        _, Hkv, Lcap, _ = k.shape
+    else:
+        _, Lcap, Hkv, _ = k.shape
+    if kv_len.dtype != torch.int32:
+        raise ValueError("kv_len must be int32")
+    o = out if out is not None else torch.empty_like(q)
+    _check(lib().bi_sdpa_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_len), max_kv_len, B, Q, Lcap, Hq, Hkv,
+                                 D, scale, int(causal), _dt(q), int(head_major), _stream(stream)), "bi_sdpa_noalloc")
     return o
 
 

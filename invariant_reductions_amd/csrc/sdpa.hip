@@ -39,6 +39,7 @@
 // The chunk level is one launch (attn_kernel); the range and row levels are a
 // second (attn_merge_kernel), one workgroup per query row.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -659,6 +660,37 @@ static bi_status attn_run(const void *q, const void *k, const void *v, void *o, 
     return launch_status();
 }
 
+// ---------------------------------------------------------------------------
+// Fixed scratch for callers that cannot allocate (bi_sdpa_noalloc): the chunk
+// partials live in this file-scope device array, one copy per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the symbol); it passes the device
+// address hipGetSymbolAddress returned for the current device.
+constexpr size_t kAttnScratchBytes = 64ull << 20;
+__device__ __align__(256) char attn_scratch[kAttnScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void *g_attn_scratch[kMaxDevices];
+static std::mutex g_attn_scratch_mu;
+
+// The current device's scratch address, looked up once per device.
+static bi_status attn_scratch_ptr(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BI_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_attn_scratch_mu);
+    if (!g_attn_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(attn_scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return BI_ERR_LAUNCH;
+        }
+        g_attn_scratch[dev] = p;
+    }
+    *out = g_attn_scratch[dev];
+    return BI_OK;
+}
+
 }  // namespace bi
 
 using namespace bi;
@@ -676,4 +708,21 @@ extern "C" bi_status bi_sdpa(const void *q, const void *k, const void *v, void *
 {
     return attn_run(q, k, v, o, kv_len, max_kv_len, B, Q, Lcap, Hq, Hkv, D, scale, causal, dtype, kv_layout, ws,
                     ws_bytes, stream);
+}
+
+extern "C" size_t bi_sdpa_noalloc_max_bytes(void) { return kAttnScratchBytes; }
+
+extern "C" bi_status bi_sdpa_noalloc(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len,
+                                     int64_t max_kv_len, int64_t B, int64_t Q, int64_t Lcap, int32_t Hq, int32_t Hkv,
+                                     int32_t D, float scale, int32_t causal, int32_t dtype, int32_t kv_layout,
+                                     hipStream_t stream)
+{
+    bi_status s = check_attn(q, k, v, o, kv_len, max_kv_len, B, Q, Lcap, Hq, Hkv, D, dtype);
+    if (s != BI_OK) return s;
+    if (bi_sdpa_workspace_bytes(B, Q, max_kv_len, Hq, D) > kAttnScratchBytes) return BI_ERR_WORKSPACE;
+    void *ws = nullptr;
+    s = attn_scratch_ptr(&ws);
+    if (s != BI_OK) return s;
+    return attn_run(q, k, v, o, kv_len, max_kv_len, B, Q, Lcap, Hq, Hkv, D, scale, causal, dtype, kv_layout, ws,
+                    kAttnScratchBytes, stream);
 }
