@@ -464,6 +464,25 @@ bi_status bi_rmsnorm_split(const void *x, const void *w, void *y, int64_t rows, 
 bi_status bi_time_next_launch(hipEvent_t start, hipEvent_t stop);
 bi_status bi_time_next_launches(hipEvent_t start, hipEvent_t stop, int32_t count);
 
+/* ------------------------------------------------------------------------
+ * Measurement probes (not part of any computation): the rates this GPU
+ * sustains, against which the kernels above are also reported.
+ *   bi_probe_read : reads `bytes` (a multiple of 16) from src in 16-byte words
+ *                   with `workgroups` workgroups of 256 threads, grid-stride;
+ *                   writes 16 bytes per workgroup to sink (workgroups * 16
+ *                   bytes).  Bytes moved: `bytes`.
+ *   bi_probe_copy : copies `bytes` from src to dst (non-overlapping).  Bytes
+ *                   moved: 2 * `bytes`.
+ *   bi_probe_mfma : `workgroups` x 4 waves, each issuing iters x 8
+ *                   independent v_mfma_f32_16x16x32_bf16 on registers (16384
+ *                   flops each); sink: fp32 [workgroups * 256].
+ * src, dst and sink 16-byte aligned.  Errors: BI_ERR_NULL, BI_ERR_SHAPE,
+ * BI_ERR_ALIGN, BI_ERR_LAUNCH.
+ * ------------------------------------------------------------------------ */
+bi_status bi_probe_read(const void *src, size_t bytes, void *sink, int32_t workgroups, hipStream_t stream);
+bi_status bi_probe_copy(const void *src, void *dst, size_t bytes, int32_t workgroups, hipStream_t stream);
+bi_status bi_probe_mfma(void *sink, int32_t workgroups, int64_t iters, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Human-readable status name (static string, never NULL). */
 const char *bi_status_str(int32_t status);

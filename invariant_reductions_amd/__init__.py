@@ -81,6 +81,9 @@ def lib():
             "bi_token_logprob": [P, P, P, I64, I64, I32, P],
             "bi_row_mean": [P, P, I64, I64, I32, P],
             "bi_rmsnorm_split": [P, P, P, I64, I64, F, I32, I32, P, SZ, P],
+            "bi_probe_read": [P, SZ, P, I32, P],
+            "bi_probe_copy": [P, P, SZ, I32, P],
+            "bi_probe_mfma": [P, I32, I64, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)

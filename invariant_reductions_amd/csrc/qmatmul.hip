@@ -138,6 +138,20 @@ __device__ inline uint16_t deq1(uint32_t q, const QGroup<QM> &g)
 //           packed binary16 multiply by f; both steps exact (at most 6
 //           significant bits, |w| <= 2688, smallest magnitude 2^-10), so the
 //           result is e2m1 * scale exactly.
+// Byte p of v as fp32 (exact): one v_cvt_f32_ubyte<p>, which reads the byte in
+// place (the compiler would otherwise extract each byte first).
+__device__ inline float cvt_f32_ubyte(uint32_t v, int p)
+{
+    float f;
+    switch (p) {
+    case 0: asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v)); break;
+    case 1: asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v)); break;
+    case 2: asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v)); break;
+    default: asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v)); break;
+    }
+    return f;
+}
+
 template <int QM>
 __device__ inline uint4 deq_word(uint32_t w, const QGroup<QM> &g)
 {
@@ -146,7 +160,7 @@ __device__ inline uint4 deq_word(uint32_t w, const QGroup<QM> &g)
     if constexpr (QM == BI_AFFINE) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const float q0 = (float)((lo >> (8 * p)) & 0xffu), q1 = (float)((hi >> (8 * p)) & 0xffu);
+            const float q0 = cvt_f32_ubyte(lo, p), q1 = cvt_f32_ubyte(hi, p);
             const f32x2 v = f32x2{__builtin_fmaf(g.s, q0, g.b), __builtin_fmaf(g.s, q1, g.b)};
             out[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
         }
@@ -328,158 +342,199 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
     }
 }
 
-// Persistent streaming form of the same reduction for short M (at most 16
-// rows), transposed weights, K a multiple of the block and 16-byte aligned x
-// and wq.  A fixed grid walks the output tiles (16 rows x NS*16 columns) t =
-// blockIdx.x, blockIdx.x + gridDim.x, ...; each wave streams its (tile,
-// block) items -- packed words, group constants and x chunks -- through a
-// register ring of D items that runs across tile boundaries, and
-// dequantizes an item only when it multiplies it.  Per output the tree is
-// exactly qmatmul_kernel's: block b of K belongs to wave b mod 8, lane group
-// g supplies [32g, 32g + 32) of the block as four steps, wave partials are
-// added in wave order.
-template <int QM, int GS, int NS, int D, bool PK>
+// Streaming form for short M (at most 16 rows), the decode path, for the
+// tile-packed (PK) and the [N, K/8] layouts, K a multiple of the block: one
+// workgroup owns a contiguous run of output tiles (16 rows x NS*16 columns,
+// the same count for every workgroup) and each wave streams its (tile, block)
+// items -- NS code chunks and their group constants -- through a register
+// ring.  When a wave owns at most
+// kQXRes blocks of K, its x chunks are loaded once and kept in registers for
+// every tile (x does not depend on the tile).  Rows >= M multiply row M - 1's
+// x and are never stored (rows are independent inside an MFMA), so no load
+// is predicated.  The tree is qmatmul_kernel's: block b of K belongs to wave b
+// mod 8, lane group g supplies [32g, 32g + 32) of the block as four steps,
+// wave partials are added in wave order.
+constexpr int kQXRes = 4;
+
+template <int QM, int GS, int NS, int D, bool XR, bool PK>
 __global__ __launch_bounds__(kQWaves * kWave, 2)
-void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wq,
-                           const void *__restrict__ scales, const uint16_t *__restrict__ biases,
-                           uint16_t *__restrict__ y, int64_t M, int64_t N, int64_t K, int ntn)
+void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wqp,
+                       const void *__restrict__ scales, const uint16_t *__restrict__ biases, uint16_t *__restrict__ y,
+                       int M, int N, int K, int ntn, int per)
 {
-    constexpr int P = kQWaves, TC = NS * 16;
+    constexpr int P = kQWaves, TC = NS * 16, CB = qconst_chunk_bytes(QM, GS);
     __shared__ float red[P][16][TC + 1];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
-    const int nb = (int)(K / kQBlock);
-    const int nmine = wave < nb ? (nb - wave + P - 1) / P : 0;        // blocks of this wave per tile
-    const int mytiles = (int)blockIdx.x < ntn ? (ntn - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-    const int items = mytiles * nmine;
-    const int64_t words = K / 8, groups = K / GS;
-    // x row of A-operand row c; rows >= M read row M - 1 and are never stored
+    const int nb = K / kQBlock, nrg = (N + 15) / 16;
+    const int nmine = wave < nb ? (nb - wave + P - 1) / P : 0;          // blocks of this wave per tile
+    const int t0 = (int)blockIdx.x * per;
+    const int ntile = max(0, min(ntn, t0 + per) - t0);
+    const int items = ntile * nmine;
+    // per-lane constants offset inside a (row group, block) chunk
+    int coff;
+    if constexpr (QM == BI_AFFINE) coff = (c * (128 / GS) + (32 * g) / GS) * 4;
+    else if constexpr (QM == BI_NVFP4) coff = c * 8 + 2 * g;
+    else coff = c * 4 + g;
+    const uint8_t *cbase = reinterpret_cast<const uint8_t *>(wqp) + (int64_t)nrg * nb * 1024;
     const uint16_t *xr = x + (int64_t)(c < M ? c : M - 1) * K + g * 32;
 
-    uint4 Wr[D][NS], Xr[D][4];
-    uint32_t Sr[D][NS], Br[D][NS];
-    // prefetch cursor: item (pu, pj) = block wave + pj*P of tile pu; holds at the last item
-    int pu = 0, pj = 0;
-    auto load_next = [&](uint4 (&Wd)[NS], uint32_t (&Sd)[NS], uint32_t (&Bd)[NS], uint4 (&Xd)[4]) {
-        const int64_t t = (int64_t)blockIdx.x + (int64_t)pu * gridDim.x;
-        const int64_t kb = (int64_t)(wave + pj * P) * kQBlock + g * 32;     // this lane's first code
+    constexpr int NR = XR ? kQXRes : D;                  // ring slots
+    uint4 W[NR][NS];
+    uint32_t S[NR][NS];
+    uint4 X[XR ? kQXRes : D][4];
+    if constexpr (XR) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
+        for (int j = 0; j < kQXRes; ++j)
+            if (j < nmine) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    X[j][s] = *reinterpret_cast<const uint4 *>(xr + (wave + j * P) * kQBlock + s * 8);
+            }
+    }
+    int lu = 0, lj = 0;                                     // load cursor: tile t0 + lu, block wave + lj*P
+    auto load_item = [&](auto dc_) {
+        constexpr int d = decltype(dc_)::value;
+        const int b = wave + lj * P;
+#pragma unroll
+        for (int jj = 0; jj < NS; ++jj) {
+            const int rg = min((t0 + lu) * NS + jj, nrg - 1);
             if constexpr (PK) {
-                const int64_t nrg = (N + 15) / 16, rg = t * NS + j;
-                qload_packed_raw<QM, GS>(wq, nrg, nb, rg < nrg ? rg : nrg - 1, wave + pj * P, lane, Wd[j], Sd[j], Bd[j]);
+                const int64_t chunk = (int64_t)rg * nb + b;
+                W[d][jj] = *reinterpret_cast<const uint4 *>(wqp + (chunk * 64 + lane) * 4);
+                const uint8_t *cp = cbase + chunk * CB + coff;
+                if constexpr (QM == BI_AFFINE) S[d][jj] = *reinterpret_cast<const uint32_t *>(cp);
+                else if constexpr (QM == BI_NVFP4) S[d][jj] = *reinterpret_cast<const uint16_t *>(cp);
+                else S[d][jj] = *cp;
             } else {
-                int64_t n = t * TC + j * 16 + c;
-                n = n < N ? n : N - 1;                                      // padding columns read a real row
-                Wd[j] = *reinterpret_cast<const uint4 *>(wq + n * words + kb / 8);
-                const int64_t gi = n * groups + kb / GS;
-                if (QM == BI_AFFINE) {
-                    Sd[j] = ((const uint16_t *)scales)[gi];
-                    Bd[j] = biases[gi];
-                } else if (QM == BI_NVFP4) {
-                    Sd[j] = ((const uint16_t *)scales)[gi / 2];             // the lane's two group bytes
-                    Bd[j] = 0;
-                } else {
-                    Sd[j] = ((const uint8_t *)scales)[gi];                  // the lane's one group byte
-                    Bd[j] = 0;
-                }
+                // [N, K/8] codes, [N, K/gs] constants; a padding row reads row N - 1
+                const int64_t n = min(rg * 16 + c, N - 1);
+                const int64_t kb = (int64_t)b * kQBlock + g * 32;         // this lane's first code
+                W[d][jj] = *reinterpret_cast<const uint4 *>(wqp + n * (K / 8) + kb / 8);
+                const int64_t gi = n * (K / GS) + kb / GS;
+                if constexpr (QM == BI_AFFINE)
+                    S[d][jj] = (uint32_t)((const uint16_t *)scales)[gi] | ((uint32_t)biases[gi] << 16);
+                else if constexpr (QM == BI_NVFP4) S[d][jj] = ((const uint16_t *)scales)[gi / 2];   // the two group bytes
+                else S[d][jj] = ((const uint8_t *)scales)[gi];
             }
         }
-        // rows >= M (MFMA padding) load nothing: their products are never stored
-        if (c < M) {
+        if constexpr (!XR) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) Xd[s] = *reinterpret_cast<const uint4 *>(xr + (kb - g * 32) + s * 8);
-        } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Xd[s] = make_uint4(0, 0, 0, 0);
+            for (int s = 0; s < 4; ++s) X[d][s] = *reinterpret_cast<const uint4 *>(xr + b * kQBlock + s * 8);
         }
-        if (pj + 1 < nmine) {
-            ++pj;
-        } else if (pu + 1 < mytiles) {
-            pj = 0;
-            ++pu;
+        if (++lj == nmine) {
+            lj = 0;
+            ++lu;
         }
     };
     f32x4 acc[NS];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+    for (int jj = 0; jj < NS; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto finish_tile = [&](int u) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
+        for (int jj = 0; jj < NS; ++jj) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][j * 16 + c] = acc[j][r];
-            acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][jj * 16 + c] = acc[jj][r];
+            acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         __syncthreads();
-        const int64_t n0 = ((int64_t)blockIdx.x + (int64_t)u * gridDim.x) * TC;
+        const int n0 = (t0 + u) * TC;
         for (int o = threadIdx.x; o < 16 * TC; o += P * kWave) {
             const int r = o / TC, cc = o % TC;
-            const int64_t col = n0 + cc;
-            if (r >= M || col >= N) continue;
+            if (r >= M || n0 + cc >= N) continue;
             float v = red[0][r][cc];
 #pragma unroll
             for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
-            y[(int64_t)r * N + col] = F16::narrow(v);
+            y[(int64_t)r * N + n0 + cc] = F16::narrow(v);
         }
         __syncthreads();
     };
+    auto compute_item = [&](auto dc_, auto jc_) {
+        constexpr int d = decltype(dc_)::value, j = decltype(jc_)::value;
+        QGroup<QM> g01[NS], g23[NS];
+#pragma unroll
+        for (int jj = 0; jj < NS; ++jj) {
+            g01[jj] = group_from_raw<QM>(S[d][jj], S[d][jj] >> 16, 0);
+            g23[jj] = QM == BI_NVFP4 ? group_from_raw<QM>(S[d][jj], 0, 2) : g01[jj];
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 xa = X[XR ? j : d][s];                 // both compile-time indices
+#pragma unroll
+            for (int jj = 0; jj < NS; ++jj) {
+                const uint32_t wv = s == 0 ? W[d][jj].x : s == 1 ? W[d][jj].y : s == 2 ? W[d][jj].z : W[d][jj].w;
+                acc[jj] = qmfma(xa, deq_word<QM>(wv, s < 2 ? g01[jj] : g23[jj]), acc[jj]);
+            }
+        }
+    };
 
-    if (items > 0) {
-        int cu = 0, cj = 0;
-        static_for<0, D - 1>([&](auto dc) {
-            constexpr int d = decltype(dc)::value;
-            load_next(Wr[d], Sr[d], Br[d], Xr[d]);
+    if (nmine > 0 && XR) {
+        // ring slot j holds block j of the tile in flight: a tile's items are
+        // requested while the previous tile's are multiplied
+        static_for<0, kQXRes>([&](auto jc) {
+            if (decltype(jc)::value < nmine) load_item(jc);
         });
+        for (int u = 0; u < ntile; ++u) {
+            static_for<0, kQXRes>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if (j < nmine) {
+                    compute_item(jc, jc);
+                    if (u + 1 < ntile) load_item(jc);
+                }
+            });
+            finish_tile(u);
+        }
+    } else if (nmine > 0) {
+        static_for<0, D - 1>([&](auto dc) {
+            if (decltype(dc)::value < items) load_item(dc);
+        });
+        int cu = 0, cj = 0;
         for (int i = 0; i < items; i += D) {
             static_for<0, D>([&](auto dc) {
                 constexpr int d = decltype(dc)::value;
-                constexpr int dn = (d + D - 1) % D;
-                load_next(Wr[dn], Sr[dn], Br[dn], Xr[dn]);
-                __builtin_amdgcn_sched_barrier(0);
+                if (i + d + D - 1 < items) load_item(std::integral_constant<int, (d + D - 1) % D>{});
                 if (i + d < items) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-                        for (int j = 0; j < NS; ++j) {
-                            const QGroup<QM> gr = group_from_raw<QM>(Sr[d][j], Br[d][j], s);
-                            const uint32_t wv = s == 0 ? Wr[d][j].x : s == 1 ? Wr[d][j].y : s == 2 ? Wr[d][j].z : Wr[d][j].w;
-                            acc[j] = qmfma(Xr[d][s], deq_word<QM>(wv, gr), acc[j]);
-                        }
-                    }
+                    compute_item(dc, std::integral_constant<int, 0>{});
                     if (++cj == nmine) {
                         finish_tile(cu);
                         cj = 0;
                         ++cu;
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
             });
         }
     } else {
         // a wave that owns no block of K still takes part in every combine
-        for (int u = 0; u < mytiles; ++u) finish_tile(u);
+        for (int u = 0; u < ntile; ++u) finish_tile(u);
     }
 }
 
 template <int QM, int GS, int NS, bool PK>
 static void launch_q_stream_t(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
-                              int64_t N, int64_t K, hipStream_t st)
+                          int64_t N, int64_t K, hipStream_t st)
 {
     const int64_t ntn = cdiv(N, NS * 16);
-    const int64_t grid = std::min<int64_t>(ntn, (int64_t)device_cu_count() * 2);
-    launch_kernel((qmatmul_stream_kernel<QM, GS, NS, 3, PK>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
-                       (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, M, N, K, (int)ntn);
+    const int64_t slots = (int64_t)device_cu_count() * 2;
+    const int64_t per = cdiv(ntn, slots), grid = cdiv(ntn, per);
+    const bool xres = cdiv(K / kQBlock, kQWaves) <= kQXRes;
+    if (xres)
+        launch_kernel((qmatmul_stream_kernel<QM, GS, NS, 3, true, PK>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
+                      (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, (int)M, (int)N, (int)K, (int)ntn,
+                      (int)per);
+    else
+        launch_kernel((qmatmul_stream_kernel<QM, GS, NS, 3, false, PK>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0,
+                      st, (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, (int)M, (int)N, (int)K,
+                      (int)ntn, (int)per);
 }
 
 template <int QM, int GS, bool PK>
 static bool try_launch_q_stream(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                                 int64_t N, int64_t K, hipStream_t st)
 {
-    if (M > 16 || K % kQBlock != 0 || !host_aligned16(x) || !host_aligned16(wq) || cdiv(N, 16) > (1ll << 30))
+    if (M > 16 || K % kQBlock != 0 || !host_aligned16(x) || !host_aligned16(wq) || N >= (1ll << 30) ||
+        K >= (1ll << 30))
         return false;
-    if (N >= 8192) launch_q_stream_t<QM, GS, 2, PK>(x, wq, s, b, y, M, N, K, st);
-    else launch_q_stream_t<QM, GS, 1, PK>(x, wq, s, b, y, M, N, K, st);
+    launch_q_stream_t<QM, GS, 1, PK>(x, wq, s, b, y, M, N, K, st);
     return true;
 }
 

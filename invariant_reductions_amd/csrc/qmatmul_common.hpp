@@ -18,20 +18,21 @@ __device__ inline f32x4 qmfma(uint4 a, uint4 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// e4m3fn byte -> fp32 (exact); S.1111.111 -> NaN.
+// e4m3fn byte -> fp32 (exact); S.1111.111 -> NaN.  Selects, no branches.
 __device__ inline float e4m3_to_f32(uint32_t s)
 {
     const uint32_t sign = (s & 0x80u) << 24, e = (s >> 3) & 0xfu, m = s & 7u;
-    if (e == 0xfu && m == 7u) return __uint_as_float(0x7fc00000u);
-    if (e == 0) return __uint_as_float(__float_as_uint((float)m * 0x1p-9f) | sign);   // subnormal m/8 * 2^-6 (exact)
-    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+    const uint32_t normal = sign | ((e + 120u) << 23) | (m << 20);
+    const uint32_t sub = __float_as_uint((float)m * 0x1p-9f) | sign;      // subnormal m/8 * 2^-6 (exact)
+    const uint32_t v = e == 0 ? sub : normal;
+    return __uint_as_float((s & 0x7fu) == 0x7fu ? 0x7fc00000u : v);
 }
 
 // OCP MX e8m0 scale byte -> fp32 (exact): 2^(e - 127), 0xFF -> NaN.
 __device__ inline float e8m0_to_f32(uint32_t e)
 {
-    if (e == 0xffu) return __uint_as_float(0x7fc00000u);
-    return e == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);   // 2^-127 is subnormal
+    const uint32_t v = e == 0 ? 0x00400000u : (e << 23);                     // 2^-127 is subnormal
+    return __uint_as_float(e == 0xffu ? 0x7fc00000u : v);
 }
 
 // Bytes of one (16-row group, K block) constants chunk of the tile-packed
