@@ -80,22 +80,47 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids, budget_s):
-    """The oracle's decode step on the host, repeated until `budget_s` seconds
-    have passed (at least one step, at most sixteen)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids):
+    """The oracle's decode step on the host: the bench's batch with every
+    core (median of up to 5 steps, at most ~12 s), and batch 1 on one core
+    (median of 3 steps).  The oracle splits only independent outputs across
+    threads; each output's fold is the same at any thread count."""
     import oracle
     from oracle import decoder as odec
     from invariant_reductions_amd.inputs import rope_tables
     cos_t, sin_t = rope_tables(ctx + 8, cfg["head_dim"])
-    kv = np.full(B, ctx, np.int32)
-    t0 = time.perf_counter()
-    n = 0
-    while n < 16:
-        odec.decode_step(W, cfg, ids, kc_host, vc_host, kv, cos_t, sin_t)
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    return n, time.perf_counter() - t0, oracle.num_threads()
+    nproc = os.cpu_count() or 1
+
+    def run(Bn, reps, budget):
+        kv = np.full(Bn, ctx, np.int32)
+        ts = []
+        t_all = time.perf_counter()
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            odec.decode_step(W, cfg, ids[:Bn], [k[:Bn] for k in kc_host], [v[:Bn] for v in vc_host], kv, cos_t, sin_t)
+            ts.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_all > budget:
+                break
+        return float(np.median(ts)), len(ts)
+
+    oracle.set_num_threads(nproc)
+    all_threads = oracle.num_threads()
+    t_all, n_all = run(B, 5, 12.0)
+    oracle.set_num_threads(1)
+    t_one, n_one = run(1, 3, 12.0)
+    oracle.set_num_threads(nproc)
+    return dict(t_all=t_all, n_all=n_all, threads=all_threads, t_one=t_one, n_one=n_one, model=cpu_model(),
+                nproc=nproc)
 
 
 def main():
@@ -105,7 +130,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--ctx", type=int, default=768)
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     args = ap.parse_args()
@@ -126,7 +150,7 @@ def main():
     t_setup = time.perf_counter()
     W = inputs.decoder_weights(cfg, seed=0)
     cap = ctx + 2 * K + Wm + 8
-    model = Decoder(cfg, W, max_batch=B, max_q=1, max_len=cap, device=dev)
+    model = Decoder(cfg, W, max_batch=B, max_q=5, max_len=cap, device=dev)      # max_q 5: the verify sweep
     rng = np.random.default_rng(1)
     Hkv, D = cfg["n_kv_heads"], cfg["head_dim"]
     kc_host, vc_host = [], []
@@ -238,18 +262,26 @@ def main():
 
     if not args.no_extras:
         out["ops"] = op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch)
-        out["invariance_overhead"] = split_overhead(torch, bi, model, B, per_shape)
+        out["decode_sweep"] = decode_sweep(torch, model, stream, cap, ctx)
+        out["measured_peaks"] = measured_peaks(torch, bi, dev)
+        out["roofline"]["frac_of_measured_read"] = round(mm_gbs / out["measured_peaks"]["hbm_read_gbs"], 4)
+        out["invariance_overhead"] = invariance_overhead(torch, bi, dev, B)
         out["qmatmul"] = qmatmul_decode(torch, bi, dev)
         out["row_ops"] = row_ops(torch, bi, model, B)
         out["sweep"] = op_sweep(torch, bi, dev)
 
     if not args.no_cpu_baseline:
-        n, secs, cores = cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids0, args.cpu_budget)
-        trc = step_traffic(cfg, B, ctx)
-        out["cpu_baseline"] = {"value": round(trc["total_bytes"] * n / secs / 1e9, 3), "unit": "GB/s",
-                               "cores": cores, "kind": "oracle",
-                               "sample": f"{n} decode step(s) of the same workload (batch {B}, context {ctx}) "
-                                         f"through the oracle's fixed-order fp32 ops, {secs:.1f} s"}
+        cb = cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids0)
+        trc, tr1 = step_traffic(cfg, B, ctx), step_traffic(cfg, 1, ctx)
+        out["cpu_baseline"] = {
+            "value": round(trc["total_bytes"] / cb["t_all"] / 1e9, 3), "unit": "GB/s", "cores": cb["threads"],
+            "kind": "oracle", "cpu": cb["model"], "nproc": cb["nproc"],
+            "sample": f"median of {cb['n_all']} decode step(s) of the same workload (batch {B}, context {ctx}) "
+                      f"through the oracle's fixed-order fp32 ops on {cb['threads']} threads: "
+                      f"{cb['t_all']:.2f} s per step",
+            "single_thread": {"value": round(tr1["total_bytes"] / cb["t_one"] / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "sample": f"median of {cb['n_one']} decode step(s) at batch 1, context {ctx}: "
+                                        f"{cb['t_one']:.2f} s per step"}}
     print(json.dumps(out), flush=True)
 
 
@@ -298,31 +330,6 @@ def _time(torch, fn, reps=20):
     return s.elapsed_time(t) / reps
 
 
-def split_overhead(torch, bi, model, B, per_shape):
-    """Invariant dense matmul (its launches inside the timed decode steps) vs the
-    fastest split-K comparison variant at the same shapes, on the decoder's own
-    weights, rotating over the layers so the weights are as cold as in a step."""
-    dev = model.dev
-    res = {}
-    mats = {(model.qkvn, model.H): [L["wqkv"] for L in model.layers], (model.H, model.qn): [L["wo"] for L in model.layers],
-            (2 * model.F, model.H): [L["wgu_il"] for L in model.layers], (model.H, model.F): [L["wdown"] for L in model.layers],
-            (model.V, model.H): [model.lm_head]}
-    for (N, K), ws_list in mats.items():
-        x = torch.randn(B, K, device=dev).to(torch.bfloat16)
-        y = torch.empty(B, N, dtype=torch.bfloat16, device=dev)
-        t_inv = float(np.mean(per_shape[(N, K)]))
-        best = None
-        for s in (2, 4, 8, 16):
-            ws = torch.empty(B * N * s * 4, dtype=torch.uint8, device=dev)
-            it = iter(range(1 << 30))
-            t = _time(torch, lambda: bi.matmul_split(x, ws_list[next(it) % len(ws_list)], s, True, out=y, ws=ws))
-            if best is None or t < best[1]:
-                best = (s, t)
-        res[f"{B}x{N}x{K}"] = {"invariant_us": round(t_inv * 1e3, 1), "best_split": best[0],
-                               "split_us": round(best[1] * 1e3, 1), "overhead": round(t_inv / best[1] - 1, 3)}
-    return res
-
-
 def _time_kernel(torch, bi, fn, reps, launches=1):
     """Mean execution time (ms) of the `launches` bi kernels `fn` launches: a
     start/stop event pair recorded by the launches themselves
@@ -350,7 +357,8 @@ def op_sweep(torch, bi, dev):
       SDPA (two launches: chunks and merge): B = 1, Q in {1, 8} at
         Lk in {1028, 8196, 16388, 65540}, and B in {4, 16, 64} at Q = 1,
         Lk = 8196."""
-    res = {"matmul": {}, "rmsnorm": {}, "sdpa": {}}
+    res = {"target": "decode shapes with >= 32 MiB of weights or KV, and RMSNorm at B = 4096: frac_hbm >= 0.70",
+           "matmul": {}, "rmsnorm": {}, "sdpa": {}}
     bf = torch.bfloat16
     for (N, K) in ((4096, 4096), (6144, 4096), (28672, 4096), (4096, 14336), (32000, 4096)):
         copies = max(2, -(-(512 << 20) // (N * K * 2)))
@@ -409,6 +417,224 @@ def op_sweep(torch, bi, dev):
                                                        "frac_mfma": round(tf / 2500.0, 4)}
         del ks, vs, wsd
     torch.cuda.empty_cache()
+    return res
+
+
+def measured_peaks(torch, bi, dev):
+    """What this GPU sustains, by the library's probes (kernel time,
+    launch-recorded events, median of 5): a streaming read and a copy of
+    1 GiB (best of three grid sizes) and back-to-back bf16 MFMA."""
+    L = bi.lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    sink = torch.empty(1 << 22, dtype=torch.uint8, device=dev)
+
+    def ktime(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            s_, t_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record()                                   # creates the event handles
+            t_.record()
+            L.bi_time_next_launch(ctypes.c_void_p(s_.cuda_event), ctypes.c_void_p(t_.cuda_event))
+            rc = fn()
+            assert rc == 0, rc
+            torch.cuda.synchronize()
+            ts.append(s_.elapsed_time(t_))
+        return float(np.median(ts)) * 1e-3
+
+    read = max(n / ktime(lambda: L.bi_probe_read(ctypes.c_void_p(a.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                                                 wg, st)) / 1e9 for wg in (512, 2048, 8192))
+    copy = max(2 * n / ktime(lambda: L.bi_probe_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n,
+                                                     wg, st)) / 1e9 for wg in (1024, 4096))
+    wg, iters = 2048, 20000
+    mf = wg * 4 * iters * 8 * 16384 / ktime(lambda: L.bi_probe_mfma(ctypes.c_void_p(sink.data_ptr()), wg, iters, st),
+                                           reps=3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": round(read, 1), "hbm_copy_gbs": round(copy, 1), "mfma_bf16_tflops": round(mf, 1),
+            "method": "bi_probe_read / bi_probe_copy over 1 GiB (best of 3 grid sizes), bi_probe_mfma "
+                      "(v_mfma_f32_16x16x32_bf16, 8 independent chains per wave); kernel time, median of 5"}
+
+
+def _ab(torch, fns, reps=11, inner=10):
+    """Median ms per call of each callable, timed in alternating order (A, B,
+    C, A, B, C, ...): every sample is one event pair around `inner` calls."""
+    ev = {k: [] for k in fns}
+    for k, f in fns.items():                      # warm every side once
+        for i in range(inner):
+            f(i)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for k, f in fns.items():
+            s_, t_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record()
+            for i in range(inner):
+                f(r * inner + i)
+            t_.record()
+            ev[k].append((s_, t_))
+    torch.cuda.synchronize()
+    return {k: float(np.median([s_.elapsed_time(t_) / inner for s_, t_ in v])) for k, v in ev.items()}
+
+
+def _raw(fn, per_call):
+    """A callable i -> fn(*per_call[i % len]) with every argument already a
+    ctypes value: the library's entry point without the Python binding's
+    checks, so a small kernel's time is not the binding's host overhead."""
+    def call(i):
+        rc = fn(*per_call[i % len(per_call)])
+        if rc != 0:
+            raise RuntimeError(f"bench call failed: {rc}")
+    return call
+
+
+def invariance_overhead(torch, bi, dev, B):
+    """Cost of invariance per op: the invariant kernel against the fastest
+    non-invariant way to compute the same thing on this GPU -- the vendor
+    libraries torch dispatches to (hipBLASLt for the matmuls, torch's RMSNorm
+    and scaled-dot-product attention, which choose their kernels and splits by
+    shape) and this library's split comparison variants (split-K matmul with a
+    cleanup reduction, split-row RMSNorm; best split count per shape).  Both
+    sides on the same stream, same operands (weights rotated over copies of
+    at least 512 MiB so that neither side finds them in a cache), median of
+    11 alternating samples of 10 calls.  overhead = t_invariant / t_best - 1
+    (negative: the invariant kernel is the faster)."""
+    import torch.nn.functional as F
+    bf, f16 = torch.bfloat16, torch.float16
+    res = {"method": "median of 11 alternating A/B samples, 10 calls each, events around the calls (same for every "
+                     "side); cold operands; this library's entry points called through ctypes with prepared "
+                     "arguments, torch's through torch", "matmul": {}, "qmatmul": {}, "rmsnorm": {}, "sdpa": {}}
+    L = bi.lib()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def verdict(t_inv, alts):
+        best = min(alts, key=alts.get)
+        return {"invariant_us": round(t_inv * 1e3, 2), **{f"{k}_us": round(v * 1e3, 2) for k, v in alts.items()},
+                "best_non_invariant": best, "overhead": round(t_inv / alts[best] - 1, 3),
+                "faster": "invariant" if t_inv <= alts[best] else best}
+
+    shapes = [(M, 4096, 4096) for M in (1, 2, 4, 8)] + [(B, N, K) for (N, K) in
+                                                         ((6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336),
+                                                          (32000, 4096))]
+    for M, N, K in shapes:
+        copies = max(2, -(-(512 << 20) // (N * K * 2)))
+        ws_ = [(torch.randn(N, K, device=dev) * 0.02).to(bf) for _ in range(copies)]
+        wp = [bi.pack_weights(w) for w in ws_]
+        x = torch.randn(M, K, device=dev).to(bf)
+        y = torch.empty(M, N, dtype=bf, device=dev)
+        mws = bi.matmul_workspace(M, N, K, device=dev)
+        fns = {"inv": _raw(L.bi_matmul_ws, [(vp(x), vp(w.data), vp(y), M, N, K, 0, 2, vp(mws), mws.numel(), st)
+                                            for w in wp]),
+               "hipblaslt": lambda i: torch.mm(x, ws_[i % copies].t(), out=y)}
+        for sp in (2, 4, 8):
+            sws = torch.empty(M * N * sp * 4, dtype=torch.uint8, device=dev)
+            fns[f"split{sp}"] = _raw(L.bi_matmul_split, [(vp(x), vp(w.data), vp(y), M, N, K, 0, 2, sp, vp(sws),
+                                                          sws.numel(), st) for w in wp])
+        t = _ab(torch, fns)
+        alts = {k: v for k, v in t.items() if k != "inv"}
+        best_split = min((k for k in alts if k.startswith("split")), key=alts.get)
+        alts = {"hipblaslt": alts["hipblaslt"], best_split: alts[best_split]}
+        res["matmul"][f"{M}x{N}x{K}"] = verdict(t["inv"], alts)
+        del ws_, wp
+    # quantized: the invariant 4-bit kernel (tile-packed) against hipBLASLt on
+    # the same matrix already dequantized to binary16 (the path without a
+    # quantized kernel)
+    N, K, gs = 28672, 4096, 32
+    from invariant_reductions_amd import inputs
+    _, wq, sc, _ = inputs.qmatmul_case(1, K, N, "mxfp4", gs, True, seed=0)
+    wq0 = torch.from_numpy(wq.view(np.int32)).to(dev)
+    sd = torch.from_numpy(sc).to(dev)
+    copies = 8
+    wqp = [bi.pack_qweights(torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff), sd, None, N, K, bi.MXFP4, gs)
+           for r in range(copies)]
+    wd = [torch.randn(N, K, device=dev).to(f16) for _ in range(3)]
+    for M in (1, 4, 8):
+        x = torch.randn(M, K, device=dev).to(f16)
+        y = torch.empty(M, N, dtype=f16, device=dev)
+        t = _ab(torch, {"inv": _raw(L.bi_qmatmul, [(vp(x), vp(w), None, None, vp(y), M, N, K, bi.MXFP4, 4, gs, 2, st)
+                                                   for w in wqp]),
+                        "hipblaslt_f16": lambda i: torch.mm(x, wd[i % 3].t(), out=y)})
+        res["qmatmul"][f"mxfp4 {M}x{N}x{K}"] = verdict(t["inv"], {"hipblaslt_f16": t["hipblaslt_f16"]})
+    del wqp, wd
+    H = 4096
+    w = torch.ones(H, dtype=bf, device=dev)
+    for Bn in (1, 64, 4096):
+        copies = max(2, min(64, -(-(512 << 20) // (Bn * H * 2))))
+        xs = [torch.randn(Bn, H, device=dev).to(bf) for _ in range(copies)]
+        y = torch.empty(Bn, H, dtype=bf, device=dev)
+        eps = ctypes.c_float(1e-6)
+        fns = {"inv": _raw(L.bi_rmsnorm, [(vp(xx), vp(w), vp(y), Bn, H, eps, 0, st) for xx in xs]),
+               "torch": lambda i: F.rms_norm(xs[i % copies], (H,), w, 1e-6)}
+        for sp in (2, 4, 8):
+            sws = torch.empty(max(16, L.bi_rmsnorm_split_workspace_bytes(Bn, sp)), dtype=torch.uint8, device=dev)
+            fns[f"split{sp}"] = _raw(L.bi_rmsnorm_split, [(vp(xx), vp(w), vp(y), Bn, H, eps, 0, sp, vp(sws),
+                                                           sws.numel(), st) for xx in xs])
+        t = _ab(torch, fns)
+        alts = {k: v for k, v in t.items() if k != "inv"}
+        best_split = min((k for k in alts if k.startswith("split")), key=alts.get)
+        res["rmsnorm"][f"{Bn}x{H}"] = verdict(t["inv"], {"torch": alts["torch"], best_split: alts[best_split]})
+        del xs
+    Hq, Hkv, D = 32, 8, 128
+    for Bn, Lk in ((1, 16388), (1, 65540), (B, 768)):
+        copies = max(2, min(8, -(-(512 << 20) // (4 * Bn * Lk * Hkv * D))))
+        ks = [torch.randn(Bn, Hkv, Lk, D, device=dev).to(bf) for _ in range(copies)]
+        vs = [torch.randn(Bn, Hkv, Lk, D, device=dev).to(bf) for _ in range(copies)]
+        q = torch.randn(Bn, 1, Hq, D, device=dev).to(bf)
+        qt = q.transpose(1, 2).contiguous()                      # [B, Hq, 1, D] for torch
+        kv = torch.full((Bn,), Lk, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        wsd = torch.empty(bi.sdpa_workspace_bytes(Bn, 1, Lk, Hq, D), dtype=torch.uint8, device=dev)
+        fns = {"inv": _raw(L.bi_sdpa, [(vp(q), vp(kk), vp(vv), vp(o), vp(kv), Lk, Bn, 1, Lk, Hq, Hkv, D,
+                                        ctypes.c_float(0.088), 1, 0, 1, vp(wsd), wsd.numel(), st)
+                                       for kk, vv in zip(ks, vs)]),
+               "torch_sdpa": lambda i: F.scaled_dot_product_attention(qt, ks[i % copies], vs[i % copies], scale=0.088,
+                                                                      enable_gqa=True)}
+        t = _ab(torch, fns)
+        res["sdpa"][f"B{Bn} Q1 Lk{Lk}"] = verdict(t["inv"], {"torch_sdpa": t["torch_sdpa"]})
+        del ks, vs
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_sweep(torch, model, stream, cap, ctx, steps=10):
+    """Config-5 step time at B in {1, 4, 16, 64}: plain greedy decoding (the
+    self-advancing one-token plan, replayed) and speculative verification
+    (one causal block of 5 tokens per sequence: the last committed token and
+    4 drafts).  Tokens/s for verification assume every draft is accepted
+    (5 tokens per sequence per step); with rejections it scales with the
+    accepted count plus one."""
+    res = {}
+    for Bs in (1, 4, 16, 64):
+        if Bs > model.max_batch:
+            continue
+        r = {}
+        model.kv_len[:Bs].fill_(ctx)
+        plan = model.plan(Bs, 1, cap, stream, advance=True)
+        for _ in range(2):
+            model.run_plan(plan)
+        model.kv_len[:Bs].fill_(ctx)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            model.run_plan(plan)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        r["plain"] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(Bs / (ms * 1e-3), 1)}
+        if model.max_q >= 5:
+            model.kv_len[:Bs].fill_(ctx + 5)
+            vplan = model.plan(Bs, 5, cap, stream)
+            model.run_plan(vplan)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                model.run_plan(vplan)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / steps
+            r["verify_q5"] = {"ms_per_step": round(ms, 4), "tokens_per_s_all_accepted": round(5 * Bs / (ms * 1e-3), 1)}
+        res[f"B{Bs}"] = r
     return res
 
 

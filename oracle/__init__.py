@@ -90,6 +90,7 @@ def lib():
         L.bo_log_softmax.argtypes = [P, P, I64, I64, I32]
         L.bo_row_mean.argtypes = [P, P, I64, I64, I32]
         L.bo_num_threads.argtypes = []; L.bo_num_threads.restype = ctypes.c_int
+        L.bo_set_num_threads.argtypes = [ctypes.c_int]; L.bo_set_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -110,6 +111,11 @@ def _dt(dtype) -> int:
 
 def num_threads() -> int:
     return lib().bo_num_threads()
+
+
+def set_num_threads(n: int) -> int:
+    """Threads of the oracle's parallel loops (over independent outputs only)."""
+    return lib().bo_set_num_threads(int(n))
 
 
 # --- number formats --------------------------------------------------------

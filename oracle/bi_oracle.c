@@ -648,6 +648,19 @@ int bo_row_mean(const void *x, float *y, int64_t rows, int64_t cols, int dtype)
     return 0;
 }
 
+/* Threads the oracle's parallel loops use from now on (n >= 1); returns the
+ * count in effect.  Each output's fold is sequential whatever n is. */
+int bo_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 int bo_num_threads(void)
 {
 #ifdef _OPENMP
