@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--ctx", type=int, default=768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--op", choices=sorted(OP_WORKLOADS),
+                    help="run only one op's profiling workload (for rocprofv3 kernel traces and counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the batch-invariant hot path is a single-GPU kernel set "
@@ -142,6 +144,9 @@ def main():
     import invariant_reductions_amd as bi
     from invariant_reductions_amd import inputs
     from invariant_reductions_amd.decoder import Decoder
+    if args.op:
+        op_workload(torch, bi, args.op)
+        return
 
     cfg = inputs.LLAMA_4L
     B, ctx, K, Wm = args.batch, args.ctx, args.steps, args.warmup
@@ -283,6 +288,118 @@ def main():
                               "sample": f"median of {cb['n_one']} decode step(s) at batch 1, context {ctx}: "
                                         f"{cb['t_one']:.2f} s per step"}}
     print(json.dumps(out), flush=True)
+
+
+def _op_matmul(torch, bi, dev):
+    """Dense projections: the decoder's at M = 64 (slot kernel), the verify
+    block of 64 sequences x 5 tokens (M = 320) and a 4096-row prompt."""
+    bf = torch.bfloat16
+    # reference point for MFMA counters: the bf16 MFMA probe (back-to-back
+    # v_mfma_f32_16x16x32_bf16, 8 waves per CU)
+    sink = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    L = bi.lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    yield "probe mfma 2048 workgroups x 4096 rounds", lambda i: L.bi_probe_mfma(ctypes.c_void_p(sink.data_ptr()), 2048,
+                                                                               4096, st), 5
+    for M, N, K in ((64, 4096, 4096), (64, 6144, 4096), (64, 28672, 4096), (320, 28672, 4096),
+                    (320, 4096, 4096), (4096, 4096, 4096), (4096, 14336, 4096)):
+        copies = max(2, -(-(512 << 20) // (N * K * 2)))
+        ws_ = [bi.pack_weights((torch.randn(N, K, device=dev) * 0.02).to(bf)) for _ in range(copies)]
+        x = torch.randn(M, K, device=dev).to(bf)
+        y = torch.empty(M, N, dtype=bf, device=dev)
+        mws = bi.matmul_workspace(M, N, K, device=dev)
+        yield f"matmul {M}x{N}x{K} packed", lambda i: bi.matmul_ws(x, ws_[i % copies], mws, out=y), 2 * copies
+        del ws_
+
+
+def _op_qmatmul(torch, bi, dev):
+    """4-bit decode projections 28672 x 4096 at M = 1, 4, 8 in the
+    transposed and tile-packed layouts, three formats."""
+    from invariant_reductions_amd import inputs
+    N, K = 28672, 4096
+    for mode, gs, qm in (("affine", 64, bi.AFFINE), ("nvfp4", 16, bi.NVFP4), ("mxfp4", 32, bi.MXFP4)):
+        x, wq, s, b = inputs.qmatmul_case(8, K, N, mode, gs, True, seed=0)
+        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
+        wq0 = torch.from_numpy(wq.view(np.int32)).to(dev)
+        sd = torch.from_numpy(s if s.dtype == np.uint8 else s.view(np.int16)).to(dev)
+        bd = None if b is None else torch.from_numpy(b.view(np.int16)).to(dev)
+        copies = 12
+        wqs = [wq0] + [torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff) for r in range(1, copies)]
+        wps = [bi.pack_qweights(w, sd, bd, N, K, qm, gs) for w in wqs]
+        for M in (1, 4, 8):
+            y = torch.empty(M, N, dtype=torch.float16, device=dev)
+            xm = xd[:M].contiguous()
+            yield (f"qmatmul {mode} gs{gs} {M}x{N}x{K} transposed",
+                   lambda i: bi.qmatmul(xm, wqs[i % copies], sd, bd, N, K, qm, gs, True, out=y), 2 * copies)
+            yield (f"qmatmul {mode} gs{gs} {M}x{N}x{K} packed",
+                   lambda i: bi.qmatmul(xm, wps[i % copies], None, None, N, K, qm, gs, out=y, packed=True), 2 * copies)
+        del wqs, wps
+
+
+def _op_sdpa(torch, bi, dev):
+    """Decode attention (32 query / 8 KV heads, d 128, head-major bf16
+    cache): one sequence at 16388 and 65540 keys, 64 sequences at 768 and
+    8196 keys, a verify block of 8 at 65540 keys; and a 2048-token causal
+    prompt (prefill)."""
+    Hq, Hkv, D = 32, 8, 128
+    for B, Q, Lk in ((1, 1, 16388), (1, 1, 65540), (1, 8, 65540), (64, 1, 768), (64, 1, 8196), (1, 2048, 2048)):
+        copies = max(2, min(8, -(-(512 << 20) // (4 * B * Lk * Hkv * D))))
+        ks = [torch.randn(B, Hkv, Lk, D, device=dev).to(torch.bfloat16) for _ in range(copies)]
+        vs = [torch.randn(B, Hkv, Lk, D, device=dev).to(torch.bfloat16) for _ in range(copies)]
+        q = torch.randn(B, Q, Hq, D, device=dev).to(torch.bfloat16)
+        kv = torch.full((B,), Lk, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        ws = torch.empty(bi.sdpa_workspace_bytes(B, Q, Lk, Hq, D), dtype=torch.uint8, device=dev)
+        yield (f"sdpa B{B} Q{Q} Lk{Lk}",
+               lambda i: bi.sdpa(q, ks[i % copies], vs[i % copies], kv, Lk, 0.088, True, out=o, ws=ws,
+                                 head_major=True), 10)
+        del ks, vs
+
+
+def _op_rmsnorm(torch, bi, dev):
+    """RMSNorm and fused add + RMSNorm over 4096-wide bf16 rows: 64 rows
+    (decode) and 4096 rows."""
+    H = 4096
+    w = torch.ones(H, dtype=torch.bfloat16, device=dev)
+    for Bn in (64, 4096):
+        copies = max(2, min(64, -(-(512 << 20) // (Bn * H * 2))))
+        xs = [torch.randn(Bn, H, device=dev).to(torch.bfloat16) for _ in range(copies)]
+        r = torch.randn(Bn, H, device=dev).to(torch.bfloat16)
+        y = torch.empty(Bn, H, dtype=torch.bfloat16, device=dev)
+        xo = torch.empty_like(y)
+        yield f"rmsnorm {Bn}x{H}", lambda i: bi.rmsnorm(xs[i % copies], w, out=y), 2 * copies
+        yield f"add_rmsnorm {Bn}x{H}", lambda i: bi.add_rmsnorm(xs[i % copies], r, w, x_out=xo, out=y), 2 * copies
+        del xs
+
+
+OP_WORKLOADS = {"matmul": _op_matmul, "qmatmul": _op_qmatmul, "sdpa": _op_sdpa, "rmsnorm": _op_rmsnorm}
+
+
+def op_workload(torch, bi, name):
+    """One op's profiling workload: a plain 256 MiB device copy first (counter
+    runs scale FETCH_SIZE / WRITE_SIZE by what it reads), then every case of
+    the op, each called repeatedly on operands rotated over copies of at least
+    512 MiB (no case finds its operands in a cache).  Prints one line per case
+    with the median event-timed call (host launch overhead included)."""
+    dev = torch.device("cuda:0")
+    bi.lib()
+    calib = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+    calib2 = torch.empty_like(calib)
+    calib2.copy_(calib)
+    torch.cuda.synchronize()
+    del calib, calib2
+    for label, fn, reps in OP_WORKLOADS[name](torch, bi, dev):
+        fn(0)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)[reps // 2]
+        print(f"case {label}: {reps} calls, median {us:.1f} us", flush=True)
+        torch.cuda.empty_cache()
 
 
 def op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch):
@@ -495,8 +612,10 @@ def invariance_overhead(torch, bi, dev, B):
     non-invariant way to compute the same thing on this GPU -- the vendor
     libraries torch dispatches to (hipBLASLt for the matmuls, torch's RMSNorm
     and scaled-dot-product attention, which choose their kernels and splits by
-    shape) and this library's split comparison variants (split-K matmul with a
-    cleanup reduction, split-row RMSNorm; best split count per shape).  Both
+    shape) and this library's split comparison variants (split-K matmul and
+    quantized matmul with a cleanup reduction, split-row RMSNorm, split-KV
+    attention with the split count as a free parameter; best split count per
+    shape).  Both
     sides on the same stream, same operands (weights rotated over copies of
     at least 512 MiB so that neither side finds them in a cache), median of
     11 alternating samples of 10 calls.  overhead = t_invariant / t_best - 1
@@ -539,26 +658,37 @@ def invariance_overhead(torch, bi, dev, B):
         alts = {"hipblaslt": alts["hipblaslt"], best_split: alts[best_split]}
         res["matmul"][f"{M}x{N}x{K}"] = verdict(t["inv"], alts)
         del ws_, wp
-    # quantized: the invariant 4-bit kernel (tile-packed) against hipBLASLt on
-    # the same matrix already dequantized to binary16 (the path without a
-    # quantized kernel)
-    N, K, gs = 28672, 4096, 32
+    # quantized: the invariant 4-bit kernel (tile-packed) against its own
+    # split-K variant (best of 2, 4, 8 splits) and hipBLASLt on the same
+    # matrix already dequantized to binary16 (the path without a quantized
+    # kernel)
     from invariant_reductions_amd import inputs
-    _, wq, sc, _ = inputs.qmatmul_case(1, K, N, "mxfp4", gs, True, seed=0)
-    wq0 = torch.from_numpy(wq.view(np.int32)).to(dev)
-    sd = torch.from_numpy(sc).to(dev)
-    copies = 8
-    wqp = [bi.pack_qweights(torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff), sd, None, N, K, bi.MXFP4, gs)
-           for r in range(copies)]
-    wd = [torch.randn(N, K, device=dev).to(f16) for _ in range(3)]
-    for M in (1, 4, 8):
-        x = torch.randn(M, K, device=dev).to(f16)
-        y = torch.empty(M, N, dtype=f16, device=dev)
-        t = _ab(torch, {"inv": _raw(L.bi_qmatmul, [(vp(x), vp(w), None, None, vp(y), M, N, K, bi.MXFP4, 4, gs, 2, st)
-                                                   for w in wqp]),
-                        "hipblaslt_f16": lambda i: torch.mm(x, wd[i % 3].t(), out=y)})
-        res["qmatmul"][f"mxfp4 {M}x{N}x{K}"] = verdict(t["inv"], {"hipblaslt_f16": t["hipblaslt_f16"]})
-    del wqp, wd
+    gs = 32
+    for N, K, Ms in ((4096, 4096, (1, 2, 4, 8)), (28672, 4096, (1, 4, 8))):
+        _, wq, sc, _ = inputs.qmatmul_case(1, K, N, "mxfp4", gs, True, seed=0)
+        wq0 = torch.from_numpy(wq.view(np.int32)).to(dev)
+        sd = torch.from_numpy(sc).to(dev)
+        copies = max(2, -(-(512 << 20) // (N * K // 2)))
+        wqp = [bi.pack_qweights(torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff), sd, None, N, K, bi.MXFP4,
+                                gs) for r in range(copies)]
+        ndd = max(2, -(-(512 << 20) // (N * K * 2)))
+        wd = [torch.randn(N, K, device=dev).to(f16) for _ in range(ndd)]
+        for M in Ms:
+            x = torch.randn(M, K, device=dev).to(f16)
+            y = torch.empty(M, N, dtype=f16, device=dev)
+            fns = {"inv": _raw(L.bi_qmatmul, [(vp(x), vp(w), None, None, vp(y), M, N, K, bi.MXFP4, 4, gs, 2, st)
+                                              for w in wqp]),
+                   "hipblaslt_f16": lambda i: torch.mm(x, wd[i % ndd].t(), out=y)}
+            for sp in (2, 4, 8):
+                qws = torch.empty(L.bi_qmatmul_split_workspace_bytes(M, N, sp), dtype=torch.uint8, device=dev)
+                fns[f"split{sp}"] = _raw(L.bi_qmatmul_split, [(vp(x), vp(w), None, None, vp(y), M, N, K, bi.MXFP4, 4,
+                                                               gs, 2, sp, vp(qws), qws.numel(), st) for w in wqp])
+            t = _ab(torch, fns)
+            alts = {k: v for k, v in t.items() if k != "inv"}
+            best_split = min((k for k in alts if k.startswith("split")), key=alts.get)
+            res["qmatmul"][f"mxfp4 {M}x{N}x{K}"] = verdict(t["inv"], {"hipblaslt_f16": alts["hipblaslt_f16"],
+                                                                      best_split: alts[best_split]})
+        del wqp, wd
     H = 4096
     w = torch.ones(H, dtype=bf, device=dev)
     for Bn in (1, 64, 4096):
@@ -592,8 +722,22 @@ def invariance_overhead(torch, bi, dev, B):
                                        for kk, vv in zip(ks, vs)]),
                "torch_sdpa": lambda i: F.scaled_dot_product_attention(qt, ks[i % copies], vs[i % copies], scale=0.088,
                                                                       enable_gqa=True)}
+        # the split-KV variant at split counts from one run per (sequence, KV
+        # head) up to runs of 4 chunks
+        nch = -(-Lk // 256)
+        for sp in sorted({1, 2, 4, 8, 16, 32, 64, 128, max(1, nch // 4)}):
+            if sp > nch:
+                continue
+            nb = L.bi_sdpa_split_workspace_bytes(Bn, 1, Lk, Hq, D, sp)
+            sws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+            fns[f"split{sp}"] = _raw(L.bi_sdpa_split, [(vp(q), vp(kk), vp(vv), vp(o), vp(kv), Lk, Bn, 1, Lk, Hq, Hkv,
+                                                        D, ctypes.c_float(0.088), 1, 0, 1, sp, vp(sws), sws.numel(),
+                                                        st) for kk, vv in zip(ks, vs)])
         t = _ab(torch, fns)
-        res["sdpa"][f"B{Bn} Q1 Lk{Lk}"] = verdict(t["inv"], {"torch_sdpa": t["torch_sdpa"]})
+        alts = {k: v for k, v in t.items() if k != "inv"}
+        best_split = min((k for k in alts if k.startswith("split")), key=alts.get)
+        res["sdpa"][f"B{Bn} Q1 Lk{Lk}"] = verdict(t["inv"], {"torch_sdpa": alts["torch_sdpa"],
+                                                             best_split: alts[best_split]})
         del ks, vs
     torch.cuda.empty_cache()
     return res

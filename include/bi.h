@@ -439,7 +439,9 @@ bi_status bi_argmax_advance(const void *x, int32_t *idx, int32_t *ids_next, int3
  * picks `splits` from the batch size gets batch-dependent bits.
  * Source: "Batch-invariant kernels ...", Case 2 (split-k), Case 3, Case 4,
  * Case 6 (Split-K / Split-KV); "Fix/speculative shape invariance", Problem.
- * bi_matmul_split takes weights in any layout of bi_matmul.
+ * bi_matmul_split takes weights in any layout of bi_matmul.  The quantized
+ * and attention variants below are built from the invariant path's own
+ * kernels, so that only the tree differs.
  * ------------------------------------------------------------------------ */
 size_t bi_matmul_split_workspace_bytes(int64_t M, int64_t N, int32_t splits);
 bi_status bi_matmul_split(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K,
@@ -450,6 +452,44 @@ size_t bi_rmsnorm_split_workspace_bytes(int64_t rows, int32_t splits);
 bi_status bi_rmsnorm_split(const void *x, const void *w, void *y, int64_t rows, int64_t H,
                            float eps, int32_t dtype, int32_t splits,
                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Split-K quantized matmul: arguments and result layout of bi_qmatmul, plus
+ * `splits` (1 .. K / 128).  Split z reduces the contiguous K blocks
+ * [z nb / splits, (z + 1) nb / splits) (nb = K / 128) with the streaming
+ * decode kernel's in-block tree, writing fp32 partials [splits, M, N] to ws;
+ * a cleanup kernel adds them in z order and rounds to binary16.  splits == 1
+ * is bi_qmatmul itself (ws unused).  Takes the 4-bit modes in the transposed
+ * (1) or packed (2) layout with M <= 16, K % 128 == 0 and 16-byte aligned x
+ * and wq; other shapes: BI_ERR_UNSUPPORTED.  Workspace: at least
+ * bi_qmatmul_split_workspace_bytes(M, N, splits) bytes, 16-byte aligned
+ * (else BI_ERR_WORKSPACE / BI_ERR_ALIGN).
+ * Source: "Fix fp quantized matmul corruption ..." (the quantized decode
+ * kernel it is built from); "Batch-invariant kernels ...", Case 2 (split-k). */
+size_t bi_qmatmul_split_workspace_bytes(int64_t M, int64_t N, int32_t splits);
+bi_status bi_qmatmul_split(const void *x, const uint32_t *wq, const void *scales, const void *biases, void *y,
+                           int64_t M, int64_t N, int64_t K, int32_t qmode, int32_t bits, int32_t group_size,
+                           int32_t w_layout, int32_t splits, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Split-KV attention: arguments of bi_sdpa, plus `splits` >= 1.  The chunks
+ * of max_kv_len keys (256 each, nch of them) are cut into runs of
+ * cps = ceil(nch / min(splits, nch)) chunks; one workgroup walks a run in
+ * order with the softmax state carried across its chunks (the chunk tree of
+ * bi_sdpa inside each chunk), and the runs' (o, m, l) are merged by
+ * bi_sdpa's merge kernel.  A single run writes the output directly (no
+ * workspace, one launch).  splits >= nch gives runs of one chunk: bi_sdpa's
+ * bits.  Requires Q * (Hq / Hkv) <= 16 (one 16-row query tile per sequence
+ * and KV head), else BI_ERR_UNSUPPORTED.  Workspace:
+ * bi_sdpa_split_workspace_bytes(B, Q, max_kv_len, Hq, D, splits) bytes (0 for
+ * a single run; ws may then be NULL), 16-byte aligned.
+ * Source: "Batch-invariant kernels ...", Case 6 (Split-KV: a split count
+ * that follows the shape); "Fix/speculative shape invariance", Problem (a
+ * split count derived from the query length). */
+size_t bi_sdpa_split_workspace_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int32_t Hq, int32_t D,
+                                     int32_t splits);
+bi_status bi_sdpa_split(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len,
+                        int64_t max_kv_len, int64_t B, int64_t Q, int64_t Lcap, int32_t Hq, int32_t Hkv,
+                        int32_t D, float scale, int32_t causal, int32_t dtype, int32_t kv_layout, int32_t splits,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Measurement hooks (not part of any computation): the next kernel (or the

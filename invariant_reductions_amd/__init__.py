@@ -21,7 +21,7 @@ __all__ = [
     "matmul", "matmul_ws", "matmul_workspace", "matmul_swiglu", "matmul_swiglu_workspace", "interleave_gate_up",
     "PackedWeight", "pack_weights", "pack_qweights", "log_softmax", "token_logprob", "row_mean",
     "qmatmul", "rmsnorm", "add_rmsnorm", "sdpa", "sdpa_workspace_bytes", "sdpa_noalloc",
-    "matmul_split", "rmsnorm_split",
+    "matmul_split", "rmsnorm_split", "qmatmul_split", "sdpa_split",
     "embed", "rope_kv_write", "silu_mul", "add", "argmax",
     "BF16", "F16", "F32", "AFFINE", "NVFP4",
 ]
@@ -81,6 +81,8 @@ def lib():
             "bi_token_logprob": [P, P, P, I64, I64, I32, P],
             "bi_row_mean": [P, P, I64, I64, I32, P],
             "bi_rmsnorm_split": [P, P, P, I64, I64, F, I32, I32, P, SZ, P],
+            "bi_qmatmul_split": [P, P, P, P, P, I64, I64, I64, I32, I32, I32, I32, I32, P, SZ, P],
+            "bi_sdpa_split": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, I32, I32, P, SZ, P],
             "bi_probe_read": [P, SZ, P, I32, P],
             "bi_probe_copy": [P, P, SZ, I32, P],
             "bi_probe_mfma": [P, I32, I64, P],
@@ -105,6 +107,10 @@ def lib():
         L.bi_matmul_split_workspace_bytes.restype = SZ
         L.bi_rmsnorm_split_workspace_bytes.argtypes = [I64, I32]
         L.bi_rmsnorm_split_workspace_bytes.restype = SZ
+        L.bi_qmatmul_split_workspace_bytes.argtypes = [I64, I64, I32]
+        L.bi_qmatmul_split_workspace_bytes.restype = SZ
+        L.bi_sdpa_split_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, I32]
+        L.bi_sdpa_split_workspace_bytes.restype = SZ
         L.bi_time_next_launch.argtypes = [P, P]
         L.bi_time_next_launch.restype = ctypes.c_int32
         L.bi_time_next_launches.argtypes = [P, P, I32]
@@ -300,6 +306,23 @@ def qmatmul(x, wq, scales, biases, N: int, K: int, qmode: int, group_size: int, 
     return y
 
 
+def qmatmul_split(x, wq, scales, biases, N: int, K: int, qmode: int, group_size: int, splits: int,
+                  transposed: bool = True, out=None, ws=None, stream=None, packed: bool = False, bits: int = 4):
+    """Non-invariant split-K comparison variant of qmatmul (see include/bi.h)."""
+    _dev(x, wq, scales, biases, out, ws)
+    M = x.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=x.device)
+    need = lib().bi_qmatmul_split_workspace_bytes(M, N, splits)
+    if ws is None and splits > 1:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    layout = W_PACKED if packed else (W_TRANSPOSED if transposed else W_NATURAL)
+    _check(lib().bi_qmatmul_split(_ptr(x), _ptr(wq), _ptr(scales), _ptr(biases), _ptr(y), M, N, K, qmode, bits,
+                                  group_size, layout, splits, _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "bi_qmatmul_split")
+    return y
+
+
 def gather_qmatmul(x, lhs, rhs, wq, scales, biases, N: int, K: int, qmode: int, group_size: int,
                    transposed: bool = True, out=None, stream=None, bits: int = 4, packed: bool = False):
     """Expert matmul: y[m] = x[lhs[m]] @ dequantize(W[rhs[m]])^T; x float16
@@ -387,6 +410,27 @@ def sdpa(q, k, v, kv_len, max_kv_len: int, scale: float, causal: bool = True, ou
     _check(lib().bi_sdpa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_len), max_kv_len, B, Q, Lcap, Hq, Hkv, D,
                          scale, int(causal), _dt(q), int(head_major), _ptr(ws), ws.numel() * ws.element_size(),
                          _stream(stream)), "bi_sdpa")
+    return o
+
+
+def sdpa_split(q, k, v, kv_len, max_kv_len: int, scale: float, splits: int, causal: bool = True, out=None,
+               ws=None, stream=None, head_major: bool = False):
+    """Non-invariant split-KV comparison variant of sdpa (see include/bi.h)."""
+    _dev(q, k, v, kv_len, out, ws)
+    B, Q, Hq, D = q.shape
+    if head_major:
+        _, Hkv, Lcap, _ = k.shape
+    else:
+        _, Lcap, Hkv, _ = k.shape
+    if kv_len.dtype != torch.int32:
+        raise ValueError("kv_len must be int32")
+    o = out if out is not None else torch.empty_like(q)
+    need = lib().bi_sdpa_split_workspace_bytes(B, Q, max_kv_len, Hq, D, splits)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().bi_sdpa_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv_len), max_kv_len, B, Q, Lcap, Hq, Hkv, D,
+                               scale, int(causal), _dt(q), int(head_major), splits, _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "bi_sdpa_split")
     return o
 
 

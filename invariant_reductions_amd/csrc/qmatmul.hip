@@ -356,18 +356,23 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
 // wave partials are added in wave order.
 constexpr int kQXRes = 4;
 
-template <int QM, int GS, int NS, int D, bool XR, bool PK>
+template <int QM, int GS, int NS, int D, bool XR, bool PK, bool SPL = false>
 __global__ __launch_bounds__(kQWaves * kWave, 2)
 void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wqp,
                        const void *__restrict__ scales, const uint16_t *__restrict__ biases, uint16_t *__restrict__ y,
-                       int M, int N, int K, int ntn, int per)
+                       int M, int N, int K, int ntn, int per, float *__restrict__ part, int splits)
 {
     constexpr int P = kQWaves, TC = NS * 16, CB = qconst_chunk_bytes(QM, GS);
     __shared__ float red[P][16][TC + 1];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int nb = K / kQBlock, nrg = (N + 15) / 16;
-    const int nmine = wave < nb ? (nb - wave + P - 1) / P : 0;          // blocks of this wave per tile
+    // The split comparison variant (SPL) reduces only the contiguous blocks
+    // [kb0, kb1) of split blockIdx.y and writes fp32 partials; the invariant
+    // kernel always covers every block.
+    const int kb0 = SPL ? (int)((int64_t)blockIdx.y * nb / splits) : 0;
+    const int nbl = SPL ? (int)((int64_t)(blockIdx.y + 1) * nb / splits) - kb0 : nb;
+    const int nmine = wave < nbl ? (nbl - wave + P - 1) / P : 0;        // blocks of this wave per tile
     const int t0 = (int)blockIdx.x * per;
     const int ntile = max(0, min(ntn, t0 + per) - t0);
     const int items = ntile * nmine;
@@ -389,13 +394,13 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
             if (j < nmine) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    X[j][s] = *reinterpret_cast<const uint4 *>(xr + (wave + j * P) * kQBlock + s * 8);
+                    X[j][s] = *reinterpret_cast<const uint4 *>(xr + (kb0 + wave + j * P) * kQBlock + s * 8);
             }
     }
     int lu = 0, lj = 0;                                     // load cursor: tile t0 + lu, block wave + lj*P
     auto load_item = [&](auto dc_) {
         constexpr int d = decltype(dc_)::value;
-        const int b = wave + lj * P;
+        const int b = kb0 + wave + lj * P;
 #pragma unroll
         for (int jj = 0; jj < NS; ++jj) {
             const int rg = min((t0 + lu) * NS + jj, nrg - 1);
@@ -445,7 +450,8 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
             float v = red[0][r][cc];
 #pragma unroll
             for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
-            y[(int64_t)r * N + n0 + cc] = F16::narrow(v);
+            if constexpr (SPL) part[((int64_t)blockIdx.y * M + r) * N + n0 + cc] = v;
+            else y[(int64_t)r * N + n0 + cc] = F16::narrow(v);
         }
         __syncthreads();
     };
@@ -520,11 +526,11 @@ static void launch_q_stream_t(const void *x, const uint32_t *wq, const void *s, 
     if (xres)
         launch_kernel((qmatmul_stream_kernel<QM, GS, NS, 3, true, PK>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0, st,
                       (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, (int)M, (int)N, (int)K, (int)ntn,
-                      (int)per);
+                      (int)per, (float *)nullptr, 1);
     else
         launch_kernel((qmatmul_stream_kernel<QM, GS, NS, 3, false, PK>), dim3((unsigned)grid), dim3(kQWaves * kWave), 0,
                       st, (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, (int)M, (int)N, (int)K,
-                      (int)ntn, (int)per);
+                      (int)ntn, (int)per, (float *)nullptr, 1);
 }
 
 template <int QM, int GS, bool PK>
@@ -536,6 +542,38 @@ static bool try_launch_q_stream(const void *x, const uint32_t *wq, const void *s
         return false;
     launch_q_stream_t<QM, GS, 1, PK>(x, wq, s, b, y, M, N, K, st);
     return true;
+}
+
+// Split-K comparison variant of the streaming kernel: split z reduces the
+// contiguous blocks [z nb / splits, (z + 1) nb / splits) into fp32 partials
+// [splits, M, N], which q_split_reduce_kernel adds in z order.  The tree then
+// depends on `splits` -- the batch-dependent split-K the invariant kernel
+// exists to avoid -- so it serves only to price invariance.
+template <int QM, int GS, bool PK>
+static void launch_q_split(const void *x, const uint32_t *wq, const void *s, const void *b, float *part, int64_t M,
+                           int64_t N, int64_t K, int splits, hipStream_t st)
+{
+    const int64_t ntn = cdiv(N, 16), slots = (int64_t)device_cu_count() * 2;
+    const int64_t per = cdiv(ntn * splits, slots), grid = cdiv(ntn, per);
+    const bool xres = cdiv(cdiv(K / kQBlock, splits), kQWaves) <= kQXRes;
+    const dim3 g((unsigned)grid, (unsigned)splits);
+    if (xres)
+        launch_kernel((qmatmul_stream_kernel<QM, GS, 1, 3, true, PK, true>), g, dim3(kQWaves * kWave), 0, st,
+                      (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)nullptr, (int)M, (int)N, (int)K,
+                      (int)ntn, (int)per, part, splits);
+    else
+        launch_kernel((qmatmul_stream_kernel<QM, GS, 1, 3, false, PK, true>), g, dim3(kQWaves * kWave), 0, st,
+                      (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)nullptr, (int)M, (int)N, (int)K,
+                      (int)ntn, (int)per, part, splits);
+}
+
+__global__ void q_split_reduce_kernel(const float *__restrict__ part, uint16_t *__restrict__ y, int64_t MN, int splits)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += (int64_t)gridDim.x * blockDim.x) {
+        float v = part[i];
+        for (int z = 1; z < splits; ++z) v = v + part[(int64_t)z * MN + i];
+        y[i] = F16::narrow(v);
+    }
 }
 
 template <int QM, int GS, bool TRANS, bool WVEC, int MT, bool PK>
@@ -1004,6 +1042,62 @@ extern "C" bi_status bi_qmatmul(const void *x, const uint32_t *wq, const void *s
     else if (group_size == 32) launch_q<BI_AFFINE, 32>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
     else if (group_size == 64) launch_q<BI_AFFINE, 64>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
     else launch_q<BI_AFFINE, 128>(x, wq, scales, biases, y, M, N, K, w_layout, stream);
+    return launch_status();
+}
+
+extern "C" size_t bi_qmatmul_split_workspace_bytes(int64_t M, int64_t N, int32_t splits)
+{
+    if (M < 1 || N < 1 || splits < 1 || M > (1ll << 31) || N > (1ll << 31)) return 0;
+    return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
+extern "C" bi_status bi_qmatmul_split(const void *x, const uint32_t *wq, const void *scales, const void *biases,
+                                      void *y, int64_t M, int64_t N, int64_t K, int32_t qmode, int32_t bits,
+                                      int32_t group_size, int32_t w_layout, int32_t splits, void *ws, size_t ws_bytes,
+                                      hipStream_t stream)
+{
+    if (splits < 1 || splits > 1024) return BI_ERR_SHAPE;
+    if (splits == 1)
+        return bi_qmatmul(x, wq, scales, biases, y, M, N, K, qmode, bits, group_size, w_layout, stream);
+    // validation of the operands first (the invariant entry point's rules)
+    const bool packed = w_layout == 2;
+    if (!x || !wq || !y || (!scales && !packed)) return BI_ERR_NULL;
+    if (M < 1 || N < 1 || K < 1 || M > (1ll << 31) || N > (1ll << 31) || K > (1ll << 31)) return BI_ERR_SHAPE;
+    if (w_layout < 0 || w_layout > 2) return BI_ERR_SHAPE;
+    const bi_status qs = check_qmode(qmode, bits, group_size);
+    if (qs != BI_OK) return qs;
+    if (!packed) {
+        if (qmode == BI_AFFINE && !biases) return BI_ERR_NULL;
+        if (qmode != BI_AFFINE && biases) return BI_ERR_GROUP;
+    }
+    if ((w_layout ? K : N) % group_size) return BI_ERR_GROUP;
+    // the split form exists for the streaming decode kernel's shapes only
+    if (!four_bit_mode(qmode, bits) || w_layout == 0 || M > 16 || K % kQBlock || N >= (1ll << 30) ||
+        K >= (1ll << 30))
+        return BI_ERR_UNSUPPORTED;
+    if (splits > K / kQBlock) return BI_ERR_SHAPE;
+    if ((((uintptr_t)x | (uintptr_t)y) & 1u) || !host_aligned16(x) || !host_aligned16(wq) ||
+        (!packed && (((uintptr_t)scales & 1u) || ((uintptr_t)biases & 1u))))
+        return BI_ERR_ALIGN;
+    if (!ws || ws_bytes < bi_qmatmul_split_workspace_bytes(M, N, splits)) return BI_ERR_WORKSPACE;
+    if (!host_aligned16(ws)) return BI_ERR_ALIGN;
+    (void)hipGetLastError();
+    float *part = (float *)ws;
+    const void *s = scales, *b = biases;
+#define BI_QSPLIT(QM_, GS_)                                                                            \
+    do {                                                                                              \
+        if (packed) launch_q_split<QM_, GS_, true>(x, wq, s, b, part, M, N, K, splits, stream);       \
+        else launch_q_split<QM_, GS_, false>(x, wq, s, b, part, M, N, K, splits, stream);             \
+    } while (0)
+    if (qmode == BI_NVFP4) BI_QSPLIT(BI_NVFP4, 16);
+    else if (qmode == BI_MXFP4) BI_QSPLIT(BI_MXFP4, 32);
+    else if (group_size == 32) BI_QSPLIT(BI_AFFINE, 32);
+    else if (group_size == 64) BI_QSPLIT(BI_AFFINE, 64);
+    else BI_QSPLIT(BI_AFFINE, 128);
+#undef BI_QSPLIT
+    const int64_t MN = M * N;
+    launch_kernel(q_split_reduce_kernel, dim3((unsigned)std::min<int64_t>(cdiv(MN, 256), 65536)), dim3(256), 0, stream,
+                  (const float *)part, (uint16_t *)y, MN, (int)splits);
     return launch_status();
 }
 

@@ -74,6 +74,7 @@ struct AttnShape {
     float scale;
     int causal;
     int64_t ks, hs;       // cache strides (elements) between consecutive keys and between KV heads
+    int cps;              // chunks per partial: 1 (the invariant tree); the split variant's run length
 };
 
 struct AttnBufs {
@@ -147,7 +148,15 @@ __device__ inline void attn_store_out(uint16_t *dst, float4 o, float l)
 //        transposed in place to vr[s2][j] = those 8 keys at d = 8 c16 + j,
 //        the MFMA B operand of P . V (k slot 8 g4 + e of step s2 = key
 //        32 s2 + 8 g4 + e, column c16 = d 8 c16 + j of output tile j).
-template <typename S, bool MG>
+//
+// SPL: the split comparison variant (one 16-row tile per item, nmg == 1).
+// Its item is a run of sh.cps consecutive chunks -- a split whose length
+// follows the caller's split count -- walked in order by one workgroup with
+// the softmax state carried across chunks (o and l rescaled to the running
+// max); the split's (o, m, l) is the partial, or with a single split the
+// output itself.  The tree then depends on the split count; it exists only
+// to price the invariant tree.
+template <typename S, bool MG, bool SPL = false>
 __global__ __launch_bounds__(kAttnWaves * kWave, 2)
 void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, int64_t nid)
 {
@@ -185,7 +194,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
         const int64_t bc = (t >> 3) / sh.Hkv * 8 + (t & 7);
         const bool exists = bc < nitems;
         it.b = exists ? (int)(bc / sh.nchunks) : 0;
-        it.c = exists ? (int)(bc - (int64_t)it.b * sh.nchunks) : -1;
+        it.c = exists ? (int)(bc - (int64_t)it.b * sh.nchunks) * (SPL ? sh.cps : 1) : -1;
         it.kvlen = seq_len(it.b);
         return it;
     };
@@ -263,185 +272,262 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
         load_v(it, vr);
     }
     while (t < nid) {
-        const Item it = decode(t);
-        const int key0 = it.c * kChunk;
-        const int wkey0 = key0 + wave * kKeysPerWave;
+        Item it = decode(t);
         int r0, r1;
         group_rows(it, r0, r1);
         const int mt0 = r0 / 16, mt1 = (r1 + 15) / 16;
         const int64_t tn = next_id(t + gridDim.x);
-        bool prefetched = false;                       // the next item's K and q are requested
-        bool vready = false;                           // this item's V is in P . V operand form
+        // SPL: the split's chunks it.c .. clast in order, with the running
+        // softmax state of row threadIdx.x / 16, d in [8 (threadIdx.x % 16), +8)
+        const int split = SPL ? it.c / sh.cps : 0;
+        const int clast = SPL ? min(it.c + sh.cps - 1, group_last_key(it) / kChunk) : it.c;
+        float rM = -INFINITY, rl = 0.0f, ro[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ro[e] = 0.0f;
+        // one chunk of the item; `more`: another chunk of this split follows
+        auto chunk = [&](const bool more) {
+            const bool has_next = more || tn < nid;
+            auto next_item = [&]() {
+                if (SPL && more) {
+                    Item nx = it;
+                    ++nx.c;
+                    return nx;
+                }
+                return decode(tn);
+            };
+            const int key0 = it.c * kChunk;
+            const int wkey0 = key0 + wave * kKeysPerWave;
+            bool prefetched = false;                       // the next item's K and q are requested
+            bool vready = false;                           // this item's V is in P . V operand form
 
-        // One 16-row query tile against this chunk.  The first tile runs on
-        // the q rows requested with the item; later tiles (verify blocks and
-        // prompts of more than 16 rows per head) request theirs first.  The
-        // first call is separate from the loop so that the waits of the
-        // common one-tile case count only the loads that precede its q.
-        auto run_tile = [&](const int mt) {
-            // Rows of the accumulator layout held by this lane: 4 g4 + i.
-            int lastk[4];
-            bool rowok[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = mt * 16 + g4 * 4 + i;
-                rowok[i] = r < R;
-                lastk[i] = rowok[i] ? last_key(it.kvlen, r / sh.G) : -1;
-                rowok[i] = rowok[i] && lastk[i] >= key0;
-            }
-            // Tile-uniform skip: no row of this tile reaches this chunk.
-            const int rlast = mt * 16 + 15 < R ? mt * 16 + 15 : R - 1;
-            const bool any = last_key(it.kvlen, rlast / sh.G) >= key0;
-            if (!any) return;
-
-            // scores: tile kt -> lane (g4, c16) reg i = row 4 g4 + i, key wkey0 + 16 kt + c16
-            float sc[4][4];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mfma16<S>(qf[s], kf[kt][s], acc);
-                const int key = wkey0 + kt * 16 + c16;
+            // One 16-row query tile against this chunk.  The first tile runs on
+            // the q rows requested with the item; later tiles (verify blocks and
+            // prompts of more than 16 rows per head) request theirs first.  The
+            // first call is separate from the loop so that the waits of the
+            // common one-tile case count only the loads that precede its q.
+            auto run_tile = [&](const int mt) {
+                // Rows of the accumulator layout held by this lane: 4 g4 + i.
+                int lastk[4];
+                bool rowok[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool vis = rowok[i] && key <= lastk[i];
-                    sc[kt][i] = vis ? acc[i] * sh.scale : -INFINITY;
+                    const int r = mt * 16 + g4 * 4 + i;
+                    rowok[i] = r < R;
+                    lastk[i] = rowok[i] ? last_key(it.kvlen, r / sh.G) : -1;
+                    rowok[i] = rowok[i] && lastk[i] >= key0;
                 }
-            }
-            // the next item's K and first q tile: requested once the last tile
-            // has read this item's
-            if (mt == mt1 - 1 && tn < nid) {
-                const Item nx = decode(tn);
-                load_k(nx, kf);
-                load_q(nx, MG ? nx.mg * sh.mgt : 0, qf);
-                prefetched = true;
-            }
+                // Tile-uniform skip: no row of this tile reaches this chunk.
+                const int rlast = mt * 16 + 15 < R ? mt * 16 + 15 : R - 1;
+                const bool any = last_key(it.kvlen, rlast / sh.G) >= key0;
+                if (!any) return;
 
-            // chunk max per row
-            float mx[4];
+                // scores: tile kt -> lane (g4, c16) reg i = row 4 g4 + i, key wkey0 + 16 kt + c16
+                float sc[4][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float m = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
+                for (int kt = 0; kt < 4; ++kt) {
+                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-                mx[i] = m;
-            }
-            if (c16 == 0) {
+                    for (int s = 0; s < 4; ++s) acc = mfma16<S>(qf[s], kf[kt][s], acc);
+                    const int key = wkey0 + kt * 16 + c16;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xm[wave][g4 * 4 + i] = mx[i];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = g4 * 4 + i;
-                mx[i] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
-            }
-            // probabilities, row sums, and the P tile as hi and lo 16-bit parts
-            float ls[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ls[i] = 0.0f;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+                    for (int i = 0; i < 4; ++i) {
+                        const bool vis = rowok[i] && key <= lastk[i];
+                        sc[kt][i] = vis ? acc[i] * sh.scale : -INFINITY;
+                    }
+                }
+                // the next item's K and first q tile: requested once the last tile
+                // has read this item's
+                if (mt == mt1 - 1 && has_next) {
+                    const Item nx = next_item();
+                    load_k(nx, kf);
+                    load_q(nx, MG ? nx.mg * sh.mgt : 0, qf);
+                    prefetched = true;
+                }
+
+                // chunk max per row
+                float mx[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool vis = sc[kt][i] != -INFINITY;
-                    const float pv = vis ? expf(sc[kt][i] - mx[i]) : 0.0f;
-                    ls[i] = ls[i] + pv;
-                    const uint16_t hi = S::narrow(pv);
-                    phi[wave][g4 * 4 + i][kt * 16 + c16] = hi;
-                    plo[wave][g4 * 4 + i][kt * 16 + c16] = S::narrow(pv - S::widen(hi));
+                    float m = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+                    mx[i] = m;
+                }
+                if (c16 == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xm[wave][g4 * 4 + i] = mx[i];
+                }
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = g4 * 4 + i;
+                    mx[i] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
+                }
+                // probabilities, row sums, and the P tile as hi and lo 16-bit parts
+                float ls[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ls[i] = 0.0f;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool vis = sc[kt][i] != -INFINITY;
+                        const float pv = vis ? expf(sc[kt][i] - mx[i]) : 0.0f;
+                        ls[i] = ls[i] + pv;
+                        const uint16_t hi = S::narrow(pv);
+                        phi[wave][g4 * 4 + i][kt * 16 + c16] = hi;
+                        plo[wave][g4 * 4 + i][kt * 16 + c16] = S::narrow(pv - S::widen(hi));
+                    }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float l = ls[i];
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) l = l + __shfl_xor(l, off, kWave);
+                    ls[i] = l;
+                }
+                if (c16 == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xl[wave][g4 * 4 + i] = ls[i];
+                }
+                __syncthreads();
+                // this item's V as the P . V B operand (its loads had the scores
+                // and the softmax to arrive)
+                if (!vready) {
+                    const int nv = wave_valid(it);
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (s2 * 32 + g4 * 8 + e >= nv) vr[s2][e] = zero4;   // p is 0 there; keep 0 * v exact
+                    transpose8x8_b16(vr[0]);
+                    transpose8x8_b16(vr[1]);
+                    vready = true;
+                }
+                // o partial of this wave: P (16 x 64) . V (64 x 128), lo parts first
+                uint4 ph[2], pq[2];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    ph[s2] = *reinterpret_cast<const uint4 *>(&phi[wave][c16][s2 * 32 + g4 * 8]);
+                    pq[s2] = *reinterpret_cast<const uint4 *>(&plo[wave][c16][s2 * 32 + g4 * 8]);
                 }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float l = ls[i];
+                for (int j = 0; j < 8; ++j) {
+                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int off = 1; off < 16; off <<= 1) l = l + __shfl_xor(l, off, kWave);
-                ls[i] = l;
-            }
-            if (c16 == 0) {
+                    for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(pq[s2], vr[s2][j], acc);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xl[wave][g4 * 4 + i] = ls[i];
-            }
-            __syncthreads();
-            // this item's V as the P . V B operand (its loads had the scores
-            // and the softmax to arrive)
-            if (!vready) {
-                const int nv = wave_valid(it);
+                    for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(ph[s2], vr[s2][j], acc);
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
+                    for (int i = 0; i < 4; ++i) ol[wave][g4 * 4 + i][c16 * 8 + j] = acc[i];
+                }
+                __syncthreads();
+                // combine the four wave partials in order and write this chunk's
+                // partial: thread -> row t / 16 of the tile, d in [8 (t % 16), +8)
+                if constexpr (SPL) {
+                    // fold the chunk into the split's running state instead
+                    const int rr = threadIdx.x >> 4, dg = threadIdx.x & 15;
+                    const int r = mt * 16 + rr;
+                    if (r < R && last_key(it.kvlen, r / sh.G) >= key0) {
+                        float oc[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (s2 * 32 + g4 * 8 + e >= nv) vr[s2][e] = zero4;   // p is 0 there; keep 0 * v exact
-                transpose8x8_b16(vr[0]);
-                transpose8x8_b16(vr[1]);
-                vready = true;
-            }
-            // o partial of this wave: P (16 x 64) . V (64 x 128), lo parts first
-            uint4 ph[2], pq[2];
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                ph[s2] = *reinterpret_cast<const uint4 *>(&phi[wave][c16][s2 * 32 + g4 * 8]);
-                pq[s2] = *reinterpret_cast<const uint4 *>(&plo[wave][c16][s2 * 32 + g4 * 8]);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(pq[s2], vr[s2][j], acc);
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(ph[s2], vr[s2][j], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ol[wave][g4 * 4 + i][c16 * 8 + j] = acc[i];
-            }
-            __syncthreads();
-            // combine the four wave partials in order and write this chunk's
-            // partial: thread -> row t / 16 of the tile, d in [8 (t % 16), +8)
-            {
-                const int rr = threadIdx.x >> 4, dg = threadIdx.x & 15;
-                const int r = mt * 16 + rr;
-                if (r < R) {
-                    const int j = r / sh.G;
-                    if (last_key(it.kvlen, j) >= key0) {
-                        const int64_t h = (int64_t)it.hk * sh.G + (r - j * sh.G);
-                        float *dst = bf.part + ((((int64_t)it.b * sh.Q + j) * sh.Hq + h) * sh.nchunks + it.c) * kPartStride;
-#pragma unroll
-                        for (int half = 0; half < 2; ++half) {
-                            const int d = dg * 8 + half * 4;
-                            const float4 o0 = *reinterpret_cast<const float4 *>(&ol[0][rr][d]);
-                            const float4 o1 = *reinterpret_cast<const float4 *>(&ol[1][rr][d]);
-                            const float4 o2 = *reinterpret_cast<const float4 *>(&ol[2][rr][d]);
-                            const float4 o3 = *reinterpret_cast<const float4 *>(&ol[3][rr][d]);
-                            float4 o;
-                            o.x = ((o0.x + o1.x) + o2.x) + o3.x;
-                            o.y = ((o0.y + o1.y) + o2.y) + o3.y;
-                            o.z = ((o0.z + o1.z) + o2.z) + o3.z;
-                            o.w = ((o0.w + o1.w) + o2.w) + o3.w;
-                            *reinterpret_cast<float4 *>(dst + d) = o;
+                        for (int e = 0; e < 8; ++e) {
+                            const int d = dg * 8 + e;
+                            oc[e] = ((ol[0][rr][d] + ol[1][rr][d]) + ol[2][rr][d]) + ol[3][rr][d];
                         }
-                        if (dg == 0) {
-                            dst[kHeadDim] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
-                            dst[kHeadDim + 1] = ((xl[0][rr] + xl[1][rr]) + xl[2][rr]) + xl[3][rr];
+                        const float mc = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
+                        const float lc = ((xl[0][rr] + xl[1][rr]) + xl[2][rr]) + xl[3][rr];
+                        if (rM == -INFINITY) {
+                            rM = mc;
+                            rl = lc;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) ro[e] = oc[e];
+                        } else {
+                            const float mn = fmaxf(rM, mc), a = expf(rM - mn), bw = expf(mc - mn);
+                            rl = rl * a + lc * bw;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) ro[e] = ro[e] * a + oc[e] * bw;
+                            rM = mn;
+                        }
+                    }
+                } else {
+                    const int rr = threadIdx.x >> 4, dg = threadIdx.x & 15;
+                    const int r = mt * 16 + rr;
+                    if (r < R) {
+                        const int j = r / sh.G;
+                        if (last_key(it.kvlen, j) >= key0) {
+                            const int64_t h = (int64_t)it.hk * sh.G + (r - j * sh.G);
+                            float *dst = bf.part +
+                                         ((((int64_t)it.b * sh.Q + j) * sh.Hq + h) * sh.nchunks + it.c) * kPartStride;
+#pragma unroll
+                            for (int half = 0; half < 2; ++half) {
+                                const int d = dg * 8 + half * 4;
+                                const float4 o0 = *reinterpret_cast<const float4 *>(&ol[0][rr][d]);
+                                const float4 o1 = *reinterpret_cast<const float4 *>(&ol[1][rr][d]);
+                                const float4 o2 = *reinterpret_cast<const float4 *>(&ol[2][rr][d]);
+                                const float4 o3 = *reinterpret_cast<const float4 *>(&ol[3][rr][d]);
+                                float4 o;
+                                o.x = ((o0.x + o1.x) + o2.x) + o3.x;
+                                o.y = ((o0.y + o1.y) + o2.y) + o3.y;
+                                o.z = ((o0.z + o1.z) + o2.z) + o3.z;
+                                o.w = ((o0.w + o1.w) + o2.w) + o3.w;
+                                *reinterpret_cast<float4 *>(dst + d) = o;
+                            }
+                            if (dg == 0) {
+                                dst[kHeadDim] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
+                                dst[kHeadDim + 1] = ((xl[0][rr] + xl[1][rr]) + xl[2][rr]) + xl[3][rr];
+                            }
                         }
                     }
                 }
+                __syncthreads();
+            };
+            run_tile(mt0);
+            for (int mt = mt0 + 1; mt < mt1; ++mt) {
+                load_q(it, mt, qf);
+                run_tile(mt);
             }
-            __syncthreads();
+            // The group's last row, in the last tile, sees key0 (the item has
+            // work), so the last tile is never skipped and the next item's K and q
+            // are already in flight; this is the fallback should it ever be.
+            if (!prefetched && has_next) {
+                const Item nx = next_item();
+                load_k(nx, kf);
+                load_q(nx, MG ? nx.mg * sh.mgt : 0, qf);
+            }
+            // the next item's V (its K and q are in flight since this item's scores)
+            if (has_next) load_v(next_item(), vr);
         };
-        run_tile(mt0);
-        for (int mt = mt0 + 1; mt < mt1; ++mt) {
-            load_q(it, mt, qf);
-            run_tile(mt);
+        if constexpr (SPL) {
+            for (;;) {
+                const bool more = it.c < clast;
+                chunk(more);
+                if (!more) break;
+                ++it.c;
+            }
+        } else {
+            chunk(false);
         }
-        // The group's last row, in the last tile, sees key0 (the item has
-        // work), so the last tile is never skipped and the next item's K and q
-        // are already in flight; this is the fallback should it ever be.
-        if (!prefetched && tn < nid) {
-            const Item nx = decode(tn);
-            load_k(nx, kf);
-            load_q(nx, MG ? nx.mg * sh.mgt : 0, qf);
+        if constexpr (SPL) {
+            // the split's partial (o, m, l), or with one split the output
+            const int rr = threadIdx.x >> 4, dg = threadIdx.x & 15;
+            const int r = mt0 * 16 + rr;
+            if (r < R && rM != -INFINITY) {
+                const int j = r / sh.G;
+                const int64_t row = ((int64_t)it.b * sh.Q + j) * sh.Hq + (int64_t)it.hk * sh.G + (r - j * sh.G);
+                if (sh.nchunks == 1) {
+                    attn_store_out<S>(bf.o + row * kHeadDim + dg * 8, make_float4(ro[0], ro[1], ro[2], ro[3]), rl);
+                    attn_store_out<S>(bf.o + row * kHeadDim + dg * 8 + 4, make_float4(ro[4], ro[5], ro[6], ro[7]), rl);
+                } else {
+                    float *dst = bf.part + (row * sh.nchunks + split) * kPartStride;
+                    *reinterpret_cast<float4 *>(dst + dg * 8) = make_float4(ro[0], ro[1], ro[2], ro[3]);
+                    *reinterpret_cast<float4 *>(dst + dg * 8 + 4) = make_float4(ro[4], ro[5], ro[6], ro[7]);
+                    if (dg == 0) {
+                        dst[kHeadDim] = rM;
+                        dst[kHeadDim + 1] = rl;
+                    }
+                }
+            }
         }
-        // the next item's V (its K and q are in flight since this item's scores)
-        if (tn < nid) load_v(decode(tn), vr);
         t = tn;
     }
 }
@@ -475,7 +561,7 @@ void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict
     const int nthr = blockDim.x, slots = nthr / 32;
     const int quad = threadIdx.x & 31, slot = threadIdx.x >> 5;
     if (lk < 0) return;                                   // a bad kv_len: nothing this row may read
-    const int nch = lk / kChunk + 1, nr = (nch + kRange - 1) / kRange;
+    const int nch = lk / (kChunk * sh.cps) + 1, nr = (nch + kRange - 1) / kRange;
     const float *pr = part + row * sh.nchunks * kPartStride;
 
     // M = max over the chunk maxima: read first when the row's ranges take
@@ -599,8 +685,10 @@ struct AttnPlan {
     size_t parts;
 };
 
+// cps: chunks per partial -- 1 for the invariant tree; the split variant's
+// run length (its partials are then per split).
 static AttnPlan attn_plan(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Lcap, int32_t Hq, int32_t Hkv,
-                          float scale, int32_t causal, int32_t kv_layout)
+                          float scale, int32_t causal, int32_t kv_layout, int cps = 1)
 {
     const int64_t D = kHeadDim;
     // kv_layout 0: [B, Lcap, Hkv, D]; 1: [B, Hkv, Lcap, D] (head-major)
@@ -613,17 +701,17 @@ static AttnPlan attn_plan(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Lcap
     const int64_t ntm = cdiv(Q * G, 16), nbase = cdiv(B * cdiv(max_kv_len, kChunk), 8) * 8 * Hkv;
     const int64_t ngroups = nbase >= 1024 ? 1 : std::max<int64_t>(1, cdiv(4096, nbase));
     const int64_t mgt = std::min<int64_t>(std::max<int64_t>(kAttnMinTiles, cdiv(ntm, ngroups)), ntm);
-    const int64_t nch = cdiv(max_kv_len, kChunk);
+    const int64_t nch = cdiv(cdiv(max_kv_len, kChunk), cps);            // partials per row
     AttnPlan p;
     p.sh = AttnShape{B, Q, Lcap, nch, cdiv(nch, kRange), max_kv_len, cdiv(ntm, mgt), Hq, Hkv, (int)G, (int)mgt,
-                     scale, causal ? 1 : 0, ks, hs};
+                     scale, causal ? 1 : 0, ks, hs, cps};
     // item ids (padded to whole groups of 8); a persistent grid of two
     // workgroups per CU, a multiple of 8 so that a workgroup stays on one XCD
     p.nid = cdiv(B * nch, 8) * 8 * Hkv * p.sh.nmg;
     p.grid = std::min<int64_t>(p.nid, (int64_t)device_cu_count() * 2 / 8 * 8);
     // merge: 32 threads per range of the longest row, whole waves, at most kMergeRanges ranges at once
     p.merge_threads = cdiv(32 * std::min<int64_t>(p.sh.nranges, kMergeRanges), kWave) * kWave;
-    p.parts = attn_partial_bytes(B, Q, max_kv_len, Hq);
+    p.parts = (size_t)(B * Q * Hq) * (size_t)nch * kPartStride * sizeof(float);
     return p;
 }
 
@@ -638,6 +726,18 @@ static void launch_attn(const AttnBufs &bf, const AttnPlan &p, hipStream_t st)
                       p.sh, p.nid);
     launch_kernel((attn_merge_kernel<S>), dim3((unsigned)(p.sh.B * p.sh.Q * p.sh.Hq)), dim3((unsigned)p.merge_threads),
                   0, st, (const float *)bf.part, bf.kv_len, bf.o, p.sh);
+}
+
+// The split comparison variant: the chunk kernel in its SPL form, then the
+// merge over the splits (none with a single split: the kernel wrote out).
+template <typename S>
+static void launch_attn_split(const AttnBufs &bf, const AttnPlan &p, hipStream_t st)
+{
+    launch_kernel((attn_kernel<S, false, true>), dim3((unsigned)p.grid), dim3(kAttnWaves * kWave), 0, st, bf, bf.kv_len,
+                  p.sh, p.nid);
+    if (p.sh.nchunks > 1)
+        launch_kernel((attn_merge_kernel<S>), dim3((unsigned)(p.sh.B * p.sh.Q * p.sh.Hq)),
+                      dim3((unsigned)p.merge_threads), 0, st, (const float *)bf.part, bf.kv_len, bf.o, p.sh);
 }
 
 // Shared by the entry points: validation, the launch plan, the launches.
@@ -708,6 +808,48 @@ extern "C" bi_status bi_sdpa(const void *q, const void *k, const void *v, void *
 {
     return attn_run(q, k, v, o, kv_len, max_kv_len, B, Q, Lcap, Hq, Hkv, D, scale, causal, dtype, kv_layout, ws,
                     ws_bytes, stream);
+}
+
+// chunks per split for `splits` splits of max_kv_len keys, and the resulting split count
+static void split_geometry(int64_t max_kv_len, int32_t splits, int &cps, int64_t &nsplit)
+{
+    const int64_t nch = cdiv(max_kv_len, kChunk);
+    cps = (int)cdiv(nch, std::min<int64_t>(splits, nch));
+    nsplit = cdiv(nch, cps);
+}
+
+extern "C" size_t bi_sdpa_split_workspace_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int32_t Hq, int32_t D,
+                                                int32_t splits)
+{
+    if (B < 1 || Q < 1 || max_kv_len < 1 || max_kv_len > kMaxKv || Hq < 1 || D != kHeadDim || splits < 1) return 0;
+    int cps;
+    int64_t nsplit;
+    split_geometry(max_kv_len, splits, cps, nsplit);
+    return nsplit == 1 ? 0 : (size_t)(B * Q * Hq) * (size_t)nsplit * kPartStride * sizeof(float);
+}
+
+extern "C" bi_status bi_sdpa_split(const void *q, const void *k, const void *v, void *o, const int32_t *kv_len,
+                                   int64_t max_kv_len, int64_t B, int64_t Q, int64_t Lcap, int32_t Hq, int32_t Hkv,
+                                   int32_t D, float scale, int32_t causal, int32_t dtype, int32_t kv_layout,
+                                   int32_t splits, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    bi_status s = check_attn(q, k, v, o, kv_len, max_kv_len, B, Q, Lcap, Hq, Hkv, D, dtype);
+    if (s != BI_OK) return s;
+    if (kv_layout != 0 && kv_layout != 1) return BI_ERR_SHAPE;
+    if (splits < 1) return BI_ERR_SHAPE;
+    if (Q * (Hq / Hkv) > 16) return BI_ERR_UNSUPPORTED;        // one 16-row query tile per (sequence, KV head)
+    int cps;
+    int64_t nsplit;
+    split_geometry(max_kv_len, splits, cps, nsplit);
+    const size_t need = bi_sdpa_split_workspace_bytes(B, Q, max_kv_len, Hq, D, splits);
+    if (need > 0 && (!ws || ws_bytes < need)) return BI_ERR_WORKSPACE;
+    if (need > 0 && !host_aligned16(ws)) return BI_ERR_ALIGN;
+    const AttnPlan p = attn_plan(B, Q, max_kv_len, Lcap, Hq, Hkv, scale, causal, kv_layout, cps);
+    AttnBufs bf{(const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, (uint16_t *)o, (float *)ws};
+    (void)hipGetLastError();
+    if (dtype == BI_BF16) launch_attn_split<BF16>(bf, p, stream);
+    else launch_attn_split<F16>(bf, p, stream);
+    return launch_status();
 }
 
 extern "C" size_t bi_sdpa_noalloc_max_bytes(void) { return kAttnScratchBytes; }

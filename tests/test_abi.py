@@ -131,6 +131,29 @@ def test_split_variant_validation():
     assert L.bi_matmul_split_workspace_bytes(4, 512, 8) == 4 * 512 * 8 * 4
 
 
+def test_quantized_and_attention_split_validation():
+    L = bi.lib()
+    MX = bi.MXFP4
+    # qmatmul_split(x, wq, scales, biases, y, M, N, K, qmode, bits, gs, layout, splits, ws, ws_bytes, stream)
+    assert L.bi_qmatmul_split(A, A, A, None, A, 4, 512, 4096, MX, 4, 32, 1, 0, A, 10 ** 9, None) == SHAPE
+    assert L.bi_qmatmul_split(A, A, A, None, A, 4, 512, 4096, MX, 4, 32, 1, 33, A, 10 ** 9, None) == SHAPE
+    assert L.bi_qmatmul_split(A, A, A, None, A, 32, 512, 4096, MX, 4, 32, 1, 4, A, 10 ** 9, None) == UNSUP
+    assert L.bi_qmatmul_split(A, A, A, None, A, 4, 512, 4096, MX, 4, 32, 0, 4, A, 10 ** 9, None) == UNSUP
+    assert L.bi_qmatmul_split(A, A, A, None, A, 4, 512, 4096, MX, 4, 32, 1, 4, None, 0, None) == WORKSPACE
+    assert L.bi_qmatmul_split(A, A, A, None, A, 4, 512, 4096, MX, 4, 32, 1, 4, A, 16, None) == WORKSPACE
+    assert L.bi_qmatmul_split(A, A, A, None, A, 4, 512, 4096, MX, 4, 31, 1, 4, A, 10 ** 9, None) == GROUP
+    assert L.bi_qmatmul_split_workspace_bytes(4, 512, 8) == 4 * 512 * 8 * 4
+    f = ctypes.c_float(0.1)
+    # sdpa_split(q, k, v, o, kv, max_kv, B, Q, Lcap, Hq, Hkv, D, scale, causal, dtype, layout, splits, ws, wsb, st)
+    assert L.bi_sdpa_split(A, A, A, A, A, 1000, 2, 1, 1024, 32, 8, 128, f, 1, 0, 0, 0, A, 10 ** 9, None) == SHAPE
+    assert L.bi_sdpa_split(A, A, A, A, A, 1000, 2, 5, 1024, 32, 8, 128, f, 1, 0, 0, 2, A, 10 ** 9, None) == UNSUP
+    assert L.bi_sdpa_split(A, A, A, A, A, 1000, 2, 1, 1024, 32, 8, 128, f, 1, 0, 0, 2, None, 0, None) == WORKSPACE
+    # 1000 keys = 4 chunks: 3 splits -> runs of 2 chunks -> 2 partials per row
+    assert L.bi_sdpa_split_workspace_bytes(2, 1, 1000, 32, 128, 3) == 2 * 32 * 2 * 132 * 4
+    assert L.bi_sdpa_split_workspace_bytes(2, 1, 1000, 32, 128, 1) == 0
+    assert L.bi_sdpa_split_workspace_bytes(2, 1, 1000, 32, 128, 99) == 2 * 32 * 4 * 132 * 4
+
+
 def test_matmul_ws_validation_and_workspace_size():
     """Workspace errors are reported before any launch; shapes that need no
     workspace report 0 bytes."""

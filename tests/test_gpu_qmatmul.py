@@ -333,3 +333,27 @@ def test_packed_layout_matches_definition():
                         consts[((r * nb + blk) * 16 + c) * (128 // gs) + q] = su[row, gi] | (bu[row, gi] << 16)
     assert np.array_equal(got[:codes.size], codes)
     assert np.array_equal(got[codes.size:], consts)
+
+
+@pytest.mark.parametrize("mode,gs", MODES)
+@pytest.mark.parametrize("packed", [False, True])
+def test_split_variant_is_correct_but_not_invariant(mode, gs, packed):
+    """Negative control for the quantized path: split-K over contiguous K
+    ranges with a cleanup reduction (bi_qmatmul_split, built from the
+    streaming decode kernel) is within the parity gate of the oracle but its
+    bits follow the split count; one split is the invariant kernel."""
+    M, K, N = 16, 4096, 2048              # 32768 outputs per split count: enough for a changed f16 bit
+    x, wq, s, b = inputs.qmatmul_case(M, K, N, mode, gs, True, seed=3)
+    r = ref(x, wq, s, b, M, N, K, mode, gs, True)
+    wqd, sd, bd = dev_q(wq, s, b)
+    if packed:
+        wqd, sd, bd = bi.pack_qweights(wqd, sd, bd, N, K, QM[mode], gs), None, None
+    xd = to_dev(x, "f16")
+    inv = to_np(bi.qmatmul(xd, wqd, sd, bd, N, K, QM[mode], gs, True, packed=packed))
+    differs = 0
+    for sp in (2, 3, 8, 32):
+        y = to_np(bi.qmatmul_split(xd, wqd, sd, bd, N, K, QM[mode], gs, sp, packed=packed))
+        assert_parity(y, r, "f16", f"splits={sp}")
+        differs += int(not bits_equal(y, inv))
+    assert differs > 0
+    assert bits_equal(to_np(bi.qmatmul_split(xd, wqd, sd, bd, N, K, QM[mode], gs, 1, packed=packed)), inv)

@@ -177,3 +177,44 @@ def test_prefill_chunking_invariance(L, chunk):
         parts.append(bi.sdpa(qd[:, s0:s1].contiguous(), kd, vd, torch.tensor([s1], dtype=torch.int32, device=dev()),
                              s1, SCALE, True))
     assert torch.equal(torch.cat(parts, dim=1).view(torch.int16), one.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,Q,Lk,causal", [(1, 1, 16388, True), (3, 1, 2000, True), (2, 4, 1300, True),
+                                           (2, 2, 700, False)])
+def test_split_variant_parity(B, Q, Lk, causal):
+    """The split-KV comparison variant (bi_sdpa_split: the chunk kernel
+    carrying its softmax state across a run of chunks, the run length set by
+    the caller's split count) is within the parity gate of the oracle at every
+    split count, and runs of one chunk are bi_sdpa's own tree.  Ragged lengths
+    (B = 3: Lk, Lk - 300, Lk - 855) and causal blocks included."""
+    q, k, v = inputs.sdpa_case(B, Q, Lk, HQ, HKV, D, seed=11)
+    kv = np.array([Lk - 300 * i - (255 if i > 1 else 0) for i in range(B)], np.int32)
+    ref = oracle.sdpa(q, k, v, kv, SCALE, causal, "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    kvd = torch.tensor(kv, device=dev())
+    inv = to_np(bi.sdpa(qd, kd, vd, kvd, Lk, SCALE, causal))
+    nch = -(-Lk // 256)
+    for sp in (1, 2, 3, 7):
+        assert_parity(to_np(bi.sdpa_split(qd, kd, vd, kvd, Lk, SCALE, sp, causal)), ref, "bf16", f"splits={sp}")
+    assert bits_equal(to_np(bi.sdpa_split(qd, kd, vd, kvd, Lk, SCALE, nch, causal)), inv)
+    assert bits_equal(to_np(bi.sdpa_split(qd, kd, vd, kvd, Lk, SCALE, 10 * nch, causal)), inv)
+
+
+def test_split_variant_bits_follow_the_split_count():
+    """Negative control: the split count changes output bits, so the
+    invariance tests can tell a split tree from the fixed one.  The two trees
+    differ by a few fp32 ulps, which a 16-bit rounding hides for most values
+    (in bf16 almost all: at 4096 outputs no split count changed a bit), so
+    the check runs in f16 over 131072 outputs (B 8, a causal block of 4)."""
+    B, Q, Lk = 8, 4, 3000
+    q, k, v = inputs.sdpa_case(B, Q, Lk, HQ, HKV, D, seed=12, dtype="f16")
+    kvd = torch.full((B,), Lk, dtype=torch.int32, device=dev())
+    qd, kd, vd = to_dev(q, "f16"), to_dev(k, "f16"), to_dev(v, "f16")
+    inv = to_np(bi.sdpa(qd, kd, vd, kvd, Lk, SCALE, True))
+    ref = oracle.sdpa(q, k, v, np.full(B, Lk, np.int32), SCALE, True, "f16")
+    changed = 0
+    for sp in (2, 3, 5):
+        y = to_np(bi.sdpa_split(qd, kd, vd, kvd, Lk, SCALE, sp, True))
+        assert_parity(y, ref, "f16", f"splits={sp}")
+        changed += int(np.count_nonzero(y.view(np.uint16) != inv.view(np.uint16)))
+    assert changed > 0
