@@ -407,6 +407,12 @@ static void launch_dense(const void *x, const void *w, void *y, float *part, int
 {
     const bool plain = splits == 1 && part == nullptr;
     if constexpr (!std::is_same_v<S, F32>) {
+        // long M: the LDS-tiled form (operands shared by the workgroup's waves)
+        if (plain && M > 64 && layout != W_NATURAL && K % 128 == 0 && K >= 1024 && host_aligned16(x) && host_aligned16(w) &&
+            M < (1ll << 31) && N < (1ll << 31) && K < (1ll << 31)) {
+            launch_dense_tile<S>(x, w, y, M, N, K, layout == W_PACKED, st);
+            return;
+        }
         if (layout == W_PACKED) {                  // K % 128 == 0 and 16-byte aligned operands (checked)
             if (plain && try_launch_stream<S, true>(x, w, y, M, N, K, st)) return;
             launch_dense_mt<S, true, true, true>(x, w, y, part, M, N, K, splits, st);

@@ -155,4 +155,10 @@ inline bi_status check_dense(const void *x, const void *w, const void *y, int64_
 void dispatch_dense(const void *x, const void *w, void *y, float *part, int64_t M, int64_t N, int64_t K,
                     int32_t dtype, int32_t layout, int splits, hipStream_t st);
 
+// The LDS-tiled form for M > 64 (dense_tile.hip): 16-bit types, transposed or
+// packed W, K % 128 == 0 and K >= 1024, x and W 16-byte aligned, M, N, K < 2^31.
+template <typename S>
+void launch_dense_tile(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K, bool packed,
+                       hipStream_t st);
+
 }  // namespace bi

@@ -130,3 +130,36 @@ def test_add_rmsnorm_rows_invariant_and_bounded():
     torch.cuda.synchronize()
     assert xg.canaries_intact() and yg.canaries_intact()
     assert bits_equal(to_np(yg.view), to_np(full))
+
+
+@pytest.mark.parametrize("rows", [2048, 2049, 4096, 5000])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_many_rows_form_equals_row_alone(rows, dtype):
+    """Thousands of rows (more rows than the GPU holds waves at once): rows,
+    fused and plain, in and out of place, equal the same rows normalized
+    alone or in a small batch, and the outputs are fenced by canaries."""
+    H = 4096
+    rng = np.random.default_rng(rows)
+    x = inputs.normal(rng, (rows, H), 3.0, dtype=dtype)
+    r = inputs.normal(rng, (rows, H), 0.5, dtype=dtype)
+    w = inputs.normal(rng, (H,), 0.1, loc=1.0, dtype=dtype)
+    xd, rd, wd = to_dev(x, dtype), to_dev(r, dtype), to_dev(w, dtype)
+    yg = Guarded((rows, H), xd.dtype, poison=0x5A)
+    bi.rmsnorm(xd, wd, 1e-6, out=yg.view)
+    xog, yag = Guarded((rows, H), xd.dtype, poison=0xA5), Guarded((rows, H), xd.dtype, poison=0x3C)
+    bi.add_rmsnorm(xd, rd, wd, 1e-6, x_out=xog.view, out=yag.view)
+    torch.cuda.synchronize()
+    assert yg.canaries_intact() and xog.canaries_intact() and yag.canaries_intact()
+    y, xo, ya = to_np(yg.view), to_np(xog.view), to_np(yag.view)
+    pick = [0, 1, rows // 2, rows - 2, rows - 1]
+    for i in pick:
+        assert bits_equal(to_np(bi.rmsnorm(xd[i:i + 1].contiguous(), wd, 1e-6)), y[i:i + 1]), i
+        xo1, ya1 = bi.add_rmsnorm(xd[i:i + 1].contiguous(), rd[i:i + 1].contiguous(), wd, 1e-6)
+        assert bits_equal(to_np(xo1), xo[i:i + 1]) and bits_equal(to_np(ya1), ya[i:i + 1]), i
+    small = to_np(bi.rmsnorm(xd[:512].contiguous(), wd, 1e-6))
+    assert bits_equal(small, y[:512])
+    assert_parity(y[pick], oracle.rmsnorm(np.ascontiguousarray(x[pick]), w, dtype, 1e-6), dtype)
+    xi = xd.clone()
+    yi = torch.empty_like(xi)
+    bi.add_rmsnorm(xi, rd, wd, 1e-6, x_out=xi, out=yi)
+    assert bits_equal(to_np(xi), xo) and bits_equal(to_np(yi), ya)
