@@ -29,8 +29,8 @@
 // per (tile, step), lane l's 16 bytes at 16 l -- so each operand read is one
 // conflict-free ds_read_b128.  They are written by direct global-to-LDS loads
 // (global_load_lds_dwordx4: lane l's 16 bytes land at 16 l of the 1 KiB the
-// instruction addresses), two buffers deep: block i + 1 streams in while
-// block i is multiplied.
+// instruction addresses), in stages of half a block, four buffers deep: the
+// three stages after the one being multiplied are in flight.
 #include "dense_common.hpp"
 
 #include <algorithm>
@@ -46,12 +46,12 @@ __global__ __launch_bounds__(kTileWaves * kWave, 1)
 void dense_tile_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
                        int M, int N, int K, int ntm, int ntn, int per_xcd)
 {
-    // two buffers, each [0: x, 1: W][tile][step][lane] (64 KiB); separate
-    // arrays, so that the compiler can tell the loads streaming into one from
-    // the reads of the other (a read of the buffer being filled would
-    // otherwise wait for every load in flight)
-    typedef uint4 Stage[2][8][4][kWave];
-    __shared__ __attribute__((aligned(16))) Stage lds0, lds1;
+    // four stage buffers, each half a block: [0: x, 1: W][tile][step of the
+    // half][lane] (32 KiB); separate arrays, so that the compiler can tell the
+    // loads streaming into one from the reads of another (a read of a buffer
+    // being filled would otherwise wait for every load in flight)
+    typedef uint4 Stage[2][8][2][kWave];
+    __shared__ __attribute__((aligned(16))) Stage lds0, lds1, lds2, lds3;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int wm = wave & 1, wn = wave >> 1;      // rows 64 wm .. +64, columns 32 wn .. +32 of the tile
@@ -108,13 +108,16 @@ void dense_tile_kernel(const uint16_t *__restrict__ x, const uint16_t *__restric
     // element offsets of (block b, step st) from src: packed chunks are 512
     // elements per step and 2048 per block; row-major ones 32 and 128
     const int sstep = (isw && PK) ? 4 * 8 * 16 : 32, sblk = (isw && PK) ? 4 * kWave * 8 : 128;
-    auto stage = [&](Stage &buf, int b) {
+    // stage u = (item u / 2, half u % 2): steps 2 (u % 2) and 2 (u % 2) + 1
+    // of block block_of(u / 2); four loads per wave
+    auto stage = [&](Stage &buf, int u) {
+        const int64_t base = (int64_t)block_of(u >> 1) * sblk + (u & 1) * 2 * sstep;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
-                __builtin_amdgcn_global_load_lds(src[h] + (int64_t)b * sblk + st * sstep,
-                                                 &buf[isw ? 1 : 0][tl0 + h][st][0], 16, 0, 0);
+            for (int st = 0; st < 2; ++st)
+                __builtin_amdgcn_global_load_lds(src[h] + base + st * sstep, &buf[isw ? 1 : 0][tl0 + h][st][0], 16,
+                                                 0, 0);
     };
 
     f32x4 acc[4][2], S0[4][2], S1[4][2], S2[4][2];
@@ -123,26 +126,41 @@ void dense_tile_kernel(const uint16_t *__restrict__ x, const uint16_t *__restric
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = S0[i][j] = S1[i][j] = S2[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // One block: four steps; the next step's operands are read from LDS
-    // while the current step multiplies (two register sets, no deeper).
+    // One half block: two steps.  A step's six operands (four x tiles, two W
+    // tiles) are read by one asm block that also waits for them: the compiler
+    // cannot tell a plain LDS read of this buffer from the direct loads still
+    // streaming into the other three, and would make every read wait for all
+    // of them.  The second step's reads are issued before the first step
+    // multiplies.
+    const uint32_t xoff = (uint32_t)(((wm * 4) * 2 * kWave + lane) * 16);              // x tile 4 wm, step 0
+    const uint32_t woff = (uint32_t)(((8 + wn * 2) * 2 * kWave + lane) * 16);          // W tile 2 wn, step 0
     auto multiply = [&](const Stage &buf) {
-        uint4 a[2][4], bb[2][2];
-        auto fetch = [&](int st, uint4 (&ar)[4], uint4 (&br)[2]) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ar[i] = buf[0][wm * 4 + i][st][lane];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) br[j] = buf[1][wn * 2 + j][st][lane];
+        const uint32_t base = (uint32_t)(uintptr_t)&buf[0][0][0][0];
+        i32x4 a[2][4], bb[2][2];
+        auto fetch = [&](int st, i32x4 (&ar)[4], i32x4 (&br)[2]) {
+            const uint32_t xa = base + xoff + st * kWave * 16, wa = base + woff + st * kWave * 16;
+            asm volatile(
+                "ds_read_b128 %0, %6\n\t"
+                "ds_read_b128 %1, %6 offset:2048\n\t"
+                "ds_read_b128 %2, %6 offset:4096\n\t"
+                "ds_read_b128 %3, %6 offset:6144\n\t"
+                "ds_read_b128 %4, %7\n\t"
+                "ds_read_b128 %5, %7 offset:2048\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(ar[0]), "=&v"(ar[1]), "=&v"(ar[2]), "=&v"(ar[3]), "=&v"(br[0]), "=&v"(br[1])
+                : "v"(xa), "v"(wa)
+                : "memory");
         };
         fetch(0, a[0], bb[0]);
-        static_for<0, 4>([&](auto stc) {
-            constexpr int st = decltype(stc)::value;
-            if constexpr (st + 1 < 4) fetch(st + 1, a[(st + 1) & 1], bb[(st + 1) & 1]);
+        fetch(1, a[1], bb[1]);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = DenseMfma<S>::mma(a[st & 1][i], bb[st & 1][j], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
-        });
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = DenseMfma<S>::mma(__builtin_bit_cast(uint4, a[st][i]), __builtin_bit_cast(uint4, bb[st][j]),
+                                                  acc[i][j]);
     };
 
     // fold slot sl's partial into the pairwise sum (uniform branches)
@@ -173,23 +191,38 @@ void dense_tile_kernel(const uint16_t *__restrict__ x, const uint16_t *__restric
                 acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
     };
-    // Item i of the slot-major walk (every slot has a block: nb >= 8): wait
-    // for its operands, start the next item's loads into the other buffer,
-    // multiply, and fold the slot when i is its last block.
+    // Stage u of the slot-major walk (every slot has a block: nb >= 8): wait
+    // for its operands (the two stages after it stay in flight), start stage
+    // u + 3 in the buffer stage u - 1 used, multiply, and after the second
+    // half of a slot's last block fold the slot.
     const int split_i = r * (q + 1);               // items of the slots with q + 1 blocks
-    auto item = [&](const Stage &cur, Stage &nxt, int i) {
-        __builtin_amdgcn_s_waitcnt(0);             // this wave's loads of item i have landed
-        __syncthreads();                           // ... everyone's; and nxt is no longer read
-        if (i + 1 < nb) stage(nxt, block_of(i + 1));
+    const int nst = 2 * nb;
+    auto step = [&](const Stage &cur, Stage &nxt, int u) {
+        if (u + 2 < nst) __builtin_amdgcn_s_waitcnt(0x0F78);        // vmcnt(8): stages u + 1, u + 2 in flight
+        else if (u + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+        else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+        // Everyone's loads of stage u have landed (each wave waited for its
+        // own above: a direct-to-LDS load counts as done once its data is in
+        // LDS) and nobody reads nxt any more.  A bare barrier: a fenced one
+        // (__syncthreads) would also wait for the stages still streaming in;
+        // the memory clobber keeps every LDS access on its side of it.
+        asm volatile("s_barrier" ::: "memory");
+        if (u + 3 < nst) stage(nxt, u + 3);
         multiply(cur);
-        const int e = i + 1;                       // slot boundaries: multiples of q + 1, then of q
-        const bool last = e <= split_i ? e % (q + 1) == 0 : (e - split_i) % q == 0;
-        if (last) fold(e <= split_i ? e / (q + 1) - 1 : r + (e - split_i) / q - 1);
+        if (u & 1) {
+            const int e = (u >> 1) + 1;            // slot boundaries: multiples of q + 1, then of q
+            const bool last = e <= split_i ? e % (q + 1) == 0 : (e - split_i) % q == 0;
+            if (last) fold(e <= split_i ? e / (q + 1) - 1 : r + (e - split_i) / q - 1);
+        }
     };
-    stage(lds0, block_of(0));
-    for (int i = 0; i < nb; i += 2) {
-        item(lds0, lds1, i);
-        if (i + 1 < nb) item(lds1, lds0, i + 1);
+    stage(lds0, 0);
+    stage(lds1, 1);
+    stage(lds2, 2);
+    for (int u = 0; u < nst; u += 4) {
+        step(lds0, lds3, u);
+        step(lds1, lds0, u + 1);
+        if (u + 2 < nst) step(lds2, lds1, u + 2);
+        if (u + 3 < nst) step(lds3, lds2, u + 3);
     }
 
     // MFMA accumulator layout: lane (g, c), register e holds row 4 g + e, column c.
