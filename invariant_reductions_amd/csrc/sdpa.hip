@@ -532,6 +532,294 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
     }
 }
 
+// Prompts (many query rows per KV head, at most 4096 keys: one range).  One
+// workgroup of 8 waves per (sequence, KV head, block of 128 query rows),
+// heaviest blocks first; wave w owns the block's 16-row tile w and plays all
+// four key quarters of every chunk itself -- the "waves" of the chunk tree
+// are the quarters [64q, 64q + 64) of a chunk, whoever computes them -- so a
+// chunk's max, l and o are combined in registers in the tree's order and no
+// partial leaves the workgroup.  The range weights need the row's maximum
+// over its chunks before any o_c is weighted, so the walk runs twice: pass
+// 1 computes every chunk max m_c (kept in LDS) and M = max m_c; pass 2
+// recomputes the scores and forms, per chunk and in ascending order,
+// o_r = sum o_c exp(m_c - M), l_r likewise, exactly as attn_merge_kernel
+// does with the partials (its row level then multiplies by exp(M - M) = 1).
+// Each quarter's K (as the score MFMA's B operand) and V (transposed into
+// the P . V operand, as attn_kernel does in registers) are staged once in
+// LDS for all eight waves, two buffers deep.
+constexpr int kPreWaves = 8, kPreRows = 16 * kPreWaves;
+constexpr int kPreMaxChunks = 16;            // max_kv <= 4096: a single range
+
+template <typename S>
+__global__ __launch_bounds__(kPreWaves * kWave, 1)
+void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, int nrb)
+{
+    typedef uint4 KStage[4][4][kWave];         // [key tile][d step][lane]: score B operands
+    typedef uint4 VStage[2][8][kWave];         // [32-key step][output tile j][lane]: P . V B operands
+    typedef uint4 VRows[kKeysPerWave][kHeadDim / 8];   // V rows of a quarter as stored
+    __shared__ __attribute__((aligned(16))) KStage k0, k1;
+    __shared__ __attribute__((aligned(16))) VStage v0, v1;
+    __shared__ __attribute__((aligned(16))) VRows w0, w1;
+    typedef uint16_t PTile[16][kKeysPerWave + 8];
+    __shared__ __attribute__((aligned(16))) PTile phi[kPreWaves], plo[kPreWaves];
+    __shared__ float mstore[kPreWaves][16][kPreMaxChunks];
+
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int g4 = lane >> 4, c16 = lane & 15;
+    const int R = (int)sh.Q * sh.G, Qi = (int)sh.Q;
+    // block id -> (b, hk, row block), the blocks of the latest positions first
+    const int per = sh.Hkv * nrb;
+    const int b = (int)blockIdx.x / per, rem = (int)blockIdx.x - b * per;
+    const int hk = rem / nrb, rb = nrb - 1 - (rem - (rem / nrb) * nrb);
+    const int kvlen = (int)min((int64_t)kv_len[b], sh.max_kv);
+    const int rt0 = rb * kPreRows + wave * 16;                  // this wave's tile
+    const int rlast = min(rb * kPreRows + kPreRows, R) - 1;     // the block's last row
+    const int lastkey = attn_last_key(kvlen, Qi, rlast / sh.G, sh.causal);
+    if (kvlen < 1 || lastkey < 0) return;                       // a bad kv_len: nothing this block may read
+    const int lastc = lastkey / kChunk;
+    const int nunits = (lastc + 1) * 4;                         // (chunk, quarter) units
+
+    // rows of the accumulator layout held by this lane: rt0 + 4 g4 + i
+    int lk[4];
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = rt0 + g4 * 4 + i;
+        ok[i] = r < R;
+        lk[i] = ok[i] ? attn_last_key(kvlen, Qi, r / sh.G, sh.causal) : -1;
+    }
+    const bool wave_rows = rt0 < R;
+    // q of row rt0 + c16 as the MFMA A operand (padding rows read row 0)
+    uint4 qf[4];
+    {
+        const int ra = rt0 + c16 < R ? rt0 + c16 : 0;
+        const int ja = ra / sh.G, ia = ra - ja * sh.G;
+        const uint16_t *qr = bf.q + (((int64_t)b * sh.Q + ja) * sh.Hq + (int64_t)hk * sh.G + ia) * kHeadDim + g4 * 8;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) qf[st] = *reinterpret_cast<const uint4 *>(qr + st * 32);
+    }
+
+    const int rs = (int)sh.ks;
+    const uint16_t *kbase = bf.k + (int64_t)b * sh.Lcap * sh.Hkv * kHeadDim + (int64_t)hk * sh.hs;
+    const uint16_t *vbase = bf.v + (int64_t)b * sh.Lcap * sh.Hkv * kHeadDim + (int64_t)hk * sh.hs;
+    // K of unit u: 16 one-KiB chunks [kt][st], two per wave, straight into LDS
+    auto stage_k = [&](KStage &dst, int u) __attribute__((always_inline)) {
+        const int key0 = (u >> 2) * kChunk + (u & 3) * kKeysPerWave;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int idx = wave * 2 + h, kt = idx >> 2, st = idx & 3;
+            const int key = min(key0 + kt * 16 + c16, kvlen - 1);   // keys past kv_len read a real key, masked
+            __builtin_amdgcn_global_load_lds(kbase + (int64_t)key * rs + st * 32 + g4 * 8, &dst[kt][st][0], 16, 0, 0);
+        }
+    };
+    // V of unit u: waves 6 and 7 bring the 32-key steps 0 and 1 into LDS as
+    // stored (4 keys per 1 KiB load), then read 8 key rows per lane back,
+    // zero keys past kv_len, transpose and store the P . V operands.  A V
+    // load never stays in flight in registers across other work.
+    auto stage_v = [&](VRows &dst, int u) __attribute__((always_inline)) {
+        const int key0 = (u >> 2) * kChunk + (u & 3) * kKeysPerWave + (wave - 6) * 32;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int key = min(key0 + t * 4 + (lane >> 4), kvlen - 1);
+            __builtin_amdgcn_global_load_lds(vbase + (int64_t)key * rs + c16 * 8, &dst[(wave - 6) * 32 + t * 4][0], 16, 0,
+                                             0);
+        }
+    };
+    auto transpose_v = [&](const VRows &src, VStage &dst, int u) __attribute__((always_inline)) {
+        const int s2 = wave - 6;
+        const int key0 = (u >> 2) * kChunk + (u & 3) * kKeysPerWave + s2 * 32 + g4 * 8;
+        uint4 vr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // keys past kv_len become zeros (p is 0 there; keep 0 * v exact), by a mask, not a select
+            const uint32_t keep = key0 + e < kvlen ? 0xffffffffu : 0u;
+            const uint4 t = src[s2 * 32 + g4 * 8 + e][c16];
+            vr[e] = make_uint4(t.x & keep, t.y & keep, t.z & keep, t.w & keep);
+        }
+        transpose8x8_b16(vr);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[s2][j][lane] = vr[j];
+    };
+    // scores of unit u for this wave's rows, masked (-inf outside a row's keys)
+    auto scores = [&](const KStage &ks_, int u, float (&sc)[4][4]) __attribute__((always_inline)) {
+        const int keyq = (u >> 2) * kChunk + (u & 3) * kKeysPerWave;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) acc = mfma16<S>(qf[st], ks_[kt][st][lane], acc);
+            const int key = keyq + kt * 16 + c16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool vis = ok[i] && key >= 0 && key <= lk[i];
+                sc[kt][i] = vis ? acc[i] * sh.scale : -INFINITY;
+            }
+        }
+    };
+
+    // ---- pass 1: chunk maxima
+    float mc[4], M[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mc[i] = M[i] = -INFINITY;
+    auto pass1_unit = [&](const KStage &cur, KStage &nxt, int u) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (u + 1 < nunits) stage_k(nxt, u + 1);
+        if (wave_rows) {
+            float sc[4][4];
+            scores(cur, u, sc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float m = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+                mc[i] = fmaxf(mc[i], m);
+            }
+            if ((u & 3) == 3) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (c16 == 0) mstore[wave][g4 * 4 + i][u >> 2] = mc[i];
+                    M[i] = fmaxf(M[i], mc[i]);
+                    mc[i] = -INFINITY;
+                }
+            }
+        }
+    };
+    stage_k(k0, 0);
+    for (int u = 0; u < nunits; u += 2) {
+        pass1_unit(k0, k1, u);
+        if (u + 1 < nunits) pass1_unit(k1, k0, u + 1);
+    }
+
+    // ---- pass 2: the chunk tree and the range combine
+    f32x4 oc[8], orr[8];
+    float lc[4], lr[4], mrow[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oc[j] = orr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lc[i] = lr[i] = mrow[i] = 0.0f;
+    // unit u: its V (loaded during unit u - 1) goes into vbuf, free since
+    // everyone passed the barrier after multiplying unit u - 2 with it
+    // the compute of unit u (pass 2)
+    auto compute2 = [&](const VStage &vbuf, const KStage &kcur, int u) __attribute__((always_inline)) {
+        if (!wave_rows) return;
+        const int c = u >> 2, qq = u & 3;
+        if (qq == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mrow[i] = mstore[wave][g4 * 4 + i][c];
+        }
+        float sc[4][4];
+        scores(kcur, u, sc);
+        // probabilities, this quarter's row sums, P as hi and lo parts
+        float ls[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ls[i] = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool vis = sc[kt][i] != -INFINITY;
+                const float pv = vis ? expf(sc[kt][i] - mrow[i]) : 0.0f;
+                ls[i] = ls[i] + pv;
+                const uint16_t hi = S::narrow(pv);
+                phi[wave][g4 * 4 + i][kt * 16 + c16] = hi;
+                plo[wave][g4 * 4 + i][kt * 16 + c16] = S::narrow(pv - S::widen(hi));
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float l = ls[i];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) l = l + __shfl_xor(l, off, kWave);
+            lc[i] = qq == 0 ? l : lc[i] + l;
+        }
+        // this quarter's o: P (16 x 64) . V (64 x 128), lo parts first
+        uint4 ph[2], pq[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            ph[s2] = *reinterpret_cast<const uint4 *>(&phi[wave][c16][s2 * 32 + g4 * 8]);
+            pq[s2] = *reinterpret_cast<const uint4 *>(&plo[wave][c16][s2 * 32 + g4 * 8]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(pq[s2], vbuf[s2][j][lane], acc);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) acc = mfma16<S>(ph[s2], vbuf[s2][j][lane], acc);
+            oc[j] = qq == 0 ? acc : oc[j] + acc;
+        }
+        if (qq == 3) {
+            // chunk c done: weight it into the range sums of the rows that see it
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (!(ok[i] && lk[i] >= c * kChunk)) continue;
+                const float w = expf(mrow[i] - M[i]);
+                if (c == 0) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) orr[j][i] = oc[j][i] * w;
+                    lr[i] = lc[i] * w;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) orr[j][i] = orr[j][i] + oc[j][i] * w;
+                    lr[i] = lr[i] + lc[i] * w;
+                }
+            }
+        }
+    };
+    // VW: this wave stages V (waves 6 and 7); the two roles run separate
+    // copies of the walk.  Unit u: everyone's loads of unit u have landed and
+    // unit u's V operands are in vcur (staged by waves 6 and 7 at the end of
+    // unit u - 1); start unit u + 1's loads, multiply, and (waves 6, 7) turn
+    // unit u + 1's V rows into vnxt -- free, since everyone passed this
+    // unit's barrier after multiplying unit u - 1 with it.
+    auto pass2_unit = [&](auto vw_, const KStage &kcur, KStage &knxt, const VStage &vcur, VStage &vnxt,
+                          VRows &wnxt, int u) __attribute__((always_inline)) {
+        constexpr bool VW = decltype(vw_)::value;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (u + 1 < nunits) {
+            stage_k(knxt, u + 1);
+            if constexpr (VW) stage_v(wnxt, u + 1);
+        }
+        compute2(vcur, kcur, u);
+        if constexpr (VW) {
+            if (u + 1 < nunits) {
+                __builtin_amdgcn_s_waitcnt(0);             // this wave's V rows of unit u + 1
+                transpose_v(wnxt, vnxt, u + 1);
+            }
+        }
+    };
+    auto pass2 = [&](auto vw_) __attribute__((always_inline)) {
+        constexpr bool VW = decltype(vw_)::value;
+        stage_k(k0, 0);
+        if constexpr (VW) {
+            stage_v(w0, 0);
+            __builtin_amdgcn_s_waitcnt(0);
+            transpose_v(w0, v0, 0);
+        }
+        for (int u = 0; u < nunits; u += 2) {
+            pass2_unit(vw_, k0, k1, v0, v1, w1, u);
+            if (u + 1 < nunits) pass2_unit(vw_, k1, k0, v1, v0, w0, u + 1);
+        }
+    };
+    if (wave >= 6) pass2(std::true_type{});
+    else pass2(std::false_type{});
+    if (!wave_rows) return;
+    // the row level of a single range: o = o_r exp(M - M), l likewise; out = RNE(o / l)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (!ok[i] || lk[i] < 0) continue;
+        const int r = rt0 + g4 * 4 + i, j = r / sh.G;
+        const int64_t row = ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (r - j * sh.G);
+        const float u = expf(M[i] - M[i]);
+        const float l = lr[i] * u;
+        uint16_t o8[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) o8[jj] = S::narrow((orr[jj][i] * u) / l);
+        *reinterpret_cast<uint4 *>(bf.o + row * kHeadDim + c16 * 8) = __builtin_bit_cast(uint4, o8);
+    }
+}
+
 // Range and row levels for one query row (b, j, h) per workgroup of
 // 32 * kMergeRanges threads: thread (r', quad) handles range r' of the current
 // batch of kMergeRanges ranges and d in [4 quad, +4).
@@ -755,6 +1043,16 @@ static bi_status attn_run(const void *q, const void *k, const void *v, void *o, 
     if (ws_bytes < p.parts) return BI_ERR_WORKSPACE;
     AttnBufs bf{(const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, (uint16_t *)o, (float *)ws};
     (void)hipGetLastError();
+    // prompts: at least one block of 128 query rows per KV head, one range of keys
+    const int64_t R = Q * (Hq / Hkv), nrb = cdiv(R, kPreRows);
+    if (R >= kPreRows && max_kv_len <= (int64_t)kPreMaxChunks * kChunk && B * Hkv * nrb < (1ll << 31)) {
+        const dim3 grid((unsigned)(B * Hkv * nrb)), block(kPreWaves * kWave);
+        if (dtype == BI_BF16)
+            launch_kernel((attn_prefill_kernel<BF16>), grid, block, 0, stream, bf, kv_len, p.sh, (int)nrb);
+        else
+            launch_kernel((attn_prefill_kernel<F16>), grid, block, 0, stream, bf, kv_len, p.sh, (int)nrb);
+        return launch_status();
+    }
     if (dtype == BI_BF16) launch_attn<BF16>(bf, p, stream);
     else launch_attn<F16>(bf, p, stream);
     return launch_status();

@@ -218,3 +218,36 @@ def test_split_variant_bits_follow_the_split_count():
         assert_parity(y, ref, "f16", f"splits={sp}")
         changed += int(np.count_nonzero(y.view(np.uint16) != inv.view(np.uint16)))
     assert changed > 0
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("head_major", [False, True])
+def test_prompt_kernel_rows_equal_lone_queries(causal, head_major):
+    """Prompts (at least 128 query rows per KV head, up to 4096 keys) take
+    the prompt-shaped kernel (a wave plays all four key quarters of a chunk;
+    two passes over the chunks).  Every row must equal the same query run
+    alone through the decode kernel at its position, with ragged lengths, a
+    partial last block of rows and both cache layouts; sampled rows are within
+    the parity gate of the oracle."""
+    B, Q, Lcap = 2, 1000, 2600
+    q, k, v = inputs.sdpa_case(B, Q, Lcap, HQ, HKV, D, seed=21)
+    kv = np.array([2600, 1900], np.int32)
+    qd = to_dev(q, "bf16")
+    kd, vd = to_dev(k, "bf16"), to_dev(v, "bf16")
+    if head_major:
+        kd, vd = kd.transpose(1, 2).contiguous(), vd.transpose(1, 2).contiguous()
+    kvd = torch.tensor(kv, device=dev())
+    full = to_np(bi.sdpa(qd, kd, vd, kvd, int(kv.max()), SCALE, causal, head_major=head_major))
+    for bb in range(B):
+        for j in (0, 1, 37, Q // 2, Q - 2, Q - 1):
+            L = int(kv[bb]) - Q + j + 1 if causal else int(kv[bb])
+            qj = qd[bb:bb + 1, j:j + 1].contiguous()
+            one = to_np(bi.sdpa(qj, kd[bb:bb + 1].contiguous(), vd[bb:bb + 1].contiguous(),
+                                torch.tensor([L], dtype=torch.int32, device=dev()), L, SCALE, True,
+                                head_major=head_major))
+            assert bits_equal(one[0, 0], full[bb, j]), (bb, j)
+    # parity: a few rows through the oracle, each as a lone query at its position
+    for j in (0, 499, 999):
+        lens = kv - Q + j + 1 if causal else kv
+        ref = oracle.sdpa(np.ascontiguousarray(q[:, j:j + 1]), k, v, lens.astype(np.int32), SCALE, True, "bf16")
+        assert_parity(full[:, j:j + 1], ref, "bf16", f"row {j}")
