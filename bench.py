@@ -265,18 +265,27 @@ def main():
         "setup_s": round(setup_s, 1),
     }
 
+    progress(f"timed {K} steps: {ms_step:.4f} ms/step")
     if not args.no_extras:
         out["ops"] = op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch)
+        progress("per-op breakdown done")
         out["decode_sweep"] = decode_sweep(torch, model, stream, cap, ctx)
+        progress("decode sweep done")
         out["measured_peaks"] = measured_peaks(torch, bi, dev)
         out["roofline"]["frac_of_measured_read"] = round(mm_gbs / out["measured_peaks"]["hbm_read_gbs"], 4)
+        progress("measured peaks done")
         out["invariance_overhead"] = invariance_overhead(torch, bi, dev, B)
+        progress("invariance overhead done")
         out["qmatmul"] = qmatmul_decode(torch, bi, dev)
         out["row_ops"] = row_ops(torch, bi, model, B)
+        progress("quantized and row ops done")
         out["sweep"] = op_sweep(torch, bi, dev)
+        progress("sweep done")
 
     if not args.no_cpu_baseline:
+        progress("CPU oracle baseline: starting")
         cb = cpu_baseline(W, cfg, B, ctx, kc_host, vc_host, ids0)
+        progress("CPU oracle baseline done")
         trc, tr1 = step_traffic(cfg, B, ctx), step_traffic(cfg, 1, ctx)
         out["cpu_baseline"] = {
             "value": round(trc["total_bytes"] / cb["t_all"] / 1e9, 3), "unit": "GB/s", "cores": cb["threads"],
@@ -402,6 +411,11 @@ def op_workload(torch, bi, name):
         torch.cuda.empty_cache()
 
 
+def progress(msg):
+    """One line on stderr per finished section (the JSON result is stdout's only line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch):
     """Per-op device time of one step (HIP events around every launch, 5 steps)."""
     reps = 5
@@ -465,6 +479,13 @@ def _time_kernel(torch, bi, fn, reps, launches=1):
     return float(np.mean([s_.elapsed_time(t_) for s_, t_ in ev]))
 
 
+def sdpa_launches(Q, Hq, Hkv, Lk):
+    """Kernels one bi_sdpa call launches: one for a prompt (at least 128 query
+    rows per KV head, at most 4096 keys: the prompt-shaped kernel), else two
+    (chunk partials, then the merge)."""
+    return 1 if Q * (Hq // Hkv) >= 128 and Lk <= 4096 else 2
+
+
 def op_sweep(torch, bi, dev):
     """The four reductions at the measurement shapes, cold (rotated copies of
     the streamed operand, at least 512 MiB in all), kernel time:
@@ -473,7 +494,10 @@ def op_sweep(torch, bi, dev):
       RMSNorm: H = 4096 at B in {1, 8, 64, 512, 4096};
       SDPA (two launches: chunks and merge): B = 1, Q in {1, 8} at
         Lk in {1028, 8196, 16388, 65540}, and B in {4, 16, 64} at Q = 1,
-        Lk = 8196."""
+        Lk = 8196;
+      4-bit quantized matmul (packed): 28672 x 4096 at M in 1..64, affine
+        group sizes 32/64/128, nvfp4, mxfp4;
+      causal prefill attention at prompts of 512 and 2048 tokens."""
     res = {"target": "decode shapes with >= 32 MiB of weights or KV, and RMSNorm at B = 4096: frac_hbm >= 0.70",
            "matmul": {}, "rmsnorm": {}, "sdpa": {}}
     bf = torch.bfloat16
@@ -511,11 +535,36 @@ def op_sweep(torch, bi, dev):
         o = torch.empty_like(q)
         wsd = torch.empty(bi.sdpa_workspace_bytes(Bn, Q, Lk, Hq, D), dtype=torch.uint8, device=dev)
         t = _time_kernel(torch, bi, lambda i: bi.sdpa(q, ks[i % copies], vs[i % copies], kv, Lk, 0.088, True, out=o,
-                                                      ws=wsd, head_major=True), reps=3 * copies, launches=2)
+                                                      ws=wsd, head_major=True), reps=3 * copies,
+                         launches=sdpa_launches(Q, Hq, Hkv, Lk))
         gbs = (kvb + 4 * Bn * Q * Hq * D) / (t * 1e-3) / 1e9
         res["sdpa"][f"B{Bn} Q{Q} Lk{Lk}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1),
                                               "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
         del ks, vs
+    # 4-bit quantized decode projection 28672 x 4096 (tile-packed, cold) over M
+    from invariant_reductions_amd import inputs
+    res["qmatmul"] = {}
+    N, K = 28672, 4096
+    for mode, gs, qm in (("affine", 32, bi.AFFINE), ("affine", 64, bi.AFFINE), ("affine", 128, bi.AFFINE),
+                         ("nvfp4", 16, bi.NVFP4), ("mxfp4", 32, bi.MXFP4)):
+        x, wq, sc, bs = inputs.qmatmul_case(64, K, N, mode, gs, True, seed=0)
+        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
+        wq0 = torch.from_numpy(wq.view(np.int32)).to(dev)
+        sd = torch.from_numpy(sc if sc.dtype == np.uint8 else sc.view(np.int16)).to(dev)
+        bd = None if bs is None else torch.from_numpy(bs.view(np.int16)).to(dev)
+        copies = 10
+        wps = [bi.pack_qweights(torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff), sd, bd, N, K, qm, gs)
+               for r in range(copies)]
+        alg = N * K // 2 + N * (K // gs) * (4 if mode == "affine" else 1)
+        for M in (1, 2, 4, 8, 16, 32, 64):
+            xm = xd[:M].contiguous()
+            y = torch.empty(M, N, dtype=torch.float16, device=dev)
+            t = _time_kernel(torch, bi, lambda i: bi.qmatmul(xm, wps[i % copies], None, None, N, K, qm, gs, out=y,
+                                                             packed=True), reps=3 * copies)
+            gbs = (alg + 2 * M * K + 2 * M * N) / (t * 1e-3) / 1e9
+            res["qmatmul"][f"{mode}-gs{gs} {M}x{N}x{K}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1),
+                                                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del wps
     # causal prefill: Q = Lk (a whole prompt in one call), flops over the visible (query, key) pairs
     res["prefill"] = {}
     for Bn, Q in ((1, 512), (1, 2048), (8, 512), (64, 512)):
@@ -527,7 +576,7 @@ def op_sweep(torch, bi, dev):
         o = torch.empty_like(q)
         wsd = torch.empty(bi.sdpa_workspace_bytes(Bn, Q, Lk, Hq, D), dtype=torch.uint8, device=dev)
         t = _time_kernel(torch, bi, lambda i: bi.sdpa(q, ks, vs, kv, Lk, 0.088, True, out=o, ws=wsd, head_major=True),
-                         reps=5, launches=2)
+                         reps=5, launches=sdpa_launches(Q, Hq, Hkv, Lk))
         pairs = Q * (Q + 1) // 2
         tf = 4 * Bn * Hq * D * pairs / (t * 1e-3) / 1e12
         res["prefill"][f"B{Bn} Q{Q} Lk{Lk} causal"] = {"us": round(t * 1e3, 2), "tflops": round(tf, 2),

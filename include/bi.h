@@ -328,8 +328,12 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
  * ranges' partials and the row's result are each added in ascending order.
  * The chunk and range a key falls in depend only on its position, and chunks
  * past a query's last key are never merged, so a row's bits do not depend on
- * B, Q, the other rows or the launch.  Two launches: the chunk partials,
- * then the range and row levels.
+ * B, Q, the other rows or the launch.  Decode and verify shapes take two
+ * launches: the chunk partials (in ws), then the range and row levels.
+ * Prompts -- at least 128 query rows per KV head (Q * Hq / Hkv >= 128) and
+ * max_kv_len <= 4096 (one range) -- take one launch that computes the same
+ * tree per block of 128 query rows without partials (ws is then unused, but
+ * is still validated, so that a caller's sizing does not depend on the path).
  * ------------------------------------------------------------------------ */
 size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int32_t Hq, int32_t D);
 

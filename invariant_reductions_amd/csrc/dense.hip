@@ -407,9 +407,14 @@ static void launch_dense(const void *x, const void *w, void *y, float *part, int
 {
     const bool plain = splits == 1 && part == nullptr;
     if constexpr (!std::is_same_v<S, F32>) {
-        // long M: the LDS-tiled form (operands shared by the workgroup's waves)
-        if (plain && M > 64 && layout != W_NATURAL && K % 128 == 0 && K >= 1024 && host_aligned16(x) && host_aligned16(w) &&
-            M < (1ll << 31) && N < (1ll << 31) && K < (1ll << 31)) {
+        // long M: the LDS-tiled form (operands shared by the workgroup's
+        // waves) once it has tiles for most CUs -- more than one 128-row tile,
+        // or at least 192 column tiles; a single row tile of a narrow matrix
+        // (a verify block of 16 sequences on a 4096-column projection) stays
+        // on the streaming kernel, which spreads it over every CU
+        if (plain && M > 64 && (M > 128 || cdiv(N, 128) >= 192) && layout != W_NATURAL && K % 128 == 0 &&
+            K >= 1024 && host_aligned16(x) && host_aligned16(w) && M < (1ll << 31) && N < (1ll << 31) &&
+            K < (1ll << 31)) {
             launch_dense_tile<S>(x, w, y, M, N, K, layout == W_PACKED, st);
             return;
         }

@@ -333,5 +333,7 @@ extern "C" const char *bi_build_info(void)
            " rmsnorm: one wave per row, 16-byte chunk v to lane v%64, per-lane fma fold, xor butterfly 32..1;"
            " sdpa: chunks of 256 keys, 4 waves x 64 keys, P as hi+lo 16-bit parts in MFMA (lo first),"
            " chunk partials merged in ranges of 16 chunks (weights exp(m_c-M_r), ascending), ranges merged"
-           " in ascending order (weights exp(M_r-M))";
+           " in ascending order (weights exp(M_r-M)); prompts (>= 128 query rows per KV head, <= 4096 keys):"
+           " the same tree in one launch, one wave playing the 4 quarters of a chunk;"
+           " dense M > 64: the same K tree walked slot by slot, x/W tiles shared through LDS";
 }

@@ -356,14 +356,19 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
 // wave partials are added in wave order.
 constexpr int kQXRes = 4;
 
-template <int QM, int GS, int NS, int D, bool XR, bool PK, bool SPL = false>
-__global__ __launch_bounds__(kQWaves * kWave, 2)
+// MT > 1 (up to 64 rows): every item's x chunks of the MT row tiles go
+// through the ring with the weights (no resident x), and each dequantized
+// weight word feeds MT MFMAs; one workgroup per CU (the ring then takes up
+// to 256 VGPRs).
+template <int QM, int GS, int NS, int D, bool XR, bool PK, bool SPL = false, int MT = 1>
+__global__ __launch_bounds__(kQWaves * kWave, MT > 1 ? 1 : 2)
 void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wqp,
                        const void *__restrict__ scales, const uint16_t *__restrict__ biases, uint16_t *__restrict__ y,
                        int M, int N, int K, int ntn, int per, float *__restrict__ part, int splits)
 {
+    static_assert(MT == 1 || (!XR && !SPL), "several row tiles: x through the ring, invariant form only");
     constexpr int P = kQWaves, TC = NS * 16, CB = qconst_chunk_bytes(QM, GS);
-    __shared__ float red[P][16][TC + 1];
+    __shared__ float red[P][16 * MT][TC + 1];
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int nb = K / kQBlock, nrg = (N + 15) / 16;
@@ -383,18 +388,21 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
     else coff = c * 4 + g;
     const uint8_t *cbase = reinterpret_cast<const uint8_t *>(wqp) + (int64_t)nrg * nb * 1024;
     const uint16_t *xr = x + (int64_t)(c < M ? c : M - 1) * K + g * 32;
+    int64_t xoff[MT];                                    // row tile i: row 16 i + c (padding rows read row M - 1)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) xoff[i] = (int64_t)(16 * i + c < M ? 16 * i + c : M - 1) * K + g * 32;
 
     constexpr int NR = XR ? kQXRes : D;                  // ring slots
     uint4 W[NR][NS];
     uint32_t S[NR][NS];
-    uint4 X[XR ? kQXRes : D][4];
+    uint4 X[XR ? kQXRes : D][MT][4];
     if constexpr (XR) {
 #pragma unroll
         for (int j = 0; j < kQXRes; ++j)
             if (j < nmine) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    X[j][s] = *reinterpret_cast<const uint4 *>(xr + (kb0 + wave + j * P) * kQBlock + s * 8);
+                    X[j][0][s] = *reinterpret_cast<const uint4 *>(xr + (kb0 + wave + j * P) * kQBlock + s * 8);
             }
     }
     int lu = 0, lj = 0;                                     // load cursor: tile t0 + lu, block wave + lj*P
@@ -425,26 +433,32 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
         }
         if constexpr (!XR) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) X[d][s] = *reinterpret_cast<const uint4 *>(xr + b * kQBlock + s * 8);
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) X[d][i][s] = *reinterpret_cast<const uint4 *>(x + xoff[i] + b * kQBlock + s * 8);
         }
         if (++lj == nmine) {
             lj = 0;
             ++lu;
         }
     };
-    f32x4 acc[NS];
+    f32x4 acc[MT][NS];
 #pragma unroll
-    for (int jj = 0; jj < NS; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NS; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto finish_tile = [&](int u) {
 #pragma unroll
-        for (int jj = 0; jj < NS; ++jj) {
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave][g * 4 + r][jj * 16 + c] = acc[jj][r];
-            acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+            for (int jj = 0; jj < NS; ++jj) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[wave][16 * i + g * 4 + r][jj * 16 + c] = acc[i][jj][r];
+                acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         __syncthreads();
         const int n0 = (t0 + u) * TC;
-        for (int o = threadIdx.x; o < 16 * TC; o += P * kWave) {
+        for (int o = threadIdx.x; o < 16 * MT * TC; o += P * kWave) {
             const int r = o / TC, cc = o % TC;
             if (r >= M || n0 + cc >= N) continue;
             float v = red[0][r][cc];
@@ -465,11 +479,12 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const uint4 xa = X[XR ? j : d][s];                 // both compile-time indices
 #pragma unroll
             for (int jj = 0; jj < NS; ++jj) {
                 const uint32_t wv = s == 0 ? W[d][jj].x : s == 1 ? W[d][jj].y : s == 2 ? W[d][jj].z : W[d][jj].w;
-                acc[jj] = qmfma(xa, deq_word<QM>(wv, s < 2 ? g01[jj] : g23[jj]), acc[jj]);
+                const uint4 wd = deq_word<QM>(wv, s < 2 ? g01[jj] : g23[jj]);   // once for every row tile
+#pragma unroll
+                for (int i = 0; i < MT; ++i) acc[i][jj] = qmfma(X[XR ? j : d][i][s], wd, acc[i][jj]);   // compile-time indices
             }
         }
     };
@@ -533,14 +548,28 @@ static void launch_q_stream_t(const void *x, const uint32_t *wq, const void *s, 
                       (int)ntn, (int)per, (float *)nullptr, 1);
 }
 
+// 17..64 rows: MT row tiles, x through a 2-deep ring, one workgroup per CU
+template <int QM, int GS, int MT, bool PK>
+static void launch_q_stream_mt(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
+                               int64_t N, int64_t K, hipStream_t st)
+{
+    const int64_t ntn = cdiv(N, 16);
+    const int64_t per = cdiv(ntn, (int64_t)device_cu_count()), grid = cdiv(ntn, per);
+    launch_kernel((qmatmul_stream_kernel<QM, GS, 1, 2, false, PK, false, MT>), dim3((unsigned)grid),
+                  dim3(kQWaves * kWave), 0, st, (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, (int)M,
+                  (int)N, (int)K, (int)ntn, (int)per, (float *)nullptr, 1);
+}
+
 template <int QM, int GS, bool PK>
 static bool try_launch_q_stream(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                                 int64_t N, int64_t K, hipStream_t st)
 {
-    if (M > 16 || K % kQBlock != 0 || !host_aligned16(x) || !host_aligned16(wq) || N >= (1ll << 30) ||
+    if (M > 64 || K % kQBlock != 0 || !host_aligned16(x) || !host_aligned16(wq) || N >= (1ll << 30) ||
         K >= (1ll << 30))
         return false;
-    launch_q_stream_t<QM, GS, 1, PK>(x, wq, s, b, y, M, N, K, st);
+    if (M <= 16) launch_q_stream_t<QM, GS, 1, PK>(x, wq, s, b, y, M, N, K, st);
+    else if (M <= 32) launch_q_stream_mt<QM, GS, 2, PK>(x, wq, s, b, y, M, N, K, st);
+    else launch_q_stream_mt<QM, GS, 4, PK>(x, wq, s, b, y, M, N, K, st);
     return true;
 }
 

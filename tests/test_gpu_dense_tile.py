@@ -1,9 +1,11 @@
-"""The LDS-tiled dense kernel for long M (M > 64, 16-bit, transposed or
-tile-packed weights, K a multiple of 128 and at least 1024): every row it
-computes equals the same row computed alone (M = 1 takes the streaming
-kernel), across ragged M and N, K with an uneven number of blocks per slot,
-both weight layouts and both 16-bit types; the outputs stay inside their
-bounds; sampled rows are within the parity gate of the oracle.  This is the
+"""The LDS-tiled dense kernel for long M (M > 128, or M > 64 with at least
+192 column tiles of 128; 16-bit, transposed or tile-packed weights, K a
+multiple of 128 and at least 1024) and the streaming kernel it hands the
+other M > 64 shapes to: every row equals the same row computed alone (M = 1
+takes the streaming kernel), across ragged M and N, K with an uneven number
+of blocks per slot, both weight layouts and both 16-bit types; the outputs
+stay inside their bounds; sampled rows are within the parity gate of the
+oracle.  This is the
 invariance of "Fix/speculative shape invariance" (Problem: the same row must
 not change with the number of rows) and "Batch-invariant kernels" (Case 3)
 for verify blocks and prompts.
@@ -21,8 +23,8 @@ from invariant_reductions_amd import inputs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,N,K", [(65, 100, 1024), (128, 4096, 4096), (129, 6144, 4096), (320, 512, 1152),
-                                   (300, 1000, 14336), (1000, 2048, 4096), (4096, 256, 2048)])
+@pytest.mark.parametrize("M,N,K", [(65, 100, 1024), (128, 4096, 4096), (80, 24577, 1024), (129, 6144, 4096),
+                                   (320, 512, 1152), (300, 1000, 14336), (1000, 2048, 4096), (4096, 256, 2048)])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("packed", [False, True])
 def test_long_m_rows_equal_row_alone(M, N, K, dtype, packed):

@@ -357,3 +357,33 @@ def test_split_variant_is_correct_but_not_invariant(mode, gs, packed):
         differs += int(not bits_equal(y, inv))
     assert differs > 0
     assert bits_equal(to_np(bi.qmatmul_split(xd, wqd, sd, bd, N, K, QM[mode], gs, 1, packed=packed)), inv)
+
+
+@pytest.mark.parametrize("mode,gs", MODES)
+@pytest.mark.parametrize("packed", [False, True])
+def test_up_to_64_rows_equal_row_alone(mode, gs, packed):
+    """17..64 rows take the streaming kernel with two or four row tiles per
+    workgroup (each dequantized weight word feeds every row tile): each row
+    equals the same row alone (one row tile), the outputs stay in bounds, and
+    sampled rows are within the parity gate of the oracle."""
+    K, N = 4096, 1000
+    x, wq, s, b = inputs.qmatmul_case(64, K, N, mode, gs, True, seed=9)
+    wqd, sd, bd = dev_q(wq, s, b)
+    if packed:
+        wqd, sd, bd = bi.pack_qweights(wqd, sd, bd, N, K, QM[mode], gs), None, None
+    xd = to_dev(x, "f16")
+    alone = {}
+    for M in (17, 32, 33, 48, 64):
+        yg = Guarded((M, N), torch.float16, poison=0x99)
+        bi.qmatmul(xd[:M].contiguous(), wqd, sd, bd, N, K, QM[mode], gs, True, out=yg.view, packed=packed)
+        torch.cuda.synchronize()
+        assert yg.canaries_intact(), M
+        y = to_np(yg.view)
+        for i in sorted({0, 15, 16, M // 2, M - 1}):
+            if i not in alone:
+                alone[i] = to_np(bi.qmatmul(xd[i:i + 1].contiguous(), wqd, sd, bd, N, K, QM[mode], gs, True,
+                                            packed=packed))
+            assert bits_equal(y[i:i + 1], alone[i]), (M, i)
+    rows = [0, 31, 63]
+    r = ref(np.ascontiguousarray(x[rows]), wq, s, b, 3, N, K, mode, gs, True)
+    assert_parity(y[rows], r, "f16")
