@@ -361,7 +361,7 @@ def _op_sdpa(torch, bi, dev):
         ws = torch.empty(bi.sdpa_workspace_bytes(B, Q, Lk, Hq, D), dtype=torch.uint8, device=dev)
         yield (f"sdpa B{B} Q{Q} Lk{Lk}",
                lambda i: bi.sdpa(q, ks[i % copies], vs[i % copies], kv, Lk, 0.088, True, out=o, ws=ws,
-                                 head_major=True), 10)
+                                 head_major=True), 10, sdpa_launches(B, Q, Hq, Hkv, Lk, _cus(torch, dev)))
         del ks, vs
 
 
@@ -389,7 +389,8 @@ def op_workload(torch, bi, name):
     runs scale FETCH_SIZE / WRITE_SIZE by what it reads), then every case of
     the op, each called repeatedly on operands rotated over copies of at least
     512 MiB (no case finds its operands in a cache).  Prints one line per case
-    with the median event-timed call (host launch overhead included)."""
+    with the library kernels one call launches and the median event-timed
+    call (host launch overhead included)."""
     dev = torch.device("cuda:0")
     bi.lib()
     calib = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
@@ -397,7 +398,7 @@ def op_workload(torch, bi, name):
     calib2.copy_(calib)
     torch.cuda.synchronize()
     del calib, calib2
-    for label, fn, reps in OP_WORKLOADS[name](torch, bi, dev):
+    for label, fn, reps, *kpc in OP_WORKLOADS[name](torch, bi, dev):
         fn(0)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -407,7 +408,7 @@ def op_workload(torch, bi, name):
             b.record()
         torch.cuda.synchronize()
         us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)[reps // 2]
-        print(f"case {label}: {reps} calls, median {us:.1f} us", flush=True)
+        print(f"case {label}: {reps} calls of {kpc[0] if kpc else 1} kernels, median {us:.1f} us", flush=True)
         torch.cuda.empty_cache()
 
 
@@ -479,11 +480,21 @@ def _time_kernel(torch, bi, fn, reps, launches=1):
     return float(np.mean([s_.elapsed_time(t_) for s_, t_ in ev]))
 
 
-def sdpa_launches(Q, Hq, Hkv, Lk):
-    """Kernels one bi_sdpa call launches: one for a prompt (at least 128 query
-    rows per KV head, at most 4096 keys: the prompt-shaped kernel), else two
-    (chunk partials, then the merge)."""
-    return 1 if Q * (Hq // Hkv) >= 128 and Lk <= 4096 else 2
+def _cus(torch, dev):
+    return torch.cuda.get_device_properties(dev).multi_processor_count
+
+
+def sdpa_launches(B, Q, Hq, Hkv, Lk, cus):
+    """Kernels one bi_sdpa call launches on a GPU of `cus` compute units: one
+    for a prompt (at least 128 query rows per KV head, at most 4096 keys: the
+    prompt-shaped kernel) and for at least 2 * cus (sequence, KV head) groups
+    of at most 16 query rows over at most 1024 keys (one workgroup walks a
+    group's chunks and merges them), else two (chunk partials, then the
+    merge)."""
+    R = Q * (Hq // Hkv)
+    if R >= 128 and Lk <= 4096:
+        return 1
+    return 1 if R <= 16 and Lk <= 1024 and B * Hkv >= 2 * cus else 2
 
 
 def op_sweep(torch, bi, dev):
@@ -492,9 +503,8 @@ def op_sweep(torch, bi, dev):
       dense (packed weights): the pages' 4096 x 4096 and the decoder's
         projections at M in 1..64;
       RMSNorm: H = 4096 at B in {1, 8, 64, 512, 4096};
-      SDPA (two launches: chunks and merge): B = 1, Q in {1, 8} at
-        Lk in {1028, 8196, 16388, 65540}, and B in {4, 16, 64} at Q = 1,
-        Lk = 8196;
+      SDPA: B = 1, Q in {1, 8} at Lk in {1028, 8196, 16388, 65540}, and
+        B in {4, 16, 64} at Q = 1, Lk = 8196;
       4-bit quantized matmul (packed): 28672 x 4096 at M in 1..64, affine
         group sizes 32/64/128, nvfp4, mxfp4;
       causal prefill attention at prompts of 512 and 2048 tokens."""
@@ -536,7 +546,7 @@ def op_sweep(torch, bi, dev):
         wsd = torch.empty(bi.sdpa_workspace_bytes(Bn, Q, Lk, Hq, D), dtype=torch.uint8, device=dev)
         t = _time_kernel(torch, bi, lambda i: bi.sdpa(q, ks[i % copies], vs[i % copies], kv, Lk, 0.088, True, out=o,
                                                       ws=wsd, head_major=True), reps=3 * copies,
-                         launches=sdpa_launches(Q, Hq, Hkv, Lk))
+                         launches=sdpa_launches(Bn, Q, Hq, Hkv, Lk, _cus(torch, dev)))
         gbs = (kvb + 4 * Bn * Q * Hq * D) / (t * 1e-3) / 1e9
         res["sdpa"][f"B{Bn} Q{Q} Lk{Lk}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1),
                                               "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
@@ -576,7 +586,7 @@ def op_sweep(torch, bi, dev):
         o = torch.empty_like(q)
         wsd = torch.empty(bi.sdpa_workspace_bytes(Bn, Q, Lk, Hq, D), dtype=torch.uint8, device=dev)
         t = _time_kernel(torch, bi, lambda i: bi.sdpa(q, ks, vs, kv, Lk, 0.088, True, out=o, ws=wsd, head_major=True),
-                         reps=5, launches=sdpa_launches(Q, Hq, Hkv, Lk))
+                         reps=5, launches=sdpa_launches(Bn, Q, Hq, Hkv, Lk, _cus(torch, dev)))
         pairs = Q * (Q + 1) // 2
         tf = 4 * Bn * Hq * D * pairs / (t * 1e-3) / 1e12
         res["prefill"][f"B{Bn} Q{Q} Lk{Lk} causal"] = {"us": round(t * 1e3, 2), "tflops": round(tf, 2),

@@ -74,7 +74,8 @@ struct AttnShape {
     float scale;
     int causal;
     int64_t ks, hs;       // cache strides (elements) between consecutive keys and between KV heads
-    int cps;              // chunks per partial: 1 (the invariant tree); the split variant's run length
+    int cps;              // chunks per work item: 1; the split variant's run; WHOLE: all of them
+    int64_t nsplit;       // work items per (sequence, KV head): nchunks; the split count; WHOLE: 1
 };
 
 struct AttnBufs {
@@ -127,6 +128,66 @@ __device__ inline void attn_store_out(uint16_t *dst, float4 o, float l)
     *reinterpret_cast<uint2 *>(dst) = pk;
 }
 
+// The range and row levels of attn_merge_kernel for the query rows of one
+// (sequence b, KV head hk) group (at most 16 rows), by one workgroup of
+// kAttnWaves waves: thread -> (row tid / 32 + 8 k, d in [4 (tid % 32), +4)),
+// ranges walked one after another with the same arithmetic in the same
+// order: M = max of the row's chunk maxima; per range r, M_r, o_r and l_r
+// over its chunks ascending; o and l as the sum of o_r exp(M_r - M) over the
+// ranges ascending (the first term assigned, not added to 0); out = RNE(o/l).
+// The partials were written by this workgroup: plain loads see them.
+template <typename S>
+__device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, int b, int hk, int kvlen)
+{
+    const int R = (int)sh.Q * sh.G;
+    const int quad = threadIdx.x & 31;
+    for (int rr = threadIdx.x >> 5; rr < R; rr += kAttnWaves * kWave / 32) {
+        const int j = rr / sh.G;
+        const int lk = attn_last_key(kvlen, (int)sh.Q, j, sh.causal);
+        if (lk < 0) continue;
+        const int64_t row = ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (rr - j * sh.G);
+        const float *pr = bf.part + row * sh.nchunks * kPartStride;
+        const int nch = lk / kChunk + 1, nr = (nch + kRange - 1) / kRange;
+        float M = -INFINITY;
+        for (int c = 0; c < nch; ++c) M = fmaxf(M, pr[c * kPartStride + kHeadDim]);
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        float l = 0.0f;
+        for (int r = 0; r < nr; ++r) {
+            const int c0 = r * kRange, n = min(nch - c0, kRange);
+            float Mr = pr[c0 * kPartStride + kHeadDim];
+            for (int i = 1; i < n; ++i) Mr = fmaxf(Mr, pr[(c0 + i) * kPartStride + kHeadDim]);
+            float w = expf(pr[c0 * kPartStride + kHeadDim] - Mr);
+            float4 ov = *reinterpret_cast<const float4 *>(pr + c0 * kPartStride + quad * 4);
+            float4 orr = make_float4(ov.x * w, ov.y * w, ov.z * w, ov.w * w);
+            float lr = pr[c0 * kPartStride + kHeadDim + 1] * w;
+            for (int i = 1; i < n; ++i) {
+                const float *pc = pr + (c0 + i) * kPartStride;
+                w = expf(pc[kHeadDim] - Mr);
+                ov = *reinterpret_cast<const float4 *>(pc + quad * 4);
+                orr.x = orr.x + ov.x * w;
+                orr.y = orr.y + ov.y * w;
+                orr.z = orr.z + ov.z * w;
+                orr.w = orr.w + ov.w * w;
+                lr = lr + pc[kHeadDim + 1] * w;
+            }
+            const float u = expf(Mr - M);
+            const float4 tv = make_float4(orr.x * u, orr.y * u, orr.z * u, orr.w * u);
+            const float tl = lr * u;
+            if (r == 0) {
+                o = tv;
+                l = tl;
+            } else {
+                o.x = o.x + tv.x;
+                o.y = o.y + tv.y;
+                o.z = o.z + tv.z;
+                o.w = o.w + tv.w;
+                l = l + tl;
+            }
+        }
+        attn_store_out<S>(bf.o + row * kHeadDim + quad * 4, o, l);
+    }
+}
+
 // The kernel: a persistent, software-pipelined walk over work items.  Work
 // item = (sequence b, chunk c, KV head hk, row group mg) -- mg picks sh.mgt of
 // the 16-row query tiles, so a long prompt with few sequences spreads over
@@ -156,10 +217,18 @@ __device__ inline void attn_store_out(uint16_t *dst, float4 o, float l)
 // max); the split's (o, m, l) is the partial, or with a single split the
 // output itself.  The tree then depends on the split count; it exists only
 // to price the invariant tree.
-template <typename S, bool MG, bool SPL = false>
+//
+// WHOLE: the invariant tree for many (sequence, KV head) groups of at most
+// 16 query rows (nmg == 1): the item is a group with all its chunks, walked
+// in order by one workgroup; every chunk's partial is written exactly as
+// above, and after the last one the same workgroup reads them back and runs
+// attn_merge_kernel's range and row levels for the group's rows -- one
+// launch, and the partials never leave the workgroup's own view.
+template <typename S, bool MG, bool SPL = false, bool WHOLE = false>
 __global__ __launch_bounds__(kAttnWaves * kWave, 2)
 void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, int64_t nid)
 {
+    constexpr bool RUNS = SPL || WHOLE;                                  // an item walks a run of chunks
     typedef uint16_t PTile[16][kKeysPerWave + 8];
     typedef float OTile[16][kHeadDim + 4];
     __shared__ __attribute__((aligned(16))) PTile phi[kAttnWaves], plo[kAttnWaves];
@@ -170,7 +239,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
     const int g4 = lane >> 4, c16 = lane & 15;
     const int R = (int)sh.Q * sh.G;                                      // query rows per KV head
     const int ntm = (R + 15) / 16;
-    const int64_t nitems = sh.B * sh.nchunks;
+    const int64_t nitems = sh.B * sh.nsplit;
     const int Qi = (int)sh.Q;
 
     // The sequence lengths, clamped to max_kv (device data the host cannot
@@ -193,8 +262,8 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
         it.hk = (int)((t >> 3) % sh.Hkv);
         const int64_t bc = (t >> 3) / sh.Hkv * 8 + (t & 7);
         const bool exists = bc < nitems;
-        it.b = exists ? (int)(bc / sh.nchunks) : 0;
-        it.c = exists ? (int)(bc - (int64_t)it.b * sh.nchunks) * (SPL ? sh.cps : 1) : -1;
+        it.b = exists ? (int)(bc / sh.nsplit) : 0;
+        it.c = exists ? (int)(bc - (int64_t)it.b * sh.nsplit) * (RUNS ? sh.cps : 1) : -1;
         it.kvlen = seq_len(it.b);
         return it;
     };
@@ -280,7 +349,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
         // SPL: the split's chunks it.c .. clast in order, with the running
         // softmax state of row threadIdx.x / 16, d in [8 (threadIdx.x % 16), +8)
         const int split = SPL ? it.c / sh.cps : 0;
-        const int clast = SPL ? min(it.c + sh.cps - 1, group_last_key(it) / kChunk) : it.c;
+        const int clast = RUNS ? min(it.c + sh.cps - 1, group_last_key(it) / kChunk) : it.c;
         float rM = -INFINITY, rl = 0.0f, ro[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ro[e] = 0.0f;
@@ -288,7 +357,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
         auto chunk = [&](const bool more) {
             const bool has_next = more || tn < nid;
             auto next_item = [&]() {
-                if (SPL && more) {
+                if (RUNS && more) {
                     Item nx = it;
                     ++nx.c;
                     return nx;
@@ -497,7 +566,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
             // the next item's V (its K and q are in flight since this item's scores)
             if (has_next) load_v(next_item(), vr);
         };
-        if constexpr (SPL) {
+        if constexpr (RUNS) {
             for (;;) {
                 const bool more = it.c < clast;
                 chunk(more);
@@ -506,6 +575,14 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
             }
         } else {
             chunk(false);
+        }
+        if constexpr (WHOLE) {
+            // the group's range and row levels, from the partials this
+            // workgroup just wrote (every store of every wave done first)
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            attn_merge_rows<S>(bf, sh, it.b, it.hk, it.kvlen);
+            __syncthreads();
         }
         if constexpr (SPL) {
             // the split's partial (o, m, l), or with one split the output
@@ -992,7 +1069,7 @@ static AttnPlan attn_plan(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Lcap
     const int64_t nch = cdiv(cdiv(max_kv_len, kChunk), cps);            // partials per row
     AttnPlan p;
     p.sh = AttnShape{B, Q, Lcap, nch, cdiv(nch, kRange), max_kv_len, cdiv(ntm, mgt), Hq, Hkv, (int)G, (int)mgt,
-                     scale, causal ? 1 : 0, ks, hs, cps};
+                     scale, causal ? 1 : 0, ks, hs, cps, nch};
     // item ids (padded to whole groups of 8); a persistent grid of two
     // workgroups per CU, a multiple of 8 so that a workgroup stays on one XCD
     p.nid = cdiv(B * nch, 8) * 8 * Hkv * p.sh.nmg;
@@ -1003,9 +1080,39 @@ static AttnPlan attn_plan(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Lcap
     return p;
 }
 
+// Short contexts (at most kWholeMaxChunks chunks) with at least one
+// (sequence, KV head) group of at most 16 query rows for each of the
+// persistent grid's workgroups (two per CU): one work item per group with
+// all its chunks, merged in the workgroup (attn_kernel's WHOLE form) --
+// every workgroup is busy without cutting the groups into chunks, and the
+// merge launch is gone.  Fewer groups keep the chunk items, which spread a
+// context over the whole chip; so do longer contexts, where a workgroup
+// streaming one group's whole cache region (every group at once, far apart)
+// reads HBM more slowly than the chunk items do (concurrent workgroups on
+// neighbouring chunks of a few groups): 8196 keys at 64 sequences x 8 KV
+// heads take 473 us whole against 437 us as chunks plus merge, while 768
+// keys take 47 us against 50 us.
+constexpr int64_t kWholeMaxChunks = 4;
+
+static bool attn_whole(const AttnPlan &p)
+{
+    return p.sh.nmg == 1 && p.sh.Q * p.sh.G <= 16 && p.sh.nchunks <= kWholeMaxChunks &&
+           p.sh.B * p.sh.Hkv >= 2 * (int64_t)device_cu_count() && p.sh.cps == 1;
+}
+
 template <typename S>
 static void launch_attn(const AttnBufs &bf, const AttnPlan &p, hipStream_t st)
 {
+    if (attn_whole(p)) {
+        AttnShape sh = p.sh;
+        sh.cps = (int)sh.nchunks;                  // one item: every chunk of the group
+        sh.nsplit = 1;
+        const int64_t nid = cdiv(sh.B, 8) * 8 * sh.Hkv;
+        const int64_t grid = std::min<int64_t>(nid, (int64_t)device_cu_count() * 2 / 8 * 8);
+        launch_kernel((attn_kernel<S, false, false, true>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st, bf,
+                      bf.kv_len, sh, nid);
+        return;
+    }
     if (p.sh.nmg > 1)
         launch_kernel((attn_kernel<S, true>), dim3((unsigned)p.grid), dim3(kAttnWaves * kWave), 0, st, bf, bf.kv_len,
                       p.sh, p.nid);

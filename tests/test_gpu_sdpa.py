@@ -251,3 +251,37 @@ def test_prompt_kernel_rows_equal_lone_queries(causal, head_major):
         lens = kv - Q + j + 1 if causal else kv
         ref = oracle.sdpa(np.ascontiguousarray(q[:, j:j + 1]), k, v, lens.astype(np.int32), SCALE, True, "bf16")
         assert_parity(full[:, j:j + 1], ref, "bf16", f"row {j}")
+
+
+@pytest.mark.parametrize("Q,head_major", [(1, False), (1, True), (4, False)])
+def test_whole_group_form_equals_lone_sequences(Q, head_major):
+    """At least two (sequence, KV head) groups of at most 16 query rows per
+    CU over at most 1024 keys: one workgroup walks all of a group's chunks and
+    merges them itself, with no merge launch.  Each sequence must equal the
+    same sequence run alone (chunk items, then the merge launch), with ragged
+    lengths on both sides of the chunk edges (256 keys), both cache layouts
+    and a causal block of 4; sampled sequences are within the parity gate of
+    the oracle.  K, V, q ~ N(0,1) bf16 drawn on the device (seeded)."""
+    cus = torch.cuda.get_device_properties(dev()).multi_processor_count
+    B, Lcap = -(-2 * cus // HKV), 1024
+    g = torch.Generator(device=dev()).manual_seed(40 + Q + 2 * head_major)
+    shape = (B, HKV, Lcap, D) if head_major else (B, Lcap, HKV, D)
+    kd = torch.randn(shape, generator=g, device=dev()).to(torch.bfloat16)
+    vd = torch.randn(shape, generator=g, device=dev()).to(torch.bfloat16)
+    qd = torch.randn((B, Q, HQ, D), generator=g, device=dev()).to(torch.bfloat16)
+    edges = [Q, 5, 255, 256, 257, 511, 512, 513, 767, 768, 769, 1023, Lcap]
+    rng = np.random.default_rng(Q)
+    kv = np.array(edges + list(rng.integers(Q, Lcap + 1, B - len(edges))), np.int32)
+    kvd = torch.tensor(kv, device=dev())
+    full = to_np(bi.sdpa(qd, kd, vd, kvd, Lcap, SCALE, True, head_major=head_major))
+    for b in range(B):
+        L = int(kv[b])
+        one = to_np(bi.sdpa(qd[b:b + 1].contiguous(), kd[b:b + 1].contiguous(), vd[b:b + 1].contiguous(),
+                            kvd[b:b + 1].contiguous(), L, SCALE, True, head_major=head_major))
+        assert bits_equal(one, full[b:b + 1]), f"sequence {b} (kv_len {L})"
+    for b in (2, 9, 12):
+        kb, vb = kd[b:b + 1], vd[b:b + 1]
+        if head_major:
+            kb, vb = kb.transpose(1, 2), vb.transpose(1, 2)
+        ref = oracle.sdpa(to_np(qd[b:b + 1]), to_np(kb), to_np(vb), kv[b:b + 1], SCALE, True, "bf16")
+        assert_parity(full[b:b + 1], ref, "bf16", f"sequence {b}")
