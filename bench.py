@@ -322,12 +322,12 @@ def _op_matmul(torch, bi, dev):
 
 
 def _op_qmatmul(torch, bi, dev):
-    """4-bit decode projections 28672 x 4096 at M = 1, 4, 8 in the
+    """4-bit decode projections 28672 x 4096 at M = 1, 4, 8, 32, 64 in the
     transposed and tile-packed layouts, three formats."""
     from invariant_reductions_amd import inputs
     N, K = 28672, 4096
     for mode, gs, qm in (("affine", 64, bi.AFFINE), ("nvfp4", 16, bi.NVFP4), ("mxfp4", 32, bi.MXFP4)):
-        x, wq, s, b = inputs.qmatmul_case(8, K, N, mode, gs, True, seed=0)
+        x, wq, s, b = inputs.qmatmul_case(64, K, N, mode, gs, True, seed=0)
         xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
         wq0 = torch.from_numpy(wq.view(np.int32)).to(dev)
         sd = torch.from_numpy(s if s.dtype == np.uint8 else s.view(np.int16)).to(dev)
@@ -335,7 +335,7 @@ def _op_qmatmul(torch, bi, dev):
         copies = 12
         wqs = [wq0] + [torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff) for r in range(1, copies)]
         wps = [bi.pack_qweights(w, sd, bd, N, K, qm, gs) for w in wqs]
-        for M in (1, 4, 8):
+        for M in (1, 4, 8, 32, 64):
             y = torch.empty(M, N, dtype=torch.float16, device=dev)
             xm = xd[:M].contiguous()
             yield (f"qmatmul {mode} gs{gs} {M}x{N}x{K} transposed",

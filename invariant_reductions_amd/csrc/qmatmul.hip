@@ -356,17 +356,19 @@ void qmatmul_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
 // wave partials are added in wave order.
 constexpr int kQXRes = 4;
 
-// MT > 1 (up to 64 rows): every item's x chunks of the MT row tiles go
-// through the ring with the weights (no resident x), and each dequantized
-// weight word feeds MT MFMAs; one workgroup per CU (the ring then takes up
-// to 256 VGPRs).
+// MT > 1 (up to 64 rows): each dequantized weight word feeds MT MFMAs, one
+// per row tile; one workgroup per CU (up to 256 VGPRs).  With resident x
+// (XR, MT = 2) the workgroup walks its tiles once per 32 rows, with those
+// rows' x chunks loaded once per pass (128 VGPRs); without, every item's x
+// chunks of the MT row tiles go through the ring with the weights.
 template <int QM, int GS, int NS, int D, bool XR, bool PK, bool SPL = false, int MT = 1>
 __global__ __launch_bounds__(kQWaves * kWave, MT > 1 ? 1 : 2)
 void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ wqp,
                        const void *__restrict__ scales, const uint16_t *__restrict__ biases, uint16_t *__restrict__ y,
                        int M, int N, int K, int ntn, int per, float *__restrict__ part, int splits)
 {
-    static_assert(MT == 1 || (!XR && !SPL), "several row tiles: x through the ring, invariant form only");
+    static_assert(MT == 1 || !SPL, "the split variant: one row tile");
+    static_assert(!XR || MT <= 2, "resident x: at most two row tiles");
     constexpr int P = kQWaves, TC = NS * 16, CB = qconst_chunk_bytes(QM, GS);
     __shared__ float red[P][16 * MT][TC + 1];
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -387,7 +389,6 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
     else if constexpr (QM == BI_NVFP4) coff = c * 8 + 2 * g;
     else coff = c * 4 + g;
     const uint8_t *cbase = reinterpret_cast<const uint8_t *>(wqp) + (int64_t)nrg * nb * 1024;
-    const uint16_t *xr = x + (int64_t)(c < M ? c : M - 1) * K + g * 32;
     int64_t xoff[MT];                                    // row tile i: row 16 i + c (padding rows read row M - 1)
 #pragma unroll
     for (int i = 0; i < MT; ++i) xoff[i] = (int64_t)(16 * i + c < M ? 16 * i + c : M - 1) * K + g * 32;
@@ -396,15 +397,20 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
     uint4 W[NR][NS];
     uint32_t S[NR][NS];
     uint4 X[XR ? kQXRes : D][MT][4];
-    if constexpr (XR) {
+    // resident x of rows [rb, rb + 16 MT) (rows >= M read row M - 1)
+    auto load_x_res = [&](int rb) {
 #pragma unroll
         for (int j = 0; j < kQXRes; ++j)
             if (j < nmine) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    X[j][0][s] = *reinterpret_cast<const uint4 *>(xr + (kb0 + wave + j * P) * kQBlock + s * 8);
+                for (int i = 0; i < MT; ++i) {
+                    const int row = min(rb + 16 * i + c, M - 1);
+                    const uint16_t *xp = x + (int64_t)row * K + g * 32 + (int64_t)(kb0 + wave + j * P) * kQBlock;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) X[j][i][s] = *reinterpret_cast<const uint4 *>(xp + s * 8);
+                }
             }
-    }
+    };
     int lu = 0, lj = 0;                                     // load cursor: tile t0 + lu, block wave + lj*P
     auto load_item = [&](auto dc_) {
         constexpr int d = decltype(dc_)::value;
@@ -447,7 +453,8 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int jj = 0; jj < NS; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto finish_tile = [&](int u) {
+    // tile u of rows [rb, rb + 16 MT): wave partials added in wave order
+    auto finish_tile = [&](int u, int rb) {
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -460,12 +467,12 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
         const int n0 = (t0 + u) * TC;
         for (int o = threadIdx.x; o < 16 * MT * TC; o += P * kWave) {
             const int r = o / TC, cc = o % TC;
-            if (r >= M || n0 + cc >= N) continue;
+            if (rb + r >= M || n0 + cc >= N) continue;
             float v = red[0][r][cc];
 #pragma unroll
             for (int p = 1; p < P; ++p) v = v + red[p][r][cc];
-            if constexpr (SPL) part[((int64_t)blockIdx.y * M + r) * N + n0 + cc] = v;
-            else y[(int64_t)r * N + n0 + cc] = F16::narrow(v);
+            if constexpr (SPL) part[((int64_t)blockIdx.y * M + rb + r) * N + n0 + cc] = v;
+            else y[(int64_t)(rb + r) * N + n0 + cc] = F16::narrow(v);
         }
         __syncthreads();
     };
@@ -491,19 +498,27 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
 
     if (nmine > 0 && XR) {
         // ring slot j holds block j of the tile in flight: a tile's items are
-        // requested while the previous tile's are multiplied
-        static_for<0, kQXRes>([&](auto jc) {
-            if (decltype(jc)::value < nmine) load_item(jc);
-        });
-        for (int u = 0; u < ntile; ++u) {
+        // requested while the previous tile's are multiplied; one pass over
+        // the tiles per 16 MT rows
+        const int npass = MT == 1 ? 1 : (M + 16 * MT - 1) / (16 * MT);       // M <= 16 with one row tile
+        for (int ps = 0; ps < npass; ++ps) {
+            const int rb = ps * 16 * MT;
+            load_x_res(rb);
+            lu = 0;
+            lj = 0;
             static_for<0, kQXRes>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                if (j < nmine) {
-                    compute_item(jc, jc);
-                    if (u + 1 < ntile) load_item(jc);
-                }
+                if (decltype(jc)::value < nmine) load_item(jc);
             });
-            finish_tile(u);
+            for (int u = 0; u < ntile; ++u) {
+                static_for<0, kQXRes>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    if (j < nmine) {
+                        compute_item(jc, jc);
+                        if (u + 1 < ntile) load_item(jc);
+                    }
+                });
+                finish_tile(u, rb);
+            }
         }
     } else if (nmine > 0) {
         static_for<0, D - 1>([&](auto dc) {
@@ -517,7 +532,7 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
                 if (i + d < items) {
                     compute_item(dc, std::integral_constant<int, 0>{});
                     if (++cj == nmine) {
-                        finish_tile(cu);
+                        finish_tile(cu, 0);
                         cj = 0;
                         ++cu;
                     }
@@ -526,7 +541,9 @@ void qmatmul_stream_kernel(const uint16_t *__restrict__ x, const uint32_t *__res
         }
     } else {
         // a wave that owns no block of K still takes part in every combine
-        for (int u = 0; u < ntile; ++u) finish_tile(u);
+        const int npass = XR && MT > 1 ? (M + 16 * MT - 1) / (16 * MT) : 1;
+        for (int ps = 0; ps < npass; ++ps)
+            for (int u = 0; u < ntile; ++u) finish_tile(u, ps * 16 * MT);
     }
 }
 
@@ -548,7 +565,22 @@ static void launch_q_stream_t(const void *x, const uint32_t *wq, const void *s, 
                       (int)ntn, (int)per, (float *)nullptr, 1);
 }
 
-// 17..64 rows: MT row tiles, x through a 2-deep ring, one workgroup per CU
+// 17..64 rows with at most kQXRes blocks of K per wave: two row tiles with
+// resident x, one pass over the workgroup's tiles per 32 rows, one
+// workgroup per CU
+template <int QM, int GS, bool PK>
+static void launch_q_stream_xr2(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
+                                int64_t N, int64_t K, hipStream_t st)
+{
+    const int64_t ntn = cdiv(N, 16);
+    const int64_t per = cdiv(ntn, (int64_t)device_cu_count()), grid = cdiv(ntn, per);
+    launch_kernel((qmatmul_stream_kernel<QM, GS, 1, 3, true, PK, false, 2>), dim3((unsigned)grid),
+                  dim3(kQWaves * kWave), 0, st, (const uint16_t *)x, wq, s, (const uint16_t *)b, (uint16_t *)y, (int)M,
+                  (int)N, (int)K, (int)ntn, (int)per, (float *)nullptr, 1);
+}
+
+// 17..64 rows, longer K: MT row tiles, x through a 2-deep ring, one
+// workgroup per CU
 template <int QM, int GS, int MT, bool PK>
 static void launch_q_stream_mt(const void *x, const uint32_t *wq, const void *s, const void *b, void *y, int64_t M,
                                int64_t N, int64_t K, hipStream_t st)
@@ -568,6 +600,7 @@ static bool try_launch_q_stream(const void *x, const uint32_t *wq, const void *s
         K >= (1ll << 30))
         return false;
     if (M <= 16) launch_q_stream_t<QM, GS, 1, PK>(x, wq, s, b, y, M, N, K, st);
+    else if (cdiv(K / kQBlock, kQWaves) <= kQXRes) launch_q_stream_xr2<QM, GS, PK>(x, wq, s, b, y, M, N, K, st);
     else if (M <= 32) launch_q_stream_mt<QM, GS, 2, PK>(x, wq, s, b, y, M, N, K, st);
     else launch_q_stream_mt<QM, GS, 4, PK>(x, wq, s, b, y, M, N, K, st);
     return true;

@@ -361,12 +361,15 @@ def test_split_variant_is_correct_but_not_invariant(mode, gs, packed):
 
 @pytest.mark.parametrize("mode,gs", MODES)
 @pytest.mark.parametrize("packed", [False, True])
-def test_up_to_64_rows_equal_row_alone(mode, gs, packed):
+@pytest.mark.parametrize("K", [4096, 640, 5120])
+def test_up_to_64_rows_equal_row_alone(mode, gs, packed, K):
     """17..64 rows take the streaming kernel with two or four row tiles per
-    workgroup (each dequantized weight word feeds every row tile): each row
-    equals the same row alone (one row tile), the outputs stay in bounds, and
-    sampled rows are within the parity gate of the oracle."""
-    K, N = 4096, 1000
+    workgroup (each dequantized weight word feeds every row tile): with x
+    resident (at most 4 blocks of K per wave; K = 640 leaves three waves
+    without a block) in one pass per 32 rows, or through the ring (K = 5120).
+    Each row equals the same row alone (one row tile), the outputs stay in
+    bounds, and sampled rows are within the parity gate of the oracle."""
+    N = 1000
     x, wq, s, b = inputs.qmatmul_case(64, K, N, mode, gs, True, seed=9)
     wqd, sd, bd = dev_q(wq, s, b)
     if packed:
