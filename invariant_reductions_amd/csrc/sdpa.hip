@@ -118,6 +118,41 @@ __device__ inline int64_t attn_row(const AttnShape &sh, int b, int hk, int rl)
     return ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (rl - j * sh.G);
 }
 
+// exp(x) = 2^(x log2 e) by the hardware's base-2 exponential: every
+// attention kernel here computes its exponentials with this one function, so
+// their trees stay bit-compatible with each other.
+__device__ inline float attn_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
+// A DPP lane move inside rows of 16 lanes (every lane active).
+template <int CTRL>
+__device__ inline float dpp_move(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E;          // quad permutes [1,0,3,2] and [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// The xor butterfly over the 16 lanes of a row (partners at distance 1, 2, 4,
+// 8; each lane adds its own value and its partner's).  Distances 1 and 2 are
+// quad permutes; once a quad holds one value, the half-row mirror reaches the
+// partner quad's value, and once a half-row holds one value the row mirror
+// reaches the other half's -- the operands of the xor butterfly, without a
+// trip through the LDS unit.
+__device__ inline float row16_sum(float l)
+{
+    l = l + dpp_move<kDppXor1>(l);
+    l = l + dpp_move<kDppXor2>(l);
+    l = l + dpp_move<kDppHalfMirror>(l);
+    return l + dpp_move<kDppMirror>(l);
+}
+__device__ inline float row16_max(float m)
+{
+    m = fmaxf(m, dpp_move<kDppXor1>(m));
+    m = fmaxf(m, dpp_move<kDppXor2>(m));
+    m = fmaxf(m, dpp_move<kDppHalfMirror>(m));
+    return fmaxf(m, dpp_move<kDppMirror>(m));
+}
+
 // Writes out = RNE(o / l) for the four d values of one quad.
 template <typename S>
 __device__ inline void attn_store_out(uint16_t *dst, float4 o, float l)
@@ -156,13 +191,13 @@ __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, 
             const int c0 = r * kRange, n = min(nch - c0, kRange);
             float Mr = pr[c0 * kPartStride + kHeadDim];
             for (int i = 1; i < n; ++i) Mr = fmaxf(Mr, pr[(c0 + i) * kPartStride + kHeadDim]);
-            float w = expf(pr[c0 * kPartStride + kHeadDim] - Mr);
+            float w = attn_exp(pr[c0 * kPartStride + kHeadDim] - Mr);
             float4 ov = *reinterpret_cast<const float4 *>(pr + c0 * kPartStride + quad * 4);
             float4 orr = make_float4(ov.x * w, ov.y * w, ov.z * w, ov.w * w);
             float lr = pr[c0 * kPartStride + kHeadDim + 1] * w;
             for (int i = 1; i < n; ++i) {
                 const float *pc = pr + (c0 + i) * kPartStride;
-                w = expf(pc[kHeadDim] - Mr);
+                w = attn_exp(pc[kHeadDim] - Mr);
                 ov = *reinterpret_cast<const float4 *>(pc + quad * 4);
                 orr.x = orr.x + ov.x * w;
                 orr.y = orr.y + ov.y * w;
@@ -170,7 +205,7 @@ __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, 
                 orr.w = orr.w + ov.w * w;
                 lr = lr + pc[kHeadDim + 1] * w;
             }
-            const float u = expf(Mr - M);
+            const float u = attn_exp(Mr - M);
             const float4 tv = make_float4(orr.x * u, orr.y * u, orr.z * u, orr.w * u);
             const float tl = lr * u;
             if (r == 0) {
@@ -418,8 +453,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float m = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
-#pragma unroll
-                    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+                    m = row16_max(m);
                     mx[i] = m;
                 }
                 if (c16 == 0) {
@@ -441,7 +475,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const bool vis = sc[kt][i] != -INFINITY;
-                        const float pv = vis ? expf(sc[kt][i] - mx[i]) : 0.0f;
+                        const float pv = vis ? attn_exp(sc[kt][i] - mx[i]) : 0.0f;
                         ls[i] = ls[i] + pv;
                         const uint16_t hi = S::narrow(pv);
                         phi[wave][g4 * 4 + i][kt * 16 + c16] = hi;
@@ -450,8 +484,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float l = ls[i];
-#pragma unroll
-                    for (int off = 1; off < 16; off <<= 1) l = l + __shfl_xor(l, off, kWave);
+                    l = row16_sum(l);
                     ls[i] = l;
                 }
                 if (c16 == 0) {
@@ -511,7 +544,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
 #pragma unroll
                             for (int e = 0; e < 8; ++e) ro[e] = oc[e];
                         } else {
-                            const float mn = fmaxf(rM, mc), a = expf(rM - mn), bw = expf(mc - mn);
+                            const float mn = fmaxf(rM, mc), a = attn_exp(rM - mn), bw = attn_exp(mc - mn);
                             rl = rl * a + lc * bw;
 #pragma unroll
                             for (int e = 0; e < 8; ++e) ro[e] = ro[e] * a + oc[e] * bw;
@@ -717,8 +750,13 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
 #pragma unroll
         for (int j = 0; j < 8; ++j) dst[s2][j][lane] = vr[j];
     };
+    // A row's last key grows with its position, so the first row of a tile
+    // with no padding rows sees the fewest keys: a unit that row sees in full
+    // is seen in full by the whole tile and needs no mask.
+    const int lkfull = rt0 + 15 < R ? attn_last_key(kvlen, Qi, rt0 / sh.G, sh.causal) : -1;
+    auto unit_full = [&](int u) { return (u >> 2) * kChunk + (u & 3) * kKeysPerWave + kKeysPerWave - 1 <= lkfull; };
     // scores of unit u for this wave's rows, masked (-inf outside a row's keys)
-    auto scores = [&](const KStage &ks_, int u, float (&sc)[4][4]) __attribute__((always_inline)) {
+    auto scores = [&](const KStage &ks_, int u, bool full, float (&sc)[4][4]) __attribute__((always_inline)) {
         const int keyq = (u >> 2) * kChunk + (u & 3) * kKeysPerWave;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -726,10 +764,15 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
 #pragma unroll
             for (int st = 0; st < 4; ++st) acc = mfma16<S>(qf[st], ks_[kt][st][lane], acc);
             const int key = keyq + kt * 16 + c16;
+            if (full) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool vis = ok[i] && key >= 0 && key <= lk[i];
-                sc[kt][i] = vis ? acc[i] * sh.scale : -INFINITY;
+                for (int i = 0; i < 4; ++i) sc[kt][i] = acc[i] * sh.scale;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool vis = ok[i] && key >= 0 && key <= lk[i];
+                    sc[kt][i] = vis ? acc[i] * sh.scale : -INFINITY;
+                }
             }
         }
     };
@@ -744,12 +787,11 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
         if (u + 1 < nunits) stage_k(nxt, u + 1);
         if (wave_rows) {
             float sc[4][4];
-            scores(cur, u, sc);
+            scores(cur, u, unit_full(u), sc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float m = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+                m = row16_max(m);
                 mc[i] = fmaxf(mc[i], m);
             }
             if ((u & 3) == 3) {
@@ -786,7 +828,8 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
             for (int i = 0; i < 4; ++i) mrow[i] = mstore[wave][g4 * 4 + i][c];
         }
         float sc[4][4];
-        scores(kcur, u, sc);
+        const bool full = unit_full(u);
+        scores(kcur, u, full, sc);
         // probabilities, this quarter's row sums, P as hi and lo parts
         float ls[4];
 #pragma unroll
@@ -795,8 +838,8 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool vis = sc[kt][i] != -INFINITY;
-                const float pv = vis ? expf(sc[kt][i] - mrow[i]) : 0.0f;
+                const bool vis = full || sc[kt][i] != -INFINITY;
+                const float pv = vis ? attn_exp(sc[kt][i] - mrow[i]) : 0.0f;
                 ls[i] = ls[i] + pv;
                 const uint16_t hi = S::narrow(pv);
                 phi[wave][g4 * 4 + i][kt * 16 + c16] = hi;
@@ -805,8 +848,7 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float l = ls[i];
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) l = l + __shfl_xor(l, off, kWave);
+            l = row16_sum(l);
             lc[i] = qq == 0 ? l : lc[i] + l;
         }
         // this quarter's o: P (16 x 64) . V (64 x 128), lo parts first
@@ -830,7 +872,7 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (!(ok[i] && lk[i] >= c * kChunk)) continue;
-                const float w = expf(mrow[i] - M[i]);
+                const float w = attn_exp(mrow[i] - M[i]);
                 if (c == 0) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) orr[j][i] = oc[j][i] * w;
@@ -888,7 +930,7 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
         if (!ok[i] || lk[i] < 0) continue;
         const int r = rt0 + g4 * 4 + i, j = r / sh.G;
         const int64_t row = ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (r - j * sh.G);
-        const float u = expf(M[i] - M[i]);
+        const float u = attn_exp(M[i] - M[i]);
         const float l = lr[i] * u;
         uint16_t o8[8];
 #pragma unroll
@@ -965,13 +1007,13 @@ void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict
 #pragma unroll
             for (int i = 1; i < kRange; ++i)
                 if (i < n) Mr = fmaxf(Mr, mv[i]);
-            float w = expf(mv[0] - Mr);
+            float w = attn_exp(mv[0] - Mr);
             orr = make_float4(ov[0].x * w, ov[0].y * w, ov[0].z * w, ov[0].w * w);
             lr = lv[0] * w;
 #pragma unroll
             for (int i = 1; i < kRange; ++i) {
                 if (i < n) {
-                    w = expf(mv[i] - Mr);
+                    w = attn_exp(mv[i] - Mr);
                     orr.x = orr.x + ov[i].x * w;
                     orr.y = orr.y + ov[i].y * w;
                     orr.z = orr.z + ov[i].z * w;
@@ -987,7 +1029,7 @@ void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict
             for (int i = 1; i < nr; ++i) M = fmaxf(M, rmax[i]);
         }
         if (r < nr) {
-            const float u = expf(Mr - M);
+            const float u = attn_exp(Mr - M);
             *reinterpret_cast<float4 *>(&term[slot][quad * 4]) =
                 make_float4(orr.x * u, orr.y * u, orr.z * u, orr.w * u);
             if (quad == 0) term[slot][kHeadDim] = lr * u;
