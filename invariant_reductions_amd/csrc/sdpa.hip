@@ -12,11 +12,14 @@
 //   keys [256c, 256c + 256) and is handled by one workgroup for all query rows
 //   of one (sequence, KV head).  Inside the chunk, wave w owns keys
 //   [64w, 64w + 64):
-//     s_t   = scale * (q . k_t)      one 16x16x32 MFMA chain over d (4 steps;
+//     s_t   = (scale log2 e) * (q . k_t)   the score in base-2 units (the
+//                                    constant rounded once); q . k_t is one
+//                                    16x16x32 MFMA chain over d (4 steps;
 //                                    step s takes d in [32s, 32s + 32), lane
 //                                    group g supplies the 8 at 32s + 8g)
 //     m_c   = max of s_t over the chunk's keys t <= p (exact, order-free)
-//     p_t   = exp(s_t - m_c); keys t > p contribute exactly +0
+//     p_t   = 2^(s_t - m_c) (= exp of the natural-unit difference; the
+//             hardware's base-2 exponential); keys t > p contribute exactly +0
 //     l_c   = sum p_t: per lane over its 4 key tiles in order, then a xor
 //             butterfly over the 16 lanes of a row (1, 2, 4, 8), then waves in
 //             order 0..3
@@ -26,10 +29,10 @@
 //             then the four wave partials added in order 0..3
 //   Ranges -- chunks are grouped in ranges of kRange = 16 (4096 keys); for the
 //   chunks 16r .. min(16r + 15, floor(p / 256)) of range r:
-//     M_r = max m_c (exact);  w_c = exp(m_c - M_r)
+//     M_r = max m_c (exact);  w_c = 2^(m_c - M_r)
 //     o_r = sum o_c * w_c and l_r = sum l_c * w_c in ascending c
 //   Row -- over the ranges 0 .. floor(p / 4096):
-//     M = max M_r (exact);  u_r = exp(M_r - M)
+//     M = max M_r (exact);  u_r = 2^(M_r - M)
 //     o = sum o_r * u_r and l = sum l_r * u_r in ascending r;  out = RNE(o / l)
 // A query row never meets another row except inside an MFMA (rows are
 // independent there), so the number of queries Q, the GQA group, the batch and
@@ -71,7 +74,7 @@ template <> __device__ inline f32x4 mfma16<F16>(uint4 a, uint4 b, f32x4 c) { ret
 struct AttnShape {
     int64_t B, Q, Lcap, nchunks, nranges, max_kv, nmg;  // nmg: row groups of mgt 16-row tiles per (b, c, hk)
     int Hq, Hkv, G, mgt;
-    float scale;
+    float scale;          // the base-2 score scale: the caller's scale x log2(e)
     int causal;
     int64_t ks, hs;       // cache strides (elements) between consecutive keys and between KV heads
     int cps;              // chunks per work item: 1; the split variant's run; WHOLE: all of them
@@ -118,10 +121,14 @@ __device__ inline int64_t attn_row(const AttnShape &sh, int b, int hk, int rl)
     return ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (rl - j * sh.G);
 }
 
-// exp(x) = 2^(x log2 e) by the hardware's base-2 exponential: every
-// attention kernel here computes its exponentials with this one function, so
-// their trees stay bit-compatible with each other.
-__device__ inline float attn_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+// Scores are kept in base-2 units: s = (q . k) x scale log2(e), the constant
+// rounded once on the host (AttnShape::scale), so that every exponential of
+// the softmax -- exp(s_nat - m_nat) = 2^(s - m) -- is the hardware's base-2
+// exponential of a difference.  Every attention kernel here takes its
+// exponentials from this one function and its scores from that one
+// constant, so their trees stay bit-compatible with each other.
+constexpr float kLog2e = 1.44269504088896341f;
+__device__ inline float attn_exp(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A DPP lane move inside rows of 16 lanes (every lane active).
 template <int CTRL>
@@ -151,6 +158,21 @@ __device__ inline float row16_max(float m)
     m = fmaxf(m, dpp_move<kDppXor2>(m));
     m = fmaxf(m, dpp_move<kDppHalfMirror>(m));
     return fmaxf(m, dpp_move<kDppMirror>(m));
+}
+
+// RNE of two floats to the 16-bit type, packed (a in the low half), by one
+// packed conversion.
+template <typename S>
+__device__ inline uint32_t narrow2(float a, float b)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    if constexpr (std::is_same_v<S, BF16>) {
+        typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
+    } else {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
+    }
 }
 
 // Writes out = RNE(o / l) for the four d values of one quad.
@@ -830,21 +852,34 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
         float sc[4][4];
         const bool full = unit_full(u);
         scores(kcur, u, full, sc);
-        // probabilities, this quarter's row sums, P as hi and lo parts
+        // probabilities, this quarter's row sums (0 + p = p: the first term
+        // is taken as it is, p being never -0), P as hi and lo parts -- rows
+        // 4 g4 + i and 4 g4 + i + 1 converted together; the unmasked form for
+        // units the whole tile sees
         float ls[4];
+        auto probs = [&](auto full_) __attribute__((always_inline)) {
+            constexpr bool FULL = decltype(full_)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ls[i] = 0.0f;
+            for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+                for (int i = 0; i < 4; i += 2) {
+                    float pv[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool vis = full || sc[kt][i] != -INFINITY;
-                const float pv = vis ? attn_exp(sc[kt][i] - mrow[i]) : 0.0f;
-                ls[i] = ls[i] + pv;
-                const uint16_t hi = S::narrow(pv);
-                phi[wave][g4 * 4 + i][kt * 16 + c16] = hi;
-                plo[wave][g4 * 4 + i][kt * 16 + c16] = S::narrow(pv - S::widen(hi));
-            }
+                    for (int h = 0; h < 2; ++h) {
+                        const float x = sc[kt][i + h];
+                        pv[h] = FULL || x != -INFINITY ? attn_exp(x - mrow[i + h]) : 0.0f;
+                        ls[i + h] = kt == 0 ? pv[h] : ls[i + h] + pv[h];
+                    }
+                    const uint32_t hp = narrow2<S>(pv[0], pv[1]);
+                    const uint32_t lp = narrow2<S>(pv[0] - S::widen((uint16_t)hp), pv[1] - S::widen((uint16_t)(hp >> 16)));
+                    phi[wave][g4 * 4 + i][kt * 16 + c16] = (uint16_t)hp;
+                    phi[wave][g4 * 4 + i + 1][kt * 16 + c16] = (uint16_t)(hp >> 16);
+                    plo[wave][g4 * 4 + i][kt * 16 + c16] = (uint16_t)lp;
+                    plo[wave][g4 * 4 + i + 1][kt * 16 + c16] = (uint16_t)(lp >> 16);
+                }
+        };
+        if (full) probs(std::true_type{});
+        else probs(std::false_type{});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float l = ls[i];
@@ -1111,7 +1146,7 @@ static AttnPlan attn_plan(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Lcap
     const int64_t nch = cdiv(cdiv(max_kv_len, kChunk), cps);            // partials per row
     AttnPlan p;
     p.sh = AttnShape{B, Q, Lcap, nch, cdiv(nch, kRange), max_kv_len, cdiv(ntm, mgt), Hq, Hkv, (int)G, (int)mgt,
-                     scale, causal ? 1 : 0, ks, hs, cps, nch};
+                     scale * kLog2e, causal ? 1 : 0, ks, hs, cps, nch};
     // item ids (padded to whole groups of 8); a persistent grid of two
     // workgroups per CU, a multiple of 8 so that a workgroup stays on one XCD
     p.nid = cdiv(B * nch, 8) * 8 * Hkv * p.sh.nmg;
