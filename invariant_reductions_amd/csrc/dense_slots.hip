@@ -317,8 +317,12 @@ static void launch_slots_mt(const void *x, const void *w, void *y, void *ws, int
         // Few column tiles: 64-column tiles with pairs of slots (four groups)
         // give as many workgroups as 128-column tiles with single slots, but
         // half the group sums to exchange and a quarter for the last arriver
-        // to read.
-        launch_slots_t<S, MT, 2, EPI, PK, 4>(x, w, y, ws, M, N, K, st);
+        // to read; 96-column tiles where those fill the CUs more evenly
+        // (6144 columns: 256 workgroups instead of 384).
+        if (cu_balance(cdiv(N, 6 * 16) * 4, cu) > cu_balance(cdiv(N, 4 * 16) * 4, cu) + 0.02)
+            launch_slots_t<S, MT, 2, EPI, PK, 6>(x, w, y, ws, M, N, K, st);
+        else
+            launch_slots_t<S, MT, 2, EPI, PK, 4>(x, w, y, ws, M, N, K, st);
     } else {
         if (ntc * 4 >= cu) launch_slots_t<S, MT, 2, EPI, PK>(x, w, y, ws, M, N, K, st);
         else launch_slots_t<S, MT, 1, EPI, PK>(x, w, y, ws, M, N, K, st);
