@@ -45,7 +45,9 @@ def same(a, b):
     (33, 4096, 14336),     # the down projection, 112 blocks
     (64, 4096, 4096),
     (64, 1000, 4224),      # 33 blocks: uneven slots
-    (64, 6144, 4096),
+    (64, 6144, 4096),      # 96-column tiles: 256 workgroups instead of 384
+    (64, 6000, 4096),      # ... the last tile ragged (48 columns)
+    (40, 5008, 1024),      # ... the last tile one wave wide
     (32, 32768, 1024),     # enough column tiles for all eight slots in one workgroup
     (64, 32768, 1024),
     (64, 28656, 256),      # 7-wave (112-column) tiles fill 256 CUs; last tile ragged
@@ -132,6 +134,8 @@ def test_run_to_run_determinism():
     (17, 14336, 4096),     # the fused slot kernel, 32-row form
     (40, 192, 896),        # few column tiles: slot groups exchange partial sums
     (64, 14336, 4096),     # the decoder's MLP at batch 64
+    (64, 3072, 4096),      # 96-column tiles
+    (40, 2504, 1024),      # 96-column tiles, the last one wave wide
     (64, 640, 4224),
     (17, 14328, 256),      # 7-wave tiles, last tile ragged
     (33, 200, 512),        # F not a multiple of 64: 8-row interleave blocks across tiles
