@@ -329,11 +329,14 @@ extern "C" const char *bi_build_info(void)
            " matmul: v_mfma_f32_16x16x32_bf16/f16 and v_mfma_f32_16x16x4_f32 for every M,"
            " K blocks of 128 (16-bit) / 16 (f32), block b in slot b%8 of 8, each slot summed in block order,"
            " slots added pairwise ((0+1)+(2+3))+((4+5)+(6+7));"
-           " qmatmul: dequantize to binary16 in registers, v_mfma_f32_16x16x32_f16, same K slicing;"
+           " qmatmul: dequantize to binary16 in registers, v_mfma_f32_16x16x32_f16, same K slicing,"
+           " each dequantized word feeding every row tile of up to 32 rows;"
            " rmsnorm: one wave per row, 16-byte chunk v to lane v%64, per-lane fma fold, xor butterfly 32..1;"
-           " sdpa: chunks of 256 keys, 4 waves x 64 keys, P as hi+lo 16-bit parts in MFMA (lo first),"
-           " chunk partials merged in ranges of 16 chunks (weights exp(m_c-M_r), ascending), ranges merged"
-           " in ascending order (weights exp(M_r-M)); prompts (>= 128 query rows per KV head, <= 4096 keys):"
+           " sdpa: scores in base-2 units (scale*log2e rounded once), exponentials 2^x by v_exp_f32,"
+           " chunks of 256 keys, 4 waves x 64 keys, P as hi+lo 16-bit parts in MFMA (lo first),"
+           " chunk partials merged in ranges of 16 chunks (weights 2^(m_c-M_r), ascending), ranges merged"
+           " in ascending order (weights 2^(M_r-M)); many short groups: one launch, the merge in the"
+           " workgroup; prompts (>= 128 query rows per KV head, <= 4096 keys):"
            " the same tree in one launch, one wave playing the 4 quarters of a chunk;"
            " dense M > 64: the same K tree walked slot by slot, x/W tiles shared through LDS";
 }
