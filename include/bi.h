@@ -318,7 +318,10 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
  *            sequence's outputs unwritten or wrong, never touches memory
  *            outside the buffers).
  *   Query head h reads key/value head h / (Hq / Hkv); Hq % Hkv == 0.
- *   D must be 128 in this build.  scale is applied to q.k in fp32.
+ *   D must be 128 in this build.  scale is applied to q.k in fp32, in
+ *   base-2 units: s = (q.k) * (scale * log2 e) with the constant rounded once
+ *   on the host, and every exponential of the softmax is 2^x -- the same
+ *   softmax, with exponentials the hardware computes directly.
  *   ws     : device workspace of at least bi_sdpa_workspace_bytes(...) bytes
  *            (the chunk partials), 16-byte aligned; its contents on entry are
  *            ignored.  Calls that share a workspace must be ordered (same
@@ -329,7 +332,11 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
  * The chunk and range a key falls in depend only on its position, and chunks
  * past a query's last key are never merged, so a row's bits do not depend on
  * B, Q, the other rows or the launch.  Decode and verify shapes take two
- * launches: the chunk partials (in ws), then the range and row levels.
+ * launches: the chunk partials (in ws), then the range and row levels; with
+ * at least two (sequence, KV head) groups of at most 16 query rows per CU
+ * over at most 1024 keys, one launch in which a workgroup walks a group's
+ * chunks, writes the same partials (in ws) and runs the range and row
+ * levels for the group's rows itself.
  * Prompts -- at least 128 query rows per KV head (Q * Hq / Hkv >= 128) and
  * max_kv_len <= 4096 (one range) -- take one launch that computes the same
  * tree per block of 128 query rows without partials (ws is then unused, but
