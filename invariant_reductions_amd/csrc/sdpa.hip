@@ -40,7 +40,10 @@
 // verify block and a lone query at the same position reduce identically.
 //
 // The chunk level is one launch (attn_kernel); the range and row levels are a
-// second (attn_merge_kernel), one workgroup per query row.
+// second (attn_merge_kernel), one workgroup per query row -- or, for many
+// short (sequence, KV head) groups, the same workgroup that wrote a group's
+// chunk partials (attn_kernel's WHOLE form, one launch); prompts take
+// attn_prefill_kernel, one launch without partials.
 #include <algorithm>
 #include <mutex>
 
