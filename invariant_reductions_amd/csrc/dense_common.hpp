@@ -161,4 +161,12 @@ template <typename S>
 void launch_dense_tile(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K, bool packed,
                        hipStream_t st);
 
+// The slot form over 64-row chunks for 64 < M <= kSlotRowsMax
+// (dense_slots.hip): 16-bit types, transposed or packed W, K % 128 == 0, x
+// and W 16-byte aligned, N, K < 2^30.
+constexpr int64_t kSlotRowsMax = 512;
+template <typename S>
+void launch_dense_slot_rows(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K, bool packed,
+                            hipStream_t st);
+
 }  // namespace bi

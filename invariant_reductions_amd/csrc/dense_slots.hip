@@ -62,6 +62,14 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, c = lane & 15;
     const int ct = blockIdx.x, grp = blockIdx.y;
+    // Row chunk blockIdx.z: rows [TR z, TR z + TR) of a call with more rows
+    // than one tile (only with all eight slots in the workgroup: no exchange)
+    {
+        const int64_t r0 = (int64_t)blockIdx.z * TR;
+        x += r0 * K;
+        y += r0 * (EPI == EPI_Y ? N : N / 2);
+        M -= r0;
+    }
     const int nb = (int)(K / KB);
     const int slot0 = grp * Q;
     const int nsteps = slot0 < nb ? (nb - slot0 + P - 1) / P : 0;
@@ -290,6 +298,31 @@ static void launch_slots_t(const void *x, const void *w, void *y, void *ws, int6
     launch_kernel((dense_slots_kernel<S, MT, Q, DW, OCC, EPI, NW, PK>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
                        dim3(NW * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, counters, M, N, K);
 }
+
+// More than 64 rows, few column tiles (bi_matmul's path, dense.hip): one
+// workgroup of 4 waves per (64-column tile, 64-row chunk) with all eight
+// slots -- no exchange, no workspace -- the row chunks of a column tile
+// reading the same W strip.  16-bit types, transposed or packed W, K a
+// multiple of the block, x and W 16-byte aligned, M <= kSlotRowsMax.
+template <typename S>
+void launch_dense_slot_rows(const void *x, const void *w, void *y, int64_t M, int64_t N, int64_t K, bool packed,
+                            hipStream_t st)
+{
+    using T = typename S::store_t;
+    constexpr int NW = 4;
+    const int64_t ntc = cdiv(N, NW * 16), nrc = cdiv(M, 64);
+    const dim3 grid((unsigned)ntc, 1u, (unsigned)nrc);
+    if (packed)
+        launch_kernel((dense_slots_kernel<S, 4, 8, 2, 2, EPI_Y, NW, true>), grid, dim3(NW * kWave), 0, st,
+                      (const T *)x, (const T *)w, (T *)y, (float *)nullptr, (unsigned *)nullptr, M, N, K);
+    else
+        launch_kernel((dense_slots_kernel<S, 4, 8, 2, 2, EPI_Y, NW, false>), grid, dim3(NW * kWave), 0, st,
+                      (const T *)x, (const T *)w, (T *)y, (float *)nullptr, (unsigned *)nullptr, M, N, K);
+}
+template void launch_dense_slot_rows<BF16>(const void *, const void *, void *, int64_t, int64_t, int64_t, bool,
+                                           hipStream_t);
+template void launch_dense_slot_rows<F16>(const void *, const void *, void *, int64_t, int64_t, int64_t, bool,
+                                          hipStream_t);
 
 // Share of the CUs busy over the rounds of a grid of `tiles` one-per-CU workgroups.
 static double cu_balance(int64_t tiles, int64_t cu) { return (double)tiles / (double)(cdiv(tiles, cu) * cu); }

@@ -1,14 +1,16 @@
-"""The LDS-tiled dense kernel for long M (M > 128, or M > 64 with at least
-192 column tiles of 128; 16-bit, transposed or tile-packed weights, K a
-multiple of 128 and at least 1024) and the streaming kernel it hands the
-other M > 64 shapes to: every row equals the same row computed alone (M = 1
-takes the streaming kernel), across ragged M and N, K with an uneven number
-of blocks per slot, both weight layouts and both 16-bit types; the outputs
-stay inside their bounds; sampled rows are within the parity gate of the
-oracle.  This is the
-invariance of "Fix/speculative shape invariance" (Problem: the same row must
-not change with the number of rows) and "Batch-invariant kernels" (Case 3)
-for verify blocks and prompts.
+"""The dense kernels for long M: the slot form over 64-row chunks (up to 512
+rows where 128 x 128 tiles would not fill the CUs: one workgroup per
+(64-column tile, 64-row chunk) with all eight slots), the LDS-tiled kernel
+(M > 128, or M > 64 with at least 192 column tiles of 128; K at least 1024)
+and the streaming kernel they hand the other M > 64 shapes to (16-bit,
+transposed or tile-packed weights, K a multiple of 128): every row equals the
+same row computed alone (M = 1 takes the streaming kernel), across ragged M
+and N, K with an uneven number of blocks per slot, both weight layouts and
+both 16-bit types; the outputs stay inside their bounds; sampled rows are
+within the parity gate of the oracle.  This is the invariance of
+"Fix/speculative shape invariance" (Problem: the same row must not change
+with the number of rows) and "Batch-invariant kernels" (Case 3) for verify
+blocks and prompts.
 
 Workload: W [N,K] ~ N(0,1)*0.02 then x [M,K] ~ N(0,1), rounded to the dtype."""
 import numpy as np
@@ -23,8 +25,18 @@ from invariant_reductions_amd import inputs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,N,K", [(65, 100, 1024), (128, 4096, 4096), (80, 24577, 1024), (129, 6144, 4096),
-                                   (320, 512, 1152), (300, 1000, 14336), (1000, 2048, 4096), (4096, 256, 2048)])
+@pytest.mark.parametrize("M,N,K", [
+    (65, 100, 1024),        # slot form over row chunks: one chunk of 64 plus one row
+    (128, 4096, 4096),      # ... two full chunks
+    (80, 24577, 1024),      # ... 193 ragged column tiles
+    (129, 6144, 4096),      # ... a last chunk of one row
+    (320, 512, 1152),       # ... five chunks, 9 blocks of K
+    (300, 1000, 14336),     # ... ragged chunk and column tile, 112 blocks of K
+    (512, 640, 256),        # ... the most rows it takes, 2 blocks of K
+    (200, 28672, 1024),     # LDS-tiled kernel: enough 128 x 128 tiles
+    (1000, 2048, 4096),     # ... more rows than the slot form takes
+    (4096, 256, 2048),
+    (200, 28672, 512)])     # streaming kernel: enough tiles, K below 1024
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("packed", [False, True])
 def test_long_m_rows_equal_row_alone(M, N, K, dtype, packed):
@@ -39,7 +51,7 @@ def test_long_m_rows_equal_row_alone(M, N, K, dtype, packed):
     rows = sorted({0, 1, 15, 16, 63, 64, M // 2, M - 2, M - 1})
     for i in rows:
         assert bits_equal(to_np(bi.matmul(xd[i:i + 1].contiguous(), wt)), y[i:i + 1]), f"row {i}"
-    # a block of 80 rows (the slot-free tile path again, other tile positions)
+    # the last 80 rows (other tile and chunk positions)
     lo = max(0, M - 80)
     assert bits_equal(to_np(bi.matmul(xd[lo:].contiguous(), wt)), y[lo:])
     assert_parity(y[rows], oracle.matmul(np.ascontiguousarray(x[rows]), w, dtype, True), dtype)
