@@ -669,7 +669,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
 
 // Prompts (many query rows per KV head, at most 4096 keys: one range).  One
 // workgroup of 8 waves per (sequence, KV head, block of 128 query rows),
-// heaviest blocks first; wave w owns the block's 16-row tile w and plays all
+// heaviest blocks of all sequences and heads first; wave w owns the block's 16-row tile w and plays all
 // four key quarters of every chunk itself -- the "waves" of the chunk tree
 // are the quarters [64q, 64q + 64) of a chunk, whoever computes them -- so a
 // chunk's max, l and o are combined in registers in the tree's order and no
@@ -702,10 +702,12 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g4 = lane >> 4, c16 = lane & 15;
     const int R = (int)sh.Q * sh.G, Qi = (int)sh.Q;
-    // block id -> (b, hk, row block), the blocks of the latest positions first
-    const int per = sh.Hkv * nrb;
-    const int b = (int)blockIdx.x / per, rem = (int)blockIdx.x - b * per;
-    const int hk = rem / nrb, rb = nrb - 1 - (rem - (rem / nrb) * nrb);
+    // block id -> (row block, b, hk): the row blocks of the latest positions
+    // (the most keys) of every (sequence, KV head) first, so the dispatcher
+    // hands out the heaviest workgroups first and the lightest fill in last
+    const int ng = (int)sh.B * sh.Hkv;
+    const int rbi = (int)blockIdx.x / ng, gi = (int)blockIdx.x - rbi * ng;
+    const int rb = nrb - 1 - rbi, b = gi / sh.Hkv, hk = gi - b * sh.Hkv;
     const int kvlen = (int)min((int64_t)kv_len[b], sh.max_kv);
     const int rt0 = rb * kPreRows + wave * 16;                  // this wave's tile
     const int rlast = min(rb * kPreRows + kPreRows, R) - 1;     // the block's last row
