@@ -412,11 +412,12 @@ static void launch_dense(const void *x, const void *w, void *y, float *part, int
         // or at least 192 column tiles; a single row tile of a narrow matrix
         // (a verify block of 16 sequences on a 4096-column projection) stays
         // on the streaming kernel, which spreads it over every CU
-        // Up to 512 rows where the 128 x 128 tiles would not fill the CUs
-        // (a verify block on a 4096- or 6144-column projection: 96 or 144
-        // tiles): the slot form, one workgroup per (64-column tile, 64-row
-        // chunk), all eight slots in it
-        if (plain && M > 64 && M <= kSlotRowsMax && cdiv(M, 128) * cdiv(N, 128) < device_cu_count() &&
+        // Up to 512 rows where the 128 x 128 tiles would fill under 5/8 of
+        // the CUs (a verify block on a 4096- or 6144-column projection: 96 or
+        // 144 tiles; with 224 tiles and more the tiled kernel is ahead): the
+        // slot form, one workgroup per (64-column tile, 64-row chunk), all
+        // eight slots in it
+        if (plain && M > 64 && M <= kSlotRowsMax && cdiv(M, 128) * cdiv(N, 128) * 8 < 5 * (int64_t)device_cu_count() &&
             layout != W_NATURAL && K % 128 == 0 && host_aligned16(x) && host_aligned16(w) && N < (1ll << 30) &&
             K < (1ll << 30)) {
             launch_dense_slot_rows<S>(x, w, y, M, N, K, layout == W_PACKED, st);

@@ -1,8 +1,8 @@
 """The dense kernels for long M: the slot form over 64-row chunks (up to 512
-rows where 128 x 128 tiles would not fill the CUs: one workgroup per
-(64-column tile, 64-row chunk) with all eight slots), the LDS-tiled kernel
-(M > 128, or M > 64 with at least 192 column tiles of 128; K at least 1024)
-and the streaming kernel they hand the other M > 64 shapes to (16-bit,
+rows where 128 x 128 tiles would fill under 5/8 of the CUs: one workgroup
+per (64-column tile, 64-row chunk) with all eight slots), the LDS-tiled
+kernel (M > 128, or M > 64 with at least 192 column tiles of 128; K at least
+1024) and the streaming kernel they hand the other M > 64 shapes to (16-bit,
 transposed or tile-packed weights, K a multiple of 128): every row equals the
 same row computed alone (M = 1 takes the streaming kernel), across ragged M
 and N, K with an uneven number of blocks per slot, both weight layouts and
@@ -28,7 +28,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("M,N,K", [
     (65, 100, 1024),        # slot form over row chunks: one chunk of 64 plus one row
     (128, 4096, 4096),      # ... two full chunks
-    (80, 24577, 1024),      # ... 193 ragged column tiles
+    (80, 24577, 1024),      # LDS-tiled kernel: one row tile, 193 ragged column tiles
     (129, 6144, 4096),      # ... a last chunk of one row
     (320, 512, 1152),       # ... five chunks, 9 blocks of K
     (300, 1000, 14336),     # ... ragged chunk and column tile, 112 blocks of K
