@@ -488,13 +488,13 @@ def sdpa_launches(B, Q, Hq, Hkv, Lk, cus):
     """Kernels one bi_sdpa call launches on a GPU of `cus` compute units: one
     for a prompt (at least 128 query rows per KV head, at most 4096 keys: the
     prompt-shaped kernel) and for at least 2 * cus (sequence, KV head) groups
-    of at most 16 query rows over at most 1024 keys (one workgroup walks a
+    of at most 32 query rows over at most 1024 keys (one workgroup walks a
     group's chunks and merges them), else two (chunk partials, then the
     merge)."""
     R = Q * (Hq // Hkv)
     if R >= 128 and Lk <= 4096:
         return 1
-    return 1 if R <= 16 and Lk <= 1024 and B * Hkv >= 2 * cus else 2
+    return 1 if R <= 32 and Lk <= 1024 and B * Hkv >= 2 * cus else 2
 
 
 def op_sweep(torch, bi, dev):

@@ -333,7 +333,7 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
  * past a query's last key are never merged, so a row's bits do not depend on
  * B, Q, the other rows or the launch.  Decode and verify shapes take two
  * launches: the chunk partials (in ws), then the range and row levels; with
- * at least two (sequence, KV head) groups of at most 16 query rows per CU
+ * at least two (sequence, KV head) groups of at most 32 query rows per CU
  * over at most 1024 keys, one launch in which a workgroup walks a group's
  * chunks, writes the same partials (in ws) and runs the range and row
  * levels for the group's rows itself.

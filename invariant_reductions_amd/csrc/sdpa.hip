@@ -279,7 +279,7 @@ __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, 
 // to price the invariant tree.
 //
 // WHOLE: the invariant tree for many (sequence, KV head) groups of at most
-// 16 query rows (nmg == 1): the item is a group with all its chunks, walked
+// 32 query rows (nmg == 1): the item is a group with all its chunks, walked
 // in order by one workgroup; every chunk's partial is written exactly as
 // above, and after the last one the same workgroup reads them back and runs
 // attn_merge_kernel's range and row levels for the group's rows -- one
@@ -1163,7 +1163,7 @@ static AttnPlan attn_plan(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Lcap
 }
 
 // Short contexts (at most kWholeMaxChunks chunks) with at least one
-// (sequence, KV head) group of at most 16 query rows for each of the
+// (sequence, KV head) group of at most 32 query rows for each of the
 // persistent grid's workgroups (two per CU): one work item per group with
 // all its chunks, merged in the workgroup (attn_kernel's WHOLE form) --
 // every workgroup is busy without cutting the groups into chunks, and the
@@ -1178,7 +1178,7 @@ constexpr int64_t kWholeMaxChunks = 4;
 
 static bool attn_whole(const AttnPlan &p)
 {
-    return p.sh.nmg == 1 && p.sh.Q * p.sh.G <= 16 && p.sh.nchunks <= kWholeMaxChunks &&
+    return p.sh.nmg == 1 && p.sh.Q * p.sh.G <= 32 && p.sh.nchunks <= kWholeMaxChunks &&
            p.sh.B * p.sh.Hkv >= 2 * (int64_t)device_cu_count() && p.sh.cps == 1;
 }
 

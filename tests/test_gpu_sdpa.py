@@ -253,15 +253,16 @@ def test_prompt_kernel_rows_equal_lone_queries(causal, head_major):
         assert_parity(full[:, j:j + 1], ref, "bf16", f"row {j}")
 
 
-@pytest.mark.parametrize("Q,head_major", [(1, False), (1, True), (4, False)])
+@pytest.mark.parametrize("Q,head_major", [(1, False), (1, True), (4, False), (5, False), (8, True)])
 def test_whole_group_form_equals_lone_sequences(Q, head_major):
-    """At least two (sequence, KV head) groups of at most 16 query rows per
+    """At least two (sequence, KV head) groups of at most 32 query rows per
     CU over at most 1024 keys: one workgroup walks all of a group's chunks and
     merges them itself, with no merge launch.  Each sequence must equal the
     same sequence run alone (chunk items, then the merge launch), with ragged
     lengths on both sides of the chunk edges (256 keys), both cache layouts
-    and a causal block of 4; sampled sequences are within the parity gate of
-    the oracle.  K, V, q ~ N(0,1) bf16 drawn on the device (seeded)."""
+    and causal blocks of 4, 5 (a verify block: two row tiles) and 8; sampled
+    sequences are within the parity gate of the oracle.  K, V, q ~ N(0,1)
+    bf16 drawn on the device (seeded)."""
     cus = torch.cuda.get_device_properties(dev()).multi_processor_count
     B, Lcap = -(-2 * cus // HKV), 1024
     g = torch.Generator(device=dev()).manual_seed(40 + Q + 2 * head_major)
@@ -269,7 +270,7 @@ def test_whole_group_form_equals_lone_sequences(Q, head_major):
     kd = torch.randn(shape, generator=g, device=dev()).to(torch.bfloat16)
     vd = torch.randn(shape, generator=g, device=dev()).to(torch.bfloat16)
     qd = torch.randn((B, Q, HQ, D), generator=g, device=dev()).to(torch.bfloat16)
-    edges = [Q, 5, 255, 256, 257, 511, 512, 513, 767, 768, 769, 1023, Lcap]
+    edges = [Q, Q + 1, 255, 256, 257, 511, 512, 513, 767, 768, 769, 1023, Lcap]
     rng = np.random.default_rng(Q)
     kv = np.array(edges + list(rng.integers(Q, Lcap + 1, B - len(edges))), np.int32)
     kvd = torch.tensor(kv, device=dev())
