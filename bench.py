@@ -486,13 +486,13 @@ def _cus(torch, dev):
 
 def sdpa_launches(B, Q, Hq, Hkv, Lk, cus):
     """Kernels one bi_sdpa call launches on a GPU of `cus` compute units: one
-    for a prompt (at least 128 query rows per KV head, at most 4096 keys: the
+    for a prompt (at least 128 query rows per KV head, at most 8192 keys: the
     prompt-shaped kernel) and for at least 2 * cus (sequence, KV head) groups
     of at most 32 query rows over at most 1024 keys (one workgroup walks a
     group's chunks and merges them), else two (chunk partials, then the
     merge)."""
     R = Q * (Hq // Hkv)
-    if R >= 128 and Lk <= 4096:
+    if R >= 128 and Lk <= 8192:
         return 1
     return 1 if R <= 32 and Lk <= 1024 and B * Hkv >= 2 * cus else 2
 
@@ -507,7 +507,7 @@ def op_sweep(torch, bi, dev):
         B in {4, 16, 64} at Q = 1, Lk = 8196;
       4-bit quantized matmul (packed): 28672 x 4096 at M in 1..64, affine
         group sizes 32/64/128, nvfp4, mxfp4;
-      causal prefill attention at prompts of 512 and 2048 tokens."""
+      causal prefill attention at prompts of 512, 2048 and 8192 tokens."""
     res = {"target": "decode shapes with >= 32 MiB of weights or KV, and RMSNorm at B = 4096: frac_hbm >= 0.70",
            "matmul": {}, "rmsnorm": {}, "sdpa": {}}
     bf = torch.bfloat16
@@ -577,7 +577,7 @@ def op_sweep(torch, bi, dev):
         del wps
     # causal prefill: Q = Lk (a whole prompt in one call), flops over the visible (query, key) pairs
     res["prefill"] = {}
-    for Bn, Q in ((1, 512), (1, 2048), (8, 512), (64, 512)):
+    for Bn, Q in ((1, 512), (1, 2048), (1, 8192), (8, 512), (64, 512)):
         Lk = Q
         ks = torch.randn(Bn, Hkv, Lk, D, device=dev).to(bf)
         vs = torch.randn(Bn, Hkv, Lk, D, device=dev).to(bf)

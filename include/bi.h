@@ -338,8 +338,8 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
  * chunks, writes the same partials (in ws) and runs the range and row
  * levels for the group's rows itself.
  * Prompts -- at least 128 query rows per KV head (Q * Hq / Hkv >= 128) and
- * max_kv_len <= 4096 (one range) -- take one launch that computes the same
- * tree per block of 128 query rows without partials (ws is then unused, but
+ * max_kv_len <= 8192 (at most two ranges) -- take one launch that computes
+ * the same tree per block of 128 query rows without partials (ws is then unused, but
  * is still validated, so that a caller's sizing does not depend on the path).
  * ------------------------------------------------------------------------ */
 size_t bi_sdpa_workspace_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int32_t Hq, int32_t D);

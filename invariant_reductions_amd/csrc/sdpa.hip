@@ -667,25 +667,28 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
     }
 }
 
-// Prompts (many query rows per KV head, at most 4096 keys: one range).  One
-// workgroup of 8 waves per (sequence, KV head, block of 128 query rows),
-// heaviest blocks of all sequences and heads first; wave w owns the block's 16-row tile w and plays all
-// four key quarters of every chunk itself -- the "waves" of the chunk tree
-// are the quarters [64q, 64q + 64) of a chunk, whoever computes them -- so a
-// chunk's max, l and o are combined in registers in the tree's order and no
-// partial leaves the workgroup.  The range weights need the row's maximum
-// over its chunks before any o_c is weighted, so the walk runs twice: pass
-// 1 computes every chunk max m_c (kept in LDS) and M = max m_c; pass 2
-// recomputes the scores and forms, per chunk and in ascending order,
-// o_r = sum o_c exp(m_c - M), l_r likewise, exactly as attn_merge_kernel
-// does with the partials (its row level then multiplies by exp(M - M) = 1).
-// Each quarter's K (as the score MFMA's B operand) and V (transposed into
-// the P . V operand, as attn_kernel does in registers) are staged once in
-// LDS for all eight waves, two buffers deep.
+// Prompts (many query rows per KV head, at most 8192 keys: one or two
+// ranges).  One workgroup of 8 waves per (sequence, KV head, block of 128
+// query rows), heaviest blocks of all sequences and heads first; wave w owns
+// the block's 16-row tile w and plays all four key quarters of every chunk
+// itself -- the "waves" of the chunk tree are the quarters [64q, 64q + 64)
+// of a chunk, whoever computes them -- so a chunk's max, l and o are
+// combined in registers in the tree's order and no partial leaves the
+// workgroup.  The range weights need the maxima of the row's chunks before
+// any o_c is weighted, so the walk runs twice: pass 1 computes every chunk
+// max m_c (kept in LDS) and M = max m_c; pass 2 recomputes the scores and
+// forms, per chunk and in ascending order, o_r = sum o_c 2^(m_c - M_r) and
+// l_r within each range, then o = sum o_r 2^(M_r - M) and l over the ranges,
+// exactly as attn_merge_kernel does with the partials.  Each quarter's K (as
+// the score MFMA's B operand) and V (transposed into the P . V operand, as
+// attn_kernel does in registers) are staged once in LDS for all eight
+// waves, two buffers deep.
 constexpr int kPreWaves = 8, kPreRows = 16 * kPreWaves;
-constexpr int kPreMaxChunks = 16;            // max_kv <= 4096: a single range
+constexpr int kPreMaxRanges = 2;             // max_kv <= 8192
 
-template <typename S>
+// NR: the ranges the launch's keys span (1 or 2); one range keeps the row
+// sums out of the registers (its range weight 2^(M_r - M) is 1).
+template <typename S, int NR>
 __global__ __launch_bounds__(kPreWaves * kWave, 1)
 void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, int nrb)
 {
@@ -697,7 +700,7 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
     __shared__ __attribute__((aligned(16))) VRows w0, w1;
     typedef uint16_t PTile[16][kKeysPerWave + 8];
     __shared__ __attribute__((aligned(16))) PTile phi[kPreWaves], plo[kPreWaves];
-    __shared__ float mstore[kPreWaves][16][kPreMaxChunks];
+    __shared__ float mstore[kPreWaves][16][NR * kRange];
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g4 = lane >> 4, c16 = lane & 15;
@@ -838,12 +841,13 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
     }
 
     // ---- pass 2: the chunk tree and the range combine
-    f32x4 oc[8], orr[8];
-    float lc[4], lr[4], mrow[4];
+    // oc, lc: the chunk's sums; orr, lr: the range's; ow, lw: the row's
+    f32x4 oc[8], orr[8], ow[8];
+    float lc[4], lr[4], lw[4], mrow[4], Mr[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) oc[j] = orr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) oc[j] = orr[j] = ow[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lc[i] = lr[i] = mrow[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) lc[i] = lr[i] = lw[i] = mrow[i] = Mr[i] = 0.0f;
     // unit u: its V (loaded during unit u - 1) goes into vbuf, free since
     // everyone passed the barrier after multiplying unit u - 2 with it
     // the compute of unit u (pass 2)
@@ -908,12 +912,39 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
             oc[j] = qq == 0 ? acc : oc[j] + acc;
         }
         if (qq == 3) {
-            // chunk c done: weight it into the range sums of the rows that see it
+            // chunk c done: weight it into the range sums of the rows that see
+            // it (range maximum M_r over the row's chunks of the range, taken
+            // from pass 1's chunk maxima as the range starts), and once a
+            // row's range is complete -- its last chunk of the range or its
+            // last chunk -- weight the range into the row sums: the range and
+            // row levels of attn_merge_kernel, in its order and arithmetic
+            const int rg = c / kRange, c0 = rg * kRange;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (!(ok[i] && lk[i] >= c * kChunk)) continue;
-                const float w = attn_exp(mrow[i] - M[i]);
-                if (c == 0) {
+                if constexpr (NR == 1) {
+                    // one range: M_r = M, and the row level is the range level
+                    // times 2^(M - M) = 1, taken at the output
+                    const float w = attn_exp(mrow[i] - M[i]);
+                    if (c == 0) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) orr[j][i] = oc[j][i] * w;
+                        lr[i] = lc[i] * w;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) orr[j][i] = orr[j][i] + oc[j][i] * w;
+                        lr[i] = lr[i] + lc[i] * w;
+                    }
+                    continue;
+                }
+                const int clast = min(c0 + kRange - 1, lk[i] / kChunk);
+                if (c == c0) {
+                    float m = mstore[wave][g4 * 4 + i][c0];
+                    for (int cc = c0 + 1; cc <= clast; ++cc) m = fmaxf(m, mstore[wave][g4 * 4 + i][cc]);
+                    Mr[i] = m;
+                }
+                const float w = attn_exp(mrow[i] - Mr[i]);
+                if (c == c0) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) orr[j][i] = oc[j][i] * w;
                     lr[i] = lc[i] * w;
@@ -921,6 +952,18 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
 #pragma unroll
                     for (int j = 0; j < 8; ++j) orr[j][i] = orr[j][i] + oc[j][i] * w;
                     lr[i] = lr[i] + lc[i] * w;
+                }
+                if (c == clast) {
+                    const float u = attn_exp(Mr[i] - M[i]);
+                    if (rg == 0) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) ow[j][i] = orr[j][i] * u;
+                        lw[i] = lr[i] * u;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) ow[j][i] = ow[j][i] + orr[j][i] * u;
+                        lw[i] = lw[i] + lr[i] * u;
+                    }
                 }
             }
         }
@@ -964,17 +1007,24 @@ void attn_prefill_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnSh
     if (wave >= 6) pass2(std::true_type{});
     else pass2(std::false_type{});
     if (!wave_rows) return;
-    // the row level of a single range: o = o_r exp(M - M), l likewise; out = RNE(o / l)
+    // out = RNE(o / l) from the row sums (one range: o = o_r 2^(M - M))
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if (!ok[i] || lk[i] < 0) continue;
         const int r = rt0 + g4 * 4 + i, j = r / sh.G;
         const int64_t row = ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (r - j * sh.G);
-        const float u = attn_exp(M[i] - M[i]);
-        const float l = lr[i] * u;
+        if constexpr (NR == 1) {
+            const float u = attn_exp(M[i] - M[i]);
+            const float l = lr[i] * u;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                ow[jj][i] = orr[jj][i] * u;
+                lw[i] = l;
+            }
+        }
         uint16_t o8[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) o8[jj] = S::narrow((orr[jj][i] * u) / l);
+        for (int jj = 0; jj < 8; ++jj) o8[jj] = S::narrow(ow[jj][i] / lw[i]);
         *reinterpret_cast<uint4 *>(bf.o + row * kHeadDim + c16 * 8) = __builtin_bit_cast(uint4, o8);
     }
 }
@@ -1232,14 +1282,19 @@ static bi_status attn_run(const void *q, const void *k, const void *v, void *o, 
     if (ws_bytes < p.parts) return BI_ERR_WORKSPACE;
     AttnBufs bf{(const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, kv_len, (uint16_t *)o, (float *)ws};
     (void)hipGetLastError();
-    // prompts: at least one block of 128 query rows per KV head, one range of keys
+    // prompts: at least one block of 128 query rows per KV head, at most
+    // two ranges of keys
     const int64_t R = Q * (Hq / Hkv), nrb = cdiv(R, kPreRows);
-    if (R >= kPreRows && max_kv_len <= (int64_t)kPreMaxChunks * kChunk && B * Hkv * nrb < (1ll << 31)) {
+    if (R >= kPreRows && max_kv_len <= (int64_t)kPreMaxRanges * kRange * kChunk && B * Hkv * nrb < (1ll << 31)) {
         const dim3 grid((unsigned)(B * Hkv * nrb)), block(kPreWaves * kWave);
-        if (dtype == BI_BF16)
-            launch_kernel((attn_prefill_kernel<BF16>), grid, block, 0, stream, bf, kv_len, p.sh, (int)nrb);
-        else
-            launch_kernel((attn_prefill_kernel<F16>), grid, block, 0, stream, bf, kv_len, p.sh, (int)nrb);
+        const bool one = max_kv_len <= (int64_t)kRange * kChunk;
+        if (dtype == BI_BF16) {
+            if (one) launch_kernel((attn_prefill_kernel<BF16, 1>), grid, block, 0, stream, bf, kv_len, p.sh, (int)nrb);
+            else launch_kernel((attn_prefill_kernel<BF16, 2>), grid, block, 0, stream, bf, kv_len, p.sh, (int)nrb);
+        } else {
+            if (one) launch_kernel((attn_prefill_kernel<F16, 1>), grid, block, 0, stream, bf, kv_len, p.sh, (int)nrb);
+            else launch_kernel((attn_prefill_kernel<F16, 2>), grid, block, 0, stream, bf, kv_len, p.sh, (int)nrb);
+        }
         return launch_status();
     }
     if (dtype == BI_BF16) launch_attn<BF16>(bf, p, stream);

@@ -286,3 +286,31 @@ def test_whole_group_form_equals_lone_sequences(Q, head_major):
             kb, vb = kb.transpose(1, 2), vb.transpose(1, 2)
         ref = oracle.sdpa(to_np(qd[b:b + 1]), to_np(kb), to_np(vb), kv[b:b + 1], SCALE, True, "bf16")
         assert_parity(full[b:b + 1], ref, "bf16", f"sequence {b}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prompt_kernel_two_ranges_rows_equal_lone_queries(causal):
+    """Prompts over more than 4096 keys (at most 8192) take the prompt kernel
+    with two ranges of 16 chunks: per row, the range maximum from the first
+    pass's chunk maxima, the range sums, and the row sums weighted range by
+    range as the merge does.  Every row equals the same query run alone
+    through the decode kernels (chunk partials, then the merge launch's range
+    and row levels), with ragged lengths on both sides of the range edge;
+    sampled rows are within the parity gate of the oracle."""
+    B, Q, Lcap = 2, 300, 6100
+    q, k, v = inputs.sdpa_case(B, Q, Lcap, HQ, HKV, D, seed=23)
+    kv = np.array([6100, 4250], np.int32)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    kvd = torch.tensor(kv, device=dev())
+    full = to_np(bi.sdpa(qd, kd, vd, kvd, int(kv.max()), SCALE, causal))
+    for bb in range(B):
+        for j in (0, 1, 150, Q - 1):
+            L = int(kv[bb]) - Q + j + 1 if causal else int(kv[bb])
+            one = to_np(bi.sdpa(qd[bb:bb + 1, j:j + 1].contiguous(), kd[bb:bb + 1].contiguous(),
+                                vd[bb:bb + 1].contiguous(), torch.tensor([L], dtype=torch.int32, device=dev()), L,
+                                SCALE, True))
+            assert bits_equal(one[0, 0], full[bb, j]), (bb, j)
+    for j in (0, Q - 1):
+        lens = kv - Q + j + 1 if causal else kv
+        ref = oracle.sdpa(np.ascontiguousarray(q[:, j:j + 1]), k, v, lens.astype(np.int32), SCALE, True, "bf16")
+        assert_parity(full[:, j:j + 1], ref, "bf16", f"row {j}")
