@@ -280,15 +280,21 @@ __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, 
 //
 // WHOLE: the invariant tree for many (sequence, KV head) groups of at most
 // 32 query rows (nmg == 1): the item is a group with all its chunks, walked
-// in order by one workgroup; every chunk's partial is written exactly as
-// above, and after the last one the same workgroup reads them back and runs
+// by one workgroup; every chunk's partial is written exactly as above, and
+// after the last one the same workgroup reads them back and runs
 // attn_merge_kernel's range and row levels for the group's rows -- one
-// launch, and the partials never leave the workgroup's own view.
+// launch, and the partials never leave the workgroup's own view.  The walk
+// takes the group's last chunk first, then the others in order: that chunk
+// is the one a decoding context fills gradually, and its few rows, requested
+// at the start, come back ahead of the full chunks' traffic instead of
+// behind all of it at the end.  Each partial lands at its own chunk index,
+// so the order of the walk never reaches the merge.
 template <typename S, bool MG, bool SPL = false, bool WHOLE = false>
 __global__ __launch_bounds__(kAttnWaves * kWave, 2)
 void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, int64_t nid)
 {
     constexpr bool RUNS = SPL || WHOLE;                                  // an item walks a run of chunks
+    static_assert(!(WHOLE && (MG || SPL)), "the whole-group form has one row group and no splits");
     typedef uint16_t PTile[16][kKeysPerWave + 8];
     typedef float OTile[16][kHeadDim + 4];
     __shared__ __attribute__((aligned(16))) PTile phi[kAttnWaves], plo[kAttnWaves];
@@ -325,6 +331,8 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
         it.b = exists ? (int)(bc / sh.nsplit) : 0;
         it.c = exists ? (int)(bc - (int64_t)it.b * sh.nsplit) * (RUNS ? sh.cps : 1) : -1;
         it.kvlen = seq_len(it.b);
+        // WHOLE: the walk starts at the group's last chunk (see below)
+        if (WHOLE && exists) it.c = max(attn_last_key(it.kvlen, Qi, (R - 1) / sh.G, sh.causal), 0) / kChunk;
         return it;
     };
     auto last_key = [&](int kvlen, int j) { return attn_last_key(kvlen, Qi, j, sh.causal); };
@@ -409,7 +417,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
         // SPL: the split's chunks it.c .. clast in order, with the running
         // softmax state of row threadIdx.x / 16, d in [8 (threadIdx.x % 16), +8)
         const int split = SPL ? it.c / sh.cps : 0;
-        const int clast = RUNS ? min(it.c + sh.cps - 1, group_last_key(it) / kChunk) : it.c;
+        const int clast = WHOLE ? it.c : RUNS ? min(it.c + sh.cps - 1, group_last_key(it) / kChunk) : it.c;
         float rM = -INFINITY, rl = 0.0f, ro[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ro[e] = 0.0f;
@@ -419,7 +427,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
             auto next_item = [&]() {
                 if (RUNS && more) {
                     Item nx = it;
-                    ++nx.c;
+                    nx.c = WHOLE && it.c == clast ? 0 : it.c + 1;
                     return nx;
                 }
                 return decode(tn);
@@ -626,10 +634,10 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
         };
         if constexpr (RUNS) {
             for (;;) {
-                const bool more = it.c < clast;
+                const bool more = WHOLE ? (it.c == clast ? clast > 0 : it.c + 1 < clast) : it.c < clast;
                 chunk(more);
                 if (!more) break;
-                ++it.c;
+                it.c = WHOLE && it.c == clast ? 0 : it.c + 1;
             }
         } else {
             chunk(false);
