@@ -348,10 +348,11 @@ def _op_qmatmul(torch, bi, dev):
 def _op_sdpa(torch, bi, dev):
     """Decode attention (32 query / 8 KV heads, d 128, head-major bf16
     cache): one sequence at 16388 and 65540 keys, 64 sequences at 768 and
-    8196 keys, a verify block of 8 at 65540 keys; and a 2048-token causal
-    prompt (prefill)."""
+    8196 keys, a verify block of 8 at 65540 keys; and causal prompts
+    (prefill) of 2048 tokens (one range of chunks) and 8192 tokens (two)."""
     Hq, Hkv, D = 32, 8, 128
-    for B, Q, Lk in ((1, 1, 16388), (1, 1, 65540), (1, 8, 65540), (64, 1, 768), (64, 1, 8196), (1, 2048, 2048)):
+    for B, Q, Lk in ((1, 1, 16388), (1, 1, 65540), (1, 8, 65540), (64, 1, 768), (64, 1, 8196), (1, 2048, 2048),
+                     (1, 8192, 8192)):
         copies = max(2, min(8, -(-(512 << 20) // (4 * B * Lk * Hkv * D))))
         ks = [torch.randn(B, Hkv, Lk, D, device=dev).to(torch.bfloat16) for _ in range(copies)]
         vs = [torch.randn(B, Hkv, Lk, D, device=dev).to(torch.bfloat16) for _ in range(copies)]
