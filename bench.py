@@ -506,8 +506,8 @@ def op_sweep(torch, bi, dev):
       RMSNorm: H = 4096 at B in {1, 8, 64, 512, 4096};
       SDPA: B = 1, Q in {1, 8} at Lk in {1028, 8196, 16388, 65540}, and
         B in {4, 16, 64} at Q = 1, Lk = 8196;
-      4-bit quantized matmul (packed): 28672 x 4096 at M in 1..64, affine
-        group sizes 32/64/128, nvfp4, mxfp4;
+      4-bit quantized matmul (packed): K = N = 4096 and the decoder's
+        projections at M in 1..64, affine group sizes 32/64/128, nvfp4, mxfp4;
       causal prefill attention at prompts of 512, 2048 and 8192 tokens."""
     res = {"target": "decode shapes with >= 32 MiB of weights or KV, and RMSNorm at B = 4096: frac_hbm >= 0.70",
            "matmul": {}, "rmsnorm": {}, "sdpa": {}}
@@ -516,7 +516,7 @@ def op_sweep(torch, bi, dev):
         copies = max(2, -(-(512 << 20) // (N * K * 2)))
         wps = [bi.pack_weights((torch.randn(N, K, device=dev) * 0.02).to(bf)) for _ in range(copies)]
         ws = bi.matmul_workspace(64, N, K, device=dev)
-        for M in (1, 2, 4, 8, 16, 32, 64):
+        for M in (1, 2, 3, 4, 8, 16, 32, 64):
             x = torch.randn(M, K, device=dev).to(bf)
             y = torch.empty(M, N, dtype=bf, device=dev)
             t = _time_kernel(torch, bi, lambda i: bi.matmul_ws(x, wps[i % copies], ws, out=y), reps=3 * copies)
@@ -552,30 +552,39 @@ def op_sweep(torch, bi, dev):
         res["sdpa"][f"B{Bn} Q{Q} Lk{Lk}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1),
                                               "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
         del ks, vs
-    # 4-bit quantized decode projection 28672 x 4096 (tile-packed, cold) over M
-    from invariant_reductions_amd import inputs
+    # 4-bit quantized matmul (tile-packed, cold) at K = N = 4096 and the decoder's projections over M.  The
+    # kernel time depends on the shapes alone, so codes and scales are drawn on the device: random 4-bit
+    # words, fp16 scales and biases (affine), scale bytes of moderate exponent (nvfp4: e4m3, mxfp4: e8m0).
     res["qmatmul"] = {}
-    N, K = 28672, 4096
-    for mode, gs, qm in (("affine", 32, bi.AFFINE), ("affine", 64, bi.AFFINE), ("affine", 128, bi.AFFINE),
-                         ("nvfp4", 16, bi.NVFP4), ("mxfp4", 32, bi.MXFP4)):
-        x, wq, sc, bs = inputs.qmatmul_case(64, K, N, mode, gs, True, seed=0)
-        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.float16)
-        wq0 = torch.from_numpy(wq.view(np.int32)).to(dev)
-        sd = torch.from_numpy(sc if sc.dtype == np.uint8 else sc.view(np.int16)).to(dev)
-        bd = None if bs is None else torch.from_numpy(bs.view(np.int16)).to(dev)
-        copies = 10
-        wps = [bi.pack_qweights(torch.bitwise_xor(wq0, (0x01010101 * r) & 0x7fffffff), sd, bd, N, K, qm, gs)
-               for r in range(copies)]
-        alg = N * K // 2 + N * (K // gs) * (4 if mode == "affine" else 1)
-        for M in (1, 2, 4, 8, 16, 32, 64):
-            xm = xd[:M].contiguous()
-            y = torch.empty(M, N, dtype=torch.float16, device=dev)
-            t = _time_kernel(torch, bi, lambda i: bi.qmatmul(xm, wps[i % copies], None, None, N, K, qm, gs, out=y,
-                                                             packed=True), reps=3 * copies)
-            gbs = (alg + 2 * M * K + 2 * M * N) / (t * 1e-3) / 1e9
-            res["qmatmul"][f"{mode}-gs{gs} {M}x{N}x{K}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1),
-                                                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-        del wps
+    gq = torch.Generator(device=dev).manual_seed(0)
+    for (N, K) in ((4096, 4096), (6144, 4096), (28672, 4096), (4096, 14336), (32000, 4096)):
+        xd = torch.randn(64, K, device=dev, generator=gq).to(torch.float16)
+        for mode, gs, qm in (("affine", 32, bi.AFFINE), ("affine", 64, bi.AFFINE), ("affine", 128, bi.AFFINE),
+                             ("nvfp4", 16, bi.NVFP4), ("mxfp4", 32, bi.MXFP4)):
+            copies = max(2, -(-(512 << 20) // (N * K // 2)))
+
+            def packed_copy():
+                wq = torch.randint(-(1 << 31), (1 << 31) - 1, (N, K // 8), dtype=torch.int32, device=dev, generator=gq)
+                if mode == "affine":
+                    sc = (torch.rand(N, K // gs, device=dev, generator=gq) * 0.01 + 0.001).to(torch.float16)
+                    bs = (torch.randn(N, K // gs, device=dev, generator=gq) * 0.01).to(torch.float16)
+                else:
+                    lo, hi = (0x28, 0x48) if mode == "nvfp4" else (120, 131)
+                    sc = torch.randint(lo, hi, (N, K // gs), dtype=torch.uint8, device=dev, generator=gq)
+                    bs = None
+                return bi.pack_qweights(wq, sc, bs, N, K, qm, gs)
+
+            wps = [packed_copy() for _ in range(copies)]
+            alg = N * K // 2 + N * (K // gs) * (4 if mode == "affine" else 1)
+            for M in (1, 2, 4, 8, 16, 32, 64):
+                xm = xd[:M].contiguous()
+                y = torch.empty(M, N, dtype=torch.float16, device=dev)
+                t = _time_kernel(torch, bi, lambda i: bi.qmatmul(xm, wps[i % copies], None, None, N, K, qm, gs,
+                                                                 out=y, packed=True), reps=3 * copies)
+                gbs = (alg + 2 * M * K + 2 * M * N) / (t * 1e-3) / 1e9
+                res["qmatmul"][f"{mode}-gs{gs} {M}x{N}x{K}"] = {"us": round(t * 1e3, 2), "gbs": round(gbs, 1),
+                                                                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            del wps
     # causal prefill: Q = Lk (a whole prompt in one call), flops over the visible (query, key) pairs
     res["prefill"] = {}
     for Bn, Q in ((1, 512), (1, 2048), (1, 8192), (8, 512), (64, 512)):
