@@ -314,3 +314,30 @@ def test_prompt_kernel_two_ranges_rows_equal_lone_queries(causal):
         lens = kv - Q + j + 1 if causal else kv
         ref = oracle.sdpa(np.ascontiguousarray(q[:, j:j + 1]), k, v, lens.astype(np.int32), SCALE, True, "bf16")
         assert_parity(full[:, j:j + 1], ref, "bf16", f"row {j}")
+
+
+@pytest.mark.parametrize("kv_pair", [(8192, 4097), (4097, 8192)])
+def test_prompt_kernel_two_ranges_f16_head_major_at_the_edges(kv_pair):
+    """The two-range prompt kernel in f16 on a head-major cache, with key
+    lengths at the limit of the one-launch form (8192) and one past the first
+    range (4097, whose last chunk holds a single key), and 40 query positions
+    (160 rows per KV head: one full block of 128 and a partial one): rows
+    equal lone queries (decode kernels) and sampled rows are within the f16
+    parity gate of the oracle."""
+    B, Q, Lcap = 2, 40, 8192
+    q, k, v = inputs.sdpa_case(B, Q, Lcap, HQ, HKV, D, seed=29, dtype="f16")
+    kv = np.array(kv_pair, np.int32)
+    kh, vh = (np.ascontiguousarray(a.transpose(0, 2, 1, 3)) for a in (k, v))
+    qd, kd, vd = to_dev(q, "f16"), to_dev(kh, "f16"), to_dev(vh, "f16")
+    full = to_np(bi.sdpa(qd, kd, vd, torch.tensor(kv, device=dev()), int(kv.max()), SCALE, True, head_major=True))
+    for bb in range(B):
+        for j in (0, 1, Q - 1):
+            L = int(kv[bb]) - Q + j + 1
+            one = to_np(bi.sdpa(qd[bb:bb + 1, j:j + 1].contiguous(), kd[bb:bb + 1].contiguous(),
+                                vd[bb:bb + 1].contiguous(), torch.tensor([L], dtype=torch.int32, device=dev()), L,
+                                SCALE, True, head_major=True))
+            assert bits_equal(one[0, 0], full[bb, j]), (bb, j)
+    for j in (0, Q - 1):
+        ref = oracle.sdpa(np.ascontiguousarray(q[:, j:j + 1]), k, v, (kv - Q + j + 1).astype(np.int32), SCALE, True,
+                          "f16")
+        assert_parity(full[:, j:j + 1], ref, "f16", f"row {j}")
