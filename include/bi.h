@@ -335,8 +335,9 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
  * launches: the chunk partials (in ws), then the range and row levels; with
  * at least two (sequence, KV head) groups of at most 32 query rows per CU
  * over at most 1024 keys, one launch in which a workgroup walks a group's
- * chunks, writes the same partials (in ws) and runs the range and row
- * levels for the group's rows itself.
+ * chunks, forms the same partials (in its LDS for groups of at most 8 query
+ * rows, else in ws) and runs the range and row levels for the group's rows
+ * itself.
  * Prompts -- at least 128 query rows per KV head (Q * Hq / Hkv >= 128) and
  * max_kv_len <= 8192 (at most two ranges) -- take one launch that computes
  * the same tree per block of 128 query rows without partials (ws is then unused, but

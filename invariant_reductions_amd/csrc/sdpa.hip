@@ -57,6 +57,11 @@ constexpr int kHeadDim = 128;        // D supported by this build
 constexpr int kAttnWaves = 4;        // waves per chunk workgroup (frozen: 64 keys each)
 constexpr int kKeysPerWave = kChunk / kAttnWaves;
 constexpr int kPartStride = kHeadDim + 4;   // floats per (row, chunk) partial: o[D], m, l, pad
+// The whole-group form (attn_kernel's WHOLE): at most this many chunks per
+// group, and with at most kWholeLdsRows query rows per group its chunk
+// partials stay in the workgroup's LDS instead of the workspace.
+constexpr int64_t kWholeMaxChunks = 4;
+constexpr int kWholeLdsRows = 8;
 constexpr int64_t kMaxKv = 1ll << 20;
 constexpr int kAttnMinTiles = 4;     // fewest query-row tiles (of 16) per work item when a prompt is split
 
@@ -195,9 +200,12 @@ __device__ inline void attn_store_out(uint16_t *dst, float4 o, float l)
 // order: M = max of the row's chunk maxima; per range r, M_r, o_r and l_r
 // over its chunks ascending; o and l as the sum of o_r exp(M_r - M) over the
 // ranges ascending (the first term assigned, not added to 0); out = RNE(o/l).
-// The partials were written by this workgroup: plain loads see them.
+// The partials were written by this workgroup: plain loads see them.  lds:
+// the group's partials in LDS (row rr's chunk c at (rr kWholeMaxChunks + c)
+// kPartStride), or null for the workspace.
 template <typename S>
-__device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, int b, int hk, int kvlen)
+__device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, int b, int hk, int kvlen,
+                                       const float *lds)
 {
     const int R = (int)sh.Q * sh.G;
     const int quad = threadIdx.x & 31;
@@ -206,7 +214,8 @@ __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, 
         const int lk = attn_last_key(kvlen, (int)sh.Q, j, sh.causal);
         if (lk < 0) continue;
         const int64_t row = ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (rr - j * sh.G);
-        const float *pr = bf.part + row * sh.nchunks * kPartStride;
+        const float *pr = lds ? lds + (int64_t)rr * kWholeMaxChunks * kPartStride
+                              : bf.part + row * sh.nchunks * kPartStride;
         const int nch = lk / kChunk + 1, nr = (nch + kRange - 1) / kRange;
         float M = -INFINITY;
         for (int c = 0; c < nch; ++c) M = fmaxf(M, pr[c * kPartStride + kHeadDim]);
@@ -280,9 +289,10 @@ __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, 
 //
 // WHOLE: the invariant tree for many (sequence, KV head) groups of at most
 // 32 query rows (nmg == 1): the item is a group with all its chunks, walked
-// by one workgroup; every chunk's partial is written exactly as above, and
-// after the last one the same workgroup reads them back and runs
-// attn_merge_kernel's range and row levels for the group's rows -- one
+// by one workgroup; every chunk's partial is formed exactly as above -- in
+// the workgroup's LDS for groups of at most kWholeLdsRows rows, else in the
+// workspace -- and after the last one the same workgroup reads them back and
+// runs attn_merge_kernel's range and row levels for the group's rows: one
 // launch, and the partials never leave the workgroup's own view.  The walk
 // takes the group's last chunk first, then the others in order: that chunk
 // is the one a decoding context fills gradually, and its few rows, requested
@@ -300,6 +310,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
     __shared__ __attribute__((aligned(16))) PTile phi[kAttnWaves], plo[kAttnWaves];
     __shared__ __attribute__((aligned(16))) OTile ol[kAttnWaves];
     __shared__ float xm[kAttnWaves][16], xl[kAttnWaves][16];
+    __shared__ __attribute__((aligned(16))) float wpart[WHOLE ? kWholeLdsRows * kWholeMaxChunks * kPartStride : 4];
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g4 = lane >> 4, c16 = lane & 15;
@@ -307,6 +318,8 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
     const int ntm = (R + 15) / 16;
     const int64_t nitems = sh.B * sh.nsplit;
     const int Qi = (int)sh.Q;
+    // WHOLE with few rows: the chunk partials in LDS
+    const bool lds_parts = WHOLE && R <= kWholeLdsRows;
 
     // The sequence lengths, clamped to max_kv (device data the host cannot
     // validate: the clamp keeps every access inside the cache and the
@@ -591,8 +604,10 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
                         const int j = r / sh.G;
                         if (last_key(it.kvlen, j) >= key0) {
                             const int64_t h = (int64_t)it.hk * sh.G + (r - j * sh.G);
-                            float *dst = bf.part +
-                                         ((((int64_t)it.b * sh.Q + j) * sh.Hq + h) * sh.nchunks + it.c) * kPartStride;
+                            float *dst =
+                                lds_parts ? &wpart[(r * kWholeMaxChunks + it.c) * kPartStride]
+                                          : bf.part + ((((int64_t)it.b * sh.Q + j) * sh.Hq + h) * sh.nchunks + it.c) *
+                                                          kPartStride;
 #pragma unroll
                             for (int half = 0; half < 2; ++half) {
                                 const int d = dg * 8 + half * 4;
@@ -647,7 +662,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
             // workgroup just wrote (every store of every wave done first)
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            attn_merge_rows<S>(bf, sh, it.b, it.hk, it.kvlen);
+            attn_merge_rows<S>(bf, sh, it.b, it.hk, it.kvlen, lds_parts ? wpart : nullptr);
             __syncthreads();
         }
         if constexpr (SPL) {
@@ -1232,8 +1247,6 @@ static AttnPlan attn_plan(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Lcap
 // neighbouring chunks of a few groups): 8196 keys at 64 sequences x 8 KV
 // heads take 473 us whole against 437 us as chunks plus merge, while 768
 // keys take 47 us against 50 us.
-constexpr int64_t kWholeMaxChunks = 4;
-
 static bool attn_whole(const AttnPlan &p)
 {
     return p.sh.nmg == 1 && p.sh.Q * p.sh.G <= 32 && p.sh.nchunks <= kWholeMaxChunks &&
