@@ -489,13 +489,14 @@ def sdpa_launches(B, Q, Hq, Hkv, Lk, cus):
     """Kernels one bi_sdpa call launches on a GPU of `cus` compute units: one
     for a prompt (at least 128 query rows per KV head, at most 8192 keys: the
     prompt-shaped kernel) and for at least 2 * cus (sequence, KV head) groups
-    of at most 32 query rows over at most 1024 keys (one workgroup walks a
-    group's chunks and merges them), else two (chunk partials, then the
-    merge)."""
+    of at most 32 query rows over at most 1024 keys, or of at most 48 (query
+    row, 256-key chunk) pairs (one workgroup walks a group's chunks and
+    merges them), else two (chunk partials, then the merge)."""
     R = Q * (Hq // Hkv)
     if R >= 128 and Lk <= 8192:
         return 1
-    return 1 if R <= 32 and Lk <= 1024 and B * Hkv >= 2 * cus else 2
+    nch = -(-Lk // 256)
+    return 1 if R <= 32 and (nch <= 4 or R * nch <= 48) and B * Hkv >= 2 * cus else 2
 
 
 def op_sweep(torch, bi, dev):

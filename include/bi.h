@@ -333,11 +333,12 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
  * past a query's last key are never merged, so a row's bits do not depend on
  * B, Q, the other rows or the launch.  Decode and verify shapes take two
  * launches: the chunk partials (in ws), then the range and row levels; with
- * at least two (sequence, KV head) groups of at most 32 query rows per CU
- * over at most 1024 keys, one launch in which a workgroup walks a group's
- * chunks, forms the same partials (in its LDS for groups of at most 8 query
- * rows, else in ws) and runs the range and row levels for the group's rows
- * itself.
+ * at least two (sequence, KV head) groups per CU of at most 32 query rows
+ * over at most 1024 keys, or of at most 48 (query row, 256-key chunk) pairs
+ * (one query over 3072 keys, two over 1536), one launch in which a
+ * workgroup walks a group's chunks, forms the same partials (in its LDS for
+ * groups of at most 8 query rows, else in ws) and runs the range and row
+ * levels for the group's rows itself.
  * Prompts -- at least 128 query rows per KV head (Q * Hq / Hkv >= 128) and
  * max_kv_len <= 8192 (at most two ranges) -- take one launch that computes
  * the same tree per block of 128 query rows without partials (ws is then unused, but

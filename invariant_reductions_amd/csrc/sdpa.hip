@@ -57,11 +57,15 @@ constexpr int kHeadDim = 128;        // D supported by this build
 constexpr int kAttnWaves = 4;        // waves per chunk workgroup (frozen: 64 keys each)
 constexpr int kKeysPerWave = kChunk / kAttnWaves;
 constexpr int kPartStride = kHeadDim + 4;   // floats per (row, chunk) partial: o[D], m, l, pad
-// The whole-group form (attn_kernel's WHOLE): at most this many chunks per
-// group, and with at most kWholeLdsRows query rows per group its chunk
-// partials stay in the workgroup's LDS instead of the workspace.
+// The whole-group form (attn_kernel's WHOLE): at most kWholeMaxChunks chunks
+// per group with its chunk partials in the workspace, or with at most
+// kWholeLdsParts (query row, chunk) partials per group (4 rows over 12
+// chunks, 8 over 6) in the workgroup's LDS.  Up to kWholeMaxChunks chunks an
+// instantiation with room for kWholeLdsSmall partials keeps them at a fixed
+// stride of kWholeMaxChunks per row (groups of at most 8 rows), which leaves
+// its registers as they were without LDS partials.
 constexpr int64_t kWholeMaxChunks = 4;
-constexpr int kWholeLdsRows = 8;
+constexpr int kWholeLdsParts = 48, kWholeLdsSmall = 32;
 constexpr int64_t kMaxKv = 1ll << 20;
 constexpr int kAttnMinTiles = 4;     // fewest query-row tiles (of 16) per work item when a prompt is split
 
@@ -201,11 +205,11 @@ __device__ inline void attn_store_out(uint16_t *dst, float4 o, float l)
 // over its chunks ascending; o and l as the sum of o_r exp(M_r - M) over the
 // ranges ascending (the first term assigned, not added to 0); out = RNE(o/l).
 // The partials were written by this workgroup: plain loads see them.  lds:
-// the group's partials in LDS (row rr's chunk c at (rr kWholeMaxChunks + c)
+// the group's partials in LDS (row rr's chunk c at (rr lcs + c)
 // kPartStride), or null for the workspace.
 template <typename S>
 __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, int b, int hk, int kvlen,
-                                       const float *lds)
+                                       const float *lds, int lcs)
 {
     const int R = (int)sh.Q * sh.G;
     const int quad = threadIdx.x & 31;
@@ -214,7 +218,7 @@ __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, 
         const int lk = attn_last_key(kvlen, (int)sh.Q, j, sh.causal);
         if (lk < 0) continue;
         const int64_t row = ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (rr - j * sh.G);
-        const float *pr = lds ? lds + (int64_t)rr * kWholeMaxChunks * kPartStride
+        const float *pr = lds ? lds + (int64_t)rr * lcs * kPartStride
                               : bf.part + row * sh.nchunks * kPartStride;
         const int nch = lk / kChunk + 1, nr = (nch + kRange - 1) / kRange;
         float M = -INFINITY;
@@ -299,7 +303,8 @@ __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, 
 // at the start, come back ahead of the full chunks' traffic instead of
 // behind all of it at the end.  Each partial lands at its own chunk index,
 // so the order of the walk never reaches the merge.
-template <typename S, bool MG, bool SPL = false, bool WHOLE = false>
+// WLP: the (query row, chunk) partials the WHOLE form's LDS holds.
+template <typename S, bool MG, bool SPL = false, bool WHOLE = false, int WLP = 0>
 __global__ __launch_bounds__(kAttnWaves * kWave, 2)
 void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, int64_t nid)
 {
@@ -310,7 +315,8 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
     __shared__ __attribute__((aligned(16))) PTile phi[kAttnWaves], plo[kAttnWaves];
     __shared__ __attribute__((aligned(16))) OTile ol[kAttnWaves];
     __shared__ float xm[kAttnWaves][16], xl[kAttnWaves][16];
-    __shared__ __attribute__((aligned(16))) float wpart[WHOLE ? kWholeLdsRows * kWholeMaxChunks * kPartStride : 4];
+    static_assert(WHOLE == (WLP > 0), "LDS partials belong to the whole-group form");
+    __shared__ __attribute__((aligned(16))) float wpart[WHOLE ? WLP * kPartStride : 4];
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g4 = lane >> 4, c16 = lane & 15;
@@ -318,8 +324,10 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
     const int ntm = (R + 15) / 16;
     const int64_t nitems = sh.B * sh.nsplit;
     const int Qi = (int)sh.Q;
-    // WHOLE with few rows: the chunk partials in LDS
-    const bool lds_parts = WHOLE && R <= kWholeLdsRows;
+    // WHOLE with few (row, chunk) partials: those in LDS
+    constexpr bool WBIG = WLP > kWholeLdsSmall;                       // launched for > kWholeMaxChunks chunks only
+    const bool lds_parts = WHOLE && (WBIG || R * (int)kWholeMaxChunks <= WLP);
+    const int lcs = WBIG ? (int)sh.nchunks : (int)kWholeMaxChunks;   // LDS partials per row
 
     // The sequence lengths, clamped to max_kv (device data the host cannot
     // validate: the clamp keeps every access inside the cache and the
@@ -605,7 +613,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
                         if (last_key(it.kvlen, j) >= key0) {
                             const int64_t h = (int64_t)it.hk * sh.G + (r - j * sh.G);
                             float *dst =
-                                lds_parts ? &wpart[(r * kWholeMaxChunks + it.c) * kPartStride]
+                                lds_parts ? &wpart[(r * lcs + it.c) * kPartStride]
                                           : bf.part + ((((int64_t)it.b * sh.Q + j) * sh.Hq + h) * sh.nchunks + it.c) *
                                                           kPartStride;
 #pragma unroll
@@ -662,7 +670,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
             // workgroup just wrote (every store of every wave done first)
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            attn_merge_rows<S>(bf, sh, it.b, it.hk, it.kvlen, lds_parts ? wpart : nullptr);
+            attn_merge_rows<S>(bf, sh, it.b, it.hk, it.kvlen, lds_parts ? wpart : nullptr, lcs);
             __syncthreads();
         }
         if constexpr (SPL) {
@@ -1235,21 +1243,24 @@ static AttnPlan attn_plan(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Lcap
     return p;
 }
 
-// Short contexts (at most kWholeMaxChunks chunks) with at least one
-// (sequence, KV head) group of at most 32 query rows for each of the
-// persistent grid's workgroups (two per CU): one work item per group with
-// all its chunks, merged in the workgroup (attn_kernel's WHOLE form) --
-// every workgroup is busy without cutting the groups into chunks, and the
-// merge launch is gone.  Fewer groups keep the chunk items, which spread a
-// context over the whole chip; so do longer contexts, where a workgroup
-// streaming one group's whole cache region (every group at once, far apart)
-// reads HBM more slowly than the chunk items do (concurrent workgroups on
-// neighbouring chunks of a few groups): 8196 keys at 64 sequences x 8 KV
-// heads take 473 us whole against 437 us as chunks plus merge, while 768
-// keys take 47 us against 50 us.
+// Short contexts (at most kWholeMaxChunks chunks, or at most kWholeLdsParts
+// (query row, chunk) partials per group) with at least one (sequence, KV
+// head) group of at most 32 query rows for each of the persistent grid's
+// workgroups (two per CU): one work item per group with all its chunks,
+// merged in the workgroup (attn_kernel's WHOLE form) -- every workgroup is
+// busy without cutting the groups into chunks, and the merge launch is gone.
+// Fewer groups keep the chunk items, which spread a context over the whole
+// chip; so do longer contexts whose partials would go to the workspace,
+// where a workgroup streaming one group's whole cache region (every group
+// at once, far apart) read HBM more slowly than the chunk items do: 8196 keys
+// at 64 sequences x 8 KV heads took 473 us whole against 437 us as chunks
+// plus merge.  With the partials in LDS the whole form is ahead: at 64 x 8
+// groups of one query, 43 against 50 us at 768 keys, 101 against 113 us at
+// 2048 and 145 against 164 us at 3072.
 static bool attn_whole(const AttnPlan &p)
 {
-    return p.sh.nmg == 1 && p.sh.Q * p.sh.G <= 32 && p.sh.nchunks <= kWholeMaxChunks &&
+    return p.sh.nmg == 1 && p.sh.Q * p.sh.G <= 32 &&
+           (p.sh.nchunks <= kWholeMaxChunks || p.sh.Q * p.sh.G * p.sh.nchunks <= kWholeLdsParts) &&
            p.sh.B * p.sh.Hkv >= 2 * (int64_t)device_cu_count() && p.sh.cps == 1;
 }
 
@@ -1262,8 +1273,12 @@ static void launch_attn(const AttnBufs &bf, const AttnPlan &p, hipStream_t st)
         sh.nsplit = 1;
         const int64_t nid = cdiv(sh.B, 8) * 8 * sh.Hkv;
         const int64_t grid = std::min<int64_t>(nid, (int64_t)device_cu_count() * 2 / 8 * 8);
-        launch_kernel((attn_kernel<S, false, false, true>), dim3((unsigned)grid), dim3(kAttnWaves * kWave), 0, st, bf,
-                      bf.kv_len, sh, nid);
+        if (sh.nchunks <= kWholeMaxChunks)
+            launch_kernel((attn_kernel<S, false, false, true, kWholeLdsSmall>), dim3((unsigned)grid),
+                          dim3(kAttnWaves * kWave), 0, st, bf, bf.kv_len, sh, nid);
+        else
+            launch_kernel((attn_kernel<S, false, false, true, kWholeLdsParts>), dim3((unsigned)grid),
+                          dim3(kAttnWaves * kWave), 0, st, bf, bf.kv_len, sh, nid);
         return;
     }
     if (p.sh.nmg > 1)

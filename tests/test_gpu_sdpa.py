@@ -253,24 +253,27 @@ def test_prompt_kernel_rows_equal_lone_queries(causal, head_major):
         assert_parity(full[:, j:j + 1], ref, "bf16", f"row {j}")
 
 
-@pytest.mark.parametrize("Q,head_major", [(1, False), (1, True), (4, False), (5, False), (8, True)])
-def test_whole_group_form_equals_lone_sequences(Q, head_major):
+@pytest.mark.parametrize("Q,head_major,Lcap", [(1, False, 1024), (1, True, 1024), (4, False, 1024), (5, False, 1024),
+                                               (8, True, 1024), (1, True, 3072), (2, False, 1536)])
+def test_whole_group_form_equals_lone_sequences(Q, head_major, Lcap):
     """At least two (sequence, KV head) groups of at most 32 query rows per
-    CU over at most 1024 keys: one workgroup walks all of a group's chunks and
-    merges them itself, with no merge launch.  Each sequence must equal the
-    same sequence run alone (chunk items, then the merge launch), with ragged
-    lengths on both sides of the chunk edges (256 keys), both cache layouts
-    and causal blocks of 4, 5 (a verify block: two row tiles) and 8; sampled
-    sequences are within the parity gate of the oracle.  K, V, q ~ N(0,1)
-    bf16 drawn on the device (seeded)."""
+    CU over at most 1024 keys, or with at most 48 (query row, chunk) partials
+    (one query over 3072 keys, two over 1536): one workgroup walks all of a
+    group's chunks and merges them itself, with no merge launch (the
+    partials in LDS when they fit, else in the workspace).  Each sequence
+    must equal the same sequence run alone (chunk items, then the merge
+    launch), with ragged lengths on both sides of the chunk edges (256 keys),
+    both cache layouts and causal blocks of 2, 4, 5 (a verify block: two row
+    tiles) and 8; sampled sequences are within the parity gate of the
+    oracle.  K, V, q ~ N(0,1) bf16 drawn on the device (seeded)."""
     cus = torch.cuda.get_device_properties(dev()).multi_processor_count
-    B, Lcap = -(-2 * cus // HKV), 1024
-    g = torch.Generator(device=dev()).manual_seed(40 + Q + 2 * head_major)
+    B = -(-2 * cus // HKV)
+    g = torch.Generator(device=dev()).manual_seed(40 + Q + 2 * head_major + Lcap)
     shape = (B, HKV, Lcap, D) if head_major else (B, Lcap, HKV, D)
     kd = torch.randn(shape, generator=g, device=dev()).to(torch.bfloat16)
     vd = torch.randn(shape, generator=g, device=dev()).to(torch.bfloat16)
     qd = torch.randn((B, Q, HQ, D), generator=g, device=dev()).to(torch.bfloat16)
-    edges = [Q, Q + 1, 255, 256, 257, 511, 512, 513, 767, 768, 769, 1023, Lcap]
+    edges = [Q, Q + 1] + [e + d for e in range(256, Lcap, 256 if Lcap <= 1024 else 512) for d in (-1, 0, 1)] + [Lcap - 1, Lcap]
     rng = np.random.default_rng(Q)
     kv = np.array(edges + list(rng.integers(Q, Lcap + 1, B - len(edges))), np.int32)
     kvd = torch.tensor(kv, device=dev())
