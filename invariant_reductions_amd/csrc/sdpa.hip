@@ -57,6 +57,7 @@ constexpr int kHeadDim = 128;        // D supported by this build
 constexpr int kAttnWaves = 4;        // waves per chunk workgroup (frozen: 64 keys each)
 constexpr int kKeysPerWave = kChunk / kAttnWaves;
 constexpr int kPartStride = kHeadDim + 4;   // floats per (row, chunk) partial: o[D], m, l, pad
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 // The whole-group form (attn_kernel's WHOLE): at most kWholeMaxChunks chunks
 // per group with its chunk partials in the workspace, or with at most
 // kWholeLdsParts (query row, chunk) partials per group (4 rows over 12
@@ -97,8 +98,18 @@ struct AttnBufs {
     const uint16_t *q, *k, *v;
     const int32_t *kv_len;
     uint16_t *o;
-    float *part;          // chunk partials [B*Q*Hq][nchunks][kPartStride]
+    float *part;          // chunk partials [B][Hkv][nchunks][Q G][kPartStride] (see attn_part_block)
 };
+
+// The workspace holds the chunk partials group-major: for (sequence b, KV
+// head hk, chunk or split c) one block of the group's Q G query rows (row r
+// = query j G + head i), kPartStride floats each; a row's partials of
+// consecutive chunks are Q G kPartStride floats apart.  First float of the
+// block:
+__device__ inline int64_t attn_part_block(const AttnShape &sh, int64_t b, int64_t hk, int64_t c)
+{
+    return ((b * sh.Hkv + hk) * sh.nchunks + c) * (sh.Q * sh.G) * kPartStride;
+}
 
 // In-place 8 x 8 transpose of 16-bit elements held by one lane: row e is
 // m[e] (elements j = 0..7); afterwards m[j] holds column j.  Pairs of rows
@@ -218,23 +229,25 @@ __device__ inline void attn_merge_rows(const AttnBufs &bf, const AttnShape &sh, 
         const int lk = attn_last_key(kvlen, (int)sh.Q, j, sh.causal);
         if (lk < 0) continue;
         const int64_t row = ((int64_t)b * sh.Q + j) * sh.Hq + (int64_t)hk * sh.G + (rr - j * sh.G);
+        // row rr's partial of chunk c at pr + c cs
         const float *pr = lds ? lds + (int64_t)rr * lcs * kPartStride
-                              : bf.part + row * sh.nchunks * kPartStride;
+                              : bf.part + attn_part_block(sh, b, hk, 0) + (int64_t)rr * kPartStride;
+        const int64_t cs = lds ? kPartStride : R * (int64_t)kPartStride;
         const int nch = lk / kChunk + 1, nr = (nch + kRange - 1) / kRange;
         float M = -INFINITY;
-        for (int c = 0; c < nch; ++c) M = fmaxf(M, pr[c * kPartStride + kHeadDim]);
+        for (int c = 0; c < nch; ++c) M = fmaxf(M, pr[c * cs + kHeadDim]);
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         float l = 0.0f;
         for (int r = 0; r < nr; ++r) {
             const int c0 = r * kRange, n = min(nch - c0, kRange);
-            float Mr = pr[c0 * kPartStride + kHeadDim];
-            for (int i = 1; i < n; ++i) Mr = fmaxf(Mr, pr[(c0 + i) * kPartStride + kHeadDim]);
-            float w = attn_exp(pr[c0 * kPartStride + kHeadDim] - Mr);
-            float4 ov = *reinterpret_cast<const float4 *>(pr + c0 * kPartStride + quad * 4);
+            float Mr = pr[c0 * cs + kHeadDim];
+            for (int i = 1; i < n; ++i) Mr = fmaxf(Mr, pr[(c0 + i) * cs + kHeadDim]);
+            float w = attn_exp(pr[c0 * cs + kHeadDim] - Mr);
+            float4 ov = *reinterpret_cast<const float4 *>(pr + c0 * cs + quad * 4);
             float4 orr = make_float4(ov.x * w, ov.y * w, ov.z * w, ov.w * w);
-            float lr = pr[c0 * kPartStride + kHeadDim + 1] * w;
+            float lr = pr[c0 * cs + kHeadDim + 1] * w;
             for (int i = 1; i < n; ++i) {
-                const float *pc = pr + (c0 + i) * kPartStride;
+                const float *pc = pr + (c0 + i) * cs;
                 w = attn_exp(pc[kHeadDim] - Mr);
                 ov = *reinterpret_cast<const float4 *>(pc + quad * 4);
                 orr.x = orr.x + ov.x * w;
@@ -611,11 +624,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
                     if (r < R) {
                         const int j = r / sh.G;
                         if (last_key(it.kvlen, j) >= key0) {
-                            const int64_t h = (int64_t)it.hk * sh.G + (r - j * sh.G);
-                            float *dst =
-                                lds_parts ? &wpart[(r * lcs + it.c) * kPartStride]
-                                          : bf.part + ((((int64_t)it.b * sh.Q + j) * sh.Hq + h) * sh.nchunks + it.c) *
-                                                          kPartStride;
+                            float4 o[2];
 #pragma unroll
                             for (int half = 0; half < 2; ++half) {
                                 const int d = dg * 8 + half * 4;
@@ -623,16 +632,37 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
                                 const float4 o1 = *reinterpret_cast<const float4 *>(&ol[1][rr][d]);
                                 const float4 o2 = *reinterpret_cast<const float4 *>(&ol[2][rr][d]);
                                 const float4 o3 = *reinterpret_cast<const float4 *>(&ol[3][rr][d]);
-                                float4 o;
-                                o.x = ((o0.x + o1.x) + o2.x) + o3.x;
-                                o.y = ((o0.y + o1.y) + o2.y) + o3.y;
-                                o.z = ((o0.z + o1.z) + o2.z) + o3.z;
-                                o.w = ((o0.w + o1.w) + o2.w) + o3.w;
-                                *reinterpret_cast<float4 *>(dst + d) = o;
+                                o[half].x = ((o0.x + o1.x) + o2.x) + o3.x;
+                                o[half].y = ((o0.y + o1.y) + o2.y) + o3.y;
+                                o[half].z = ((o0.z + o1.z) + o2.z) + o3.z;
+                                o[half].w = ((o0.w + o1.w) + o2.w) + o3.w;
                             }
-                            if (dg == 0) {
-                                dst[kHeadDim] = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
-                                dst[kHeadDim + 1] = ((xl[0][rr] + xl[1][rr]) + xl[2][rr]) + xl[3][rr];
+                            const float mc = fmaxf(fmaxf(xm[0][rr], xm[1][rr]), fmaxf(xm[2][rr], xm[3][rr]));
+                            const float lc = ((xl[0][rr] + xl[1][rr]) + xl[2][rr]) + xl[3][rr];
+                            if (lds_parts) {
+                                float *dst = &wpart[(r * lcs + it.c) * kPartStride];
+#pragma unroll
+                                for (int half = 0; half < 2; ++half)
+                                    *reinterpret_cast<float4 *>(dst + dg * 8 + half * 4) = o[half];
+                                if (dg == 0) {
+                                    dst[kHeadDim] = mc;
+                                    dst[kHeadDim + 1] = lc;
+                                }
+                            } else {
+                                // the (sequence, KV head, chunk) block of R row partials: a
+                                // wave-uniform base and a 32-bit row offset (no per-lane
+                                // 64-bit address to keep alive across the walk)
+                                const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+                                    bf.part + attn_part_block(sh, it.b, it.hk, it.c), (short)0, 0x7fffffff, 0x00020000);
+                                const int voff = r * (kPartStride * 4) + dg * 32;
+#pragma unroll
+                                for (int half = 0; half < 2; ++half)
+                                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o[half]), prs,
+                                                                           voff + half * 16, 0, 0);
+                                if (dg == 0)                   // voff is the row's first byte here
+                                    __builtin_amdgcn_raw_buffer_store_b64(
+                                        i32x2{__builtin_bit_cast(int, mc), __builtin_bit_cast(int, lc)}, prs,
+                                        voff + kHeadDim * 4, 0, 0);
                             }
                         }
                     }
@@ -684,7 +714,7 @@ void attn_kernel(AttnBufs bf, const int32_t *__restrict__ kv_len, AttnShape sh, 
                     attn_store_out<S>(bf.o + row * kHeadDim + dg * 8, make_float4(ro[0], ro[1], ro[2], ro[3]), rl);
                     attn_store_out<S>(bf.o + row * kHeadDim + dg * 8 + 4, make_float4(ro[4], ro[5], ro[6], ro[7]), rl);
                 } else {
-                    float *dst = bf.part + (row * sh.nchunks + split) * kPartStride;
+                    float *dst = bf.part + attn_part_block(sh, it.b, it.hk, split) + (int64_t)r * kPartStride;
                     *reinterpret_cast<float4 *>(dst + dg * 8) = make_float4(ro[0], ro[1], ro[2], ro[3]);
                     *reinterpret_cast<float4 *>(dst + dg * 8 + 4) = make_float4(ro[4], ro[5], ro[6], ro[7]);
                     if (dg == 0) {
@@ -1082,15 +1112,18 @@ void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict
     __shared__ __attribute__((aligned(16))) float term[kMergeRanges][kHeadDim + 4];
     __shared__ float red[32 * kMergeRanges / kWave], rmax[kMergeRanges];
     const int64_t row = blockIdx.x;                       // (b * Q + j) * Hq + h
-    const int j = (int)((row / sh.Hq) % sh.Q);
+    const int j = (int)((row / sh.Hq) % sh.Q), h = (int)(row % sh.Hq);
     const int64_t b = row / (sh.Hq * sh.Q);
+    const int hk = h / sh.G;
     const int kvlen = (int)min((int64_t)kv_len[b], sh.max_kv);
     const int lk = attn_last_key(kvlen, (int)sh.Q, j, sh.causal);
     const int nthr = blockDim.x, slots = nthr / 32;
     const int quad = threadIdx.x & 31, slot = threadIdx.x >> 5;
     if (lk < 0) return;                                   // a bad kv_len: nothing this row may read
     const int nch = lk / (kChunk * sh.cps) + 1, nr = (nch + kRange - 1) / kRange;
-    const float *pr = part + row * sh.nchunks * kPartStride;
+    // this row's partial of chunk (or split) c at pr + c cs
+    const float *pr = part + attn_part_block(sh, b, hk, 0) + ((int64_t)j * sh.G + (h - hk * sh.G)) * kPartStride;
+    const int64_t cs = sh.Q * sh.G * (int64_t)kPartStride;
 
     // M = max over the chunk maxima: read first when the row's ranges take
     // several batches, else taken from the range maxima below (the same value:
@@ -1098,7 +1131,7 @@ void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict
     const bool one_batch = nr <= slots;
     float M = -INFINITY;
     if (!one_batch) {
-        for (int c = threadIdx.x; c < nch; c += nthr) M = fmaxf(M, pr[c * kPartStride + kHeadDim]);
+        for (int c = threadIdx.x; c < nch; c += nthr) M = fmaxf(M, pr[c * cs + kHeadDim]);
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
@@ -1119,7 +1152,7 @@ void attn_merge_kernel(const float *__restrict__ part, const int32_t *__restrict
             float4 ov[kRange];
 #pragma unroll
             for (int i = 0; i < kRange; ++i) {
-                const float *pc = pr + (c0 + min(i, n - 1)) * kPartStride;   // stays on written partials
+                const float *pc = pr + (c0 + min(i, n - 1)) * cs;   // stays on written partials
                 mv[i] = pc[kHeadDim];
                 lv[i] = pc[kHeadDim + 1];
                 ov[i] = *reinterpret_cast<const float4 *>(pc + quad * 4);
@@ -1201,7 +1234,7 @@ static bi_status check_attn(const void *q, const void *k, const void *v, const v
     return BI_OK;
 }
 
-// Workspace: the chunk partials, fp32 [B*Q*Hq][nchunks][kPartStride].
+// Workspace: the chunk partials, fp32 [B][Hkv][nchunks][Q Hq / Hkv][kPartStride].
 static size_t attn_partial_bytes(int64_t B, int64_t Q, int64_t max_kv_len, int64_t Hq)
 {
     return (size_t)(B * Q * Hq) * (size_t)cdiv(max_kv_len, kChunk) * kPartStride * sizeof(float);
