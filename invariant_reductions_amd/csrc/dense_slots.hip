@@ -259,7 +259,12 @@ constexpr int64_t kSlotTileCols = kDenseWaves * 16;
 constexpr int64_t kSlotMaxTiles = 16384;                    // N up to 2^21 columns
 constexpr size_t kSlotCounterBytes = kSlotMaxTiles * sizeof(unsigned);
 
-static int slot_mt(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+// Row tiles of the slot form: one up to 16 rows, else four (padding rows
+// read row M - 1 and are never stored).  Two tiles at 17..32 rows ran slower
+// than four on every decoder projection (18.9 against 14.8 us on 6144 x 4096
+// at 32 rows): the four-tile instantiations get the slot pairs over 64- or
+// 96-column tiles and their register budget.
+static int slot_mt(int64_t M) { return M <= 16 ? 1 : 4; }
 
 // Row counts the slot form takes: 16 < M <= 64, and down to M = 9 or 13 when
 // the weight is large -- there the one-workgroup-per-tile kernel reads each
@@ -373,11 +378,9 @@ static bool try_launch_slots(const void *x, const void *w, void *y, void *ws, si
     if (ws_bytes < slot_ws_bytes(M, N, kDenseWaves)) return false;
     if (packed) {
         if (slot_mt(M) == 1) launch_slots_mt<S, 1, EPI, true>(x, w, y, ws, M, N, K, st);
-        else if (slot_mt(M) == 2) launch_slots_mt<S, 2, EPI, true>(x, w, y, ws, M, N, K, st);
         else launch_slots_mt<S, 4, EPI, true>(x, w, y, ws, M, N, K, st);
     } else {
         if (slot_mt(M) == 1) launch_slots_mt<S, 1, EPI, false>(x, w, y, ws, M, N, K, st);
-        else if (slot_mt(M) == 2) launch_slots_mt<S, 2, EPI, false>(x, w, y, ws, M, N, K, st);
         else launch_slots_mt<S, 4, EPI, false>(x, w, y, ws, M, N, K, st);
     }
     return true;
