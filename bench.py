@@ -48,9 +48,10 @@ def step_traffic(cfg, B, ctx):
     mm_bytes = sum(2 * (N * K + M * K + M * O) for M, N, K, O in mm)
     swiglu_bytes = L * 2 * (2 * F * H + B * H + B * F)
     mm_flops = sum(2 * M * N * K for M, N, K, _ in mm)
-    # one plain RMSNorm (x -> h), then 2L residual adds fused with the norm that
-    # follows them (x, r -> x, h)
-    norm_bytes = (4 * B * H + 2 * H) + 2 * L * (8 * B * H + 2 * H)
+    # the first RMSNorm fused with the embedding lookup (h written, w read; the
+    # row itself is counted under embed), then 2L residual adds fused with the
+    # norm that follows them (x, r -> x, h)
+    norm_bytes = (2 * B * H + 2 * H) + 2 * L * (8 * B * H + 2 * H)
     attn_bytes = L * (4 * B * ctx * Hkv * D + 4 * B * Hq * D)
     attn_flops = L * 4 * B * Hq * D * ctx
     glue_bytes = (2 * B * H * 2                              # embed
@@ -439,7 +440,7 @@ def op_breakdown(model, plan, stream, B, ctx_mean, cfg, torch):
     tr = step_traffic(cfg, B, ctx_mean)
     H, L = cfg["hidden"], cfg["n_layers"]
     bytes_of = {"matmul": tr["mm_bytes"] - tr["swiglu_bytes"], "matmul_swiglu": tr["swiglu_bytes"],
-                "sdpa": tr["attn_bytes"], "rmsnorm": 4 * B * H + 2 * H,
+                "sdpa": tr["attn_bytes"], "embed_rmsnorm": 6 * B * H + 2 * H,
                 "add_rmsnorm": 2 * L * (8 * B * H + 2 * H)}
     res = {}
     for name, ms in tot.items():

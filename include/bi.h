@@ -298,6 +298,24 @@ bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, const void *
                          int64_t rows, int64_t H, float eps, int32_t dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Embedding lookup fused with the RMSNorm that reads it (a decoder step's
+ * first norm):
+ *   x_out[t, :] = table[ids[t], :]   (the bits bi_embed gives: a zero row for
+ *                                     an id outside [0, V))
+ *   y           = bi_rmsnorm(x_out)  (the same tree, the same bits)
+ * Source: as bi_rmsnorm; "Batch-invariant kernels ...", Mental model (a
+ * gather is pointwise over rows, so fusing it changes no reduction).
+ *   ids : device int32 [T];  table : [V, H] of `dtype` (BI_BF16 or BI_F16);
+ *   x_out, y : [T, H];  w : [H].  x_out and y must not alias the table.
+ *   One launch when H is a multiple of 8, H <= 4096 and the table, w, x_out
+ *   and y are 16-byte aligned; otherwise bi_embed then bi_rmsnorm (and their
+ *   requirements).  Errors: as bi_rmsnorm, BI_ERR_DTYPE for BI_F32,
+ *   BI_ERR_SHAPE for V outside [1, 2^31).
+ * ------------------------------------------------------------------------ */
+bi_status bi_embed_rmsnorm(const int32_t *ids, const void *table, void *x_out, const void *w, void *y,
+                           int64_t T, int64_t V, int64_t H, float eps, int32_t dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Decode / verify / prefill scaled-dot-product attention (GQA).
  * Source: "Fix/speculative shape invariance", Problem and Changes (the
  * softmax reduction layout of a query must be the same alone or inside a

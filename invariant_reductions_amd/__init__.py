@@ -67,6 +67,7 @@ def lib():
             "bi_sdpa": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, I32, P, SZ, P],
             "bi_sdpa_noalloc": [P, P, P, P, P, I64, I64, I64, I64, I32, I32, I32, F, I32, I32, I32, P],
             "bi_embed": [P, P, P, I64, I64, I64, P],
+            "bi_embed_rmsnorm": [P, P, P, P, P, I64, I64, I64, F, I32, P],
             "bi_rope_kv_write": [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, I32, I64, I32, P],
             "bi_silu_mul": [P, P, I64, I64, P],
             "bi_add": [P, P, P, I64, P],
@@ -463,6 +464,18 @@ def embed(ids, table, out=None, stream=None):
     y = out if out is not None else torch.empty((T, H), dtype=table.dtype, device=table.device)
     _check(lib().bi_embed(_ptr(ids), _ptr(table), _ptr(y), T, V, H, _stream(stream)), "bi_embed")
     return y
+
+
+def embed_rmsnorm(ids, table, w, eps: float = 1e-6, x_out=None, out=None, stream=None):
+    """x_out = embed(ids, table), out = rmsnorm(x_out, w) in one launch (same bits)."""
+    _dev(ids, table, w, x_out, out)
+    T = ids.numel()
+    V, H = table.shape
+    xo = x_out if x_out is not None else torch.empty((T, H), dtype=table.dtype, device=table.device)
+    y = out if out is not None else torch.empty((T, H), dtype=table.dtype, device=table.device)
+    _check(lib().bi_embed_rmsnorm(_ptr(ids), _ptr(table), _ptr(xo), _ptr(w), _ptr(y), T, V, H, eps, _dt(table),
+                                  _stream(stream)), "bi_embed_rmsnorm")
+    return xo, y
 
 
 def rope_kv_write(qkv, q_out, kc, vc, kv_len, cos_t, sin_t, B: int, Q: int, Hq: int, Hkv: int, D: int, stream=None,

@@ -119,17 +119,28 @@ __device__ inline uint4 row_chunk(const typename S::store_t *xr, const typename 
 // (with ADD, the sums this lane stored in the first phase).
 // ADD: the row is RNE(x + r), written to xo (which may alias x), and then
 // normalized -- the residual add of a pre-norm block fused with its norm.
-template <typename S, bool VEC, bool CACHED, bool ADD>
+// GATHER (cached, no ADD): row t is row ids[t] of the table x of V rows (a
+// zero row for an id outside [0, V)), written to xo as bi_embed writes it,
+// then normalized -- the embedding lookup fused with the first norm.
+template <typename S, bool VEC, bool CACHED, bool ADD, bool GATHER = false>
 __global__ __launch_bounds__(kNormRowsPerBlock * kWave)
 void rmsnorm_kernel(const typename S::store_t *x, const typename S::store_t *__restrict__ r,
                     typename S::store_t *xo, const typename S::store_t *__restrict__ w,
-                    typename S::store_t *__restrict__ y, int64_t rows, int64_t H, float eps)
+                    typename S::store_t *__restrict__ y, int64_t rows, int64_t H, float eps,
+                    const int32_t *__restrict__ ids, int64_t V)
 {
+    static_assert(!GATHER || (VEC && CACHED && !ADD), "the gather form is the cached plain norm, 16-byte rows");
     constexpr int E = S::kElemsPer16B;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kNormRowsPerBlock + wave_id();
     if (row >= rows) return;
-    const typename S::store_t *xr = x + row * H;
+    int32_t id = 0;
+    bool idok = true;
+    if constexpr (GATHER) {
+        id = ids[row];
+        idok = id >= 0 && id < V;
+    }
+    const typename S::store_t *xr = GATHER ? x + (int64_t)(idok ? id : 0) * H : x + row * H;
     const typename S::store_t *rr = ADD ? r + row * H : nullptr;
     typename S::store_t *xor_ = ADD ? xo + row * H : nullptr;
     typename S::store_t *yr = y + row * H;
@@ -175,11 +186,18 @@ void rmsnorm_kernel(const typename S::store_t *x, const typename S::store_t *__r
 #pragma unroll
             for (int i = 0; i < kNormCached; ++i) {
                 const int64_t v = lane + (int64_t)i * kWave;
-                cache[i] = row_chunk<S, VEC, ADD>(xr, rr, xor_, v, H, v < nch);
+                cache[i] = row_chunk<S, VEC, ADD>(xr, rr, xor_, v, H, v < nch && idok);
                 float xv[E];
                 chunk_vals<S>(cache[i], xv);
 #pragma unroll
                 for (int e = 0; e < E; ++e) ss = __builtin_fmaf(xv[e], xv[e], ss);
+            }
+            if constexpr (GATHER) {
+#pragma unroll
+                for (int i = 0; i < kNormCached; ++i) {
+                    const int64_t v = lane + (int64_t)i * kWave;
+                    if (v < nch) *reinterpret_cast<uint4 *>(xo + row * H + v * E) = cache[i];
+                }
             }
         }
         ss = wave_sum_butterfly(ss);
@@ -252,10 +270,19 @@ static void launch_rmsnorm(const void *x, const void *r, void *xo, const void *w
     dim3 grid((unsigned)cdiv(rows, kNormRowsPerBlock)), block(kNormRowsPerBlock * kWave);
     const T *xt = (const T *)x, *rt = (const T *)r, *wt = (const T *)w;
     T *xot = (T *)xo, *yt = (T *)y;
-    if (vec && cached) launch_kernel((rmsnorm_kernel<S, true, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
-    else if (vec) launch_kernel((rmsnorm_kernel<S, true, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
-    else if (cached) launch_kernel((rmsnorm_kernel<S, false, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
-    else launch_kernel((rmsnorm_kernel<S, false, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps);
+    const int32_t *noids = nullptr;                  // no gather
+    if (vec && cached)
+        launch_kernel((rmsnorm_kernel<S, true, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps, noids,
+                      (int64_t)0);
+    else if (vec)
+        launch_kernel((rmsnorm_kernel<S, true, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps, noids,
+                      (int64_t)0);
+    else if (cached)
+        launch_kernel((rmsnorm_kernel<S, false, true, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps, noids,
+                      (int64_t)0);
+    else
+        launch_kernel((rmsnorm_kernel<S, false, false, ADD>), grid, block, 0, st, xt, rt, xot, wt, yt, rows, H, eps,
+                      noids, (int64_t)0);
 }
 
 template <typename S>
@@ -313,6 +340,37 @@ extern "C" bi_status bi_add_rmsnorm(const void *x, const void *r, void *x_out, c
     else if (dtype == BI_F16) launch_rmsnorm<F16, true>(x, r, x_out, w, y, rows, H, eps, stream);
     else launch_rmsnorm<F32, true>(x, r, x_out, w, y, rows, H, eps, stream);
     return launch_status();
+}
+
+extern "C" bi_status bi_embed_rmsnorm(const int32_t *ids, const void *table, void *x_out, const void *w, void *y,
+                                      int64_t T, int64_t V, int64_t H, float eps, int32_t dtype, hipStream_t stream)
+{
+    bi_status s = check_norm(table, w, y, T, H, eps, dtype);
+    if (s != BI_OK) return s;
+    if (!ids || !x_out) return BI_ERR_NULL;
+    if (dtype == BI_F32) return BI_ERR_DTYPE;             // the embedding is a 16-bit table
+    if (V < 1 || V > (1ll << 31) - 1) return BI_ERR_SHAPE;
+    if (((uintptr_t)x_out & 1u) || ((uintptr_t)ids & 3u)) return BI_ERR_ALIGN;
+    const bool fused = H % 8 == 0 && cdiv(H / 8, kWave) <= kNormCached && host_aligned16(table) &&
+                       host_aligned16(w) && host_aligned16(y) && host_aligned16(x_out);
+    (void)hipGetLastError();
+    if (fused) {
+        const dim3 grid((unsigned)cdiv(T, kNormRowsPerBlock)), block(kNormRowsPerBlock * kWave);
+        if (dtype == BI_BF16)
+            launch_kernel((rmsnorm_kernel<BF16, true, true, false, true>), grid, block, 0, stream,
+                          (const uint16_t *)table, (const uint16_t *)nullptr, (uint16_t *)x_out, (const uint16_t *)w,
+                          (uint16_t *)y, T, H, eps, ids, V);
+        else
+            launch_kernel((rmsnorm_kernel<F16, true, true, false, true>), grid, block, 0, stream,
+                          (const uint16_t *)table, (const uint16_t *)nullptr, (uint16_t *)x_out, (const uint16_t *)w,
+                          (uint16_t *)y, T, H, eps, ids, V);
+        return launch_status();
+    }
+    // other shapes: the lookup, then the norm (the same bits; bi_embed's own
+    // requirements apply)
+    s = bi_embed(ids, table, x_out, T, V, H, stream);
+    if (s != BI_OK) return s;
+    return bi_rmsnorm(x_out, w, y, T, H, eps, dtype, stream);
 }
 
 extern "C" size_t bi_rmsnorm_split_workspace_bytes(int64_t rows, int32_t splits)

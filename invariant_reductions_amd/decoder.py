@@ -24,8 +24,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (W_PACKED, add_rmsnorm, argmax, embed, interleave_gate_up, lib, matmul_swiglu, matmul_ws,
-               pack_weights, rmsnorm, rope_kv_write, sdpa, sdpa_workspace_bytes)
+from . import (W_PACKED, add_rmsnorm, argmax, embed_rmsnorm, interleave_gate_up, lib, matmul_swiglu, matmul_ws,
+               pack_weights, rope_kv_write, sdpa, sdpa_workspace_bytes)
 from .inputs import rope_tables
 
 
@@ -97,11 +97,11 @@ class Decoder:
         qkv, q, o = self.qkv[:T], self.q[:T], self.o[:T]
         a = self.a[:T]
         kv = self.kv_len[:B]
-        embed(self.ids[:T], self.embed_w, out=x)
         scale = 1.0 / float(np.sqrt(self.D))
-        # Every residual add is fused with the RMSNorm that reads its result
-        # (the next block's norm, or the final norm after the last layer).
-        rmsnorm(x, self.layers[0]["attn_norm"], self.eps, out=h)
+        # The embedding lookup is fused with the first RMSNorm, and every
+        # residual add with the RMSNorm that reads its result (the next
+        # block's norm, or the final norm after the last layer).
+        embed_rmsnorm(self.ids[:T], self.embed_w, self.layers[0]["attn_norm"], self.eps, x_out=x, out=h)
         for li, Lw in enumerate(self.layers):
             matmul_ws(h, Lw["wqkv"], self.mws, out=qkv)
             kc, vc = self.kc[li][:B], self.vc[li][:B]
@@ -140,11 +140,12 @@ class Decoder:
         kv = self.kv_len[:B]
         scale = ctypes.c_float(1.0 / float(np.sqrt(self.D)))
         eps = ctypes.c_float(self.eps)
-        steps = [("embed", L.bi_embed, (p(self.ids), p(self.embed_w), p(x), T, self.V, H, st))]
+        steps = [("embed_rmsnorm", L.bi_embed_rmsnorm, (p(self.ids), p(self.embed_w), p(x),
+                                                         p(self.layers[0]["attn_norm"]), p(h), T, self.V, H, eps, 0,
+                                                         st))]
         mws, mwsb = p(self.mws), self.mws.numel()
         mm = lambda xin, w, out, N, K: ("matmul", L.bi_matmul_ws, (p(xin), p(w.data), p(out), T, N, K, 0, W_PACKED, mws,
                                                                     mwsb, st))
-        steps.append(("rmsnorm", L.bi_rmsnorm, (p(x), p(self.layers[0]["attn_norm"]), p(h), T, H, eps, 0, st)))
         for li, Lw in enumerate(self.layers):
             kc, vc = self.kc[li], self.vc[li]
             Lcap = kc.shape[2]

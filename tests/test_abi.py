@@ -161,7 +161,8 @@ def test_matmul_ws_validation_and_workspace_size():
     need = L.bi_matmul_ws_workspace_bytes(64, 4096, 4096, 0, 1)
     # fixed 64 KiB counter area + 32 column tiles x 8 groups x 8 waves x 4 KiB records
     assert need == 65536 + 32 * 8 * 8 * 4 * 4 * 64 * 4
-    assert L.bi_matmul_ws_workspace_bytes(17, 4096, 4096, 0, 1) == 65536 + 32 * 8 * 8 * 2 * 4 * 64 * 4
+    # from 17 rows the slot form takes four 16-row tiles (records of 4 KiB)
+    assert L.bi_matmul_ws_workspace_bytes(17, 4096, 4096, 0, 1) == 65536 + 32 * 8 * 8 * 4 * 4 * 64 * 4
     assert L.bi_matmul_ws_workspace_bytes(16, 4096, 4096, 0, 1) == 0      # short M: bi_matmul's kernels
     assert L.bi_matmul_ws_workspace_bytes(8, 28672, 4096, 0, 1) == 0
     # 8 < M <= 16 on a large weight: the slot form, 16-row tiles (1 KiB records)
@@ -285,6 +286,20 @@ def test_row_reduction_validation():
     assert L.bi_log_softmax(A, A, 4, 32000, 9, None) == DTYPE
     assert L.bi_log_softmax(ODD, A, 4, 32000, 0, None) == ALIGN
     assert L.bi_row_mean(A, P(0x10002), 4, 32000, 0, None) == ALIGN
+
+
+def test_embed_rmsnorm_validation():
+    L = bi.lib()
+    ids = P(0x10000)
+    assert L.bi_embed_rmsnorm(None, A, A, A, A, 4, 1000, 4096, 1e-6, 0, None) == NULL
+    assert L.bi_embed_rmsnorm(ids, A, None, A, A, 4, 1000, 4096, 1e-6, 0, None) == NULL
+    assert L.bi_embed_rmsnorm(P(0x10002), A, A, A, A, 4, 1000, 4096, 1e-6, 0, None) == ALIGN
+    assert L.bi_embed_rmsnorm(ids, A, ODD, A, A, 4, 1000, 4096, 1e-6, 0, None) == ALIGN
+    assert L.bi_embed_rmsnorm(ids, A, A, A, A, 0, 1000, 4096, 1e-6, 0, None) == SHAPE
+    assert L.bi_embed_rmsnorm(ids, A, A, A, A, 4, 0, 4096, 1e-6, 0, None) == SHAPE
+    assert L.bi_embed_rmsnorm(ids, A, A, A, A, 4, 1000, 4096, -1.0, 0, None) == SHAPE
+    assert L.bi_embed_rmsnorm(ids, A, A, A, A, 4, 1000, 4096, 1e-6, 2, None) == DTYPE   # f32: not a 16-bit table
+    assert L.bi_embed_rmsnorm(ids, A, A, A, A, 4, 1000, 4096, 1e-6, 9, None) == DTYPE
 
 
 def test_add_rmsnorm_validation():

@@ -5,7 +5,7 @@ import torch
 
 import invariant_reductions_amd as bi
 import oracle
-from gpu_util import bits_equal, dev, to_dev, to_np
+from gpu_util import assert_parity, bits_equal, dev, to_dev, to_np
 from invariant_reductions_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -17,6 +17,36 @@ def test_embed_gathers_rows():
     ids = rng.integers(0, 1000, size=37).astype(np.int32)
     out = to_np(bi.embed(torch.from_numpy(ids).to(dev()), to_dev(table, "bf16")))
     assert bits_equal(out, table[ids])
+
+
+@pytest.mark.parametrize("dtype,H,T", [("bf16", 4096, 64), ("f16", 4096, 7), ("bf16", 8192, 5), ("bf16", 1000, 3)])
+def test_embed_rmsnorm_equals_lookup_then_norm(dtype, H, T):
+    """The lookup fused with the first norm gives bi_embed's rows (zero rows for
+    ids outside [0, V)) and bi_rmsnorm's bits on them; 8192 columns (past the
+    one-launch form) and 1000 (not 16-byte rows) take the two-launch path and
+    must agree too.  The norm of the gathered rows is within the gate of the
+    oracle's."""
+    V = 1000
+    rng = np.random.default_rng(H + T)
+    table = inputs.normal(rng, (V, H), 3.0, dtype=dtype)
+    w = inputs.to_storage(1.0 + 0.1 * rng.standard_normal(H).astype(np.float32), dtype)
+    ids = rng.integers(0, V, size=T).astype(np.int32)
+    if T >= 3:
+        ids[1], ids[2] = -1, V                            # outside the table: zero rows
+    idd = torch.from_numpy(ids).to(dev())
+    td, wd = to_dev(table, dtype), to_dev(w, dtype)
+    if H % 8:
+        with pytest.raises(bi.BIError):                   # bi_embed's 16-byte rows
+            bi.embed_rmsnorm(idd, td, wd)
+        return
+    xo, y = bi.embed_rmsnorm(idd, td, wd)
+    x_ref = bi.embed(idd, td)
+    y_ref = bi.rmsnorm(x_ref, wd)
+    assert bits_equal(to_np(xo), to_np(x_ref))
+    assert bits_equal(to_np(y), to_np(y_ref))
+    rows = np.where(((ids >= 0) & (ids < V))[:, None], table[np.clip(ids, 0, V - 1)], 0).astype(table.dtype)
+    assert bits_equal(to_np(xo), rows)
+    assert_parity(to_np(y), oracle.rmsnorm(rows, w, dtype, 1e-6), dtype, f"{T}x{H}")
 
 
 @pytest.mark.parametrize("D", [128, 24])
