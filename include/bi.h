@@ -124,15 +124,18 @@ bi_status bi_pack_weights(const void *w, void *wp, int64_t N, int64_t K, int32_t
  * workspace, the slots of one output may be computed by different workgroups;
  * the partial sums of aligned slot groups meet in the workspace and are added
  * in the fixed tree order by whichever workgroup finishes last (also for
- * 8 < M <= 16 when N >= 16384, and 12 < M <= 16 when N K > 4096 * 4096).
- * Every other call runs bi_matmul's kernels.  w and w_layout as in bi_matmul (the slot
+ * 8 < M <= 16 when N >= 16384, and 12 < M <= 16 when N K > 4096 * 4096; and
+ * for 64 < M <= 128 when N < 20480, each 64-row chunk with its own counters
+ * and sums -- a verify block on a narrow projection).  Every other call runs
+ * bi_matmul's kernels.  w and w_layout as in bi_matmul (the slot
  * form takes BI_W_TRANSPOSED and BI_W_PACKED weights).
  *   ws, ws_bytes: device memory of at least
  *     bi_matmul_ws_workspace_bytes(M, N, K, dtype, w_layout) bytes
  *     (0 means no workspace is needed and ws may be NULL), 16-byte aligned,
  *     filled with zero bytes before its first use.  Its first 64 KiB hold
- *     per-column-tile counters that every call leaves at zero again, so one
- *     workspace sized for the largest shape serves calls of any shape.
+ *     per-(column tile, row chunk) counters that every call leaves at zero
+ *     again, so one workspace sized for the largest shape serves calls of any
+ *     shape (the size grows with the rows past 64).
  *     Calls that share a workspace must be ordered (same stream or
  *     synchronised); concurrent ones race.
  *   Errors: as bi_matmul, plus BI_ERR_WORKSPACE when ws is NULL or too small

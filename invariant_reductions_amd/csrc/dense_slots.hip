@@ -63,7 +63,8 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
     const int g = lane >> 4, c = lane & 15;
     const int ct = blockIdx.x, grp = blockIdx.y;
     // Row chunk blockIdx.z: rows [TR z, TR z + TR) of a call with more rows
-    // than one tile (only with all eight slots in the workgroup: no exchange)
+    // than one tile; with an exchange, each (column tile, row chunk) has its
+    // own counter and group sums
     {
         const int64_t r0 = (int64_t)blockIdx.z * TR;
         x += r0 * K;
@@ -219,8 +220,9 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
         // sums only after it has seen the count.
         constexpr int CPOL_DEVICE = 16;            // sc1
         constexpr int REC = MT * kWave * 16;       // bytes per (group, wave)
+        const int64_t tile = (int64_t)blockIdx.z * gridDim.x + ct;           // (row chunk, column tile)
         const __amdgpu_buffer_rsrc_t rsrc =
-            __builtin_amdgcn_make_buffer_rsrc(part + (int64_t)ct * GRP * NW * (REC / 4), (short)0, GRP * NW * REC, 0x00020000);
+            __builtin_amdgcn_make_buffer_rsrc(part + tile * GRP * NW * (REC / 4), (short)0, GRP * NW * REC, 0x00020000);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, h[m]), rsrc,
@@ -228,12 +230,12 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
         __builtin_amdgcn_s_waitcnt(0);             // every store of this wave acknowledged
         __syncthreads();
         if (threadIdx.x == 0) {
-            const unsigned prev = __hip_atomic_fetch_add(&counters[ct], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             s_last = prev == (unsigned)(GRP - 1);
         }
         __syncthreads();
         if (!s_last) return;
-        if (threadIdx.x == 0) __hip_atomic_store(&counters[ct], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         f32x4 out[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -257,6 +259,7 @@ void dense_slots_kernel(const typename S::store_t *__restrict__ x, const typenam
 // call that shares the workspace.
 constexpr int64_t kSlotTileCols = kDenseWaves * 16;
 constexpr int64_t kSlotMaxTiles = 16384;                    // N up to 2^21 columns
+constexpr int64_t kSlotExchRowsMax = 128;                   // rows of the form with an exchange
 constexpr size_t kSlotCounterBytes = kSlotMaxTiles * sizeof(unsigned);
 
 // Row tiles of the slot form: one up to 16 rows, else four (padding rows
@@ -273,7 +276,14 @@ static int slot_mt(int64_t M) { return M <= 16 ? 1 : 4; }
 // on 4096 x 4096 the streaming kernel stays ahead).
 static bool slot_takes(int64_t M, int64_t N, int64_t K)
 {
-    if (M > 64 || M < 1) return false;
+    if (M > kSlotExchRowsMax || M < 1) return false;
+    // two 64-row chunks, each meeting its own group sums, where the tiled
+    // kernel's 128 x 128 tiles would fill under 5/8 of the CUs (the narrow
+    // projections of a 16-sequence verify block: 80 x 4096 x 14336 40 us,
+    // 62 us with all eight slots per workgroup); from 129 rows the chunks
+    // with all eight slots per workgroup and no exchange are ahead (320 x
+    // 4096 x 14336: 85 against 104 us), bi_matmul's form
+    if (M > 64) return cdiv(N, 128) * 8 < 5 * (int64_t)device_cu_count();
     if (M > 16) return true;
     if (N >= 16384) return M > 8;
     return M > 12 && N * K > 4096ll * 4096ll;
@@ -282,7 +292,8 @@ static bool slot_takes(int64_t M, int64_t N, int64_t K)
 static size_t slot_ws_bytes(int64_t M, int64_t N, int groups)
 {
     const int64_t rec = (int64_t)slot_mt(M) * 4 * kWave * (int64_t)sizeof(float);
-    return kSlotCounterBytes + (size_t)(cdiv(N, kSlotTileCols) * groups * kDenseWaves * rec);
+    const int64_t nrc = cdiv(M, slot_mt(M) * 16);                       // row chunks, each with its own sums
+    return kSlotCounterBytes + (size_t)(nrc * cdiv(N, kSlotTileCols) * groups * kDenseWaves * rec);
 }
 
 template <typename S, int MT, int Q, int EPI, bool PK, int NW = kDenseWaves>
@@ -293,15 +304,16 @@ static void launch_slots_t(const void *x, const void *w, void *y, void *ws, int6
     // group-sum records: (N / 16 NW tiles) x (8 / Q groups) x NW waves fit in
     // slot_ws_bytes's (N / 128) x 8 x 8 whenever NW Q >= 8 or there is no exchange
     static_assert(NW == kDenseWaves || Q == kDenseWaves || NW * Q >= kDenseWaves, "group sums exceed the workspace");
-    const int64_t ntc = cdiv(N, NW * 16);
+    const int64_t ntc = cdiv(N, NW * 16), nrc = cdiv(M, MT * 16);      // column tiles, row chunks
     unsigned *counters = (unsigned *)ws;
     float *part = (float *)((char *)ws + kSlotCounterBytes);
     // W ring depth and waves per SIMD: two workgroups per CU (at most 128
     // VGPRs) wherever the accumulators allow it.
     constexpr int DW = MT == 4 ? 2 : 4;
     constexpr int OCC = Q * MT <= 4 ? 4 : 2;
-    launch_kernel((dense_slots_kernel<S, MT, Q, DW, OCC, EPI, NW, PK>), dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q)),
-                       dim3(NW * kWave), 0, st, (const T *)x, (const T *)w, (T *)y, part, counters, M, N, K);
+    launch_kernel((dense_slots_kernel<S, MT, Q, DW, OCC, EPI, NW, PK>),
+                  dim3((unsigned)ntc, (unsigned)(kDenseWaves / Q), (unsigned)nrc), dim3(NW * kWave), 0, st,
+                  (const T *)x, (const T *)w, (T *)y, part, counters, M, N, K);
 }
 
 // More than 64 rows, few column tiles (bi_matmul's path, dense.hip): one
@@ -338,12 +350,13 @@ template <typename S, int MT, int EPI, bool PK>
 static void launch_slots_mt(const void *x, const void *w, void *y, void *ws, int64_t M, int64_t N, int64_t K,
                             hipStream_t st)
 {
-    const int64_t ntc = cdiv(N, kSlotTileCols), cu = device_cu_count();
+    // (tiles counted over all row chunks of a call past one chunk)
+    const int64_t nrc = cdiv(M, MT * 16), ntc = cdiv(N, kSlotTileCols) * nrc, cu = device_cu_count();
     // All eight slots in one workgroup (no exchange) once the column tiles
     // alone come close to one per CU; with 7-wave (112-column) tiles when
     // those fill the CUs more evenly (one such workgroup runs per CU).
     if (ntc * 4 >= cu * 3) {
-        if (cu_balance(cdiv(N, 7 * 16), cu) > cu_balance(ntc, cu) + 0.02)
+        if (cu_balance(cdiv(N, 7 * 16) * nrc, cu) > cu_balance(ntc, cu) + 0.02)
             launch_slots_t<S, MT, 8, EPI, PK, 7>(x, w, y, ws, M, N, K, st);
         else
             launch_slots_t<S, MT, 8, EPI, PK>(x, w, y, ws, M, N, K, st);
@@ -357,7 +370,7 @@ static void launch_slots_mt(const void *x, const void *w, void *y, void *ws, int
         // half the group sums to exchange and a quarter for the last arriver
         // to read; 96-column tiles where those fill the CUs more evenly
         // (6144 columns: 256 workgroups instead of 384).
-        if (cu_balance(cdiv(N, 6 * 16) * 4, cu) > cu_balance(cdiv(N, 4 * 16) * 4, cu) + 0.02)
+        if (cu_balance(cdiv(N, 6 * 16) * 4 * nrc, cu) > cu_balance(cdiv(N, 4 * 16) * 4 * nrc, cu) + 0.02)
             launch_slots_t<S, MT, 2, EPI, PK, 6>(x, w, y, ws, M, N, K, st);
         else
             launch_slots_t<S, MT, 2, EPI, PK, 4>(x, w, y, ws, M, N, K, st);
@@ -413,7 +426,7 @@ using namespace bi;
 extern "C" size_t bi_matmul_ws_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t w_layout)
 {
     if (N < 1 || K < 1 || !slot_takes(M, N, K) || (w_layout != W_TRANS && w_layout != W_PACKED) || (dtype != BI_BF16 && dtype != BI_F16) ||
-        cdiv(N, kSlotTileCols) > kSlotMaxTiles)
+        cdiv(N, kSlotTileCols) > kSlotMaxTiles || (M > 64 && cdiv(M, 64) * cdiv(N, 64) > kSlotMaxTiles))
         return 0;
     return slot_ws_bytes(M, N, kDenseWaves);
 }

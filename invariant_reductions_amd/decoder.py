@@ -80,7 +80,9 @@ class Decoder:
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=d)
         # one zero-filled matmul workspace for every projection (calls are stream-ordered)
         mshapes = [(self.qkvn, self.H), (self.H, self.qn), (2 * self.F, self.H), (self.H, self.F), (self.V, self.H)]
-        need = max(lib().bi_matmul_ws_workspace_bytes(min(T, 64), n, k, 0, 1) for n, k in mshapes)
+        # (the slot form takes up to 128 rows on the narrow projections, every
+        # 64-row chunk with its own group sums: size for the most rows a call has)
+        need = max(lib().bi_matmul_ws_workspace_bytes(m, n, k, 0, 1) for n, k in mshapes for m in {min(T, 64), min(T, 128)})
         self.mws = torch.zeros(max(int(need), 16), dtype=torch.uint8, device=d)
         # the fused gate/up + SwiGLU call has its own (its size covers the
         # scratch product of the shapes the fused kernel does not take)

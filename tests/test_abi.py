@@ -168,7 +168,11 @@ def test_matmul_ws_validation_and_workspace_size():
     # 8 < M <= 16 on a large weight: the slot form, 16-row tiles (1 KiB records)
     assert L.bi_matmul_ws_workspace_bytes(9, 28672, 4096, 0, 1) == 65536 + 224 * 8 * 8 * 1 * 4 * 64 * 4
     assert L.bi_matmul_ws_workspace_bytes(64, 128 * 16385, 128, 0, 1) == 0   # beyond the counter area
-    assert L.bi_matmul_ws_workspace_bytes(65, 4096, 4096, 0, 1) == 0      # long M: bi_matmul's kernels
+    # past 64 rows on a narrow weight (256 CUs assumed without a GPU): every
+    # 64-row chunk has its own group sums
+    assert L.bi_matmul_ws_workspace_bytes(65, 4096, 4096, 0, 1) == 65536 + 2 * 32 * 8 * 8 * 4 * 4 * 64 * 4
+    assert L.bi_matmul_ws_workspace_bytes(100, 28672, 4096, 0, 1) == 0    # wide: bi_matmul's tiled kernel
+    assert L.bi_matmul_ws_workspace_bytes(129, 4096, 4096, 0, 1) == 0     # longer M: bi_matmul's kernels
     assert L.bi_matmul_ws_workspace_bytes(64, 4096, 4096, 2, 1) == 0      # f32
     assert L.bi_matmul_ws_workspace_bytes(64, 4096, 4096, 0, 0) == 0      # natural layout
     assert L.bi_matmul_ws(A, A, A, 64, 4096, 4096, 0, 1, None, 0, None) == WORKSPACE

@@ -52,7 +52,13 @@ def same(a, b):
     (64, 32768, 1024),
     (64, 28656, 256),      # 7-wave (112-column) tiles fill 256 CUs; last tile ragged
     (20, 28656, 384),
-    (65, 512, 4096),       # long M: bi_matmul's kernels
+    (65, 512, 4096),       # past 64 rows: 64-row chunks, each with its own group sums
+    (80, 6144, 4096),      # a verify block of 16 sequences on the QKV projection
+    (80, 4096, 14336),     # ... on the down projection
+    (128, 4096, 4096),     # the most rows the form with an exchange takes
+    (100, 1000, 896),      # ragged chunk, ragged column tile
+    (129, 4096, 4096),     # past that: bi_matmul's kernels
+    (320, 6144, 4096),     # a verify block of 64 sequences
     (64, 512, 4100),       # K not a multiple of 128: bi_matmul's kernels
 ])
 def test_bits_equal_plain_matmul(dtype, M, N, K):
@@ -95,10 +101,12 @@ def test_oracle_parity(dtype, M, N, K):
 def test_workspace_reuse_leaves_counters_zero():
     """One workspace across calls of different shapes in stream order: every
     result is right and the counter area is zero after each call."""
-    big = bi.matmul_workspace(64, 32000, 4096, device=dev())
     L = bi.lib()
+    need = max(L.bi_matmul_ws_workspace_bytes(*sh, 0, 1) for sh in ((64, 32000, 4096), (128, 6144, 4096)))
+    big = torch.zeros(need, dtype=torch.uint8, device=dev())
     for (M, N, K) in ((64, 32000, 4096), (64, 4096, 4096), (7, 4096, 14336), (64, 1000, 4224), (1, 96, 128),
-                      (64, 32000, 4096), (64, 4096, 4096), (64, 28672, 4096), (1, 32000, 4096)):
+                      (128, 6144, 4096), (80, 4096, 14336), (64, 32000, 4096), (64, 4096, 4096), (100, 4096, 4096),
+                      (64, 28672, 4096), (1, 32000, 4096)):
         x = rand((M, K), "bf16", seed=M + N)
         w = rand((N, K), "bf16", seed=N + K, scale=0.02)
         y = bi.matmul_ws(x, w, big)
@@ -237,7 +245,7 @@ def test_packed_swiglu_and_split_variant():
     wu = rand((F, K), "bf16", seed=8, scale=0.02)
     wil = bi.interleave_gate_up(wg, wu)
     wilp = bi.pack_weights(wil)
-    ws = bi.matmul_swiglu_workspace(64, F, K, device=dev())
+    ws = bi.matmul_swiglu_workspace(70, F, K, device=dev())       # sized for the most rows of the calls below
     for M in (1, 17, 64, 70):
         x = rand((M, K), "bf16", seed=M)
         assert same(bi.matmul_swiglu(x, wilp, ws), bi.matmul_swiglu(x, wil, ws)), f"M={M}"
