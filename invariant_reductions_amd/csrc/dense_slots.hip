@@ -262,12 +262,17 @@ constexpr int64_t kSlotMaxTiles = 16384;                    // N up to 2^21 colu
 constexpr int64_t kSlotExchRowsMax = 128;                   // rows of the form with an exchange
 constexpr size_t kSlotCounterBytes = kSlotMaxTiles * sizeof(unsigned);
 
-// Row tiles of the slot form: one up to 16 rows, else four (padding rows
-// read row M - 1 and are never stored).  Two tiles at 17..32 rows ran slower
-// than four on every decoder projection (18.9 against 14.8 us on 6144 x 4096
-// at 32 rows): the four-tile instantiations get the slot pairs over 64- or
-// 96-column tiles and their register budget.
-static int slot_mt(int64_t M) { return M <= 16 ? 1 : 4; }
+// Row tiles of the slot form: four (padding rows read row M - 1 and are
+// never stored), or one up to 16 rows on a weight with enough column tiles
+// for a workgroup per CU with half the slots.  Two tiles at 17..32 rows ran
+// slower than four on every decoder projection (18.9 against 14.8 us on 6144
+// x 4096 at 32 rows; 16.3 against 14.8 at 16 rows): the four-tile
+// instantiations get the slot pairs over 64- or 96-column tiles and their
+// register budget; on the wide weights one tile stays ~2% ahead.
+static int slot_mt(int64_t M, int64_t N)
+{
+    return M <= 16 && cdiv(N, kSlotTileCols) * 2 >= (int64_t)device_cu_count() ? 1 : 4;
+}
 
 // Row counts the slot form takes: 16 < M <= 64, and down to M = 9 or 13 when
 // the weight is large -- there the one-workgroup-per-tile kernel reads each
@@ -291,8 +296,8 @@ static bool slot_takes(int64_t M, int64_t N, int64_t K)
 
 static size_t slot_ws_bytes(int64_t M, int64_t N, int groups)
 {
-    const int64_t rec = (int64_t)slot_mt(M) * 4 * kWave * (int64_t)sizeof(float);
-    const int64_t nrc = cdiv(M, slot_mt(M) * 16);                       // row chunks, each with its own sums
+    const int64_t rec = (int64_t)slot_mt(M, N) * 4 * kWave * (int64_t)sizeof(float);
+    const int64_t nrc = cdiv(M, slot_mt(M, N) * 16);                    // row chunks, each with its own sums
     return kSlotCounterBytes + (size_t)(nrc * cdiv(N, kSlotTileCols) * groups * kDenseWaves * rec);
 }
 
@@ -390,10 +395,10 @@ static bool try_launch_slots(const void *x, const void *w, void *y, void *ws, si
         return false;
     if (ws_bytes < slot_ws_bytes(M, N, kDenseWaves)) return false;
     if (packed) {
-        if (slot_mt(M) == 1) launch_slots_mt<S, 1, EPI, true>(x, w, y, ws, M, N, K, st);
+        if (slot_mt(M, N) == 1) launch_slots_mt<S, 1, EPI, true>(x, w, y, ws, M, N, K, st);
         else launch_slots_mt<S, 4, EPI, true>(x, w, y, ws, M, N, K, st);
     } else {
-        if (slot_mt(M) == 1) launch_slots_mt<S, 1, EPI, false>(x, w, y, ws, M, N, K, st);
+        if (slot_mt(M, N) == 1) launch_slots_mt<S, 1, EPI, false>(x, w, y, ws, M, N, K, st);
         else launch_slots_mt<S, 4, EPI, false>(x, w, y, ws, M, N, K, st);
     }
     return true;
