@@ -336,7 +336,7 @@ extern "C" const char *bi_build_info(void)
            " chunks of 256 keys, 4 waves x 64 keys, P as hi+lo 16-bit parts in MFMA (lo first),"
            " chunk partials merged in ranges of 16 chunks (weights 2^(m_c-M_r), ascending), ranges merged"
            " in ascending order (weights 2^(M_r-M)); many short groups: one launch, the merge in the"
-           " workgroup; prompts (>= 128 query rows per KV head, <= 4096 keys):"
+           " workgroup; prompts (>= 128 query rows per KV head, <= 8192 keys):"
            " the same tree in one launch, one wave playing the 4 quarters of a chunk;"
            " dense M > 64: the same K tree walked slot by slot, x/W tiles shared through LDS";
 }
