@@ -700,7 +700,7 @@ def invariance_overhead(torch, bi, dev, B):
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
-    def verdict(t_inv, alts):
+    def overhead_entry(t_inv, alts):
         best = min(alts, key=alts.get)
         return {"invariant_us": round(t_inv * 1e3, 2), **{f"{k}_us": round(v * 1e3, 2) for k, v in alts.items()},
                 "best_non_invariant": best, "overhead": round(t_inv / alts[best] - 1, 3),
@@ -727,7 +727,7 @@ def invariance_overhead(torch, bi, dev, B):
         alts = {k: v for k, v in t.items() if k != "inv"}
         best_split = min((k for k in alts if k.startswith("split")), key=alts.get)
         alts = {"hipblaslt": alts["hipblaslt"], best_split: alts[best_split]}
-        res["matmul"][f"{M}x{N}x{K}"] = verdict(t["inv"], alts)
+        res["matmul"][f"{M}x{N}x{K}"] = overhead_entry(t["inv"], alts)
         del ws_, wp
     # quantized: the invariant 4-bit kernel (tile-packed) against its own
     # split-K variant (best of 2, 4, 8 splits) and hipBLASLt on the same
@@ -757,7 +757,7 @@ def invariance_overhead(torch, bi, dev, B):
             t = _ab(torch, fns)
             alts = {k: v for k, v in t.items() if k != "inv"}
             best_split = min((k for k in alts if k.startswith("split")), key=alts.get)
-            res["qmatmul"][f"mxfp4 {M}x{N}x{K}"] = verdict(t["inv"], {"hipblaslt_f16": alts["hipblaslt_f16"],
+            res["qmatmul"][f"mxfp4 {M}x{N}x{K}"] = overhead_entry(t["inv"], {"hipblaslt_f16": alts["hipblaslt_f16"],
                                                                       best_split: alts[best_split]})
         del wqp, wd
     H = 4096
@@ -776,7 +776,7 @@ def invariance_overhead(torch, bi, dev, B):
         t = _ab(torch, fns)
         alts = {k: v for k, v in t.items() if k != "inv"}
         best_split = min((k for k in alts if k.startswith("split")), key=alts.get)
-        res["rmsnorm"][f"{Bn}x{H}"] = verdict(t["inv"], {"torch": alts["torch"], best_split: alts[best_split]})
+        res["rmsnorm"][f"{Bn}x{H}"] = overhead_entry(t["inv"], {"torch": alts["torch"], best_split: alts[best_split]})
         del xs
     Hq, Hkv, D = 32, 8, 128
     for Bn, Lk in ((1, 16388), (1, 65540), (B, 768)):
@@ -807,7 +807,7 @@ def invariance_overhead(torch, bi, dev, B):
         t = _ab(torch, fns)
         alts = {k: v for k, v in t.items() if k != "inv"}
         best_split = min((k for k in alts if k.startswith("split")), key=alts.get)
-        res["sdpa"][f"B{Bn} Q1 Lk{Lk}"] = verdict(t["inv"], {"torch_sdpa": alts["torch_sdpa"],
+        res["sdpa"][f"B{Bn} Q1 Lk{Lk}"] = overhead_entry(t["inv"], {"torch_sdpa": alts["torch_sdpa"],
                                                              best_split: alts[best_split]})
         del ks, vs
     torch.cuda.empty_cache()
