@@ -99,7 +99,7 @@ def test_tokens_vary_between_sequences(plain64):
     assert len({tuple(r) for r in toks64}) > 1
 
 
-@pytest.mark.parametrize("B,mode", [(64, "replay"), (16, "corrupt"), (1, "corrupt")])
+@pytest.mark.parametrize("B,mode", [(64, "replay"), (16, "corrupt"), (4, "corrupt"), (1, "corrupt")])
 def test_speculative_equals_plain(model, prompts, plain64, B, mode):
     toks64, cs64 = plain64
 
