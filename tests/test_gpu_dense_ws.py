@@ -35,13 +35,13 @@ def same(a, b):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("M,N,K", [
     (1, 96, 128),          # M <= 16: bi_matmul's kernels
-    (9, 28672, 512),       # 8 < M <= 16 on a large weight: the slot form (16-row tiles)
-    (13, 6144, 4096),
+    (9, 28672, 512),       # 8 < M <= 16 on a wide weight: the slot form with one 16-row tile
+    (13, 6144, 4096),      # ... on a narrow one: four row tiles (padding rows never stored)
     (12, 6144, 4096),      # ... but not here: bi_matmul's kernels
     (17, 96, 128),         # one block: slots 1..7 own nothing
     (23, 1000, 896),       # 7 blocks, ragged column tile
     (16, 4096, 4096),
-    (17, 6144, 4096),      # two row tiles of the 32-row form
+    (17, 6144, 4096),      # four row tiles, 17 rows
     (33, 4096, 14336),     # the down projection, 112 blocks
     (64, 4096, 4096),
     (64, 1000, 4224),      # 33 blocks: uneven slots
